@@ -1,0 +1,307 @@
+"""Benchmark of the MI355X KDA library (one GPU).
+
+One step = one pass of the whole hot path over one batch: the chunk-local kernel, the
+inter-chunk kernel (prefill of the batch) and one decode step per sequence continuing
+from the prefill's final states.  The headline batch is B=4, H=8, T=2048, dk=dv=128,
+bf16 inputs, fp32 state.  Three input sets are rotated so the ~105 MB working set
+cannot stay resident in the 256 MB Infinity Cache.
+
+The JSON line also carries, measured in the same run:
+  * "k3_layer": prefill of B=1, H=96, T=65,536 (the K3 layer shape),
+  * "decode":   128 recurrent steps over B=256 x H=96 heads (1.6 GB of fp32 state),
+  * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
+each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|varlen|none]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+CHUNK = 16
+
+
+def prefill_flops_per_token_head(dk: int, dv: int) -> float:
+    """Algorithmic flops per token-head of the chunked prefill: the three dk x dv products per
+    token (K+ S, Q+ S, K~^T Delta), the triangular halves of the 16x16 tiles (A_kk, A_qk,
+    T' (V - K+S), A_qk Delta), and the state decay."""
+    return 6 * dk * dv + CHUNK * (3 * dk + 2 * dv) + 2 * dk * dv / CHUNK
+
+
+def prefill_bytes_per_token_head(dk: int, dv: int, in_bytes: int = 2) -> float:
+    """Algorithmic HBM bytes per token-head: q, k, log_alpha, v, beta read once, o (fp32) written once."""
+    return in_bytes * (3 * dk + dv + 1) + 4 * dv
+
+
+def inter_chunk_bytes_per_token_head(dk: int, dv: int, in_bytes: int = 2) -> float:
+    """The inter-chunk kernel's own algorithmic traffic: q, k, log_alpha, v read, o written, and the
+    chunk-local matrices T' and A_qk (2 x 16 x 16 fp32 per 16 tokens) read."""
+    return in_bytes * (3 * dk + dv) + 4 * dv + 2 * 16 * 16 * 4 / CHUNK
+
+
+def decode_bytes_per_head(dk: int, dv: int, in_bytes: int = 2) -> float:
+    """Decode step: fp32 state read + written, q, k, log_alpha, v, beta read, o written."""
+    return 2 * dk * dv * 4 + in_bytes * (3 * dk + dv + 1) + 4 * dv
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every KDA call is enqueued on)."""
+
+    def __init__(self, torch, n: int):
+        self.torch = torch
+        self.start = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.end = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.i = 0
+
+    def __enter__(self):
+        self.start[self.i].record()
+        return self
+
+    def __exit__(self, *exc):
+        self.end[self.i].record()
+        self.i += 1
+
+    def mean_ms(self) -> float:
+        return sum(s.elapsed_time(e) for s, e in zip(self.start[:self.i], self.end[:self.i])) / max(self.i, 1)
+
+
+def cpu_baseline(workload, seed: int = 0) -> dict:
+    """The fp64 oracle (as it stands) on the host cores: the whole headline batch
+    (prefill of every sequence and head, then one decode token per sequence)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    x = workloads.prefill_inputs(workload, device="cpu", seed=seed)
+    d = workloads.decode_step_inputs(workloads.custom([1] * workload.nseq, workload.H, workload.dk, workload.dv),
+                                     0, device="cpu", seed=seed)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    names = ("q", "k", "v", "log_alpha", "beta")
+    args = [x[n].double().numpy() for n in names]
+    t0 = time.perf_counter()
+    _, fin = oracle.prefill(*args, cu_seqlens=x["cu_seqlens"].numpy(), nthreads=cores)
+    oracle.decode(*(d[n].double().numpy() for n in names), fin, nthreads=cores)
+    dt = time.perf_counter() - t0
+    tokens = workload.total_tokens + workload.nseq
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"whole batch: prefill of {workload.nseq}x{workload.seqlens[0]} tokens x {workload.H} heads "
+                      f"(dk=dv={workload.dk}) + 1 decode token per sequence, fp64, {cores} threads"}
+
+
+def bench_main(args, torch, kda, workloads, dev):
+    w = workloads.workload(2)
+    N, H, dk, dv, nseq = w.total_tokens, w.H, w.dk, w.dv, w.nseq
+    sets = [workloads.prefill_inputs(w, device=dev, seed=s) for s in range(3)]
+    dw = workloads.custom([1] * nseq, H, dk, dv)
+    dsets = [workloads.decode_step_inputs(dw, 0, device=dev, seed=s) for s in range(3)]
+    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
+    o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+    od = torch.empty((nseq, H, dv), dtype=torch.float32, device=dev)
+    n_ev = args.warmup + args.steps
+    t_cl, t_ic, t_dec = Timer(torch, n_ev), Timer(torch, n_ev), Timer(torch, n_ev)
+
+    def step(i, timed):
+        x, d = sets[i % 3], dsets[i % 3]
+        if timed:
+            with t_cl:
+                kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+            with t_ic:
+                kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
+                                    o=o, final_state=fin)
+            with t_dec:
+                kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
+        else:
+            kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+            kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
+                                o=o, final_state=fin)
+            kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # wall-clock of exactly K untimed-by-event steps (no per-kernel events inside)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, False)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-kernel durations: the same K steps again with HIP events around each launch
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    ms_cl, ms_ic, ms_dec = t_cl.mean_ms(), t_ic.mean_ms(), t_dec.mean_ms()
+    tokens = N + nseq
+    th = N * H
+    flops = th * prefill_flops_per_token_head(dk, dv)
+    return {
+        "w": w, "wall_ms": wall_ms, "tokens": tokens, "ms_chunk_local": ms_cl, "ms_inter_chunk": ms_ic,
+        "ms_decode": ms_dec, "prefill_tflops": flops / ((ms_cl + ms_ic) * 1e-3) / 1e12,
+        "ic_bytes": th * inter_chunk_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4,
+        "cl_bytes": th * (2 * (2 * dk + dk + 1)) + (N // 16 + nseq) * H * 2048,
+    }
+
+
+def bench_prefill_workload(index, torch, kda, workloads, dev, reps: int):
+    w = workloads.workload(index)
+    N, H, dk, dv, nseq = w.total_tokens, w.H, w.dk, w.dv, w.nseq
+    log(f"[bench] generating workload {w.name}: {w.notes}")
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
+    o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+    t_cl, t_ic = Timer(torch, reps + 1), Timer(torch, reps + 1)
+
+    def run():
+        with t_cl:
+            kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+        with t_ic:
+            kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
+                                o=o, final_state=fin)
+
+    run()
+    torch.cuda.synchronize()
+    t_cl.i = t_ic.i = 0
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms_cl, ms_ic = t_cl.mean_ms(), t_ic.mean_ms()
+    ms = ms_cl + ms_ic
+    th = N * H
+    flops = th * prefill_flops_per_token_head(dk, dv)
+    alg_bytes = th * prefill_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4
+    res = {
+        "workload": w.name, "tokens": N, "heads": H, "sequences": nseq, "ms": round(ms, 4),
+        "ms_chunk_local": round(ms_cl, 4), "ms_inter_chunk": round(ms_ic, 4),
+        "tokens_per_s": N / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
+        "mfma_peak_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "hbm_gbs_algorithmic": alg_bytes / (ms * 1e-3) / 1e9,
+        "hbm_roofline_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "t_hbm_ms": alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+    }
+    if index == 5:
+        res["seqlens"] = list(w.seqlens)
+    del x, ws, o, fin
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(torch, kda, workloads, dev):
+    w = workloads.workload(4)
+    B, H, dk, dv = w.nseq, w.H, w.dk, w.dv
+    log(f"[bench] generating decode workload: {w.notes}")
+    state = workloads.decode_initial_state(B, H, dk, dv, device=dev)
+    steps = [workloads.decode_step_inputs(w, s, device=dev) for s in range(w.decode_steps)]
+    o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    # one untimed warm-up step on a scratch copy of the state
+    scratch = state.clone()
+    kda.kda_decode_step(steps[0]["q"], steps[0]["k"], steps[0]["v"], steps[0]["log_alpha"], steps[0]["beta"],
+                        scratch, o=o)
+    del scratch
+    torch.cuda.synchronize()
+    t = Timer(torch, w.decode_steps)
+    for x in steps:
+        with t:
+            kda.kda_decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state, o=o)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    per_step = B * H * decode_bytes_per_head(dk, dv)
+    gbs = per_step / (ms * 1e-3) / 1e9
+    res = {"workload": w.name, "heads": B * H, "steps": w.decode_steps, "ms_per_step": round(ms, 5),
+           "bytes_per_step": per_step, "gbs": gbs, "hbm_peak_frac": gbs / HBM_PEAK_GBS,
+           "tokens_per_s": B / (ms * 1e-3)}
+    del state, steps, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all", choices=["all", "main", "k3", "decode", "varlen", "none"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (heads and sequences shard "
+              "across GPUs with no exchange -- see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gated_delta_rule_51_amd as kda
+    import workloads
+
+    if not os.path.exists(kda.LIBRARY):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    out = {"metric": "KDA prefill tokens/s + TFLOP/s (% MFMA peak); decode state GB/s (% HBM peak)",
+           "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic"}
+
+    if args.only in ("all", "main"):
+        log("[bench] headline step: batched prefill B=4 H=8 T=2048 + 1 decode token per sequence")
+        m = bench_main(args, torch, kda, workloads, dev)
+        w = m["w"]
+        out["value"] = m["tokens"] / (m["wall_ms"] * 1e-3)
+        out["ms_per_step"] = round(m["wall_ms"], 5)
+        out["config"] = {"workload": "batched_prefill_then_decode", "batch": w.nseq, "heads": w.H,
+                         "seq_len": w.seqlens[0], "dk": w.dk, "dv": w.dv, "chunk": CHUNK,
+                         "inputs": "bf16", "state": "fp32", "output": "fp32",
+                         "step": "kda_chunk_local + kda_inter_chunk over the batch, then kda_decode_step "
+                                 "(1 token per sequence) from the final states",
+                         "input_sets_rotated": 3}
+        kernels = {"chunk_local": m["ms_chunk_local"], "inter_chunk": m["ms_inter_chunk"],
+                   "decode": m["ms_decode"]}
+        out["kernel_ms"] = {k: round(v, 5) for k, v in kernels.items()}
+        out["prefill_tflops"] = m["prefill_tflops"]
+        out["prefill_mfma_peak_frac"] = m["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS
+        dom = max(("chunk_local", "inter_chunk"), key=lambda k: kernels[k])
+        b = m["ic_bytes"] if dom == "inter_chunk" else m["cl_bytes"]
+        ach = b / (kernels[dom] * 1e-3) / 1e9
+        out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                           "algorithmic_bytes_per_launch": b}
+        if not args.no_cpu_baseline:
+            log("[bench] cpu baseline: fp64 oracle on the same batch")
+            out["cpu_baseline"] = cpu_baseline(w)
+    if args.only in ("all", "k3"):
+        log("[bench] K3 layer prefill B=1 H=96 T=65536")
+        out["k3_layer"] = bench_prefill_workload(3, torch, kda, workloads, dev, reps=5)
+    if args.only in ("all", "decode"):
+        log("[bench] recurrent decode B=256 H=96, 128 steps")
+        out["decode"] = bench_decode(torch, kda, workloads, dev)
+    if args.only in ("all", "varlen"):
+        log("[bench] varlen 1M-token prefill")
+        out["varlen_1m"] = bench_prefill_workload(5, torch, kda, workloads, dev, reps=3)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

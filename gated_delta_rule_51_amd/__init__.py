@@ -1,0 +1,210 @@
+"""MI355X-native Kimi Delta Attention (KDA): Python binding of the C ABI in include/kda.h.
+
+This module only marshals arguments: it checks devices, dtypes and shapes,
+allocates outputs and workspaces with torch (device memory is the only thing
+torch provides here), and calls the HIP library through ctypes on torch's
+current stream.  Every step of the computation runs in the library's kernels;
+there is no CPU or PyTorch fallback.  If the library has not been built the
+first call raises.
+
+Names mirror the C entry points:
+    kda_prefill, kda_chunk_local, kda_inter_chunk, kda_decode_step,
+    kda_prefill_workspace_bytes, kda_status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libkda_mi355x.so")
+CHUNK = 16
+GATE_LOWER_BOUND = -5.0
+
+KDA_F32, KDA_BF16 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE",
+          4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
+EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
+           "kda_decode_step", "kda_status_string", "kda_last_hip_error")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(message)
+        self.code = code
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the HIP library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"KDA HIP library not found at {path}; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_prefill_workspace_bytes.restype = sz
+    lib.kda_prefill_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                vp, vp, vp, sz, vp]
+    lib.kda_chunk_local.restype = ctypes.c_int
+    lib.kda_chunk_local.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.kda_inter_chunk.restype = ctypes.c_int
+    lib.kda_inter_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                    vp, sz, vp, vp, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_last_hip_error.restype = i32
+    lib.kda_last_hip_error.argtypes = []
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def kda_status_string(code: int) -> str:
+    return load_library().kda_status_string(int(code)).decode()
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        lib = load_library()
+        msg = lib.kda_status_string(code).decode()
+        if code == 6:
+            msg += f" (hipError {lib.kda_last_hip_error()})"
+        raise KDAError(code, msg)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KDA_BF16
+    if t == torch.float32:
+        return KDA_F32
+    raise TypeError(f"KDA inputs must be bfloat16 or float32, got {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_inputs(q, k, v, log_alpha, beta):
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU (got {t.device}); the KDA library has no CPU path")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, log_alpha and beta must share one dtype")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (N, H, dk) or log_alpha.shape != (N, H, dk) or v.shape != (N, H, dv) or beta.shape != (N, H):
+        raise ValueError("expected q, k, log_alpha [N, H, dk], v [N, H, dv], beta [N, H]")
+    return N, H, dk, dv
+
+
+def kda_prefill_workspace_bytes(total_tokens: int, nseq: int, H: int, dk: int, dv: int,
+                                dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load_library().kda_prefill_workspace_bytes(total_tokens, nseq, H, dk, dv, _dtype_code(dtype)))
+
+
+def _cu(cu_seqlens, N, device):
+    if cu_seqlens is None:
+        return torch.tensor([0, N], dtype=torch.int32, device=device)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor on the inputs' device")
+    return cu_seqlens
+
+
+def alloc_workspace(total_tokens: int, nseq: int, H: int, dk: int, dv: int, dtype, device) -> torch.Tensor:
+    nbytes = kda_prefill_workspace_bytes(total_tokens, nseq, H, dk, dv, dtype)
+    return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=device)
+
+
+def kda_prefill(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
+                output_final_state: bool = True, o=None, final_state=None, workspace=None,
+                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill over packed sequences (see include/kda.h).
+
+    q, k, log_alpha: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; one dtype (bf16 or fp32).
+    cu_seqlens: int32 [nseq + 1] on the device (None = one sequence of N tokens).
+    init_state: fp32 [nseq, H, dk, dv] or None.  Returns (o fp32 [N, H, dv], final_state).
+    """
+    N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    cu = _cu(cu_seqlens, N, q.device)
+    nseq = cu.numel() - 1
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    if init_state is not None and (init_state.dtype != torch.float32 or tuple(init_state.shape) != (nseq, H, dk, dv)
+                                   or not init_state.is_contiguous()):
+        raise ValueError("init_state must be contiguous fp32 [nseq, H, dk, dv]")
+    if workspace is None:
+        workspace = alloc_workspace(N, nseq, H, dk, dv, q.dtype, q.device)
+    _check(load_library().kda_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
+        H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, final_state
+
+
+def kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, workspace, *, stream=None) -> torch.Tensor:
+    """Chunk-local phase only; writes T' and A_qk per (chunk slot, head) into ``workspace``."""
+    N, H, dk = q.shape
+    nseq = cu_seqlens.numel() - 1
+    _check(load_library().kda_chunk_local(
+        _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), nseq, N, H, dk,
+        _dtype_code(q.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
+
+
+def kda_inter_chunk(q, k, v, log_alpha, cu_seqlens, workspace, init_state=None, *, o=None,
+                    final_state=None, output_final_state: bool = True, stream=None):
+    """Inter-chunk phase only; reads the workspace written by kda_chunk_local."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    nseq = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check(load_library().kda_inter_chunk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(init_state), _ptr(cu_seqlens), nseq, N, H,
+        dk, dv, _dtype_code(q.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(o), _ptr(final_state), _stream(stream)))
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None, stream=None) -> torch.Tensor:
+    """One decode token for B x H heads; ``state`` (fp32 [B, H, dk, dv]) is updated in place.
+
+    q, k, log_alpha: [B, H, dk]; v: [B, H, dv]; beta: [B, H].  Returns o fp32 [B, H, dv].
+    """
+    B, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv) or not state.is_contiguous() \
+            or state.device != q.device:
+        raise ValueError("state must be contiguous fp32 [B, H, dk, dv] on the inputs' device")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    _check(load_library().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o), B, H, dk, dv,
+        _dtype_code(q.dtype), _stream(stream)))
+    return o

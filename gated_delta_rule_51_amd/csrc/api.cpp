@@ -1,0 +1,168 @@
+// C ABI of the KDA library: argument validation on the host, then launches on
+// the caller's stream.  No allocation, no synchronisation, no printing.
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+kda_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return KDA_OK;
+    g_last_hip_error = static_cast<int32_t>(e);
+    return KDA_ERR_HIP;
+}
+
+kda_status check_common(int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                        kda_dtype dt) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (nseq < 1 || H < 1 || total_tokens < 0 || total_tokens >= (int64_t(1) << 31))
+        return KDA_ERR_SHAPE;
+    // grid limits: chunk slots and (sequence, head) chains must fit a 32-bit grid
+    if (kda::chunk_slots(total_tokens, nseq) >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if ((int64_t)nseq * H >= (int64_t(1) << 28)) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+size_t workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H) {
+    return static_cast<size_t>(kda::chunk_slots(total_tokens, nseq)) * static_cast<size_t>(H) *
+           kda::WS_FLOATS_PER_CHUNK_HEAD * sizeof(float);
+}
+
+kda_status check_ptrs(std::initializer_list<const void *> required,
+                      std::initializer_list<const void *> optional) {
+    for (const void *p : required)
+        if (!p) return KDA_ERR_NULL;
+    for (const void *p : required)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    for (const void *p : optional)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+// Token-indexed inputs: q, k, v, log_alpha are read four elements at a time (8 bytes
+// for bf16, 16 for fp32); beta (when the entry point takes it) is read element by
+// element.  With no tokens they may be NULL.
+kda_status check_inputs(std::initializer_list<const void *> vec4, bool takes_beta, const void *beta,
+                        bool bf16, bool any_tokens) {
+    const uintptr_t elem = bf16 ? 2u : 4u;
+    for (const void *p : vec4) {
+        if (!p) {
+            if (any_tokens) return KDA_ERR_NULL;
+            continue;
+        }
+        if (reinterpret_cast<uintptr_t>(p) & (4 * elem - 1)) return KDA_ERR_ALIGN;
+    }
+    if (!takes_beta) return KDA_OK;
+    if (beta) {
+        if (reinterpret_cast<uintptr_t>(beta) & (elem - 1)) return KDA_ERR_ALIGN;
+    } else if (any_tokens) {
+        return KDA_ERR_NULL;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
+                                   int32_t dv, kda_dtype dt) {
+    if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    return workspace_bytes(total_tokens, nseq, H);
+}
+
+kda_status kda_chunk_local(const void *q, const void *k, const void *log_alpha, const void *beta,
+                           const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, int32_t H,
+                           int32_t dk, kda_dtype dt, void *workspace, size_t ws_bytes, void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, 16, dt);
+    if (st != KDA_OK) return st;
+    st = check_inputs({q, k, log_alpha}, true, beta, dt == KDA_BF16, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {});
+    if (st != KDA_OK) return st;
+    if (!workspace || ws_bytes < workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    kda::ChunkLocalArgs a{q, k, log_alpha, beta, cu_seqlens, nseq, H, dk, total_tokens,
+                          dt == KDA_BF16, static_cast<float *>(workspace), stream};
+    return hip_status(kda::launch_chunk_local(a));
+}
+
+kda_status kda_inter_chunk(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const float *init_state, const int32_t *cu_seqlens, int32_t nseq,
+                           int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                           const void *workspace, size_t ws_bytes, float *o, float *final_state,
+                           void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    st = check_inputs({q, k, v, log_alpha}, false, nullptr, dt == KDA_BF16, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
+    if (st != KDA_OK) return st;
+    if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    if (!workspace || ws_bytes < workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    kda::InterChunkArgs a{q, k, v, log_alpha, init_state, cu_seqlens, nseq, H, dk, dv,
+                          total_tokens, dt == KDA_BF16, static_cast<const float *>(workspace), o,
+                          final_state, 0, stream};
+    return hip_status(kda::launch_inter_chunk(a));
+}
+
+kda_status kda_prefill(const void *q, const void *k, const void *v, const void *log_alpha,
+                       const void *beta, const float *init_state, const int32_t *cu_seqlens,
+                       int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                       kda_dtype dt, float *o, float *final_state, void *workspace, size_t ws_bytes,
+                       void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
+    if (st != KDA_OK) return st;
+    if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    if (!workspace || ws_bytes < workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    st = kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, nseq, total_tokens, H, dk, dt,
+                         workspace, ws_bytes, stream);
+    if (st != KDA_OK) return st;
+    return kda_inter_chunk(q, k, v, log_alpha, init_state, cu_seqlens, nseq, total_tokens, H, dk,
+                           dv, dt, workspace, ws_bytes, o, final_state, stream);
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, float *state, float *o, int32_t B, int32_t H,
+                           int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || (int64_t)B * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, true);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({state, o}, {});
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
+    return hip_status(kda::launch_decode(a));
+}
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer is misaligned (fp32 buffers 16 B; q/k/v/log_alpha 4 elements; beta 1 element)";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: nseq, H, B or total_tokens out of range";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk/dv not in {16,32,64,128} or unknown dtype";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed (see kda_last_hip_error)";
+        default: return "KDA: unknown status";
+    }
+}
+
+int32_t kda_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

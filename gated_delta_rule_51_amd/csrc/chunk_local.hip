@@ -1,0 +1,182 @@
+// Chunk-local phase of the KDA prefill (gfx950): one wave per (16-token
+// chunk, head), fully parallel.
+//
+// Chunked form (Kimi K3 report digest, "Kimi Delta Attention": the output of
+// chunk t is an inter-chunk term (Gamma (.) Q) S plus an intra-chunk term
+// A V~).  With G_r the inclusive cumulative log-decay of token r inside the
+// chunk (per key channel), K+ = K (.) e^{G}, K- = K (.) e^{-G}, Q+ = Q (.) e^{G}:
+//     A_kk = diag(beta) * strictly_lower(K+ K-^T)      (16 x 16)
+//     T    = (I + A_kk)^{-1}                            (unit lower triangular)
+//     A_qk = lower_incl_diag(Q+ K-^T)                   (16 x 16)
+// This kernel writes T' = T diag(beta) and A_qk to the workspace.  The
+// pseudo-keys W = T' K+ and pseudo-values U = T' V are applied by the
+// inter-chunk phase in the factored form Delta = T' (V - K+ S) = U - W S.
+//
+// Bounded decay (same page, "bounded decay" section): g >= -5, so over a
+// 16-token chunk G lies in [-80, 0] and e^{-G} <= e^80 stays inside fp32/bf16
+// range.  The decayed key-key and query-key blocks are therefore dense
+// 16x16xdk matrix products on the matrix cores; e^{+-G} are formed as running
+// products of e^{+-g} (no exp of a large argument).
+//
+// Precision: A_kk uses single-bf16 operands (its rounding error is damped by
+// the triangular solve); A_qk uses split-bf16 operands (hi*hi + lo*hi + hi*lo,
+// ~16-bit mantissas) because it feeds the output directly.  fp32 inputs use
+// fp32 MFMAs throughout.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <int DK, typename T>
+__global__ __launch_bounds__(64) void chunk_local_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ g,
+    const T *__restrict__ beta, const int32_t *__restrict__ cu, int32_t nseq, int32_t H,
+    float *__restrict__ ws) {
+    constexpr bool F32 = sizeof(T) == 4;
+    constexpr int NB = DK / 16;
+    constexpr int LD = DK + 4;  // padded LDS row (floats)
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x;
+
+    // Which sequence owns this slot: the largest s with floor(cu[s]/16) + s <= slot.
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)(cu[mid] / 16) + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int s = lo;
+    const int64_t bos = cu[s], eos = cu[s + 1];
+    const int64_t j = slot - ((int64_t)(bos / 16) + s);
+    if (j < 0 || 16 * j >= eos - bos) return;  // slot not used by any chunk
+    const int64_t t0 = bos + 16 * j;
+    const int n = (int)((eos - t0) < 16 ? (eos - t0) : 16);
+
+    __shared__ float sP[16][LD];     // e^{G_r}   (running product of alpha)
+    __shared__ float sPi[16][LD];    // e^{-G_r}
+    __shared__ float sA[16][17];
+    __shared__ float sBeta[16];
+
+    // Per key channel: running products over the chunk's tokens (pads: g = 0).
+    // Unconditional loads from clamped rows (n >= 1), padding zeroed by a select.
+    for (int c = lane; c < DK; c += 64) {
+        float gv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float x = load_in(g + ((t0 + (r < n ? r : n - 1)) * H + h) * DK + c);
+            gv[r] = (r < n) ? x : 0.f;
+        }
+        float p = 1.f, pi = 1.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p *= decay_exp(gv[r]);
+            pi *= decay_exp(-gv[r]);
+            sP[r][c] = p;
+            sPi[r][c] = pi;
+        }
+    }
+    if (lane < 16) {
+        const float b = load_in(beta + (t0 + (lane < n ? lane : n - 1)) * H + h);
+        sBeta[lane] = (lane < n) ? b : 0.f;
+    }
+    __syncthreads();
+
+    // Operands in the A/B fragment layout: lane (g4, m) holds token m, channels
+    // 16b + 4*g4 + 0..3 of K+, K-, Q+.
+    const int m = lane & 15, g4 = lane >> 4;
+    const bool valid = m < n;
+    const int64_t mrow = t0 + (valid ? m : n - 1);
+    const T *krow = k + (mrow * H + h) * DK;
+    const T *qrow = q + (mrow * H + h) * DK;
+    f32x4 akk = zero4(), aqk = zero4();
+    auto operands = [&](int b, f32x4 &kp, f32x4 &km, f32x4 &qp) {
+        const int c = 16 * b + 4 * g4;
+        const f32x4 kl = load_in4(krow + c);
+        const f32x4 ql = load_in4(qrow + c);
+        const f32x4 kk = valid ? kl : zero4();
+        const f32x4 qq = valid ? ql : zero4();
+        const f32x4 P = *reinterpret_cast<const f32x4 *>(&sP[m][c]);
+        const f32x4 Pi = *reinterpret_cast<const f32x4 *>(&sPi[m][c]);
+        kp = kk * P;
+        km = kk * Pi;
+        qp = qq * P;
+    };
+    if constexpr (F32) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            f32x4 kp, km, qp;
+            operands(b, kp, km, qp);
+            akk = mma_f32_k16(kp, km, akk);
+            aqk = mma_f32_k16(qp, km, aqk);
+        }
+    } else if constexpr (NB == 1) {
+        f32x4 kp, km, qp;
+        operands(0, kp, km, qp);
+        akk = mma16(to_bf16x4(kp), to_bf16x4(km), akk);
+        aqk = mma_split_k16(split4(qp), split4(km), aqk);
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; b += 2) {
+            f32x4 kp0, km0, qp0, kp1, km1, qp1;
+            operands(b, kp0, km0, qp0);
+            operands(b + 1, kp1, km1, qp1);
+            akk = mma_single_k32(to_bf16x4(kp0), to_bf16x4(kp1), to_bf16x4(km0), to_bf16x4(km1), akk);
+            aqk = mma_split_k32(split4(qp0), split4(qp1), split4(km0), split4(km1), aqk);
+        }
+    }
+
+    // Accumulator lane (g4, i) holds rows r = 4*g4 + jj of column i.
+    float *wsT = ws + (slot * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
+    float *wsA = wsT + 256;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int r = 4 * g4 + jj, i = m;
+        sA[r][i] = (r > i) ? sBeta[r] * akk[jj] : 0.f;
+        wsA[r * 16 + i] = (r >= i) ? aqk[jj] : 0.f;
+    }
+    __syncthreads();
+
+    // T = (I + A_kk)^{-1} by forward substitution; lane c builds column c:
+    // T[r][c] = [r == c] - sum_{i < r} A[r][i] T[i][c]  (T[i][c] = 0 for i < c).
+    if (lane < 16) {
+        const int c = lane;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc += sA[r][i] * t[i];
+            t[r] = ((r == c) ? 1.f : 0.f) - acc;
+        }
+        const float bc = sBeta[c];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wsT[r * 16 + c] = t[r] * bc;
+    }
+}
+
+template <int DK, typename T>
+static hipError_t launch_cl_t(const ChunkLocalArgs &a) {
+    const int64_t slots = chunk_slots(a.total_tokens, a.nseq);
+    hipLaunchKernelGGL((chunk_local_kernel<DK, T>), dim3((unsigned)slots, (unsigned)a.H), dim3(64), 0,
+                       (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.g,
+                       (const T *)a.beta, a.cu, a.nseq, a.H, a.ws);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_cl_dt(const ChunkLocalArgs &a) {
+    switch (a.dk) {
+        case 16: return launch_cl_t<16, T>(a);
+        case 32: return launch_cl_t<32, T>(a);
+        case 64: return launch_cl_t<64, T>(a);
+        case 128: return launch_cl_t<128, T>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_chunk_local(const ChunkLocalArgs &a) {
+    return a.bf16 ? launch_cl_dt<__bf16>(a) : launch_cl_dt<float>(a);
+}
+
+}  // namespace kda

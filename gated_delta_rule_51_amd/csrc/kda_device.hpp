@@ -1,0 +1,164 @@
+// Device building blocks shared by the KDA kernels (gfx950 / CDNA4, wave64).
+//
+// Fragment convention.  Every matrix operand is cut into 16x16 tiles.  A
+// "frag4" of a 16x16 tile X is what one lane of a 64-lane wave holds of it:
+//     lane l = 16*g + n  (g = l / 16 in 0..3, n = l % 16) holds X[4g + j][n], j = 0..3.
+// This is the accumulator layout of the 16x16 MFMA instructions, so a product's
+// result is a frag4.  A product D += A * B over a 16-long contraction takes
+//     A as the frag4 of A^T  (lane (g, m) holds A[m][4g + j]) and
+//     B as the frag4 of B    (lane (g, n) holds B[4g + j][n]).
+// The hardware maps (lane group g, register slot) to the contraction index in
+// the same way for A and B, so any consistent packing of two 16-long blocks
+// into the 32-long contraction of v_mfma_f32_16x16x32_bf16 is valid; the
+// helpers below put block 0 in slots 0..3 and block 1 in slots 4..7.
+//
+// Precision.  A "split" operand x = hi + lo holds the bf16 rounding of x in hi
+// and the bf16 rounding of the residual in lo (about 16 mantissa bits in
+// total).  A split product uses hi*hi + lo*hi + hi*lo (and lo*lo where it costs
+// nothing), all accumulated in fp32 by the matrix cores.  For fp32 inputs the products use
+// v_mfma_f32_16x16x4_f32, which multiplies in full fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CHUNK = 16;
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 x) {
+    return bf16_bits_to_f32(__builtin_bit_cast(uint16_t, x));
+}
+
+// Round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    bf16x4 r;
+    r[0] = f32_to_bf16(x[0]);
+    r[1] = f32_to_bf16(x[1]);
+    r[2] = f32_to_bf16(x[2]);
+    r[3] = f32_to_bf16(x[3]);
+    return r;
+}
+
+__device__ __forceinline__ f32x4 from_bf16x4(bf16x4 x) {
+    f32x4 r;
+    r[0] = bf16_to_f32(x[0]);
+    r[1] = bf16_to_f32(x[1]);
+    r[2] = bf16_to_f32(x[2]);
+    r[3] = bf16_to_f32(x[3]);
+    return r;
+}
+
+struct Split4 {
+    bf16x4 hi, lo;
+};
+
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+    s.hi = to_bf16x4(x);
+    s.lo = to_bf16x4(x - from_bf16x4(s.hi));
+    return s;
+}
+
+// Input element loads: T is float or __bf16; the value is widened exactly.
+template <typename T>
+__device__ __forceinline__ float load_in(const T *p) {
+    if constexpr (sizeof(T) == 4) {
+        return *p;
+    } else {
+        return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(p));
+    }
+}
+
+// Four consecutive input elements (8-byte aligned for bf16, 16-byte for fp32).
+template <typename T>
+__device__ __forceinline__ f32x4 load_in4(const T *p) {
+    if constexpr (sizeof(T) == 4) {
+        return *reinterpret_cast<const f32x4 *>(p);
+    } else {
+        const u16x4 b = *reinterpret_cast<const u16x4 *>(p);
+        f32x4 r;
+        r[0] = bf16_bits_to_f32(b[0]);
+        r[1] = bf16_bits_to_f32(b[1]);
+        r[2] = bf16_bits_to_f32(b[2]);
+        r[3] = bf16_bits_to_f32(b[3]);
+        return r;
+    }
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A single 16-long contraction runs on the 32-long instruction with the upper
+// half zero.  The 16x16x16 bf16 MFMA is deliberately not used: chained with the
+// 16x16x32 form in these kernels it produced wrong, schedule-dependent results
+// on gfx950, while the 16x16x32-only code is exact in the same tests.
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    const bf16x4 z = {};
+    return mma32(cat(a, z), cat(b, z), c);
+}
+
+// fp32 product over one 16-long block: four 16x16x4 fp32 MFMAs; MFMA j uses
+// contraction index 4g + j from lane group g.
+__device__ __forceinline__ f32x4 mma_f32_k16(f32x4 a, f32x4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+
+// Split product over one 16-long block, as two K=32 MFMAs sharing the A
+// operand [a.hi | a.lo]: against [b.hi | b.hi] (hi*hi + lo*hi) and against
+// [b.lo | b.lo] (hi*lo + lo*lo), i.e. the full product of the split values.
+__device__ __forceinline__ f32x4 mma_split_k16(const Split4 &a, const Split4 &b, f32x4 c) {
+    const bf16x8 aa = cat(a.hi, a.lo);
+    c = mma32(aa, cat(b.hi, b.hi), c);
+    return mma32(aa, cat(b.lo, b.lo), c);
+}
+
+// Split A against an exactly representable bf16 B: hi*B + lo*B, one K=32 MFMA.
+__device__ __forceinline__ f32x4 mma_splitA_k16(const Split4 &a, bf16x4 b, f32x4 c) {
+    return mma32(cat(a.hi, a.lo), cat(b, b), c);
+}
+
+// Split product over two 16-long blocks (0 and 1): three K=32 MFMAs.
+__device__ __forceinline__ f32x4 mma_split_k32(const Split4 &a0, const Split4 &a1,
+                                               const Split4 &b0, const Split4 &b1, f32x4 c) {
+    c = mma32(cat(a0.hi, a1.hi), cat(b0.hi, b1.hi), c);
+    c = mma32(cat(a0.lo, a1.lo), cat(b0.hi, b1.hi), c);
+    return mma32(cat(a0.hi, a1.hi), cat(b0.lo, b1.lo), c);
+}
+
+// Single-bf16 product over two 16-long blocks: one K=32 MFMA.
+__device__ __forceinline__ f32x4 mma_single_k32(bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 c) {
+    return mma32(cat(a0, a1), cat(b0, b1), c);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// exp for the decay factors: ROCm's device expf (full-accuracy path).
+__device__ __forceinline__ float decay_exp(float x) { return expf(x); }
+
+}  // namespace kda

@@ -1,0 +1,54 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the
+// kernel translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Workspace per (chunk slot, head): T' = (I + A_kk)^-1 diag(beta), then A_qk,
+// each a row-major 16x16 fp32 matrix.
+constexpr int WS_FLOATS_PER_CHUNK_HEAD = 2 * 16 * 16;
+
+// Chunk slots: sequence s owns slots floor(cu[s]/16) + s + j, j < ceil(len_s/16).
+// The map is injective and bounded by floor(N/16) + nseq.
+inline int64_t chunk_slots(int64_t total_tokens, int32_t nseq) { return total_tokens / 16 + nseq; }
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *state, *o;
+    int32_t B, H, dk, dv;
+    bool bf16;
+    void *stream;
+};
+
+struct ChunkLocalArgs {
+    const void *q, *k, *g, *beta;
+    const int32_t *cu;
+    int32_t nseq, H, dk;
+    int64_t total_tokens;
+    bool bf16;
+    float *ws;
+    void *stream;
+};
+
+struct InterChunkArgs {
+    const void *q, *k, *v, *g;
+    const float *init;
+    const int32_t *cu;
+    int32_t nseq, H, dk, dv;
+    int64_t total_tokens;
+    bool bf16;
+    const float *ws;
+    float *o, *fin;
+    int32_t waves_per_group;  // 0 = choose automatically
+    void *stream;
+};
+
+hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_chunk_local(const ChunkLocalArgs &a);
+hipError_t launch_inter_chunk(const InterChunkArgs &a);
+
+}  // namespace kda

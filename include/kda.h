@@ -1,0 +1,153 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * The operator (Kimi K3 technical-report digest, discuss.pytorch.kr, section
+ * "Kimi Delta Attention", the per-head update equation):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * per head, with q_t, k_t in R^dk, v_t in R^dv, state S_t in R^{dk x dv},
+ * per-key-channel retention alpha_t = exp(log_alpha_t) in (0,1]^dk and scalar
+ * write strength beta_t in [0,1].  The state is fp32 and lives in a fixed
+ * dk x dv block per head (128 x 128 in the K3 layer).
+ *
+ * Input contract (not clamped in-kernel):
+ *   * -5 <= log_alpha <= 0.  The bounded-decay section of the same page fixes
+ *     the lower bound g_min = -5, which keeps the 16-token cumulative decay in
+ *     [-80, 0] so the chunked factors e^{+-G} stay inside fp32/bf16 range.
+ *     Values below -5 are out of contract (results may be Inf/NaN).
+ *   * beta in [0, 1].  k is expected L2-normalised by the caller (the page
+ *     normalises q and k before the recurrence); the operator applies no
+ *     1/sqrt(dk) scale to q.
+ *
+ * Layouts (row-major, contiguous, N = total_tokens = sum of sequence lengths):
+ *   q, k, log_alpha : [N, H, dk]      v : [N, H, dv]      beta : [N, H]
+ *   all five share one dtype: KDA_BF16 (bfloat16) or KDA_F32 (float).
+ *   cu_seqlens  : int32 [nseq + 1] in DEVICE memory, cu[0] = 0, non-decreasing,
+ *                 cu[nseq] = N (sequence s is tokens [cu[s], cu[s+1]); empty
+ *                 sequences are allowed).
+ *   init_state  : fp32 [nseq, H, dk, dv] or NULL (zero initial state).
+ *   o           : fp32 [N, H, dv].
+ *   final_state : fp32 [nseq, H, dk, dv] or NULL (not written).  It may alias
+ *                 init_state: each (sequence, head) block is read in full
+ *                 before it is written.
+ *   Decode: q, k, log_alpha [B, H, dk], v [B, H, dv], beta [B, H], state fp32
+ *   [B, H, dk, dv] updated in place (the in-place per-step state update that
+ *   the serving section names as the decode bottleneck), o fp32 [B, H, dv].
+ *
+ * Supported shapes: dk, dv in {16, 32, 64, 128} (any combination); H >= 1;
+ * nseq >= 1; total_tokens >= 0 (< 2^31).  Chunk length is fixed at 16 tokens.
+ *
+ * Ownership and synchronisation: every buffer is allocated by the caller; the
+ * library never allocates, frees or synchronises.  Pointers are device
+ * pointers unless stated otherwise.  Work is enqueued on `stream` (a
+ * hipStream_t; NULL = the default stream) and the call returns at once.
+ * Inputs are read-only; o / final_state must not alias the inputs (except the
+ * final_state == init_state case above).  Every device pointer must be 16-byte
+ * aligned.
+ *
+ * Errors: argument errors are detected on the host before any launch and
+ * returned as a status; nothing is launched then.  A failed launch returns
+ * KDA_ERR_HIP and kda_last_hip_error() gives the hipError_t (per thread).
+ * Faults inside a kernel surface at the caller's next synchronisation.  The
+ * library does not print, throw or abort.  Results are bitwise reproducible
+ * for a given shape on a given device (no atomics, fixed reduction order).
+ * Calls are reentrant; concurrent calls on different streams are safe as long
+ * as their output buffers (and workspaces) are distinct.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,         /* a required pointer is NULL */
+    KDA_ERR_ALIGN = 2,        /* a pointer is not 16-byte aligned */
+    KDA_ERR_SHAPE = 3,        /* nseq < 1, H < 1, B < 1, or total_tokens out of range */
+    KDA_ERR_UNSUPPORTED = 4,  /* dk / dv not in {16,32,64,128}, or unknown dtype */
+    KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kda_prefill_workspace_bytes */
+    KDA_ERR_HIP = 6           /* a kernel launch failed; see kda_last_hip_error() */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,              /* q, k, v, log_alpha, beta are float */
+    KDA_BF16 = 1              /* q, k, v, log_alpha, beta are bfloat16 */
+} kda_dtype;
+
+#define KDA_CHUNK 16
+#define KDA_GATE_LOWER_BOUND (-5.0f)
+
+/* Bytes of device workspace kda_prefill / kda_chunk_local / kda_inter_chunk
+ * need: per chunk slot and head, the 16x16 fp32 matrices T' = (I + A_kk)^-1
+ * diag(beta) and A_qk (2 KiB), for floor(N/16) + nseq chunk slots.  Returns 0
+ * for invalid arguments. */
+size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
+                                   int32_t dk, int32_t dv, kda_dtype dt);
+
+/* Chunkwise prefill over packed variable-length sequences: the chunk-local
+ * phase (kda_chunk_local) followed by the inter-chunk phase
+ * (kda_inter_chunk) on `stream`.  Computes o for every token and, if
+ * final_state != NULL, the state after each sequence's last token.
+ * (Chunked form: same page, "chunk-parallel form" paragraph and equation
+ * O_[t] = (Gamma (.) Q_[t]) S_[t] + A_[t] V~_[t].) */
+kda_status kda_prefill(const void *q, const void *k, const void *v,
+                       const void *log_alpha, const void *beta,
+                       const float *init_state, const int32_t *cu_seqlens,
+                       int32_t nseq, int64_t total_tokens, int32_t H,
+                       int32_t dk, int32_t dv, kda_dtype dt,
+                       float *o, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Phase 1 of kda_prefill, embarrassingly parallel over (chunk, head): the
+ * cumulative log-decay of each 16-token chunk, the strictly lower triangular
+ * beta-weighted decayed key block A_kk = diag(beta) tril_-1(K+ K-^T), its
+ * unit-lower-triangular inverse T = (I + A_kk)^-1 (stored as T diag(beta)),
+ * and the decayed query-key block A_qk = tril(Q+ K-^T).  Writes `workspace`.
+ * (Bounded-decay section: the -5 floor keeps e^{+-G} in range so the
+ * diagonal tiles are dense matrix products.) */
+kda_status kda_chunk_local(const void *q, const void *k, const void *log_alpha,
+                           const void *beta, const int32_t *cu_seqlens,
+                           int32_t nseq, int64_t total_tokens, int32_t H,
+                           int32_t dk, kda_dtype dt,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Phase 2 of kda_prefill: the sequential state propagation over the chunks
+ * of each sequence, per (sequence, head, 16-column slice of dv), with the
+ * fp32 state held on chip.  Reads the workspace written by kda_chunk_local
+ * for the same inputs.  (KDA systems section: the recurrence across chunks
+ * is the serial, head-parallel phase.) */
+kda_status kda_inter_chunk(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const float *init_state,
+                           const int32_t *cu_seqlens, int32_t nseq,
+                           int64_t total_tokens, int32_t H, int32_t dk,
+                           int32_t dv, kda_dtype dt, const void *workspace,
+                           size_t workspace_bytes, float *o,
+                           float *final_state, void *stream);
+
+/* One recurrent decode step for B x H heads: the state is read once and
+ * written once, in place.  (Per-token update equation; serving section:
+ * decode is bound by the in-place state update.) */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta,
+                           float *state, float *o, int32_t B, int32_t H,
+                           int32_t dk, int32_t dv, kda_dtype dt, void *stream);
+
+/* Static string naming a status code. */
+const char *kda_status_string(kda_status s);
+
+/* hipError_t (as int) of the most recent KDA_ERR_HIP on the calling thread,
+ * 0 if none. */
+int32_t kda_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -35,7 +35,7 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 
 def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
     """Compile the oracle with gcc into a shared library and return its path."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
+    cmd = ["gcc", "-O3", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
            *extra_flags, source, "-o", output + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(output + ".tmp", output)

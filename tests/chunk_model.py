@@ -1,0 +1,61 @@
+"""fp64 numpy model of the chunkwise (16-token) evaluation of the KDA recurrence.
+
+Test-only.  It is NOT the oracle: it models the algebra the HIP kernels implement
+so that the derivation can be checked against the oracle on the CPU, and so the
+chunk-local kernel's intermediates (T' = (I + A_kk)^-1 diag(beta) and A_qk) have
+something to be compared with.  Derivation, for a chunk of n <= 16 tokens with
+incoming state S (report digest, "Kimi Delta Attention": the chunked output is an
+inter-chunk term (Gamma (.) Q) S plus an intra-chunk term A V~):
+
+    G_r  = sum_{i<=r} g_i                        (per key channel)
+    K+   = K (.) e^{G},   K- = K (.) e^{-G},   Q+ = Q (.) e^{G},   K~ = K (.) e^{G_n - G}
+    A_kk = diag(beta) strictly_lower(K+ K-^T)     T' = (I + A_kk)^{-1} diag(beta)
+    W    = T' K+,   U = T' V,   A_qk = lower_incl_diag(Q+ K-^T)
+    Delta = U - W S
+    O     = Q+ S + A_qk Delta
+    S_out = Diag(e^{G_n}) S + K~^T Delta
+"""
+import numpy as np
+
+C = 16
+
+
+def chunk_local(q, k, g, beta):
+    """Per-chunk quantities for one head: q, k, g are [n, dk], beta [n].
+    Returns dict with G, Kp, Km, Qp, Kt, Tp (T'), Aqk."""
+    n = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    Kp, Km = k * np.exp(G), k * np.exp(-G)
+    Qp = q * np.exp(G)
+    Kt = k * np.exp(G[-1] - G)
+    A = np.diag(beta) @ np.tril(Kp @ Km.T, -1)
+    T = np.linalg.inv(np.eye(n) + A)
+    return dict(G=G, Kp=Kp, Km=Km, Qp=Qp, Kt=Kt, A=A, T=T, Tp=T @ np.diag(beta),
+                Aqk=np.tril(Qp @ Km.T))
+
+
+def prefill(q, k, v, g, beta, cu_seqlens=None, init_state=None, chunk=C, keep=False):
+    """Same interface as the oracle's prefill; optionally keeps per-chunk (Tp, Aqk)."""
+    q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.array([0, N]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    nseq = len(cu) - 1
+    o = np.zeros((N, H, dv))
+    fin = np.zeros((nseq, H, dk, dv))
+    kept = {}
+    for s in range(nseq):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if init_state is None else np.array(init_state[s, h], dtype=np.float64)
+            for c0 in range(cu[s], cu[s + 1], chunk):
+                c1 = min(cu[s + 1], c0 + chunk)
+                loc = chunk_local(q[c0:c1, h], k[c0:c1, h], g[c0:c1, h], beta[c0:c1, h])
+                W = loc["Tp"] @ loc["Kp"]
+                U = loc["Tp"] @ v[c0:c1, h]
+                D = U - W @ S
+                o[c0:c1, h] = loc["Qp"] @ S + loc["Aqk"] @ D
+                S = np.exp(loc["G"][-1])[:, None] * S + loc["Kt"].T @ D
+                if keep:
+                    kept[(s, h, (c0 - cu[s]) // chunk)] = loc
+            fin[s, h] = S
+    return (o, fin, kept) if keep else (o, fin)

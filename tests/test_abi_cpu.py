@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it builds for gfx950, loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments on the host before any launch.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_51_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIBRARY):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return kda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_library_is_built_for_gfx950_only():
+    blob = open(kda.LIBRARY, "rb").read()
+    assert b"gfx950" in blob
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in blob
+
+
+def test_status_strings(lib):
+    for code, name in kda.STATUS.items():
+        assert kda.kda_status_string(code).startswith(name)
+    assert "unknown" in kda.kda_status_string(99)
+
+
+def test_workspace_bytes(lib):
+    # floor(N/16) + nseq chunk slots, 2 KiB per slot and head
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 96, 128, 128) == (4096 + 1) * 96 * 2048
+    assert kda.kda_prefill_workspace_bytes(0, 3, 2, 16, 16) == 3 * 2 * 2048
+    assert kda.kda_prefill_workspace_bytes(64, 1, 1, 24, 16) == 0   # unsupported dk
+    assert kda.kda_prefill_workspace_bytes(64, 0, 1, 16, 16) == 0   # nseq < 1
+    assert kda.kda_prefill_workspace_bytes(-1, 1, 1, 16, 16) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, init=None, cu=FAKE, nseq=1, N=64, H=1, dk=16,
+             dv=16, dt=kda.KDA_BF16, o=FAKE, fin=None, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.kda_prefill(a["q"], a["k"], a["v"], a["g"], a["b"], a["init"], a["cu"], a["nseq"], a["N"],
+                           a["H"], a["dk"], a["dv"], a["dt"], a["o"], a["fin"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert _prefill(lib, q=None) == 1                 # KDA_ERR_NULL
+    assert _prefill(lib, o=None) == 1
+    assert _prefill(lib, cu=None) == 1
+    assert _prefill(lib, k=FAKE + 2) == 2             # KDA_ERR_ALIGN
+    assert _prefill(lib, init=FAKE + 8) == 2
+    assert _prefill(lib, nseq=0) == 3                 # KDA_ERR_SHAPE
+    assert _prefill(lib, H=0) == 3
+    assert _prefill(lib, N=-5) == 3
+    assert _prefill(lib, N=1 << 31) == 3
+    assert _prefill(lib, dk=24) == 4                  # KDA_ERR_UNSUPPORTED
+    assert _prefill(lib, dv=256) == 4
+    assert _prefill(lib, dt=7) == 4
+    assert _prefill(lib, wsb=100) == 5                # KDA_ERR_WORKSPACE
+    assert _prefill(lib, ws=None, wsb=1 << 20) == 5
+
+
+def test_phase_entry_points_reject_bad_arguments(lib):
+    f = lib.kda_chunk_local
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 16, 1, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 48, 1, FAKE, 1 << 20, None) == 4
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 16, 1, FAKE, 16, None) == 5
+    g = lib.kda_inter_chunk
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 64, 1, 16, 16, 1, FAKE, 16, FAKE, None, None) == 5
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 64, 1, 16, 16, 1, FAKE, 1 << 20, None, None, None) == 1
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 64, 0, 16, 16, 1, FAKE, 1 << 20, FAKE, None, None) == 3
+
+
+def test_decode_rejects_bad_arguments(lib):
+    f = lib.kda_decode_step
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 16, 16, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 1, 1, 16, 16, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 16, 16, 1, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 80, 1, None) == 4
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    x = torch.zeros((16, 1, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_prefill(x, x, x, x, torch.zeros((16, 1), dtype=torch.bfloat16))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        kda.load_library(str(tmp_path / "absent.so"))

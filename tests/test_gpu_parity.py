@@ -1,0 +1,276 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Bar: max|x - ref| <= tol * RMS(ref) per output tensor, tol = 1e-2 for bf16 inputs with
+fp32 state, 1e-5 for fp32 inputs.  Inputs are seeded and synthetic (workloads module),
+generated on the GPU and copied to the host for the oracle.  Full-size workloads are
+run in full on the GPU and checked on a sample of heads the oracle recomputes exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunk_model
+import gated_delta_rule_51_amd as kda
+import oracle
+import workloads
+from parity import TOL, assert_close, oracle_prefill, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    kda.load_library()
+    return torch.device("cuda:0")
+
+
+def _prefill_case(dev, seqlens, H, dk, dv, dtype, seed=0, gate="neg_softplus", init=False,
+                  heads=None, edit=None):
+    w = workloads.custom(seqlens, H, dk, dv, dtype, gate)
+    x = workloads.prefill_inputs(w, device=dev, seed=seed)
+    if edit is not None:
+        edit(x)
+    init_state = workloads.random_state(len(seqlens), H, dk, dv, device=dev, seed=seed) if init else None
+    say(f"  case: seqlens={list(seqlens)[:8]}{'...' if len(seqlens) > 8 else ''} N={w.total_tokens} "
+        f"H={H} dk={dk} dv={dv} {dtype} init={init}")
+    o, fin = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], init_state)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x, init_state, heads=heads)
+    if heads is not None:
+        o, fin = o[:, heads], fin[:, heads]
+    tol = TOL[dtype]
+    assert_close(o, o_ref, tol, "o")
+    assert_close(fin, f_ref, tol, "final_state")
+    return x, o, fin
+
+
+# ----------------------------------------------------------------- chunk-local phase
+
+@pytest.mark.parametrize("dtype,dk", [(torch.float32, 16), (torch.float32, 128),
+                                      (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_chunk_local_matches_chunked_model(dev, dtype, dk):
+    """Kernel 1's T' = (I + A_kk)^-1 diag(beta) and A_qk for every chunk against the fp64
+    chunked-form model on the same (rounded) inputs."""
+    seqlens, H = [40, 16, 7], 2
+    w = workloads.custom(seqlens, H, dk, 16, dtype)
+    x = workloads.prefill_inputs(w, device=dev, seed=3)
+    say(f"  case: chunk_local dk={dk} {dtype}")
+    nseq = len(seqlens)
+    ws = kda.alloc_workspace(w.total_tokens, nseq, H, dk, 16, dtype, dev)
+    ws.fill_(float("nan"))
+    kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+    torch.cuda.synchronize()
+    wsn = ws.cpu().double().numpy().reshape(-1, H, 2, 16, 16)
+    cpu = {n: x[n].cpu().double().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
+    _, _, kept = chunk_model.prefill(cpu["q"], cpu["k"], cpu["v"], cpu["log_alpha"], cpu["beta"],
+                                     cu_seqlens=workloads.cu_seqlens_of(seqlens), keep=True)
+    cu = workloads.cu_seqlens_of(seqlens)
+    tol_t = 1e-5 if dtype == torch.float32 else 2e-2
+    tol_a = 1e-5 if dtype == torch.float32 else 1e-3
+    for (s, h, j), loc in kept.items():
+        slot = cu[s] // 16 + s + j
+        n = loc["Tp"].shape[0]
+        Tp = np.zeros((16, 16))
+        Tp[:n, :n] = loc["Tp"]
+        Aq = np.zeros((16, 16))
+        Aq[:n, :n] = loc["Aqk"]
+        gT, gA = wsn[slot, h, 0], wsn[slot, h, 1]
+        eT = np.max(np.abs(gT - Tp)) / np.max(np.abs(Tp))
+        eA = np.max(np.abs(gA - Aq)) / np.max(np.abs(Aq))
+        assert eT <= tol_t and eA <= tol_a, f"chunk (s={s},h={h},j={j}): T' err {eT:.2e}, A_qk err {eA:.2e}"
+
+
+# ----------------------------------------------------------------- the five workloads
+
+def test_workload1_tiny_fp32_prefill(dev):
+    w = workloads.workload(1)
+    _prefill_case(dev, w.seqlens, w.H, w.dk, w.dv, w.dtype, gate=w.gate)
+
+
+def test_workload1_tiny_fp32_decode(dev):
+    """The tiny workload stepped token by token through the decode kernel."""
+    w = workloads.workload(1)
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    T = w.total_tokens
+    state = torch.zeros((1, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    outs = []
+    for t in range(T):
+        outs.append(kda.kda_decode_step(*(x[n][t:t + 1].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                        state).clone())
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x)
+    assert_close(torch.cat(outs), o_ref, TOL[torch.float32], "decode o (64 steps)")
+    assert_close(state, f_ref, TOL[torch.float32], "decode state")
+
+
+def test_workload2_batched_prefill(dev):
+    w = workloads.workload(2)
+    _prefill_case(dev, w.seqlens, w.H, w.dk, w.dv, w.dtype)
+
+
+def test_workload3_k3_layer_sampled_heads(dev):
+    """B=1, H=96, T=65,536: full run on the GPU, oracle on 4 heads."""
+    w = workloads.workload(3)
+    heads = [0, 31, 64, 95]
+    _prefill_case(dev, w.seqlens, w.H, w.dk, w.dv, w.dtype, heads=heads)
+    torch.cuda.empty_cache()
+
+
+def test_workload4_decode_sampled_heads(dev):
+    """B=256 x H=96, 128 steps from a unit-Frobenius random state; oracle on 48 sampled heads."""
+    w = workloads.workload(4)
+    B, H = w.nseq, w.H
+    state = workloads.decode_initial_state(B, H, w.dk, w.dv, device=dev)
+    rng = np.random.default_rng(0)
+    bi = torch.tensor(rng.integers(0, B, 48), device=dev)
+    hi = torch.tensor(rng.integers(0, H, 48), device=dev)
+    ref_state = state[bi, hi].unsqueeze(0).cpu().double().numpy()  # [1, 48, dk, dv]
+    o_gpu, o_ref = [], []
+    say(f"  case: decode B={B} H={H} steps={w.decode_steps}")
+    for step in range(w.decode_steps):
+        x = workloads.decode_step_inputs(w, step, device=dev)
+        o = kda.kda_decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state)
+        o_gpu.append(o[bi, hi].cpu())
+        sub = [x[n][bi, hi].unsqueeze(0).cpu() for n in ("q", "k", "v", "log_alpha", "beta")]
+        orf, ref_state = oracle.decode(*sub, ref_state)
+        o_ref.append(orf[0])
+    torch.cuda.synchronize()
+    assert_close(torch.stack(o_gpu), np.stack(o_ref), TOL[torch.bfloat16], "decode o (128 steps)")
+    assert_close(state[bi, hi], ref_state[0], TOL[torch.bfloat16], "decode state after 128 steps")
+    del state
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_workload5_varlen_1m_sampled_head(dev):
+    """1,048,576 packed tokens in ~27 log-uniform sequences, H=96: full run, oracle on 1 head."""
+    w = workloads.workload(5)
+    _prefill_case(dev, w.seqlens, w.H, w.dk, w.dv, w.dtype, heads=[17])
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (16, 128), (128, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged_lengths_and_shapes(dev, dk, dv, dtype):
+    """Empty, single-token, exact-chunk and ragged sequences, with an initial state."""
+    _prefill_case(dev, [17, 0, 1, 33, 100, 16, 15], 3, dk, dv, dtype, seed=dk + dv, init=True)
+
+
+def test_zero_tokens(dev):
+    """N = 0: every final state equals its initial state."""
+    H, d = 2, 64
+    z = torch.empty((0, H, d), dtype=torch.bfloat16, device=dev)
+    zb = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    init = workloads.random_state(2, H, d, d, device=dev)
+    o, fin = kda.kda_prefill(z, z, z, z, zb, cu, init)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, d) and torch.equal(fin, init)
+
+
+def test_gate_and_beta_extremes(dev):
+    """g at the -5 floor and at 0, beta exactly 0 and 1."""
+    def edit(x):
+        g, b = x["log_alpha"], x["beta"]
+        g[0::3] = -5.0
+        g[1::5] = 0.0
+        b[0::4] = 0.0
+        b[1::4] = 1.0
+    _prefill_case(dev, [64, 37], 4, 128, 128, torch.bfloat16, seed=9, init=True, edit=edit)
+    _prefill_case(dev, [64, 37], 2, 32, 32, torch.float32, seed=9, gate="uniform", init=True, edit=edit)
+
+
+def test_final_state_may_alias_initial_state(dev):
+    w = workloads.custom([50, 20], 2, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=4)
+    init = workloads.random_state(2, 2, 128, 128, device=dev, seed=4)
+    o1, f1 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], init.clone())
+    buf = init.clone()
+    o2, f2 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], buf,
+                             final_state=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, buf)
+
+
+# ----------------------------------------------------------------- cross-path invariants
+
+def test_decode_steps_match_prefill(dev):
+    """T decode steps and one prefill of T tokens agree (both also against the oracle)."""
+    w = workloads.custom([45], 3, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=5)
+    init = workloads.random_state(1, 3, 128, 128, device=dev, seed=5)
+    o_p, f_p = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], init)
+    state = init.clone()
+    outs = [kda.kda_decode_step(*(x[n][t:t + 1].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                state) for t in range(45)]
+    torch.cuda.synchronize()
+    o_d = torch.cat(outs)
+    o_ref, f_ref = oracle_prefill(x, init)
+    assert_close(o_d, o_ref, TOL[torch.bfloat16], "decode o")
+    assert_close(state, f_ref, TOL[torch.bfloat16], "decode state")
+    assert_close(o_d, o_p.double().cpu().numpy(), TOL[torch.bfloat16], "decode vs prefill o")
+
+
+def test_split_prefill_resumes_exactly(dev):
+    """prefill(0:t1) then prefill(t1:T, init = final_1) against prefill(0:T) and the oracle."""
+    w = workloads.custom([300], 2, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=6)
+    o, f = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"])
+    parts = []
+    state = None
+    for a, b in ((0, 123), (123, 300)):
+        sl = [x[n][a:b].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+        op, state = kda.kda_prefill(*sl, None, state)
+        parts.append(op)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x)
+    assert_close(torch.cat(parts), o_ref, TOL[torch.bfloat16], "split o")
+    assert_close(state, f_ref, TOL[torch.bfloat16], "split final state")
+    assert rel_err(torch.cat(parts), o.double().cpu().numpy()) <= TOL[torch.bfloat16]
+
+
+def test_varlen_packing_equals_separate_calls(dev):
+    seqlens = [70, 5, 33]
+    w = workloads.custom(seqlens, 2, 64, 64, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=7)
+    o, f = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    cu = workloads.cu_seqlens_of(seqlens)
+    for s in range(len(seqlens)):
+        sl = [x[n][cu[s]:cu[s + 1]].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+        os_, fs = kda.kda_prefill(*sl)
+        torch.cuda.synchronize()
+        # chunk boundaries are aligned to each sequence's start in both calls: identical arithmetic
+        assert torch.equal(os_, o[cu[s]:cu[s + 1]]) and torch.equal(fs[0], f[s])
+
+
+def test_bitwise_deterministic(dev):
+    w = workloads.custom([200, 77], 4, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=8)
+    r1 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    r2 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    st = workloads.random_state(4, 8, 128, 128, device=dev)
+    st1, st2 = st.clone(), st.clone()
+    d = workloads.decode_step_inputs(workloads.custom([1] * 4, 8, 128, 128), 0, device=dev)
+    o1 = kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], st1)
+    o2 = kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], st2)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+
+
+def test_waves_per_group_variants_agree(dev, monkeypatch):
+    """The 2-, 4- and 8-wave workgroup shapes of the inter-chunk kernel give the same bits."""
+    w = workloads.custom([130, 64], 3, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=10)
+    outs = []
+    for nw in ("2", "4", "8"):
+        monkeypatch.setenv("KDA_WAVES", nw)
+        outs.append(kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"]))
+    torch.cuda.synchronize()
+    for o, f in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(f, outs[0][1])
+    o_ref, f_ref = oracle_prefill(x)
+    assert_close(outs[0][0], o_ref, TOL[torch.bfloat16], "o")
