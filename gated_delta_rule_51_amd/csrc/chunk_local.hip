@@ -8,7 +8,8 @@
 //     A_kk = diag(beta) * strictly_lower(K+ K-^T)      (16 x 16)
 //     T    = (I + A_kk)^{-1}                            (unit lower triangular)
 //     A_qk = lower_incl_diag(Q+ K-^T)                   (16 x 16)
-// This kernel writes T' = T diag(beta) and A_qk to the workspace.  The
+// This kernel writes T' = T diag(beta) and A_qk to the workspace, as MFMA
+// A-operand fragments (split bf16 for bf16 inputs, fp32 for fp32 inputs).  The
 // pseudo-keys W = T' K+ and pseudo-values U = T' V are applied by the
 // inter-chunk phase in the factored form Delta = T' (V - K+ S) = U - W S.
 //
@@ -70,8 +71,13 @@ __global__ __launch_bounds__(64) void chunk_local_kernel(
         float p = 1.f, pi = 1.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p *= decay_exp(gv[r]);
-            pi *= decay_exp(-gv[r]);
+            if constexpr (F32) {
+                p *= decay_exp(gv[r]);
+                pi *= decay_exp(-gv[r]);
+            } else {
+                p *= decay_exp_fast(gv[r]);
+                pi *= decay_exp_fast(-gv[r]);
+            }
             sP[r][c] = p;
             sPi[r][c] = pi;
         }
@@ -127,21 +133,21 @@ __global__ __launch_bounds__(64) void chunk_local_kernel(
     }
 
     // Accumulator lane (g4, i) holds rows r = 4*g4 + jj of column i.
-    float *wsT = ws + (slot * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
-    float *wsA = wsT + 256;
+    __shared__ float sAq[16][17];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int r = 4 * g4 + jj, i = m;
         sA[r][i] = (r > i) ? sBeta[r] * akk[jj] : 0.f;
-        wsA[r * 16 + i] = (r >= i) ? aqk[jj] : 0.f;
+        sAq[r][i] = (r >= i) ? aqk[jj] : 0.f;
     }
     __syncthreads();
 
     // T = (I + A_kk)^{-1} by forward substitution; lane c builds column c:
     // T[r][c] = [r == c] - sum_{i < r} A[r][i] T[i][c]  (T[i][c] = 0 for i < c).
+    // T' = T diag(beta) overwrites A_kk in LDS (every lane has read it by then).
+    float t[16];
     if (lane < 16) {
         const int c = lane;
-        float t[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = 0.f;
@@ -149,9 +155,28 @@ __global__ __launch_bounds__(64) void chunk_local_kernel(
             for (int i = 0; i < r; ++i) acc += sA[r][i] * t[i];
             t[r] = ((r == c) ? 1.f : 0.f) - acc;
         }
-        const float bc = sBeta[c];
+    }
+    __syncthreads();
+    if (lane < 16) {
+        const float bc = sBeta[lane];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wsT[r * 16 + c] = t[r] * bc;
+        for (int r = 0; r < 16; ++r) sA[r][lane] = t[r] * bc;
+    }
+    __syncthreads();
+
+    // Store T' and A_qk as A-operand fragments of the 16x16 MFMA: lane (g4, m)
+    // holds M[m][4*g4 + 0..3] -- split {hi, lo} bf16 for bf16 inputs, fp32 for
+    // fp32 inputs -- so the inter-chunk phase loads them with one 16-byte read
+    // per lane.
+    const f32x4 tv = {sA[m][4 * g4], sA[m][4 * g4 + 1], sA[m][4 * g4 + 2], sA[m][4 * g4 + 3]};
+    const f32x4 av = {sAq[m][4 * g4], sAq[m][4 * g4 + 1], sAq[m][4 * g4 + 2], sAq[m][4 * g4 + 3]};
+    float *w = ws + (slot * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
+    if constexpr (F32) {
+        reinterpret_cast<f32x4 *>(w)[lane] = tv;
+        reinterpret_cast<f32x4 *>(w + 256)[lane] = av;
+    } else {
+        reinterpret_cast<Split4 *>(w)[lane] = split4(tv);
+        reinterpret_cast<Split4 *>(w + 256)[lane] = split4(av);
     }
 }
 

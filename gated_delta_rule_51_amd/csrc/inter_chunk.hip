@@ -16,12 +16,16 @@
 // 16-column slice of dv and keeps its 16 x dk x fp32 state slice in registers
 // for the whole sequence.  A workgroup of NW waves covers NW slices of one
 // (sequence, head) and shares the chunk-dependent operands through LDS:
-//   * prep1 (one thread per key channel): e^{g}, running prefix/suffix
-//     products, Gamma, K~ fragments; T' and A_qk fragments from the workspace;
-//   * prep2 (one thread per (token, 4 channels)): Q+ and K+ fragments.
+//   * prep1: per key channel, one "prefix" job (e^{G_r}, Gamma) and one
+//     "suffix" job (K~ = K (.) e^{G_15 - G_r}), spread over all threads; T' and
+//     A_qk fragments from the workspace;
+//   * prep2 (one item per (token, 4 channels)): Q+ and K+ fragments.
 // The prep of chunk c+1 runs while the waves advance the state through chunk
 // c (double-buffered LDS, two barriers per chunk), and the raw inputs of
-// chunk c+2 are loaded into registers meanwhile.  This overlaps the
+// chunk c+2 are loaded into registers meanwhile.  Inputs are read through
+// buffer resources whose base is the chunk's first token (uniform, in SGPRs):
+// per-lane offsets stay constant from chunk to chunk, and the rows of a ragged
+// last chunk are parked out of bounds so the hardware returns zeros.  This overlaps the
 // token-parallel work with the serial recurrence, as the page's KDA systems
 // section describes for its own chunkwise kernel.
 //
@@ -40,36 +44,60 @@ namespace kda {
 template <int DK, int DV, typename T, int NW>
 struct IC {
     static constexpr bool F32 = sizeof(T) == 4;
+    static constexpr uint32_t EB = sizeof(T);               // input element bytes
     static constexpr int NT = 64 * NW;
-    static constexpr int NB = DK / 16;
-    static constexpr int CPT = (DK + NT - 1) / NT;        // channels per thread (prep1)
-    static constexpr int IPT = (4 * DK + NT - 1) / NT;    // (token, quad) items per thread (prep2)
-    static constexpr int EPT = (256 + NT - 1) / NT;       // T' / A_qk elements per thread
-    using OpT = std::conditional_t<F32, f32x4, Split4>;   // split operand fragment
-    using KpT = std::conditional_t<F32, f32x4, bf16x4>;   // single operand fragment
+    static constexpr int NB = DK / 16;                       // 16-channel key blocks
+    static constexpr int NPAIR = (NB + 1) / 2;               // block pairs (one K=32 MFMA each)
+    static constexpr int UNITS = 4 * DK;                     // (token, 4-channel group) units of a chunk tile
+    static constexpr int UPT = (UNITS + NT - 1) / NT;
+    // prep1 splits each key channel's 16 tokens into NPART parts (1, 2 or 4) held
+    // by lanes of one wave, CPW channels per wave, TP tokens per part; with fewer
+    // threads than channels each thread takes CPT channels.
+    static constexpr int NPART = (NT / DK) >= 4 ? 4 : ((NT / DK) >= 2 ? 2 : 1);
+    static constexpr int CPW = 64 / NPART;
+    static constexpr int TP = 16 / NPART;
+    static constexpr int CPT = DK > NT ? DK / NT : 1;
+    static constexpr bool PREP1_FULL = NW * CPW * CPT == DK;   // every thread owns a real channel
+    static constexpr bool UNITS_FULL = (UNITS % NT) == 0;
+    static constexpr int VW = 16 * NW;                       // v columns of this workgroup
+    static constexpr int MU = 2 * 16 * 16 * 4 / 8;           // T' + A_qk fragments in 8-byte units (256)
+    static constexpr int MPT = (MU + NT - 1) / NT;
+    static constexpr int LDT = DK + (F32 ? 4 : 8);           // padded stage row (elements)
+    using OpT = std::conditional_t<F32, f32x4, Split4>;     // split operand fragment (K~, T', A_qk)
+    using Raw4 = std::conditional_t<F32, u32x4, u32x2>;     // four raw input elements
 };
 
-template <int DK, int DV, typename T, int NW>
-struct Raw {
-    using C = IC<DK, DV, T, NW>;
-    float g[C::CPT][16];
-    float k[C::CPT][16];
-    f32x4 q4[C::IPT];
-    f32x4 k4[C::IPT];
-    float tp[C::EPT];
-    float aq[C::EPT];
+// LDS operand set of one chunk.
+//   qp_hi/qp_lo[p][lane]: Q+ for block pair p in the A-fragment layout, the two
+//     blocks' four-element halves packed back to back (one K=32 MFMA operand);
+//   kp[p][lane]: K+ (single bf16), same packing;
+//   kt[b][lane]: K~ for block b in the K-side layout, {hi, lo};
+//   gam: e^{G_n} per channel.
+// (T' and A_qk arrive from the chunk-local phase already in fragment form and
+// are loaded by each wave straight into registers.)
+template <int DK, typename T>
+struct OpsBF16 {
+    static constexpr int NB = DK / 16, NPAIR = (NB + 1) / 2;
+    bf16x8 qp_hi[NPAIR][64];
+    bf16x8 qp_lo[NPAIR][64];
+    bf16x8 kp[NPAIR][64];
+    Split4 kt[NB][64];
+    float gam[DK];
+};
+
+template <int DK, typename T>
+struct OpsF32 {
+    static constexpr int NB = DK / 16;
+    f32x4 qp[NB][64];
+    f32x4 kp[NB][64];
+    f32x4 kt[NB][64];
+    float gam[DK];
 };
 
 template <typename O>
 __device__ __forceinline__ O make_op(f32x4 x) {
     if constexpr (std::is_same_v<O, f32x4>) return x;
     else return split4(x);
-}
-
-template <typename O>
-__device__ __forceinline__ O make_kp(f32x4 x) {
-    if constexpr (std::is_same_v<O, f32x4>) return x;
-    else return to_bf16x4(x);
 }
 
 template <typename O>
@@ -83,16 +111,35 @@ __device__ __forceinline__ void set_op_elem(O &dst, int slot, float x) {
     }
 }
 
+template <bool F32>
+__device__ __forceinline__ float gate_exp(float x) {
+    if constexpr (F32) return decay_exp(x);
+    else return decay_exp_fast(x);
+}
+
+// Split a pair of state tiles into pair-packed bf16 operands.
+__device__ __forceinline__ void split_pair(const f32x4 &a, const f32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+    const bf16x4 ah = to_bf16x4(a), bh = to_bf16x4(b);
+    const bf16x4 al = to_bf16x4(a - from_bf16x4(ah)), bl = to_bf16x4(b - from_bf16x4(bh));
+    hi = cat(ah, bh);
+    lo = cat(al, bl);
+}
+
 template <int DK, int DV, typename T, int NW>
-__global__ __launch_bounds__(64 * NW) void inter_chunk_kernel(
+__global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
     int32_t nseq, int32_t H, const float *__restrict__ ws, float *__restrict__ o,
     float *__restrict__ fin, int32_t nsplit, int32_t nchains) {
     using C = IC<DK, DV, T, NW>;
     using OpT = typename C::OpT;
-    using KpT = typename C::KpT;
-    constexpr int NT = C::NT, NB = C::NB, CPT = C::CPT, IPT = C::IPT, EPT = C::EPT;
+    using Raw4 = typename C::Raw4;
+    using Ops = std::conditional_t<C::F32, OpsF32<DK, T>, OpsBF16<DK, T>>;
+    constexpr bool F32 = C::F32;
+    constexpr uint32_t EB = C::EB;
+    constexpr int NT = C::NT, NB = C::NB, NPAIR = C::NPAIR, UPT = C::UPT;
+    constexpr int NPART = C::NPART, CPW = C::CPW, TP = C::TP, CPT = C::CPT;
+    constexpr int LDT = C::LDT;
 
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by
     // linear id, so all slices of one (sequence, head) get the same id mod 8
@@ -110,18 +157,23 @@ __global__ __launch_bounds__(64 * NW) void inter_chunk_kernel(
     const int g4 = lane >> 4, n16 = lane & 15;
     const int col0 = (split * NW + wave) * 16;
 
-    __shared__ OpT sQp[2][NB][64];
-    __shared__ KpT sKp[2][NB][64];
-    __shared__ OpT sKt[2][NB][64];
-    __shared__ OpT sTp[2][64];
-    __shared__ OpT sAq[2][64];
-    __shared__ float sGam[2][DK];
-    __shared__ float sP[16][DK + 4];
+    constexpr int VW = C::VW, MPT = C::MPT;
+    // (vector loads/stores of 8 and 16 bytes address these arrays: 16-byte aligned)
+    __shared__ __attribute__((aligned(16))) Ops ops[2];
+    __shared__ __attribute__((aligned(16))) T stq[2][16][LDT];   // raw chunk tiles, token-major
+    __shared__ __attribute__((aligned(16))) T stk[2][16][LDT];
+    __shared__ __attribute__((aligned(16))) T stg[2][16][LDT];
+    __shared__ __attribute__((aligned(16))) T stv[2][16][VW + 4];         // this workgroup's v columns
+    __shared__ __attribute__((aligned(16))) uint32_t stm[2][2 * 16 * 16]; // T', A_qk fragments (workspace copy)
+    __shared__ __attribute__((aligned(16))) float sP[16][DK + 4];
 
     const int64_t bos = cu[s], eos = cu[s + 1];
     const int nc = (int)((eos - bos + 15) / 16);
     const int64_t slot0 = bos / 16 + s;
     const int64_t hd = (int64_t)s * H + h;
+    const uint32_t rowK = (uint32_t)H * DK * EB;   // bytes between tokens in q, k, g
+    const uint32_t rowV = (uint32_t)H * DV * EB;   // ... in v
+    const uint32_t rowO = (uint32_t)H * DV * 4;    // ... in o
 
     // ---- state slice: rows 16b + 4*g4 + jj, column col0 + n16 (frag4 layout)
     f32x4 S[NB];
@@ -135,196 +187,297 @@ __global__ __launch_bounds__(64 * NW) void inter_chunk_kernel(
         const int64_t left = eos - (bos + 16 * (int64_t)c);
         return left < 16 ? (int)left : 16;
     };
-
-    // Loads are unconditional (addresses clamped to a valid token row / channel,
-    // padding zeroed by a select afterwards) so the compiler issues them back to
-    // back instead of branching and waiting on each one.  A chunk that exists has
-    // n >= 1 tokens, so row t0 + min(t, n-1) is always inside the sequence.
-    auto load_raw = [&](Raw<DK, DV, T, NW> &R, int c) {
+    // Buffer resource of chunk c for this head: base = the head's slice of the
+    // chunk's first token.  Rows at or past the chunk length are parked at an
+    // out-of-bounds offset, so their loads return zeros and stores are dropped.
+    auto rsrc_in = [&](const T *base, int c, int d) {
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(c);
-#pragma unroll
-        for (int ci = 0; ci < CPT; ++ci) {
-            const int ch = tid + ci * NT;
-            const int chc = ch < DK ? ch : DK - 1;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool ok = ch < DK && r < n;
-                const int rr = r < n ? r : n - 1;
-                const int64_t off = ((t0 + rr) * H + h) * DK + chc;
-                const float gv = load_in(g + off);
-                const float kv = load_in(k + off);
-                R.g[ci][r] = ok ? gv : 0.f;
-                R.k[ci][r] = ok ? kv : 0.f;
-            }
-        }
-#pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) {
-            const int item = tid + ii * NT;
-            const int itc = item < 4 * DK ? item : 4 * DK - 1;
-            const int t = itc / (DK / 4), a = itc % (DK / 4);
-            const bool ok = item < 4 * DK && t < n;
-            const int tt = t < n ? t : n - 1;
-            const int64_t off = ((t0 + tt) * H + h) * DK + 4 * a;
-            const f32x4 qv = load_in4(q + off);
-            const f32x4 kv = load_in4(k + off);
-            R.q4[ii] = ok ? qv : zero4();
-            R.k4[ii] = ok ? kv : zero4();
-        }
-        const float *w = ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
-#pragma unroll
-        for (int ei = 0; ei < EPT; ++ei) {
-            const int e = (NT - 1 - tid) + ei * NT;
-            const int ec = e < 256 ? e : 255;
-            const float tv = w[ec], av = w[256 + ec];
-            R.tp[ei] = e < 256 ? tv : 0.f;
-            R.aq[ei] = e < 256 ? av : 0.f;
-        }
+        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB);
     };
+    // Look-ahead loads past the last chunk re-read the last chunk (results unused).
+    auto clampc = [&](int c) { return c < nc ? c : nc - 1; };
 
-    auto prep1 = [&](const Raw<DK, DV, T, NW> &R, int buf) {
-#pragma unroll
-        for (int ci = 0; ci < CPT; ++ci) {
-            const int ch = tid + ci * NT;
-            if (ch < DK) {
-                float a[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] = decay_exp(R.g[ci][r]);
-                float p = 1.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p *= a[r];
-                    sP[r][ch] = p;
-                }
-                sGam[buf][ch] = p;
-                float kt[16];
-                float f = 1.f;  // product of alpha over tokens after r
-#pragma unroll
-                for (int r = 15; r >= 0; --r) {
-                    kt[r] = R.k[ci][r] * f;
-                    f *= a[r];
-                }
-#pragma unroll
-                for (int tq = 0; tq < 4; ++tq)
-                    sKt[buf][ch >> 4][tq * 16 + (ch & 15)] =
-                        make_op<OpT>(f32x4{kt[4 * tq], kt[4 * tq + 1], kt[4 * tq + 2], kt[4 * tq + 3]});
-            }
-        }
-#pragma unroll
-        for (int ei = 0; ei < EPT; ++ei) {
-            const int e = (NT - 1 - tid) + ei * NT;
-            if (e < 256) {
-                const int r = e >> 4, col = e & 15;
-                const int ln = (col >> 2) * 16 + r;
-                set_op_elem(sTp[buf][ln], col & 3, R.tp[ei]);
-                set_op_elem(sAq[buf][ln], col & 3, R.aq[ei]);
-            }
-        }
+    // ---- raw loads of one chunk, all issued together three chunks ahead and
+    // parked in the LDS stage one chunk ahead:
+    //   q, k, g tiles: unit u = (token u / (DK/4), channels 4 (u % (DK/4)) .. +3);
+    //   v: unit = (token, 4 of this workgroup's columns) -- one per thread;
+    //   T' and A_qk fragments: 2 KiB copied in 8-byte units.
+    struct Units {
+        Raw4 q[UPT], k[UPT], g[UPT];
+        Raw4 v;
+        u32x2 m[MPT];
     };
-
-    auto prep2 = [&](const Raw<DK, DV, T, NW> &R, int buf) {
-#pragma unroll
-        for (int ii = 0; ii < IPT; ++ii) {
-            const int item = tid + ii * NT;
-            if (item < 4 * DK) {
-                const int t = item / (DK / 4), a = item % (DK / 4);
-                const int c = 4 * a;
-                const f32x4 P = *reinterpret_cast<const f32x4 *>(&sP[t][c]);
-                const int ln = ((c & 15) >> 2) * 16 + t;
-                sQp[buf][c >> 4][ln] = make_op<OpT>(R.q4[ii] * P);
-                sKp[buf][c >> 4][ln] = make_kp<KpT>(R.k4[ii] * P);
-            }
-        }
-    };
-
-    auto load_v = [&](int c) -> f32x4 {
-        const int64_t t0 = bos + 16 * (int64_t)c;
+    auto load_units = [&](Units &U, int c) {
         const int n = chunk_len(c);
+        const rsrc_t rq = rsrc_in(q, c, DK), rk = rsrc_in(k, c, DK), rg = rsrc_in(g, c, DK);
+#pragma unroll
+        for (int ui = 0; ui < UPT; ++ui) {
+            const int u = tid + ui * NT;
+            const int t = u / (DK / 4), a = u % (DK / 4);
+            const uint32_t off = (u < C::UNITS && t < n) ? t * rowK + 4 * a * EB : OOB;
+            if constexpr (F32) {
+                U.q[ui] = buf_load_u32x4(rq, off);
+                U.k[ui] = buf_load_u32x4(rk, off);
+                U.g[ui] = buf_load_u32x4(rg, off);
+            } else {
+                U.q[ui] = buf_load_u32x2(rq, off);
+                U.k[ui] = buf_load_u32x2(rk, off);
+                U.g[ui] = buf_load_u32x2(rg, off);
+            }
+        }
+        {
+            const rsrc_t rv = rsrc_in(v, c, DV);
+            const int t = tid / (VW / 4), a = tid % (VW / 4);
+            const uint32_t off = t < n ? t * rowV + (split * VW + 4 * a) * EB : OOB;
+            if constexpr (F32) U.v = buf_load_u32x4(rv, off);
+            else U.v = buf_load_u32x2(rv, off);
+        }
+        const u32x2 *w = reinterpret_cast<const u32x2 *>(ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD);
+#pragma unroll
+        for (int mi = 0; mi < MPT; ++mi) {
+            const int e = tid + mi * NT;
+            U.m[mi] = w[e < C::MU ? e : C::MU - 1];
+        }
+    };
+    auto store_units = [&](const Units &U, int sb) {
+#pragma unroll
+        for (int ui = 0; ui < UPT; ++ui) {
+            const int u = tid + ui * NT;
+            if (C::UNITS_FULL || u < C::UNITS) {
+                const int t = u / (DK / 4), a = u % (DK / 4);
+                *reinterpret_cast<Raw4 *>(&stq[sb][t][4 * a]) = U.q[ui];
+                *reinterpret_cast<Raw4 *>(&stk[sb][t][4 * a]) = U.k[ui];
+                *reinterpret_cast<Raw4 *>(&stg[sb][t][4 * a]) = U.g[ui];
+            }
+        }
+        {
+            const int t = tid / (VW / 4), a = tid % (VW / 4);
+            *reinterpret_cast<Raw4 *>(&stv[sb][t][4 * a]) = U.v;
+        }
+#pragma unroll
+        for (int mi = 0; mi < MPT; ++mi) {
+            const int e = tid + mi * NT;
+            if (e < C::MU) *reinterpret_cast<u32x2 *>(&stm[sb][2 * e]) = U.m[mi];
+        }
+    };
+
+    // ---- per-wave operands of the chunk in stage buffer sb: T' and A_qk
+    // fragments, and the v fragment (rows 4*g4 + jj, column col0 + n16).
+    struct Frags {
+        OpT tp, aq;
+    };
+    auto stage_frags = [&](int sb) {
+        Frags F;
+        F.tp = reinterpret_cast<const OpT *>(&stm[sb][0])[lane];
+        F.aq = reinterpret_cast<const OpT *>(&stm[sb][0])[64 + lane];
+        return F;
+    };
+    auto stage_v = [&](int sb) {
         f32x4 r;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int t = 4 * g4 + jj;
-            const int tt = t < n ? t : n - 1;
-            const float x = load_in(v + ((t0 + tt) * H + h) * DV + col0 + n16);
-            r[jj] = t < n ? x : 0.f;
-        }
+        for (int jj = 0; jj < 4; ++jj) r[jj] = load_in(&stv[sb][4 * g4 + jj][wave * 16 + n16]);
         return r;
     };
 
-    // One chunk of the recurrence for this wave's 16 columns.
-    auto advance = [&](int buf, f32x4 vc, int c) {
+    // ---- prep1 (chunk in stage buffer sb -> operand set ob): per key channel, the
+    // running products of alpha = e^{g} over the chunk's tokens (padding tokens
+    // hold g = 0, i.e. alpha = 1): P_r = e^{G_r} (to LDS for prep2), Gamma = P_15,
+    // and K~_r = k_r e^{G_15 - G_r}.  A thread takes TP consecutive tokens of one
+    // channel, forms local prefix / suffix products, and combines them with the
+    // other parts of the channel through two lane shuffles at most; every thread
+    // runs the same instruction stream.
+    auto prep1 = [&](int sb, int ob) {
+        const int part = lane / CPW;
+        const int r0 = part * TP;
+#pragma unroll
+        for (int ci = 0; ci < CPT; ++ci) {
+            const int ch = wave * CPW + (lane % CPW) + ci * NT;
+            const bool valid = ch < DK;
+            const int chc = valid ? ch : 0;
+            float a[TP], kk[TP], lp[TP], ls[TP];
+#pragma unroll
+            for (int i = 0; i < TP; ++i) {
+                a[i] = gate_exp<F32>(load_in(&stg[sb][r0 + i][chc]));
+                kk[i] = load_in(&stk[sb][r0 + i][chc]);
+            }
+            float p = 1.f;
+#pragma unroll
+            for (int i = 0; i < TP; ++i) {
+                p *= a[i];
+                lp[i] = p;
+            }
+            float f = 1.f;
+#pragma unroll
+            for (int i = TP - 1; i >= 0; --i) {
+                ls[i] = f;
+                f *= a[i];
+            }
+            // combine the parts: pre = product of earlier parts, suf = of later parts
+            float pre = 1.f, suf = 1.f, tot = p;
+            if constexpr (NPART == 2) {
+                const float o1 = __shfl_xor(p, 32);
+                pre = part ? o1 : 1.f;
+                suf = part ? 1.f : o1;
+                tot = p * o1;
+            } else if constexpr (NPART == 4) {
+                const float o1 = __shfl_xor(p, 16);
+                const float pp = p * o1;
+                const bool low = (part & 1) == 0;
+                const float o2 = __shfl_xor(pp, 32);
+                const bool lowpair = part < 2;
+                pre = (low ? 1.f : o1) * (lowpair ? 1.f : o2);
+                suf = (low ? o1 : 1.f) * (lowpair ? o2 : 1.f);
+                tot = pp * o2;
+            }
+            if (C::PREP1_FULL || valid) {
+#pragma unroll
+                for (int i = 0; i < TP; ++i) sP[r0 + i][ch] = pre * lp[i];
+                if (part == 0) ops[ob].gam[ch] = tot;
+#pragma unroll
+                for (int qi = 0; qi < TP / 4; ++qi) {
+                    const int tq = r0 / 4 + qi;
+                    f32x4 kt;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) kt[j] = kk[4 * qi + j] * (ls[4 * qi + j] * suf);
+                    ops[ob].kt[ch >> 4][tq * 16 + (ch & 15)] = make_op<OpT>(kt);
+                }
+            }
+        }
+    };
+
+    // ---- prep2: per unit (token, 4 channels), Q+ and K+ fragments from P.
+    auto prep2 = [&](int sb, int ob) {
+#pragma unroll
+        for (int ui = 0; ui < UPT; ++ui) {
+            const int u = tid + ui * NT;
+            if (C::UNITS_FULL || u < C::UNITS) {
+                const int t = u / (DK / 4), a = u % (DK / 4);
+                const int c = 4 * a;
+                const f32x4 P = *reinterpret_cast<const f32x4 *>(&sP[t][c]);
+                const f32x4 qv = load_in4(&stq[sb][t][c]) * P;
+                const f32x4 kv = load_in4(&stk[sb][t][c]) * P;
+                const int b = c >> 4;
+                const int ln = ((c & 15) >> 2) * 16 + t;
+                if constexpr (F32) {
+                    ops[ob].qp[b][ln] = qv;
+                    ops[ob].kp[b][ln] = kv;
+                } else {
+                    const Split4 qs = split4(qv);
+                    bf16x4 *qh = reinterpret_cast<bf16x4 *>(&ops[ob].qp_hi[b >> 1][ln]) + (b & 1);
+                    bf16x4 *ql = reinterpret_cast<bf16x4 *>(&ops[ob].qp_lo[b >> 1][ln]) + (b & 1);
+                    bf16x4 *kh = reinterpret_cast<bf16x4 *>(&ops[ob].kp[b >> 1][ln]) + (b & 1);
+                    *qh = qs.hi;
+                    *ql = qs.lo;
+                    *kh = to_bf16x4(kv);
+                    if constexpr (NB == 1) {  // a lone block: the pair's upper half must be zero
+                        const bf16x4 z = {};
+                        qh[1] = z;
+                        ql[1] = z;
+                        kh[1] = z;
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- one chunk of the recurrence for this wave's 16 columns (operand set ob)
+    auto advance = [&](int ob, f32x4 vc, const Frags &F, int c) {
+        const Ops &P = ops[ob];
         f32x4 O;
-        if constexpr (C::F32) {
+        if constexpr (F32) {
             f32x4 X = zero4();
 #pragma unroll
-            for (int b = 0; b < NB; ++b) X = mma_f32_k16(sKp[buf][b][lane], S[b], X);
-            const f32x4 D = mma_f32_k16(sTp[buf][lane], vc - X, zero4());
-            O = mma_f32_k16(sAq[buf][lane], D, zero4());
+            for (int b = 0; b < NB; ++b) X = mma_f32_k16(P.kp[b][lane], S[b], X);
+            const f32x4 D = mma_f32_k16(F.tp, vc - X, zero4());
+            O = mma_f32_k16(F.aq, D, zero4());
 #pragma unroll
-            for (int b = 0; b < NB; ++b) O = mma_f32_k16(sQp[buf][b][lane], S[b], O);
+            for (int b = 0; b < NB; ++b) O = mma_f32_k16(P.qp[b][lane], S[b], O);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sGam[buf][16 * b + 4 * g4]);
-                S[b] = mma_f32_k16(sKt[buf][b][lane], D, S[b] * gam);
+                const f32x4 gam = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * g4]);
+                S[b] = mma_f32_k16(P.kt[b][lane], D, S[b] * gam);
             }
         } else {
-            Split4 Ss[NB];
+            bf16x8 Shi[NPAIR], Slo[NPAIR];
+            const bf16x4 z = {};
 #pragma unroll
-            for (int b = 0; b < NB; ++b) Ss[b] = split4(S[b]);
+            for (int p = 0; p < NPAIR; ++p) {
+                if constexpr (NB == 1) {
+                    const Split4 s0 = split4(S[0]);
+                    Shi[p] = cat(s0.hi, z);
+                    Slo[p] = cat(s0.lo, z);
+                } else {
+                    split_pair(S[2 * p], S[2 * p + 1], Shi[p], Slo[p]);
+                }
+            }
+            // X = K+ S (single bf16), Delta = T' (V - X) (split), O = A_qk Delta + Q+ S (split)
             f32x4 X = zero4();
-            if constexpr (NB == 1) {
-                X = mma16(sKp[buf][0][lane], Ss[0].hi, X);
-            } else {
 #pragma unroll
-                for (int b = 0; b < NB; b += 2)
-                    X = mma_single_k32(sKp[buf][b][lane], sKp[buf][b + 1][lane], Ss[b].hi, Ss[b + 1].hi, X);
-            }
-            const f32x4 D = mma_split_k16(sTp[buf][lane], split4(vc - X), zero4());
+            for (int p = 0; p < NPAIR; ++p) X = mma32(P.kp[p][lane], Shi[p], X);
+            const Split4 Ys = split4(vc - X);
+            const Split4 &Tp = F.tp;
+            const bf16x8 tpp = cat(Tp.hi, Tp.lo);
+            f32x4 D = mma32(tpp, cat(Ys.hi, Ys.hi), zero4());
+            D = mma32(tpp, cat(Ys.lo, Ys.lo), D);
             const Split4 Ds = split4(D);
-            O = mma_split_k16(sAq[buf][lane], Ds, zero4());
-            if constexpr (NB == 1) {
-                O = mma_split_k16(sQp[buf][0][lane], Ss[0], O);
-            } else {
+            const bf16x8 dhh = cat(Ds.hi, Ds.hi), dll = cat(Ds.lo, Ds.lo);
+            const Split4 &Aq = F.aq;
+            const bf16x8 aqq = cat(Aq.hi, Aq.lo);
+            O = mma32(aqq, dhh, zero4());
+            O = mma32(aqq, dll, O);
 #pragma unroll
-                for (int b = 0; b < NB; b += 2)
-                    O = mma_split_k32(sQp[buf][b][lane], sQp[buf][b + 1][lane], Ss[b], Ss[b + 1], O);
+            for (int p = 0; p < NPAIR; ++p) {
+                O = mma32(P.qp_hi[p][lane], Shi[p], O);
+                O = mma32(P.qp_lo[p][lane], Shi[p], O);
+                O = mma32(P.qp_hi[p][lane], Slo[p], O);
             }
+            // S <- Diag(Gamma) S + K~^T Delta
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sGam[buf][16 * b + 4 * g4]);
-                S[b] = mma_split_k16(sKt[buf][b][lane], Ds, S[b] * gam);
+                const f32x4 gam = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * g4]);
+                const Split4 kt = P.kt[b][lane];
+                const bf16x8 ktt = cat(kt.hi, kt.lo);
+                f32x4 acc = mma32(ktt, dhh, S[b] * gam);
+                S[b] = mma32(ktt, dll, acc);
             }
         }
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(c);
+        const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV, (uint32_t)n * rowO);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int t = 4 * g4 + jj;
-            if (t < n) o[((t0 + t) * H + h) * DV + col0 + n16] = O[jj];
+            buf_store_f32(O[jj], ro, t < n ? t * rowO + (col0 + n16) * 4u : OOB);
         }
     };
 
+    // Pipeline (iteration c): [barrier] advance(c) || prep1(c+1) [barrier]
+    // prep2(c+1); park the raw loads of chunk c+2 (issued one iteration earlier)
+    // in the stage buffer chunk c just vacated; issue the loads of chunk c+3.
+    // The body is branch-free: look-ahead past the last chunk re-reads the last
+    // chunk and fills buffers nobody reads, so the compiler can interleave the
+    // recurrence with the prep, and the only wait on global loads sits one full
+    // iteration after their issue.
     if (nc > 0) {
-        Raw<DK, DV, T, NW> R;
-        load_raw(R, 0);
-        prep1(R, 0);
+        Units U;
+        load_units(U, 0);
+        store_units(U, 0);
+        load_units(U, clampc(1));
+        store_units(U, 1);
+        load_units(U, clampc(2));
         __syncthreads();
-        prep2(R, 0);
-        f32x4 vcur = load_v(0);
-        if (nc > 1) load_raw(R, 1);
+        prep1(0, 0);
         __syncthreads();
+        prep2(0, 0);
         for (int c = 0; c < nc; ++c) {
-            const int buf = c & 1;
-            const f32x4 vnext = (c + 1 < nc) ? load_v(c + 1) : zero4();
-            advance(buf, vcur, c);
-            if (c + 1 < nc) prep1(R, buf ^ 1);
             __syncthreads();
-            if (c + 1 < nc) {
-                prep2(R, buf ^ 1);
-                if (c + 2 < nc) load_raw(R, c + 2);
-            }
+            advance(c & 1, stage_v(c & 1), stage_frags(c & 1), c);
+            prep1((c + 1) & 1, (c + 1) & 1);
             __syncthreads();
-            vcur = vnext;
+            prep2((c + 1) & 1, (c + 1) & 1);
+            store_units(U, c & 1);
+            load_units(U, clampc(c + 3));
         }
     }
 
@@ -374,6 +527,10 @@ hipError_t launch_inter_chunk(const InterChunkArgs &a) {
     int nw = a.waves_per_group;
     if (nw <= 0) {
         nw = default_waves(a.dk, a.dv);
+        // dk = dv = 128: one 8-wave workgroup per (sequence, head) when there are
+        // enough chains to give every CU one; otherwise two 4-wave workgroups per
+        // chain so that twice as many CUs work on the serial recurrence.
+        if (a.dk == 128 && a.dv == 128) nw = ((int64_t)a.nseq * a.H >= 256) ? 8 : 4;
         // Tuning knob: KDA_WAVES in {2, 4, 8} for dk = dv = 128.
         if (a.dk == 128 && a.dv == 128) {
             if (const char *e = getenv("KDA_WAVES")) {

@@ -45,28 +45,24 @@ __device__ __forceinline__ float bf16_to_f32(__bf16 x) {
 // Round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
 
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-    bf16x4 r;
-    r[0] = f32_to_bf16(x[0]);
-    r[1] = f32_to_bf16(x[1]);
-    r[2] = f32_to_bf16(x[2]);
-    r[3] = f32_to_bf16(x[3]);
-    return r;
-}
+// Vector conversion: lowers to two packed v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Widen four bf16 by moving each into the high half of a 32-bit word (explicit
+// bit operations on the packed pairs, so no element is converted twice).
 __device__ __forceinline__ f32x4 from_bf16x4(bf16x4 x) {
-    f32x4 r;
-    r[0] = bf16_to_f32(x[0]);
-    r[1] = bf16_to_f32(x[1]);
-    r[2] = bf16_to_f32(x[2]);
-    r[3] = bf16_to_f32(x[3]);
-    return r;
+    const u32x2_t w = __builtin_bit_cast(u32x2_t, x);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
 }
 
 struct Split4 {
     bf16x4 hi, lo;
 };
 
+// x = hi + lo: hi = bf16(x), lo = bf16(x - hi); 3 VALU operations per element.
 __device__ __forceinline__ Split4 split4(f32x4 x) {
     Split4 s;
     s.hi = to_bf16x4(x);
@@ -160,5 +156,51 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // exp for the decay factors: ROCm's device expf (full-accuracy path).
 __device__ __forceinline__ float decay_exp(float x) { return expf(x); }
+
+// exp through the hardware 2^x (v_exp_f32) on x * log2(e).  For the gate range
+// [-5, 0] the rounding of the product costs at most ~4e-7 relative, far below
+// the bf16 operand rounding it feeds; used for bf16 inputs only.
+__device__ __forceinline__ float decay_exp_fast(float x) { return __expf(x); }
+
+// ---------------------------------------------------------------- buffer access
+//
+// Raw buffer resources (gfx9 family word 3 = 0x00020000): the base address is
+// uniform (SGPRs), the per-lane byte offset is a VGPR.  A lane whose offset is at
+// or beyond num_records reads zeros and its stores are dropped by the hardware;
+// OOB is used to park padding lanes of a ragged chunk.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t BUF_WORD3 = 0x00020000u;
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)BUF_WORD3);
+}
+
+__device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load_u32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 buf_load_u32x2(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 buf_load_u32x4(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+
+// Widen packed input elements held in 32-bit words.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 }  // namespace kda

@@ -9,7 +9,9 @@
 namespace kda {
 
 // Workspace per (chunk slot, head): T' = (I + A_kk)^-1 diag(beta), then A_qk,
-// each a row-major 16x16 fp32 matrix.
+// each stored as the A-operand fragment of a 16x16 MFMA (64 lanes x 16 bytes:
+// lane 16g + m holds row m, columns 4g..4g+3; as {hi[4], lo[4]} bf16 for bf16
+// inputs, as 4 fp32 for fp32 inputs).  2 KiB per (chunk slot, head).
 constexpr int WS_FLOATS_PER_CHUNK_HEAD = 2 * 16 * 16;
 
 // Chunk slots: sequence s owns slots floor(cu[s]/16) + s + j, j < ceil(len_s/16).

@@ -47,6 +47,19 @@ def _prefill_case(dev, seqlens, H, dk, dv, dtype, seed=0, gate="neg_softplus", i
 
 # ----------------------------------------------------------------- chunk-local phase
 
+def decode_workspace(ws, H, dtype):
+    """The workspace holds, per (chunk slot, head), T' then A_qk as 16x16 MFMA A-operand
+    fragments: lane 16g + m holds row m, columns 4g..4g+3 ({hi[4], lo[4]} bf16 for bf16
+    inputs, 4 fp32 for fp32 inputs).  Returns [slots, H, 2, 16, 16] float64."""
+    if dtype == torch.float32:
+        fr = ws.cpu().double().numpy().reshape(-1, H, 2, 4, 16, 4)           # [.., g, m, j]
+    else:
+        b = ws.cpu().view(torch.bfloat16).double().numpy().reshape(-1, H, 2, 4, 16, 8)
+        fr = b[..., :4] + b[..., 4:]
+    # M[m][4g + j] = fr[g][m][j]
+    return np.ascontiguousarray(fr.transpose(0, 1, 2, 4, 3, 5)).reshape(fr.shape[0], H, 2, 16, 16)
+
+
 @pytest.mark.parametrize("dtype,dk", [(torch.float32, 16), (torch.float32, 128),
                                       (torch.bfloat16, 64), (torch.bfloat16, 128)])
 def test_chunk_local_matches_chunked_model(dev, dtype, dk):
@@ -61,7 +74,7 @@ def test_chunk_local_matches_chunked_model(dev, dtype, dk):
     ws.fill_(float("nan"))
     kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
     torch.cuda.synchronize()
-    wsn = ws.cpu().double().numpy().reshape(-1, H, 2, 16, 16)
+    wsn = decode_workspace(ws, H, dtype)
     cpu = {n: x[n].cpu().double().numpy() for n in ("q", "k", "v", "log_alpha", "beta")}
     _, _, kept = chunk_model.prefill(cpu["q"], cpu["k"], cpu["v"], cpu["log_alpha"], cpu["beta"],
                                      cu_seqlens=workloads.cu_seqlens_of(seqlens), keep=True)
@@ -262,15 +275,21 @@ def test_bitwise_deterministic(dev):
 
 
 def test_waves_per_group_variants_agree(dev, monkeypatch):
-    """The 2-, 4- and 8-wave workgroup shapes of the inter-chunk kernel give the same bits."""
+    """The 2-, 4- and 8-wave workgroup shapes of the inter-chunk kernel each meet the bar and
+    agree with each other (the per-channel products are grouped differently per shape, so
+    only each shape on its own is bitwise reproducible)."""
     w = workloads.custom([130, 64], 3, 128, 128, torch.bfloat16)
     x = workloads.prefill_inputs(w, device=dev, seed=10)
+    o_ref, f_ref = oracle_prefill(x)
     outs = []
     for nw in ("2", "4", "8"):
         monkeypatch.setenv("KDA_WAVES", nw)
         outs.append(kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"]))
-    torch.cuda.synchronize()
+        again = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+        torch.cuda.synchronize()
+        assert torch.equal(outs[-1][0], again[0]) and torch.equal(outs[-1][1], again[1])
+        assert_close(outs[-1][0], o_ref, TOL[torch.bfloat16], f"o (NW={nw})")
+        assert_close(outs[-1][1], f_ref, TOL[torch.bfloat16], f"final_state (NW={nw})")
     for o, f in outs[1:]:
-        assert torch.equal(o, outs[0][0]) and torch.equal(f, outs[0][1])
-    o_ref, f_ref = oracle_prefill(x)
-    assert_close(outs[0][0], o_ref, TOL[torch.bfloat16], "o")
+        assert rel_err(o, outs[0][0].double().cpu().numpy()) <= TOL[torch.bfloat16]
+        assert rel_err(f, outs[0][1].double().cpu().numpy()) <= TOL[torch.bfloat16]
