@@ -58,6 +58,51 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/inter_chunk.hip", "gated_delta_rule_51_amd/csrc/kda_device.hpp",
+                  "gated_delta_rule_51_amd/csrc/kda_launch.hpp")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "inter_chunk_batched_prefill_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per inter-chunk launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when it is missing or was taken on different kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.strip()
+        if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, dev, gib: float = 1.0, reps: int = 3) -> None:
+    """A plain device copy of known size (read + write gib GiB each), so hardware byte
+    counters collected over this run can be scaled to true bytes."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 class Timer:
     """HIP events on torch's current stream (the stream every KDA call is enqueued on)."""
 
@@ -242,6 +287,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all", choices=["all", "main", "k3", "decode", "varlen", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (heads and sequences shard "
@@ -259,6 +306,8 @@ def main() -> int:
         __graft_entry__.build()
     kda.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     out = {"metric": "KDA prefill tokens/s + TFLOP/s (% MFMA peak); decode state GB/s (% HBM peak)",
            "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -285,7 +334,8 @@ def main() -> int:
         b = m["ic_bytes"] if dom == "inter_chunk" else m["cl_bytes"]
         ach = b / (kernels[dom] * 1e-3) / 1e9
         out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                           "traffic": measured_traffic() if dom == "inter_chunk" else None,
                            "algorithmic_bytes_per_launch": b}
         if not args.no_cpu_baseline:
             log("[bench] cpu baseline: fp64 oracle on the same batch")
