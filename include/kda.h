@@ -44,8 +44,10 @@
  * pointers unless stated otherwise.  Work is enqueued on `stream` (a
  * hipStream_t; NULL = the default stream) and the call returns at once.
  * Inputs are read-only; o / final_state must not alias the inputs (except the
- * final_state == init_state case above).  Every device pointer must be 16-byte
- * aligned.
+ * final_state == init_state case above).  Alignment: fp32 buffers (state,
+ * o, init/final state, workspace) 16 bytes; q, k, v, log_alpha four elements
+ * (8 bytes for bf16, 16 for fp32); beta one element.  With total_tokens == 0
+ * the token-indexed pointers may be NULL.
  *
  * Errors: argument errors are detected on the host before any launch and
  * returned as a status; nothing is launched then.  A failed launch returns
@@ -69,7 +71,7 @@ extern "C" {
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,         /* a required pointer is NULL */
-    KDA_ERR_ALIGN = 2,        /* a pointer is not 16-byte aligned */
+    KDA_ERR_ALIGN = 2,        /* a pointer violates the alignment rules above */
     KDA_ERR_SHAPE = 3,        /* nseq < 1, H < 1, B < 1, or total_tokens out of range */
     KDA_ERR_UNSUPPORTED = 4,  /* dk / dv not in {16,32,64,128}, or unknown dtype */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kda_prefill_workspace_bytes */
