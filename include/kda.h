@@ -87,9 +87,11 @@ typedef enum kda_dtype {
 #define KDA_GATE_LOWER_BOUND (-5.0f)
 
 /* Bytes of device workspace kda_prefill / kda_chunk_local / kda_inter_chunk
- * need: per chunk slot and head, the 16x16 fp32 matrices T' = (I + A_kk)^-1
- * diag(beta) and A_qk (2 KiB), for floor(N/16) + nseq chunk slots.  Returns 0
- * for invalid arguments. */
+ * need: per chunk slot and head, the 16x16 matrices T' = (I + A_kk)^-1
+ * diag(beta) and A_qk, each as a 1 KiB matrix-core operand fragment (a
+ * hi/lo bfloat16 pair per element for KDA_BF16, fp32 for KDA_F32), for
+ * floor(N/16) + nseq chunk slots.  The layout is private to the library.
+ * Returns 0 for invalid arguments. */
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype dt);
 
