@@ -10,9 +10,22 @@
 // Each state element is read once and written once, in place.  The serving
 // section of the same page names this in-place state traffic as the decode
 // bottleneck, so the kernel is built around streaming the fp32 state at HBM
-// rate: 16-byte vector loads/stores, all of a thread's rows in flight at
-// once, column reductions through LDS.  No matrix cores are used (about one
-// flop per byte).
+// rate.  No matrix cores are used (about one flop per byte).
+//
+// Shape of the launch: a persistent grid of at most GRID_THREADS / NT
+// workgroups walks the heads with stride gridDim.x, so at any moment the
+// resident workgroups stream neighbouring 64 KiB state blocks (DRAM-page
+// friendly), and each workgroup issues the loads of its next head's state
+// before it reduces and writes back the current one, keeping reads and
+// writes in flight together.  Thread (rg, c4) holds column quad c4 of rows
+// rg, rg + RP, ... in registers.
+//
+// Column sums S'^T k and S'^T q go through LDS in two stages: every row
+// group writes its partial quads, then P = RP/8 neighbouring lanes own one
+// output column, each adds 8 partials (rows part, part + P, ...; the row
+// stride is padded so the lanes of a wave hit distinct banks) and the P
+// lanes combine by cross-lane shuffles.  Every thread then reads back only
+// the two quads it needs.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -20,74 +33,124 @@ namespace kda {
 
 template <int DK, int DV>
 struct DecodeShape {
-    static constexpr int NC4 = DV / 4;                                   // column quads per row
-    static constexpr int RP = (DK < 256 / NC4) ? DK : 256 / NC4;         // rows per pass
-    static constexpr int NT = NC4 * RP;                                  // threads per head
-    static constexpr int NR = DK / RP;                                   // rows per thread
+    static constexpr int NC4 = DV / 4;                       // column quads per row
+    static constexpr int RP_CAP = 1024 / NC4 < 64 ? 1024 / NC4 : 64;
+    static constexpr int RP = DK < RP_CAP ? DK : RP_CAP;     // row groups (>= 16)
+    static constexpr int NT = NC4 * RP;                      // threads per workgroup
+    static constexpr int NR = DK / RP;                       // rows per thread
+    static constexpr int P = RP / 8;                         // lanes per output column
+    static constexpr int STRIDE = DV + ((64 / P - DV % 64) + 64) % 64;  // floats per partial row
+    static constexpr int NKW = (DK + 63) / 64;               // waves that reduce k.q
+    static_assert(RP >= 16 && RP % 8 == 0 && NT % 64 == 0 && NT >= 64 * NKW, "decode shape");
+    static_assert(NT / P == 2 * DV, "one output column per P lanes");
+    static_assert(STRIDE % 4 == 0, "partial rows hold aligned quads");
 };
+
+// Total threads of the persistent grid (4 Mi state floats in flight at most).
+constexpr int64_t GRID_THREADS = 1 << 20;
 
 template <int DK, int DV, typename T>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
-    float *__restrict__ o) {
+    float *__restrict__ o, int64_t heads) {
     using Sh = DecodeShape<DK, DV>;
-    constexpr int NC4 = Sh::NC4, RP = Sh::RP, NT = Sh::NT, NR = Sh::NR;
-    const int64_t head = blockIdx.x;  // b * H + h
+    constexpr int NC4 = Sh::NC4, RP = Sh::RP, NR = Sh::NR, P = Sh::P, NKW = Sh::NKW;
     const int tid = threadIdx.x;
     const int c4 = tid % NC4;
     const int rg = tid / NC4;
+    const int64_t stride = gridDim.x;
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
-    __shared__ f32x4 s_red[2][RP][NC4];
-    __shared__ float s_kq[RP];
+    __shared__ __attribute__((aligned(16))) float s_red[2][RP][Sh::STRIDE];
+    __shared__ __attribute__((aligned(16))) float s_fin[2][DV];
+    __shared__ float s_kq[2][NKW];
 
-    float *S = state + head * (int64_t)(DK * DV);
-    f32x4 rows[NR];
+    auto load_rows = [&](f32x4 (&rows)[NR], int64_t head) {
+        const float *S = state + head * (int64_t)(DK * DV);
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-        rows[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (int64_t)(rg + r * RP) * DV) + c4);
+        for (int r = 0; r < NR; ++r)
+            rows[r] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4 *>(S + (int64_t)(rg + r * RP) * DV) + c4);
+    };
 
-    for (int i = tid; i < DK; i += NT) {
-        s_k[i] = load_in(k + head * DK + i);
-        s_q[i] = load_in(q + head * DK + i);
-        s_a[i] = decay_exp(load_in(g + head * DK + i));
-    }
-    const f32x4 vv = load_in4(v + head * DV + 4 * c4);
-    const float b = load_in(beta + head);
-    __syncthreads();
-
-    f32x4 pv = zero4(), pq = zero4();
-    float pkq = 0.f;
+    // One head.  LDS reuse across heads: s_k/s_q/s_a are last read before the
+    // second barrier, s_red before the third, s_fin after the third (rewritten
+    // only after the next head's second barrier), s_kq is double-buffered.
+    auto step = [&](f32x4 (&rows)[NR], f32x4 (&nxt)[NR], int64_t head, int par) {
+        float kk = 0.f, qq = 0.f;
+        if (tid < DK) {
+            kk = load_in(k + head * DK + tid);
+            qq = load_in(q + head * DK + tid);
+            s_k[tid] = kk;
+            s_q[tid] = qq;
+            s_a[tid] = decay_exp(load_in(g + head * DK + tid));
+        }
+        if (tid < 64 * NKW) {  // whole waves: k.q by cross-lane sums
+            float kq = kk * qq;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int row = rg + r * RP;
-        rows[r] = rows[r] * s_a[row];             // forget
-        pv += s_k[row] * rows[r];                  // partial S'^T k
-        pq += s_q[row] * rows[r];                  // partial S'^T q
-        pkq += s_k[row] * s_q[row];
-    }
-    s_red[0][rg][c4] = pv;
-    s_red[1][rg][c4] = pq;
-    if (c4 == 0) s_kq[rg] = pkq;
-    __syncthreads();
+            for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
+            if ((tid & 63) == 0) s_kq[par][tid >> 6] = kq;
+        }
+        const f32x4 vv = load_in4(v + head * DV + 4 * c4);
+        const float b = load_in(beta + head);
+        if (head + stride < heads) load_rows(nxt, head + stride);
+        __syncthreads();
 
-    f32x4 vhat = zero4(), rq = zero4();
-    float kq = 0.f;
+        f32x4 pv = zero4(), pq = zero4();
+        float kr[NR];
 #pragma unroll
-    for (int i = 0; i < RP; ++i) {
-        vhat += s_red[0][i][c4];
-        rq += s_red[1][i][c4];
-        kq += s_kq[i];
-    }
-    const f32x4 delta = b * (vv - vhat);
-    if (rg == 0) reinterpret_cast<f32x4 *>(o + head * DV)[c4] = rq + kq * delta;
+        for (int r = 0; r < NR; ++r) {
+            const int row = rg + r * RP;
+            kr[r] = s_k[row];
+            rows[r] = rows[r] * s_a[row];  // forget
+            pv += kr[r] * rows[r];         // partial S'^T k
+            pq += s_q[row] * rows[r];      // partial S'^T q
+        }
+        *reinterpret_cast<f32x4 *>(&s_red[0][rg][4 * c4]) = pv;
+        *reinterpret_cast<f32x4 *>(&s_red[1][rg][4 * c4]) = pq;
+        __syncthreads();
 
+        {
+            const int out = tid / P, part = tid % P;
+            const int arr = out / DV, col = out % DV;
+            float x = 0.f;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int row = rg + r * RP;
-        const f32x4 nr = rows[r] + s_k[row] * delta;  // erase + write
-        __builtin_nontemporal_store(nr, reinterpret_cast<f32x4 *>(S + (int64_t)row * DV) + c4);
+            for (int j = 0; j < 8; ++j) x += s_red[arr][part + P * j][col];
+#pragma unroll
+            for (int m = 1; m < P; m <<= 1) x += __shfl_xor(x, m);
+            if (part == 0) s_fin[arr][col] = x;
+        }
+        __syncthreads();
+
+        const f32x4 vhat = *reinterpret_cast<const f32x4 *>(&s_fin[0][4 * c4]);
+        const f32x4 rq = *reinterpret_cast<const f32x4 *>(&s_fin[1][4 * c4]);
+        float kq = 0.f;
+#pragma unroll
+        for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
+        const f32x4 delta = b * (vv - vhat);
+        if (rg == 0) reinterpret_cast<f32x4 *>(o + head * DV)[c4] = rq + kq * delta;
+
+        float *S = state + head * (int64_t)(DK * DV);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int row = rg + r * RP;
+            __builtin_nontemporal_store(rows[r] + kr[r] * delta,  // erase + write
+                                        reinterpret_cast<f32x4 *>(S + (int64_t)row * DV) + c4);
+        }
+    };
+
+    int64_t head = blockIdx.x;
+    if (head >= heads) return;
+    f32x4 ra[NR], rb[NR];
+    load_rows(ra, head);
+    for (;;) {  // two heads per trip so the register sets swap roles without copies
+        step(ra, rb, head, 0);
+        head += stride;
+        if (head >= heads) break;
+        step(rb, ra, head, 1);
+        head += stride;
+        if (head >= heads) break;
     }
 }
 
@@ -95,9 +158,11 @@ template <int DK, int DV, typename T>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
     using Sh = DecodeShape<DK, DV>;
     const int64_t heads = (int64_t)a.B * a.H;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), dim3((unsigned)heads), dim3(Sh::NT), 0,
+    const int64_t cap = GRID_THREADS / Sh::NT;
+    const int64_t grid = heads < cap ? heads : cap;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), dim3((unsigned)grid), dim3(Sh::NT), 0,
                        (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.v,
-                       (const T *)a.g, (const T *)a.beta, a.state, a.o);
+                       (const T *)a.g, (const T *)a.beta, a.state, a.o, heads);
     return hipGetLastError();
 }
 
