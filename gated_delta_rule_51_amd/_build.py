@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libkda_mi355x.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk_local.hip", "inter_chunk.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk_local.hip", "inter_chunk.hip", "inter_chunk_ws.hip"]
 ARCH = "gfx950"
 
 

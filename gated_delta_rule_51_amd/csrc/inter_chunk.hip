@@ -32,6 +32,7 @@
 // Precision: K+ S uses single-bf16 operands; T'(V - K+S), Q+ S, A_qk Delta and
 // K~^T Delta use split-bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation;
 // the state stays fp32.  fp32 inputs use fp32 MFMAs throughout.
+#include <stdio.h>
 #include <stdlib.h>
 
 #include <type_traits>
@@ -524,19 +525,43 @@ static hipError_t launch_ic_dt(const InterChunkArgs &a, int nw) {
 }
 
 hipError_t launch_inter_chunk(const InterChunkArgs &a) {
+    // Kernel choice.  The serial recurrence is latency-bound while there are
+    // few (sequence, head) chains: then bf16 inputs with dk >= 32 run the
+    // warp-specialised kernel (inter_chunk_ws.hip), whose producer waves take
+    // the token-parallel work off the consumers' critical path.  With enough
+    // chains to give every CU a full workgroup (dk = dv = 128: 256 or more),
+    // the work is throughput-bound and this file's kernel, which does the
+    // per-chunk preparation once per chain, is faster.
+    // Tuning knobs: KDA_WS = "<consumers>x<producers>" forces the warp-
+    // specialised kernel with that shape; KDA_WAVES in {2, 4, 8} forces this
+    // file's kernel with that many waves (dk = dv = 128).
+    const int64_t nchains = (int64_t)a.nseq * a.H;
+    const char *classic = getenv("KDA_WAVES");
+    const char *ws_shape = getenv("KDA_WS");
+    const bool big = a.dk == 128 && a.dv == 128 && nchains >= 256;
+    if (a.bf16 && a.dk >= 32 && a.waves_per_group == 0 && !classic && (!big || ws_shape)) {
+        int ncw = nchains < 64 ? 2 : 4;
+        if (ncw > a.dv / 16) ncw = a.dv / 16;
+        int npw = a.dk / 16 < 4 ? a.dk / 16 : 4;
+        if (ws_shape) {
+            int c = 0, p = 0;
+            if (sscanf(ws_shape, "%dx%d", &c, &p) == 2) {
+                ncw = c;
+                npw = p;
+            }
+        }
+        return launch_inter_chunk_ws(a, ncw, npw);
+    }
     int nw = a.waves_per_group;
     if (nw <= 0) {
         nw = default_waves(a.dk, a.dv);
         // dk = dv = 128: one 8-wave workgroup per (sequence, head) when there are
         // enough chains to give every CU one; otherwise two 4-wave workgroups per
         // chain so that twice as many CUs work on the serial recurrence.
-        if (a.dk == 128 && a.dv == 128) nw = ((int64_t)a.nseq * a.H >= 256) ? 8 : 4;
-        // Tuning knob: KDA_WAVES in {2, 4, 8} for dk = dv = 128.
-        if (a.dk == 128 && a.dv == 128) {
-            if (const char *e = getenv("KDA_WAVES")) {
-                const int w = atoi(e);
-                if (w == 2 || w == 4 || w == 8) nw = w;
-            }
+        if (a.dk == 128 && a.dv == 128) nw = big ? 8 : 4;
+        if (a.dk == 128 && a.dv == 128 && classic) {
+            const int w = atoi(classic);
+            if (w == 2 || w == 4 || w == 8) nw = w;
         }
     }
     return a.bf16 ? launch_ic_dt<__bf16>(a, nw) : launch_ic_dt<float>(a, nw);

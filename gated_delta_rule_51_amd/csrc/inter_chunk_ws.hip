@@ -1,0 +1,378 @@
+// Inter-chunk phase of the KDA prefill, warp-specialised form for bf16 inputs
+// (gfx950).  Same algebra as inter_chunk.hip (Kimi K3 report digest, "Kimi
+// Delta Attention": the chunk output is the inter-chunk term (Gamma (.) Q) S
+// plus the intra-chunk term; the state advances as Diag(Gamma) S + K~^T Delta):
+//     K+ = K (.) e^{G},  Q+ = Q (.) e^{G},  K~ = K (.) e^{G_n - G},  Gamma = e^{G_n}
+//     Delta = T' (V - K+ S),   O = Q+ S + A_qk Delta,   S <- Diag(Gamma) S + K~^T Delta
+//
+// A workgroup serves one (sequence, head) and NC 16-column slices of dv.  Its
+// waves have two roles:
+//   * NC consumer waves each keep a 16-column fp32 state slice in registers
+//     and advance it chunk by chunk (matrix cores; the serial part);
+//   * NP producer waves build the state-independent operands of the next
+//     chunk (Q+, K+, K~, Gamma) into LDS while the consumers work.
+// One barrier per chunk hands a finished operand set from producers to
+// consumers (two sets in LDS, used alternately).  Splitting the roles takes
+// the token-parallel work off the consumers' critical path and lets the two
+// kinds of work share each SIMD.
+//
+// Producers load q, k and g of a chunk as token rows with four consecutive
+// channels per lane (one 8-byte load each; the operand layout of Q+ and K+).
+// A product with the identity turns g and k into four consecutive tokens of
+// one channel per lane, and the cumulative log-decay G of the chunk is then a
+// product with a 0/1 triangle, G^T = g^T L^T and Gs = U g (Gs_r = sum over
+// later tokens = G_n - G_r).  The first lands in the operand layout of Q+ and
+// K+, the second in that of K~^T (channel rows, four consecutive tokens per
+// lane), so every operand is formed where it is needed and written with one
+// vector store.  g is bf16 and the triangles are 0/1, so the sums are exact up
+// to fp32 accumulation.
+// Each role loads its own inputs straight from HBM three chunks ahead:
+// producers q/k/g, consumers T', A_qk (workspace fragments) and their v
+// columns (transposed on the matrix cores like the producers' g and k).  Padding tokens of a ragged last chunk load as zeros (g = 0 keeps
+// the decay unchanged, k = 0 removes them from every product).
+//
+// Precision as in inter_chunk.hip: K+ S single bf16, everything else split
+// bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation, fp32 state.
+#include <stdlib.h>
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <int DK>
+struct WsOps {
+    static constexpr int NB = DK / 16, NPAIR = NB / 2;
+    bf16x8 qp_hi[NPAIR][64];  // Q+ A-fragments, block pairs packed (one K=32 MFMA operand)
+    bf16x8 qp_lo[NPAIR][64];
+    bf16x8 kp[NPAIR][64];     // K+ (single bf16), same packing
+    Split4 kt[NB][64];        // K~^T A-fragments (channel rows, 4 tokens per lane), {hi, lo}
+    float gam[DK];            // e^{G_n} per channel
+};
+
+__device__ __forceinline__ f32x4 unpack_bf16x4(u32x2 w) {
+    return f32x4{lo_bf16(w[0]), hi_bf16(w[0]), lo_bf16(w[1]), hi_bf16(w[1])};
+}
+
+// B operand of the 16x16 identity (lane (g4, n) holds I[4 g4 + j][n]).  A 16x16
+// bf16 tile held as the A operand of a product -- row m in lane group m, four
+// consecutive columns per lane -- times this returns the same tile in the
+// accumulator layout (four consecutive rows per lane, one column per lane):
+// a transpose of the register layout on the matrix cores, exact for bf16 data.
+__device__ __forceinline__ bf16x4 identity_operand(int g4, int l16) {
+    u16x4 bits;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bits[j] = (4 * g4 + j == l16) ? 0x3f80 : 0;
+    return __builtin_bit_cast(bf16x4, bits);
+}
+
+template <int DK, int DV, int NC, int NP>
+__global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(2, 2))) void inter_chunk_ws_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const __bf16 *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
+    int32_t H, const float *__restrict__ ws, float *__restrict__ o, float *__restrict__ fin,
+    int32_t nsplit, int32_t nchains) {
+    constexpr int NB = DK / 16, NPAIR = NB / 2, BPW = NB / NP;
+    constexpr uint32_t EB = 2;
+    static_assert(NB % 2 == 0 && NB % NP == 0, "channel blocks split evenly over producers");
+    static_assert(DV % (16 * NC) == 0, "column slices");
+
+    // XCD-aware order (as in inter_chunk.hip): all slices of one chain share an XCD.
+    const int L = blockIdx.x;
+    const int xcd = L & 7;
+    const int sx = L >> 3;
+    const int split = sx % nsplit;
+    const int chain = (sx / nsplit) * 8 + xcd;
+    if (chain >= nchains) return;
+    const int s = chain / H, h = chain % H;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g4 = lane >> 4, l16 = lane & 15;
+
+    __shared__ __attribute__((aligned(16))) WsOps<DK> ops[2];
+
+    const int64_t bos = cu[s], eos = cu[s + 1];
+    const int nc = (int)((eos - bos + 15) / 16);
+    const int64_t slot0 = bos / 16 + s;
+    const int64_t hd = (int64_t)s * H + h;
+    const uint32_t rowK = (uint32_t)H * DK * EB;   // bytes between tokens in q, k, g
+    const uint32_t rowV = (uint32_t)H * DV * EB;   // ... in v
+    const uint32_t rowO = (uint32_t)H * DV * 4;    // ... in o
+
+    auto chunk_len = [&](int c) -> int {
+        const int64_t left = eos - (bos + 16 * (int64_t)c);
+        return left < 16 ? (int)left : 16;
+    };
+    // Look-ahead loads past the last chunk re-read the last chunk (results unused).
+    auto clampc = [&](int c) { return c < nc ? c : nc - 1; };
+    // Buffer resource over chunk c of this head; rows past the chunk are out of bounds.
+    auto rsrc_in = [&](const __bf16 *base, int c, int d) {
+        const int64_t t0 = bos + 16 * (int64_t)c;
+        const int n = chunk_len(c);
+        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB);
+    };
+
+    if (wave < NC) {
+        // ============================================================ consumer
+        // The consumers carry the serial chain; when both roles are ready to
+        // issue on a SIMD, theirs go first and the producers fill the gaps.
+        __builtin_amdgcn_s_setprio(2);
+        // State slice: rows 16 b + 4 g4 + jj, column col0 + l16 (accumulator layout).
+        const int col0 = (split * NC + wave) * 16;
+        f32x4 S[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                S[b][jj] = init ? init[(hd * DK + 16 * b + 4 * g4 + jj) * DV + col0 + l16] : 0.f;
+
+        if (nc > 0) {
+            // Per-chunk consumer inputs: T' and A_qk fragments (workspace), and
+            // v of token l16, columns col0 + 4 g4 .. +3 (one 8-byte load; the
+            // identity product below turns it into rows 4 g4 + jj, column
+            // col0 + l16, the layout of the state slice).
+            struct CIn {
+                u32x4 tp, aq;
+                u32x2 v;
+            };
+            const bf16x4 ID = identity_operand(g4, l16);
+            auto cload = [&](CIn &X, int c) {
+                const float *wsc = ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
+                const rsrc_t rw = make_rsrc(wsc, WS_FLOATS_PER_CHUNK_HEAD * 4u);
+                X.tp = buf_load_u32x4(rw, lane * 16u);
+                X.aq = buf_load_u32x4(rw, (64 + lane) * 16u);
+                const int n = chunk_len(c);
+                const rsrc_t rv = rsrc_in(v, c, DV);
+                X.v = buf_load_u32x2(rv, l16 < n ? l16 * rowV + (col0 + 4 * g4) * EB : OOB);
+            };
+            auto advance = [&](int ob, const CIn &X, int c) {
+                const WsOps<DK> &P = ops[ob];
+                // Operand reads go out first, in two batches, so their LDS latency
+                // overlaps the state split and the K+ S products instead of
+                // stalling each matrix-core instruction that consumes them.
+                bf16x8 kpr[NPAIR], qhr[NPAIR], qlr[NPAIR];
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    kpr[p] = P.kp[p][lane];
+                    qhr[p] = P.qp_hi[p][lane];
+                    qlr[p] = P.qp_lo[p][lane];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const Split4 Tp = __builtin_bit_cast(Split4, X.tp);
+                const Split4 Aq = __builtin_bit_cast(Split4, X.aq);
+                const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, X.v), ID, zero4());
+                bf16x8 Shi[NPAIR], Slo[NPAIR];
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    const bf16x4 ah = to_bf16x4(S[2 * p]), bh = to_bf16x4(S[2 * p + 1]);
+                    const bf16x4 al = to_bf16x4(S[2 * p] - from_bf16x4(ah));
+                    const bf16x4 bl = to_bf16x4(S[2 * p + 1] - from_bf16x4(bh));
+                    Shi[p] = cat(ah, bh);
+                    Slo[p] = cat(al, bl);
+                }
+                // X = K+ S (single bf16), two independent partial sums
+                f32x4 Xa = zero4(), Xb = zero4();
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    if (p & 1) Xb = mma32(kpr[p], Shi[p], Xb);
+                    else Xa = mma32(kpr[p], Shi[p], Xa);
+                }
+                Split4 ktr[NB];
+                f32x4 gmr[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    ktr[b] = P.kt[b][lane];
+                    gmr[b] = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * g4]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // Q+ S for the output (hi*hi, lo*hi, hi*lo in three independent
+                // sums); it does not depend on Delta and fills the gaps of the
+                // Delta chain below.
+                f32x4 Oa = zero4(), Ob = zero4(), Oc = zero4();
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    Oa = mma32(qhr[p], Shi[p], Oa);
+                    Ob = mma32(qlr[p], Shi[p], Ob);
+                    Oc = mma32(qhr[p], Slo[p], Oc);
+                }
+                // Delta = T' (V - X)
+                const Split4 Ys = split4(vc - (Xa + Xb));
+                const bf16x8 tpp = cat(Tp.hi, Tp.lo);
+                f32x4 D = mma32(tpp, cat(Ys.hi, Ys.hi), zero4());
+                D = mma32(tpp, cat(Ys.lo, Ys.lo), D);
+                const Split4 Ds = split4(D);
+                const bf16x8 dhh = cat(Ds.hi, Ds.hi), dll = cat(Ds.lo, Ds.lo);
+                // S <- Diag(Gamma) S + K~^T Delta
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const bf16x8 ktt = cat(ktr[b].hi, ktr[b].lo);
+                    const f32x4 acc = mma32(ktt, dhh, S[b] * gmr[b]);
+                    S[b] = mma32(ktt, dll, acc);
+                }
+                // O = Q+ S + A_qk Delta
+                const bf16x8 aqq = cat(Aq.hi, Aq.lo);
+                f32x4 O = mma32(aqq, dhh, Oa);
+                O = mma32(aqq, dll, O);
+                O += Ob + Oc;
+                const int64_t t0 = bos + 16 * (int64_t)c;
+                const int n = chunk_len(c);
+                const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV, (uint32_t)n * rowO);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int t = 4 * g4 + jj;
+                    buf_store_f32(O[jj], ro, t < n ? t * rowO + (col0 + l16) * 4u : OOB);
+                }
+            };
+
+            // Chunk c uses operand set c & 1 and the inputs loaded three chunks
+            // earlier; the register sets rotate X0 -> X1 -> X2.
+            CIn X0, X1, X2;
+            cload(X0, 0);
+            cload(X1, clampc(1));
+            cload(X2, clampc(2));
+            __syncthreads();  // operand set 0 ready
+            auto citer = [&](int c, CIn &X) {
+                advance(c & 1, X, c);
+                cload(X, clampc(c + 3));
+                __syncthreads();  // set c+1 ready; set c free
+            };
+            for (int c = 0; c < nc; c += 3) {
+                citer(c, X0);
+                if (c + 1 >= nc) break;
+                citer(c + 1, X1);
+                if (c + 2 >= nc) break;
+                citer(c + 2, X2);
+            }
+        }
+        if (fin) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    fin[(hd * DK + 16 * b + 4 * g4 + jj) * DV + col0 + l16] = S[b][jj];
+        }
+    } else if (nc > 0) {
+        // ============================================================ producer
+        // Lane (g4, l16): token l16, channels 16 b + 4 g4 .. +3 of blocks
+        // b = pw * BPW + bi.
+        const int pw = wave - NC;
+        // Constant 0/1 triangles as matrix-core operands (bf16 1.0 = 0x3f80):
+        //   LT, B operand of G^T = g^T L^T: lane (g4, n) holds L[n][4 g4 + j] = [4 g4 + j <= n];
+        //   UT, A operand of Gs  = U g:     lane (g4, i) holds U[i][4 g4 + j] = [4 g4 + j >  i].
+        // G_r = sum_{t <= r} g_t is the cumulative log-decay, Gs_r = sum_{t > r} g_t = G_n - G_r.
+        u16x4 lt_bits, ut_bits;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lt_bits[j] = (4 * g4 + j <= l16) ? 0x3f80 : 0;
+            ut_bits[j] = (4 * g4 + j > l16) ? 0x3f80 : 0;
+        }
+        const bf16x4 LT = __builtin_bit_cast(bf16x4, lt_bits);
+        const bf16x4 UT = __builtin_bit_cast(bf16x4, ut_bits);
+        const bf16x4 ID = identity_operand(g4, l16);
+        // Per block b = pw * BPW + bi: q, k, g of token l16, channels 16 b + 4 g4 .. +3
+        // (the operand layout of Q+ and K+), one 8-byte load each.
+        struct PIn {
+            u32x2 q[BPW], k[BPW], g[BPW];
+        };
+        auto pload = [&](PIn &R, int c) {
+            const int n = chunk_len(c);
+            const rsrc_t rq = rsrc_in(q, c, DK), rk = rsrc_in(k, c, DK), rg = rsrc_in(g, c, DK);
+#pragma unroll
+            for (int bi = 0; bi < BPW; ++bi) {
+                const int b = pw * BPW + bi;
+                const uint32_t off = l16 < n ? l16 * rowK + (16 * b + 4 * g4) * EB : OOB;
+                R.q[bi] = buf_load_u32x2(rq, off);
+                R.k[bi] = buf_load_u32x2(rk, off);
+                R.g[bi] = buf_load_u32x2(rg, off);
+            }
+        };
+        auto produce = [&](const PIn &R, int ob) {
+            WsOps<DK> &P = ops[ob];
+#pragma unroll
+            for (int bi = 0; bi < BPW; ++bi) {
+                const int b = pw * BPW + bi;
+                // g and k as tokens 4 g4 + jj of channel 16 b + l16 (exact: bf16 values)
+                const bf16x4 ga = __builtin_bit_cast(bf16x4, R.g[bi]);
+                const f32x4 gt = mma16(ga, ID, zero4());
+                const f32x4 kc = mma16(__builtin_bit_cast(bf16x4, R.k[bi]), ID, zero4());
+                const bf16x4 gf = to_bf16x4(gt);
+                const f32x4 GT = mma16(gf, LT, zero4());   // G at token l16, channels 16 b + 4 g4 + jj
+                const f32x4 GS = mma16(UT, gf, zero4());   // Gs at tokens 4 g4 + jj, channel 16 b + l16
+                f32x4 Pp, F;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    Pp[j] = decay_exp_fast(GT[j]);   // e^{G_r}
+                    F[j] = decay_exp_fast(GS[j]);    // e^{G_n - G_r}
+                }
+                const Split4 qs = split4(unpack_bf16x4(R.q[bi]) * Pp);
+                bf16x4 *qh = reinterpret_cast<bf16x4 *>(&P.qp_hi[b >> 1][lane]) + (b & 1);
+                bf16x4 *ql = reinterpret_cast<bf16x4 *>(&P.qp_lo[b >> 1][lane]) + (b & 1);
+                bf16x4 *kh = reinterpret_cast<bf16x4 *>(&P.kp[b >> 1][lane]) + (b & 1);
+                *qh = qs.hi;
+                *ql = qs.lo;
+                *kh = to_bf16x4(unpack_bf16x4(R.k[bi]) * Pp);
+                P.kt[b][lane] = split4(kc * F);
+                if (l16 == 15) *reinterpret_cast<f32x4 *>(&P.gam[16 * b + 4 * g4]) = Pp;
+            }
+        };
+
+        // Iteration c builds the operands of chunk c+1 into set (c+1) & 1 from
+        // inputs loaded three chunks earlier; register sets rotate R1 -> R2 -> R0.
+        PIn R0, R1, R2;
+        pload(R0, 0);
+        pload(R1, clampc(1));
+        pload(R2, clampc(2));
+        produce(R0, 0);
+        pload(R0, clampc(3));
+        __syncthreads();  // operand set 0 ready
+        auto piter = [&](int c, PIn &R) {
+            produce(R, (c + 1) & 1);
+            pload(R, clampc(c + 4));
+            __syncthreads();
+        };
+        for (int c = 0; c < nc; c += 3) {
+            piter(c, R1);
+            if (c + 1 >= nc) break;
+            piter(c + 1, R2);
+            if (c + 2 >= nc) break;
+            piter(c + 2, R0);
+        }
+    }
+}
+
+template <int DK, int DV, int NC, int NP>
+static hipError_t launch_ws_t(const InterChunkArgs &a) {
+    const int nchains = a.nseq * a.H;
+    const int nsplit = DV / (16 * NC);
+    const int64_t grid = ((int64_t)nchains + 7) / 8 * 8 * nsplit;
+    hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP>), dim3((unsigned)grid),
+                       dim3(64 * (NC + NP)), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
+                       (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
+                       a.H, a.ws, a.o, a.fin, nsplit, nchains);
+    return hipGetLastError();
+}
+
+// Shapes: consumers NC (16 columns each), producers NP.  Returns
+// hipErrorInvalidValue for a shape that is not instantiated.
+hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw) {
+#define KDA_WS_CASE(DKV, DVV, NCV, NPV) \
+    if (a.dk == DKV && a.dv == DVV && ncw == NCV && npw == NPV) return launch_ws_t<DKV, DVV, NCV, NPV>(a);
+    // dk = dv = 128: the default shapes (4 or 2 consumers, 4 producers) and
+    // the others a tuning sweep may pick
+    KDA_WS_CASE(128, 128, 4, 4) KDA_WS_CASE(128, 128, 2, 4) KDA_WS_CASE(128, 128, 4, 2)
+    KDA_WS_CASE(128, 128, 1, 4) KDA_WS_CASE(128, 128, 2, 2) KDA_WS_CASE(128, 128, 1, 2)
+    // the other head sizes: min(dv/16, 4) or min(dv/16, 2) consumers, min(dk/16, 4) producers
+#define KDA_WS_DEF(DKV, DVV) KDA_WS_CASE(DKV, DVV, ((DVV / 16) < 4 ? (DVV / 16) : 4), ((DKV / 16) < 4 ? (DKV / 16) : 4))
+#define KDA_WS_DEF2(DKV, DVV) KDA_WS_CASE(DKV, DVV, ((DVV / 16) < 2 ? (DVV / 16) : 2), ((DKV / 16) < 4 ? (DKV / 16) : 4))
+#define KDA_WS_ROW(DKV) KDA_WS_DEF(DKV, 16) KDA_WS_DEF(DKV, 32) KDA_WS_DEF(DKV, 64) KDA_WS_DEF(DKV, 128) \
+    KDA_WS_DEF2(DKV, 64) KDA_WS_DEF2(DKV, 128)
+    KDA_WS_ROW(32) KDA_WS_ROW(64) KDA_WS_ROW(128)
+#undef KDA_WS_ROW
+#undef KDA_WS_DEF2
+#undef KDA_WS_DEF
+#undef KDA_WS_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -274,22 +274,27 @@ def test_bitwise_deterministic(dev):
     assert torch.equal(o1, o2) and torch.equal(st1, st2)
 
 
-def test_waves_per_group_variants_agree(dev, monkeypatch):
-    """The 2-, 4- and 8-wave workgroup shapes of the inter-chunk kernel each meet the bar and
-    agree with each other (the per-channel products are grouped differently per shape, so
-    only each shape on its own is bitwise reproducible)."""
+@pytest.mark.parametrize("knob,values", [
+    ("KDA_WAVES", ("2", "4", "8")),                          # one-role kernel
+    ("KDA_WS", ("4x4", "2x4", "4x2", "1x4", "2x2", "1x2")),  # consumer x producer waves
+])
+def test_workgroup_shape_variants_agree(dev, monkeypatch, knob, values):
+    """Every workgroup shape of both inter-chunk kernels meets the bar, is bitwise
+    reproducible on its own, and agrees with the other shapes (the per-channel decay sums
+    are grouped differently per shape, so shapes agree to the tolerance, not bitwise)."""
     w = workloads.custom([130, 64], 3, 128, 128, torch.bfloat16)
     x = workloads.prefill_inputs(w, device=dev, seed=10)
     o_ref, f_ref = oracle_prefill(x)
     outs = []
-    for nw in ("2", "4", "8"):
-        monkeypatch.setenv("KDA_WAVES", nw)
+    for val in values:
+        monkeypatch.setenv(knob, val)
+        say(f"{knob}={val}")
         outs.append(kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"]))
         again = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
         torch.cuda.synchronize()
         assert torch.equal(outs[-1][0], again[0]) and torch.equal(outs[-1][1], again[1])
-        assert_close(outs[-1][0], o_ref, TOL[torch.bfloat16], f"o (NW={nw})")
-        assert_close(outs[-1][1], f_ref, TOL[torch.bfloat16], f"final_state (NW={nw})")
+        assert_close(outs[-1][0], o_ref, TOL[torch.bfloat16], f"o ({knob}={val})")
+        assert_close(outs[-1][1], f_ref, TOL[torch.bfloat16], f"final_state ({knob}={val})")
     for o, f in outs[1:]:
         assert rel_err(o, outs[0][0].double().cpu().numpy()) <= TOL[torch.bfloat16]
         assert rel_err(f, outs[0][1].double().cpu().numpy()) <= TOL[torch.bfloat16]
