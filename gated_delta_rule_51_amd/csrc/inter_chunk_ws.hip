@@ -32,7 +32,10 @@
 // the decay unchanged, k = 0 removes them from every product).
 //
 // Precision as in inter_chunk.hip: K+ S single bf16, everything else split
-// bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation, fp32 state.
+// bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation, fp32 state.  The
+// residuals lo = x - hi of those splits are formed on the matrix cores (an
+// exact product with -I), which keeps the vector ALUs -- the busiest unit
+// here -- for the rest.
 #include <stdlib.h>
 
 #include "kda_device.hpp"
@@ -64,6 +67,27 @@ __device__ __forceinline__ bf16x4 identity_operand(int g4, int l16) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) bits[j] = (4 * g4 + j == l16) ? 0x3f80 : 0;
     return __builtin_bit_cast(bf16x4, bits);
+}
+
+// A operands of -I in one half of the 32-long contraction and 0 in the other:
+// with B = cat(hi_a, hi_b) (two bf16 tiles in the layout of the accumulator),
+// mma32(neg_identity_operand<0>, B, x) = x - hi_a and <1> gives x - hi_b.
+// With hi = x rounded to bf16 that difference is exactly representable, and
+// the matrix core forms it exactly (one nonzero product, fp32 accumulation):
+// the residual of a hi/lo bf16 split without vector-ALU unpacking.
+template <int HALF>
+__device__ __forceinline__ bf16x8 neg_identity_operand(int g4, int l16) {
+    u16x4 bits;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bits[j] = (4 * g4 + j == l16) ? 0xbf80 : 0;
+    const bf16x4 m = __builtin_bit_cast(bf16x4, bits), z = {};
+    return HALF == 0 ? cat(m, z) : cat(z, m);
+}
+// x = hi + lo in bf16, x in the accumulator layout; returns lo, sets hh = cat(hi, hi).
+__device__ __forceinline__ bf16x4 split_lo(f32x4 x, const bf16x8 &nil, bf16x8 &hh) {
+    const bf16x4 hi = to_bf16x4(x);
+    hh = cat(hi, hi);
+    return to_bf16x4(mma32(nil, hh, x));
 }
 
 template <int DK, int DV, int NC, int NP>
@@ -115,9 +139,6 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
 
     if (wave < NC) {
         // ============================================================ consumer
-        // The consumers carry the serial chain; when both roles are ready to
-        // issue on a SIMD, theirs go first and the producers fill the gaps.
-        __builtin_amdgcn_s_setprio(2);
         // State slice: rows 16 b + 4 g4 + jj, column col0 + l16 (accumulator layout).
         const int col0 = (split * NC + wave) * 16;
         f32x4 S[NB];
@@ -137,6 +158,7 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                 u32x2 v;
             };
             const bf16x4 ID = identity_operand(g4, l16);
+            const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
             auto cload = [&](CIn &X, int c) {
                 const float *wsc = ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
                 const rsrc_t rw = make_rsrc(wsc, WS_FLOATS_PER_CHUNK_HEAD * 4u);
@@ -162,14 +184,13 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                 const Split4 Tp = __builtin_bit_cast(Split4, X.tp);
                 const Split4 Aq = __builtin_bit_cast(Split4, X.aq);
                 const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, X.v), ID, zero4());
+                // S = Shi + Slo (bf16), residuals on the matrix cores
                 bf16x8 Shi[NPAIR], Slo[NPAIR];
 #pragma unroll
                 for (int p = 0; p < NPAIR; ++p) {
-                    const bf16x4 ah = to_bf16x4(S[2 * p]), bh = to_bf16x4(S[2 * p + 1]);
-                    const bf16x4 al = to_bf16x4(S[2 * p] - from_bf16x4(ah));
-                    const bf16x4 bl = to_bf16x4(S[2 * p + 1] - from_bf16x4(bh));
-                    Shi[p] = cat(ah, bh);
-                    Slo[p] = cat(al, bl);
+                    Shi[p] = cat(to_bf16x4(S[2 * p]), to_bf16x4(S[2 * p + 1]));
+                    Slo[p] = cat(to_bf16x4(mma32(NIL, Shi[p], S[2 * p])),
+                                 to_bf16x4(mma32(NIH, Shi[p], S[2 * p + 1])));
                 }
                 // X = K+ S (single bf16), two independent partial sums
                 f32x4 Xa = zero4(), Xb = zero4();
@@ -197,12 +218,13 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                     Oc = mma32(qhr[p], Slo[p], Oc);
                 }
                 // Delta = T' (V - X)
-                const Split4 Ys = split4(vc - (Xa + Xb));
+                bf16x8 yhh, dhh;
+                const bf16x4 ylo = split_lo(vc - (Xa + Xb), NIL, yhh);
                 const bf16x8 tpp = cat(Tp.hi, Tp.lo);
-                f32x4 D = mma32(tpp, cat(Ys.hi, Ys.hi), zero4());
-                D = mma32(tpp, cat(Ys.lo, Ys.lo), D);
-                const Split4 Ds = split4(D);
-                const bf16x8 dhh = cat(Ds.hi, Ds.hi), dll = cat(Ds.lo, Ds.lo);
+                f32x4 D = mma32(tpp, yhh, zero4());
+                D = mma32(tpp, cat(ylo, ylo), D);
+                const bf16x4 dlo = split_lo(D, NIL, dhh);
+                const bf16x8 dll = cat(dlo, dlo);
                 // S <- Diag(Gamma) S + K~^T Delta
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -270,6 +292,7 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
         const bf16x4 LT = __builtin_bit_cast(bf16x4, lt_bits);
         const bf16x4 UT = __builtin_bit_cast(bf16x4, ut_bits);
         const bf16x4 ID = identity_operand(g4, l16);
+        const bf16x8 NIL = neg_identity_operand<0>(g4, l16);
         // Per block b = pw * BPW + bi: q, k, g of token l16, channels 16 b + 4 g4 .. +3
         // (the operand layout of Q+ and K+), one 8-byte load each.
         struct PIn {
@@ -305,14 +328,18 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                     Pp[j] = decay_exp_fast(GT[j]);   // e^{G_r}
                     F[j] = decay_exp_fast(GS[j]);    // e^{G_n - G_r}
                 }
-                const Split4 qs = split4(unpack_bf16x4(R.q[bi]) * Pp);
+                // Q+ and K~ as hi + lo; both are in the accumulator layout (of Q+^T
+                // and of K~), so the residual comes from the matrix cores.
+                bf16x8 qhh, khh;
+                const bf16x4 qlo = split_lo(unpack_bf16x4(R.q[bi]) * Pp, NIL, qhh);
+                const bf16x4 klo = split_lo(kc * F, NIL, khh);
                 bf16x4 *qh = reinterpret_cast<bf16x4 *>(&P.qp_hi[b >> 1][lane]) + (b & 1);
                 bf16x4 *ql = reinterpret_cast<bf16x4 *>(&P.qp_lo[b >> 1][lane]) + (b & 1);
                 bf16x4 *kh = reinterpret_cast<bf16x4 *>(&P.kp[b >> 1][lane]) + (b & 1);
-                *qh = qs.hi;
-                *ql = qs.lo;
+                *qh = __builtin_shufflevector(qhh, qhh, 0, 1, 2, 3);
+                *ql = qlo;
                 *kh = to_bf16x4(unpack_bf16x4(R.k[bi]) * Pp);
-                P.kt[b][lane] = split4(kc * F);
+                P.kt[b][lane] = Split4{__builtin_shufflevector(khh, khh, 0, 1, 2, 3), klo};
                 if (l16 == 15) *reinterpret_cast<f32x4 *>(&P.gam[16 * b + 4 * g4]) = Pp;
             }
         };
