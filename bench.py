@@ -58,8 +58,8 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/inter_chunk.hip", "gated_delta_rule_51_amd/csrc/kda_device.hpp",
-                  "gated_delta_rule_51_amd/csrc/kda_launch.hpp")
+KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/inter_chunk.hip", "gated_delta_rule_51_amd/csrc/inter_chunk_ws.hip",
+                  "gated_delta_rule_51_amd/csrc/kda_device.hpp", "gated_delta_rule_51_amd/csrc/kda_launch.hpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "inter_chunk_batched_prefill_traffic.txt")
 
 
@@ -74,8 +74,9 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per inter-chunk launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary, or None when it is missing or was taken on different kernel sources."""
+    """(HBM bytes per inter-chunk launch, HIP kernel name) from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or (None, None) when it is missing or was taken on
+    different kernel sources."""
     try:
         fields = {}
         with open(TRAFFIC_SUMMARY) as f:
@@ -84,10 +85,10 @@ def measured_traffic():
                     key, val = line.split(":", 1)
                     fields[key.strip()] = val.strip()
         if fields.get("kernel_source_sha256_16") != kernel_source_hash():
-            return None
-        return float(fields["traffic_bytes_per_launch"])
+            return None, None
+        return float(fields["traffic_bytes_per_launch"]), fields.get("kernel")
     except (OSError, KeyError, ValueError):
-        return None
+        return None, None
 
 
 def copy_calibration(torch, dev, gib: float = 1.0, reps: int = 3) -> None:
@@ -333,10 +334,12 @@ def main() -> int:
         dom = max(("chunk_local", "inter_chunk"), key=lambda k: kernels[k])
         b = m["ic_bytes"] if dom == "inter_chunk" else m["cl_bytes"]
         ach = b / (kernels[dom] * 1e-3) / 1e9
+        traffic, hip_kernel = measured_traffic() if dom == "inter_chunk" else (None, None)
         out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": measured_traffic() if dom == "inter_chunk" else None,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                            "algorithmic_bytes_per_launch": b}
+        if hip_kernel:
+            out["roofline"]["hip_kernel"] = hip_kernel
         if not args.no_cpu_baseline:
             log("[bench] cpu baseline: fp64 oracle on the same batch")
             out["cpu_baseline"] = cpu_baseline(w)
