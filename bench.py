@@ -204,7 +204,7 @@ def bench_main(args, torch, kda, workloads, dev):
         "w": w, "wall_ms": wall_ms, "tokens": tokens, "ms_chunk_local": ms_cl, "ms_inter_chunk": ms_ic,
         "ms_decode": ms_dec, "prefill_tflops": flops / ((ms_cl + ms_ic) * 1e-3) / 1e12,
         "ic_bytes": th * inter_chunk_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4,
-        "cl_bytes": th * (2 * (2 * dk + dk + 1)) + (N // 16) * H * 2048 + (N // 32) * H * 2048,
+        "cl_bytes": th * (2 * (2 * dk + dk + 1)) + (N // 16 + nseq) * H * 2048,
     }
 
 

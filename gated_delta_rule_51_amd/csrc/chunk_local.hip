@@ -1,30 +1,17 @@
-// Chunk-local phase of the KDA prefill (gfx950): one wave per (pair of
-// consecutive 16-token chunks of a sequence, head), fully parallel.
+// Chunk-local phase of the KDA prefill (gfx950): one wave per (16-token
+// chunk, head), fully parallel.
 //
 // Chunked form (Kimi K3 report digest, "Kimi Delta Attention": the output of
 // chunk t is an inter-chunk term (Gamma (.) Q) S plus an intra-chunk term
-// A V~).  With G_r the inclusive cumulative log-decay of token r inside a
+// A V~).  With G_r the inclusive cumulative log-decay of token r inside the
 // chunk (per key channel), K+ = K (.) e^{G}, K- = K (.) e^{-G}, Q+ = Q (.) e^{G}:
 //     A_kk = diag(beta) * strictly_lower(K+ K-^T)      (16 x 16)
 //     T    = (I + A_kk)^{-1}                            (unit lower triangular)
 //     A_qk = lower_incl_diag(Q+ K-^T)                   (16 x 16)
-// The pseudo-keys W = T' K+ and pseudo-values U = T' V (T' = T diag(beta)) are
-// applied by the inter-chunk phase in the factored form Delta = T' (V - K+ S).
-//
-// Two chunks taken as one 32-token chunk have the block lower-triangular
-//     T'_32  = [[T'_0, 0], [T'_10, T'_1]],    A_qk,32 = [[A_qk,0, 0], [A_qk,10, A_qk,1]]
-// with, for K~_0 = K_0 (.) e^{G_0,15 - G_0} (keys decayed to the end of chunk
-// 0) and K+_1, Q+_1 taken from the start of chunk 1,
-//     S_10 = K+_1 K~_0^T,   T'_10 = -T'_1 S_10 T'_0,   A_qk,10 = Q+_1 K~_0^T
-// (from T_10 = -T_1 A_10 T_0 and A_10 = diag(beta_1) S_10).  Every decay factor
-// in these products is at most 1, so the 32-token step needs nothing outside
-// fp32 range.  This kernel writes, per chunk slot, T' and A_qk of the chunk
-// and, for the second chunk of a pair, the cross blocks T'_10 and A_qk,10, so
-// the inter-chunk phase can advance the state either 16 or 32 tokens at a time.
-// Workspace layout per (chunk slot, head), floats: [0, 256) T', [256, 512) A_qk,
-// [512, 768) T'_10, [768, 1024) A_qk,10, each 16 x 16 as the A-operand fragment
-// of the matrix-core product (lane 16 g + m holds row m, columns 4g .. 4g+3;
-// {hi[4], lo[4]} bf16 for bf16 inputs, 4 fp32 for fp32 inputs).
+// This kernel writes T' = T diag(beta) and A_qk to the workspace, as MFMA
+// A-operand fragments (split bf16 for bf16 inputs, fp32 for fp32 inputs).  The
+// pseudo-keys W = T' K+ and pseudo-values U = T' V are applied by the
+// inter-chunk phase in the factored form Delta = T' (V - K+ S) = U - W S.
 //
 // Bounded decay (same page, "bounded decay" section): g >= -5, so over a
 // 16-token chunk G lies in [-80, 0] and e^{-G} <= e^80 stays inside fp32/bf16
@@ -33,9 +20,9 @@
 // products of e^{+-g} (no exp of a large argument).
 //
 // Precision: A_kk uses single-bf16 operands (its rounding error is damped by
-// the triangular solve); A_qk and the cross products use split-bf16 operands
-// (hi*hi + lo*hi + hi*lo, ~16-bit mantissas); the triangular solves and
-// T'_10 are fp32.  fp32 inputs use fp32 MFMAs throughout.
+// the triangular solve); A_qk uses split-bf16 operands (hi*hi + lo*hi + hi*lo,
+// ~16-bit mantissas) because it feeds the output directly.  fp32 inputs use
+// fp32 MFMAs throughout.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -49,216 +36,153 @@ __global__ __launch_bounds__(64) void chunk_local_kernel(
     constexpr bool F32 = sizeof(T) == 4;
     constexpr int NB = DK / 16;
     constexpr int LD = DK + 4;  // padded LDS row (floats)
-    const int64_t pslot = blockIdx.x;
+    const int64_t slot = blockIdx.x;
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
 
-    // Which sequence owns this pair slot: the largest s with floor(cu[s]/32) + s <= pslot.
-    // (Sequence s owns pair slots floor(cu[s]/32) + s + p, p < ceil(len_s / 32): an
-    // injective map into floor(N/32) + nseq slots.)
+    // Which sequence owns this slot: the largest s with floor(cu[s]/16) + s <= slot.
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)(cu[mid] / 32) + mid <= pslot) lo = mid;
+        if ((int64_t)(cu[mid] / 16) + mid <= slot) lo = mid;
         else hi = mid - 1;
     }
     const int s = lo;
     const int64_t bos = cu[s], eos = cu[s + 1];
-    const int64_t p = pslot - ((int64_t)(bos / 32) + s);
-    if (p < 0 || 32 * p >= eos - bos) return;  // slot not used by any pair
-    const int64_t tp = bos + 32 * p;           // first token of the pair
-    const int n0 = (int)((eos - tp) < 16 ? (eos - tp) : 16);
-    const int64_t left1 = eos - tp - 16;
-    const int n1 = (int)(left1 <= 0 ? 0 : (left1 < 16 ? left1 : 16));
-    const int64_t cslot = bos / 16 + s + 2 * p;  // chunk slot of the pair's first chunk
+    const int64_t j = slot - ((int64_t)(bos / 16) + s);
+    if (j < 0 || 16 * j >= eos - bos) return;  // slot not used by any chunk
+    const int64_t t0 = bos + 16 * j;
+    const int n = (int)((eos - t0) < 16 ? (eos - t0) : 16);
 
-    __shared__ float sP[2][16][LD];     // e^{G_r}   (running product of alpha), per chunk
-    __shared__ float sPi[2][16][LD];    // e^{-G_r}
-    __shared__ float sA[2][16][17];     // A_kk, then T'
-    __shared__ float sAq[2][16][17];    // A_qk
-    __shared__ float sX[16][17];        // S_10, then S_10 T'_0
-    __shared__ float sAx[16][17];       // A_qk,10
-    __shared__ float sBeta[2][16];
+    __shared__ float sP[16][LD];     // e^{G_r}   (running product of alpha)
+    __shared__ float sPi[16][LD];    // e^{-G_r}
+    __shared__ float sA[16][17];
+    __shared__ float sBeta[16];
 
-    // Row r of chunk u is a real token when r < n_u.  Loads of padding rows read a
-    // real row of the pair (results replaced by zeros), so no load leaves the tensors.
-    auto tok = [&](int u, int r) -> int64_t {
-        const int nu = u ? n1 : n0;
-        return nu > 0 ? tp + 16 * u + (r < nu ? r : nu - 1) : tp;
-    };
-
-    // Per (chunk, key channel): running products over the chunk's tokens (pads: g = 0).
-    for (int e = lane; e < 2 * DK; e += 64) {
-        const int u = e / DK, c = e % DK;
-        const int nu = u ? n1 : n0;
+    // Per key channel: running products over the chunk's tokens (pads: g = 0).
+    // Unconditional loads from clamped rows (n >= 1), padding zeroed by a select.
+    for (int c = lane; c < DK; c += 64) {
         float gv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float x = load_in(g + (tok(u, r) * H + h) * DK + c);
-            gv[r] = (r < nu) ? x : 0.f;
+            const float x = load_in(g + ((t0 + (r < n ? r : n - 1)) * H + h) * DK + c);
+            gv[r] = (r < n) ? x : 0.f;
         }
-        float pr = 1.f, pi = 1.f;
+        float p = 1.f, pi = 1.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             if constexpr (F32) {
-                pr *= decay_exp(gv[r]);
+                p *= decay_exp(gv[r]);
                 pi *= decay_exp(-gv[r]);
             } else {
-                pr *= decay_exp_fast(gv[r]);
+                p *= decay_exp_fast(gv[r]);
                 pi *= decay_exp_fast(-gv[r]);
             }
-            sP[u][r][c] = pr;
-            sPi[u][r][c] = pi;
+            sP[r][c] = p;
+            sPi[r][c] = pi;
         }
     }
-    if (lane < 32) {
-        const int u = lane >> 4, r = lane & 15;
-        const float b = load_in(beta + tok(u, r) * H + h);
-        sBeta[u][r] = (r < (u ? n1 : n0)) ? b : 0.f;
+    if (lane < 16) {
+        const float b = load_in(beta + (t0 + (lane < n ? lane : n - 1)) * H + h);
+        sBeta[lane] = (lane < n) ? b : 0.f;
     }
     __syncthreads();
 
     // Operands in the A/B fragment layout: lane (g4, m) holds token m, channels
-    // 16b + 4*g4 + 0..3 of K+, K-, Q+ (per chunk) and of K~_0 = K-_0 (.) e^{G_0,15}.
+    // 16b + 4*g4 + 0..3 of K+, K-, Q+.
     const int m = lane & 15, g4 = lane >> 4;
-    struct Ops {
-        f32x4 kp, km, qp;
-    };
-    auto operands = [&](int u, int b) {
-        const int nu = u ? n1 : n0;
-        const bool valid = m < nu;
-        const int64_t row = tok(u, m);
+    const bool valid = m < n;
+    const int64_t mrow = t0 + (valid ? m : n - 1);
+    const T *krow = k + (mrow * H + h) * DK;
+    const T *qrow = q + (mrow * H + h) * DK;
+    f32x4 akk = zero4(), aqk = zero4();
+    auto operands = [&](int b, f32x4 &kp, f32x4 &km, f32x4 &qp) {
         const int c = 16 * b + 4 * g4;
-        const f32x4 kl = load_in4(k + (row * H + h) * DK + c);
-        const f32x4 ql = load_in4(q + (row * H + h) * DK + c);
+        const f32x4 kl = load_in4(krow + c);
+        const f32x4 ql = load_in4(qrow + c);
         const f32x4 kk = valid ? kl : zero4();
         const f32x4 qq = valid ? ql : zero4();
-        const f32x4 P = *reinterpret_cast<const f32x4 *>(&sP[u][m][c]);
-        const f32x4 Pi = *reinterpret_cast<const f32x4 *>(&sPi[u][m][c]);
-        return Ops{kk * P, kk * Pi, qq * P};
+        const f32x4 P = *reinterpret_cast<const f32x4 *>(&sP[m][c]);
+        const f32x4 Pi = *reinterpret_cast<const f32x4 *>(&sPi[m][c]);
+        kp = kk * P;
+        km = kk * Pi;
+        qp = qq * P;
     };
-    auto decayed_to_end = [&](const Ops &o0, int b) {  // K~_0 for block b
-        return o0.km * *reinterpret_cast<const f32x4 *>(&sP[0][15][16 * b + 4 * g4]);
-    };
-    f32x4 akk0 = zero4(), aqk0 = zero4(), akk1 = zero4(), aqk1 = zero4();
-    f32x4 s10 = zero4(), aq10 = zero4();
     if constexpr (F32) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const Ops o0 = operands(0, b), o1 = operands(1, b);
-            const f32x4 kt0 = decayed_to_end(o0, b);
-            akk0 = mma_f32_k16(o0.kp, o0.km, akk0);
-            aqk0 = mma_f32_k16(o0.qp, o0.km, aqk0);
-            akk1 = mma_f32_k16(o1.kp, o1.km, akk1);
-            aqk1 = mma_f32_k16(o1.qp, o1.km, aqk1);
-            s10 = mma_f32_k16(o1.kp, kt0, s10);
-            aq10 = mma_f32_k16(o1.qp, kt0, aq10);
+            f32x4 kp, km, qp;
+            operands(b, kp, km, qp);
+            akk = mma_f32_k16(kp, km, akk);
+            aqk = mma_f32_k16(qp, km, aqk);
         }
     } else if constexpr (NB == 1) {
-        const Ops o0 = operands(0, 0), o1 = operands(1, 0);
-        const Split4 kt0 = split4(decayed_to_end(o0, 0));
-        const Split4 km0 = split4(o0.km), km1 = split4(o1.km);
-        akk0 = mma16(to_bf16x4(o0.kp), to_bf16x4(o0.km), akk0);
-        aqk0 = mma_split_k16(split4(o0.qp), km0, aqk0);
-        akk1 = mma16(to_bf16x4(o1.kp), to_bf16x4(o1.km), akk1);
-        aqk1 = mma_split_k16(split4(o1.qp), km1, aqk1);
-        s10 = mma_split_k16(split4(o1.kp), kt0, s10);
-        aq10 = mma_split_k16(split4(o1.qp), kt0, aq10);
+        f32x4 kp, km, qp;
+        operands(0, kp, km, qp);
+        akk = mma16(to_bf16x4(kp), to_bf16x4(km), akk);
+        aqk = mma_split_k16(split4(qp), split4(km), aqk);
     } else {
 #pragma unroll
         for (int b = 0; b < NB; b += 2) {
-            const Ops a0 = operands(0, b), b0 = operands(0, b + 1);
-            const Ops a1 = operands(1, b), b1 = operands(1, b + 1);
-            const Split4 ktA = split4(decayed_to_end(a0, b)), ktB = split4(decayed_to_end(b0, b + 1));
-            akk0 = mma_single_k32(to_bf16x4(a0.kp), to_bf16x4(b0.kp), to_bf16x4(a0.km), to_bf16x4(b0.km), akk0);
-            aqk0 = mma_split_k32(split4(a0.qp), split4(b0.qp), split4(a0.km), split4(b0.km), aqk0);
-            akk1 = mma_single_k32(to_bf16x4(a1.kp), to_bf16x4(b1.kp), to_bf16x4(a1.km), to_bf16x4(b1.km), akk1);
-            aqk1 = mma_split_k32(split4(a1.qp), split4(b1.qp), split4(a1.km), split4(b1.km), aqk1);
-            s10 = mma_split_k32(split4(a1.kp), split4(b1.kp), ktA, ktB, s10);
-            aq10 = mma_split_k32(split4(a1.qp), split4(b1.qp), ktA, ktB, aq10);
+            f32x4 kp0, km0, qp0, kp1, km1, qp1;
+            operands(b, kp0, km0, qp0);
+            operands(b + 1, kp1, km1, qp1);
+            akk = mma_single_k32(to_bf16x4(kp0), to_bf16x4(kp1), to_bf16x4(km0), to_bf16x4(km1), akk);
+            aqk = mma_split_k32(split4(qp0), split4(qp1), split4(km0), split4(km1), aqk);
         }
     }
 
     // Accumulator lane (g4, i) holds rows r = 4*g4 + jj of column i.
+    __shared__ float sAq[16][17];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int r = 4 * g4 + jj, i = m;
-        sA[0][r][i] = (r > i) ? sBeta[0][r] * akk0[jj] : 0.f;
-        sAq[0][r][i] = (r >= i) ? aqk0[jj] : 0.f;
-        sA[1][r][i] = (r > i) ? sBeta[1][r] * akk1[jj] : 0.f;
-        sAq[1][r][i] = (r >= i) ? aqk1[jj] : 0.f;
-        sX[r][i] = s10[jj];
-        sAx[r][i] = aq10[jj];
+        sA[r][i] = (r > i) ? sBeta[r] * akk[jj] : 0.f;
+        sAq[r][i] = (r >= i) ? aqk[jj] : 0.f;
     }
     __syncthreads();
 
-    // T = (I + A_kk)^{-1} by forward substitution, both chunks at once: lane
-    // 16u + c builds column c of chunk u's T:
+    // T = (I + A_kk)^{-1} by forward substitution; lane c builds column c:
     // T[r][c] = [r == c] - sum_{i < r} A[r][i] T[i][c]  (T[i][c] = 0 for i < c).
-    // T' = T diag(beta) then overwrites A_kk in LDS (every lane has read it by then).
+    // T' = T diag(beta) overwrites A_kk in LDS (every lane has read it by then).
     float t[16];
-    const int su = (lane >> 4) & 1, sc = lane & 15;
-    if (lane < 32) {
+    if (lane < 16) {
+        const int c = lane;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < r; ++i) acc += sA[su][r][i] * t[i];
-            t[r] = ((r == sc) ? 1.f : 0.f) - acc;
+            for (int i = 0; i < r; ++i) acc += sA[r][i] * t[i];
+            t[r] = ((r == c) ? 1.f : 0.f) - acc;
         }
     }
     __syncthreads();
-    if (lane < 32) {
-        const float bc = sBeta[su][sc];
+    if (lane < 16) {
+        const float bc = sBeta[lane];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sA[su][r][sc] = t[r] * bc;
+        for (int r = 0; r < 16; ++r) sA[r][lane] = t[r] * bc;
     }
     __syncthreads();
 
-    // Cross block T'_10 = -T'_1 (S_10 T'_0), fp32; lane (g4, m) forms row m,
-    // columns 4*g4 .. +3 (the fragment layout it is stored in).
-    f32x4 t10 = zero4();
-    if (n1 > 0) {
-        f32x4 y = zero4();
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            y += sX[m][i] * f32x4{sA[0][i][4 * g4], sA[0][i][4 * g4 + 1], sA[0][i][4 * g4 + 2],
-                                  sA[0][i][4 * g4 + 3]};
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sX[m][4 * g4 + j] = y[j];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            t10 -= sA[1][m][i] * f32x4{sX[i][4 * g4], sX[i][4 * g4 + 1], sX[i][4 * g4 + 2], sX[i][4 * g4 + 3]};
-    }
-
-    // Store T' and A_qk (and the cross blocks for the second chunk) as A-operand
-    // fragments of the 16x16 MFMA: lane (g4, m) holds M[m][4*g4 + 0..3] -- split
-    // {hi, lo} bf16 for bf16 inputs, fp32 for fp32 inputs -- so the inter-chunk
-    // phase loads each with one 16-byte read per lane.
-    auto row4 = [&](const float (*M)[17]) {
-        return f32x4{M[m][4 * g4], M[m][4 * g4 + 1], M[m][4 * g4 + 2], M[m][4 * g4 + 3]};
-    };
-    auto put = [&](float *dst, f32x4 v) {
-        if constexpr (F32) reinterpret_cast<f32x4 *>(dst)[lane] = v;
-        else reinterpret_cast<Split4 *>(dst)[lane] = split4(v);
-    };
-    float *w0 = ws + (cslot * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
-    put(w0, row4(sA[0]));
-    put(w0 + 256, row4(sAq[0]));
-    if (n1 > 0) {
-        float *w1 = ws + ((cslot + 1) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
-        put(w1, row4(sA[1]));
-        put(w1 + 256, row4(sAq[1]));
-        put(w1 + 512, t10);
-        put(w1 + 768, row4(sAx));
+    // Store T' and A_qk as A-operand fragments of the 16x16 MFMA: lane (g4, m)
+    // holds M[m][4*g4 + 0..3] -- split {hi, lo} bf16 for bf16 inputs, fp32 for
+    // fp32 inputs -- so the inter-chunk phase loads them with one 16-byte read
+    // per lane.
+    const f32x4 tv = {sA[m][4 * g4], sA[m][4 * g4 + 1], sA[m][4 * g4 + 2], sA[m][4 * g4 + 3]};
+    const f32x4 av = {sAq[m][4 * g4], sAq[m][4 * g4 + 1], sAq[m][4 * g4 + 2], sAq[m][4 * g4 + 3]};
+    float *w = ws + (slot * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
+    if constexpr (F32) {
+        reinterpret_cast<f32x4 *>(w)[lane] = tv;
+        reinterpret_cast<f32x4 *>(w + 256)[lane] = av;
+    } else {
+        reinterpret_cast<Split4 *>(w)[lane] = split4(tv);
+        reinterpret_cast<Split4 *>(w + 256)[lane] = split4(av);
     }
 }
 
 template <int DK, typename T>
 static hipError_t launch_cl_t(const ChunkLocalArgs &a) {
-    const int64_t slots = pair_slots(a.total_tokens, a.nseq);
+    const int64_t slots = chunk_slots(a.total_tokens, a.nseq);
     hipLaunchKernelGGL((chunk_local_kernel<DK, T>), dim3((unsigned)slots, (unsigned)a.H), dim3(64), 0,
                        (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.g,
                        (const T *)a.beta, a.cu, a.nseq, a.H, a.ws);

@@ -8,20 +8,15 @@
 
 namespace kda {
 
-// Workspace per (chunk slot, head): T' = (I + A_kk)^-1 diag(beta), A_qk, and --
-// for the second chunk of a pair -- the cross blocks T'_10 and A_qk,10 that
-// join it to the chunk before (see chunk_local.hip), each stored as the
-// A-operand fragment of a 16x16 MFMA (64 lanes x 16 bytes: lane 16g + m holds
-// row m, columns 4g..4g+3; as {hi[4], lo[4]} bf16 for bf16 inputs, as 4 fp32
-// for fp32 inputs).  4 KiB per (chunk slot, head).
-constexpr int WS_FLOATS_PER_CHUNK_HEAD = 4 * 16 * 16;
+// Workspace per (chunk slot, head): T' = (I + A_kk)^-1 diag(beta), then A_qk,
+// each stored as the A-operand fragment of a 16x16 MFMA (64 lanes x 16 bytes:
+// lane 16g + m holds row m, columns 4g..4g+3; as {hi[4], lo[4]} bf16 for bf16
+// inputs, as 4 fp32 for fp32 inputs).  2 KiB per (chunk slot, head).
+constexpr int WS_FLOATS_PER_CHUNK_HEAD = 2 * 16 * 16;
 
 // Chunk slots: sequence s owns slots floor(cu[s]/16) + s + j, j < ceil(len_s/16).
 // The map is injective and bounded by floor(N/16) + nseq.
 inline int64_t chunk_slots(int64_t total_tokens, int32_t nseq) { return total_tokens / 16 + nseq; }
-// Pair slots (one chunk-local wave each): sequence s owns floor(cu[s]/32) + s + p,
-// p < ceil(len_s/32); bounded by floor(N/32) + nseq.
-inline int64_t pair_slots(int64_t total_tokens, int32_t nseq) { return total_tokens / 32 + nseq; }
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;

@@ -88,13 +88,10 @@ typedef enum kda_dtype {
 
 /* Bytes of device workspace kda_prefill / kda_chunk_local / kda_inter_chunk
  * need: per chunk slot and head, the 16x16 matrices T' = (I + A_kk)^-1
- * diag(beta) and A_qk of the chunk, plus -- for the second chunk of each pair
- * of consecutive chunks of a sequence -- the blocks T'_10 and A_qk,10 that join
- * it to the chunk before (the off-diagonal blocks of the same matrices taken
- * over the 32 tokens of the pair), each as a 1 KiB matrix-core operand fragment
- * (a hi/lo bfloat16 pair per element for KDA_BF16, fp32 for KDA_F32): 4 KiB
- * per slot, for floor(N/16) + nseq chunk slots.  The layout is private to the
- * library.  Returns 0 for invalid arguments. */
+ * diag(beta) and A_qk, each as a 1 KiB matrix-core operand fragment (a
+ * hi/lo bfloat16 pair per element for KDA_BF16, fp32 for KDA_F32), for
+ * floor(N/16) + nseq chunk slots.  The layout is private to the library.
+ * Returns 0 for invalid arguments. */
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype dt);
 

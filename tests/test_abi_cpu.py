@@ -52,8 +52,8 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     # floor(N/16) + nseq chunk slots, 2 KiB per slot and head
-    assert kda.kda_prefill_workspace_bytes(65536, 1, 96, 128, 128) == (4096 + 1) * 96 * 4096
-    assert kda.kda_prefill_workspace_bytes(0, 3, 2, 16, 16) == 3 * 2 * 4096
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 96, 128, 128) == (4096 + 1) * 96 * 2048
+    assert kda.kda_prefill_workspace_bytes(0, 3, 2, 16, 16) == 3 * 2 * 2048
     assert kda.kda_prefill_workspace_bytes(64, 1, 1, 24, 16) == 0   # unsupported dk
     assert kda.kda_prefill_workspace_bytes(64, 0, 1, 16, 16) == 0   # nseq < 1
     assert kda.kda_prefill_workspace_bytes(-1, 1, 1, 16, 16) == 0

@@ -48,26 +48,24 @@ def _prefill_case(dev, seqlens, H, dk, dv, dtype, seed=0, gate="neg_softplus", i
 # ----------------------------------------------------------------- chunk-local phase
 
 def decode_workspace(ws, H, dtype):
-    """The workspace holds, per (chunk slot, head), T', A_qk, T'_10, A_qk,10 as 16x16 MFMA
-    A-operand fragments: lane 16g + m holds row m, columns 4g..4g+3 ({hi[4], lo[4]} bf16 for
-    bf16 inputs, 4 fp32 for fp32 inputs).  Returns [slots, H, 4, 16, 16] float64."""
+    """The workspace holds, per (chunk slot, head), T' then A_qk as 16x16 MFMA A-operand
+    fragments: lane 16g + m holds row m, columns 4g..4g+3 ({hi[4], lo[4]} bf16 for bf16
+    inputs, 4 fp32 for fp32 inputs).  Returns [slots, H, 2, 16, 16] float64."""
     if dtype == torch.float32:
-        fr = ws.cpu().double().numpy().reshape(-1, H, 4, 4, 16, 4)           # [.., g, m, j]
+        fr = ws.cpu().double().numpy().reshape(-1, H, 2, 4, 16, 4)           # [.., g, m, j]
     else:
-        b = ws.cpu().view(torch.bfloat16).double().numpy().reshape(-1, H, 4, 4, 16, 8)
+        b = ws.cpu().view(torch.bfloat16).double().numpy().reshape(-1, H, 2, 4, 16, 8)
         fr = b[..., :4] + b[..., 4:]
     # M[m][4g + j] = fr[g][m][j]
-    return np.ascontiguousarray(fr.transpose(0, 1, 2, 4, 3, 5)).reshape(fr.shape[0], H, 4, 16, 16)
+    return np.ascontiguousarray(fr.transpose(0, 1, 2, 4, 3, 5)).reshape(fr.shape[0], H, 2, 16, 16)
 
 
 @pytest.mark.parametrize("dtype,dk", [(torch.float32, 16), (torch.float32, 128),
-                                      (torch.bfloat16, 16), (torch.bfloat16, 64), (torch.bfloat16, 128)])
+                                      (torch.bfloat16, 64), (torch.bfloat16, 128)])
 def test_chunk_local_matches_chunked_model(dev, dtype, dk):
-    """Kernel 1's T' = (I + A_kk)^-1 diag(beta) and A_qk for every chunk, and the cross
-    blocks T'_10, A_qk,10 of every pair of consecutive chunks, against the fp64 chunked-form
-    model on the same (rounded) inputs.  The cross blocks are checked as the lower-left
-    blocks of the model's T' and A_qk over the pair's 32 tokens taken as one chunk."""
-    seqlens, H = [40, 16, 7, 64, 50], 2
+    """Kernel 1's T' = (I + A_kk)^-1 diag(beta) and A_qk for every chunk against the fp64
+    chunked-form model on the same (rounded) inputs."""
+    seqlens, H = [40, 16, 7], 2
     w = workloads.custom(seqlens, H, dk, 16, dtype)
     x = workloads.prefill_inputs(w, device=dev, seed=3)
     say(f"  case: chunk_local dk={dk} {dtype}")
@@ -83,10 +81,6 @@ def test_chunk_local_matches_chunked_model(dev, dtype, dk):
     cu = workloads.cu_seqlens_of(seqlens)
     tol_t = 1e-5 if dtype == torch.float32 else 2e-2
     tol_a = 1e-5 if dtype == torch.float32 else 1e-3
-
-    def err(got, ref):
-        return np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30)
-
     for (s, h, j), loc in kept.items():
         slot = cu[s] // 16 + s + j
         n = loc["Tp"].shape[0]
@@ -94,21 +88,10 @@ def test_chunk_local_matches_chunked_model(dev, dtype, dk):
         Tp[:n, :n] = loc["Tp"]
         Aq = np.zeros((16, 16))
         Aq[:n, :n] = loc["Aqk"]
-        eT, eA = err(wsn[slot, h, 0], Tp), err(wsn[slot, h, 1], Aq)
+        gT, gA = wsn[slot, h, 0], wsn[slot, h, 1]
+        eT = np.max(np.abs(gT - Tp)) / np.max(np.abs(Tp))
+        eA = np.max(np.abs(gA - Aq)) / np.max(np.abs(Aq))
         assert eT <= tol_t and eA <= tol_a, f"chunk (s={s},h={h},j={j}): T' err {eT:.2e}, A_qk err {eA:.2e}"
-        if j % 2 == 1:  # second chunk of a pair: cross blocks against the 32-token model
-            t0 = cu[s] + 16 * (j - 1)
-            t1 = min(cu[s + 1], t0 + 32)
-            pair = chunk_model.chunk_local(cpu["q"][t0:t1, h], cpu["k"][t0:t1, h],
-                                           cpu["log_alpha"][t0:t1, h], cpu["beta"][t0:t1, h])
-            n1 = t1 - t0 - 16
-            Tx = np.zeros((16, 16))
-            Tx[:n1] = pair["Tp"][16:, :16]
-            Ax = np.zeros((16, 16))
-            Ax[:n1] = pair["Aqk"][16:, :16]
-            eTx, eAx = err(wsn[slot, h, 2], Tx), err(wsn[slot, h, 3], Ax)
-            assert eTx <= tol_t and eAx <= tol_a, \
-                f"pair (s={s},h={h},j={j - 1},{j}): T'_10 err {eTx:.2e}, A_qk,10 err {eAx:.2e}"
 
 
 # ----------------------------------------------------------------- the five workloads
