@@ -19,6 +19,10 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libkda_mi355x.so")
 SOURCES = ["api.cpp", "decode.hip", "chunk_local.hip", "inter_chunk.hip", "inter_chunk_ws.hip"]
 ARCH = "gfx950"
+# Per-file additions.  chunk_local: matrix-core results in VGPRs (not AGPRs) --
+# every result there is read by the vector ALU next, and the accumulator-register
+# form cost a move per element.
+EXTRA_FLAGS = {"chunk_local.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -36,7 +40,7 @@ def flags() -> list:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     res = subprocess.run(cmd, capture_output=True, text=True)

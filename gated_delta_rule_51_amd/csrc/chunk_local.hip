@@ -1,5 +1,7 @@
 // Chunk-local phase of the KDA prefill (gfx950): one wave per (16-token
-// chunk, head), fully parallel.
+// chunk, head), fully parallel.  Two kernels with the same outputs: one for
+// fp32 inputs (fp32 matrix cores, running products of e^{+-g}), and one for
+// bf16 inputs laid out for the bf16 matrix cores (described above it).
 //
 // Chunked form (Kimi K3 report digest, "Kimi Delta Attention": the output of
 // chunk t is an inter-chunk term (Gamma (.) Q) S plus an intra-chunk term
@@ -29,7 +31,7 @@
 namespace kda {
 
 template <int DK, typename T>
-__global__ __launch_bounds__(64) void chunk_local_kernel(
+__global__ __launch_bounds__(64) void chunk_local_f32_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ g,
     const T *__restrict__ beta, const int32_t *__restrict__ cu, int32_t nseq, int32_t H,
     float *__restrict__ ws) {
@@ -180,12 +182,192 @@ __global__ __launch_bounds__(64) void chunk_local_kernel(
     }
 }
 
+
+// bf16 inputs.  Same outputs; the work is laid out for the matrix cores:
+//   * q, k, g of the chunk are read through buffer resources based at the
+//     chunk's first token (8-byte loads of 4 channels of one token per lane --
+//     the A-operand layout of K+, K-, Q+; padding rows read as zeros);
+//   * the cumulative log-decay G is a product with the 0/1 lower triangle,
+//     G^T = g^T L^T, after an identity product turns g into 4 tokens of one
+//     channel per lane (both exact: g is bf16), so e^{+-G} = exp(+-G) need no
+//     per-token running products and no LDS round trip (|G| <= 80);
+//   * the hi/lo splits of Q+ and K- take their residuals from the matrix core
+//     (an exact product with -I) instead of vector-ALU unpacking;
+//   * the triangular solve reads the rows of A_kk as 16-byte vectors.
+template <int DK>
+__global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ g,
+    const __bf16 *__restrict__ beta, const int32_t *__restrict__ cu, int32_t nseq, int32_t H,
+    float *__restrict__ ws) {
+    constexpr int NB = DK / 16;
+    constexpr uint32_t EB = 2;
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x;
+
+    // Which sequence owns this slot: the largest s with floor(cu[s]/16) + s <= slot.
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)(cu[mid] / 16) + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int s = lo;
+    const int64_t bos = cu[s], eos = cu[s + 1];
+    const int64_t j = slot - ((int64_t)(bos / 16) + s);
+    if (j < 0 || 16 * j >= eos - bos) return;  // slot not used by any chunk
+    const int64_t t0 = bos + 16 * j;
+    const int n = (int)((eos - t0) < 16 ? (eos - t0) : 16);
+
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const uint32_t rowK = (uint32_t)H * DK * EB;
+    const rsrc_t rq = make_rsrc(q + (t0 * H + h) * DK, (uint32_t)n * rowK);
+    const rsrc_t rk = make_rsrc(k + (t0 * H + h) * DK, (uint32_t)n * rowK);
+    const rsrc_t rg = make_rsrc(g + (t0 * H + h) * DK, (uint32_t)n * rowK);
+    const rsrc_t rb = make_rsrc(beta + t0 * H + h, (uint32_t)n * (uint32_t)H * EB);
+
+    __shared__ __attribute__((aligned(16))) float sA[16][20];   // A_kk, then T'
+    __shared__ __attribute__((aligned(16))) float sAq[16][20];  // A_qk
+    __shared__ float sBeta[16];
+
+    // All loads first: token l16, channels 16 b + 4 g4 .. +3 of q, k, g.
+    const uint32_t row = l16 < n ? l16 * rowK : OOB;
+    u32x2 gr[NB], kr[NB], qr[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint32_t o = row == OOB ? OOB : row + (16 * b + 4 * g4) * EB;
+        gr[b] = buf_load_u32x2(rg, o);
+        kr[b] = buf_load_u32x2(rk, o);
+        qr[b] = buf_load_u32x2(rq, o);
+    }
+    if (lane < 16) sBeta[lane] = bf16_bits_to_f32(buf_load_u16(rb, lane < n ? lane * (uint32_t)H * EB : OOB));
+
+    // Constant operands.  Channel blocks are handled in pairs, so every 32-long
+    // operand carries two blocks' data; a constant B with the wanted matrix in
+    // one half and 0 in the other (or -I in one half of A) selects the block.
+    const bf16x4 z4 = {};
+    const bf16x4 ID = identity_operand(g4, l16);
+    u16x4 lt_bits;  // L^T: lane (g4, n) holds L[n][4 g4 + j] = [4 g4 + j <= n]
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) lt_bits[jj] = (4 * g4 + jj <= l16) ? 0x3f80 : 0;
+    const bf16x4 LT = __builtin_bit_cast(bf16x4, lt_bits);
+    const bf16x8 IDL = cat(ID, z4), IDH = cat(z4, ID), LTL = cat(LT, z4), LTH = cat(z4, LT);
+    const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
+
+    // Operands of blocks b0, b1 (token l16, channels 16 b + 4 g4 + jj):
+    // K+ = K e^{G}, K- = K e^{-G}, Q+ = Q e^{G}.
+    struct Pair {
+        f32x4 kp[2], km[2], qp[2];
+    };
+    auto operands = [&](int b0, int b1) {
+        const bf16x8 ga = cat(__builtin_bit_cast(bf16x4, gr[b0]), __builtin_bit_cast(bf16x4, gr[b1]));
+        // g as 4 tokens of one channel per lane, then G^T = g^T L^T (both exact)
+        const bf16x8 gf = cat(to_bf16x4(mma32(ga, IDL, zero4())), to_bf16x4(mma32(ga, IDH, zero4())));
+        const f32x4 G[2] = {mma32(gf, LTL, zero4()), mma32(gf, LTH, zero4())};
+        Pair r;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 P, Pi;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                P[jj] = decay_exp_fast(G[u][jj]);
+                Pi[jj] = decay_exp_fast(-G[u][jj]);
+            }
+            const f32x4 kk = unpack_bf16x4(kr[u ? b1 : b0]);
+            r.kp[u] = kk * P;
+            r.km[u] = kk * Pi;
+            r.qp[u] = unpack_bf16x4(qr[u ? b1 : b0]) * P;
+        }
+        return r;
+    };
+    // hi (pair-packed) and the two lo halves of a pair of values held in the
+    // accumulator layout of their transposes; residuals from the matrix core.
+    struct SplitPair {
+        bf16x8 hi, lo;
+    };
+    auto split_pair = [&](const f32x4 &x0, const f32x4 &x1) {
+        const bf16x8 hh = cat(to_bf16x4(x0), to_bf16x4(x1));
+        return SplitPair{hh, cat(to_bf16x4(mma32(NIL, hh, x0)), to_bf16x4(mma32(NIH, hh, x1)))};
+    };
+    f32x4 akk = zero4(), aqk = zero4();
+    constexpr int NP2 = (NB + 1) / 2;
+#pragma unroll
+    for (int pi = 0; pi < NP2; ++pi) {
+        const int b0 = 2 * pi, b1 = (2 * pi + 1 < NB) ? 2 * pi + 1 : 2 * pi;
+        Pair r = operands(b0, b1);
+        if (b1 == b0) {  // a lone block (dk = 16): the second half must not contribute
+            r.kp[1] = zero4();
+            r.qp[1] = zero4();
+        }
+        const SplitPair qs = split_pair(r.qp[0], r.qp[1]);
+        const SplitPair ms = split_pair(r.km[0], r.km[1]);
+        // A_kk: single bf16;  A_qk: hi*hi + lo*hi + hi*lo
+        akk = mma32(cat(to_bf16x4(r.kp[0]), to_bf16x4(r.kp[1])), ms.hi, akk);
+        aqk = mma32(qs.hi, ms.hi, aqk);
+        aqk = mma32(qs.lo, ms.hi, aqk);
+        aqk = mma32(qs.hi, ms.lo, aqk);
+    }
+    __syncthreads();  // sBeta visible
+
+    // Accumulator lane (g4, i) holds rows r = 4*g4 + jj of column i.
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int r = 4 * g4 + jj, i = l16;
+        sA[r][i] = (r > i) ? sBeta[r] * akk[jj] : 0.f;
+        sAq[r][i] = (r >= i) ? aqk[jj] : 0.f;
+    }
+    __syncthreads();
+
+    // T = (I + A_kk)^{-1} by forward substitution; lane c builds column c:
+    // T[r][c] = [r == c] - sum_{i < r} A[r][i] T[i][c]; rows of A come as four
+    // 16-byte reads (the same address for every lane).
+    float t[16];
+    if (lane < 16) {
+        const int c = lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sA[r][4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q4 + e < r) acc += a[e] * t[4 * q4 + e];
+            }
+            t[r] = ((r == c) ? 1.f : 0.f) - acc;
+        }
+    }
+    __syncthreads();
+    if (lane < 16) {
+        const float bc = sBeta[lane];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sA[r][lane] = t[r] * bc;
+    }
+    __syncthreads();
+
+    // T' and A_qk as A-operand fragments: lane (g4, m) holds M[m][4*g4 + 0..3], {hi, lo}.
+    const f32x4 tv = *reinterpret_cast<const f32x4 *>(&sA[l16][4 * g4]);
+    const f32x4 av = *reinterpret_cast<const f32x4 *>(&sAq[l16][4 * g4]);
+    float *w = ws + (slot * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
+    const SplitPair ts = split_pair(tv, av);
+    reinterpret_cast<Split4 *>(w)[lane] = Split4{__builtin_shufflevector(ts.hi, ts.hi, 0, 1, 2, 3),
+                                                 __builtin_shufflevector(ts.lo, ts.lo, 0, 1, 2, 3)};
+    reinterpret_cast<Split4 *>(w + 256)[lane] = Split4{__builtin_shufflevector(ts.hi, ts.hi, 4, 5, 6, 7),
+                                                       __builtin_shufflevector(ts.lo, ts.lo, 4, 5, 6, 7)};
+}
+
 template <int DK, typename T>
 static hipError_t launch_cl_t(const ChunkLocalArgs &a) {
     const int64_t slots = chunk_slots(a.total_tokens, a.nseq);
-    hipLaunchKernelGGL((chunk_local_kernel<DK, T>), dim3((unsigned)slots, (unsigned)a.H), dim3(64), 0,
-                       (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.g,
-                       (const T *)a.beta, a.cu, a.nseq, a.H, a.ws);
+    const dim3 grid((unsigned)slots, (unsigned)a.H);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((chunk_local_bf16_kernel<DK>), grid, dim3(64), 0, (hipStream_t)a.stream,
+                           (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.g,
+                           (const __bf16 *)a.beta, a.cu, a.nseq, a.H, a.ws);
+    else
+        hipLaunchKernelGGL((chunk_local_f32_kernel<DK, T>), grid, dim3(64), 0, (hipStream_t)a.stream,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.g, (const T *)a.beta, a.cu,
+                           a.nseq, a.H, a.ws);
     return hipGetLastError();
 }
 

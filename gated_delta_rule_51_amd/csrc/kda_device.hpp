@@ -203,4 +203,43 @@ __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// ---------------------------------------------------------------- matrix-core layout helpers
+
+__device__ __forceinline__ f32x4 unpack_bf16x4(u32x2 w) {
+    return f32x4{lo_bf16(w[0]), hi_bf16(w[0]), lo_bf16(w[1]), hi_bf16(w[1])};
+}
+
+// B operand of the 16x16 identity (lane (g4, n) holds I[4 g4 + j][n]).  A 16x16
+// bf16 tile held as the A operand of a product -- row m in lane group m, four
+// consecutive columns per lane -- times this returns the same tile in the
+// accumulator layout (four consecutive rows per lane, one column per lane):
+// a transpose of the register layout on the matrix cores, exact for bf16 data.
+__device__ __forceinline__ bf16x4 identity_operand(int g4, int l16) {
+    u16x4 bits;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bits[j] = (4 * g4 + j == l16) ? 0x3f80 : 0;
+    return __builtin_bit_cast(bf16x4, bits);
+}
+
+// A operands of -I in one half of the 32-long contraction and 0 in the other:
+// with B = cat(hi_a, hi_b) (two bf16 tiles in the layout of the accumulator),
+// mma32(neg_identity_operand<0>, B, x) = x - hi_a and <1> gives x - hi_b.
+// With hi = x rounded to bf16 that difference is exactly representable, and
+// the matrix core forms it exactly (one nonzero product, fp32 accumulation):
+// the residual of a hi/lo bf16 split without vector-ALU unpacking.
+template <int HALF>
+__device__ __forceinline__ bf16x8 neg_identity_operand(int g4, int l16) {
+    u16x4 bits;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bits[j] = (4 * g4 + j == l16) ? 0xbf80 : 0;
+    const bf16x4 m = __builtin_bit_cast(bf16x4, bits), z = {};
+    return HALF == 0 ? cat(m, z) : cat(z, m);
+}
+// x = hi + lo in bf16, x in the accumulator layout; returns lo, sets hh = cat(hi, hi).
+__device__ __forceinline__ bf16x4 split_lo(f32x4 x, const bf16x8 &nil, bf16x8 &hh) {
+    const bf16x4 hi = to_bf16x4(x);
+    hh = cat(hi, hi);
+    return to_bf16x4(mma32(nil, hh, x));
+}
+
 }  // namespace kda
