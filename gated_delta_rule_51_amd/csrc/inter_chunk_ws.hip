@@ -26,7 +26,8 @@
 // lane), so every operand is formed where it is needed and written with one
 // vector store.  g is bf16 and the triangles are 0/1, so the sums are exact up
 // to fp32 accumulation.
-// Each role loads its own inputs straight from HBM three chunks ahead:
+// Each role loads its own inputs straight from HBM three chunks ahead (past the
+// last chunk through empty buffer resources, which return zeros):
 // producers q/k/g, consumers T', A_qk (workspace fragments) and their v
 // columns (transposed on the matrix cores like the producers' g and k).  Padding tokens of a ragged last chunk load as zeros (g = 0 keeps
 // the decay unchanged, k = 0 removes them from every product).
@@ -87,17 +88,29 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
     const uint32_t rowV = (uint32_t)H * DV * EB;   // ... in v
     const uint32_t rowO = (uint32_t)H * DV * 4;    // ... in o
 
+    // Chunks at or past the end get an empty buffer resource, so look-ahead loads
+    // there return zeros without touching memory.
+    const int len = (int)(eos - bos);
+    // (The clamp compiles to a vector instruction; readfirstlane keeps the result
+    // -- the same in every lane -- scalar, so the buffer resources built from it
+    // stay uniform and their loads need no per-lane loop.)
     auto chunk_len = [&](int c) -> int {
-        const int64_t left = eos - (bos + 16 * (int64_t)c);
-        return left < 16 ? (int)left : 16;
+        const int left = len - 16 * c;
+        return __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left < 16 ? left : 16));
     };
-    // Look-ahead loads past the last chunk re-read the last chunk (results unused).
-    auto clampc = [&](int c) { return c < nc ? c : nc - 1; };
-    // Buffer resource over chunk c of this head; rows past the chunk are out of bounds.
+    // Buffer resource over chunk c of this head: base = the chunk's first token,
+    // length = its rows (an empty resource past the end).
     auto rsrc_in = [&](const __bf16 *base, int c, int d) {
         const int64_t t0 = bos + 16 * (int64_t)c;
-        const int n = chunk_len(c);
-        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB);
+        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)chunk_len(c) * (uint32_t)H * d * EB);
+    };
+    auto rsrc_out = [&](int c) {
+        const int64_t t0 = bos + 16 * (int64_t)c;
+        return make_rsrc(o + (t0 * H + h) * DV, (uint32_t)chunk_len(c) * rowO);
+    };
+    auto rsrc_ws = [&](int c) {
+        return make_rsrc(ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD,
+                         c < nc ? WS_FLOATS_PER_CHUNK_HEAD * 4u : 0u);
     };
 
     if (wave < NC) {
@@ -123,13 +136,11 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
             const bf16x4 ID = identity_operand(g4, l16);
             const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
             auto cload = [&](CIn &X, int c) {
-                const float *wsc = ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD;
-                const rsrc_t rw = make_rsrc(wsc, WS_FLOATS_PER_CHUNK_HEAD * 4u);
+                const rsrc_t rw = rsrc_ws(c);
                 X.tp = buf_load_u32x4(rw, lane * 16u);
                 X.aq = buf_load_u32x4(rw, (64 + lane) * 16u);
-                const int n = chunk_len(c);
                 const rsrc_t rv = rsrc_in(v, c, DV);
-                X.v = buf_load_u32x2(rv, l16 < n ? l16 * rowV + (col0 + 4 * g4) * EB : OOB);
+                X.v = buf_load_u32x2(rv, l16 * rowV + (col0 + 4 * g4) * EB);
             };
             auto advance = [&](int ob, const CIn &X, int c) {
                 const WsOps<DK> &P = ops[ob];
@@ -200,26 +211,22 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                 f32x4 O = mma32(aqq, dhh, Oa);
                 O = mma32(aqq, dll, O);
                 O += Ob + Oc;
-                const int64_t t0 = bos + 16 * (int64_t)c;
-                const int n = chunk_len(c);
-                const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV, (uint32_t)n * rowO);
+                const rsrc_t ro = rsrc_out(c);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int t = 4 * g4 + jj;
-                    buf_store_f32(O[jj], ro, t < n ? t * rowO + (col0 + l16) * 4u : OOB);
-                }
+                for (int jj = 0; jj < 4; ++jj)
+                    buf_store_f32(O[jj], ro, (4 * g4 + jj) * rowO + (col0 + l16) * 4u);
             };
 
             // Chunk c uses operand set c & 1 and the inputs loaded three chunks
             // earlier; the register sets rotate X0 -> X1 -> X2.
             CIn X0, X1, X2;
             cload(X0, 0);
-            cload(X1, clampc(1));
-            cload(X2, clampc(2));
+            cload(X1, 1);
+            cload(X2, 2);
             __syncthreads();  // operand set 0 ready
             auto citer = [&](int c, CIn &X) {
                 advance(c & 1, X, c);
-                cload(X, clampc(c + 3));
+                cload(X, c + 3);
                 __syncthreads();  // set c+1 ready; set c free
             };
             for (int c = 0; c < nc; c += 3) {
@@ -255,55 +262,74 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
         const bf16x4 LT = __builtin_bit_cast(bf16x4, lt_bits);
         const bf16x4 UT = __builtin_bit_cast(bf16x4, ut_bits);
         const bf16x4 ID = identity_operand(g4, l16);
-        const bf16x8 NIL = neg_identity_operand<0>(g4, l16);
         // Per block b = pw * BPW + bi: q, k, g of token l16, channels 16 b + 4 g4 .. +3
         // (the operand layout of Q+ and K+), one 8-byte load each.
         struct PIn {
             u32x2 q[BPW], k[BPW], g[BPW];
         };
         auto pload = [&](PIn &R, int c) {
-            const int n = chunk_len(c);
             const rsrc_t rq = rsrc_in(q, c, DK), rk = rsrc_in(k, c, DK), rg = rsrc_in(g, c, DK);
 #pragma unroll
             for (int bi = 0; bi < BPW; ++bi) {
-                const int b = pw * BPW + bi;
-                const uint32_t off = l16 < n ? l16 * rowK + (16 * b + 4 * g4) * EB : OOB;
+                const uint32_t off = l16 * rowK + (16 * (pw * BPW + bi) + 4 * g4) * EB;
                 R.q[bi] = buf_load_u32x2(rq, off);
                 R.k[bi] = buf_load_u32x2(rk, off);
                 R.g[bi] = buf_load_u32x2(rg, off);
             }
         };
+        // The wave's channel blocks are handled in pairs, so every 32-long operand
+        // carries two blocks' data and a constant operand with the wanted matrix in
+        // one half (0 in the other) selects the block: no operand is padded.
+        const bf16x4 z4 = {};
+        const bf16x8 IDL = cat(ID, z4), IDH = cat(z4, ID), LTL = cat(LT, z4), LTH = cat(z4, LT);
+        const bf16x8 UTL = cat(UT, z4), UTH = cat(z4, UT);
+        const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
         auto produce = [&](const PIn &R, int ob) {
             WsOps<DK> &P = ops[ob];
 #pragma unroll
-            for (int bi = 0; bi < BPW; ++bi) {
-                const int b = pw * BPW + bi;
+            for (int bp = 0; bp < BPW; bp += 2) {
+                const int i0 = bp, i1 = (bp + 1 < BPW) ? bp + 1 : bp;  // a lone block pairs with itself
+                const bf16x8 ga = cat(__builtin_bit_cast(bf16x4, R.g[i0]), __builtin_bit_cast(bf16x4, R.g[i1]));
+                const bf16x8 ka = cat(__builtin_bit_cast(bf16x4, R.k[i0]), __builtin_bit_cast(bf16x4, R.k[i1]));
                 // g and k as tokens 4 g4 + jj of channel 16 b + l16 (exact: bf16 values)
-                const bf16x4 ga = __builtin_bit_cast(bf16x4, R.g[bi]);
-                const f32x4 gt = mma16(ga, ID, zero4());
-                const f32x4 kc = mma16(__builtin_bit_cast(bf16x4, R.k[bi]), ID, zero4());
-                const bf16x4 gf = to_bf16x4(gt);
-                const f32x4 GT = mma16(gf, LT, zero4());   // G at token l16, channels 16 b + 4 g4 + jj
-                const f32x4 GS = mma16(UT, gf, zero4());   // Gs at tokens 4 g4 + jj, channel 16 b + l16
-                f32x4 Pp, F;
+                const bf16x8 gf = cat(to_bf16x4(mma32(ga, IDL, zero4())), to_bf16x4(mma32(ga, IDH, zero4())));
+                const f32x4 kc[2] = {mma32(ka, IDL, zero4()), mma32(ka, IDH, zero4())};
+                // G at token l16, channels 16 b + 4 g4 + jj; Gs at tokens 4 g4 + jj, channel 16 b + l16
+                const f32x4 GT[2] = {mma32(gf, LTL, zero4()), mma32(gf, LTH, zero4())};
+                const f32x4 GS[2] = {mma32(UTL, gf, zero4()), mma32(UTH, gf, zero4())};
+                f32x4 Pp[2], qv[2], ktv[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    Pp[j] = decay_exp_fast(GT[j]);   // e^{G_r}
-                    F[j] = decay_exp_fast(GS[j]);    // e^{G_n - G_r}
+                for (int u = 0; u < 2; ++u) {
+                    f32x4 F;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        Pp[u][j] = decay_exp_fast(GT[u][j]);   // e^{G_r}
+                        F[j] = decay_exp_fast(GS[u][j]);       // e^{G_n - G_r}
+                    }
+                    qv[u] = unpack_bf16x4(R.q[u ? i1 : i0]) * Pp[u];
+                    ktv[u] = kc[u] * F;
                 }
-                // Q+ and K~ as hi + lo; both are in the accumulator layout (of Q+^T
-                // and of K~), so the residual comes from the matrix cores.
-                bf16x8 qhh, khh;
-                const bf16x4 qlo = split_lo(unpack_bf16x4(R.q[bi]) * Pp, NIL, qhh);
-                const bf16x4 klo = split_lo(kc * F, NIL, khh);
-                bf16x4 *qh = reinterpret_cast<bf16x4 *>(&P.qp_hi[b >> 1][lane]) + (b & 1);
-                bf16x4 *ql = reinterpret_cast<bf16x4 *>(&P.qp_lo[b >> 1][lane]) + (b & 1);
-                bf16x4 *kh = reinterpret_cast<bf16x4 *>(&P.kp[b >> 1][lane]) + (b & 1);
-                *qh = __builtin_shufflevector(qhh, qhh, 0, 1, 2, 3);
-                *ql = qlo;
-                *kh = to_bf16x4(unpack_bf16x4(R.k[bi]) * Pp);
-                P.kt[b][lane] = Split4{__builtin_shufflevector(khh, khh, 0, 1, 2, 3), klo};
-                if (l16 == 15) *reinterpret_cast<f32x4 *>(&P.gam[16 * b + 4 * g4]) = Pp;
+                // Q+ and K~ as hi + lo (both held in the accumulator layout of a tile:
+                // Q+^T and K~), residuals from the matrix core
+                const bf16x8 qh = cat(to_bf16x4(qv[0]), to_bf16x4(qv[1]));
+                const bf16x8 kth = cat(to_bf16x4(ktv[0]), to_bf16x4(ktv[1]));
+                const bf16x4 ql[2] = {to_bf16x4(mma32(NIL, qh, qv[0])), to_bf16x4(mma32(NIH, qh, qv[1]))};
+                const bf16x4 ktl[2] = {to_bf16x4(mma32(NIL, kth, ktv[0])), to_bf16x4(mma32(NIH, kth, ktv[1]))};
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (u == 1 && i1 == i0) break;
+                    const int b = pw * BPW + (u ? i1 : i0);
+                    bf16x4 *qhp = reinterpret_cast<bf16x4 *>(&P.qp_hi[b >> 1][lane]) + (b & 1);
+                    bf16x4 *qlp = reinterpret_cast<bf16x4 *>(&P.qp_lo[b >> 1][lane]) + (b & 1);
+                    bf16x4 *kpp = reinterpret_cast<bf16x4 *>(&P.kp[b >> 1][lane]) + (b & 1);
+                    *qhp = u ? __builtin_shufflevector(qh, qh, 4, 5, 6, 7) : __builtin_shufflevector(qh, qh, 0, 1, 2, 3);
+                    *qlp = ql[u];
+                    *kpp = to_bf16x4(unpack_bf16x4(R.k[u ? i1 : i0]) * Pp[u]);
+                    P.kt[b][lane] = Split4{u ? __builtin_shufflevector(kth, kth, 4, 5, 6, 7)
+                                             : __builtin_shufflevector(kth, kth, 0, 1, 2, 3),
+                                           ktl[u]};
+                    if (l16 == 15) *reinterpret_cast<f32x4 *>(&P.gam[16 * b + 4 * g4]) = Pp[u];
+                }
             }
         };
 
@@ -311,14 +337,14 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
         // inputs loaded three chunks earlier; register sets rotate R1 -> R2 -> R0.
         PIn R0, R1, R2;
         pload(R0, 0);
-        pload(R1, clampc(1));
-        pload(R2, clampc(2));
+        pload(R1, 1);
+        pload(R2, 2);
         produce(R0, 0);
-        pload(R0, clampc(3));
+        pload(R0, 3);
         __syncthreads();  // operand set 0 ready
         auto piter = [&](int c, PIn &R) {
             produce(R, (c + 1) & 1);
-            pload(R, clampc(c + 4));
+            pload(R, c + 4);
             __syncthreads();
         };
         for (int c = 0; c < nc; c += 3) {
