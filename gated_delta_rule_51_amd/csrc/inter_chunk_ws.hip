@@ -16,21 +16,22 @@
 // the token-parallel work off the consumers' critical path and lets the two
 // kinds of work share each SIMD.
 //
-// Producers load q, k and g of a chunk as token rows with four consecutive
-// channels per lane (one 8-byte load each; the operand layout of Q+ and K+).
-// A product with the identity turns g and k into four consecutive tokens of
-// one channel per lane, and the cumulative log-decay G of the chunk is then a
-// product with a 0/1 triangle, G^T = g^T L^T and Gs = U g (Gs_r = sum over
-// later tokens = G_n - G_r).  The first lands in the operand layout of Q+ and
-// K+, the second in that of K~^T (channel rows, four consecutive tokens per
-// lane), so every operand is formed where it is needed and written with one
-// vector store.  g is bf16 and the triangles are 0/1, so the sums are exact up
-// to fp32 accumulation.
-// Each role loads its own inputs straight from HBM three chunks ahead (past the
-// last chunk through empty buffer resources, which return zeros):
-// producers q/k/g, consumers T', A_qk (workspace fragments) and their v
-// columns (transposed on the matrix cores like the producers' g and k).  Padding tokens of a ragged last chunk load as zeros (g = 0 keeps
-// the decay unchanged, k = 0 removes them from every product).
+// Producers hold q, k and g of a chunk as token rows with four consecutive
+// channels per block per lane (the operand layout of Q+ and K+; they arrive
+// through a per-wave LDS stage, see pload below).  A product with the identity
+// turns g and k into four consecutive tokens of one channel per lane, and the
+// cumulative log-decay G of the chunk is then a product with a 0/1 triangle,
+// G^T = g^T L^T and Gs = U g (Gs_r = sum over later tokens = G_n - G_r).  The
+// first lands in the operand layout of Q+ and K+, the second in that of K~^T
+// (channel rows, four consecutive tokens per lane), so every operand is formed
+// where it is needed and written with one vector store.  g is bf16 and the
+// triangles are 0/1, so the sums are exact up to fp32 accumulation.
+// Each role loads its own inputs straight from HBM ahead of use (past the last
+// chunk through empty buffer resources, which return zeros): producers q/k/g,
+// consumers T', A_qk (workspace fragments) and their v columns (transposed on
+// the matrix cores like the producers' g and k).  Padding tokens of a ragged
+// last chunk load as zeros (g = 0 keeps the decay unchanged, k = 0 removes
+// them from every product).
 //
 // Precision as in inter_chunk.hip: K+ S single bf16, everything else split
 // bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation, fp32 state.  The
@@ -44,6 +45,25 @@
 
 namespace kda {
 
+// Waves of a workgroup and their roles.  Wave w and wave w + 4 run on the same
+// SIMD (waves 0..3 on four different ones).  With one or two consumers and more
+// than four waves, the waves that would share a SIMD with a consumer stay idle
+// (they only take part in the barriers), so each consumer has its SIMD to itself
+// and the producers pair up on the others.
+template <int NC, int NP>
+struct WsLayout {
+    static constexpr int NIDLE = (NC + NP > 4 && NC <= 2) ? NC : 0;
+    static constexpr int NW = NC + NP + NIDLE;
+    // role of wave w: consumer index (>= 0), producer index - NP (in [-NP, 0)), or
+    // -NP - 1 for an idle wave
+    static __device__ __forceinline__ int role(int w) {
+        if (w < NC) return w;
+        if (w < 4 || NIDLE == 0) return w - NC - NP;
+        if (w < 4 + NIDLE) return -NP - 1;
+        return w - NC - NIDLE - NP;
+    }
+};
+
 template <int DK>
 struct WsOps {
     static constexpr int NB = DK / 16, NPAIR = NB / 2;
@@ -55,7 +75,7 @@ struct WsOps {
 };
 
 template <int DK, int DV, int NC, int NP>
-__global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(2, 2))) void inter_chunk_ws_kernel(
+__global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_waves_per_eu(2, 2))) void inter_chunk_ws_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
     int32_t H, const float *__restrict__ ws, float *__restrict__ o, float *__restrict__ fin,
@@ -75,7 +95,8 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
     const int s = chain / H, h = chain % H;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int lane = tid & 63;
+    const int role = WsLayout<NC, NP>::role(tid >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
 
     __shared__ __attribute__((aligned(16))) WsOps<DK> ops[2];
@@ -113,16 +134,26 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                          c < nc ? WS_FLOATS_PER_CHUNK_HEAD * 4u : 0u);
     };
 
-    if (wave < NC) {
+    if (role == -NP - 1) {
+        // idle wave: the same barriers as the others
+        if (nc > 0)
+            for (int c = 0; c <= nc; ++c) __syncthreads();
+    } else if (role >= 0) {
+        const int wave = role;
         // ============================================================ consumer
-        // State slice: rows 16 b + 4 g4 + jj, column col0 + l16 (accumulator layout).
+        // State slice: internal rows 16 b + 4 g4 + jj, column col0 + l16 (accumulator
+        // layout); internal row 16 b + 4 g4 + jj is key channel mrow(b, jj) of the
+        // state in memory (the relabelling the producers' loads use).
         const int col0 = (split * NC + wave) * 16;
+        auto mrow = [&](int b, int jj) { return 32 * (b >> 1) + 8 * g4 + 4 * (b & 1) + jj; };
+        // (an empty buffer resource without an initial state: the loads return 0)
+        const rsrc_t rinit = make_rsrc(init ? init + hd * DK * DV : init, init ? DK * DV * 4u : 0u);
         f32x4 S[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                S[b][jj] = init ? init[(hd * DK + 16 * b + 4 * g4 + jj) * DV + col0 + l16] : 0.f;
+                S[b][jj] = __builtin_bit_cast(float, buf_load_u32(rinit, (mrow(b, jj) * DV + col0 + l16) * 4u));
 
         if (nc > 0) {
             // Per-chunk consumer inputs: T' and A_qk fragments (workspace), and
@@ -229,26 +260,30 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                 cload(X, c + 3);
                 __syncthreads();  // set c+1 ready; set c free
             };
-            for (int c = 0; c < nc; c += 3) {
+            // Whole groups of three in the loop and the remainder after it: with
+            // an exit inside the loop body the compiler merged the loop's entry
+            // and back edge conservatively and waited there for every load in
+            // flight, including the ones issued just before.
+            int c = 0;
+            for (; c + 3 <= nc; c += 3) {
                 citer(c, X0);
-                if (c + 1 >= nc) break;
                 citer(c + 1, X1);
-                if (c + 2 >= nc) break;
                 citer(c + 2, X2);
             }
+            if (c < nc) citer(c, X0);
+            if (c + 1 < nc) citer(c + 1, X1);
         }
         if (fin) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    fin[(hd * DK + 16 * b + 4 * g4 + jj) * DV + col0 + l16] = S[b][jj];
+                    fin[(hd * DK + mrow(b, jj)) * DV + col0 + l16] = S[b][jj];
         }
     } else if (nc > 0) {
         // ============================================================ producer
-        // Lane (g4, l16): token l16, channels 16 b + 4 g4 .. +3 of blocks
-        // b = pw * BPW + bi.
-        const int pw = wave - NC;
+        // Producer pw builds the operands of channel blocks pw * BPW .. + BPW - 1.
+        const int pw = role + NP;
         // Constant 0/1 triangles as matrix-core operands (bf16 1.0 = 0x3f80):
         //   LT, B operand of G^T = g^T L^T: lane (g4, n) holds L[n][4 g4 + j] = [4 g4 + j <= n];
         //   UT, A operand of Gs  = U g:     lane (g4, i) holds U[i][4 g4 + j] = [4 g4 + j >  i].
@@ -262,21 +297,50 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
         const bf16x4 LT = __builtin_bit_cast(bf16x4, lt_bits);
         const bf16x4 UT = __builtin_bit_cast(bf16x4, ut_bits);
         const bf16x4 ID = identity_operand(g4, l16);
-        // Per block b = pw * BPW + bi: q, k, g of token l16, channels 16 b + 4 g4 .. +3
-        // (the operand layout of Q+ and K+), one 8-byte load each.
+        // Raw q, k, g.  Inside the kernel the 32 channels of block pair P are
+        // ordered so that what one lane needs of the pair -- channels 4 g4 .. +3 of
+        // block 2P and of block 2P+1 -- are the eight consecutive memory channels
+        // 32 P + 8 g4 .. +7:
+        //     internal channel 16 (2P + h) + 4 g4 + j  <->  memory channel 32 P + 8 g4 + 4 h + j
+        // (a relabelling of the key channels; the state rows follow it).  Loads then
+        // read whole 64-byte pieces of a pair's token row with four consecutive lanes
+        // per row (lane L: row L / 4, bytes 16 (L % 4)), so the address unit sees
+        // one cache line per four lanes instead of one per lane, and a round trip
+        // through the wave's own LDS stage gives the operand layout (lane (g4, l16):
+        // token l16, the 16 bytes at 16 g4).
+        constexpr int NPW = (BPW + 1) / 2;  // block pairs this wave touches
+        const int pair0 = (pw * BPW) / 2;
         struct PIn {
-            u32x2 q[BPW], k[BPW], g[BPW];
+            u32x4 d[3][NPW];  // q, k, g
         };
         auto pload = [&](PIn &R, int c) {
             const rsrc_t rq = rsrc_in(q, c, DK), rk = rsrc_in(k, c, DK), rg = rsrc_in(g, c, DK);
 #pragma unroll
-            for (int bi = 0; bi < BPW; ++bi) {
-                const uint32_t off = l16 * rowK + (16 * (pw * BPW + bi) + 4 * g4) * EB;
-                R.q[bi] = buf_load_u32x2(rq, off);
-                R.k[bi] = buf_load_u32x2(rk, off);
-                R.g[bi] = buf_load_u32x2(rg, off);
+            for (int pp = 0; pp < NPW; ++pp) {
+                const uint32_t off = (lane >> 2) * rowK + 64u * (pair0 + pp) + 16u * (lane & 3);
+                R.d[0][pp] = buf_load_u32x4(rq, off);
+                R.d[1][pp] = buf_load_u32x4(rk, off);
+                R.d[2][pp] = buf_load_u32x4(rg, off);
             }
         };
+        // Per-wave stage: 16 token rows of 64 bytes per (tensor, pair), rows padded to
+        // 80 bytes so the operand-layout reads (16 rows, one 16-byte piece each) hit
+        // distinct banks.
+        __shared__ __attribute__((aligned(16))) u32x4 stage[NP][3][NPW][16][5];
+        auto stage_put = [&](const PIn &R) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int pp = 0; pp < NPW; ++pp) stage[pw][t][pp][lane >> 2][lane & 3] = R.d[t][pp];
+        };
+        auto stage_get = [&](PIn &A) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int pp = 0; pp < NPW; ++pp) A.d[t][pp] = stage[pw][t][pp][l16][g4];
+        };
+        // The 8 bytes of block half h (0: block 2P, 1: block 2P+1) in a staged piece.
+        auto half = [](const u32x4 &x, int h) { return h ? u32x2{x[2], x[3]} : u32x2{x[0], x[1]}; };
         // The wave's channel blocks are handled in pairs, so every 32-long operand
         // carries two blocks' data and a constant operand with the wanted matrix in
         // one half (0 in the other) selects the block: no operand is padded.
@@ -284,13 +348,18 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
         const bf16x8 IDL = cat(ID, z4), IDH = cat(z4, ID), LTL = cat(LT, z4), LTH = cat(z4, LT);
         const bf16x8 UTL = cat(UT, z4), UTH = cat(z4, UT);
         const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
-        auto produce = [&](const PIn &R, int ob) {
+        auto produce = [&](const PIn &A, int ob) {
             WsOps<DK> &P = ops[ob];
 #pragma unroll
-            for (int bp = 0; bp < BPW; bp += 2) {
-                const int i0 = bp, i1 = (bp + 1 < BPW) ? bp + 1 : bp;  // a lone block pairs with itself
-                const bf16x8 ga = cat(__builtin_bit_cast(bf16x4, R.g[i0]), __builtin_bit_cast(bf16x4, R.g[i1]));
-                const bf16x8 ka = cat(__builtin_bit_cast(bf16x4, R.k[i0]), __builtin_bit_cast(bf16x4, R.k[i1]));
+            for (int pp = 0; pp < NPW; ++pp) {
+                // blocks b0, b1 of this pair; a wave with one block (BPW = 1) pairs it with itself
+                const int hb = (BPW == 1) ? (pw & 1) : 0;
+                const int b0 = (BPW == 1) ? pw : pw * BPW + 2 * pp, b1 = (BPW == 1) ? pw : b0 + 1;
+                const u32x2 Rq[2] = {half(A.d[0][pp], hb), half(A.d[0][pp], BPW == 1 ? hb : 1)};
+                const u32x2 Rk[2] = {half(A.d[1][pp], hb), half(A.d[1][pp], BPW == 1 ? hb : 1)};
+                const u32x2 Rg[2] = {half(A.d[2][pp], hb), half(A.d[2][pp], BPW == 1 ? hb : 1)};
+                const bf16x8 ga = cat(__builtin_bit_cast(bf16x4, Rg[0]), __builtin_bit_cast(bf16x4, Rg[1]));
+                const bf16x8 ka = cat(__builtin_bit_cast(bf16x4, Rk[0]), __builtin_bit_cast(bf16x4, Rk[1]));
                 // g and k as tokens 4 g4 + jj of channel 16 b + l16 (exact: bf16 values)
                 const bf16x8 gf = cat(to_bf16x4(mma32(ga, IDL, zero4())), to_bf16x4(mma32(ga, IDH, zero4())));
                 const f32x4 kc[2] = {mma32(ka, IDL, zero4()), mma32(ka, IDH, zero4())};
@@ -306,7 +375,7 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                         Pp[u][j] = decay_exp_fast(GT[u][j]);   // e^{G_r}
                         F[j] = decay_exp_fast(GS[u][j]);       // e^{G_n - G_r}
                     }
-                    qv[u] = unpack_bf16x4(R.q[u ? i1 : i0]) * Pp[u];
+                    qv[u] = unpack_bf16x4(Rq[u]) * Pp[u];
                     ktv[u] = kc[u] * F;
                 }
                 // Q+ and K~ as hi + lo (both held in the accumulator layout of a tile:
@@ -317,14 +386,14 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
                 const bf16x4 ktl[2] = {to_bf16x4(mma32(NIL, kth, ktv[0])), to_bf16x4(mma32(NIH, kth, ktv[1]))};
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    if (u == 1 && i1 == i0) break;
-                    const int b = pw * BPW + (u ? i1 : i0);
+                    if (u == 1 && b1 == b0) break;
+                    const int b = u ? b1 : b0;
                     bf16x4 *qhp = reinterpret_cast<bf16x4 *>(&P.qp_hi[b >> 1][lane]) + (b & 1);
                     bf16x4 *qlp = reinterpret_cast<bf16x4 *>(&P.qp_lo[b >> 1][lane]) + (b & 1);
                     bf16x4 *kpp = reinterpret_cast<bf16x4 *>(&P.kp[b >> 1][lane]) + (b & 1);
                     *qhp = u ? __builtin_shufflevector(qh, qh, 4, 5, 6, 7) : __builtin_shufflevector(qh, qh, 0, 1, 2, 3);
                     *qlp = ql[u];
-                    *kpp = to_bf16x4(unpack_bf16x4(R.k[u ? i1 : i0]) * Pp[u]);
+                    *kpp = to_bf16x4(unpack_bf16x4(Rk[u]) * Pp[u]);
                     P.kt[b][lane] = Split4{u ? __builtin_shufflevector(kth, kth, 4, 5, 6, 7)
                                              : __builtin_shufflevector(kth, kth, 0, 1, 2, 3),
                                            ktl[u]};
@@ -333,27 +402,37 @@ __global__ __launch_bounds__(64 * (NC + NP)) __attribute__((amdgpu_waves_per_eu(
             }
         };
 
-        // Iteration c builds the operands of chunk c+1 into set (c+1) & 1 from
-        // inputs loaded three chunks earlier; register sets rotate R1 -> R2 -> R0.
-        PIn R0, R1, R2;
+        // Iteration c builds the operands of chunk c+1 into set (c+1) & 1, then
+        // passes chunk c+2 (registers loaded three iterations earlier) through the
+        // stage, so its LDS latency falls in the barrier wait, and reuses those
+        // registers for chunk c+5; register sets rotate R2 -> R0 -> R1.
+        PIn R0, R1, R2, A;
         pload(R0, 0);
         pload(R1, 1);
         pload(R2, 2);
-        produce(R0, 0);
+        stage_put(R0);
+        stage_get(A);  // (the wave's own LDS accesses stay in order)
+        produce(A, 0);
+        stage_put(R1);
+        stage_get(A);
         pload(R0, 3);
+        pload(R1, 4);
         __syncthreads();  // operand set 0 ready
         auto piter = [&](int c, PIn &R) {
-            produce(R, (c + 1) & 1);
-            pload(R, c + 4);
+            produce(A, (c + 1) & 1);
+            stage_put(R);
+            stage_get(A);
+            pload(R, c + 5);
             __syncthreads();
         };
-        for (int c = 0; c < nc; c += 3) {
-            piter(c, R1);
-            if (c + 1 >= nc) break;
-            piter(c + 1, R2);
-            if (c + 2 >= nc) break;
-            piter(c + 2, R0);
+        int c = 0;  // (loop form as for the consumers)
+        for (; c + 3 <= nc; c += 3) {
+            piter(c, R2);
+            piter(c + 1, R0);
+            piter(c + 2, R1);
         }
+        if (c < nc) piter(c, R2);
+        if (c + 1 < nc) piter(c + 1, R0);
     }
 }
 
@@ -363,7 +442,7 @@ static hipError_t launch_ws_t(const InterChunkArgs &a) {
     const int nsplit = DV / (16 * NC);
     const int64_t grid = ((int64_t)nchains + 7) / 8 * 8 * nsplit;
     hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP>), dim3((unsigned)grid),
-                       dim3(64 * (NC + NP)), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
+                       dim3(64 * WsLayout<NC, NP>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
                        (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
                        a.H, a.ws, a.o, a.fin, nsplit, nchains);
     return hipGetLastError();
