@@ -185,8 +185,8 @@ __global__ __launch_bounds__(64) void chunk_local_f32_kernel(
 
 // bf16 inputs.  Same outputs; the work is laid out for the matrix cores:
 //   * q, k, g of the chunk are read through buffer resources based at the
-//     chunk's first token (8-byte loads of 4 channels of one token per lane --
-//     the A-operand layout of K+, K-, Q+; padding rows read as zeros);
+//     chunk's first token (4 channels of one token per lane and block -- the
+//     A-operand layout of K+, K-, Q+; padding rows read as zeros);
 //   * the cumulative log-decay G is a product with the 0/1 lower triangle,
 //     G^T = g^T L^T, after an identity product turns g into 4 tokens of one
 //     channel per lane (both exact: g is bf16), so e^{+-G} = exp(+-G) need no
@@ -230,15 +230,35 @@ __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
     __shared__ __attribute__((aligned(16))) float sAq[16][20];  // A_qk
     __shared__ float sBeta[16];
 
-    // All loads first: token l16, channels 16 b + 4 g4 .. +3 of q, k, g.
+    // All loads first: token l16, channels 16 b + 4 g4 .. +3 of q, k, g (block b
+    // in the kernel's own channel order).  The products below contract over the
+    // channels, so any consistent order will do; with two or more blocks the
+    // kernel takes, in block pair P, internal channel 16 (2P + h) + 4 g4 + j to be
+    // memory channel 32 P + 8 g4 + 4 h + j, which makes what a lane needs of the
+    // pair one 16-byte piece (half the load instructions, each touching the same
+    // 16 token rows).
     const uint32_t row = l16 < n ? l16 * rowK : OOB;
     u32x2 gr[NB], kr[NB], qr[NB];
+    if constexpr (NB % 2 == 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const uint32_t o = row == OOB ? OOB : row + (16 * b + 4 * g4) * EB;
-        gr[b] = buf_load_u32x2(rg, o);
-        kr[b] = buf_load_u32x2(rk, o);
-        qr[b] = buf_load_u32x2(rq, o);
+        for (int p = 0; p < NB / 2; ++p) {
+            const uint32_t o = row == OOB ? OOB : row + (32 * p + 8 * g4) * EB;
+            const u32x4 gx = buf_load_u32x4(rg, o), kx = buf_load_u32x4(rk, o), qx = buf_load_u32x4(rq, o);
+            gr[2 * p] = u32x2{gx[0], gx[1]};
+            gr[2 * p + 1] = u32x2{gx[2], gx[3]};
+            kr[2 * p] = u32x2{kx[0], kx[1]};
+            kr[2 * p + 1] = u32x2{kx[2], kx[3]};
+            qr[2 * p] = u32x2{qx[0], qx[1]};
+            qr[2 * p + 1] = u32x2{qx[2], qx[3]};
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint32_t o = row == OOB ? OOB : row + (16 * b + 4 * g4) * EB;
+            gr[b] = buf_load_u32x2(rg, o);
+            kr[b] = buf_load_u32x2(rk, o);
+            qr[b] = buf_load_u32x2(rq, o);
+        }
     }
     if (lane < 16) sBeta[lane] = bf16_bits_to_f32(buf_load_u16(rb, lane < n ? lane * (uint32_t)H * EB : OOB));
 

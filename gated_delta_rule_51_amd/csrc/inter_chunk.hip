@@ -525,32 +525,36 @@ static hipError_t launch_ic_dt(const InterChunkArgs &a, int nw) {
 }
 
 hipError_t launch_inter_chunk(const InterChunkArgs &a) {
-    // Kernel choice.  The serial recurrence is latency-bound while there are
-    // few (sequence, head) chains: then bf16 inputs with dk >= 32 run the
-    // warp-specialised kernel (inter_chunk_ws.hip), whose producer waves take
-    // the token-parallel work off the consumers' critical path.  With enough
-    // chains to give every CU a full workgroup (dk = dv = 128: 256 or more),
-    // the work is throughput-bound and this file's kernel, which does the
-    // per-chunk preparation once per chain, is faster.
+    // Kernel choice.  bf16 inputs with dk >= 32 run the warp-specialised kernel
+    // (inter_chunk_ws.hip), whose producer waves take the token-parallel work
+    // off the consumers' critical path; it is the faster one both while the
+    // serial recurrence is latency-bound (few (sequence, head) chains) and when
+    // thousands of chains make the work throughput-bound.  This file's kernel
+    // serves fp32 inputs and dk = 16.
     // Tuning knobs: KDA_WS = "<consumers>x<producers>" forces the warp-
-    // specialised kernel with that shape; KDA_WAVES in {2, 4, 8} forces this
-    // file's kernel with that many waves (dk = dv = 128).
+    // specialised kernel with that shape (a trailing 's' selects its form with
+    // separate chain and output waves per slice); KDA_WAVES in {2, 4, 8}
+    // forces this file's kernel with that many waves (dk = dv = 128).
     const int64_t nchains = (int64_t)a.nseq * a.H;
     const char *classic = getenv("KDA_WAVES");
     const char *ws_shape = getenv("KDA_WS");
     const bool big = a.dk == 128 && a.dv == 128 && nchains >= 256;
-    if (a.bf16 && a.dk >= 32 && a.waves_per_group == 0 && !classic && (!big || ws_shape)) {
+    if (a.bf16 && a.dk >= 32 && a.waves_per_group == 0 && !classic) {
         int ncw = nchains < 64 ? 2 : 4;
         if (ncw > a.dv / 16) ncw = a.dv / 16;
         int npw = a.dk / 16 < 4 ? a.dk / 16 : 4;
+        bool split = false;
         if (ws_shape) {
             int c = 0, p = 0;
-            if (sscanf(ws_shape, "%dx%d", &c, &p) == 2) {
+            char sfx = 0;
+            const int got = sscanf(ws_shape, "%dx%d%c", &c, &p, &sfx);
+            if (got >= 2) {
                 ncw = c;
                 npw = p;
+                split = got == 3 && sfx == 's';
             }
         }
-        return launch_inter_chunk_ws(a, ncw, npw);
+        return launch_inter_chunk_ws(a, ncw, npw, split);
     }
     int nw = a.waves_per_group;
     if (nw <= 0) {
