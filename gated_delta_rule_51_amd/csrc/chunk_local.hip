@@ -198,11 +198,14 @@ template <int DK>
 __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ g,
     const __bf16 *__restrict__ beta, const int32_t *__restrict__ cu, int32_t nseq, int32_t H,
-    float *__restrict__ ws) {
+    float *__restrict__ ws, int64_t base) {
     constexpr int NB = DK / 16;
     constexpr uint32_t EB = 2;
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y;
+    // Item id = slot * H + head: the heads of one chunk are neighbours, so the
+    // waves in flight read neighbouring pieces of the same token rows.
+    const int64_t id = base + blockIdx.x;
+    const int64_t slot = id / H;
+    const int h = (int)(id - slot * H);
     const int lane = threadIdx.x;
 
     // Which sequence owns this slot: the largest s with floor(cu[s]/16) + s <= slot.
@@ -380,11 +383,18 @@ template <int DK, typename T>
 static hipError_t launch_cl_t(const ChunkLocalArgs &a) {
     const int64_t slots = chunk_slots(a.total_tokens, a.nseq);
     const dim3 grid((unsigned)slots, (unsigned)a.H);
-    if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((chunk_local_bf16_kernel<DK>), grid, dim3(64), 0, (hipStream_t)a.stream,
-                           (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.g,
-                           (const __bf16 *)a.beta, a.cu, a.nseq, a.H, a.ws);
-    else
+    if constexpr (sizeof(T) == 2) {
+        // one wave per (slot, head) item, in launches of at most 2^25 workgroups
+        const int64_t items = slots * a.H, per_launch = int64_t(1) << 25;
+        for (int64_t base = 0; base < items; base += per_launch) {
+            const int64_t n = items - base < per_launch ? items - base : per_launch;
+            hipLaunchKernelGGL((chunk_local_bf16_kernel<DK>), dim3((unsigned)n), dim3(64), 0, (hipStream_t)a.stream,
+                               (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.g,
+                               (const __bf16 *)a.beta, a.cu, a.nseq, a.H, a.ws, base);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    } else
         hipLaunchKernelGGL((chunk_local_f32_kernel<DK, T>), grid, dim3(64), 0, (hipStream_t)a.stream,
                            (const T *)a.q, (const T *)a.k, (const T *)a.g, (const T *)a.beta, a.cu,
                            a.nseq, a.H, a.ws);
