@@ -532,9 +532,8 @@ hipError_t launch_inter_chunk(const InterChunkArgs &a) {
     // thousands of chains make the work throughput-bound.  This file's kernel
     // serves fp32 inputs and dk = 16.
     // Tuning knobs: KDA_WS = "<consumers>x<producers>" forces the warp-
-    // specialised kernel with that shape (a trailing 's' selects its form with
-    // separate chain and output waves per slice); KDA_WAVES in {2, 4, 8}
-    // forces this file's kernel with that many waves (dk = dv = 128).
+    // specialised kernel with that shape; KDA_WAVES in {2, 4, 8} forces this
+    // file's kernel with that many waves (dk = dv = 128).
     const int64_t nchains = (int64_t)a.nseq * a.H;
     const char *classic = getenv("KDA_WAVES");
     const char *ws_shape = getenv("KDA_WS");
@@ -543,18 +542,14 @@ hipError_t launch_inter_chunk(const InterChunkArgs &a) {
         int ncw = nchains < 64 ? 2 : 4;
         if (ncw > a.dv / 16) ncw = a.dv / 16;
         int npw = a.dk / 16 < 4 ? a.dk / 16 : 4;
-        bool split = false;
         if (ws_shape) {
             int c = 0, p = 0;
-            char sfx = 0;
-            const int got = sscanf(ws_shape, "%dx%d%c", &c, &p, &sfx);
-            if (got >= 2) {
+            if (sscanf(ws_shape, "%dx%d", &c, &p) == 2) {
                 ncw = c;
                 npw = p;
-                split = got == 3 && sfx == 's';
             }
         }
-        return launch_inter_chunk_ws(a, ncw, npw, split);
+        return launch_inter_chunk_ws(a, ncw, npw);
     }
     int nw = a.waves_per_group;
     if (nw <= 0) {

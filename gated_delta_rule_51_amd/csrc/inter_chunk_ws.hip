@@ -46,34 +46,21 @@
 namespace kda {
 
 // Waves of a workgroup and their roles.  Wave w and wave w + 4 run on the same
-// SIMD (waves 0..3 on four different ones).
-//   * Without SPLIT, each of the NC consumer waves advances its state slice and
-//     also forms the outputs.  With one or two consumers and more than four
-//     waves, the waves that would share a SIMD with a consumer stay idle (they
-//     only take part in the barriers), so each consumer has its SIMD to itself
-//     and the producers pair up on the others.
-//   * With SPLIT, each slice has a chain wave (the state recurrence only) and an
-//     output wave that forms O one chunk behind from the state and Delta the
-//     chain wave leaves in LDS; chain and output waves sit on different SIMDs,
-//     each next to one producer.
-template <int NC, int NP, bool SPLIT>
+// SIMD (waves 0..3 on four different ones).  With one or two consumers and more
+// than four waves, the waves that would share a SIMD with a consumer stay idle
+// (they only take part in the barriers), so each consumer has its SIMD to itself
+// and the producers pair up on the others.
+template <int NC, int NP>
 struct WsLayout {
-    static constexpr int NCW = SPLIT ? 2 * NC : NC;
-    static constexpr int NIDLE = (!SPLIT && NC + NP > 4 && NC <= 2) ? NC : 0;
-    static constexpr int NW = NCW + NP + NIDLE;
-    static constexpr int NSETS = SPLIT ? 3 : 2;  // operand sets in LDS
-    enum { CHAIN = 0, OUT = 1, PROD = 2, IDLE = 3 };
-    static __device__ __forceinline__ int kind(int w) {
-        if (w < NC) return CHAIN;
-        if (SPLIT) return w < 2 * NC ? OUT : PROD;
-        if (w < 4 || NIDLE == 0) return PROD;
-        return w < 4 + NIDLE ? IDLE : PROD;
-    }
-    // slice index (CHAIN, OUT) or producer index (PROD)
-    static __device__ __forceinline__ int index(int w) {
+    static constexpr int NIDLE = (NC + NP > 4 && NC <= 2) ? NC : 0;
+    static constexpr int NW = NC + NP + NIDLE;
+    // role of wave w: consumer index (>= 0), producer index - NP (in [-NP, 0)), or
+    // -NP - 1 for an idle wave
+    static __device__ __forceinline__ int role(int w) {
         if (w < NC) return w;
-        if (SPLIT) return w < 2 * NC ? w - NC : w - 2 * NC;
-        return (w < 4 || NIDLE == 0) ? w - NC : w - NC - NIDLE;
+        if (w < 4 || NIDLE == 0) return w - NC - NP;
+        if (w < 4 + NIDLE) return -NP - 1;
+        return w - NC - NIDLE - NP;
     }
 };
 
@@ -87,15 +74,8 @@ struct WsOps {
     float gam[DK];            // e^{G_n} per channel
 };
 
-// State and Delta handed from a chain wave to its output wave (SPLIT).
-template <int DK>
-struct WsXchg {
-    f32x4 S[DK / 16][64];  // state before the chunk, accumulator layout
-    u32x4 D[64];           // Delta of the chunk: {hi, lo} bf16x4
-};
-
-template <int DK, int DV, int NC, int NP, bool SPLIT>
-__global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((amdgpu_waves_per_eu(2, 2))) void inter_chunk_ws_kernel(
+template <int DK, int DV, int NC, int NP>
+__global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_waves_per_eu(2, 2))) void inter_chunk_ws_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
     int32_t H, const float *__restrict__ ws, float *__restrict__ o, float *__restrict__ fin,
@@ -116,12 +96,10 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    using Lay = WsLayout<NC, NP, SPLIT>;
-    const int kind = Lay::kind(tid >> 6), widx = Lay::index(tid >> 6);
+    const int role = WsLayout<NC, NP>::role(tid >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
 
-    __shared__ __attribute__((aligned(16))) WsOps<DK> ops[Lay::NSETS];
-    __shared__ __attribute__((aligned(16))) WsXchg<DK> xch[SPLIT ? 2 : 1][SPLIT ? NC : 1];
+    __shared__ __attribute__((aligned(16))) WsOps<DK> ops[2];
 
     const int64_t bos = cu[s], eos = cu[s + 1];
     const int nc = (int)((eos - bos + 15) / 16);
@@ -156,12 +134,12 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
                          c < nc ? WS_FLOATS_PER_CHUNK_HEAD * 4u : 0u);
     };
 
-    if (kind == Lay::IDLE) {
+    if (role == -NP - 1) {
         // idle wave: the same barriers as the others
         if (nc > 0)
             for (int c = 0; c <= nc; ++c) __syncthreads();
-    } else if (kind == Lay::CHAIN) {
-        const int wave = widx;
+    } else if (role >= 0) {
+        const int wave = role;
         // ============================================================ consumer
         // State slice: internal rows 16 b + 4 g4 + jj, column col0 + l16 (accumulator
         // layout); internal row 16 b + 4 g4 + jj is key channel mrow(b, jj) of the
@@ -191,56 +169,12 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
             auto cload = [&](CIn &X, int c) {
                 const rsrc_t rw = rsrc_ws(c);
                 X.tp = buf_load_u32x4(rw, lane * 16u);
-                if (!SPLIT) X.aq = buf_load_u32x4(rw, (64 + lane) * 16u);
+                X.aq = buf_load_u32x4(rw, (64 + lane) * 16u);
                 const rsrc_t rv = rsrc_in(v, c, DV);
                 X.v = buf_load_u32x2(rv, l16 * rowV + (col0 + 4 * g4) * EB);
             };
             auto advance = [&](int ob, const CIn &X, int c) {
                 const WsOps<DK> &P = ops[ob];
-                if constexpr (SPLIT) {
-                    // chain wave: hand S to the output wave, then the recurrence
-                    WsXchg<DK> &XO = xch[c & 1][wave];
-                    bf16x8 kpr[NPAIR];
-#pragma unroll
-                    for (int p = 0; p < NPAIR; ++p) kpr[p] = P.kp[p][lane];
-                    __builtin_amdgcn_sched_barrier(0);
-                    const Split4 Tp = __builtin_bit_cast(Split4, X.tp);
-                    const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, X.v), ID, zero4());
-                    bf16x8 Shi[NPAIR];
-#pragma unroll
-                    for (int p = 0; p < NPAIR; ++p) Shi[p] = cat(to_bf16x4(S[2 * p]), to_bf16x4(S[2 * p + 1]));
-                    f32x4 Xa = zero4(), Xb = zero4();
-#pragma unroll
-                    for (int p = 0; p < NPAIR; ++p) {
-                        if (p & 1) Xb = mma32(kpr[p], Shi[p], Xb);
-                        else Xa = mma32(kpr[p], Shi[p], Xa);
-                    }
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) XO.S[b][lane] = S[b];
-                    Split4 ktr[NB];
-                    f32x4 gmr[NB];
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        ktr[b] = P.kt[b][lane];
-                        gmr[b] = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * g4]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    bf16x8 yhh, dhh;
-                    const bf16x4 ylo = split_lo(vc - (Xa + Xb), NIL, yhh);
-                    const bf16x8 tpp = cat(Tp.hi, Tp.lo);
-                    f32x4 D = mma32(tpp, yhh, zero4());
-                    D = mma32(tpp, cat(ylo, ylo), D);
-                    const bf16x4 dlo = split_lo(D, NIL, dhh);
-                    XO.D[lane] = __builtin_bit_cast(u32x4, cat(__builtin_shufflevector(dhh, dhh, 0, 1, 2, 3), dlo));
-                    const bf16x8 dll = cat(dlo, dlo);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const bf16x8 ktt = cat(ktr[b].hi, ktr[b].lo);
-                        const f32x4 acc = mma32(ktt, dhh, S[b] * gmr[b]);
-                        S[b] = mma32(ktt, dll, acc);
-                    }
-                    return;
-                }
                 // Operand reads go out first, in two batches, so their LDS latency
                 // overlaps the state split and the K+ S products instead of
                 // stalling each matrix-core instruction that consumes them.
@@ -321,10 +255,8 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
             cload(X1, 1);
             cload(X2, 2);
             __syncthreads();  // operand set 0 ready
-            // (with three operand sets, chunk c uses set c % 3: i below, static in
-            // the three-way unrolled loop)
-            auto citer = [&](int c, int i, CIn &X) {
-                advance(SPLIT ? i : (c & 1), X, c);
+            auto citer = [&](int c, CIn &X) {
+                advance(c & 1, X, c);
                 cload(X, c + 3);
                 __syncthreads();  // set c+1 ready; set c free
             };
@@ -334,12 +266,12 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
             // flight, including the ones issued just before.
             int c = 0;
             for (; c + 3 <= nc; c += 3) {
-                citer(c, 0, X0);
-                citer(c + 1, 1, X1);
-                citer(c + 2, 2, X2);
+                citer(c, X0);
+                citer(c + 1, X1);
+                citer(c + 2, X2);
             }
-            if (c < nc) citer(c, 0, X0);
-            if (c + 1 < nc) citer(c + 1, 1, X1);
+            if (c < nc) citer(c, X0);
+            if (c + 1 < nc) citer(c + 1, X1);
         }
         if (fin) {
 #pragma unroll
@@ -348,87 +280,10 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
                 for (int jj = 0; jj < 4; ++jj)
                     fin[(hd * DK + mrow(b, jj)) * DV + col0 + l16] = S[b][jj];
         }
-    } else if (kind == Lay::OUT) {
-        if constexpr (SPLIT) {
-            // ========================================================== output
-            // O of chunk c = Q+_c S + A_qk,c Delta_c, with S (the state before
-            // chunk c) and Delta_c from the chain wave of this slice; done in
-            // iteration c + 1 (operand sets are kept for three chunks).
-            const int wave = widx;
-            const int col0 = (split * NC + wave) * 16;
-            if (nc > 0) {
-                const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
-                auto aload = [&](u32x4 &A, int c) { A = buf_load_u32x4(rsrc_ws(c), (64 + lane) * 16u); };
-                auto out_step = [&](int c, int iset, const u32x4 &Aw) {
-                    const WsOps<DK> &P = ops[iset];
-                    const WsXchg<DK> &XI = xch[c & 1][wave];
-                    bf16x8 qhr[NPAIR], qlr[NPAIR];
-                    f32x4 Sv[NB];
-#pragma unroll
-                    for (int p = 0; p < NPAIR; ++p) {
-                        qhr[p] = P.qp_hi[p][lane];
-                        qlr[p] = P.qp_lo[p][lane];
-                    }
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) Sv[b] = XI.S[b][lane];
-                    const u32x4 dd = XI.D[lane];
-                    // S = Shi + Slo (bf16), residuals on the matrix cores; Q+ S as
-                    // hi*hi + lo*hi + hi*lo in three independent sums
-                    f32x4 Oa = zero4(), Ob = zero4(), Oc = zero4();
-#pragma unroll
-                    for (int p = 0; p < NPAIR; ++p) {
-                        const bf16x8 Shi = cat(to_bf16x4(Sv[2 * p]), to_bf16x4(Sv[2 * p + 1]));
-                        const bf16x8 Slo = cat(to_bf16x4(mma32(NIL, Shi, Sv[2 * p])),
-                                               to_bf16x4(mma32(NIH, Shi, Sv[2 * p + 1])));
-                        Oa = mma32(qhr[p], Shi, Oa);
-                        Ob = mma32(qlr[p], Shi, Ob);
-                        Oc = mma32(qhr[p], Slo, Oc);
-                    }
-                    const Split4 Aq = __builtin_bit_cast(Split4, Aw);
-                    const bf16x8 aqq = cat(Aq.hi, Aq.lo);
-                    const bf16x4 dhi = __builtin_bit_cast(bf16x4, u32x2{dd[0], dd[1]});
-                    const bf16x4 dlo = __builtin_bit_cast(bf16x4, u32x2{dd[2], dd[3]});
-                    f32x4 O = mma32(aqq, cat(dhi, dhi), Oa);
-                    O = mma32(aqq, cat(dlo, dlo), O);
-                    O += Ob + Oc;
-                    const rsrc_t ro = rsrc_out(c);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        buf_store_f32(O[jj], ro, (4 * g4 + jj) * rowO + (col0 + l16) * 4u);
-                };
-                // A_qk of chunk j is held in register set j % 3.
-                u32x4 A0, A1, A2;
-                aload(A0, 0);
-                aload(A1, 1);
-                aload(A2, 2);
-                __syncthreads();  // operand set 0 ready
-                auto oiter = [&](int c, int iprev, u32x4 &Ap) {
-                    if (c >= 1) {
-                        out_step(c - 1, iprev, Ap);
-                        aload(Ap, c + 2);
-                    }
-                    __syncthreads();
-                };
-                int c = 0;  // (loop form as for the consumers)
-                for (; c + 3 <= nc; c += 3) {
-                    oiter(c, 2, A2);
-                    oiter(c + 1, 0, A0);
-                    oiter(c + 2, 1, A1);
-                }
-                if (c < nc) oiter(c, 2, A2);
-                if (c + 1 < nc) oiter(c + 1, 0, A0);
-                // the last chunk: its operands and Delta are visible after the last barrier
-                const int last = nc - 1, il = last % 3;
-                u32x4 Al = A0;
-                if (il == 1) Al = A1;
-                if (il == 2) Al = A2;
-                out_step(last, il, Al);
-            }
-        }
     } else if (nc > 0) {
         // ============================================================ producer
         // Producer pw builds the operands of channel blocks pw * BPW .. + BPW - 1.
-        const int pw = widx;
+        const int pw = role + NP;
         // Constant 0/1 triangles as matrix-core operands (bf16 1.0 = 0x3f80):
         //   LT, B operand of G^T = g^T L^T: lane (g4, n) holds L[n][4 g4 + j] = [4 g4 + j <= n];
         //   UT, A operand of Gs  = U g:     lane (g4, i) holds U[i][4 g4 + j] = [4 g4 + j >  i].
@@ -563,8 +418,8 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
         pload(R0, 3);
         pload(R1, 4);
         __syncthreads();  // operand set 0 ready
-        auto piter = [&](int c, int inext, PIn &R) {
-            produce(A, Lay::NSETS == 3 ? inext : ((c + 1) & 1));
+        auto piter = [&](int c, PIn &R) {
+            produce(A, (c + 1) & 1);
             stage_put(R);
             stage_get(A);
             pload(R, c + 5);
@@ -572,22 +427,22 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP, SPLIT>::NW)) __attribute__((
         };
         int c = 0;  // (loop form as for the consumers)
         for (; c + 3 <= nc; c += 3) {
-            piter(c, 1, R2);
-            piter(c + 1, 2, R0);
-            piter(c + 2, 0, R1);
+            piter(c, R2);
+            piter(c + 1, R0);
+            piter(c + 2, R1);
         }
-        if (c < nc) piter(c, 1, R2);
-        if (c + 1 < nc) piter(c + 1, 2, R0);
+        if (c < nc) piter(c, R2);
+        if (c + 1 < nc) piter(c + 1, R0);
     }
 }
 
-template <int DK, int DV, int NC, int NP, bool SPLIT>
+template <int DK, int DV, int NC, int NP>
 static hipError_t launch_ws_t(const InterChunkArgs &a) {
     const int nchains = a.nseq * a.H;
     const int nsplit = DV / (16 * NC);
     const int64_t grid = ((int64_t)nchains + 7) / 8 * 8 * nsplit;
-    hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP, SPLIT>), dim3((unsigned)grid),
-                       dim3(64 * WsLayout<NC, NP, SPLIT>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
+    hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP>), dim3((unsigned)grid),
+                       dim3(64 * WsLayout<NC, NP>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
                        (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
                        a.H, a.ws, a.o, a.fin, nsplit, nchains);
     return hipGetLastError();
@@ -595,18 +450,13 @@ static hipError_t launch_ws_t(const InterChunkArgs &a) {
 
 // Shapes: consumers NC (16 columns each), producers NP.  Returns
 // hipErrorInvalidValue for a shape that is not instantiated.
-hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw, bool split) {
+hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw) {
 #define KDA_WS_CASE(DKV, DVV, NCV, NPV) \
-    if (a.dk == DKV && a.dv == DVV && ncw == NCV && npw == NPV && !split) \
-        return launch_ws_t<DKV, DVV, NCV, NPV, false>(a);
-#define KDA_WS_SPLIT(DKV, DVV, NCV, NPV) \
-    if (a.dk == DKV && a.dv == DVV && ncw == NCV && npw == NPV && split) \
-        return launch_ws_t<DKV, DVV, NCV, NPV, true>(a);
+    if (a.dk == DKV && a.dv == DVV && ncw == NCV && npw == NPV) return launch_ws_t<DKV, DVV, NCV, NPV>(a);
     // dk = dv = 128: the default shapes (4 or 2 consumers, 4 producers) and
     // the others a tuning sweep may pick
     KDA_WS_CASE(128, 128, 4, 4) KDA_WS_CASE(128, 128, 2, 4) KDA_WS_CASE(128, 128, 4, 2)
     KDA_WS_CASE(128, 128, 1, 4) KDA_WS_CASE(128, 128, 2, 2) KDA_WS_CASE(128, 128, 1, 2)
-    KDA_WS_SPLIT(128, 128, 2, 4)
     // the other head sizes: min(dv/16, 4) or min(dv/16, 2) consumers, min(dk/16, 4) producers
 #define KDA_WS_DEF(DKV, DVV) KDA_WS_CASE(DKV, DVV, ((DVV / 16) < 4 ? (DVV / 16) : 4), ((DKV / 16) < 4 ? (DKV / 16) : 4))
 #define KDA_WS_DEF2(DKV, DVV) KDA_WS_CASE(DKV, DVV, ((DVV / 16) < 2 ? (DVV / 16) : 2), ((DKV / 16) < 4 ? (DKV / 16) : 4))
@@ -616,7 +466,6 @@ hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw, bool
 #undef KDA_WS_ROW
 #undef KDA_WS_DEF2
 #undef KDA_WS_DEF
-#undef KDA_WS_SPLIT
 #undef KDA_WS_CASE
     return hipErrorInvalidValue;
 }

@@ -54,6 +54,6 @@ hipError_t launch_chunk_local(const ChunkLocalArgs &a);
 hipError_t launch_inter_chunk(const InterChunkArgs &a);
 // Warp-specialised inter-chunk kernel (bf16, dk >= 32): ncw consumer and npw
 // producer waves per workgroup; hipErrorInvalidValue for a shape not built.
-hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw, bool split);
+hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw);
 
 }  // namespace kda
