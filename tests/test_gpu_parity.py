@@ -284,6 +284,43 @@ def test_bitwise_deterministic(dev):
     assert torch.equal(o1, o2) and torch.equal(st1, st2)
 
 
+def test_graph_replays_match_eager(dev):
+    """The three-call step (chunk-local, inter-chunk, decode of one more token from the
+    final states) captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bitwise.  The library
+    enqueues kernels only (no memsets, no allocation), so it can be captured."""
+    w = workloads.custom([256, 256], 2, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=31)
+    d = workloads.decode_step_inputs(workloads.custom([1, 1], 2, 128, 128), 0, device=dev, seed=32)
+    ws = kda.alloc_workspace(w.total_tokens, w.nseq, w.H, w.dk, w.dv, torch.bfloat16, dev)
+    o = torch.empty((w.total_tokens, w.H, w.dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.nseq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    od = torch.empty((w.nseq, w.H, w.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+        kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
+                            o=o, final_state=fin)
+        kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (o.clone(), fin.clone(), od.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        o.zero_(), fin.zero_(), od.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert torch.equal(o, ref[0]) and torch.equal(fin, ref[1]) and torch.equal(od, ref[2])
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(od, ref[2])
+
+
 @pytest.mark.parametrize("knob,values", [
     ("KDA_WAVES", ("2", "4", "8")),                          # one-role kernel
     ("KDA_WS", ("4x4", "2x4", "4x2", "1x4", "2x2", "1x2")),  # consumer x producer waves
