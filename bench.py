@@ -9,6 +9,8 @@ cannot stay resident in the 256 MB Infinity Cache.
 The JSON line also carries, measured in the same run:
   * "k3_layer": prefill of B=1, H=96, T=65,536 (the K3 layer shape),
   * "decode":   128 recurrent steps over B=256 x H=96 heads (1.6 GB of fp32 state),
+  * "decode_window_4" / "_8": the same 128 steps as windows of 4 or 8 draft tokens
+    (speculative verification: one state read and write per window),
   * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
 each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
 
@@ -52,6 +54,12 @@ def inter_chunk_bytes_per_token_head(dk: int, dv: int, in_bytes: int = 2) -> flo
 def decode_bytes_per_head(dk: int, dv: int, in_bytes: int = 2) -> float:
     """Decode step: fp32 state read + written, q, k, log_alpha, v, beta read, o written."""
     return 2 * dk * dv * 4 + in_bytes * (3 * dk + dv + 1) + 4 * dv
+
+
+def window_bytes_per_head(dk: int, dv: int, T: int, in_bytes: int = 2) -> float:
+    """Decode window of T tokens: fp32 state read + written once, T tokens of inputs read and
+    outputs written."""
+    return 2 * dk * dv * 4 + T * (in_bytes * (3 * dk + dv + 1) + 4 * dv)
 
 
 def log(msg: str) -> None:
@@ -252,12 +260,10 @@ def bench_prefill_workload(index, torch, kda, workloads, dev, reps: int):
     return res
 
 
-def bench_decode(torch, kda, workloads, dev):
+def bench_decode(torch, kda, workloads, dev, steps):
     w = workloads.workload(4)
     B, H, dk, dv = w.nseq, w.H, w.dk, w.dv
-    log(f"[bench] generating decode workload: {w.notes}")
     state = workloads.decode_initial_state(B, H, dk, dv, device=dev)
-    steps = [workloads.decode_step_inputs(w, s, device=dev) for s in range(w.decode_steps)]
     o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
     # one untimed warm-up step on a scratch copy of the state
     scratch = state.clone()
@@ -276,7 +282,41 @@ def bench_decode(torch, kda, workloads, dev):
     res = {"workload": w.name, "heads": B * H, "steps": w.decode_steps, "ms_per_step": round(ms, 5),
            "bytes_per_step": per_step, "gbs": gbs, "hbm_peak_frac": gbs / HBM_PEAK_GBS,
            "tokens_per_s": B / (ms * 1e-3)}
-    del state, steps, o
+    del state, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_window(torch, kda, workloads, dev, steps, T: int):
+    """The decode workload's steps regrouped into windows of T drafts (speculative verification):
+    one kda_decode_window call per window, accepted counts uniform on [1, T] per sequence."""
+    w = workloads.workload(4)
+    B, H, dk, dv = w.nseq, w.H, w.dk, w.dv
+    state = workloads.decode_initial_state(B, H, dk, dv, device=dev)
+    names = ("q", "k", "v", "log_alpha", "beta")
+    nwin = len(steps) // T
+    wins = [{n: torch.stack([steps[i * T + t][n] for t in range(T)], dim=1).contiguous() for n in names}
+            for i in range(nwin)]
+    accs = [workloads.window_accept(B, T, device=dev, seed=i, lo=1) for i in range(nwin)]
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    scratch = state.clone()
+    kda.kda_decode_window(*(wins[0][n] for n in names), scratch, accs[0], o=o)
+    del scratch
+    torch.cuda.synchronize()
+    t = Timer(torch, nwin)
+    for x, a in zip(wins, accs):
+        with t:
+            kda.kda_decode_window(*(x[n] for n in names), state, a, o=o)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    per_win = B * H * window_bytes_per_head(dk, dv, T)
+    gbs = per_win / (ms * 1e-3) / 1e9
+    accepted = float(torch.stack(accs).double().mean()) * B
+    res = {"workload": f"{w.name}_window", "T": T, "heads": B * H, "windows": nwin,
+           "ms_per_window": round(ms, 5), "bytes_per_window": per_win, "gbs": gbs,
+           "hbm_peak_frac": gbs / HBM_PEAK_GBS, "draft_tokens_per_s": B * T / (ms * 1e-3),
+           "accepted_tokens_per_s": accepted / (ms * 1e-3)}
+    del state, wins, o
     torch.cuda.empty_cache()
     return res
 
@@ -348,7 +388,14 @@ def main() -> int:
         out["k3_layer"] = bench_prefill_workload(3, torch, kda, workloads, dev, reps=5)
     if args.only in ("all", "decode"):
         log("[bench] recurrent decode B=256 H=96, 128 steps")
-        out["decode"] = bench_decode(torch, kda, workloads, dev)
+        w4 = workloads.workload(4)
+        steps = [workloads.decode_step_inputs(w4, s, device=dev) for s in range(w4.decode_steps)]
+        out["decode"] = bench_decode(torch, kda, workloads, dev, steps)
+        for T in (4, 8):
+            log(f"[bench] decode windows of {T} drafts (speculative verification), B=256 H=96")
+            out[f"decode_window_{T}"] = bench_decode_window(torch, kda, workloads, dev, steps, T)
+        del steps
+        torch.cuda.empty_cache()
     if args.only in ("all", "varlen"):
         log("[bench] varlen 1M-token prefill")
         out["varlen_1m"] = bench_prefill_workload(5, torch, kda, workloads, dev, reps=3)

@@ -9,7 +9,7 @@ first call raises.
 
 Names mirror the C entry points:
     kda_prefill, kda_chunk_local, kda_inter_chunk, kda_decode_step,
-    kda_prefill_workspace_bytes, kda_status_string.
+    kda_decode_window, kda_prefill_workspace_bytes, kda_status_string.
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
-           "kda_decode_step", "kda_status_string", "kda_last_hip_error")
+           "kda_decode_step", "kda_decode_window", "kda_status_string", "kda_last_hip_error")
 
 _lib = None
 
@@ -61,6 +61,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                     vp, sz, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.kda_decode_window.restype = ctypes.c_int
+    lib.kda_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                      vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_hip_error.restype = i32
@@ -103,7 +106,7 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _check_inputs(q, k, v, log_alpha, beta):
+def _check_tensors(q, k, v, log_alpha, beta):
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -113,6 +116,10 @@ def _check_inputs(q, k, v, log_alpha, beta):
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, log_alpha and beta must share one dtype")
+
+
+def _check_inputs(q, k, v, log_alpha, beta):
+    _check_tensors(q, k, v, log_alpha, beta)
     N, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != (N, H, dk) or log_alpha.shape != (N, H, dk) or v.shape != (N, H, dv) or beta.shape != (N, H):
@@ -208,3 +215,34 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None, stream=None) -> 
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o), B, H, dk, dv,
         _dtype_code(q.dtype), _stream(stream)))
     return o
+
+
+def kda_decode_window(q, k, v, log_alpha, beta, state, accept=None, *, o=None, output_o: bool = True,
+                      stream=None) -> Optional[torch.Tensor]:
+    """A window of T tokens per sequence (speculative verification); ``state`` is updated in place.
+
+    q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H].  ``accept``: int32 [B] on
+    the device (None = all T accepted); the state ends after the first clamp(accept[b], 0, T)
+    tokens of sequence b.  Returns o fp32 [B, T, H, dv] (the output of every token of the
+    window), or None with ``output_o=False``.
+    """
+    _check_tensors(q, k, v, log_alpha, beta)
+    if q.dim() != 4:
+        raise ValueError("expected q, k, log_alpha [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, T, H, dk) or log_alpha.shape != (B, T, H, dk) or v.shape != (B, T, H, dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("expected q, k, log_alpha [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv) or not state.is_contiguous() \
+            or state.device != q.device:
+        raise ValueError("state must be contiguous fp32 [B, H, dk, dv] on the inputs' device")
+    if accept is not None and (accept.dtype != torch.int32 or tuple(accept.shape) != (B,)
+                               or accept.device != q.device or not accept.is_contiguous()):
+        raise ValueError("accept must be a contiguous int32 [B] tensor on the inputs' device")
+    if output_o and o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    _check(load_library().kda_decode_window(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o if output_o else None),
+        _ptr(accept), B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
+    return o if output_o else None

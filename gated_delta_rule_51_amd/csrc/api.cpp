@@ -150,6 +150,23 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const vo
     return hip_status(kda::launch_decode(a));
 }
 
+kda_status kda_decode_window(const void *q, const void *k, const void *v, const void *log_alpha,
+                             const void *beta, float *state, float *o, const int32_t *accept,
+                             int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                             void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || (int64_t)B * T * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, true);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({state}, {o});
+    if (st != KDA_OK) return st;
+    if (accept && (reinterpret_cast<uintptr_t>(accept) & 3u)) return KDA_ERR_ALIGN;
+    kda::DecodeWindowArgs a{q, k, v, log_alpha, beta, state, o, accept,
+                            B, T, H, dk, dv, dt == KDA_BF16, stream};
+    return hip_status(kda::launch_decode_window(a));
+}
+
 const char *kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";

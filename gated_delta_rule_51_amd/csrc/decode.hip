@@ -31,10 +31,10 @@
 
 namespace kda {
 
-template <int DK, int DV>
+template <int DK, int DV, int MAXT = 1024>
 struct DecodeShape {
     static constexpr int NC4 = DV / 4;                       // column quads per row
-    static constexpr int RP_CAP = 1024 / NC4 < 64 ? 1024 / NC4 : 64;
+    static constexpr int RP_CAP = MAXT / NC4 < 64 ? MAXT / NC4 : 64;
     static constexpr int RP = DK < RP_CAP ? DK : RP_CAP;     // row groups (>= 16)
     static constexpr int NT = NC4 * RP;                      // threads per workgroup
     static constexpr int NR = DK / RP;                       // rows per thread
@@ -154,6 +154,192 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     }
 }
 
+// A window of Tw consecutive tokens per sequence (speculative-decoding
+// verification and replay; Kimi K3 report digest, serving section): the state
+// of each (sequence, head) is read once, carried through the window in
+// registers, and written back once -- the state after the first acc tokens,
+// acc = accept[b] clamped to [0, Tw] (all Tw without accept; no write when 0) --
+// while o gets the output of every token of the window.  Per token the work is
+// the single-token step above; the next token's inputs are loaded while the
+// current token is reduced, and the next head's state during the window's first
+// token, so its latency hides behind the whole window.  With Tw tokens per state
+// pass the kernel does Tw times the arithmetic per byte of the single step, so
+// beyond a few tokens it is bound by the vector ALUs, not HBM: the workgroups
+// are half as large (two per compute unit, at most 128 registers per lane) so
+// that one's barrier waits are filled by the other's arithmetic.  Inputs are
+// [B, Tw, H, ...] (token-major within a sequence).
+// Threads per window workgroup, at most.
+constexpr int WINDOW_THREADS = 512;
+
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__((DecodeShape<DK, DV, WINDOW_THREADS>::NT))
+__attribute__((amdgpu_waves_per_eu((2 * DecodeShape<DK, DV, WINDOW_THREADS>::NT + 255) / 256, 8)))
+void decode_window_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
+    float *__restrict__ o, const int32_t *__restrict__ accept, int64_t heads, int32_t H, int32_t Tw) {
+    using Sh = DecodeShape<DK, DV, WINDOW_THREADS>;
+    constexpr int NC4 = Sh::NC4, RP = Sh::RP, NR = Sh::NR, P = Sh::P, NKW = Sh::NKW;
+    const int tid = threadIdx.x;
+    const int c4 = tid % NC4;
+    const int rg = tid / NC4;
+    const int64_t stride = gridDim.x;
+
+    __shared__ float s_k[DK], s_q[DK], s_a[DK];
+    __shared__ __attribute__((aligned(16))) float s_red[2][RP][Sh::STRIDE];
+    __shared__ __attribute__((aligned(16))) float s_fin[2][DV];
+    __shared__ float s_kq[2][NKW];
+
+    struct Tok {
+        float k, q, g, b;  // k, q, g of key channel tid (tid < DK)
+        f32x4 v;           // v of columns 4 c4 .. +3
+    };
+    // Token inputs through buffer resources based at the token's row (uniform),
+    // so every lane offset is a loop-invariant 32-bit register.  Head indices
+    // stay below 2^31 (B * T * H < 2^31 is checked on the host).
+    auto load_tok = [&](Tok &x, uint32_t hd, int t) {
+        const uint32_t bq = hd / (uint32_t)H;
+        const int64_t row = ((int64_t)bq * Tw + t) * H + (hd - bq * (uint32_t)H);
+        if (tid < DK) {
+            const uint32_t off = tid * (uint32_t)sizeof(T);
+            const rsrc_t rk = make_rsrc(k + row * DK, DK * sizeof(T));
+            const rsrc_t rq = make_rsrc(q + row * DK, DK * sizeof(T));
+            const rsrc_t rgt = make_rsrc(g + row * DK, DK * sizeof(T));
+            if constexpr (sizeof(T) == 4) {
+                x.k = __uint_as_float(buf_load_u32(rk, off));
+                x.q = __uint_as_float(buf_load_u32(rq, off));
+                x.g = __uint_as_float(buf_load_u32(rgt, off));
+            } else {
+                x.k = bf16_bits_to_f32(buf_load_u16(rk, off));
+                x.q = bf16_bits_to_f32(buf_load_u16(rq, off));
+                x.g = bf16_bits_to_f32(buf_load_u16(rgt, off));
+            }
+        } else {
+            x.k = x.q = x.g = 0.f;
+        }
+        const rsrc_t rv = make_rsrc(v + row * DV, DV * sizeof(T));
+        if constexpr (sizeof(T) == 4)
+            x.v = __builtin_bit_cast(f32x4, buf_load_u32x4(rv, 16u * c4));
+        else
+            x.v = unpack_bf16x4(buf_load_u32x2(rv, 8u * c4));
+        x.b = load_in(beta + row);
+    };
+    // State rows go through a buffer resource per head: one 32-bit lane offset
+    // (row rg, quad c4) serves all NR rows, the row step is the uniform offset.
+    const uint32_t soff = (uint32_t)(rg * DV + 4 * c4) * 4u;
+    constexpr uint32_t ROW_STEP = RP * DV * 4u, NT_POLICY = 2;  // non-temporal
+    auto state_rsrc = [&](int64_t hd) {
+        return make_rsrc(state + hd * (int64_t)(DK * DV), DK * DV * 4u);
+    };
+    auto load_rows = [&](f32x4 (&rows)[NR], int64_t hd) {
+        const rsrc_t rs = state_rsrc(hd);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            rows[r] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff, r * ROW_STEP, NT_POLICY));
+    };
+
+    Tok cur, nxt;
+    int par = 0;
+    // One (sequence, head): the window's tokens in order, the state rows in
+    // registers throughout.  The next head's state rows (into nrows) are
+    // loaded during the first token, its first token during the last.
+    auto window = [&](f32x4 (&rows)[NR], f32x4 (&nrows)[NR], int64_t head) {
+        const int64_t bq = head / H;
+        int acc = Tw;
+        if (accept) {
+            acc = accept[bq];
+            acc = acc < 0 ? 0 : (acc > Tw ? Tw : acc);
+        }
+        const bool more = head + stride < heads;
+        const rsrc_t rs = state_rsrc(head);
+        for (int t = 0; t < Tw; ++t) {
+            // LDS reuse across tokens as across heads in the single-token kernel
+            if (tid < DK) {
+                s_k[tid] = cur.k;
+                s_q[tid] = cur.q;
+                s_a[tid] = decay_exp(cur.g);
+            }
+            if (tid < 64 * NKW) {
+                float kq = cur.k * cur.q;
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
+                if ((tid & 63) == 0) s_kq[par][tid >> 6] = kq;
+            }
+            const f32x4 vv = cur.v;
+            const float bb = cur.b;
+            if (t == 0 && more) load_rows(nrows, head + stride);
+            if (t + 1 < Tw) {
+                load_tok(nxt, head, t + 1);
+            } else if (more) {
+                load_tok(nxt, head + stride, 0);
+            }
+            __syncthreads();
+
+            f32x4 pv = zero4(), pq = zero4();
+            float kr[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const int row = rg + r * RP;
+                kr[r] = s_k[row];
+                rows[r] = rows[r] * s_a[row];  // forget
+                pv += kr[r] * rows[r];
+                pq += s_q[row] * rows[r];
+            }
+            *reinterpret_cast<f32x4 *>(&s_red[0][rg][4 * c4]) = pv;
+            *reinterpret_cast<f32x4 *>(&s_red[1][rg][4 * c4]) = pq;
+            __syncthreads();
+            {
+                const int out = tid / P, part = tid % P;
+                const int arr = out / DV, col = out % DV;
+                float x = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x += s_red[arr][part + P * j][col];
+#pragma unroll
+                for (int m = 1; m < P; m <<= 1) x += __shfl_xor(x, m);
+                if (part == 0) s_fin[arr][col] = x;
+            }
+            __syncthreads();
+
+            const f32x4 vhat = *reinterpret_cast<const f32x4 *>(&s_fin[0][4 * c4]);
+            const f32x4 rq = *reinterpret_cast<const f32x4 *>(&s_fin[1][4 * c4]);
+            float kq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
+            const f32x4 delta = bb * (vv - vhat);
+            if (o && rg == 0) {
+                const int64_t row = (bq * Tw + t) * H + (head - bq * H);
+                reinterpret_cast<f32x4 *>(o + row * DV)[c4] = rq + kq * delta;
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) rows[r] += kr[r] * delta;  // erase + write
+            if (t + 1 == acc) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, rows[r]), rs, soff,
+                                                           r * ROW_STEP, NT_POLICY);
+            }
+            cur = nxt;
+            par ^= 1;
+        }
+    };
+
+    int64_t head = blockIdx.x;
+    if (head >= heads) return;
+    f32x4 ra[NR], rb[NR];
+    load_rows(ra, head);
+    load_tok(cur, head, 0);
+    nxt = cur;
+    for (;;) {  // two heads per trip so the register sets swap roles without copies
+        window(ra, rb, head);
+        head += stride;
+        if (head >= heads) break;
+        window(rb, ra, head);
+        head += stride;
+        if (head >= heads) break;
+    }
+}
+
 template <int DK, int DV, typename T>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
     using Sh = DecodeShape<DK, DV>;
@@ -179,6 +365,33 @@ static hipError_t launch_decode_dt(const DecodeArgs &a) {
 
 hipError_t launch_decode(const DecodeArgs &a) {
     return a.bf16 ? launch_decode_dt<__bf16>(a) : launch_decode_dt<float>(a);
+}
+
+template <int DK, int DV, typename T>
+static hipError_t launch_window_t(const DecodeWindowArgs &a) {
+    using Sh = DecodeShape<DK, DV, WINDOW_THREADS>;
+    const int64_t heads = (int64_t)a.B * a.H;
+    const int64_t cap = GRID_THREADS / Sh::NT;
+    const int64_t grid = heads < cap ? heads : cap;
+    hipLaunchKernelGGL((decode_window_kernel<DK, DV, T>), dim3((unsigned)grid), dim3(Sh::NT), 0,
+                       (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.v,
+                       (const T *)a.g, (const T *)a.beta, a.state, a.o, a.accept, heads, a.H, a.T);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_window_dt(const DecodeWindowArgs &a) {
+#define KDA_WIN_CASE(DKV, DVV) \
+    if (a.dk == DKV && a.dv == DVV) return launch_window_t<DKV, DVV, T>(a);
+#define KDA_WIN_ROW(DKV) KDA_WIN_CASE(DKV, 16) KDA_WIN_CASE(DKV, 32) KDA_WIN_CASE(DKV, 64) KDA_WIN_CASE(DKV, 128)
+    KDA_WIN_ROW(16) KDA_WIN_ROW(32) KDA_WIN_ROW(64) KDA_WIN_ROW(128)
+#undef KDA_WIN_ROW
+#undef KDA_WIN_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_window(const DecodeWindowArgs &a) {
+    return a.bf16 ? launch_window_dt<__bf16>(a) : launch_window_dt<float>(a);
 }
 
 }  // namespace kda

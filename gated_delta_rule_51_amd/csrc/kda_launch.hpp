@@ -26,6 +26,15 @@ struct DecodeArgs {
     void *stream;
 };
 
+struct DecodeWindowArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *state, *o;          // o may be NULL (no outputs)
+    const int32_t *accept;     // device [B] or NULL (all T tokens accepted)
+    int32_t B, T, H, dk, dv;
+    bool bf16;
+    void *stream;
+};
+
 struct ChunkLocalArgs {
     const void *q, *k, *g, *beta;
     const int32_t *cu;
@@ -50,6 +59,7 @@ struct InterChunkArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_decode_window(const DecodeWindowArgs &a);
 hipError_t launch_chunk_local(const ChunkLocalArgs &a);
 hipError_t launch_inter_chunk(const InterChunkArgs &a);
 // Warp-specialised inter-chunk kernel (bf16, dk >= 32): ncw consumer and npw

@@ -35,6 +35,8 @@
  *   Decode: q, k, log_alpha [B, H, dk], v [B, H, dv], beta [B, H], state fp32
  *   [B, H, dk, dv] updated in place (the in-place per-step state update that
  *   the serving section names as the decode bottleneck), o fp32 [B, H, dv].
+ *   Decode window: as decode with a window axis T after B (see
+ *   kda_decode_window).
  *
  * Supported shapes: dk, dv in {16, 32, 64, 128} (any combination); H >= 1;
  * nseq >= 1; total_tokens >= 0 (< 2^31).  Chunk length is fixed at 16 tokens.
@@ -142,6 +144,40 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const void *log_alpha, const void *beta,
                            float *state, float *o, int32_t B, int32_t H,
                            int32_t dk, int32_t dv, kda_dtype dt, void *stream);
+
+/* A window of T consecutive tokens per sequence in one call, for speculative
+ * decoding: the T draft tokens of each sequence are verified in one pass and
+ * the state is advanced only over the tokens the verifier accepted.  (Serving
+ * section of the same page: the decode step is bound by the in-place state
+ * update, and a speculative-decoding scheme has to replay the recurrence over
+ * the accepted tokens; the plain reading taken here is that the accepted
+ * tokens are a prefix of the window.)
+ *
+ * Per (sequence b, head h) this equals T calls of kda_decode_step on the
+ * tokens of the window in order, except that the state is read once and
+ * written at most once: o receives the output of every token of the window
+ * (computed from the running state, as if every draft were accepted so far),
+ * while state receives the state after the first acc = clamp(accept[b], 0, T)
+ * tokens.  acc == 0 leaves the state untouched (not even rewritten).
+ *
+ *   q, k, log_alpha : [B, T, H, dk]   v : [B, T, H, dv]   beta : [B, T, H]
+ *                     (one dtype, KDA_BF16 or KDA_F32; alignment as above)
+ *   state           : fp32 [B, H, dk, dv], device, updated in place.
+ *   o               : fp32 [B, T, H, dv], or NULL (outputs not written).
+ *   accept          : int32 [B] in DEVICE memory (4-byte aligned), or NULL
+ *                     (all T tokens accepted).  Values outside [0, T] are
+ *                     clamped.
+ *   B, H >= 1, T >= 1, B * T * H < 2^31.
+ *
+ * State traffic is that of one decode step per window, so a T-token window
+ * costs far less than T single steps while T stays small; long windows
+ * (hundreds of tokens) belong to kda_prefill instead.  Errors as for
+ * kda_decode_step. */
+kda_status kda_decode_window(const void *q, const void *k, const void *v,
+                             const void *log_alpha, const void *beta,
+                             float *state, float *o, const int32_t *accept,
+                             int32_t B, int32_t T, int32_t H, int32_t dk,
+                             int32_t dv, kda_dtype dt, void *stream);
 
 /* Static string naming a status code. */
 const char *kda_status_string(kda_status s);

@@ -106,6 +106,22 @@ def test_decode_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 80, 1, None) == 4
 
 
+def test_decode_window_rejects_bad_arguments(lib):
+    f = lib.kda_decode_window
+    # q k v g beta state o accept B T H dk dv dt stream
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 1, 4, 1, 16, 16, 1, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 16, 16, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 4, 1, 16, 16, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None, 1, 4, 1, 16, 16, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None, 1, 4, 1, 16, 16, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 4, 1, 16, 16, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 0, 1, 16, 16, 1, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 1, 16, 16, 1, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1 << 16, 1 << 8, 1 << 7, 16, 16, 1, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 16, 24, 1, None) == 4
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 16, 16, 3, None) == 4
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
 

@@ -155,6 +155,112 @@ def test_workload4_decode_sampled_heads(dev):
     torch.cuda.empty_cache()
 
 
+# ----------------------------------------------------------------- decode windows
+
+def _oracle_window(x, init, accepts):
+    """T oracle decode steps from ``init``; the state kept per sequence is the one after its
+    first accepts[b] tokens.  Returns (o [B, T, H, dv], state [B, H, dk, dv]) in float64."""
+    T = x["q"].shape[1]
+    st = init.detach().cpu().double().numpy()
+    snaps, outs = [st], []
+    for t in range(T):
+        ot, st = oracle.decode(*(x[n][:, t].cpu() for n in ("q", "k", "v", "log_alpha", "beta")), st)
+        outs.append(ot)
+        snaps.append(st)
+    return np.stack(outs, axis=1), np.stack([snaps[a][b] for b, a in enumerate(accepts)])
+
+
+def _window_case(dev, B, T, H, dk, dv, dtype, accept, seed=0, output_o=True):
+    w = workloads.custom([1] * B, H, dk, dv, dtype)
+    x = workloads.decode_window_inputs(w, T, 0, device=dev, seed=seed)
+    init = workloads.random_state(B, H, dk, dv, device=dev, seed=seed)
+    state = init.clone()
+    acc = None if accept is None else torch.tensor(accept, dtype=torch.int32, device=dev)
+    say(f"  case: window B={B} T={T} H={H} dk={dk} dv={dv} {dtype} accept={accept} o={output_o}")
+    o = kda.kda_decode_window(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state, acc,
+                              output_o=output_o)
+    torch.cuda.synchronize()
+    accepts = [T] * B if accept is None else [min(max(a, 0), T) for a in accept]
+    o_ref, st_ref = _oracle_window(x, init, accepts)
+    if output_o:
+        assert_close(o, o_ref, TOL[dtype], "window o")
+    else:
+        assert o is None
+    assert_close(state, st_ref, TOL[dtype], "window state")
+    for b, a in enumerate(accepts):
+        if a == 0:
+            assert torch.equal(state[b], init[b]), f"sequence {b} accepted nothing but its state changed"
+    return x, init, state, o
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.float32, 16, 16), (torch.float32, 128, 128),
+                                         (torch.bfloat16, 128, 128), (torch.bfloat16, 64, 32),
+                                         (torch.bfloat16, 32, 128), (torch.float32, 16, 64)])
+def test_decode_window_matches_oracle(dev, dtype, dk, dv):
+    """Five sequences, windows of 5 drafts, accepted counts 0, 2, 5 and two out of range."""
+    _window_case(dev, 5, 5, 3, dk, dv, dtype, [0, 2, 5, 9, -3], seed=dk + dv)
+
+
+def test_decode_window_without_accept_or_outputs(dev):
+    _window_case(dev, 2, 3, 2, 128, 128, torch.bfloat16, None, seed=3)
+    _window_case(dev, 3, 4, 2, 128, 64, torch.bfloat16, [1, 4, 3], seed=4, output_o=False)
+
+
+def test_decode_window_equals_decode_steps(dev):
+    """A fully accepted window and the same tokens through kda_decode_step one by one; a
+    window of one token and a single step."""
+    w = workloads.custom([1] * 4, 3, 128, 128, torch.bfloat16)
+    x = workloads.decode_window_inputs(w, 6, 0, device=dev, seed=11)
+    init = workloads.random_state(4, 3, 128, 128, device=dev, seed=11)
+    sw, ss = init.clone(), init.clone()
+    ow = kda.kda_decode_window(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], sw)
+    os_ = torch.stack([kda.kda_decode_step(*(x[n][:, t].contiguous()
+                                             for n in ("q", "k", "v", "log_alpha", "beta")), ss)
+                       for t in range(6)], dim=1)
+    torch.cuda.synchronize()
+    assert_close(ow, os_, 1e-6, "window vs steps o")
+    assert_close(sw, ss, 1e-6, "window vs steps state")
+    s1, s2 = init.clone(), init.clone()
+    o1 = kda.kda_decode_window(*(x[n][:, :1].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")), s1)
+    o2 = kda.kda_decode_step(*(x[n][:, 0].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")), s2)
+    torch.cuda.synchronize()
+    assert_close(o1[:, 0], o2, 1e-6, "one-token window vs step o")
+    assert_close(s1, s2, 1e-6, "one-token window vs step state")
+
+
+def test_decode_window_many_heads_per_workgroup(dev):
+    """1,100 heads of 128x128: more than the persistent grid holds, so workgroups carry the
+    state of a second head in the other register set; every head checked."""
+    _window_case(dev, 550, 3, 2, 128, 128, torch.float32,
+                 workloads.window_accept(550, 3, seed=5).tolist(), seed=5)
+
+
+def test_decode_window_workload_sampled_heads(dev):
+    """The decode workload's shape (B=256 x H=96), windows of 4 drafts, two windows in a row
+    with seeded accepted counts; oracle on 48 sampled heads."""
+    w = workloads.workload(4)
+    B, H, T = w.nseq, w.H, 4
+    state = workloads.decode_initial_state(B, H, w.dk, w.dv, device=dev)
+    rng = np.random.default_rng(1)
+    bi = torch.tensor(rng.integers(0, B, 48), device=dev)
+    hi = torch.tensor(rng.integers(0, H, 48), device=dev)
+    ref_state = state[bi, hi].cpu().double().numpy()        # [48, dk, dv], as 48 sequences of 1 head
+    say(f"  case: decode window B={B} H={H} T={T}, 2 windows")
+    for win in range(2):
+        x = workloads.decode_window_inputs(w, T, win, device=dev)
+        acc = workloads.window_accept(B, T, device=dev, seed=win)
+        o = kda.kda_decode_window(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state, acc)
+        torch.cuda.synchronize()
+        sub = {n: x[n][bi, :, hi].unsqueeze(2).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")}
+        accepts = acc[bi].tolist()
+        o_ref, st = _oracle_window(sub, torch.from_numpy(ref_state).unsqueeze(1), accepts)
+        ref_state = st[:, 0]
+        assert_close(o[bi, :, hi], o_ref[:, :, 0], TOL[torch.bfloat16], f"window {win} o")
+        assert_close(state[bi, hi], ref_state, TOL[torch.bfloat16], f"window {win} state")
+    del state
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.slow
 def test_workload5_varlen_1m_sampled_head(dev):
     """1,048,576 packed tokens in ~27 log-uniform sequences, H=96: full run, oracle on 1 head."""

@@ -17,6 +17,10 @@ Value distributions follow the five workloads the library is measured on:
 5. ``varlen_1m``   1,048,576 packed tokens, sequence lengths log-uniform in
                    [512, 262,144], H=96, d=128, distributions as in 2.
 
+Decode windows (speculative verification) regroup the decode workload's steps:
+window i of T tokens holds steps i*T .. i*T+T-1, and the number of accepted
+drafts per sequence is uniform on [lo, T].
+
 Keys are L2-normalised by the caller in the Kimi K3 design (report digest,
 "Kimi Delta Attention": q and k are L2-normalised after the short convolution),
 so the generator normalises k in fp32 before rounding to the input dtype.
@@ -32,7 +36,7 @@ import torch
 
 CHUNK = 16
 GATE_LOWER_BOUND = -5.0
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "state": 6, "lengths": 7}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "state": 6, "lengths": 7, "accept": 8}
 
 
 @dataclass(frozen=True)
@@ -197,6 +201,20 @@ def decode_step_inputs(w: Workload, step: int, device="cpu", seed: int = 0) -> D
         out[kind] = _fill(kind, shape, gen, device, w.dtype, max(B, 1), w.gate)
     out["log_alpha"] = out.pop("g")
     return out
+
+
+def decode_window_inputs(w: Workload, T: int, window: int, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """q, k, v, log_alpha [B, T, H, d] and beta [B, T, H]: decode steps window*T .. window*T+T-1
+    stacked along a window axis after B (the same values decode_step_inputs gives per step)."""
+    steps = [decode_step_inputs(w, window * T + t, device=device, seed=seed) for t in range(T)]
+    return {n: torch.stack([s[n] for s in steps], dim=1).contiguous() for n in steps[0]}
+
+
+def window_accept(B: int, T: int, device="cpu", seed: int = 0, lo: int = 0) -> torch.Tensor:
+    """int32 [B]: accepted drafts per sequence, uniform on [lo, T]."""
+    gen = _gen("cpu", seed, 4, TENSOR_IDS["accept"])
+    a = torch.randint(lo, T + 1, (B,), generator=gen, dtype=torch.int64)
+    return a.to(dtype=torch.int32, device=device)
 
 
 def random_state(nseq: int, H: int, dk: int, dv: int, device="cpu", seed: int = 0, scale: float = 1.0) -> torch.Tensor:
