@@ -170,9 +170,11 @@ def _oracle_window(x, init, accepts):
     return np.stack(outs, axis=1), np.stack([snaps[a][b] for b, a in enumerate(accepts)])
 
 
-def _window_case(dev, B, T, H, dk, dv, dtype, accept, seed=0, output_o=True):
-    w = workloads.custom([1] * B, H, dk, dv, dtype)
+def _window_case(dev, B, T, H, dk, dv, dtype, accept, seed=0, output_o=True, gate="neg_softplus", edit=None):
+    w = workloads.custom([1] * B, H, dk, dv, dtype, gate)
     x = workloads.decode_window_inputs(w, T, 0, device=dev, seed=seed)
+    if edit is not None:
+        edit(x)
     init = workloads.random_state(B, H, dk, dv, device=dev, seed=seed)
     state = init.clone()
     acc = None if accept is None else torch.tensor(accept, dtype=torch.int32, device=dev)
@@ -204,6 +206,18 @@ def test_decode_window_matches_oracle(dev, dtype, dk, dv):
 def test_decode_window_without_accept_or_outputs(dev):
     _window_case(dev, 2, 3, 2, 128, 128, torch.bfloat16, None, seed=3)
     _window_case(dev, 3, 4, 2, 128, 64, torch.bfloat16, [1, 4, 3], seed=4, output_o=False)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_window_long_strong_decay(dev, dtype):
+    """Windows of 20 tokens with log-decay uniform on [-5, 0) and, in a second case, at the
+    bound -5 for every channel and token; accepted counts 0 to 20."""
+    acc = [0, 7, 8, 9, 16, 17, 20]
+    _window_case(dev, 7, 20, 2, 128, 128, dtype, acc, seed=21, gate="uniform")
+
+    def floor(x):
+        x["log_alpha"].fill_(-5.0)
+    _window_case(dev, 7, 20, 2, 64, 128, dtype, acc, seed=22, edit=floor)
 
 
 def test_decode_window_equals_decode_steps(dev):
