@@ -9,7 +9,8 @@ first call raises.
 
 Names mirror the C entry points:
     kda_prefill, kda_chunk_local, kda_inter_chunk, kda_decode_step,
-    kda_decode_window, kda_prefill_workspace_bytes, kda_status_string.
+    kda_decode_window, kda_prefill_workspace_bytes, kda_status_string,
+    kda_gate, kda_short_conv, kda_out_norm_gate (the layer's passes around the recurrence).
 """
 from __future__ import annotations
 
@@ -28,7 +29,8 @@ KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
-           "kda_decode_step", "kda_decode_window", "kda_status_string", "kda_last_hip_error")
+           "kda_decode_step", "kda_decode_window", "kda_gate", "kda_short_conv", "kda_out_norm_gate",
+           "kda_status_string", "kda_last_hip_error")
 
 _lib = None
 
@@ -64,6 +66,13 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_window.restype = ctypes.c_int
     lib.kda_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                       vp]
+    i64, f32 = ctypes.c_int64, ctypes.c_float
+    lib.kda_gate.restype = ctypes.c_int
+    lib.kda_gate.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp]
+    lib.kda_short_conv.restype = ctypes.c_int
+    lib.kda_short_conv.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, ctypes.c_int, vp, vp]
+    lib.kda_out_norm_gate.restype = ctypes.c_int
+    lib.kda_out_norm_gate.argtypes = [vp, vp, vp, f32, i64, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_hip_error.restype = i32
@@ -246,3 +255,79 @@ def kda_decode_window(q, k, v, log_alpha, beta, state, accept=None, *, o=None, o
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o if output_o else None),
         _ptr(accept), B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
     return o if output_o else None
+
+
+def _check_dev(name, t, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device}); the KDA library has no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def kda_gate(z, A_log, *, out=None, stream=None) -> torch.Tensor:
+    """Bounded decay gate log_alpha = -5 * Sigmoid(exp(A_log[h]) * z); z [N, H, dk] (bf16 or fp32),
+    A_log fp32 [H].  Returns log_alpha in z's dtype (``out`` may be z itself)."""
+    if not isinstance(z, torch.Tensor) or z.device.type != "cuda":
+        raise ValueError("z must be a tensor on a GPU; the KDA library has no CPU path")
+    N, H, dk = z.shape
+    _check_dev("z", z, z.device)
+    _check_dev("A_log", A_log, z.device, torch.float32, (H,))
+    if out is None:
+        out = torch.empty_like(z)
+    _check_dev("out", out, z.device, z.dtype, z.shape)
+    _check(load_library().kda_gate(_ptr(z), _ptr(A_log), N, H, dk, _dtype_code(z.dtype), _ptr(out),
+                                   _stream(stream)))
+    return out
+
+
+def kda_short_conv(x, w, cu_seqlens=None, cache=None, *, l2norm: bool = False, eps: float = 1e-6,
+                   cache_out=None, y=None, stream=None):
+    """ShortConv prologue: y = Swish(causal 4-tap depthwise convolution of x) [L2-normalised over d].
+
+    x [N, H, d] (bf16 or fp32); w fp32 [H, d, 4] (tap j multiplies x_{t-j}); cu_seqlens int32
+    [nseq + 1] on the device (None = one sequence); cache fp32 [nseq, H, d, 3] (the 3 inputs before
+    each sequence, oldest first) or None.  Returns (y, cache_out) with cache_out the 3 last inputs
+    per sequence (``cache_out`` may be ``cache`` to update it in place).
+    """
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a tensor on a GPU; the KDA library has no CPU path")
+    N, H, d = x.shape
+    cu = _cu(cu_seqlens, N, x.device)
+    nseq = cu.numel() - 1
+    _check_dev("x", x, x.device)
+    _check_dev("w", w, x.device, torch.float32, (H, d, 4))
+    if cache is not None:
+        _check_dev("cache", cache, x.device, torch.float32, (nseq, H, d, 3))
+    if cache_out is None:
+        cache_out = torch.empty((nseq, H, d, 3), dtype=torch.float32, device=x.device)
+    _check_dev("cache_out", cache_out, x.device, torch.float32, (nseq, H, d, 3))
+    if y is None:
+        y = torch.empty_like(x)
+    _check_dev("y", y, x.device, x.dtype, x.shape)
+    _check(load_library().kda_short_conv(
+        _ptr(x), _ptr(w), _ptr(cache), _ptr(cache_out), _ptr(cu), nseq, N, H, d, int(bool(l2norm)),
+        float(eps), _dtype_code(x.dtype), _ptr(y), _stream(stream)))
+    return y, cache_out
+
+
+def kda_out_norm_gate(o, u, w, eps: float = 1e-6, *, y=None, stream=None) -> torch.Tensor:
+    """Output epilogue y = Sigmoid(u) * RMSNorm(o) * w per (token, head); o fp32 [N, H, dv], u [N, H, dv]
+    (bf16 or fp32), w fp32 [dv].  Returns y in u's dtype."""
+    if not isinstance(o, torch.Tensor) or o.device.type != "cuda":
+        raise ValueError("o must be a tensor on a GPU; the KDA library has no CPU path")
+    N, H, dv = o.shape
+    _check_dev("o", o, o.device, torch.float32)
+    _check_dev("u", u, o.device, None, (N, H, dv))
+    _check_dev("w", w, o.device, torch.float32, (dv,))
+    if y is None:
+        y = torch.empty_like(u)
+    _check_dev("y", y, o.device, u.dtype, u.shape)
+    _check(load_library().kda_out_norm_gate(_ptr(o), _ptr(u), _ptr(w), float(eps), N, H, dv,
+                                            _dtype_code(u.dtype), _ptr(y), _stream(stream)))
+    return y

@@ -167,6 +167,53 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v, const 
     return hip_status(kda::launch_decode_window(a));
 }
 
+kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int32_t dk, kda_dtype dt,
+                    void *log_alpha, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk)) return KDA_ERR_UNSUPPORTED;
+    if (H < 1 || N < 0 || N >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({z, log_alpha}, false, nullptr, dt == KDA_BF16, N > 0);
+    if (st != KDA_OK) return st;
+    if (!A_log) return KDA_ERR_NULL;
+    kda::GateArgs a{z, A_log, log_alpha, N, H, dk, dt == KDA_BF16, stream};
+    return hip_status(kda::launch_gate(a));
+}
+
+kda_status kda_short_conv(const void *x, const float *w, const float *cache_in, float *cache_out,
+                          const int32_t *cu_seqlens, int32_t nseq, int64_t N, int32_t H, int32_t d,
+                          int32_t l2norm, float eps, kda_dtype dt, void *y, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(d)) return KDA_ERR_UNSUPPORTED;
+    if (nseq < 1 || H < 1 || N < 0 || N >= (int64_t(1) << 31) || !(eps >= 0.f && eps <= 3.4e38f))
+        return KDA_ERR_SHAPE;
+    if ((int64_t)nseq * H * d >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({x, y}, false, nullptr, dt == KDA_BF16, N > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({w, cu_seqlens}, {});
+    if (st != KDA_OK) return st;
+    if ((cache_in && (reinterpret_cast<uintptr_t>(cache_in) & 3u)) ||
+        (cache_out && (reinterpret_cast<uintptr_t>(cache_out) & 3u)))
+        return KDA_ERR_ALIGN;
+    if (N > 0 && x == y) return KDA_ERR_SHAPE;
+    kda::ShortConvArgs a{x, w, cache_in, cache_out, cu_seqlens, nseq, N, H, d, l2norm != 0, eps,
+                         dt == KDA_BF16, y, stream};
+    return hip_status(kda::launch_short_conv(a));
+}
+
+kda_status kda_out_norm_gate(const float *o, const void *u, const float *w, float eps, int64_t N, int32_t H,
+                             int32_t dv, kda_dtype dt, void *y, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (H < 1 || N < 0 || N >= (int64_t(1) << 31) || !(eps >= 0.f && eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({u, y}, false, nullptr, dt == KDA_BF16, N > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({w}, {o});
+    if (st != KDA_OK) return st;
+    if (N > 0 && !o) return KDA_ERR_NULL;
+    kda::OutNormGateArgs a{o, u, w, eps, N, H, dv, dt == KDA_BF16, y, stream};
+    return hip_status(kda::launch_out_norm_gate(a));
+}
+
 const char *kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";

@@ -58,6 +58,47 @@ struct InterChunkArgs {
     void *stream;
 };
 
+struct GateArgs {
+    const void *z;             // decay logits [N, H, dk]
+    const float *A_log;        // [H]
+    void *g;                   // log-decay out [N, H, dk], input dtype
+    int64_t N;
+    int32_t H, dk;
+    bool bf16;
+    void *stream;
+};
+
+struct ShortConvArgs {
+    const void *x;             // [N, H, d]
+    const float *w;            // [H, d, 4]
+    const float *cache_in;     // [nseq, H, d, 3] or NULL
+    float *cache_out;          // [nseq, H, d, 3] or NULL (may equal cache_in)
+    const int32_t *cu;         // [nseq + 1]
+    int32_t nseq;
+    int64_t N;
+    int32_t H, d;
+    bool l2norm;
+    float eps;
+    bool bf16;
+    void *y;                   // [N, H, d], input dtype
+    void *stream;
+};
+
+struct OutNormGateArgs {
+    const float *o;            // [N, H, dv]
+    const void *u;             // gate logits [N, H, dv], input dtype
+    const float *w;            // [dv]
+    float eps;
+    int64_t N;
+    int32_t H, dv;
+    bool bf16;
+    void *y;                   // [N, H, dv], input dtype
+    void *stream;
+};
+
+hipError_t launch_gate(const GateArgs &a);
+hipError_t launch_short_conv(const ShortConvArgs &a);
+hipError_t launch_out_norm_gate(const OutNormGateArgs &a);
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_decode_window(const DecodeWindowArgs &a);
 hipError_t launch_chunk_local(const ChunkLocalArgs &a);

@@ -179,6 +179,52 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v,
                              int32_t B, int32_t T, int32_t H, int32_t dk,
                              int32_t dv, kda_dtype dt, void *stream);
 
+/* ------------------------------------------------------------------------
+ * The layer's passes around the recurrence (same page: the bounded-decay
+ * section for the gate; the paragraph after the update equation for the
+ * prologue -- a short convolution of kernel size 4 and Swish on q, k and v,
+ * then L2 normalisation of q and k; the output-gate section for the epilogue
+ * -- per-head RMSNorm of the recurrent output times a Sigmoid gate).  Each is
+ * one streaming pass (HBM-bound), enqueued on `stream` like the calls above;
+ * the projections that feed them (z, u, the pre-convolution q/k/v) and W_o are
+ * the caller's.  dk, d, dv in {16, 32, 64, 128}; N in [0, 2^31); H >= 1;
+ * eps >= 0 and finite.  [.., d] tensors in the input dtype are read and
+ * written four elements at a time (alignment as for q above); fp32 weight and
+ * cache arrays 16 bytes.
+ * ------------------------------------------------------------------------ */
+
+/* Decay gate: log_alpha = -5 * Sigmoid(exp(A_log[h]) * z), the bounded
+ * log-decay the recurrence takes, written in the input dtype (what a caller
+ * would pass to kda_prefill).  z, log_alpha: [N, H, dk] (may be the same
+ * buffer); A_log: fp32 [H]. */
+kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H,
+                    int32_t dk, kda_dtype dt, void *log_alpha, void *stream);
+
+/* ShortConv prologue over packed sequences: per (head, channel)
+ *   y_t = Swish(sum_{j=0..3} w[h][c][j] * x_{t-j}),  Swish(a) = a Sigmoid(a),
+ * then, if l2norm != 0, y_t / sqrt(sum_c y_{t,c}^2 + eps) over the d channels
+ * of the head (for q and k).  Inputs before a sequence's first token come from
+ * cache_in (the 3 preceding inputs, oldest first; NULL = zeros), so a sequence
+ * can be continued from an earlier call; cache_out (or NULL) receives each
+ * sequence's last 3 inputs, oldest first (reaching into cache_in when the
+ * sequence is shorter than 3), and may be cache_in itself.
+ *   x, y: [N, H, d] (input dtype, distinct buffers); w: fp32 [H, d, 4];
+ *   cu_seqlens: int32 [nseq + 1] device (as kda_prefill);
+ *   cache_in, cache_out: fp32 [nseq, H, d, 3]. */
+kda_status kda_short_conv(const void *x, const float *w, const float *cache_in,
+                          float *cache_out, const int32_t *cu_seqlens,
+                          int32_t nseq, int64_t N, int32_t H, int32_t d,
+                          int32_t l2norm, float eps, kda_dtype dt, void *y,
+                          void *stream);
+
+/* Output epilogue: y = Sigmoid(u) * o / sqrt(mean_c(o_c^2) + eps) * w over
+ * the dv channels of each (token, head).  o: fp32 [N, H, dv] (the recurrence's
+ * output); u: gate logits [N, H, dv] (input dtype); w: fp32 [dv]; y: [N, H, dv]
+ * in the input dtype (the operand of the caller's W_o). */
+kda_status kda_out_norm_gate(const float *o, const void *u, const float *w,
+                             float eps, int64_t N, int32_t H, int32_t dv,
+                             kda_dtype dt, void *y, void *stream);
+
 /* Static string naming a status code. */
 const char *kda_status_string(kda_status s);
 

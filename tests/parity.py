@@ -33,7 +33,8 @@ def rel_err(x, ref) -> float:
 def assert_close(x, ref, tol, what):
     e = rel_err(x, ref)
     say(f"    {what}: max|err|/rms = {e:.3e} (tol {tol:.0e})")
-    assert np.all(np.isfinite(x.detach().cpu().numpy() if isinstance(x, torch.Tensor) else x)), f"{what}: non-finite"
+    assert np.all(np.isfinite(x.detach().double().cpu().numpy() if isinstance(x, torch.Tensor) else x)), \
+        f"{what}: non-finite"
     assert e <= tol, f"{what}: max|err|/RMS(ref) = {e:.3e} > {tol:.1e}"
     return e
 

@@ -133,3 +133,28 @@ def test_python_binding_refuses_cpu_tensors(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         kda.load_library(str(tmp_path / "absent.so"))
+
+
+def test_layer_passes_reject_bad_arguments(lib):
+    g = lib.kda_gate  # z A_log N H dk dt out stream
+    assert g(FAKE, None, 8, 2, 16, 1, FAKE, None) == 1
+    assert g(None, FAKE, 8, 2, 16, 1, FAKE, None) == 1
+    assert g(FAKE + 2, FAKE, 8, 2, 16, 1, FAKE, None) == 2
+    assert g(FAKE, FAKE, 8, 0, 16, 1, FAKE, None) == 3
+    assert g(FAKE, FAKE, -1, 2, 16, 1, FAKE, None) == 3
+    assert g(FAKE, FAKE, 8, 2, 24, 1, FAKE, None) == 4
+    c = lib.kda_short_conv  # x w cin cout cu nseq N H d l2 eps dt y stream
+    assert c(FAKE, None, None, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 1
+    assert c(FAKE, FAKE, None, None, None, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 1
+    assert c(FAKE, FAKE + 4, None, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 2
+    assert c(FAKE, FAKE, FAKE + 2, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 2
+    assert c(FAKE, FAKE, None, None, FAKE, 0, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 3
+    assert c(FAKE, FAKE, None, None, FAKE, 1, 8, 2, 16, 0, -1.0, 1, FAKE + 64, None) == 3
+    assert c(FAKE, FAKE, None, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE, None) == 3   # y aliases x
+    assert c(FAKE, FAKE, None, None, FAKE, 1, 8, 2, 48, 0, 1e-6, 1, FAKE + 64, None) == 4
+    e = lib.kda_out_norm_gate  # o u w eps N H dv dt y stream
+    assert e(None, FAKE, FAKE, 1e-6, 8, 2, 16, 1, FAKE, None) == 1
+    assert e(FAKE, FAKE, None, 1e-6, 8, 2, 16, 1, FAKE, None) == 1
+    assert e(FAKE + 4, FAKE, FAKE, 1e-6, 8, 2, 16, 1, FAKE, None) == 2
+    assert e(FAKE, FAKE, FAKE, float("nan"), 8, 2, 16, 1, FAKE, None) == 3
+    assert e(FAKE, FAKE, FAKE, 1e-6, 8, 2, 20, 1, FAKE, None) == 4

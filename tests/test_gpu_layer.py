@@ -1,0 +1,163 @@
+"""GPU parity of the layer's passes around the recurrence (decay gate, ShortConv prologue,
+RMSNorm + output-gate epilogue) against the fp64 layer oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_51_amd as kda
+import workloads
+from oracle import layer
+from parity import TOL, assert_close, oracle_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    kda.load_library()
+    return torch.device("cuda:0")
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def assert_rounded(x, ref, dtype, what):
+    """fp32 results: the recurrence's bar (max|err| <= 1e-5 RMS(ref)).  Results written in
+    bf16 are the fp32 value rounded to nearest: per element within half a unit in the last
+    place (at most 2^-8 |ref|) plus the fp32 evaluation error."""
+    if dtype == torch.float32:
+        return assert_close(x, ref, TOL[torch.float32], what)
+    xv, ref = _np(x), np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    err = np.abs(xv - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * rms
+    say(f"    {what}: max(err / bound) = {float(np.max(err / bound)) if ref.size else 0.0:.3f}")
+    assert np.all(np.isfinite(xv)), f"{what}: non-finite"
+    assert np.all(err <= bound), f"{what}: bf16 result off by more than half an ulp"
+
+
+def _bf16_round(x):
+    return torch.from_numpy(np.asarray(x)).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("dtype,dk", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 128),
+                                      (torch.bfloat16, 32)])
+def test_gate_matches_oracle(dev, dtype, dk):
+    x = workloads.layer_inputs(37, 3, dk, dtype, device=dev, seed=dk)
+    say(f"  case: gate N=37 H=3 dk={dk} {dtype}")
+    g = kda.kda_gate(x["z"], x["A_log"])
+    torch.cuda.synchronize()
+    ref = layer.gate(_np(x["z"]), _np(x["A_log"]))
+    err = np.abs(_np(g) - ref)
+    # fp32: evaluation error only; bf16: the result is rounded to the input dtype, so at
+    # most one unit in the last place (2^-7 relative) off the exact value
+    tol = 1e-6 * 5 if dtype == torch.float32 else 2.0 ** -7 * np.abs(ref) + 1e-7
+    assert np.all(err <= tol), f"gate error {err.max():.3e}"
+    assert np.all(_np(g) >= -5.0) and np.all(_np(g) <= 0.0)
+    z2 = x["z"].clone()
+    kda.kda_gate(z2, x["A_log"], out=z2)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(z2, g)
+
+
+def test_gate_feeds_prefill(dev):
+    """Decay logits -> kda_gate -> kda_prefill against the oracle recurrence run on the
+    oracle's gate (rounded to bf16, the dtype the recurrence takes)."""
+    w = workloads.custom([40, 9], 2, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=8)
+    li = workloads.layer_inputs(49, 2, 128, torch.bfloat16, device=dev, seed=8)
+    g = kda.kda_gate(li["z"], li["A_log"])
+    o, fin = kda.kda_prefill(x["q"], x["k"], x["v"], g, x["beta"], x["cu_seqlens"])
+    torch.cuda.synchronize()
+    g_ref = _bf16_round(layer.gate(_np(li["z"]), _np(li["A_log"])))
+    x2 = dict(x)
+    x2["log_alpha"] = torch.from_numpy(g_ref).to(torch.bfloat16).to(dev)
+    o_ref, f_ref = oracle_prefill(x2)
+    assert_close(o, o_ref, TOL[torch.bfloat16], "o")
+    assert_close(fin, f_ref, TOL[torch.bfloat16], "final_state")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 128),
+                                     (torch.bfloat16, 64)])
+@pytest.mark.parametrize("l2norm", [False, True])
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_short_conv_matches_oracle(dev, dtype, d, l2norm, with_cache):
+    """Packed sequences of 5, 0, 1, 2, 17 and 33 tokens (empty, shorter than the filter,
+    several lanes of rows), with and without an incoming cache."""
+    seqlens = [5, 0, 1, 2, 17, 33]
+    cu = torch.tensor(workloads.cu_seqlens_of(seqlens), dtype=torch.int32, device=dev)
+    N, H = sum(seqlens), 3
+    li = workloads.layer_inputs(N, H, d, dtype, nseq=len(seqlens), device=dev, seed=d + 7)
+    cache = li["conv_cache"] if with_cache else None
+    say(f"  case: short_conv seqlens={seqlens} H={H} d={d} {dtype} l2norm={l2norm} cache={with_cache}")
+    y, c_out = kda.kda_short_conv(li["x"], li["conv_w"], cu, cache, l2norm=l2norm, eps=1e-6)
+    torch.cuda.synchronize()
+    y_ref, c_ref = layer.short_conv(_np(li["x"]), _np(li["conv_w"]), _np(cu),
+                                    None if cache is None else _np(cache), l2norm=l2norm, eps=1e-6)
+    assert_rounded(y, y_ref, dtype, "y")
+    assert np.array_equal(_np(c_out), c_ref), "cache_out is a copy of inputs and must be exact"
+    if with_cache:  # the cache updated in place
+        c2 = cache.clone()
+        kda.kda_short_conv(li["x"], li["conv_w"], cu, c2, l2norm=l2norm, eps=1e-6, cache_out=c2)
+        torch.cuda.synchronize()
+        assert torch.equal(c2, c_out)
+
+
+def test_short_conv_resumes_across_calls(dev):
+    """A sequence in two calls, the second starting from the first call's cache, equals
+    one call (bitwise: every output reads the same inputs)."""
+    li = workloads.layer_inputs(40, 2, 128, torch.bfloat16, device=dev, seed=3)
+    y_all, c_all = kda.kda_short_conv(li["x"], li["conv_w"], l2norm=True)
+    y1, c1 = kda.kda_short_conv(li["x"][:13].contiguous(), li["conv_w"], l2norm=True)
+    y2, c2 = kda.kda_short_conv(li["x"][13:].contiguous(), li["conv_w"], None, c1, l2norm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2]), y_all)
+    assert torch.equal(c2, c_all)
+
+
+@pytest.mark.parametrize("dtype,dv", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 128),
+                                      (torch.bfloat16, 32)])
+def test_out_norm_gate_matches_oracle(dev, dtype, dv):
+    li = workloads.layer_inputs(41, 3, dv, dtype, device=dev, seed=dv + 1)
+    say(f"  case: out_norm_gate N=41 H=3 dv={dv} {dtype}")
+    y = kda.kda_out_norm_gate(li["o"], li["u"], li["norm_w"], 1e-6)
+    torch.cuda.synchronize()
+    ref = layer.out_norm_gate(_np(li["o"]), _np(li["u"]), _np(li["norm_w"]), 1e-6)
+    assert_rounded(y, ref, dtype, "y")
+    z = kda.kda_out_norm_gate(torch.zeros_like(li["o"]), li["u"], li["norm_w"], 1e-6)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z) == 0
+
+
+def test_layer_passes_k3_shape_sampled_rows(dev):
+    """The K3 layer shape (65,536 tokens x 96 heads, d = 128, bf16): every pass over the
+    whole tensor, the oracle on 256 sampled (token, head) rows (the conv on the 4 tokens
+    each sampled output reads)."""
+    N, H, d = 65536, 96, 128
+    li = workloads.layer_inputs(N, H, d, torch.bfloat16, device=dev, seed=11)
+    say(f"  case: layer passes N={N} H={H} d={d} bf16")
+    g = kda.kda_gate(li["z"], li["A_log"])
+    y, _ = kda.kda_short_conv(li["x"], li["conv_w"], l2norm=True)
+    e = kda.kda_out_norm_gate(li["o"], li["u"], li["norm_w"], 1e-6)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    ts = rng.integers(0, N, 256)
+    hs = rng.integers(0, H, 256)
+    ti, hi = torch.tensor(ts, device=dev), torch.tensor(hs, device=dev)
+    A = _np(li["A_log"])
+    g_ref = np.stack([layer.gate(_np(li["z"][t:t + 1, h:h + 1]), A[h:h + 1])[0, 0] for t, h in zip(ts, hs)])
+    err = np.abs(_np(g[ti, hi]) - g_ref)
+    assert np.all(err <= 2.0 ** -7 * np.abs(g_ref) + 1e-7), f"gate error {err.max():.3e}"
+    y_ref = []
+    for t, h in zip(ts, hs):
+        lo = max(0, t - 3)
+        yy, _ = layer.short_conv(_np(li["x"][lo:t + 1, h:h + 1]), _np(li["conv_w"][h:h + 1]), l2norm=True,
+                                 eps=1e-6)
+        y_ref.append(yy[-1, 0])
+    assert_rounded(y[ti, hi], np.stack(y_ref), torch.bfloat16, "conv rows")
+    e_ref = layer.out_norm_gate(_np(li["o"][ti, hi]), _np(li["u"][ti, hi]), _np(li["norm_w"]), 1e-6)
+    assert_rounded(e[ti, hi], e_ref, torch.bfloat16, "epilogue rows")
+    del li, g, y, e
+    torch.cuda.empty_cache()

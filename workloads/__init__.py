@@ -36,7 +36,8 @@ import torch
 
 CHUNK = 16
 GATE_LOWER_BOUND = -5.0
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "state": 6, "lengths": 7, "accept": 8}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "state": 6, "lengths": 7, "accept": 8,
+              "z": 9, "A_log": 10, "x": 11, "conv_w": 12, "conv_cache": 13, "o": 14, "u": 15, "norm_w": 16}
 
 
 @dataclass(frozen=True)
@@ -215,6 +216,27 @@ def window_accept(B: int, T: int, device="cpu", seed: int = 0, lo: int = 0) -> t
     gen = _gen("cpu", seed, 4, TENSOR_IDS["accept"])
     a = torch.randint(lo, T + 1, (B,), generator=gen, dtype=torch.int64)
     return a.to(dtype=torch.int32, device=device)
+
+
+def layer_inputs(N: int, H: int, d: int, dtype=torch.bfloat16, nseq: int = 1, device="cpu",
+                 seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Synthetic tensors for the layer's passes around the recurrence (random-init weights):
+    z decay logits ~ N(0, 2^2) and A_log ~ U[-1, 1] per head; x pre-convolution activations
+    ~ N(0, 1); conv_w ~ N(0, 0.5^2) [H, d, 4]; conv_cache ~ N(0, 1) [nseq, H, d, 3] (fp32);
+    o ~ N(0, 1) fp32 (a recurrent output); u gate logits ~ N(0, 1); norm_w ~ 1 + N(0, 0.1^2)."""
+    out: Dict[str, torch.Tensor] = {}
+    for kind, shape, scale, shift, dt in (("z", (N, H, d), 2.0, 0.0, dtype), ("x", (N, H, d), 1.0, 0.0, dtype),
+                                          ("conv_w", (H, d, 4), 0.5, 0.0, torch.float32),
+                                          ("conv_cache", (nseq, H, d, 3), 1.0, 0.0, torch.float32),
+                                          ("o", (N, H, d), 1.0, 0.0, torch.float32),
+                                          ("u", (N, H, d), 1.0, 0.0, dtype),
+                                          ("norm_w", (d,), 0.1, 1.0, torch.float32)):
+        gen = _gen(device, seed, 50, TENSOR_IDS[kind])
+        t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * scale + shift
+        out[kind] = t.to(dt)
+    gen = _gen(device, seed, 50, TENSOR_IDS["A_log"])
+    out["A_log"] = torch.rand((H,), generator=gen, device=device, dtype=torch.float32) * 2.0 - 1.0
+    return out
 
 
 def random_state(nseq: int, H: int, dk: int, dv: int, device="cpu", seed: int = 0, scale: float = 1.0) -> torch.Tensor:
