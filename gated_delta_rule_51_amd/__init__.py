@@ -29,7 +29,8 @@ KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
-           "kda_decode_step", "kda_decode_window", "kda_gate", "kda_short_conv", "kda_out_norm_gate",
+           "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
+           "kda_gate", "kda_short_conv", "kda_out_norm_gate",
            "kda_status_string", "kda_last_hip_error")
 
 _lib = None
@@ -67,6 +68,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                       vp]
     i64, f32 = ctypes.c_int64, ctypes.c_float
+    lib.kda_decode_step_fused.restype = ctypes.c_int
+    lib.kda_decode_step_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32,
+                                          ctypes.c_int, vp]
+    lib.kda_decode_window_fused.restype = ctypes.c_int
+    lib.kda_decode_window_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
+                                            i32, i32, ctypes.c_int, vp]
     lib.kda_gate.restype = ctypes.c_int
     lib.kda_gate.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_short_conv.restype = ctypes.c_int
@@ -331,3 +338,65 @@ def kda_out_norm_gate(o, u, w, eps: float = 1e-6, *, y=None, stream=None) -> tor
     _check(load_library().kda_out_norm_gate(_ptr(o), _ptr(u), _ptr(w), float(eps), N, H, dv,
                                             _dtype_code(u.dtype), _ptr(y), _stream(stream)))
     return y
+
+
+def _fusion_args(o_shape, dtype, device, H, dv, gate_A_log, out_gate, norm_w, y, want_y):
+    if gate_A_log is not None:
+        _check_dev("gate_A_log", gate_A_log, device, torch.float32, (H,))
+    if out_gate is None:
+        return None
+    _check_dev("out_gate", out_gate, device, dtype, o_shape)
+    _check_dev("norm_w", norm_w, device, torch.float32, (dv,))
+    if y is None and want_y:
+        y = torch.empty(o_shape, dtype=dtype, device=device)
+    _check_dev("y", y, device, dtype, o_shape)
+    return y
+
+
+def kda_decode_step_fused(q, k, v, gate, beta, state, *, gate_A_log=None, out_gate=None, norm_w=None,
+                          norm_eps: float = 1e-6, o=None, output_o: bool = True, y=None, stream=None):
+    """kda_decode_step with the layer's gate (``gate_A_log``: ``gate`` holds decay logits) and
+    output epilogue (``out_gate``, ``norm_w``: y = Sigmoid(out_gate) RMSNorm(o) norm_w) fused in.
+    Returns (o or None, y or None)."""
+    B, H, dk, dv = _check_inputs(q, k, v, gate, beta)
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv) or not state.is_contiguous() \
+            or state.device != q.device:
+        raise ValueError("state must be contiguous fp32 [B, H, dk, dv] on the inputs' device")
+    y = _fusion_args((B, H, dv), q.dtype, q.device, H, dv, gate_A_log, out_gate, norm_w, y, True)
+    if not output_o and out_gate is None:
+        raise ValueError("output_o=False needs out_gate (nothing would be written)")
+    if output_o and o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    _check(load_library().kda_decode_step_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_A_log), _ptr(beta), _ptr(state),
+        _ptr(o if output_o else None), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y), B, H, dk, dv,
+        _dtype_code(q.dtype), _stream(stream)))
+    return (o if output_o else None), y
+
+
+def kda_decode_window_fused(q, k, v, gate, beta, state, accept=None, *, gate_A_log=None, out_gate=None,
+                            norm_w=None, norm_eps: float = 1e-6, o=None, output_o: bool = True, y=None,
+                            stream=None):
+    """kda_decode_window with the gate and output epilogue fused in (see kda_decode_step_fused);
+    out_gate and y are [B, T, H, dv].  Returns (o or None, y or None)."""
+    _check_tensors(q, k, v, gate, beta)
+    if q.dim() != 4:
+        raise ValueError("expected q, k, gate [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, T, H, dk) or gate.shape != (B, T, H, dk) or v.shape != (B, T, H, dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("expected q, k, gate [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv) or not state.is_contiguous() \
+            or state.device != q.device:
+        raise ValueError("state must be contiguous fp32 [B, H, dk, dv] on the inputs' device")
+    if accept is not None:
+        _check_dev("accept", accept, q.device, torch.int32, (B,))
+    y = _fusion_args((B, T, H, dv), q.dtype, q.device, H, dv, gate_A_log, out_gate, norm_w, y, True)
+    if output_o and o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    _check(load_library().kda_decode_window_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_A_log), _ptr(beta), _ptr(state),
+        _ptr(o if output_o else None), _ptr(accept), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
+        B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
+    return (o if output_o else None), y

@@ -69,6 +69,18 @@ kda_status check_inputs(std::initializer_list<const void *> vec4, bool takes_bet
     return KDA_OK;
 }
 
+// Checks of the fused-work arguments shared by the decode entry points.
+kda_status check_fusion(const float *A_log, const void *u, const float *w, float eps, const void *y, bool bf16) {
+    if (A_log && (reinterpret_cast<uintptr_t>(A_log) & 3u)) return KDA_ERR_ALIGN;
+    if (!u) return KDA_OK;
+    if (!w || !y) return KDA_ERR_NULL;
+    if (!aligned16(w)) return KDA_ERR_ALIGN;
+    const uintptr_t vec = bf16 ? 7u : 15u;
+    if ((reinterpret_cast<uintptr_t>(u) & vec) || (reinterpret_cast<uintptr_t>(y) & vec)) return KDA_ERR_ALIGN;
+    if (!(eps >= 0.f && eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,35 +148,59 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
                            dv, dt, workspace, ws_bytes, o, final_state, stream);
 }
 
-kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
-                           const void *beta, float *state, float *o, int32_t B, int32_t H,
-                           int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
+kda_status kda_decode_step_fused(const void *q, const void *k, const void *v, const void *gate,
+                                 const float *gate_A_log, const void *beta, float *state, float *o,
+                                 const void *out_gate, const float *norm_w, float norm_eps, void *y,
+                                 int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || (int64_t)B * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
-    kda_status st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, true);
+    kda_status st = check_inputs({q, k, v, gate}, true, beta, dt == KDA_BF16, true);
     if (st != KDA_OK) return st;
-    st = check_ptrs({state, o}, {});
+    st = check_ptrs({state}, {o});
     if (st != KDA_OK) return st;
-    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
+    if (!o && !out_gate) return KDA_ERR_NULL;
+    st = check_fusion(gate_A_log, out_gate, norm_w, norm_eps, y, dt == KDA_BF16);
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs a{q, k, v, gate, beta, state, o, B, H, dk, dv, dt == KDA_BF16, stream,
+                      {gate_A_log, out_gate, norm_w, norm_eps, y}};
     return hip_status(kda::launch_decode(a));
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, float *state, float *o, int32_t B, int32_t H,
+                           int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
+    if (!o) return KDA_ERR_NULL;
+    return kda_decode_step_fused(q, k, v, log_alpha, nullptr, beta, state, o, nullptr, nullptr, 0.f, nullptr,
+                                 B, H, dk, dv, dt, stream);
+}
+
+kda_status kda_decode_window_fused(const void *q, const void *k, const void *v, const void *gate,
+                                   const float *gate_A_log, const void *beta, float *state, float *o,
+                                   const int32_t *accept, const void *out_gate, const float *norm_w,
+                                   float norm_eps, void *y, int32_t B, int32_t T, int32_t H, int32_t dk,
+                                   int32_t dv, kda_dtype dt, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || (int64_t)B * T * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({q, k, v, gate}, true, beta, dt == KDA_BF16, true);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({state}, {o});
+    if (st != KDA_OK) return st;
+    if (accept && (reinterpret_cast<uintptr_t>(accept) & 3u)) return KDA_ERR_ALIGN;
+    st = check_fusion(gate_A_log, out_gate, norm_w, norm_eps, y, dt == KDA_BF16);
+    if (st != KDA_OK) return st;
+    kda::DecodeWindowArgs a{q, k, v, gate, beta, state, o, accept, B, T, H, dk, dv, dt == KDA_BF16, stream,
+                            {gate_A_log, out_gate, norm_w, norm_eps, y}};
+    return hip_status(kda::launch_decode_window(a));
 }
 
 kda_status kda_decode_window(const void *q, const void *k, const void *v, const void *log_alpha,
                              const void *beta, float *state, float *o, const int32_t *accept,
                              int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
                              void *stream) {
-    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
-    if (B < 1 || T < 1 || H < 1 || (int64_t)B * T * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
-    kda_status st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, true);
-    if (st != KDA_OK) return st;
-    st = check_ptrs({state}, {o});
-    if (st != KDA_OK) return st;
-    if (accept && (reinterpret_cast<uintptr_t>(accept) & 3u)) return KDA_ERR_ALIGN;
-    kda::DecodeWindowArgs a{q, k, v, log_alpha, beta, state, o, accept,
-                            B, T, H, dk, dv, dt == KDA_BF16, stream};
-    return hip_status(kda::launch_decode_window(a));
+    return kda_decode_window_fused(q, k, v, log_alpha, nullptr, beta, state, o, accept, nullptr, nullptr, 0.f,
+                                   nullptr, B, T, H, dk, dv, dt, stream);
 }
 
 kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int32_t dk, kda_dtype dt,

@@ -49,11 +49,39 @@ struct DecodeShape {
 // Total threads of the persistent grid (4 Mi state floats in flight at most).
 constexpr int64_t GRID_THREADS = 1 << 20;
 
-template <int DK, int DV, typename T>
+// Fused layer work (Kimi K3 report digest: the bounded-decay section's gate
+// g = g_min Sigmoid(e^{A_h} z) with g_min = -5, and the output-gate section's
+// per-head RMSNorm times a Sigmoid gate), evaluated in fp32 where the decode
+// kernels already hold the operands: the gate on the key channels before the
+// forget step, the epilogue on the output row (the NC4 lanes that hold it sit
+// in the first wave, so its mean square is a few cross-lane adds).
+__device__ __forceinline__ float gate_from_logit(float z, float scale) {
+    return -5.0f / (1.0f + expf(-scale * z));
+}
+
+template <int NC4, typename T>
+__device__ __forceinline__ void epilogue_store(const DecodeFusion &fx, int64_t row, int c4, f32x4 ov) {
+    float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+    for (int m = 1; m < NC4; m <<= 1) ss += __shfl_xor(ss, m);
+    const float inv = 1.f / sqrtf(ss * (1.f / (4 * NC4)) + fx.eps);
+    const f32x4 uv = load_in4(reinterpret_cast<const T *>(fx.u) + row * (4 * NC4) + 4 * c4);
+    const f32x4 wv = *reinterpret_cast<const f32x4 *>(fx.w + 4 * c4);
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = ov[j] * inv * wv[j] / (1.f + expf(-uv[j]));
+    T *y = reinterpret_cast<T *>(fx.y) + row * (4 * NC4) + 4 * c4;
+    if constexpr (sizeof(T) == 4)
+        *reinterpret_cast<f32x4 *>(y) = r;
+    else
+        *reinterpret_cast<bf16x4 *>(y) = to_bf16x4(r);
+}
+
+template <int DK, int DV, typename T, bool FX>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
-    float *__restrict__ o, int64_t heads) {
+    float *__restrict__ o, int64_t heads, int32_t H, DecodeFusion fx) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int NC4 = Sh::NC4, RP = Sh::RP, NR = Sh::NR, P = Sh::P, NKW = Sh::NKW;
     const int tid = threadIdx.x;
@@ -84,7 +112,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
             qq = load_in(q + head * DK + tid);
             s_k[tid] = kk;
             s_q[tid] = qq;
-            s_a[tid] = decay_exp(load_in(g + head * DK + tid));
+            const float gz = load_in(g + head * DK + tid);
+            s_a[tid] = decay_exp(FX && fx.A_log ? gate_from_logit(gz, expf(fx.A_log[head % H])) : gz);
         }
         if (tid < 64 * NKW) {  // whole waves: k.q by cross-lane sums
             float kq = kk * qq;
@@ -129,7 +158,11 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 #pragma unroll
         for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
         const f32x4 delta = b * (vv - vhat);
-        if (rg == 0) reinterpret_cast<f32x4 *>(o + head * DV)[c4] = rq + kq * delta;
+        if (rg == 0) {
+            const f32x4 ov = rq + kq * delta;
+            if (o) reinterpret_cast<f32x4 *>(o + head * DV)[c4] = ov;
+            if (FX && fx.u) epilogue_store<NC4, T>(fx, head, c4, ov);
+        }
 
         float *S = state + head * (int64_t)(DK * DV);
 #pragma unroll
@@ -171,13 +204,14 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 // Threads per window workgroup, at most.
 constexpr int WINDOW_THREADS = 512;
 
-template <int DK, int DV, typename T>
+template <int DK, int DV, typename T, bool FX>
 __global__ __launch_bounds__((DecodeShape<DK, DV, WINDOW_THREADS>::NT))
 __attribute__((amdgpu_waves_per_eu((2 * DecodeShape<DK, DV, WINDOW_THREADS>::NT + 255) / 256, 8)))
 void decode_window_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
-    float *__restrict__ o, const int32_t *__restrict__ accept, int64_t heads, int32_t H, int32_t Tw) {
+    float *__restrict__ o, const int32_t *__restrict__ accept, int64_t heads, int32_t H, int32_t Tw,
+    DecodeFusion fx) {
     using Sh = DecodeShape<DK, DV, WINDOW_THREADS>;
     constexpr int NC4 = Sh::NC4, RP = Sh::RP, NR = Sh::NR, P = Sh::P, NKW = Sh::NKW;
     const int tid = threadIdx.x;
@@ -253,12 +287,13 @@ void decode_window_kernel(
         }
         const bool more = head + stride < heads;
         const rsrc_t rs = state_rsrc(head);
+        const float gscale = FX && fx.A_log ? expf(fx.A_log[head - bq * H]) : 0.f;
         for (int t = 0; t < Tw; ++t) {
             // LDS reuse across tokens as across heads in the single-token kernel
             if (tid < DK) {
                 s_k[tid] = cur.k;
                 s_q[tid] = cur.q;
-                s_a[tid] = decay_exp(cur.g);
+                s_a[tid] = decay_exp(FX && fx.A_log ? gate_from_logit(cur.g, gscale) : cur.g);
             }
             if (tid < 64 * NKW) {
                 float kq = cur.k * cur.q;
@@ -307,9 +342,11 @@ void decode_window_kernel(
 #pragma unroll
             for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
             const f32x4 delta = bb * (vv - vhat);
-            if (o && rg == 0) {
+            if (rg == 0) {
                 const int64_t row = (bq * Tw + t) * H + (head - bq * H);
-                reinterpret_cast<f32x4 *>(o + row * DV)[c4] = rq + kq * delta;
+                const f32x4 ov = rq + kq * delta;
+                if (o) reinterpret_cast<f32x4 *>(o + row * DV)[c4] = ov;
+                if (FX && fx.u) epilogue_store<NC4, T>(fx, row, c4, ov);
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) rows[r] += kr[r] * delta;  // erase + write
@@ -346,9 +383,11 @@ static hipError_t launch_decode_t(const DecodeArgs &a) {
     const int64_t heads = (int64_t)a.B * a.H;
     const int64_t cap = GRID_THREADS / Sh::NT;
     const int64_t grid = heads < cap ? heads : cap;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), dim3((unsigned)grid), dim3(Sh::NT), 0,
-                       (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.v,
-                       (const T *)a.g, (const T *)a.beta, a.state, a.o, heads);
+    const bool fused = a.fx.A_log || a.fx.u;
+    hipLaunchKernelGGL((fused ? decode_kernel<DK, DV, T, true> : decode_kernel<DK, DV, T, false>),
+                       dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
+                       (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.state, a.o, heads,
+                       a.H, a.fx);
     return hipGetLastError();
 }
 
@@ -373,9 +412,11 @@ static hipError_t launch_window_t(const DecodeWindowArgs &a) {
     const int64_t heads = (int64_t)a.B * a.H;
     const int64_t cap = GRID_THREADS / Sh::NT;
     const int64_t grid = heads < cap ? heads : cap;
-    hipLaunchKernelGGL((decode_window_kernel<DK, DV, T>), dim3((unsigned)grid), dim3(Sh::NT), 0,
-                       (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.v,
-                       (const T *)a.g, (const T *)a.beta, a.state, a.o, a.accept, heads, a.H, a.T);
+    const bool fused = a.fx.A_log || a.fx.u;
+    hipLaunchKernelGGL((fused ? decode_window_kernel<DK, DV, T, true> : decode_window_kernel<DK, DV, T, false>),
+                       dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
+                       (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.state, a.o,
+                       a.accept, heads, a.H, a.T, a.fx);
     return hipGetLastError();
 }
 

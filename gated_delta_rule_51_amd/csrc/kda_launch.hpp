@@ -18,12 +18,22 @@ constexpr int WS_FLOATS_PER_CHUNK_HEAD = 2 * 16 * 16;
 // The map is injective and bounded by floor(N/16) + nseq.
 inline int64_t chunk_slots(int64_t total_tokens, int32_t nseq) { return total_tokens / 16 + nseq; }
 
+// Optional work fused into the decode kernels (all NULL: plain decode).
+struct DecodeFusion {
+    const float *A_log;        // [H]: g holds decay logits z, log-decay = -5 Sigmoid(e^{A_h} z)
+    const void *u;             // output-gate logits shaped like o (input dtype): y = Sigmoid(u) RMSNorm(o) w
+    const float *w;            // [dv] RMSNorm weight
+    float eps;
+    void *y;                   // shaped like o, input dtype
+};
+
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
-    float *state, *o;
+    float *state, *o;          // o may be NULL when the epilogue writes y
     int32_t B, H, dk, dv;
     bool bf16;
     void *stream;
+    DecodeFusion fx;
 };
 
 struct DecodeWindowArgs {
@@ -33,6 +43,7 @@ struct DecodeWindowArgs {
     int32_t B, T, H, dk, dv;
     bool bf16;
     void *stream;
+    DecodeFusion fx;
 };
 
 struct ChunkLocalArgs {

@@ -179,6 +179,34 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v,
                              int32_t B, int32_t T, int32_t H, int32_t dk,
                              int32_t dv, kda_dtype dt, void *stream);
 
+/* kda_decode_step and kda_decode_window with the layer's gate and epilogue
+ * fused in (the passes below, evaluated where the decode kernels already hold
+ * the operands, so a decode step of the layer is one launch):
+ *   * gate_A_log != NULL: `gate` holds the decay logits z (same layout as
+ *     log_alpha) and the kernel takes log-decay g = -5 Sigmoid(exp(A_log[h]) z)
+ *     in fp32 (not rounded to the input dtype); gate_A_log is fp32 [H].
+ *     NULL: `gate` is log_alpha as in kda_decode_step.
+ *   * out_gate != NULL: y = Sigmoid(out_gate) * o / sqrt(mean(o^2) + norm_eps)
+ *     * norm_w over the dv channels of each output row, written in the input
+ *     dtype; out_gate and y are shaped like o (input dtype, 4-element aligned),
+ *     norm_w fp32 [dv] (16-byte aligned), norm_eps >= 0.  o may then be NULL
+ *     (not written).
+ * Everything else as in the unfused calls. */
+kda_status kda_decode_step_fused(const void *q, const void *k, const void *v,
+                                 const void *gate, const float *gate_A_log,
+                                 const void *beta, float *state, float *o,
+                                 const void *out_gate, const float *norm_w,
+                                 float norm_eps, void *y, int32_t B, int32_t H,
+                                 int32_t dk, int32_t dv, kda_dtype dt, void *stream);
+
+kda_status kda_decode_window_fused(const void *q, const void *k, const void *v,
+                                   const void *gate, const float *gate_A_log,
+                                   const void *beta, float *state, float *o,
+                                   const int32_t *accept, const void *out_gate,
+                                   const float *norm_w, float norm_eps, void *y,
+                                   int32_t B, int32_t T, int32_t H, int32_t dk,
+                                   int32_t dv, kda_dtype dt, void *stream);
+
 /* ------------------------------------------------------------------------
  * The layer's passes around the recurrence (same page: the bounded-decay
  * section for the gate; the paragraph after the update equation for the

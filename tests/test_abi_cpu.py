@@ -158,3 +158,17 @@ def test_layer_passes_reject_bad_arguments(lib):
     assert e(FAKE + 4, FAKE, FAKE, 1e-6, 8, 2, 16, 1, FAKE, None) == 2
     assert e(FAKE, FAKE, FAKE, float("nan"), 8, 2, 16, 1, FAKE, None) == 3
     assert e(FAKE, FAKE, FAKE, 1e-6, 8, 2, 20, 1, FAKE, None) == 4
+
+
+def test_fused_decode_rejects_bad_arguments(lib):
+    f = lib.kda_decode_step_fused  # q k v gate A beta state o u w eps y B H dk dv dt stream
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None, 0.0, None, 1, 1, 16, 16, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 16, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 0.0, FAKE, 1, 1, 16, 16, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 0.0, FAKE, 1, 1, 16, 16, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, -1.0, FAKE, 1, 1, 16, 16, 1, None) == 3
+    g = lib.kda_decode_window_fused  # q k v gate A beta state o acc u w eps y B T H dk dv dt stream
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, None, 0.0, FAKE, 1, 2, 1, 16, 16, 1,
+             None) == 1
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, 0.0, None, 1, 0, 1, 16, 16, 1,
+             None) == 3

@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import gated_delta_rule_51_amd as kda
+import oracle
 import workloads
 from oracle import layer
 from parity import TOL, assert_close, oracle_prefill, say
@@ -161,3 +162,87 @@ def test_layer_passes_k3_shape_sampled_rows(dev):
     assert_rounded(e[ti, hi], e_ref, torch.bfloat16, "epilogue rows")
     del li, g, y, e
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- fused decode
+
+def _assert_y(y, ref, dtype, what):
+    """The epilogue's output carries the recurrence's error (the 1e-2 / 1e-5 RMS bar) and,
+    in bf16, its rounding (half an ulp, at most 2^-8 |ref|)."""
+    yv, ref = _np(y), np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = TOL[dtype] * rms + (2.0 ** -8 * np.abs(ref) if dtype == torch.bfloat16 else 0.0)
+    say(f"    {what}: max(err / bound) = {float(np.max(np.abs(yv - ref) / bound)):.3f}")
+    assert np.all(np.isfinite(yv)) and np.all(np.abs(yv - ref) <= bound), f"{what} off"
+
+
+def _decode_case(dev, dtype, dk, dv, B=3, H=4, seed=0):
+    w = workloads.custom([1] * B, H, dk, dv, dtype)
+    x = workloads.decode_step_inputs(w, 0, device=dev, seed=seed)
+    lk = workloads.layer_inputs(B, H, dk, dtype, device=dev, seed=seed)
+    lv = workloads.layer_inputs(B, H, dv, dtype, device=dev, seed=seed + 100)
+    state = workloads.random_state(B, H, dk, dv, device=dev, seed=seed)
+    return x, lk, lv, state
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 128), (torch.float32, 16, 64),
+                                         (torch.bfloat16, 64, 32), (torch.float32, 128, 128)])
+def test_decode_step_fused_matches_oracle(dev, dtype, dk, dv):
+    """Gate from logits and the RMSNorm + Sigmoid epilogue inside the decode kernel, against
+    the oracle gate, the oracle recurrence and the oracle epilogue in sequence."""
+    x, lk, lv, state0 = _decode_case(dev, dtype, dk, dv, seed=dk + dv)
+    say(f"  case: fused decode B=3 H=4 dk={dk} dv={dv} {dtype}")
+    st = state0.clone()
+    o, y = kda.kda_decode_step_fused(x["q"], x["k"], x["v"], lk["z"], x["beta"], st, gate_A_log=lk["A_log"],
+                                     out_gate=lv["u"], norm_w=lv["norm_w"], norm_eps=1e-6)
+    torch.cuda.synchronize()
+    g = layer.gate(_np(lk["z"]), _np(lk["A_log"]))
+    o_ref, s_ref = oracle.decode(_np(x["q"]), _np(x["k"]), _np(x["v"]), g, _np(x["beta"]), _np(state0))
+    y_ref = layer.out_norm_gate(o_ref, _np(lv["u"]), _np(lv["norm_w"]), 1e-6)
+    assert_close(o, o_ref, TOL[dtype], "o")
+    assert_close(st, s_ref, TOL[dtype], "state")
+    _assert_y(y, y_ref, dtype, "y")
+    # each fusion alone, and y without o
+    st = state0.clone()
+    o2, y2 = kda.kda_decode_step_fused(x["q"], x["k"], x["v"], lk["z"], x["beta"], st, gate_A_log=lk["A_log"])
+    st3 = state0.clone()
+    o3, y3 = kda.kda_decode_step_fused(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], st3,
+                                       out_gate=lv["u"], norm_w=lv["norm_w"], output_o=False)
+    torch.cuda.synchronize()
+    assert y2 is None and o3 is None
+    assert torch.equal(o2, o)
+    o3_ref, _ = oracle.decode(_np(x["q"]), _np(x["k"]), _np(x["v"]), _np(x["log_alpha"]), _np(x["beta"]),
+                              _np(state0))
+    _assert_y(y3, layer.out_norm_gate(o3_ref, _np(lv["u"]), _np(lv["norm_w"]), 1e-6), dtype, "y (epilogue only)")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_window_fused_matches_oracle(dev, dtype):
+    B, T, H, dk, dv = 3, 5, 2, 128, 128
+    w = workloads.custom([1] * B, H, dk, dv, dtype)
+    x = workloads.decode_window_inputs(w, T, 0, device=dev, seed=41)
+    lk = workloads.layer_inputs(B * T, H, dk, dtype, device=dev, seed=41)
+    lv = workloads.layer_inputs(B * T, H, dv, dtype, device=dev, seed=42)
+    z = lk["z"].view(B, T, H, dk)
+    u = lv["u"].view(B, T, H, dv)
+    state0 = workloads.random_state(B, H, dk, dv, device=dev, seed=41)
+    st = state0.clone()
+    acc = torch.tensor([0, 3, 5], dtype=torch.int32, device=dev)
+    say(f"  case: fused window B={B} T={T} H={H} {dtype}")
+    o, y = kda.kda_decode_window_fused(x["q"], x["k"], x["v"], z, x["beta"], st, acc, gate_A_log=lk["A_log"],
+                                       out_gate=u, norm_w=lv["norm_w"], norm_eps=1e-6)
+    torch.cuda.synchronize()
+    g = layer.gate(_np(lk["z"]), _np(lk["A_log"])).reshape(B, T, H, dk)
+    s = _np(state0)
+    snaps, outs = [s], []
+    for t in range(T):
+        ot, s = oracle.decode(_np(x["q"][:, t]), _np(x["k"][:, t]), _np(x["v"][:, t]), g[:, t],
+                              _np(x["beta"][:, t]), s)
+        outs.append(ot)
+        snaps.append(s)
+    o_ref = np.stack(outs, axis=1)
+    s_ref = np.stack([snaps[a][b] for b, a in enumerate([0, 3, 5])])
+    assert_close(o, o_ref, TOL[dtype], "o")
+    assert_close(st, s_ref, TOL[dtype], "state")
+    assert torch.equal(st[0], state0[0])
+    _assert_y(y, layer.out_norm_gate(o_ref, _np(u), _np(lv["norm_w"]), 1e-6), dtype, "y")
