@@ -11,6 +11,9 @@ The JSON line also carries, measured in the same run:
   * "decode":   128 recurrent steps over B=256 x H=96 heads (1.6 GB of fp32 state),
   * "decode_window_4" / "_8": the same 128 steps as windows of 4 or 8 draft tokens
     (speculative verification: one state read and write per window),
+  * "layer": the passes around the recurrence (decay gate, ShortConv prologue, RMSNorm +
+    output-gate epilogue) on the K3 layer shape, and the fused decode step against the
+    same operations as separate launches,
   * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
 each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
 
@@ -321,6 +324,75 @@ def bench_decode_window(torch, kda, workloads, dev, steps, T: int):
     return res
 
 
+def _event_ms(torch, fn, reps: int) -> float:
+    """Mean milliseconds per call of fn() over reps back-to-back calls on torch's current stream
+    (every library call is enqueued there), after one untimed call."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_layer(torch, kda, workloads, dev, steps):
+    """The layer's passes around the recurrence.  Prefill side, on the K3 layer shape (65,536
+    tokens x 96 heads, d = 128, bf16): the decay gate, the ShortConv prologue of q (with L2
+    norm) and the epilogue, each one HBM pass (GB/s of algorithmic bytes against 8 TB/s).
+    Decode side, on the decode workload (B=256 x H=96) and at B=4: one fused launch (gate +
+    step + epilogue) against the same three operations as separate launches."""
+    N, H, d = 65536, 96, 128
+    li = workloads.layer_inputs(N, H, d, torch.bfloat16, device=dev, seed=0)
+    g = torch.empty_like(li["z"])
+    y = torch.empty_like(li["x"])
+    e = torch.empty_like(li["u"])
+    cache = torch.empty((1, H, d, 3), dtype=torch.float32, device=dev)
+    elems = N * H * d
+    res = {"shape": {"tokens": N, "heads": H, "d": d, "dtype": "bf16"}}
+    for name, fn, nbytes in (
+            ("gate", lambda: kda.kda_gate(li["z"], li["A_log"], out=g), 4 * elems),
+            ("short_conv_l2", lambda: kda.kda_short_conv(li["x"], li["conv_w"], l2norm=True, cache_out=cache, y=y),
+             4 * elems),
+            ("out_norm_gate", lambda: kda.kda_out_norm_gate(li["o"], li["u"], li["norm_w"], 1e-6, y=e),
+             8 * elems)):
+        ms = _event_ms(torch, fn, 10)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 5), "bytes": nbytes, "gbs": gbs, "hbm_peak_frac": gbs / HBM_PEAK_GBS}
+    del li, g, y, e
+    torch.cuda.empty_cache()
+
+    w4 = workloads.workload(4)
+    for B in (w4.nseq, 4):
+        Hd, dk, dv = w4.H, w4.dk, w4.dv
+        x = {n: t[:B].contiguous() for n, t in steps[0].items()}
+        lk = workloads.layer_inputs(B, Hd, dk, torch.bfloat16, device=dev, seed=1)
+        lv = workloads.layer_inputs(B, Hd, dv, torch.bfloat16, device=dev, seed=2)
+        state = workloads.decode_initial_state(B, Hd, dk, dv, device=dev)
+        o = torch.empty((B, Hd, dv), dtype=torch.float32, device=dev)
+        yv = torch.empty((B, Hd, dv), dtype=torch.bfloat16, device=dev)
+        gz = torch.empty_like(lk["z"])
+
+        def fused():
+            kda.kda_decode_step_fused(x["q"], x["k"], x["v"], lk["z"], x["beta"], state, gate_A_log=lk["A_log"],
+                                      out_gate=lv["u"], norm_w=lv["norm_w"], output_o=False, y=yv)
+
+        def separate():
+            kda.kda_gate(lk["z"], lk["A_log"], out=gz)
+            kda.kda_decode_step(x["q"], x["k"], x["v"], gz, x["beta"], state, o=o)
+            kda.kda_out_norm_gate(o, lv["u"], lv["norm_w"], 1e-6, y=yv)
+
+        reps = 50 if B > 16 else 500
+        ms_f, ms_s = _event_ms(torch, fused, reps), _event_ms(torch, separate, reps)
+        res[f"decode_b{B}"] = {"batch": B, "heads": Hd, "ms_fused": round(ms_f, 5), "ms_separate": round(ms_s, 5),
+                               "speedup": ms_s / ms_f}
+        del x, lk, lv, state, o, yv, gz
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +466,8 @@ def main() -> int:
         for T in (4, 8):
             log(f"[bench] decode windows of {T} drafts (speculative verification), B=256 H=96")
             out[f"decode_window_{T}"] = bench_decode_window(torch, kda, workloads, dev, steps, T)
+        log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
+        out["layer"] = bench_layer(torch, kda, workloads, dev, steps)
         del steps
         torch.cuda.empty_cache()
     if args.only in ("all", "varlen"):

@@ -69,6 +69,19 @@ kda_status check_inputs(std::initializer_list<const void *> vec4, bool takes_bet
     return KDA_OK;
 }
 
+// The layer passes read and write [.., d] rows eight elements at a time: 16-byte
+// aligned; with no rows they may be NULL.
+kda_status check_rows16(std::initializer_list<const void *> ptrs, bool any_rows) {
+    for (const void *p : ptrs) {
+        if (!p) {
+            if (any_rows) return KDA_ERR_NULL;
+            continue;
+        }
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    }
+    return KDA_OK;
+}
+
 // Checks of the fused-work arguments shared by the decode entry points.
 kda_status check_fusion(const float *A_log, const void *u, const float *w, float eps, const void *y, bool bf16) {
     if (A_log && (reinterpret_cast<uintptr_t>(A_log) & 3u)) return KDA_ERR_ALIGN;
@@ -208,7 +221,7 @@ kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk)) return KDA_ERR_UNSUPPORTED;
     if (H < 1 || N < 0 || N >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
-    kda_status st = check_inputs({z, log_alpha}, false, nullptr, dt == KDA_BF16, N > 0);
+    kda_status st = check_rows16({z, log_alpha}, N > 0);
     if (st != KDA_OK) return st;
     if (!A_log) return KDA_ERR_NULL;
     kda::GateArgs a{z, A_log, log_alpha, N, H, dk, dt == KDA_BF16, stream};
@@ -223,7 +236,7 @@ kda_status kda_short_conv(const void *x, const float *w, const float *cache_in, 
     if (nseq < 1 || H < 1 || N < 0 || N >= (int64_t(1) << 31) || !(eps >= 0.f && eps <= 3.4e38f))
         return KDA_ERR_SHAPE;
     if ((int64_t)nseq * H * d >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
-    kda_status st = check_inputs({x, y}, false, nullptr, dt == KDA_BF16, N > 0);
+    kda_status st = check_rows16({x, y}, N > 0);
     if (st != KDA_OK) return st;
     st = check_ptrs({w, cu_seqlens}, {});
     if (st != KDA_OK) return st;
@@ -241,7 +254,7 @@ kda_status kda_out_norm_gate(const float *o, const void *u, const float *w, floa
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
     if (H < 1 || N < 0 || N >= (int64_t(1) << 31) || !(eps >= 0.f && eps <= 3.4e38f)) return KDA_ERR_SHAPE;
-    kda_status st = check_inputs({u, y}, false, nullptr, dt == KDA_BF16, N > 0);
+    kda_status st = check_rows16({u, y}, N > 0);
     if (st != KDA_OK) return st;
     st = check_ptrs({w}, {o});
     if (st != KDA_OK) return st;

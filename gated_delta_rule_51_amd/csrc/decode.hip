@@ -55,21 +55,28 @@ constexpr int64_t GRID_THREADS = 1 << 20;
 // kernels already hold the operands: the gate on the key channels before the
 // forget step, the epilogue on the output row (the NC4 lanes that hold it sit
 // in the first wave, so its mean square is a few cross-lane adds).
+// (hardware exp and reciprocal, about 1e-6 relative: these sit on the serial
+// path of each head, between barriers)
 __device__ __forceinline__ float gate_from_logit(float z, float scale) {
-    return -5.0f / (1.0f + expf(-scale * z));
+    return -5.0f * __builtin_amdgcn_rcpf(1.0f + __expf(-scale * z));
+}
+
+// The output-gate logits of row `row`, columns 4 c4 .. +3 (loaded ahead of use).
+template <int NC4, typename T>
+__device__ __forceinline__ f32x4 epilogue_gate(const DecodeFusion &fx, int64_t row, int c4) {
+    return load_in4(reinterpret_cast<const T *>(fx.u) + row * (4 * NC4) + 4 * c4);
 }
 
 template <int NC4, typename T>
-__device__ __forceinline__ void epilogue_store(const DecodeFusion &fx, int64_t row, int c4, f32x4 ov) {
+__device__ __forceinline__ void epilogue_store(const DecodeFusion &fx, int64_t row, int c4, f32x4 ov, f32x4 uv,
+                                               f32x4 wv) {
     float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
 #pragma unroll
     for (int m = 1; m < NC4; m <<= 1) ss += __shfl_xor(ss, m);
-    const float inv = 1.f / sqrtf(ss * (1.f / (4 * NC4)) + fx.eps);
-    const f32x4 uv = load_in4(reinterpret_cast<const T *>(fx.u) + row * (4 * NC4) + 4 * c4);
-    const f32x4 wv = *reinterpret_cast<const f32x4 *>(fx.w + 4 * c4);
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.f / (4 * NC4)) + fx.eps);
     f32x4 r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = ov[j] * inv * wv[j] / (1.f + expf(-uv[j]));
+    for (int j = 0; j < 4; ++j) r[j] = ov[j] * inv * wv[j] * __builtin_amdgcn_rcpf(1.f + __expf(-uv[j]));
     T *y = reinterpret_cast<T *>(fx.y) + row * (4 * NC4) + 4 * c4;
     if constexpr (sizeof(T) == 4)
         *reinterpret_cast<f32x4 *>(y) = r;
@@ -94,6 +101,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     __shared__ __attribute__((aligned(16))) float s_fin[2][DV];
     __shared__ float s_kq[2][NKW];
 
+    // the RMSNorm weight of this lane's columns (epilogue lanes: rg == 0)
+    f32x4 ep_w = zero4();
+    if (FX && fx.u && rg == 0) ep_w = *reinterpret_cast<const f32x4 *>(fx.w + 4 * c4);
+
     auto load_rows = [&](f32x4 (&rows)[NR], int64_t head) {
         const float *S = state + head * (int64_t)(DK * DV);
 #pragma unroll
@@ -113,7 +124,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
             s_k[tid] = kk;
             s_q[tid] = qq;
             const float gz = load_in(g + head * DK + tid);
-            s_a[tid] = decay_exp(FX && fx.A_log ? gate_from_logit(gz, expf(fx.A_log[head % H])) : gz);
+            s_a[tid] = decay_exp(FX && fx.A_log ? gate_from_logit(gz, __expf(fx.A_log[head % H])) : gz);
         }
         if (tid < 64 * NKW) {  // whole waves: k.q by cross-lane sums
             float kq = kk * qq;
@@ -123,6 +134,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
         }
         const f32x4 vv = load_in4(v + head * DV + 4 * c4);
         const float b = load_in(beta + head);
+        f32x4 ep_u = zero4();
+        if (FX && fx.u && rg == 0) ep_u = epilogue_gate<NC4, T>(fx, head, c4);
         if (head + stride < heads) load_rows(nxt, head + stride);
         __syncthreads();
 
@@ -161,7 +174,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
         if (rg == 0) {
             const f32x4 ov = rq + kq * delta;
             if (o) reinterpret_cast<f32x4 *>(o + head * DV)[c4] = ov;
-            if (FX && fx.u) epilogue_store<NC4, T>(fx, head, c4, ov);
+            if (FX && fx.u) epilogue_store<NC4, T>(fx, head, c4, ov, ep_u, ep_w);
         }
 
         float *S = state + head * (int64_t)(DK * DV);
@@ -275,6 +288,8 @@ void decode_window_kernel(
 
     Tok cur, nxt;
     int par = 0;
+    f32x4 ep_w = zero4();  // RMSNorm weight of this lane's columns (epilogue lanes: rg == 0)
+    if (FX && fx.u && rg == 0) ep_w = *reinterpret_cast<const f32x4 *>(fx.w + 4 * c4);
     // One (sequence, head): the window's tokens in order, the state rows in
     // registers throughout.  The next head's state rows (into nrows) are
     // loaded during the first token, its first token during the last.
@@ -287,7 +302,7 @@ void decode_window_kernel(
         }
         const bool more = head + stride < heads;
         const rsrc_t rs = state_rsrc(head);
-        const float gscale = FX && fx.A_log ? expf(fx.A_log[head - bq * H]) : 0.f;
+        const float gscale = FX && fx.A_log ? __expf(fx.A_log[head - bq * H]) : 0.f;
         for (int t = 0; t < Tw; ++t) {
             // LDS reuse across tokens as across heads in the single-token kernel
             if (tid < DK) {
@@ -303,6 +318,8 @@ void decode_window_kernel(
             }
             const f32x4 vv = cur.v;
             const float bb = cur.b;
+            f32x4 ep_u = zero4();
+            if (FX && fx.u && rg == 0) ep_u = epilogue_gate<NC4, T>(fx, (bq * Tw + t) * H + (head - bq * H), c4);
             if (t == 0 && more) load_rows(nrows, head + stride);
             if (t + 1 < Tw) {
                 load_tok(nxt, head, t + 1);
@@ -346,7 +363,7 @@ void decode_window_kernel(
                 const int64_t row = (bq * Tw + t) * H + (head - bq * H);
                 const f32x4 ov = rq + kq * delta;
                 if (o) reinterpret_cast<f32x4 *>(o + row * DV)[c4] = ov;
-                if (FX && fx.u) epilogue_store<NC4, T>(fx, row, c4, ov);
+                if (FX && fx.u) epilogue_store<NC4, T>(fx, row, c4, ov, ep_u, ep_w);
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) rows[r] += kr[r] * delta;  // erase + write

@@ -6,9 +6,9 @@
 // of q and k; the output-gate section: per-head RMSNorm times a Sigmoid gate).
 //
 // All three are one streaming pass over [N, H, d] rows: HBM-bound, no matrix
-// work.  A thread owns four consecutive channels of one (token, head) row (one
-// 8- or 16-byte access per tensor); the d/4 threads of a row sit in one wave,
-// so a row sum (L2 or RMS norm) is a few cross-lane adds.
+// work.  A lane owns eight consecutive channels of one (token, head) row (one
+// 16-byte access per bf16 tensor); the d/8 lanes of a row sit in one wave, so
+// a row sum (L2 or RMS norm) is a few cross-lane adds.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -17,15 +17,54 @@ namespace kda {
 constexpr int LAYER_THREADS = 256;
 constexpr float GATE_MIN = -5.0f;  // g_min of the bounded gate
 
-__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x)); }
+// Sigmoid on the hardware exp and reciprocal (about 1e-6 relative; every use
+// here is rounded to the input dtype or compared at the fp32 bar).
+__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+// Eight consecutive elements of one row: one 16-byte access for bf16, two for fp32.
+struct V8 {
+    f32x4 a, b;
+};
 
 template <typename T>
-__device__ __forceinline__ void store_out4(T *p, f32x4 x) {
+__device__ __forceinline__ V8 load8(const T *p) {
     if constexpr (sizeof(T) == 4) {
-        *reinterpret_cast<f32x4 *>(p) = x;
+        return V8{*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
     } else {
-        *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(x);  // round to nearest even
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+        return V8{f32x4{lo_bf16(w[0]), hi_bf16(w[0]), lo_bf16(w[1]), hi_bf16(w[1])},
+                  f32x4{lo_bf16(w[2]), hi_bf16(w[2]), lo_bf16(w[3]), hi_bf16(w[3])}};
     }
+}
+
+// The same for data read once (streamed past the caches).
+template <typename T>
+__device__ __forceinline__ V8 load8_stream(const T *p) {
+    if constexpr (sizeof(T) == 4) {
+        return V8{__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p)),
+                  __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4))};
+    } else {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return V8{f32x4{lo_bf16(w[0]), hi_bf16(w[0]), lo_bf16(w[1]), hi_bf16(w[1])},
+                  f32x4{lo_bf16(w[2]), hi_bf16(w[2]), lo_bf16(w[3]), hi_bf16(w[3])}};
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const V8 &x) {
+    if constexpr (sizeof(T) == 4) {
+        __builtin_nontemporal_store(x.a, reinterpret_cast<f32x4 *>(p));
+        __builtin_nontemporal_store(x.b, reinterpret_cast<f32x4 *>(p + 4));
+    } else {
+        // round to nearest even, then one streaming 16-byte store
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, cat(to_bf16x4(x.a), to_bf16x4(x.b))),
+                                    reinterpret_cast<u32x4 *>(p));
+    }
+}
+
+__device__ __forceinline__ float sumsq(const V8 &x) {
+    const f32x4 s = x.a * x.a + x.b * x.b;
+    return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 // Sum over the R lanes of a row (R a power of two, rows aligned to R lanes).
@@ -39,21 +78,34 @@ __device__ __forceinline__ float row_sum(float x) {
 // ------------------------------------------------------------------ decay gate
 // g = -5 Sigmoid(e^{A_h} z) for every (token, head, channel); the result is
 // written in the input dtype, the form the recurrence's entry points take.
+// Eight channels per lane; dk is a power of two, so the row is a shift.
 template <typename T>
 __global__ __launch_bounds__(LAYER_THREADS) void gate_kernel(const T *__restrict__ z,
                                                              const float *__restrict__ A_log,
-                                                             T *__restrict__ g, int64_t quads, int32_t H,
-                                                             int32_t dk) {
+                                                             T *__restrict__ g, int64_t octs, int32_t H,
+                                                             int32_t dk_shift) {
+    // GATE_UNROLL octets per trip, all loads issued first, so each lane keeps
+    // several 16-byte loads in flight
+    constexpr int GATE_UNROLL = 4;
     const int64_t stride = (int64_t)gridDim.x * LAYER_THREADS;
-    for (int64_t i = (int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x; i < quads; i += stride) {
-        const int64_t e = 4 * i;
-        const int h = (int)((e / dk) % H);
-        const float s = expf(A_log[h]);
-        const f32x4 x = load_in4(z + e);
-        f32x4 r;
+    for (int64_t i0 = (int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x; i0 < octs; i0 += GATE_UNROLL * stride) {
+        V8 x[GATE_UNROLL];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = GATE_MIN * sigmoidf(s * x[j]);
-        store_out4(g + e, r);
+        for (int u = 0; u < GATE_UNROLL; ++u)
+            if (i0 + u * stride < octs) x[u] = load8_stream(z + 8 * (i0 + u * stride));
+#pragma unroll
+        for (int u = 0; u < GATE_UNROLL; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i >= octs) break;
+            const uint32_t row = (uint32_t)((8 * i) >> dk_shift);  // (token, head) row, < 2^31
+            const float s = __expf(A_log[row % (uint32_t)H]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[u].a[j] = GATE_MIN * sigmoidf(s * x[u].a[j]);
+                x[u].b[j] = GATE_MIN * sigmoidf(s * x[u].b[j]);
+            }
+            store8(g + 8 * i, x[u]);
+        }
     }
 }
 
@@ -61,53 +113,94 @@ __global__ __launch_bounds__(LAYER_THREADS) void gate_kernel(const T *__restrict
 // y_t = Swish(sum_{j<4} w[j] x_{t-j}) per (head, channel), inputs before the
 // sequence's first token from its cache (3 values, oldest first; zeros without
 // a cache), then optionally y / sqrt(sum_c y^2 + eps) over the row.
+//
+// A work item is a run of RUN consecutive tokens of one head; its D/8 lanes
+// (eight channels each) walk the run carrying the last three inputs in
+// registers, so each input row is read about once (plus three rows per run),
+// and neighbouring items are neighbouring heads of the same tokens (coalesced
+// rows).  A run that crosses into the next sequence restarts the window there.
+constexpr int CONV_RUN = 16;
+
 template <typename T, int D>
 __global__ __launch_bounds__(LAYER_THREADS) void short_conv_kernel(
     const T *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cache,
-    const int32_t *__restrict__ cu, int32_t nseq, int64_t rows, int32_t H, bool l2norm, float eps,
+    const int32_t *__restrict__ cu, int32_t nseq, int64_t N, int32_t H, bool l2norm, float eps,
     T *__restrict__ y) {
-    constexpr int R = D / 4;  // threads per (token, head) row
+    constexpr int R = D / 8;  // lanes per (token, head) row
+    const int64_t items = (N + CONV_RUN - 1) / CONV_RUN * H;
     const int64_t stride = (int64_t)gridDim.x * LAYER_THREADS / R;
-    const int c0 = 4 * (threadIdx.x % R);
-    for (int64_t row = ((int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x) / R; row < rows; row += stride) {
-        const int64_t t = row / H;
-        const int h = (int)(row - t * H);
-        // sequence of token t: the last s with cu[s] <= t
-        int lo = 0, hi = nseq - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cu[mid] <= t) lo = mid;
+    const int c0 = 8 * (threadIdx.x % R);
+    for (int64_t item = ((int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x) / R; item < items; item += stride) {
+        const int64_t run = item / H;
+        const int h = (int)(item - run * H);
+        const int64_t t0 = run * CONV_RUN;
+        const int64_t t1 = t0 + CONV_RUN < N ? t0 + CONV_RUN : N;
+        float wv[4][8];  // tap j of channel c0 + m
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const f32x4 wm = *reinterpret_cast<const f32x4 *>(w + ((int64_t)h * D + c0 + m) * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wv[j][m] = wm[j];
+        }
+        // sequence of token t0: the last s with cu[s] <= t0
+        int s = 0, hi = nseq - 1;
+        while (s < hi) {
+            const int mid = (s + hi + 1) >> 1;
+            if (cu[mid] <= t0) s = mid;
             else hi = mid - 1;
         }
-        const int64_t bos = cu[lo];
-        f32x4 wv[4];  // the 4 taps of channel c0 + m
+        int64_t bos = cu[s], eos = cu[s + 1];
+        // the window x_{t-1}, x_{t-2}, x_{t-3} before token t (cache position 3 + t - j - bos)
+        V8 win[3];
+        auto fill = [&](int64_t t) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) wv[m] = *reinterpret_cast<const f32x4 *>(w + ((int64_t)h * D + c0 + m) * 4);
-        f32x4 acc = zero4();
+            for (int j = 1; j <= 3; ++j) {
+                const int64_t src = t - j;
+                if (src >= bos) {
+                    win[j - 1] = load8(x + (src * H + h) * D + c0);
+                } else if (cache) {
+                    const float *cp = cache + (((int64_t)s * H + h) * D + c0) * 3 + (3 + (src - bos));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t src = t - j;
-            f32x4 xv;
-            if (src >= bos) {
-                xv = load_in4(x + (src * H + h) * D + c0);
-            } else if (cache) {  // position 3 + (src - bos) of the cache, oldest first
-                const float *cp = cache + (((int64_t)lo * H + h) * D + c0) * 3 + (3 + (src - bos));
-#pragma unroll
-                for (int m = 0; m < 4; ++m) xv[m] = cp[3 * m];
-            } else {
-                xv = zero4();
+                    for (int m = 0; m < 4; ++m) {
+                        win[j - 1].a[m] = cp[3 * m];
+                        win[j - 1].b[m] = cp[3 * (m + 4)];
+                    }
+                } else {
+                    win[j - 1] = V8{zero4(), zero4()};
+                }
             }
+        };
+        fill(t0);
+        V8 xn = load8(x + (t0 * H + h) * D + c0);  // the next token's input, one token ahead
+        for (int64_t t = t0; t < t1; ++t) {
+            if (t == eos) {  // the run enters the next non-empty sequence
+                while (cu[s + 1] <= t) ++s;
+                bos = cu[s];
+                eos = cu[s + 1];
+                fill(t);
+            }
+            const V8 xt = xn;
+            if (t + 1 < t1) xn = load8(x + ((t + 1) * H + h) * D + c0);
+            V8 r;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] += wv[m][j] * xv[m];
+            for (int m = 0; m < 4; ++m) {
+                const float aa = wv[0][m] * xt.a[m] + wv[1][m] * win[0].a[m] + wv[2][m] * win[1].a[m] +
+                                 wv[3][m] * win[2].a[m];
+                const float ab = wv[0][m + 4] * xt.b[m] + wv[1][m + 4] * win[0].b[m] +
+                                 wv[2][m + 4] * win[1].b[m] + wv[3][m + 4] * win[2].b[m];
+                r.a[m] = aa * sigmoidf(aa);  // Swish
+                r.b[m] = ab * sigmoidf(ab);
+            }
+            if (l2norm) {
+                const float inv = __builtin_amdgcn_rsqf(row_sum<R>(sumsq(r)) + eps);
+                r.a = r.a * inv;
+                r.b = r.b * inv;
+            }
+            store8(y + (t * H + h) * D + c0, r);
+            win[2] = win[1];
+            win[1] = win[0];
+            win[0] = xt;
         }
-        f32x4 r;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) r[m] = acc[m] * sigmoidf(acc[m]);  // Swish
-        if (l2norm) {
-            const float ss = row_sum<R>(r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3]);
-            r = r * (1.f / sqrtf(ss + eps));
-        }
-        store_out4(y + row * D + c0, r);
     }
 }
 
@@ -147,19 +240,35 @@ __global__ __launch_bounds__(LAYER_THREADS) void out_norm_gate_kernel(const floa
                                                                       const T *__restrict__ u,
                                                                       const float *__restrict__ w, float eps,
                                                                       int64_t rows, T *__restrict__ y) {
-    constexpr int R = D / 4;
+    constexpr int R = D / 8;
     const int64_t stride = (int64_t)gridDim.x * LAYER_THREADS / R;
-    const int c0 = 4 * (threadIdx.x % R);
-    const f32x4 wv = *reinterpret_cast<const f32x4 *>(w + c0);
-    for (int64_t row = ((int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x) / R; row < rows; row += stride) {
-        const f32x4 ov = *reinterpret_cast<const f32x4 *>(o + row * D + c0);
-        const f32x4 uv = load_in4(u + row * D + c0);
-        const float ms = row_sum<R>(ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3]) * (1.f / D);
-        const float inv = 1.f / sqrtf(ms + eps);
-        f32x4 r;
+    const int c0 = 8 * (threadIdx.x % R);
+    const V8 wv = load8(w + c0);
+    // two rows per trip, loads first (the lanes of a row stay together: both
+    // rows are tested for the whole row group)
+    for (int64_t r0 = ((int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x) / R; r0 < rows; r0 += 2 * stride) {
+        V8 ov[2], uv[2];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) r[m] = sigmoidf(uv[m]) * ov[m] * inv * wv[m];
-        store_out4(y + row * D + c0, r);
+        for (int k = 0; k < 2; ++k) {
+            const int64_t row = r0 + k * stride;
+            if (row < rows) {
+                ov[k] = load8_stream(o + row * D + c0);
+                uv[k] = load8_stream(u + row * D + c0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t row = r0 + k * stride;
+            if (row >= rows) break;
+            const float inv = __builtin_amdgcn_rsqf(row_sum<R>(sumsq(ov[k])) * (1.f / D) + eps);
+            V8 r;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                r.a[m] = sigmoidf(uv[k].a[m]) * ov[k].a[m] * inv * wv.a[m];
+                r.b[m] = sigmoidf(uv[k].b[m]) * ov[k].b[m] * inv * wv.b[m];
+            }
+            store8(y + row * D + c0, r);
+        }
     }
 }
 
@@ -174,22 +283,24 @@ static unsigned layer_blocks(int64_t threads) {
 }
 
 hipError_t launch_gate(const GateArgs &a) {
-    const int64_t quads = a.N * a.H * a.dk / 4;
-    if (quads == 0) return hipSuccess;
+    const int64_t octs = a.N * a.H * a.dk / 8;
+    if (octs == 0) return hipSuccess;
+    const int shift = __builtin_ctz((unsigned)a.dk);
     const hipStream_t st = (hipStream_t)a.stream;
     if (a.bf16)
-        hipLaunchKernelGGL(gate_kernel<__bf16>, dim3(layer_blocks(quads)), dim3(LAYER_THREADS), 0, st,
-                           (const __bf16 *)a.z, a.A_log, (__bf16 *)a.g, quads, a.H, a.dk);
+        hipLaunchKernelGGL(gate_kernel<__bf16>, dim3(layer_blocks(octs)), dim3(LAYER_THREADS), 0, st,
+                           (const __bf16 *)a.z, a.A_log, (__bf16 *)a.g, octs, a.H, shift);
     else
-        hipLaunchKernelGGL(gate_kernel<float>, dim3(layer_blocks(quads)), dim3(LAYER_THREADS), 0, st,
-                           (const float *)a.z, a.A_log, (float *)a.g, quads, a.H, a.dk);
+        hipLaunchKernelGGL(gate_kernel<float>, dim3(layer_blocks(octs)), dim3(LAYER_THREADS), 0, st,
+                           (const float *)a.z, a.A_log, (float *)a.g, octs, a.H, shift);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static void launch_conv_t(const ShortConvArgs &a, int64_t rows) {
-    hipLaunchKernelGGL((short_conv_kernel<T, D>), dim3(layer_blocks(rows * (D / 4))), dim3(LAYER_THREADS), 0,
-                       (hipStream_t)a.stream, (const T *)a.x, a.w, a.cache_in, a.cu, a.nseq, rows, a.H,
+static void launch_conv_t(const ShortConvArgs &a) {
+    const int64_t items = (a.N + CONV_RUN - 1) / CONV_RUN * a.H;
+    hipLaunchKernelGGL((short_conv_kernel<T, D>), dim3(layer_blocks(items * (D / 8))), dim3(LAYER_THREADS), 0,
+                       (hipStream_t)a.stream, (const T *)a.x, a.w, a.cache_in, a.cu, a.nseq, a.N, a.H,
                        a.l2norm, a.eps, (T *)a.y);
 }
 
@@ -198,10 +309,10 @@ static hipError_t launch_conv_dt(const ShortConvArgs &a) {
     const int64_t rows = a.N * a.H;
     if (rows > 0) {
         switch (a.d) {
-            case 16: launch_conv_t<T, 16>(a, rows); break;
-            case 32: launch_conv_t<T, 32>(a, rows); break;
-            case 64: launch_conv_t<T, 64>(a, rows); break;
-            case 128: launch_conv_t<T, 128>(a, rows); break;
+            case 16: launch_conv_t<T, 16>(a); break;
+            case 32: launch_conv_t<T, 32>(a); break;
+            case 64: launch_conv_t<T, 64>(a); break;
+            case 128: launch_conv_t<T, 128>(a); break;
             default: return hipErrorInvalidValue;
         }
         const hipError_t e = hipGetLastError();
@@ -223,7 +334,7 @@ hipError_t launch_short_conv(const ShortConvArgs &a) {
 
 template <typename T, int D>
 static void launch_epi_t(const OutNormGateArgs &a, int64_t rows) {
-    hipLaunchKernelGGL((out_norm_gate_kernel<T, D>), dim3(layer_blocks(rows * (D / 4))), dim3(LAYER_THREADS), 0,
+    hipLaunchKernelGGL((out_norm_gate_kernel<T, D>), dim3(layer_blocks(rows * (D / 8))), dim3(LAYER_THREADS), 0,
                        (hipStream_t)a.stream, a.o, (const T *)a.u, a.w, a.eps, rows, (T *)a.y);
 }
 

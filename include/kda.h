@@ -216,9 +216,9 @@ kda_status kda_decode_window_fused(const void *q, const void *k, const void *v,
  * one streaming pass (HBM-bound), enqueued on `stream` like the calls above;
  * the projections that feed them (z, u, the pre-convolution q/k/v) and W_o are
  * the caller's.  dk, d, dv in {16, 32, 64, 128}; N in [0, 2^31); H >= 1;
- * eps >= 0 and finite.  [.., d] tensors in the input dtype are read and
- * written four elements at a time (alignment as for q above); fp32 weight and
- * cache arrays 16 bytes.
+ * eps >= 0 and finite.  [.., d] tensors (input dtype, and o) are read and
+ * written eight elements at a time and must be 16-byte aligned; fp32 weight
+ * arrays 16 bytes, caches 4 bytes.
  * ------------------------------------------------------------------------ */
 
 /* Decay gate: log_alpha = -5 * Sigmoid(exp(A_log[h]) * z), the bounded
