@@ -17,7 +17,7 @@ The JSON line also carries, measured in the same run:
   * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
 each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|varlen|none]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|layer|varlen|none]
 """
 from __future__ import annotations
 
@@ -338,7 +338,7 @@ def _event_ms(torch, fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def bench_layer(torch, kda, workloads, dev, steps):
+def bench_layer(torch, kda, workloads, dev):
     """The layer's passes around the recurrence.  Prefill side, on the K3 layer shape (65,536
     tokens x 96 heads, d = 128, bf16): the decay gate, the ShortConv prologue of q (with L2
     norm) and the epilogue, each one HBM pass (GB/s of algorithmic bytes against 8 TB/s).
@@ -365,9 +365,10 @@ def bench_layer(torch, kda, workloads, dev, steps):
     torch.cuda.empty_cache()
 
     w4 = workloads.workload(4)
+    step0 = workloads.decode_step_inputs(w4, 0, device=dev)
     for B in (w4.nseq, 4):
         Hd, dk, dv = w4.H, w4.dk, w4.dv
-        x = {n: t[:B].contiguous() for n, t in steps[0].items()}
+        x = {n: t[:B].contiguous() for n, t in step0.items()}
         lk = workloads.layer_inputs(B, Hd, dk, torch.bfloat16, device=dev, seed=1)
         lv = workloads.layer_inputs(B, Hd, dv, torch.bfloat16, device=dev, seed=2)
         state = workloads.decode_initial_state(B, Hd, dk, dv, device=dev)
@@ -398,13 +399,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", choices=["all", "main", "k3", "decode", "varlen", "none"])
+    ap.add_argument("--only", default="all", choices=["all", "main", "k3", "decode", "layer", "varlen", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 (heads and sequences shard "
+        print("bench.py: measures one GPU; --gpus must be 1 (heads and sequences shard "
               "across GPUs with no exchange -- see the design notes)", file=sys.stderr)
         return 2
 
@@ -466,10 +467,11 @@ def main() -> int:
         for T in (4, 8):
             log(f"[bench] decode windows of {T} drafts (speculative verification), B=256 H=96")
             out[f"decode_window_{T}"] = bench_decode_window(torch, kda, workloads, dev, steps, T)
-        log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
-        out["layer"] = bench_layer(torch, kda, workloads, dev, steps)
         del steps
         torch.cuda.empty_cache()
+    if args.only in ("all", "layer"):
+        log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
+        out["layer"] = bench_layer(torch, kda, workloads, dev)
     if args.only in ("all", "varlen"):
         log("[bench] varlen 1M-token prefill")
         out["varlen_1m"] = bench_prefill_workload(5, torch, kda, workloads, dev, reps=3)

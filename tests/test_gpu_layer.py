@@ -246,3 +246,34 @@ def test_decode_window_fused_matches_oracle(dev, dtype):
     assert_close(st, s_ref, TOL[dtype], "state")
     assert torch.equal(st[0], state0[0])
     _assert_y(y, layer.out_norm_gate(o_ref, _np(u), _np(lv["norm_w"]), 1e-6), dtype, "y")
+
+
+def test_layer_passes_with_no_tokens(dev):
+    """N = 0: nothing to compute; the ShortConv cache of empty sequences passes through."""
+    H, d = 2, 64
+    z = torch.empty((0, H, d), dtype=torch.bfloat16, device=dev)
+    A = torch.zeros((H,), dtype=torch.float32, device=dev)
+    assert kda.kda_gate(z, A).shape == (0, H, d)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    li = workloads.layer_inputs(1, H, d, torch.bfloat16, nseq=2, device=dev, seed=5)
+    y, c = kda.kda_short_conv(z, li["conv_w"], cu, li["conv_cache"], l2norm=True)
+    e = kda.kda_out_norm_gate(torch.empty((0, H, d), dtype=torch.float32, device=dev), z, li["norm_w"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, H, d) and e.shape == (0, H, d)
+    assert torch.equal(c, li["conv_cache"])
+
+
+def test_fused_window_of_one_token_equals_fused_step(dev):
+    """A one-token fused window and the fused decode step (same kernels' arithmetic per token)."""
+    x, lk, lv, state0 = _decode_case(dev, torch.bfloat16, 128, 128, B=4, H=3, seed=9)
+    s1, s2 = state0.clone(), state0.clone()
+    o1, y1 = kda.kda_decode_step_fused(x["q"], x["k"], x["v"], lk["z"], x["beta"], s1, gate_A_log=lk["A_log"],
+                                       out_gate=lv["u"], norm_w=lv["norm_w"])
+    w = {n: t.unsqueeze(1).contiguous() for n, t in x.items()}
+    o2, y2 = kda.kda_decode_window_fused(w["q"], w["k"], w["v"], lk["z"].unsqueeze(1).contiguous(), w["beta"], s2,
+                                         gate_A_log=lk["A_log"], out_gate=lv["u"].unsqueeze(1).contiguous(),
+                                         norm_w=lv["norm_w"])
+    torch.cuda.synchronize()
+    assert_close(o2[:, 0], _np(o1), 1e-6, "o")
+    assert_close(s2, _np(s1), 1e-6, "state")
+    _assert_y(y2[:, 0], _np(y1), torch.bfloat16, "y")
