@@ -390,6 +390,33 @@ def bench_layer(torch, kda, workloads, dev):
         res[f"decode_b{B}"] = {"batch": B, "heads": Hd, "ms_fused": round(ms_f, 5), "ms_separate": round(ms_s, 5),
                                "speedup": ms_s / ms_f}
         del x, lk, lv, state, o, yv, gz
+
+    # windows of 4 drafts at B=256: the fused call (gate in the window kernel, epilogue as a
+    # second launch over o) against gate + window + epilogue as three launches
+    B, T, Hd, dk, dv = w4.nseq, 4, w4.H, w4.dk, w4.dv
+    xw = workloads.decode_window_inputs(w4, T, 0, device=dev)
+    lk = workloads.layer_inputs(B * T, Hd, dk, torch.bfloat16, device=dev, seed=3)
+    lv = workloads.layer_inputs(B * T, Hd, dv, torch.bfloat16, device=dev, seed=4)
+    z, u = lk["z"].view(B, T, Hd, dk), lv["u"].view(B, T, Hd, dv)
+    acc = workloads.window_accept(B, T, device=dev, seed=0, lo=1)
+    state = workloads.decode_initial_state(B, Hd, dk, dv, device=dev)
+    o = torch.empty((B, T, Hd, dv), dtype=torch.float32, device=dev)
+    yv = torch.empty((B, T, Hd, dv), dtype=torch.bfloat16, device=dev)
+    gz = torch.empty_like(z)
+
+    def wfused():
+        kda.kda_decode_window_fused(xw["q"], xw["k"], xw["v"], z, xw["beta"], state, acc, gate_A_log=lk["A_log"],
+                                    out_gate=u, norm_w=lv["norm_w"], o=o, output_o=False, y=yv)
+
+    def wseparate():
+        kda.kda_gate(lk["z"], lk["A_log"], out=gz.view(B * T, Hd, dk))
+        kda.kda_decode_window(xw["q"], xw["k"], xw["v"], gz, xw["beta"], state, acc, o=o)
+        kda.kda_out_norm_gate(o.view(B * T, Hd, dv), lv["u"], lv["norm_w"], 1e-6, y=yv.view(B * T, Hd, dv))
+
+    ms_f, ms_s = _event_ms(torch, wfused, 20), _event_ms(torch, wseparate, 20)
+    res["decode_window4_b256"] = {"batch": B, "T": T, "heads": Hd, "ms_fused": round(ms_f, 5),
+                                  "ms_separate": round(ms_s, 5), "speedup": ms_s / ms_f}
+    del xw, lk, lv, state, o, yv, gz
     torch.cuda.empty_cache()
     return res
 

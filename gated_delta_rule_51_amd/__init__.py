@@ -393,10 +393,11 @@ def kda_decode_window_fused(q, k, v, gate, beta, state, accept=None, *, gate_A_l
     if accept is not None:
         _check_dev("accept", accept, q.device, torch.int32, (B,))
     y = _fusion_args((B, T, H, dv), q.dtype, q.device, H, dv, gate_A_log, out_gate, norm_w, y, True)
-    if output_o and o is None:
+    # the window's epilogue runs over o, so o is materialised whenever out_gate is given
+    if (output_o or out_gate is not None) and o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     _check(load_library().kda_decode_window_fused(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_A_log), _ptr(beta), _ptr(state),
-        _ptr(o if output_o else None), _ptr(accept), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
+        _ptr(o), _ptr(accept), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
         B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
     return (o if output_o else None), y

@@ -203,6 +203,11 @@ kda_status kda_decode_window_fused(const void *q, const void *k, const void *v, 
     if (accept && (reinterpret_cast<uintptr_t>(accept) & 3u)) return KDA_ERR_ALIGN;
     st = check_fusion(gate_A_log, out_gate, norm_w, norm_eps, y, dt == KDA_BF16);
     if (st != KDA_OK) return st;
+    if (out_gate) {  // the window's epilogue runs over o: o is required, rows 16-byte aligned
+        if (!o) return KDA_ERR_NULL;
+        st = check_rows16({out_gate, y}, true);
+        if (st != KDA_OK) return st;
+    }
     kda::DecodeWindowArgs a{q, k, v, gate, beta, state, o, accept, B, T, H, dk, dv, dt == KDA_BF16, stream,
                             {gate_A_log, out_gate, norm_w, norm_eps, y}};
     return hip_status(kda::launch_decode_window(a));

@@ -26,6 +26,8 @@
 // stride is padded so the lanes of a wave hit distinct banks) and the P
 // lanes combine by cross-lane shuffles.  Every thread then reads back only
 // the two quads it needs.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -53,18 +55,31 @@ constexpr int64_t GRID_THREADS = 1 << 20;
 // g = g_min Sigmoid(e^{A_h} z) with g_min = -5, and the output-gate section's
 // per-head RMSNorm times a Sigmoid gate), evaluated in fp32 where the decode
 // kernels already hold the operands: the gate on the key channels before the
-// forget step, the epilogue on the output row (the NC4 lanes that hold it sit
-// in the first wave, so its mean square is a few cross-lane adds).
+// forget step (both kernels); the epilogue on the output row in the
+// single-token kernel (the NC4 lanes that hold it sit in the first wave, so its
+// mean square is a few cross-lane adds) -- the window runs it as a second pass.
 // (hardware exp and reciprocal, about 1e-6 relative: these sit on the serial
 // path of each head, between barriers)
 __device__ __forceinline__ float gate_from_logit(float z, float scale) {
     return -5.0f * __builtin_amdgcn_rcpf(1.0f + __expf(-scale * z));
 }
 
-// The output-gate logits of row `row`, columns 4 c4 .. +3 (loaded ahead of use).
+// The output-gate logits of row `row`, columns 4 c4 .. +3, loaded ahead of use
+// and kept as loaded (two registers for bf16) until the epilogue widens them.
+template <typename T>
+using GateRaw = typename std::conditional<sizeof(T) == 4, f32x4, u32x2>::type;
+
 template <int NC4, typename T>
-__device__ __forceinline__ f32x4 epilogue_gate(const DecodeFusion &fx, int64_t row, int c4) {
-    return load_in4(reinterpret_cast<const T *>(fx.u) + row * (4 * NC4) + 4 * c4);
+__device__ __forceinline__ GateRaw<T> epilogue_gate(const DecodeFusion &fx, int64_t row, int c4) {
+    return *reinterpret_cast<const GateRaw<T> *>(reinterpret_cast<const T *>(fx.u) + row * (4 * NC4) + 4 * c4);
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 widen_gate(GateRaw<T> x) {
+    if constexpr (sizeof(T) == 4)
+        return x;
+    else
+        return unpack_bf16x4(x);
 }
 
 template <int NC4, typename T>
@@ -134,7 +149,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
         }
         const f32x4 vv = load_in4(v + head * DV + 4 * c4);
         const float b = load_in(beta + head);
-        f32x4 ep_u = zero4();
+        GateRaw<T> ep_u = {};
         if (FX && fx.u && rg == 0) ep_u = epilogue_gate<NC4, T>(fx, head, c4);
         if (head + stride < heads) load_rows(nxt, head + stride);
         __syncthreads();
@@ -174,7 +189,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
         if (rg == 0) {
             const f32x4 ov = rq + kq * delta;
             if (o) reinterpret_cast<f32x4 *>(o + head * DV)[c4] = ov;
-            if (FX && fx.u) epilogue_store<NC4, T>(fx, head, c4, ov, ep_u, ep_w);
+            if (FX && fx.u) epilogue_store<NC4, T>(fx, head, c4, ov, widen_gate<T>(ep_u), ep_w);
         }
 
         float *S = state + head * (int64_t)(DK * DV);
@@ -288,8 +303,6 @@ void decode_window_kernel(
 
     Tok cur, nxt;
     int par = 0;
-    f32x4 ep_w = zero4();  // RMSNorm weight of this lane's columns (epilogue lanes: rg == 0)
-    if (FX && fx.u && rg == 0) ep_w = *reinterpret_cast<const f32x4 *>(fx.w + 4 * c4);
     // One (sequence, head): the window's tokens in order, the state rows in
     // registers throughout.  The next head's state rows (into nrows) are
     // loaded during the first token, its first token during the last.
@@ -318,8 +331,6 @@ void decode_window_kernel(
             }
             const f32x4 vv = cur.v;
             const float bb = cur.b;
-            f32x4 ep_u = zero4();
-            if (FX && fx.u && rg == 0) ep_u = epilogue_gate<NC4, T>(fx, (bq * Tw + t) * H + (head - bq * H), c4);
             if (t == 0 && more) load_rows(nrows, head + stride);
             if (t + 1 < Tw) {
                 load_tok(nxt, head, t + 1);
@@ -359,12 +370,8 @@ void decode_window_kernel(
 #pragma unroll
             for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
             const f32x4 delta = bb * (vv - vhat);
-            if (rg == 0) {
-                const int64_t row = (bq * Tw + t) * H + (head - bq * H);
-                const f32x4 ov = rq + kq * delta;
-                if (o) reinterpret_cast<f32x4 *>(o + row * DV)[c4] = ov;
-                if (FX && fx.u) epilogue_store<NC4, T>(fx, row, c4, ov, ep_u, ep_w);
-            }
+            const int64_t orow = (bq * Tw + t) * H + (head - bq * H);
+            if (o && rg == 0) reinterpret_cast<f32x4 *>(o + orow * DV)[c4] = rq + kq * delta;
 #pragma unroll
             for (int r = 0; r < NR; ++r) rows[r] += kr[r] * delta;  // erase + write
             if (t + 1 == acc) {
@@ -373,6 +380,7 @@ void decode_window_kernel(
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, rows[r]), rs, soff,
                                                            r * ROW_STEP, NT_POLICY);
             }
+
             cur = nxt;
             par ^= 1;
         }
@@ -429,12 +437,18 @@ static hipError_t launch_window_t(const DecodeWindowArgs &a) {
     const int64_t heads = (int64_t)a.B * a.H;
     const int64_t cap = GRID_THREADS / Sh::NT;
     const int64_t grid = heads < cap ? heads : cap;
-    const bool fused = a.fx.A_log || a.fx.u;
+    const bool fused = a.fx.A_log != nullptr;
     hipLaunchKernelGGL((fused ? decode_window_kernel<DK, DV, T, true> : decode_window_kernel<DK, DV, T, false>),
                        dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.state, a.o,
                        a.accept, heads, a.H, a.T, a.fx);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.fx.u) return e;
+    // The epilogue as a second pass over the window's outputs: inside the window
+    // kernel its registers pushed the token loop into spills, whose reloads then
+    // waited on every prefetch in flight.
+    const OutNormGateArgs ep{a.o, a.fx.u, a.fx.w, a.fx.eps, (int64_t)a.B * a.T, a.H, a.dv, a.bf16, a.fx.y, a.stream};
+    return launch_out_norm_gate(ep);
 }
 
 template <typename T>

@@ -189,8 +189,10 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v,
  *   * out_gate != NULL: y = Sigmoid(out_gate) * o / sqrt(mean(o^2) + norm_eps)
  *     * norm_w over the dv channels of each output row, written in the input
  *     dtype; out_gate and y are shaped like o (input dtype, 4-element aligned),
- *     norm_w fp32 [dv] (16-byte aligned), norm_eps >= 0.  o may then be NULL
- *     (not written).
+ *     norm_w fp32 [dv] (16-byte aligned), norm_eps >= 0.  In the single step
+ *     o may then be NULL (not written).  The window computes the epilogue as a
+ *     second launch over o (inside the window kernel it cost more than it
+ *     saved), so there o is required and out_gate, y are 16-byte aligned.
  * Everything else as in the unfused calls. */
 kda_status kda_decode_step_fused(const void *q, const void *k, const void *v,
                                  const void *gate, const float *gate_A_log,
