@@ -154,15 +154,22 @@ def cpu_baseline(workload, seed: int = 0) -> dict:
         cores = os.cpu_count() or 1
     names = ("q", "k", "v", "log_alpha", "beta")
     args = [x[n].double().numpy() for n in names]
-    t0 = time.perf_counter()
-    _, fin = oracle.prefill(*args, cu_seqlens=x["cu_seqlens"].numpy(), nthreads=cores)
-    oracle.decode(*(d[n].double().numpy() for n in names), fin, nthreads=cores)
-    dt = time.perf_counter() - t0
-    tokens = workload.total_tokens + workload.nseq
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "seconds": dt,
-            "sample": f"whole batch: prefill of {workload.nseq}x{workload.seqlens[0]} tokens x {workload.H} heads "
-                      f"(dk=dv={workload.dk}) + 1 decode token per sequence, fp64, {cores} threads"}
+    dargs = [d[n].double().numpy() for n in names]
+    threads = min(cores, workload.nseq * workload.H)  # the oracle runs one thread per (sequence, head) at most
+    # the whole batch, repeated until about 10 s of host time have been measured
+    reps, dt = 0, 0.0
+    while dt < 10.0 or reps < 1:
+        t0 = time.perf_counter()
+        _, fin = oracle.prefill(*args, cu_seqlens=x["cu_seqlens"].numpy(), nthreads=threads)
+        oracle.decode(*dargs, fin, nthreads=threads)
+        dt += time.perf_counter() - t0
+        reps += 1
+    tokens = (workload.total_tokens + workload.nseq) * reps
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": dt, "repetitions": reps,
+            "sample": f"whole batch, {reps} times: prefill of {workload.nseq}x{workload.seqlens[0]} tokens x "
+                      f"{workload.H} heads (dk=dv={workload.dk}) + 1 decode token per sequence, fp64, "
+                      f"{threads} threads"}
 
 
 def bench_main(args, torch, kda, workloads, dev):
