@@ -298,15 +298,19 @@ def kda_short_conv(x, w, cu_seqlens=None, cache=None, *, l2norm: bool = False, e
     """ShortConv prologue: y = Swish(causal 4-tap depthwise convolution of x) [L2-normalised over d].
 
     x [N, H, d] (bf16 or fp32); w fp32 [H, d, 4] (tap j multiplies x_{t-j}); cu_seqlens int32
-    [nseq + 1] on the device (None = one sequence); cache fp32 [nseq, H, d, 3] (the 3 inputs before
-    each sequence, oldest first) or None.  Returns (y, cache_out) with cache_out the 3 last inputs
+    [nseq + 1] on the device (None = one sequence; "decode" = every token its own sequence, as in a
+    decode step); cache fp32 [nseq, H, d, 3] (the 3 inputs before each sequence, oldest first) or
+    None.  Returns (y, cache_out) with cache_out the 3 last inputs
     per sequence (``cache_out`` may be ``cache`` to update it in place).
     """
     if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
         raise ValueError("x must be a tensor on a GPU; the KDA library has no CPU path")
     N, H, d = x.shape
-    cu = _cu(cu_seqlens, N, x.device)
-    nseq = cu.numel() - 1
+    if isinstance(cu_seqlens, str) and cu_seqlens == "decode":  # one token per sequence
+        cu, nseq = None, N
+    else:
+        cu = _cu(cu_seqlens, N, x.device)
+        nseq = cu.numel() - 1
     _check_dev("x", x, x.device)
     _check_dev("w", w, x.device, torch.float32, (H, d, 4))
     if cache is not None:

@@ -243,8 +243,10 @@ kda_status kda_short_conv(const void *x, const float *w, const float *cache_in, 
     if ((int64_t)nseq * H * d >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     kda_status st = check_rows16({x, y}, N > 0);
     if (st != KDA_OK) return st;
-    st = check_ptrs({w, cu_seqlens}, {});
+    st = check_ptrs({w}, {});
     if (st != KDA_OK) return st;
+    if (!cu_seqlens && nseq != N) return KDA_ERR_SHAPE;  // one token per sequence
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return KDA_ERR_ALIGN;
     if ((cache_in && (reinterpret_cast<uintptr_t>(cache_in) & 3u)) ||
         (cache_out && (reinterpret_cast<uintptr_t>(cache_out) & 3u)))
         return KDA_ERR_ALIGN;

@@ -142,14 +142,24 @@ __global__ __launch_bounds__(LAYER_THREADS) void short_conv_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) wv[j][m] = wm[j];
         }
-        // sequence of token t0: the last s with cu[s] <= t0
-        int s = 0, hi = nseq - 1;
-        while (s < hi) {
-            const int mid = (s + hi + 1) >> 1;
-            if (cu[mid] <= t0) s = mid;
-            else hi = mid - 1;
+        // sequence of token t0: the last s with cu[s] <= t0 (without cu_seqlens,
+        // every token is a sequence of its own: a decode step)
+        int s = 0;
+        int64_t bos, eos;
+        if (cu) {
+            int hi = nseq - 1;
+            while (s < hi) {
+                const int mid = (s + hi + 1) >> 1;
+                if (cu[mid] <= t0) s = mid;
+                else hi = mid - 1;
+            }
+            bos = cu[s];
+            eos = cu[s + 1];
+        } else {
+            s = (int)t0;
+            bos = t0;
+            eos = t0 + 1;
         }
-        int64_t bos = cu[s], eos = cu[s + 1];
         // the window x_{t-1}, x_{t-2}, x_{t-3} before token t (cache position 3 + t - j - bos)
         V8 win[3];
         auto fill = [&](int64_t t) {
@@ -174,9 +184,15 @@ __global__ __launch_bounds__(LAYER_THREADS) void short_conv_kernel(
         V8 xn = load8(x + (t0 * H + h) * D + c0);  // the next token's input, one token ahead
         for (int64_t t = t0; t < t1; ++t) {
             if (t == eos) {  // the run enters the next non-empty sequence
-                while (cu[s + 1] <= t) ++s;
-                bos = cu[s];
-                eos = cu[s + 1];
+                if (cu) {
+                    while (cu[s + 1] <= t) ++s;
+                    bos = cu[s];
+                    eos = cu[s + 1];
+                } else {
+                    s = (int)t;
+                    bos = t;
+                    eos = t + 1;
+                }
                 fill(t);
             }
             const V8 xt = xn;
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(LAYER_THREADS) void conv_cache_kernel(const T *__re
     const int64_t s = i / ((int64_t)H * d);
     const int64_t hc = i - s * H * d;
     const int h = (int)(hc / d), c = (int)(hc - (int64_t)h * d);
-    const int64_t bos = cu[s], eos = cu[s + 1], len = eos - bos;
+    const int64_t bos = cu ? cu[s] : s, eos = cu ? cu[s + 1] : s + 1, len = eos - bos;
     float v[3];
 #pragma unroll
     for (int m = 0; m < 3; ++m) {

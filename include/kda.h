@@ -239,7 +239,9 @@ kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H,
  * sequence's last 3 inputs, oldest first (reaching into cache_in when the
  * sequence is shorter than 3), and may be cache_in itself.
  *   x, y: [N, H, d] (input dtype, distinct buffers); w: fp32 [H, d, 4];
- *   cu_seqlens: int32 [nseq + 1] device (as kda_prefill);
+ *   cu_seqlens: int32 [nseq + 1] device (as kda_prefill), or NULL with
+ *   nseq == N: every token its own sequence (a decode step, the cache carrying
+ *   each sequence's history);
  *   cache_in, cache_out: fp32 [nseq, H, d, 3]. */
 kda_status kda_short_conv(const void *x, const float *w, const float *cache_in,
                           float *cache_out, const int32_t *cu_seqlens,

@@ -145,7 +145,7 @@ def test_layer_passes_reject_bad_arguments(lib):
     assert g(FAKE, FAKE, 8, 2, 24, 1, FAKE, None) == 4
     c = lib.kda_short_conv  # x w cin cout cu nseq N H d l2 eps dt y stream
     assert c(FAKE, None, None, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 1
-    assert c(FAKE, FAKE, None, None, None, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 1
+    assert c(FAKE, FAKE, None, None, None, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 3  # no cu: nseq == N
     assert c(FAKE, FAKE + 4, None, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 2
     assert c(FAKE, FAKE, FAKE + 2, None, FAKE, 1, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 2
     assert c(FAKE, FAKE, None, None, FAKE, 0, 8, 2, 16, 0, 1e-6, 1, FAKE + 64, None) == 3

@@ -277,3 +277,50 @@ def test_fused_window_of_one_token_equals_fused_step(dev):
     assert_close(o2[:, 0], _np(o1), 1e-6, "o")
     assert_close(s2, _np(s1), 1e-6, "state")
     _assert_y(y2[:, 0], _np(y1), torch.bfloat16, "y")
+
+
+def test_short_conv_decode_mode(dev):
+    """Without cu_seqlens every token is its own sequence (a decode step): B tokens, each
+    convolved with its sequence's cache, and the cache shifted by one, in place."""
+    B, H, d = 6, 3, 128
+    li = workloads.layer_inputs(B, H, d, torch.bfloat16, nseq=B, device=dev, seed=13)
+    cache = li["conv_cache"].clone()
+    y, c = kda.kda_short_conv(li["x"], li["conv_w"], "decode", cache, l2norm=True, cache_out=cache)
+    torch.cuda.synchronize()
+    cu = np.arange(B + 1)
+    y_ref, c_ref = layer.short_conv(_np(li["x"]), _np(li["conv_w"]), cu, _np(li["conv_cache"]), l2norm=True,
+                                    eps=1e-6)
+    assert_rounded(y, y_ref, torch.bfloat16, "y")
+    assert np.array_equal(_np(cache), c_ref)
+
+
+def test_layer_pipeline_end_to_end(dev):
+    """ShortConv (q, k with L2, v) -> gate -> prefill -> epilogue through the library, against
+    the same pipeline in the oracles, fed with the library's own bf16 roundings of each
+    intermediate (the recurrence takes its inputs in bf16)."""
+    seqlens = [37, 20]
+    N, H, dk, dv = sum(seqlens), 2, 128, 128
+    cu = torch.tensor(workloads.cu_seqlens_of(seqlens), dtype=torch.int32, device=dev)
+    lq = workloads.layer_inputs(N, H, dk, torch.bfloat16, nseq=2, device=dev, seed=21)
+    lk = workloads.layer_inputs(N, H, dk, torch.bfloat16, nseq=2, device=dev, seed=22)
+    lv = workloads.layer_inputs(N, H, dv, torch.bfloat16, nseq=2, device=dev, seed=23)
+    beta = torch.sigmoid(torch.randn((N, H), generator=torch.Generator(device=dev).manual_seed(5),
+                                     device=dev)).to(torch.bfloat16)
+    q, _ = kda.kda_short_conv(lq["x"], lq["conv_w"], cu, l2norm=True)
+    k, _ = kda.kda_short_conv(lk["x"], lk["conv_w"], cu, l2norm=True)
+    v, _ = kda.kda_short_conv(lv["x"], lv["conv_w"], cu)
+    g = kda.kda_gate(lk["z"], lk["A_log"])
+    o, fin = kda.kda_prefill(q, k, v, g, beta, cu)
+    y = kda.kda_out_norm_gate(o, lv["u"], lv["norm_w"], 1e-6)
+    torch.cuda.synchronize()
+    # each stage against its oracle on the library's inputs to that stage
+    for name, got, ref in (
+            ("q", q, layer.short_conv(_np(lq["x"]), _np(lq["conv_w"]), _np(cu), l2norm=True)[0]),
+            ("k", k, layer.short_conv(_np(lk["x"]), _np(lk["conv_w"]), _np(cu), l2norm=True)[0]),
+            ("v", v, layer.short_conv(_np(lv["x"]), _np(lv["conv_w"]), _np(cu))[0])):
+        assert_rounded(got, ref, torch.bfloat16, name)
+    x = {"q": q, "k": k, "v": v, "log_alpha": g, "beta": beta, "cu_seqlens": cu}
+    o_ref, f_ref = oracle_prefill(x)
+    assert_close(o, o_ref, TOL[torch.bfloat16], "o")
+    assert_close(fin, f_ref, TOL[torch.bfloat16], "final_state")
+    _assert_y(y, layer.out_norm_gate(o_ref, _np(lv["u"]), _np(lv["norm_w"]), 1e-6), torch.bfloat16, "y")
