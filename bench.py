@@ -350,7 +350,9 @@ def bench_layer(torch, kda, workloads, dev):
     tokens x 96 heads, d = 128, bf16): the decay gate, the ShortConv prologue of q (with L2
     norm) and the epilogue, each one HBM pass (GB/s of algorithmic bytes against 8 TB/s).
     Decode side, on the decode workload (B=256 x H=96) and at B=4: one fused launch (gate +
-    step + epilogue) against the same three operations as separate launches."""
+    step + epilogue) against the same three operations as separate launches, and the whole
+    layer core per token (ShortConv of q, k, v + gate + step + epilogue) in one launch against
+    six."""
     N, H, d = 65536, 96, 128
     li = workloads.layer_inputs(N, H, d, torch.bfloat16, device=dev, seed=0)
     g = torch.empty_like(li["z"])
@@ -396,7 +398,33 @@ def bench_layer(torch, kda, workloads, dev):
         ms_f, ms_s = _event_ms(torch, fused, reps), _event_ms(torch, separate, reps)
         res[f"decode_b{B}"] = {"batch": B, "heads": Hd, "ms_fused": round(ms_f, 5), "ms_separate": round(ms_s, 5),
                                "speedup": ms_s / ms_f}
-        del x, lk, lv, state, o, yv, gz
+
+        # the whole layer core per token: ShortConv of q, k, v from their caches, gate, step,
+        # epilogue -- one launch against six
+        C = 2 * dk + dv
+        lx = workloads.layer_inputs(B, Hd, C, torch.bfloat16, nseq=B, device=dev, seed=5)
+        qkv, cw, cache = lx["x"], lx["conv_w"], lx["conv_cache"]
+        parts = [(0, dk, True), (dk, 2 * dk, True), (2 * dk, C, False)]
+        xs = [qkv[..., lo:hi].contiguous() for lo, hi, _ in parts]
+        ws = [cw[:, lo:hi].contiguous() for lo, hi, _ in parts]
+        cs = [cache[:, :, lo:hi].contiguous() for lo, hi, _ in parts]
+        ys = [torch.empty_like(xx) for xx in xs]
+
+        def layer_fused():
+            kda.kda_decode_layer_step(qkv, cw, cache, lk["z"], x["beta"], state, dk=dk, gate_A_log=lk["A_log"],
+                                      out_gate=lv["u"], norm_w=lv["norm_w"], output_o=False, y=yv)
+
+        def layer_separate():
+            for (lo, hi, l2), xx, ww, cc, yy in zip(parts, xs, ws, cs, ys):
+                kda.kda_short_conv(xx, ww, "decode", cc, l2norm=l2, cache_out=cc, y=yy)
+            kda.kda_gate(lk["z"], lk["A_log"], out=gz)
+            kda.kda_decode_step(ys[0], ys[1], ys[2], gz, x["beta"], state, o=o)
+            kda.kda_out_norm_gate(o, lv["u"], lv["norm_w"], 1e-6, y=yv)
+
+        ms_f, ms_s = _event_ms(torch, layer_fused, reps), _event_ms(torch, layer_separate, reps)
+        res[f"decode_layer_b{B}"] = {"batch": B, "heads": Hd, "ms_fused": round(ms_f, 5),
+                                     "ms_separate": round(ms_s, 5), "speedup": ms_s / ms_f}
+        del x, lk, lv, state, o, yv, gz, lx, xs, ws, cs, ys
 
     # windows of 4 drafts at B=256: the fused call (gate in the window kernel, epilogue as a
     # second launch over o) against gate + window + epilogue as three launches

@@ -30,6 +30,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE"
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
+           "kda_decode_layer_step",
            "kda_gate", "kda_short_conv", "kda_out_norm_gate",
            "kda_status_string", "kda_last_hip_error")
 
@@ -74,6 +75,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_window_fused.restype = ctypes.c_int
     lib.kda_decode_window_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
                                             i32, i32, ctypes.c_int, vp]
+    lib.kda_decode_layer_step.restype = ctypes.c_int
+    lib.kda_decode_layer_step.argtypes = [vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
+                                          i32, ctypes.c_int, vp]
     lib.kda_gate.restype = ctypes.c_int
     lib.kda_gate.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_short_conv.restype = ctypes.c_int
@@ -404,4 +408,36 @@ def kda_decode_window_fused(q, k, v, gate, beta, state, accept=None, *, gate_A_l
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_A_log), _ptr(beta), _ptr(state),
         _ptr(o), _ptr(accept), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
         B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
+    return (o if output_o else None), y
+
+
+def kda_decode_layer_step(qkv, conv_w, conv_cache, gate, beta, state, *, dk: int, l2_eps: float = 1e-6,
+                          gate_A_log=None, out_gate=None, norm_w=None, norm_eps: float = 1e-6, o=None,
+                          output_o: bool = True, y=None, stream=None):
+    """One decode step of the layer core in one launch: ShortConv + Swish (+ L2 for q, k) of the
+    new token from ``conv_cache`` (updated in place), the gate, the recurrence and the epilogue.
+
+    qkv [B, H, 2 dk + dv] (q | k | v channels per head); conv_w fp32 [H, 2 dk + dv, 4]; conv_cache
+    fp32 [B, H, 2 dk + dv, 3]; gate [B, H, dk] (decay logits with ``gate_A_log``, else log-decay);
+    beta [B, H]; state fp32 [B, H, dk, dv].  Returns (o or None, y or None)."""
+    if not isinstance(qkv, torch.Tensor) or qkv.device.type != "cuda":
+        raise ValueError("qkv must be a tensor on a GPU; the KDA library has no CPU path")
+    B, H, C = qkv.shape
+    dv = C - 2 * dk
+    dev = qkv.device
+    _check_dev("qkv", qkv, dev)
+    _check_dev("conv_w", conv_w, dev, torch.float32, (H, C, 4))
+    _check_dev("conv_cache", conv_cache, dev, torch.float32, (B, H, C, 3))
+    _check_dev("gate", gate, dev, qkv.dtype, (B, H, dk))
+    _check_dev("beta", beta, dev, qkv.dtype, (B, H))
+    _check_dev("state", state, dev, torch.float32, (B, H, dk, dv))
+    y = _fusion_args((B, H, dv), qkv.dtype, dev, H, dv, gate_A_log, out_gate, norm_w, y, True)
+    if not output_o and out_gate is None:
+        raise ValueError("output_o=False needs out_gate (nothing would be written)")
+    if output_o and o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    _check(load_library().kda_decode_layer_step(
+        _ptr(qkv), _ptr(conv_w), _ptr(conv_cache), float(l2_eps), _ptr(gate), _ptr(gate_A_log), _ptr(beta),
+        _ptr(state), _ptr(o if output_o else None), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
+        B, H, dk, dv, _dtype_code(qkv.dtype), _stream(stream)))
     return (o if output_o else None), y

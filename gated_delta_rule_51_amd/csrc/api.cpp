@@ -180,6 +180,29 @@ kda_status kda_decode_step_fused(const void *q, const void *k, const void *v, co
     return hip_status(kda::launch_decode(a));
 }
 
+kda_status kda_decode_layer_step(const void *qkv, const float *conv_w, float *conv_cache, float l2_eps,
+                                 const void *gate, const float *gate_A_log, const void *beta, float *state, float *o,
+                                 const void *out_gate, const float *norm_w, float norm_eps, void *y, int32_t B,
+                                 int32_t H, int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || (int64_t)B * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if (!(l2_eps >= 0.f && l2_eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    // qkv rows are read element-wise (q, k) and four at a time (v): 4-element aligned
+    kda_status st = check_inputs({qkv, gate}, true, beta, dt == KDA_BF16, true);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({state, conv_w}, {o});
+    if (st != KDA_OK) return st;
+    if (!conv_cache) return KDA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(conv_cache) & 3u) return KDA_ERR_ALIGN;
+    if (!o && !out_gate) return KDA_ERR_NULL;
+    st = check_fusion(gate_A_log, out_gate, norm_w, norm_eps, y, dt == KDA_BF16);
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs a{qkv, nullptr, nullptr, gate, beta, state, o, B, H, dk, dv, dt == KDA_BF16, stream,
+                      {gate_A_log, out_gate, norm_w, norm_eps, y, conv_w, conv_cache, l2_eps}};
+    return hip_status(kda::launch_decode(a));
+}
+
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
                            const void *beta, float *state, float *o, int32_t B, int32_t H,
                            int32_t dk, int32_t dv, kda_dtype dt, void *stream) {

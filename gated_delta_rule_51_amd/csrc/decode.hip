@@ -99,7 +99,7 @@ __device__ __forceinline__ void epilogue_store(const DecodeFusion &fx, int64_t r
         *reinterpret_cast<bf16x4 *>(y) = to_bf16x4(r);
 }
 
-template <int DK, int DV, typename T, bool FX>
+template <int DK, int DV, typename T, bool FX, bool CONV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
@@ -115,6 +115,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     __shared__ __attribute__((aligned(16))) float s_red[2][RP][Sh::STRIDE];
     __shared__ __attribute__((aligned(16))) float s_fin[2][DV];
     __shared__ float s_kq[2][NKW];
+    // prologue: squared norms of q and k per wave, the convolved v (double-buffered)
+    __shared__ float s_nq[CONV ? NKW : 1], s_nk[CONV ? NKW : 1];
+    __shared__ __attribute__((aligned(16))) float s_vv[CONV ? 2 : 1][CONV ? DV : 4];
+    constexpr int RS = 2 * DK + DV;  // pre-convolution row (q | k | v channels)
 
     // the RMSNorm weight of this lane's columns (epilogue lanes: rg == 0)
     f32x4 ep_w = zero4();
@@ -133,36 +137,92 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     // only after the next head's second barrier), s_kq is double-buffered.
     auto step = [&](f32x4 (&rows)[NR], f32x4 (&nxt)[NR], int64_t head, int par) {
         float kk = 0.f, qq = 0.f;
+        // prologue: y = Swish(w0 x_t + w1 x_{t-1} + w2 x_{t-2} + w3 x_{t-3}) per
+        // channel from the 3-input cache, which then shifts in x_t (each channel
+        // is read and written by one thread)
+        const T *xr = q + head * RS;
+        float *cc = CONV ? fx.conv_cache + head * RS * 3 : nullptr;
+        const float *wr = CONV ? fx.conv_w + (head % H) * RS * 4 : nullptr;
+        auto conv1 = [&](float x, int ch) -> float {
+            float *c = cc + ch * 3;
+            const float c0 = c[0], c1 = c[1], c2 = c[2];
+            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(wr + ch * 4);
+            const float a = w4[0] * x + w4[1] * c2 + w4[2] * c1 + w4[3] * c0;
+            c[0] = c1;
+            c[1] = c2;
+            c[2] = x;
+            return a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+        };
         if (tid < DK) {
-            kk = load_in(k + head * DK + tid);
-            qq = load_in(q + head * DK + tid);
+            if constexpr (CONV) {
+                qq = conv1(load_in(xr + tid), tid);
+                kk = conv1(load_in(xr + DK + tid), DK + tid);
+            } else {
+                kk = load_in(k + head * DK + tid);
+                qq = load_in(q + head * DK + tid);
+            }
             s_k[tid] = kk;
             s_q[tid] = qq;
             const float gz = load_in(g + head * DK + tid);
             s_a[tid] = decay_exp(FX && fx.A_log ? gate_from_logit(gz, __expf(fx.A_log[head % H])) : gz);
         }
-        if (tid < 64 * NKW) {  // whole waves: k.q by cross-lane sums
-            float kq = kk * qq;
+        if (tid < 64 * NKW) {  // whole waves: k.q (and the norms) by cross-lane sums
+            float kq = kk * qq, nq = qq * qq, nk = kk * kk;
 #pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
-            if ((tid & 63) == 0) s_kq[par][tid >> 6] = kq;
+            for (int m = 32; m >= 1; m >>= 1) {
+                kq += __shfl_xor(kq, m);
+                if (CONV) {
+                    nq += __shfl_xor(nq, m);
+                    nk += __shfl_xor(nk, m);
+                }
+            }
+            if ((tid & 63) == 0) {
+                s_kq[par][tid >> 6] = kq;
+                if (CONV) {
+                    s_nq[tid >> 6] = nq;
+                    s_nk[tid >> 6] = nk;
+                }
+            }
         }
-        const f32x4 vv = load_in4(v + head * DV + 4 * c4);
+        f32x4 vv;
+        if constexpr (CONV) {
+            // v's columns, each convolved once (row groups 0..3 take one column of
+            // every quad) and shared through LDS
+            if (rg < 4) {
+                const int col = 4 * c4 + rg;
+                s_vv[par][col] = conv1(load_in(xr + 2 * DK + col), 2 * DK + col);
+            }
+            vv = zero4();
+        } else {
+            vv = load_in4(v + head * DV + 4 * c4);
+        }
         const float b = load_in(beta + head);
         GateRaw<T> ep_u = {};
         if (FX && fx.u && rg == 0) ep_u = epilogue_gate<NC4, T>(fx, head, c4);
         if (head + stride < heads) load_rows(nxt, head + stride);
         __syncthreads();
 
+        // L2 normalisation of q and k (prologue): applied where they are read
+        float inv_q = 1.f, inv_k = 1.f;
+        if constexpr (CONV) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int w = 0; w < NKW; ++w) {
+                sq += s_nq[w];
+                sk += s_nk[w];
+            }
+            inv_q = __builtin_amdgcn_rsqf(sq + fx.l2eps);
+            inv_k = __builtin_amdgcn_rsqf(sk + fx.l2eps);
+        }
         f32x4 pv = zero4(), pq = zero4();
         float kr[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int row = rg + r * RP;
-            kr[r] = s_k[row];
-            rows[r] = rows[r] * s_a[row];  // forget
-            pv += kr[r] * rows[r];         // partial S'^T k
-            pq += s_q[row] * rows[r];      // partial S'^T q
+            kr[r] = CONV ? s_k[row] * inv_k : s_k[row];
+            rows[r] = rows[r] * s_a[row];                     // forget
+            pv += kr[r] * rows[r];                            // partial S'^T k
+            pq += (CONV ? s_q[row] * inv_q : s_q[row]) * rows[r];  // partial S'^T q
         }
         *reinterpret_cast<f32x4 *>(&s_red[0][rg][4 * c4]) = pv;
         *reinterpret_cast<f32x4 *>(&s_red[1][rg][4 * c4]) = pq;
@@ -185,6 +245,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
         float kq = 0.f;
 #pragma unroll
         for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
+        if constexpr (CONV) {
+            kq *= inv_k * inv_q;
+            vv = *reinterpret_cast<const f32x4 *>(&s_vv[par][4 * c4]);
+        }
         const f32x4 delta = b * (vv - vhat);
         if (rg == 0) {
             const f32x4 ov = rq + kq * delta;
@@ -408,9 +472,11 @@ static hipError_t launch_decode_t(const DecodeArgs &a) {
     const int64_t heads = (int64_t)a.B * a.H;
     const int64_t cap = GRID_THREADS / Sh::NT;
     const int64_t grid = heads < cap ? heads : cap;
-    const bool fused = a.fx.A_log || a.fx.u;
-    hipLaunchKernelGGL((fused ? decode_kernel<DK, DV, T, true> : decode_kernel<DK, DV, T, false>),
-                       dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
+    const bool conv = a.fx.conv_w != nullptr;
+    const bool fused = conv || a.fx.A_log || a.fx.u;
+    auto kern = conv ? decode_kernel<DK, DV, T, true, true>
+                     : (fused ? decode_kernel<DK, DV, T, true, false> : decode_kernel<DK, DV, T, false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.state, a.o, heads,
                        a.H, a.fx);
     return hipGetLastError();

@@ -25,6 +25,11 @@ struct DecodeFusion {
     const float *w;            // [dv] RMSNorm weight
     float eps;
     void *y;                   // shaped like o, input dtype
+    // ShortConv prologue (single-step kernel only): q points at the pre-convolution
+    // rows [B, H, 2 dk + dv] (q | k | v channels), k and v are unused
+    const float *conv_w;       // [H, 2 dk + dv, 4], tap j on x_{t-j}
+    float *conv_cache;         // [B, H, 2 dk + dv, 3], oldest first, updated in place
+    float l2eps;               // L2 normalisation of q and k
 };
 
 struct DecodeArgs {

@@ -209,6 +209,28 @@ kda_status kda_decode_window_fused(const void *q, const void *k, const void *v,
                                    int32_t B, int32_t T, int32_t H, int32_t dk,
                                    int32_t dv, kda_dtype dt, void *stream);
 
+/* One decode step of the whole layer core in one launch: the ShortConv
+ * prologue of the new token (the passes below: Swish of the 4-tap causal
+ * convolution, with each channel's 3 previous inputs taken from and shifted
+ * into conv_cache; q and k then L2-normalised with l2_eps), the gate (as in
+ * kda_decode_step_fused when gate_A_log != NULL), the recurrent step and, if
+ * out_gate != NULL, the epilogue.
+ *   qkv        : [B, H, 2 dk + dv] pre-convolution activations, per head the
+ *                q, k and v channels in that order (input dtype; 4-element
+ *                aligned);
+ *   conv_w     : fp32 [H, 2 dk + dv, 4] (tap j multiplies x_{t-j}), 16-byte
+ *                aligned;
+ *   conv_cache : fp32 [B, H, 2 dk + dv, 3] (oldest first), updated in place;
+ *   gate, beta, state, o, out_gate, norm_w, norm_eps, y as in
+ *   kda_decode_step_fused. */
+kda_status kda_decode_layer_step(const void *qkv, const float *conv_w,
+                                 float *conv_cache, float l2_eps,
+                                 const void *gate, const float *gate_A_log,
+                                 const void *beta, float *state, float *o,
+                                 const void *out_gate, const float *norm_w,
+                                 float norm_eps, void *y, int32_t B, int32_t H,
+                                 int32_t dk, int32_t dv, kda_dtype dt, void *stream);
+
 /* ------------------------------------------------------------------------
  * The layer's passes around the recurrence (same page: the bounded-decay
  * section for the gate; the paragraph after the update equation for the

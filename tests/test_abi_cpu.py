@@ -172,3 +172,17 @@ def test_fused_decode_rejects_bad_arguments(lib):
              None) == 1
     assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, 0.0, None, 1, 0, 1, 16, 16, 1,
              None) == 3
+
+
+def test_decode_layer_step_rejects_bad_arguments(lib):
+    f = lib.kda_decode_layer_step  # qkv w cache eps gate A beta state o u nw neps y B H dk dv dt stream
+    assert f(FAKE, None, FAKE, 1e-6, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 16, 1,
+             None) == 1
+    assert f(FAKE, FAKE, None, 1e-6, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 16, 1,
+             None) == 1
+    assert f(FAKE, FAKE + 4, FAKE, 1e-6, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 16, 1,
+             None) == 2
+    assert f(FAKE, FAKE, FAKE, -1.0, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 16, 1,
+             None) == 3
+    assert f(FAKE, FAKE, FAKE, 1e-6, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 48, 1,
+             None) == 4

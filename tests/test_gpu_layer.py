@@ -324,3 +324,34 @@ def test_layer_pipeline_end_to_end(dev):
     assert_close(o, o_ref, TOL[torch.bfloat16], "o")
     assert_close(fin, f_ref, TOL[torch.bfloat16], "final_state")
     _assert_y(y, layer.out_norm_gate(o_ref, _np(lv["u"]), _np(lv["norm_w"]), 1e-6), torch.bfloat16, "y")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 128), (torch.float32, 16, 64),
+                                         (torch.bfloat16, 64, 32)])
+def test_decode_layer_step_matches_oracle(dev, dtype, dk, dv):
+    """ShortConv (+ L2 for q, k) from the cache, gate, recurrence and epilogue in one launch,
+    against the oracles in sequence; the cache after the step is exact (it holds inputs)."""
+    B, H = 3, 4
+    C = 2 * dk + dv
+    lx = workloads.layer_inputs(B, H, C, dtype, nseq=B, device=dev, seed=dk + 3 * dv)
+    lk = workloads.layer_inputs(B, H, dk, dtype, device=dev, seed=dk + 1)
+    lv = workloads.layer_inputs(B, H, dv, dtype, device=dev, seed=dv + 2)
+    beta = workloads.decode_step_inputs(workloads.custom([1] * B, H, dk, dv, dtype), 0, device=dev, seed=4)["beta"]
+    state0 = workloads.random_state(B, H, dk, dv, device=dev, seed=dk)
+    st, cache = state0.clone(), lx["conv_cache"].clone()
+    say(f"  case: decode layer step B={B} H={H} dk={dk} dv={dv} {dtype}")
+    o, y = kda.kda_decode_layer_step(lx["x"], lx["conv_w"], cache, lk["z"], beta, st, dk=dk, l2_eps=1e-6,
+                                     gate_A_log=lk["A_log"], out_gate=lv["u"], norm_w=lv["norm_w"], norm_eps=1e-6)
+    torch.cuda.synchronize()
+    cu = np.arange(B + 1)
+    x, w, c0 = _np(lx["x"]), _np(lx["conv_w"]), _np(lx["conv_cache"])
+    parts = {}
+    for name, lo, hi, l2 in (("q", 0, dk, True), ("k", dk, 2 * dk, True), ("v", 2 * dk, C, False)):
+        parts[name] = layer.short_conv(x[..., lo:hi], w[:, lo:hi], cu, c0[:, :, lo:hi], l2norm=l2, eps=1e-6)
+    g = layer.gate(_np(lk["z"]), _np(lk["A_log"]))
+    o_ref, s_ref = oracle.decode(parts["q"][0], parts["k"][0], parts["v"][0], g, _np(beta), _np(state0))
+    assert_close(o, o_ref, TOL[dtype], "o")
+    assert_close(st, s_ref, TOL[dtype], "state")
+    _assert_y(y, layer.out_norm_gate(o_ref, _np(lv["u"]), _np(lv["norm_w"]), 1e-6), dtype, "y")
+    c_ref = np.concatenate([parts[n][1] for n in ("q", "k", "v")], axis=2)
+    assert np.array_equal(_np(cache), c_ref), "conv cache after the step"
