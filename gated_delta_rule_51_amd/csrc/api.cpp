@@ -248,7 +248,8 @@ kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int
                     void *log_alpha, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk)) return KDA_ERR_UNSUPPORTED;
-    if (H < 1 || N < 0 || N >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    // (token, head) rows are indexed in 32 bits
+    if (H < 1 || N < 0 || N >= (int64_t(1) << 31) || N * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     kda_status st = check_rows16({z, log_alpha}, N > 0);
     if (st != KDA_OK) return st;
     if (!A_log) return KDA_ERR_NULL;
@@ -261,7 +262,8 @@ kda_status kda_short_conv(const void *x, const float *w, const float *cache_in, 
                           int32_t l2norm, float eps, kda_dtype dt, void *y, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(d)) return KDA_ERR_UNSUPPORTED;
-    if (nseq < 1 || H < 1 || N < 0 || N >= (int64_t(1) << 31) || !(eps >= 0.f && eps <= 3.4e38f))
+    if (nseq < 1 || H < 1 || N < 0 || N >= (int64_t(1) << 31) || N * H >= (int64_t(1) << 31) ||
+        !(eps >= 0.f && eps <= 3.4e38f))
         return KDA_ERR_SHAPE;
     if ((int64_t)nseq * H * d >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     kda_status st = check_rows16({x, y}, N > 0);
@@ -283,7 +285,9 @@ kda_status kda_out_norm_gate(const float *o, const void *u, const float *w, floa
                              int32_t dv, kda_dtype dt, void *y, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
-    if (H < 1 || N < 0 || N >= (int64_t(1) << 31) || !(eps >= 0.f && eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    if (H < 1 || N < 0 || N >= (int64_t(1) << 31) || N * H >= (int64_t(1) << 31) ||
+        !(eps >= 0.f && eps <= 3.4e38f))
+        return KDA_ERR_SHAPE;
     kda_status st = check_rows16({u, y}, N > 0);
     if (st != KDA_OK) return st;
     st = check_ptrs({w}, {o});

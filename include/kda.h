@@ -240,6 +240,7 @@ kda_status kda_decode_layer_step(const void *qkv, const float *conv_w,
  * one streaming pass (HBM-bound), enqueued on `stream` like the calls above;
  * the projections that feed them (z, u, the pre-convolution q/k/v) and W_o are
  * the caller's.  dk, d, dv in {16, 32, 64, 128}; N in [0, 2^31); H >= 1;
+ * N * H < 2^31;
  * eps >= 0 and finite.  [.., d] tensors (input dtype, and o) are read and
  * written eight elements at a time and must be 16-byte aligned; fp32 weight
  * arrays 16 bytes, caches 4 bytes.

@@ -186,3 +186,10 @@ def test_decode_layer_step_rejects_bad_arguments(lib):
              None) == 3
     assert f(FAKE, FAKE, FAKE, 1e-6, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 48, 1,
              None) == 4
+
+
+def test_layer_passes_reject_too_many_rows(lib):
+    N, H = 1 << 26, 64  # N * H = 2^32 (token, head) rows
+    assert lib.kda_gate(FAKE, FAKE, N, H, 16, 1, FAKE, None) == 3
+    assert lib.kda_out_norm_gate(FAKE, FAKE, FAKE, 1e-6, N, H, 16, 1, FAKE, None) == 3
+    assert lib.kda_short_conv(FAKE, FAKE, None, None, FAKE, 1, N, H, 16, 0, 1e-6, 1, FAKE + 64, None) == 3
