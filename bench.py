@@ -373,6 +373,34 @@ def bench_layer(torch, kda, workloads, dev):
     del li, g, y, e
     torch.cuda.empty_cache()
 
+    # the whole prefill layer core on the same shape: ShortConv of q, k (with L2) and v, the
+    # gate, chunk-local + inter-chunk, the epilogue (eight launches)
+    w3 = workloads.workload(3)
+    x3 = workloads.prefill_inputs(w3, device=dev, seed=0)
+    lq = workloads.layer_inputs(N, H, d, torch.bfloat16, device=dev, seed=7)
+    cu = x3["cu_seqlens"]
+    ws = kda.alloc_workspace(N, 1, H, d, d, torch.bfloat16, dev)
+    bufs = {n: torch.empty_like(x3["q"]) for n in ("q", "k", "v", "g")}
+    o3 = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    fin3 = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+    y3 = torch.empty_like(x3["q"])
+    cache3 = torch.empty((1, H, d, 3), dtype=torch.float32, device=dev)
+
+    def layer_prefill():
+        kda.kda_short_conv(x3["q"], lq["conv_w"], cu, l2norm=True, cache_out=cache3, y=bufs["q"])
+        kda.kda_short_conv(x3["k"], lq["conv_w"], cu, l2norm=True, cache_out=cache3, y=bufs["k"])
+        kda.kda_short_conv(x3["v"], lq["conv_w"], cu, cache_out=cache3, y=bufs["v"])
+        kda.kda_gate(lq["z"], lq["A_log"], out=bufs["g"])
+        kda.kda_prefill(bufs["q"], bufs["k"], bufs["v"], bufs["g"], x3["beta"], cu, o=o3, final_state=fin3,
+                        workspace=ws)
+        kda.kda_out_norm_gate(o3, lq["u"], lq["norm_w"], 1e-6, y=y3)
+
+    ms = _event_ms(torch, layer_prefill, 5)
+    res["prefill_layer_k3"] = {"tokens": N, "heads": H, "ms": round(ms, 5), "tokens_per_s": N / (ms * 1e-3),
+                               "launches": 8}
+    del x3, lq, ws, bufs, o3, fin3, y3, cache3
+    torch.cuda.empty_cache()
+
     w4 = workloads.workload(4)
     step0 = workloads.decode_step_inputs(w4, 0, device=dev)
     for B in (w4.nseq, 4):
