@@ -72,6 +72,11 @@ class Oracle:
             _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _i64p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             _f64p, _f64p, ctypes.c_int]
+        lib.kda_oracle_backward_f64.restype = ctypes.c_int
+        lib.kda_oracle_backward_f64.argtypes = [
+            _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _i64p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p]
         lib.kda_oracle_decode_f64.restype = ctypes.c_int
         lib.kda_oracle_decode_f64.argtypes = [
             _f64p, _f64p, _f64p, _f64p, _f64p, _f64p,
@@ -137,6 +142,31 @@ class Oracle:
         return o, st
 
 
+    def backward(self, q, k, v, log_alpha, beta, dO, cu_seqlens=None, init_state=None, dfinal=None):
+        """Gradients of a loss L with dL/do = dO and dL/dfinal_state = dfinal (None = 0).
+
+        Returns a dict with dq, dk, dlog_alpha [N, H, dk], dv [N, H, dv], dbeta [N, H] and
+        dinit [nseq, H, dk, dv] (float64).  Single-threaded; meant for small cases.
+        """
+        q, k, v, g, b, do = (_as_f64(t) for t in (q, k, v, log_alpha, beta, dO))
+        N, H, dk = q.shape
+        dv = v.shape[2]
+        cu = np.array([0, N], dtype=np.int64) if cu_seqlens is None else \
+            np.ascontiguousarray(np.asarray(_as_f64(cu_seqlens), dtype=np.int64))
+        nseq = cu.shape[0] - 1
+        init = None if init_state is None else _as_f64(init_state)
+        dfin = None if dfinal is None else _as_f64(dfinal)
+        out = {"dq": np.zeros((N, H, dk)), "dk": np.zeros((N, H, dk)), "dv": np.zeros((N, H, dv)),
+               "dlog_alpha": np.zeros((N, H, dk)), "dbeta": np.zeros((N, H)), "dinit": np.zeros((nseq, H, dk, dv))}
+        rc = self._lib.kda_oracle_backward_f64(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(init), cu.ctypes.data_as(_i64p), nseq, H, dk, dv,
+            _ptr(do), _ptr(dfin), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+            _ptr(out["dbeta"]), _ptr(out["dinit"]))
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_backward_f64 failed with code {rc}")
+        return out
+
+
 _default: Optional[Oracle] = None
 
 
@@ -155,3 +185,8 @@ def prefill(*args, **kwargs):
 def decode(*args, **kwargs):
     """Module-level shortcut for ``Oracle().decode``."""
     return default().decode(*args, **kwargs)
+
+
+def backward(*args, **kwargs):
+    """Module-level shortcut for ``Oracle().backward``."""
+    return default().backward(*args, **kwargs)

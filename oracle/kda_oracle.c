@@ -203,3 +203,126 @@ int kda_oracle_decode_f64(const double *q, const double *k, const double *v,
     job.decode = 1;
     return run_job(&job, nthreads);
 }
+
+/* ----------------------------------------------------------------------
+ * Reverse mode of the recurrence (the gradients a training step needs),
+ * the chain rule taken through the four stages above in reverse order, one
+ * (sequence, head) at a time, single-threaded (test sizes).
+ *
+ * For a loss L with dL/do_t = dO_t and dL/dS_final = dfinal, the adjoint
+ * A = dL/dS is carried backwards from the last token:
+ *   read   o_t = S_t^T q_t          : A += q_t dO_t^T,   dq_t = S_t dO_t
+ *   write  S_t = E + beta k v^T     : dv_t = beta A^T k,  dbeta += (A^T k).v
+ *   erase  E = P - beta k (k^T P)   : with e = A^T k and u = P^T k,
+ *            dbeta -= e.u,  dk_t = beta A (v - u) - beta P e  (with the
+ *            write's term),  dP = A - beta k e^T
+ *   forget P = Diag(alpha) S_{t-1}  : dg_t[i] = sum_j dP[i][j] P[i][j]
+ *            (d alpha_i / d g_i = alpha_i), A <- Diag(alpha) dP
+ * and dinit = A after the first token.  The states S_{t-1} are recomputed by
+ * the forward recurrence and kept for the whole sequence.
+ *
+ * Layouts as the forward; dO [N, H, dv]; dfinal [nseq, H, dk, dv] or NULL
+ * (zero); outputs dq, dk, dg [N, H, dk], dv [N, H, dv], dbeta [N, H],
+ * dinit [nseq, H, dk, dv] or NULL.  Returns 0, or a negative number on bad
+ * arguments or allocation failure.
+ */
+int kda_oracle_backward_f64(const double *q, const double *k, const double *v,
+                            const double *g, const double *beta,
+                            const double *init_state, const int64_t *cu,
+                            int64_t nseq, int64_t H, int64_t dk, int64_t dv,
+                            const double *dO, const double *dfinal,
+                            double *dq, double *dkk, double *dvv, double *dg,
+                            double *dbeta, double *dinit) {
+    if (nseq < 1 || H < 1 || dk < 1 || dv < 1 || !cu || !dO) return -10;
+    if (cu[0] != 0) return -11;
+    int64_t Tmax = 0;
+    for (int64_t s = 0; s < nseq; ++s) {
+        if (cu[s + 1] < cu[s]) return -12;
+        if (cu[s + 1] - cu[s] > Tmax) Tmax = cu[s + 1] - cu[s];
+    }
+    const size_t blk = (size_t)(dk * dv);
+    double *st = (double *)malloc(sizeof(double) * blk * (size_t)(Tmax + 1));  /* S_0 .. S_T */
+    double *A = (double *)malloc(sizeof(double) * blk);
+    double *P = (double *)malloc(sizeof(double) * blk);
+    double *scr = (double *)malloc(sizeof(double) * (size_t)(dv > dk ? dv : dk) * 4);
+    if (!st || !A || !P || !scr) { free(st); free(A); free(P); free(scr); return -20; }
+    double *ob = scr, *e = scr + (dv > dk ? dv : dk), *u = e + (dv > dk ? dv : dk);
+    for (int64_t s = 0; s < nseq; ++s) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t T = cu[s + 1] - cu[s];
+            /* forward, keeping every state */
+            if (init_state) memcpy(st, init_state + (s * H + h) * dk * dv, sizeof(double) * blk);
+            else memset(st, 0, sizeof(double) * blk);
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t r = (cu[s] + t) * H + h;
+                memcpy(st + (size_t)(t + 1) * blk, st + (size_t)t * blk, sizeof(double) * blk);
+                kda_token_step(st + (size_t)(t + 1) * blk, dk, dv, q + r * dk, k + r * dk, v + r * dv,
+                               g + r * dk, beta[r], ob, u);
+            }
+            /* adjoint of the final state */
+            if (dfinal) memcpy(A, dfinal + (s * H + h) * dk * dv, sizeof(double) * blk);
+            else memset(A, 0, sizeof(double) * blk);
+            for (int64_t t = T - 1; t >= 0; --t) {
+                const int64_t r = (cu[s] + t) * H + h;
+                const double *qt = q + r * dk, *kt = k + r * dk, *vt = v + r * dv, *gt = g + r * dk;
+                const double *dot = dO + r * dv;
+                const double bt = beta[r];
+                const double *Sp = st + (size_t)t * blk;       /* S_{t-1} */
+                const double *Sn = st + (size_t)(t + 1) * blk; /* S_t */
+                /* read */
+                for (int64_t i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < dv; ++j) {
+                        A[i * dv + j] += qt[i] * dot[j];
+                        acc += Sn[i * dv + j] * dot[j];
+                    }
+                    dq[r * dk + i] = acc;
+                }
+                /* forget (forward): P = Diag(alpha) S_{t-1}; w = k^T P (the erase's row vector) */
+                for (int64_t i = 0; i < dk; ++i) {
+                    const double a = exp(gt[i]);
+                    for (int64_t j = 0; j < dv; ++j) P[i * dv + j] = a * Sp[i * dv + j];
+                }
+                for (int64_t j = 0; j < dv; ++j) {
+                    double w = 0.0, ee = 0.0;
+                    for (int64_t i = 0; i < dk; ++i) {
+                        w += kt[i] * P[i * dv + j];
+                        ee += kt[i] * A[i * dv + j];
+                    }
+                    u[j] = w;  /* k^T P */
+                    e[j] = ee; /* A^T k */
+                }
+                /* write: S_t = E + beta k v^T */
+                double db = 0.0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    dvv[r * dv + j] = bt * e[j];
+                    db += e[j] * vt[j];
+                }
+                /* erase: E = P - beta k (k^T P) = P - beta k u^T */
+                for (int64_t j = 0; j < dv; ++j) db -= e[j] * u[j];
+                dbeta[r] = db;
+                for (int64_t i = 0; i < dk; ++i) {
+                    /* d/dk of beta k v^T and of -beta k u^T with u = P^T k */
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < dv; ++j)
+                        acc += A[i * dv + j] * bt * (vt[j] - u[j]) - bt * P[i * dv + j] * e[j];
+                    dkk[r * dk + i] = acc;
+                }
+                /* dP = A - beta k e^T; then the forget stage */
+                for (int64_t i = 0; i < dk; ++i) {
+                    const double a = exp(gt[i]);
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < dv; ++j) {
+                        const double dp = A[i * dv + j] - bt * kt[i] * e[j];
+                        acc += dp * P[i * dv + j];
+                        A[i * dv + j] = a * dp;
+                    }
+                    dg[r * dk + i] = acc;
+                }
+            }
+            if (dinit) memcpy(dinit + (s * H + h) * dk * dv, A, sizeof(double) * blk);
+        }
+    }
+    free(st); free(A); free(P); free(scr);
+    return 0;
+}
