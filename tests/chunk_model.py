@@ -59,3 +59,59 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, init_state=None, chunk=C, keep=Fa
                     kept[(s, h, (c0 - cu[s]) // chunk)] = loc
             fin[s, h] = S
     return (o, fin, kept) if keep else (o, fin)
+
+
+def backward(q, k, v, g, beta, dO, cu_seqlens=None, init_state=None, dfinal=None, chunk=C):
+    """Gradients in chunk form (the algebra of the GPU backward), same outputs as the oracle's
+    reverse mode.  Per chunk with incoming state S0, its Delta, and the adjoint S^ of the
+    state after the chunk (dO of later chunks and dfinal included):
+
+        X  = A_qk^T dO + K~ S^            E = T^T X   (rows eps_r = S^_r^T k_r)
+        dV = diag(beta) E                  S^ <- Diag(e^{G_n}) S^ + Q+^T dO - K+^T dV
+        dQ = e^{G} (.) (dO S0^T + tril(dO Delta^T) K-)
+        a  = e^{-G} (.) (triu(Delta dO^T) Q+ - striu(Delta dV^T) K+ + e^{G_n} (.) (Delta S^^T))
+        b  = diag(beta) e^{G} (.) (E S0^T + stril(E Delta^T) K-)
+        dK = a - b,   U = K+ S0 + stril(K+ K-^T) Delta,   dbeta_r = eps_r . (v_r - u_r)
+        dg_t = rowsum(dfinal (.) S_T) + sum_{s >= t} (q_s (.) dq_s - k_s (.) (a_s + b_s))
+    """
+    q, k, v, g, beta, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta, dO))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.array([0, N]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    nseq = len(cu) - 1
+    out = {"dq": np.zeros((N, H, dk)), "dk": np.zeros((N, H, dk)), "dv": np.zeros((N, H, dv)),
+           "dlog_alpha": np.zeros((N, H, dk)), "dbeta": np.zeros((N, H)), "dinit": np.zeros((nseq, H, dk, dv))}
+    for s in range(nseq):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if init_state is None else np.array(init_state[s, h], dtype=np.float64)
+            saved = []
+            for c0 in range(cu[s], cu[s + 1], chunk):
+                c1 = min(cu[s + 1], c0 + chunk)
+                loc = chunk_local(q[c0:c1, h], k[c0:c1, h], g[c0:c1, h], beta[c0:c1, h])
+                D = loc["Tp"] @ (v[c0:c1, h] - loc["Kp"] @ S)
+                saved.append((c0, c1, loc, S.copy(), D))
+                S = np.exp(loc["G"][-1])[:, None] * S + loc["Kt"].T @ D
+            Sh = np.zeros((dk, dv)) if dfinal is None else np.array(dfinal[s, h], dtype=np.float64)
+            incr = np.zeros((cu[s + 1] - cu[s], dk))
+            boundary = np.sum(Sh * S, axis=1)
+            for c0, c1, loc, S0, D in reversed(saved):
+                b = beta[c0:c1, h]
+                Ob = dO[c0:c1, h]
+                eG, emG, eGn = np.exp(loc["G"]), np.exp(-loc["G"]), np.exp(loc["G"][-1])
+                X = loc["Aqk"].T @ Ob + loc["Kt"] @ Sh
+                E = loc["T"].T @ X
+                dV = b[:, None] * E
+                dQ = eG * (Ob @ S0.T + np.tril(Ob @ D.T) @ loc["Km"])
+                a = emG * (np.triu(D @ Ob.T) @ loc["Qp"] - np.triu(D @ dV.T, 1) @ loc["Kp"]
+                           + eGn[None, :] * (D @ Sh.T))
+                bb = b[:, None] * eG * (E @ S0.T + np.tril(E @ D.T, -1) @ loc["Km"])
+                U = loc["Kp"] @ S0 + np.tril(loc["Kp"] @ loc["Km"].T, -1) @ D
+                out["dq"][c0:c1, h] = dQ
+                out["dk"][c0:c1, h] = a - bb
+                out["dv"][c0:c1, h] = dV
+                out["dbeta"][c0:c1, h] = np.sum(E * (v[c0:c1, h] - U), axis=1)
+                incr[c0 - cu[s]:c1 - cu[s]] = q[c0:c1, h] * dQ - k[c0:c1, h] * (a + bb)
+                Sh = eGn[:, None] * Sh + loc["Qp"].T @ Ob - loc["Kp"].T @ dV
+            out["dinit"][s, h] = Sh
+            out["dlog_alpha"][cu[s]:cu[s + 1], h] = boundary[None, :] + np.cumsum(incr[::-1], axis=0)[::-1]
+    return out

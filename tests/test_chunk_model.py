@@ -60,3 +60,28 @@ def test_chunk_factors_stay_in_range_at_gate_floor():
     G = np.cumsum(np.full(16, -5.0))
     assert np.exp(-G).max() < np.finfo(np.float32).max
     assert np.exp(G).min() > np.finfo(np.float32).tiny
+
+
+@pytest.mark.parametrize("seqlens,init,dfin", [([40, 0, 17, 16, 1], True, True), ([33], False, False),
+                                               ([5, 48], True, False)])
+def test_chunked_backward_matches_oracle_reverse_mode(seqlens, init, dfin):
+    """The chunk-form gradients (the GPU backward's algebra) against the oracle's reverse mode."""
+    rng = np.random.default_rng(len(seqlens) + sum(seqlens))
+    N, H, dk, dv = sum(seqlens), 2, 16, 8
+    q = rng.standard_normal((N, H, dk))
+    k = rng.standard_normal((N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, H, dv))
+    g = rng.uniform(-5.0, 0.0, (N, H, dk))
+    b = rng.uniform(0.0, 1.0, (N, H))
+    dO = rng.standard_normal((N, H, dv))
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
+    S0 = rng.standard_normal((len(seqlens), H, dk, dv)) if init else None
+    dF = rng.standard_normal((len(seqlens), H, dk, dv)) if dfin else None
+    ref = oracle.backward(q, k, v, g, b, dO, cu_seqlens=cu, init_state=S0, dfinal=dF)
+    got = chunk_model.backward(q, k, v, g, b, dO, cu_seqlens=cu, init_state=S0, dfinal=dF)
+    for name in ref:
+        r = ref[name]
+        scale = max(1e-300, float(np.sqrt(np.mean(r * r)))) if r.size else 1.0
+        err = float(np.max(np.abs(got[name] - r))) if r.size else 0.0
+        assert err <= 1e-9 * max(scale, 1.0), f"{name}: max|err| = {err:.3e} (rms {scale:.3e})"
