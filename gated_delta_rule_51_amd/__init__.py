@@ -30,7 +30,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE"
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
-           "kda_decode_layer_step",
+           "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_gate", "kda_short_conv", "kda_out_norm_gate",
            "kda_status_string", "kda_last_hip_error")
 
@@ -78,6 +78,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_layer_step.restype = ctypes.c_int
     lib.kda_decode_layer_step.argtypes = [vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
                                           i32, ctypes.c_int, vp]
+    lib.kda_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_backward_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_prefill_backward.restype = ctypes.c_int
+    lib.kda_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_gate.restype = ctypes.c_int
     lib.kda_gate.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_short_conv.restype = ctypes.c_int
@@ -441,3 +446,34 @@ def kda_decode_layer_step(qkv, conv_w, conv_cache, gate, beta, state, *, dk: int
         _ptr(state), _ptr(o if output_o else None), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
         B, H, dk, dv, _dtype_code(qkv.dtype), _stream(stream)))
     return (o if output_o else None), y
+
+
+def kda_prefill_backward(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, init_state=None, d_final=None, *,
+                         need_d_init: bool = True, workspace=None, stream=None):
+    """Gradients of kda_prefill for a loss with dL/do = d_o (fp32 [N, H, dv]) and
+    dL/d(final state) = d_final (fp32 [nseq, H, dk, dv] or None).  Returns a dict of fp32 tensors:
+    dq, dk, dlog_alpha [N, H, dk], dv [N, H, dv], dbeta [N, H], dinit [nseq, H, dk, dv] (or None)."""
+    N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    dev = q.device
+    cu = _cu(cu_seqlens, N, dev)
+    nseq = cu.numel() - 1
+    _check_dev("d_o", d_o, dev, torch.float32, (N, H, dv))
+    if d_final is not None:
+        _check_dev("d_final", d_final, dev, torch.float32, (nseq, H, dk, dv))
+    if init_state is not None:
+        _check_dev("init_state", init_state, dev, torch.float32, (nseq, H, dk, dv))
+    lib = load_library()
+    if workspace is None:
+        nbytes = int(lib.kda_prefill_backward_workspace_bytes(N, nseq, H, dk, dv, _dtype_code(q.dtype)))
+        workspace = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((N, H, dk), **f32), "dk": torch.empty((N, H, dk), **f32),
+           "dv": torch.empty((N, H, dv), **f32), "dlog_alpha": torch.empty((N, H, dk), **f32),
+           "dbeta": torch.empty((N, H), **f32),
+           "dinit": torch.empty((nseq, H, dk, dv), **f32) if need_d_init else None}
+    _check(lib.kda_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N, H, dk, dv,
+        _dtype_code(q.dtype), _ptr(d_o), _ptr(d_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dinit"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

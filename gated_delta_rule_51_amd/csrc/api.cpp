@@ -244,6 +244,40 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v, const 
                                    nullptr, B, T, H, dk, dv, dt, stream);
 }
 
+size_t kda_prefill_backward_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
+                                            int32_t dv, kda_dtype dt) {
+    if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    return static_cast<size_t>(kda::backward_workspace_floats(total_tokens, nseq, H, dk, dv)) * sizeof(float);
+}
+
+kda_status kda_prefill_backward(const void *q, const void *k, const void *v, const void *log_alpha,
+                                const void *beta, const float *init_state, const int32_t *cu_seqlens, int32_t nseq,
+                                int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                const float *d_o, const float *d_final, float *d_q, float *d_k, float *d_v,
+                                float *d_log_alpha, float *d_beta, float *d_init, void *workspace, size_t ws_bytes,
+                                void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    const bool any = total_tokens > 0;
+    st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, any);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {init_state, d_final, d_init});
+    if (st != KDA_OK) return st;
+    for (const void *p : {static_cast<const void *>(d_o), static_cast<const void *>(d_q),
+                          static_cast<const void *>(d_k), static_cast<const void *>(d_v),
+                          static_cast<const void *>(d_log_alpha), static_cast<const void *>(d_beta)}) {
+        if (!p && any) return KDA_ERR_NULL;
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return KDA_ERR_ALIGN;
+    }
+    const size_t need = static_cast<size_t>(kda::backward_workspace_floats(total_tokens, nseq, H, dk, dv)) * 4;
+    if (!workspace || ws_bytes < need) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    kda::BackwardArgs a{q, k, v, log_alpha, beta, init_state, cu_seqlens, nseq, total_tokens, H, dk, dv,
+                        dt == KDA_BF16, d_o, d_final, d_q, d_k, d_v, d_log_alpha, d_beta, d_init,
+                        static_cast<float *>(workspace), stream};
+    return hip_status(kda::launch_backward(a));
+}
+
 kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int32_t dk, kda_dtype dt,
                     void *log_alpha, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;

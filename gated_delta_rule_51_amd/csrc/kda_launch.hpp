@@ -112,6 +112,25 @@ struct OutNormGateArgs {
     void *stream;
 };
 
+struct BackwardArgs {
+    const void *q, *k, *v, *g, *beta;  // forward inputs [N, H, .], input dtype
+    const float *init;                 // [nseq, H, dk, dv] or NULL
+    const int32_t *cu;
+    int32_t nseq;
+    int64_t N;
+    int32_t H, dk_, dv_;
+    bool bf16;
+    const float *dO;                   // [N, H, dv]
+    const float *dfinal;               // [nseq, H, dk, dv] or NULL
+    float *dq, *dk, *dv, *dg, *dbeta;  // [N, H, dk] x3 (dq, dk, dlog_alpha), [N, H, dv], [N, H]
+    float *dinit;                      // [nseq, H, dk, dv] or NULL
+    float *ws;                         // backward_workspace_floats(...) floats
+    void *stream;
+};
+
+hipError_t launch_backward(const BackwardArgs &a);
+int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv);
+
 hipError_t launch_gate(const GateArgs &a);
 hipError_t launch_short_conv(const ShortConvArgs &a);
 hipError_t launch_out_norm_gate(const OutNormGateArgs &a);

@@ -137,6 +137,37 @@ kda_status kda_inter_chunk(const void *q, const void *k, const void *v,
                            size_t workspace_bytes, float *o,
                            float *final_state, void *stream);
 
+/* Backward pass of kda_prefill (for training): the gradients of a loss L with
+ * dL/do = d_o and dL/d(final_state) = d_final (NULL = zero) with respect to q,
+ * k, v, log_alpha, beta and the initial state, for the same inputs as the
+ * forward call.  The recurrence (same page, update equation) is differentiated
+ * in chunk form: a forward sweep recomputes the state at every chunk start, a
+ * reverse sweep carries the state adjoint A (A <- Diag(e^{G_n}) A + Q+^T dO -
+ * K+^T dV per chunk), and a parallel pass forms dq, dk, dbeta per chunk; the
+ * log-decay gradient is the reverse cumulative sum over each sequence of
+ * q (.) dq - k (.) (the two parts of dk's sum), started from
+ * rowsum(d_final (.) final_state).  fp32 throughout.
+ *   d_o: fp32 [N, H, dv];  d_final, d_init: fp32 [nseq, H, dk, dv] or NULL;
+ *   d_q, d_k, d_log_alpha: fp32 [N, H, dk];  d_v: fp32 [N, H, dv];
+ *   d_beta: fp32 [N, H];  all written in full (d_init if not NULL).
+ *   workspace: kda_prefill_backward_workspace_bytes(...) bytes, 16-byte aligned
+ *   (per chunk slot and head: the state and its adjoint, dk x dv fp32 each,
+ *   plus two 16 x dv blocks; plus the final states). */
+size_t kda_prefill_backward_workspace_bytes(int64_t total_tokens, int32_t nseq,
+                                            int32_t H, int32_t dk, int32_t dv,
+                                            kda_dtype dt);
+
+kda_status kda_prefill_backward(const void *q, const void *k, const void *v,
+                                const void *log_alpha, const void *beta,
+                                const float *init_state,
+                                const int32_t *cu_seqlens, int32_t nseq,
+                                int64_t total_tokens, int32_t H, int32_t dk,
+                                int32_t dv, kda_dtype dt, const float *d_o,
+                                const float *d_final, float *d_q, float *d_k,
+                                float *d_v, float *d_log_alpha, float *d_beta,
+                                float *d_init, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* One recurrent decode step for B x H heads: the state is read once and
  * written once, in place.  (Per-token update equation; serving section:
  * decode is bound by the in-place state update.) */

@@ -193,3 +193,27 @@ def test_layer_passes_reject_too_many_rows(lib):
     assert lib.kda_gate(FAKE, FAKE, N, H, 16, 1, FAKE, None) == 3
     assert lib.kda_out_norm_gate(FAKE, FAKE, FAKE, 1e-6, N, H, 16, 1, FAKE, None) == 3
     assert lib.kda_short_conv(FAKE, FAKE, None, None, FAKE, 1, N, H, 16, 0, 1e-6, 1, FAKE + 64, None) == 3
+
+
+def test_backward_workspace_and_arguments(lib):
+    nb = lib.kda_prefill_backward_workspace_bytes(64, 2, 3, 16, 32, 1)
+    slots = 64 // 16 + 2
+    assert nb == 4 * (2 * slots * 3 * 16 * 32 + 2 * slots * 3 * 16 * 32 + 2 * 3 * 16 * 32)
+    assert lib.kda_prefill_backward_workspace_bytes(64, 0, 3, 16, 32, 1) == 0
+    f = lib.kda_prefill_backward
+    # q k v g b init cu nseq N H dk dv dt dO dF dq dk dv dg db dinit ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 64, 1, 16, 16, 1, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+            FAKE, None, FAKE, 1 << 30, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a13=None) == 1          # d_o missing
+    assert call(a18=None) == 1          # d_log_alpha missing
+    assert call(a15=FAKE + 2) == 2      # d_q misaligned
+    assert call(a21=None) == 5          # no workspace
+    assert call(a22=16) == 5            # workspace too small
+    assert call(a10=24) == 4            # dk
+    assert call(a7=0) == 3              # nseq

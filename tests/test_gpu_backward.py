@@ -1,0 +1,98 @@
+"""GPU parity of the prefill backward pass (kda_prefill_backward, through the C ABI) against
+the fp64 oracle's reverse mode.  The backward computes in fp32 for both input dtypes."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_51_amd as kda
+import oracle
+import workloads
+from parity import assert_close, say
+
+pytestmark = pytest.mark.gpu
+
+# fp32 arithmetic throughout (inputs of either dtype are exact in it): the fp32 bar, except for
+# the log-decay gradient, a reverse cumulative sum over the sequence of per-token increments
+# larger than their sum (they partly cancel), whose fp32 error grows with the length (measured
+# up to 3.1e-5 RMS at 2048 tokens): 1e-4.
+TOLS = {"dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "dlog_alpha": 1e-4, "dbeta": 1e-5, "dinit": 1e-5}
+NAMES = tuple(TOLS)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    kda.load_library()
+    return torch.device("cuda:0")
+
+
+def _case(dev, seqlens, H, dk, dv, dtype, seed, init=True, dfinal=True, gate="neg_softplus"):
+    w = workloads.custom(seqlens, H, dk, dv, dtype, gate)
+    x = workloads.prefill_inputs(w, device=dev, seed=seed)
+    N, nseq = w.total_tokens, len(seqlens)
+    gen = torch.Generator(device=dev).manual_seed(1000 + seed)
+    d_o = torch.randn((N, H, dv), generator=gen, device=dev)
+    S0 = workloads.random_state(nseq, H, dk, dv, device=dev, seed=seed) if init else None
+    dF = torch.randn((nseq, H, dk, dv), generator=gen, device=dev) if dfinal else None
+    return x, d_o, S0, dF
+
+
+def _check(dev, x, d_o, S0, dF, heads=None):
+    got = kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, x["cu_seqlens"], S0, dF)
+    torch.cuda.synchronize()
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, heads])
+    cpu = {n: sel(x[n]).cpu() for n in ("q", "k", "v", "log_alpha", "beta")}
+    ref = oracle.backward(cpu["q"], cpu["k"], cpu["v"], cpu["log_alpha"], cpu["beta"], sel(d_o).cpu(),
+                          cu_seqlens=x["cu_seqlens"].cpu(), init_state=None if S0 is None else sel(S0).cpu(),
+                          dfinal=None if dF is None else sel(dF).cpu())
+    for n in NAMES:
+        assert_close(sel(got[n]), ref[n], TOLS[n], n)
+    return got
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.float32, 16, 16), (torch.float32, 32, 64),
+                                         (torch.bfloat16, 128, 128), (torch.bfloat16, 64, 16)])
+def test_backward_matches_oracle(dev, dtype, dk, dv):
+    """Ragged and empty sequences, a one-token sequence, initial state and final-state gradient."""
+    seqlens = [40, 0, 17, 16, 1]
+    x, d_o, S0, dF = _case(dev, seqlens, 2, dk, dv, dtype, seed=dk + dv)
+    say(f"  case: backward seqlens={seqlens} H=2 dk={dk} dv={dv} {dtype}")
+    _check(dev, x, d_o, S0, dF)
+
+
+def test_backward_without_initial_state_or_final_gradient(dev):
+    x, d_o, _, _ = _case(dev, [33, 5], 3, 128, 64, torch.bfloat16, seed=3, init=False, dfinal=False)
+    say("  case: backward without init / d_final")
+    _check(dev, x, d_o, None, None)
+
+
+def test_backward_strong_decay(dev):
+    """log-decay uniform on [-5, 0): the chunk factors e^{+-G} span the full e^{80} range."""
+    x, d_o, S0, dF = _case(dev, [64, 29], 2, 64, 64, torch.float32, seed=4, gate="uniform")
+    say("  case: backward, strong decay")
+    _check(dev, x, d_o, S0, dF)
+
+
+def test_backward_no_tokens(dev):
+    """N = 0: the initial state's gradient is the final state's."""
+    H, dk, dv = 2, 32, 32
+    e = torch.empty((0, H, dk), dtype=torch.bfloat16, device=dev)
+    ev = torch.empty((0, H, dv), dtype=torch.bfloat16, device=dev)
+    eb = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    dF = torch.randn((2, H, dk, dv), device=dev)
+    got = kda.kda_prefill_backward(e, e, ev, e, eb, torch.empty((0, H, dv), device=dev), cu, None, dF)
+    torch.cuda.synchronize()
+    assert torch.equal(got["dinit"], dF)
+
+
+def test_backward_batched_workload_sampled_heads(dev):
+    """The batched workload's shape (B=4 x 2048 tokens, H=8, d=128, bf16): the whole backward
+    on the GPU, the oracle on 2 sampled heads of every sequence."""
+    w = workloads.workload(2)
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    d_o = torch.randn((w.total_tokens, w.H, w.dv), generator=gen, device=dev)
+    dF = torch.randn((w.nseq, w.H, w.dk, w.dv), generator=gen, device=dev)
+    say("  case: backward B=4 T=2048 H=8 d=128, heads [1, 6]")
+    _check(dev, x, d_o, None, dF, heads=[1, 6])
