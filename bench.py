@@ -14,10 +14,11 @@ The JSON line also carries, measured in the same run:
   * "layer": the passes around the recurrence (decay gate, ShortConv prologue, RMSNorm +
     output-gate epilogue) on the K3 layer shape, and the fused decode step against the
     same operations as separate launches,
+  * "backward": the prefill backward on the batched workload and the K3 layer,
   * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
 each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|layer|varlen|none]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|layer|backward|varlen|none]
 """
 from __future__ import annotations
 
@@ -484,12 +485,48 @@ def bench_layer(torch, kda, workloads, dev):
     return res
 
 
+def bench_backward(index, torch, kda, workloads, dev, reps: int):
+    """The prefill backward (kda_prefill_backward) on a prefill workload, with the forward time of
+    the same call for reference.  Per token-head the backward moves, at least, its inputs (q, k,
+    log_alpha, v, beta and dO) and gradients (fp32), and the per-chunk state and adjoint
+    checkpoints: written once and read once, 4 x dk x dv x 4 B per 16 tokens."""
+    w = workloads.workload(index)
+    log(f"[bench] generating workload {w.name} for the backward")
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    N, H, dk, dv = w.total_tokens, w.H, w.dk, w.dv
+    gen = torch.Generator(device=dev).manual_seed(1)
+    d_o = torch.randn((N, H, dv), generator=gen, device=dev)
+    d_f = torch.randn((w.nseq, H, dk, dv), generator=gen, device=dev)
+    nbytes = int(kda.load_library().kda_prefill_backward_workspace_bytes(N, w.nseq, H, dk, dv, 1))
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+
+    def bwd():
+        kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, x["cu_seqlens"], None, d_f,
+                                 workspace=ws)
+
+    def fwd():
+        kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+
+    ms_b = _event_ms(torch, bwd, reps)
+    ms_f = _event_ms(torch, fwd, reps)
+    per_th = 2 * (3 * dk + dv + 1) + 4 * dv + 4 * (3 * dk + dv + 1) + 4 * 4 * dk * dv / CHUNK
+    gbs = N * H * per_th / (ms_b * 1e-3) / 1e9
+    res = {"workload": w.name, "tokens": N, "heads": H, "ms_backward": round(ms_b, 4), "ms_forward": round(ms_f, 4),
+           "backward_over_forward": ms_b / ms_f, "tokens_per_s": N / (ms_b * 1e-3),
+           "algorithmic_bytes": N * H * per_th, "gbs": gbs, "hbm_peak_frac": gbs / HBM_PEAK_GBS,
+           "workspace_bytes": nbytes}
+    del x, d_o, d_f, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", choices=["all", "main", "k3", "decode", "layer", "varlen", "none"])
+    ap.add_argument("--only", default="all",
+                    choices=["all", "main", "k3", "decode", "layer", "backward", "varlen", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for scaling hardware byte counters)")
@@ -559,6 +596,10 @@ def main() -> int:
             out[f"decode_window_{T}"] = bench_decode_window(torch, kda, workloads, dev, steps, T)
         del steps
         torch.cuda.empty_cache()
+    if args.only in ("all", "backward"):
+        log("[bench] prefill backward: batched workload and the K3 layer")
+        out["backward"] = {"batched": bench_backward(2, torch, kda, workloads, dev, reps=5),
+                           "k3_layer": bench_backward(3, torch, kda, workloads, dev, reps=2)}
     if args.only in ("all", "layer"):
         log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
         out["layer"] = bench_layer(torch, kda, workloads, dev)

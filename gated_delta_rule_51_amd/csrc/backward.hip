@@ -51,61 +51,62 @@ template <int DK, typename T>
 __device__ void chunk_prep(ChunkOps<DK> &P, const T *q, const T *k, const T *g, const T *beta, int64_t t0,
                            int n, int32_t H, int h) {
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < 16 * DK; idx += BWD_THREADS) {
-        const int r = idx / DK, ch = idx % DK;
-        const int64_t e = ((t0 + r) * H + h) * DK + ch;
-        const bool in = r < n;
-        P.Q[r][ch] = in ? load_in(q + e) : 0.f;
-        P.K[r][ch] = in ? load_in(k + e) : 0.f;
-        P.G[r][ch] = in ? load_in(g + e) : 0.f;
-    }
     if (tid < 16) P.beta[tid] = tid < n ? load_in(beta + (t0 + tid) * H + h) : 0.f;
-    __syncthreads();
+    // One thread per key channel walks the chunk's rows: the cumulative log-decay in
+    // registers, one exp per element (e^{-G} and e^{G_n - G} from e^{G} and e^{G_n}).
     for (int ch = tid; ch < DK; ch += BWD_THREADS) {
-        float run = 0.f;
+        float G[16], qv[16], kv[16];
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
-            run += P.G[r][ch];
-            P.G[r][ch] = run;
+            const int64_t e = ((t0 + r) * H + h) * DK + ch;
+            const bool in = r < n;
+            G[r] = in ? load_in(g + e) : 0.f;
+            qv[r] = in ? load_in(q + e) : 0.f;
+            kv[r] = in ? load_in(k + e) : 0.f;
         }
-        P.gam[ch] = expf(run);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 16 * DK; idx += BWD_THREADS) {
-        const int r = idx / DK, ch = idx % DK;
-        const float G = P.G[r][ch], k_ = P.K[r][ch];
-        const float ep = expf(G), em = expf(-G);
-        P.Kp[r][ch] = k_ * ep;
-        P.Km[r][ch] = k_ * em;
-        P.Qp[r][ch] = P.Q[r][ch] * ep;
-        P.Kt[r][ch] = k_ * expf(P.G[15][ch] - G);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) G[r] += G[r - 1];
+        const float egn = expf(G[15]);
+        P.gam[ch] = egn;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float ep = expf(G[r]), em = 1.f / ep;
+            P.Q[r][ch] = qv[r];
+            P.K[r][ch] = kv[r];
+            P.G[r][ch] = G[r];
+            P.Kp[r][ch] = kv[r] * ep;
+            P.Km[r][ch] = kv[r] * em;
+            P.Qp[r][ch] = qv[r] * ep;
+            P.Kt[r][ch] = kv[r] * (egn * em);
+        }
     }
     __syncthreads();
     {
         const int r = tid / 16, i = tid % 16;  // 256 threads: one (r, i) entry each
         float kk = 0.f, qk = 0.f;
         for (int ch = 0; ch < DK; ++ch) {
-            kk += P.Kp[r][ch] * P.Km[i][ch];
-            qk += P.Qp[r][ch] * P.Km[i][ch];
+            const float km = P.Km[i][ch];
+            kk += P.Kp[r][ch] * km;
+            qk += P.Qp[r][ch] * km;
         }
         P.Ap[r][i] = i < r ? kk : 0.f;
         P.A[r][i] = i < r ? P.beta[r] * kk : 0.f;
         P.Aqk[r][i] = i <= r ? qk : 0.f;
     }
     __syncthreads();
-    if (tid < 16) {  // column j of the unit lower triangular inverse, by forward substitution
+    if (tid < 16) {
+        // column j of the unit lower triangular inverse by forward substitution, the
+        // column in registers (every index compile-time, so nothing goes to scratch)
         const int j = tid;
+        float t[16];
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float x;
-            if (i < j) {
-                x = 0.f;
-            } else if (i == j) {
-                x = 1.f;
-            } else {
-                x = 0.f;
-                for (int m = j; m < i; ++m) x -= P.A[i][m] * P.T[m][j];
-            }
-            P.T[i][j] = x;
-            P.Tp[i][j] = x * P.beta[j];
+            float x = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) x -= (m >= j ? P.A[i][m] : 0.f) * t[m];
+            t[i] = i < j ? 0.f : x;
+            P.T[i][j] = t[i];
+            P.Tp[i][j] = t[i] * P.beta[j];
         }
     }
     __syncthreads();
@@ -375,8 +376,22 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_dg_scan_kernel(const int32_t 
         const float *a = dfinal + i * DV, *b = sfin + i * DV;
         for (int j = 0; j < DV; ++j) run += a[j] * b[j];
     }
-    for (int64_t t = cu[s + 1] - 1; t >= cu[s]; --t) {
-        const int64_t e = (t * H + h) * DK + ch;
+    // sixteen tokens per trip, their loads issued before the sums, so they overlap
+    const int64_t bos = cu[s];
+    int64_t t = cu[s + 1] - 1;
+    const int64_t step = (int64_t)H * DK;
+    for (; t - 15 >= bos; t -= 16) {
+        float x[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) x[m] = dg[((t - m) * H + h) * DK + ch];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            run += x[m];
+            dg[((t - m) * H + h) * DK + ch] = run;
+        }
+    }
+    for (; t >= bos; --t) {
+        const int64_t e = t * step + (int64_t)h * DK + ch;
         run += dg[e];
         dg[e] = run;
     }
