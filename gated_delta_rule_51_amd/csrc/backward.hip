@@ -15,16 +15,16 @@
 // (the last because raising g_t[c] only rescales row c of S_{t-1}).  T = (I + A_kk)^-1
 // itself is needed (E), not only T' = T diag(beta).
 //
-// Four kernels, all fp32 on the vector ALUs with the chunk's operands in LDS:
-//   1. fwd_ckpt  per (sequence, head, 16-column slice): the forward chunk recurrence,
-//      writing S at every chunk start and every chunk's Delta (and the final state);
-//   2. adjoint   per (sequence, head, 16-column slice): the adjoint recurrence in
-//      reverse chunk order, writing dV, S^ after every chunk, E, and dinit;
+// Five kernels, all in fp32 (the products on the fp32 matrix cores where they are dense):
+//   0. mats      per (chunk, head): T', T^T, A_qk^T and stril(K+ K-^T);
+//   1. fwd sweep per (sequence, head, slices of 16 dv columns): the forward chunk
+//      recurrence, writing S at every chunk start, every chunk's Delta, the final state;
+//   2. adjoint   the same grid, chunks in reverse: dV, S^ after every chunk, E, dinit;
 //   3. grads     per (chunk, head), all dv columns in 16-column slices: dq, dk, dbeta
 //      and the log-decay increments;
 //   4. dg_scan   per (sequence, head, key channel): the reverse cumulative sum.
 // The column slices of 1 and 2 are independent (the state's columns evolve
-// separately), the chunks of 3 too, so only the recurrences in 1 and 2 are serial.
+// separately), the chunks of 0 and 3 too, so only the recurrences in 1 and 2 are serial.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -32,18 +32,17 @@ namespace kda {
 
 constexpr int BWD_THREADS = 256;
 
-// The state-independent quantities of one chunk (n <= 16 tokens; rows past n are
-// zero with g = 0, an exact no-op), in fp32.
+// The state-independent elementwise quantities of one chunk that the gradient kernel
+// reads (n <= 16 tokens; rows past n are zero with g = 0, an exact no-op), in fp32.
+// Rows are padded by one float, so reads of one channel across rows hit distinct banks.
 template <int DK>
 struct ChunkOps {
-    float Q[16][DK], K[16][DK];        // raw q, k
-    float G[16][DK];                   // cumulative log-decay
-    float Kp[16][DK], Km[16][DK];      // K e^{G}, K e^{-G}
-    float Qp[16][DK], Kt[16][DK];      // Q e^{G}, K e^{G_n - G}
-    float gam[DK];                     // e^{G_n}
-    float A[16][16], Ap[16][16];       // diag(beta) stril(K+ K-^T), stril(K+ K-^T)
-    float Aqk[16][16];                 // tril(Q+ K-^T)
-    float T[16][16], Tp[16][16];       // (I + A)^-1, T diag(beta)
+    float Q[16][DK + 1], K[16][DK + 1];    // raw q, k
+    float G[16][DK + 1];                   // cumulative log-decay
+    float Kp[16][DK + 1], Km[16][DK + 1];  // K e^{G}, K e^{-G}
+    float Qp[16][DK + 1];                  // Q e^{G}
+    float gam[DK];                         // e^{G_n}
+    float Ap[16][16];                      // stril(K+ K-^T)
     float beta[16];
 };
 
@@ -53,7 +52,7 @@ __device__ void chunk_prep(ChunkOps<DK> &P, const T *q, const T *k, const T *g, 
     const int tid = threadIdx.x;
     if (tid < 16) P.beta[tid] = tid < n ? load_in(beta + (t0 + tid) * H + h) : 0.f;
     // One thread per key channel walks the chunk's rows: the cumulative log-decay in
-    // registers, one exp per element (e^{-G} and e^{G_n - G} from e^{G} and e^{G_n}).
+    // registers, one exp per element (e^{-G} from e^{G}).
     for (int ch = tid; ch < DK; ch += BWD_THREADS) {
         float G[16], qv[16], kv[16];
 #pragma unroll
@@ -66,8 +65,7 @@ __device__ void chunk_prep(ChunkOps<DK> &P, const T *q, const T *k, const T *g, 
         }
 #pragma unroll
         for (int r = 1; r < 16; ++r) G[r] += G[r - 1];
-        const float egn = expf(G[15]);
-        P.gam[ch] = egn;
+        P.gam[ch] = expf(G[15]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float ep = expf(G[r]), em = 1.f / ep;
@@ -77,39 +75,8 @@ __device__ void chunk_prep(ChunkOps<DK> &P, const T *q, const T *k, const T *g, 
             P.Kp[r][ch] = kv[r] * ep;
             P.Km[r][ch] = kv[r] * em;
             P.Qp[r][ch] = qv[r] * ep;
-            P.Kt[r][ch] = kv[r] * (egn * em);
         }
     }
-    __syncthreads();
-    {
-        const int r = tid / 16, i = tid % 16;  // 256 threads: one (r, i) entry each
-        float kk = 0.f, qk = 0.f;
-        for (int ch = 0; ch < DK; ++ch) {
-            const float km = P.Km[i][ch];
-            kk += P.Kp[r][ch] * km;
-            qk += P.Qp[r][ch] * km;
-        }
-        P.Ap[r][i] = i < r ? kk : 0.f;
-        P.A[r][i] = i < r ? P.beta[r] * kk : 0.f;
-        P.Aqk[r][i] = i <= r ? qk : 0.f;
-    }
-    __syncthreads();
-    if (tid < 16) {
-        // column j of the unit lower triangular inverse by forward substitution, the
-        // column in registers (every index compile-time, so nothing goes to scratch)
-        const int j = tid;
-        float t[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float x = i == j ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) x -= (m >= j ? P.A[i][m] : 0.f) * t[m];
-            t[i] = i < j ? 0.f : x;
-            P.T[i][j] = t[i];
-            P.Tp[i][j] = t[i] * P.beta[j];
-        }
-    }
-    __syncthreads();
 }
 
 // Chunk c of sequence s occupies slot cu[s]/16 + s + c (the prefill workspace's map).
@@ -117,130 +84,444 @@ __device__ __forceinline__ int64_t slot_of(const int32_t *cu, int s, int c) {
     return (int64_t)cu[s] / 16 + s + c;
 }
 
-// ------------------------------------------------------------------ 1. forward checkpoints
-template <int DK, int DV, typename T>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_fwd_ckpt_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g,
-    const T *__restrict__ beta, const float *__restrict__ init, const int32_t *__restrict__ cu, int32_t H,
-    float *__restrict__ sck, float *__restrict__ dbuf, float *__restrict__ sfin) {
-    constexpr int NSL = DV / 16;
-    const int chain = blockIdx.x / NSL, col0 = (blockIdx.x % NSL) * 16;
-    const int s = chain / H, h = chain % H;
-    const int tid = threadIdx.x;
-    __shared__ ChunkOps<DK> P;
-    __shared__ float S[DK][16], Y[16][16], D[16][16];
-    const int64_t hd = (int64_t)s * H + h;
-    for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-        const int ch = idx / 16, col = idx % 16;
-        S[ch][col] = init ? init[(hd * DK + ch) * DV + col0 + col] : 0.f;
+// ------------------------------------------------------------------ row-layout chunk operands
+// Lane l = 16 g + m of a wave holds, of key-channel block b, token m and the four
+// channels 16b + 4g + j (j = 0..3): the A-operand layout of a product contracting
+// over the key channels (and, for the second factor of such a product, its B-operand
+// layout).  The cumulative log-decay of a channel over the chunk is then a prefix sum
+// across the 16 lanes of a DPP row, and its value at the last token sits in lane 15
+// of the row.
+
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {  // lane m reads lane m - N of its row, 0 before it
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ f32x4 row_prefix(f32x4 x) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[j] += row_shr<1>(x[j]);
+        x[j] += row_shr<2>(x[j]);
+        x[j] += row_shr<4>(x[j]);
+        x[j] += row_shr<8>(x[j]);
     }
-    const int64_t bos = cu[s], len = cu[s + 1] - bos;
-    const int nc = (int)((len + 15) / 16);
-    for (int c = 0; c < nc; ++c) {
-        __syncthreads();
-        const int64_t t0 = bos + 16 * c;
-        const int n = (int)(len - 16 * c < 16 ? len - 16 * c : 16);
-        chunk_prep<DK>(P, q, k, g, beta, t0, n, H, h);
-        const int64_t slot = slot_of(cu, s, c);
-        for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-            const int ch = idx / 16, col = idx % 16;
-            sck[((slot * H + h) * DK + ch) * DV + col0 + col] = S[ch][col];
-        }
-        {
-            const int r = tid / 16, col = tid % 16;
-            float ks = 0.f;
-            for (int ch = 0; ch < DK; ++ch) ks += P.Kp[r][ch] * S[ch][col];
-            const float vv = r < n ? load_in(v + ((t0 + r) * H + h) * DV + col0 + col) : 0.f;
-            Y[r][col] = vv - ks;
-        }
-        __syncthreads();
-        {
-            const int r = tid / 16, col = tid % 16;
-            float d = 0.f;
-            for (int m = 0; m < 16; ++m) d += P.Tp[r][m] * Y[m][col];
-            D[r][col] = d;
-            dbuf[((slot * H + h) * 16 + r) * DV + col0 + col] = d;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-            const int ch = idx / 16, col = idx % 16;
-            float x = P.gam[ch] * S[ch][col];
-            for (int r = 0; r < 16; ++r) x += P.Kt[r][ch] * D[r][col];
-            S[ch][col] = x;
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-        const int ch = idx / 16, col = idx % 16;
-        sfin[(hd * DK + ch) * DV + col0 + col] = S[ch][col];
+    return x;
+}
+
+// Inputs of one chunk are read through a buffer resource based at the chunk's first
+// token row of the head and as long as its n rows: reads of rows past n return zeros
+// without a branch (a guarded load would make the compiler wait for it at the join).
+template <typename T>
+__device__ __forceinline__ rsrc_t chunk_rsrc(const T *base, int64_t t0, int n, int32_t H, int h, int D) {
+    return make_rsrc(base + (t0 * H + h) * (int64_t)D, (uint32_t)n * (uint32_t)H * (uint32_t)D * sizeof(T));
+}
+
+// Four consecutive input elements at byte offset off.
+template <typename T>
+__device__ __forceinline__ f32x4 buf_in4(rsrc_t r, uint32_t off) {
+    if constexpr (sizeof(T) == 4) {
+        const u32x4 w = buf_load_u32x4(r, off);
+        return f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+    } else {
+        return unpack_bf16x4(buf_load_u32x2(r, off));
     }
 }
 
-// ------------------------------------------------------------------ 2. adjoint sweep
-template <int DK, int DV, typename T>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_adjoint_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ g, const T *__restrict__ beta,
-    const float *__restrict__ dO, const float *__restrict__ dfinal, const int32_t *__restrict__ cu, int32_t H,
-    float *__restrict__ hck, float *__restrict__ ebuf, float *__restrict__ dv, float *__restrict__ dinit) {
-    constexpr int NSL = DV / 16;
-    const int chain = blockIdx.x / NSL, col0 = (blockIdx.x % NSL) * 16;
-    const int s = chain / H, h = chain % H;
-    const int tid = threadIdx.x;
-    __shared__ ChunkOps<DK> P;
-    __shared__ float Sh[DK][16], Ob[16][16], X[16][16], dV[16][16];
-    const int64_t hd = (int64_t)s * H + h;
-    for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-        const int ch = idx / 16, col = idx % 16;
-        Sh[ch][col] = dfinal ? dfinal[(hd * DK + ch) * DV + col0 + col] : 0.f;
+template <typename T>
+__device__ __forceinline__ float buf_in(rsrc_t r, uint32_t off) {
+    if constexpr (sizeof(T) == 4) return __uint_as_float(buf_load_u32(r, off));
+    else return bf16_bits_to_f32(buf_load_u16(r, off));
+}
+
+// Four channels c0.. of token m of a chunk seen through chunk_rsrc (row layout).
+template <typename T>
+__device__ __forceinline__ f32x4 load_row4(rsrc_t r, int m, int32_t H, int D, int c0) {
+    return buf_in4<T>(r, ((uint32_t)m * (uint32_t)H * (uint32_t)D + (uint32_t)c0) * sizeof(T));
+}
+
+// Column col of the four tokens 4g + j (the accumulator layout), through chunk_rsrc.
+template <typename T>
+__device__ __forceinline__ f32x4 load_col4(rsrc_t r, int gq, int32_t H, int D, int col) {
+    f32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        x[j] = buf_in<T>(r, ((uint32_t)(4 * gq + j) * (uint32_t)H * (uint32_t)D + (uint32_t)col) * sizeof(T));
+    return x;
+}
+
+// Tokens in chunk c of a sequence of len tokens (0 outside it), wave-uniform.
+__device__ __forceinline__ int chunk_len(int64_t len, int c) {
+    const int64_t r = len - 16 * (int64_t)c;
+    return __builtin_amdgcn_readfirstlane(c < 0 || r <= 0 ? 0 : (r < 16 ? (int)r : 16));
+}
+
+// The decay-weighted operands of one block from its raw g, k (and q): e^{G}, e^{-G} and
+// e^{G_n - G} per element, G the inclusive cumulative log-decay.
+struct RowOps {
+    f32x4 kp, km, kt, qp, egn;  // K e^{G}, K e^{-G}, K e^{G_n - G}, Q e^{G}, e^{G_n}
+};
+
+__device__ __forceinline__ RowOps row_ops(f32x4 g, f32x4 k, f32x4 q, int lane) {
+    const f32x4 G = row_prefix(g);
+    RowOps o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float ep = expf(G[j]), em = __builtin_amdgcn_rcpf(ep);
+        const float en = __shfl(ep, lane | 15);
+        o.kp[j] = k[j] * ep;
+        o.km[j] = k[j] * em;
+        o.kt[j] = k[j] * (en * em);
+        o.qp[j] = q[j] * ep;
+        o.egn[j] = en;
     }
+    return o;
+}
+
+// The sequence owning chunk slot `slot`: the last s with cu[s]/16 + s <= slot.
+__device__ __forceinline__ int seq_of_slot(const int32_t *cu, int32_t nseq, int64_t slot) {
+    int s = 0, hi = nseq - 1;
+    while (s < hi) {
+        const int mid = (s + hi + 1) >> 1;
+        if (slot_of(cu, mid, 0) <= slot) s = mid;
+        else hi = mid - 1;
+    }
+    return s;
+}
+
+// ------------------------------------------------------------------ 0. chunk matrices
+// Per (chunk slot, head), four 16x16 fp32 matrices stored row-major, each the matrix
+// whose row m lane (g, m) reads as an MFMA A operand (columns 4g..4g+3):
+constexpr int MAT_TP = 0;    // T' = T diag(beta)            (Delta = T'(V - K+ S))
+constexpr int MAT_TT = 1;    // T^T                          (E = T^T X)
+constexpr int MAT_AQKT = 2;  // A_qk^T, A_qk = tril(Q+ K-^T)  (A_qk^T dO)
+constexpr int MAT_AP = 3;    // stril(K+ K-^T)                (U = K+ S0 + Ap Delta)
+constexpr int NMAT = 4;
+constexpr int MATS_WAVES = 4;
+
+__device__ __forceinline__ f32x4 plus_identity(f32x4 x, int g4, int l16, float s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (4 * g4 + j == l16 ? s : 0.f) + x[j];
+    return x;
+}
+
+// One wave per (slot, head).  K+ K-^T and Q+ K-^T on the fp32 matrix cores straight from
+// the row layout; A = diag(beta) stril(K+ K-^T) is nilpotent (A^16 = 0), so
+// T = (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8): eight 16x16 products.  A matrix
+// X held in the accumulator layout (lane (g, n): X[4g + j][n]) is the B operand of X and
+// the A operand of X^T, so each power is formed together with its transpose.
+template <int DK, typename T>
+__global__ __launch_bounds__(64 * MATS_WAVES) void bwd_mats_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ g, const T *__restrict__ beta,
+    const int32_t *__restrict__ cu, int32_t nseq, int32_t H, int64_t items, float *__restrict__ mats) {
+    constexpr int NB = DK / 16;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
+    __shared__ float tr[MATS_WAVES][16][20];
+    int64_t item = (int64_t)blockIdx.x * MATS_WAVES + wave;
+    const bool in_grid = item < items;
+    if (!in_grid) item = items - 1;  // every wave reaches the barrier below
+    const int64_t slot = item / H;
+    const int h = (int)(item % H);
+    const int s = seq_of_slot(cu, nseq, slot);
+    const int64_t bos = cu[s], len = cu[s + 1] - bos;
+    const int c = (int)(slot - slot_of(cu, s, 0));
+    const int n = chunk_len(len, c);
+    const int64_t t0 = bos + 16 * (int64_t)c;
+    const rsrc_t rq = chunk_rsrc(q, t0, n, H, h, DK), rk = chunk_rsrc(k, t0, n, H, h, DK);
+    const rsrc_t rg = chunk_rsrc(g, t0, n, H, h, DK), rb = chunk_rsrc(beta, t0, n, H, h, 1);
+
+    f32x4 akk = zero4(), aqk = zero4();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int c0 = 16 * b + 4 * gq;
+        const RowOps o = row_ops(load_row4<T>(rg, m, H, DK, c0), load_row4<T>(rk, m, H, DK, c0),
+                                 load_row4<T>(rq, m, H, DK, c0), lane);
+        akk = mma_f32_k16(o.kp, o.km, akk);
+        aqk = mma_f32_k16(o.qp, o.km, aqk);
+    }
+    const f32x4 br = load_col4<T>(rb, gq, H, 1, 0);                             // beta of rows 4g + j
+    const float bc = buf_in<T>(rb, (uint32_t)m * (uint32_t)H * sizeof(T));   // beta of column m
+    f32x4 ac;  // A = diag(beta) stril(K+ K-^T), accumulator layout
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ac[j] = m < 4 * gq + j ? br[j] * akk[j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tr[wave][4 * gq + j][m] = ac[j];
+    __syncthreads();
+    const f32x4 at = *reinterpret_cast<const f32x4 *>(&tr[wave][m][4 * gq]);  // A^T, accumulator layout
+    const f32x4 z = zero4();
+    const f32x4 a2 = mma_f32_k16(at, ac, z), a2t = mma_f32_k16(ac, at, z);
+    const f32x4 a4 = mma_f32_k16(a2t, a2, z), a4t = mma_f32_k16(a2, a2t, z);
+    const f32x4 a8 = mma_f32_k16(a4t, a4, z);
+    const f32x4 r1 = mma_f32_k16(plus_identity(a4t, gq, m, 1.f), plus_identity(a8, gq, m, 1.f), z);
+    const f32x4 r2 = mma_f32_k16(plus_identity(a2t, gq, m, 1.f), r1, z);
+    const f32x4 tc = mma_f32_k16(plus_identity(-at, gq, m, 1.f), r2, z);  // T, accumulator layout
+    if (!in_grid || n == 0) return;
+    float *out = mats + item * (NMAT * 256);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * gq + j;
+        out[MAT_TP * 256 + r * 16 + m] = tc[j] * bc;
+        out[MAT_AP * 256 + r * 16 + m] = m < r ? akk[j] : 0.f;
+    }
+    f32x4 qt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qt[j] = m <= 4 * gq + j ? aqk[j] : 0.f;
+    *reinterpret_cast<f32x4 *>(out + MAT_TT * 256 + m * 16 + 4 * gq) = tc;
+    *reinterpret_cast<f32x4 *>(out + MAT_AQKT * 256 + m * 16 + 4 * gq) = qt;
+}
+
+
+// ------------------------------------------------------------------ 1/2. the two sweeps
+// A workgroup serves one (sequence, head) and NS 16-column slices of dv, one wave each;
+// the wave keeps its dk x 16 slice of the state (or of the adjoint) in registers as NB
+// accumulator tiles (tile b, lane (g, n): row 16b + 4g + j, column n of the slice).
+// Per chunk the waves first build the next chunk's decay operands together (channel
+// block b by wave b mod NS) into the other half of a double-buffered LDS set, then
+// advance their slice with fp32 MFMAs reading this chunk's set; one barrier per chunk.
+// Raw inputs are loaded two chunks ahead, per-slice inputs one chunk ahead.
+template <int DK>
+struct SweepSet {
+    float rows[16][DK + 4];  // forward: K+ rows;  adjoint: K~ rows
+    float trA[DK][20];       // forward: K~^T;     adjoint: Q+^T
+    float trB[DK][20];       // adjoint: K+^T
+    float gam[DK];           // e^{G_n}
+};
+
+template <int DK, int NS, bool ADJ, typename T>
+struct SweepPrep {
+    // wave w builds channel blocks w, w + NS, ... (a block index past NB reads an empty
+    // resource and writes nothing); no branch around the loads, so the compiler waits
+    // for them only where build() uses them
+    static constexpr int NB = DK / 16, NBW = (NB + NS - 1) / NS;
+    f32x4 rg[NBW], rk[NBW], rq[NBW];
+
+    __device__ __forceinline__ void load(const T *q, const T *k, const T *g, int64_t t0, int n, int32_t H, int h,
+                                         int wave, int lane) {
+        const int m = lane % 16, gq = lane / 16;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int b = wave + NS * i;
+            const int nb = b < NB ? n : 0;
+            const int c0 = (b < NB ? 16 * b : 0) + 4 * gq;
+            rg[i] = load_row4<T>(chunk_rsrc(g, t0, nb, H, h, DK), m, H, DK, c0);
+            rk[i] = load_row4<T>(chunk_rsrc(k, t0, nb, H, h, DK), m, H, DK, c0);
+            if (ADJ) rq[i] = load_row4<T>(chunk_rsrc(q, t0, nb, H, h, DK), m, H, DK, c0);
+        }
+    }
+
+    __device__ __forceinline__ void build(SweepSet<DK> &P, int wave, int lane) const {
+        const int m = lane % 16, gq = lane / 16;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int b = wave + NS * i;
+            const RowOps o = row_ops(rg[i], rk[i], ADJ ? rq[i] : rk[i], lane);
+            if (NB % NS != 0 && b >= NB) continue;
+            const int c0 = 16 * b + 4 * gq;
+            *reinterpret_cast<f32x4 *>(&P.rows[m][c0]) = ADJ ? o.kt : o.kp;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                P.trA[c0 + j][m] = ADJ ? o.qp[j] : o.kt[j];
+                if (ADJ) P.trB[c0 + j][m] = o.kp[j];
+            }
+            if (m == 15) *reinterpret_cast<f32x4 *>(&P.gam[c0]) = o.egn;
+        }
+    }
+};
+
+// The 16x16 matrix `which` of chunk c as an A operand, through a resource that is empty
+// for chunks outside the sequence (so look-ahead reads there return zeros).
+__device__ __forceinline__ f32x4 load_mat(const float *mats, const int32_t *cu, int s, int c, int nc, int32_t H,
+                                          int h, int which, int lane) {
+    const bool in = c >= 0 && c < nc;
+    const int64_t slot = in ? slot_of(cu, s, c) : 0;
+    const rsrc_t r = make_rsrc(mats + ((slot * H + h) * NMAT + which) * 256, in ? 1024u : 0u);
+    const u32x4 w = buf_load_u32x4(r, ((uint32_t)(lane % 16) * 16u + 4u * (uint32_t)(lane / 16)) * 4u);
+    return f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+}
+
+// vmcnt(0) with expcnt and lgkmcnt left free: used once after the prologue's state loads,
+// so the loop that follows carries no pending load into its first iteration.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Producer waves per workgroup of the sweeps: every SIMD gets work (a lone slice wave
+// has three helpers), at most one producer per SIMD.
+template <int NS>
+struct SweepShape {
+    static constexpr int NP = NS == 1 ? 3 : (NS == 2 ? 2 : 4);
+    static constexpr int THREADS = 64 * (NS + NP);
+};
+
+template <int DK, int DV, int NS, typename T>
+__global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
+    const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g, const float *__restrict__ init,
+    const int32_t *__restrict__ cu, int32_t H, const float *__restrict__ mats, float *__restrict__ sck,
+    float *__restrict__ dbuf, float *__restrict__ sfin) {
+    constexpr int NB = DK / 16, NG = DV / 16 / NS, NP = SweepShape<NS>::NP;
+    const int chain = blockIdx.x / NG, sg = blockIdx.x % NG;
+    const int s = chain / H, h = chain % H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
+    __shared__ SweepSet<DK> L[2];
+    const int64_t hd = (int64_t)s * H + h;
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int nc = (int)((len + 15) / 16);
-    for (int c = nc - 1; c >= 0; --c) {
+
+    if (wave >= NS) {
+        // ---------------------------------------------------------------- producer
+        // Look-ahead past the last chunk reads empty resources and builds an unused set,
+        // so the loop body has no branch.
+        const int pw = wave - NS;
+        SweepPrep<DK, NP, false, T> pre;
+        auto load_raw = [&](int c) { pre.load(k, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane); };
+        load_raw(0);
+        pre.build(L[0], pw, lane);
+        load_raw(1);
         __syncthreads();
-        const int64_t t0 = bos + 16 * c;
-        const int n = (int)(len - 16 * c < 16 ? len - 16 * c : 16);
-        chunk_prep<DK>(P, q, k, g, beta, t0, n, H, h);
-        const int64_t slot = slot_of(cu, s, c);
-        for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-            const int ch = idx / 16, col = idx % 16;
-            hck[((slot * H + h) * DK + ch) * DV + col0 + col] = Sh[ch][col];
+        for (int c = 0; c < nc; ++c) {
+            pre.build(L[(c + 1) & 1], pw, lane);
+            load_raw(c + 2);
+            __syncthreads();
         }
-        {
-            const int r = tid / 16, col = tid % 16;
-            Ob[r][col] = r < n ? dO[((t0 + r) * H + h) * DV + col0 + col] : 0.f;
-        }
-        __syncthreads();
-        {
-            const int r = tid / 16, col = tid % 16;
-            float x = 0.f;
-            for (int i = 0; i < 16; ++i) x += P.Aqk[i][r] * Ob[i][col];
-            for (int ch = 0; ch < DK; ++ch) x += P.Kt[r][ch] * Sh[ch][col];
-            X[r][col] = x;
-        }
-        __syncthreads();
-        {
-            const int r = tid / 16, col = tid % 16;
-            float e = 0.f;
-            for (int i = 0; i < 16; ++i) e += P.T[i][r] * X[i][col];
-            ebuf[((slot * H + h) * 16 + r) * DV + col0 + col] = e;
-            const float d = P.beta[r] * e;
-            dV[r][col] = d;
-            if (r < n) dv[((t0 + r) * H + h) * DV + col0 + col] = d;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-            const int ch = idx / 16, col = idx % 16;
-            float x = P.gam[ch] * Sh[ch][col];
-            for (int r = 0; r < 16; ++r) x += P.Qp[r][ch] * Ob[r][col] - P.Kp[r][ch] * dV[r][col];
-            Sh[ch][col] = x;
-        }
+        return;
     }
+    // -------------------------------------------------------------------- slice wave
+    const int col0 = (sg * NS + wave) * 16;
+    f32x4 S[NB];
+    {  // (an empty resource without an initial state: its loads return 0)
+        const rsrc_t ri = make_rsrc(init ? init + hd * DK * DV : init, init ? DK * DV * 4u : 0u);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) S[b] = load_col4<float>(ri, 4 * b + gq, 1, DV, col0 + m);
+        wait_vm0();
+    }
+    f32x4 vn, tpn;  // the next chunk's v slice and T'
+    auto load_slice = [&](int c) {
+        vn = load_col4<T>(chunk_rsrc(v, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, DV), gq, H, DV, col0 + m);
+        tpn = load_mat(mats, cu, s, c, nc, H, h, MAT_TP, lane);
+    };
+    load_slice(0);
     __syncthreads();
-    if (dinit)
-        for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-            const int ch = idx / 16, col = idx % 16;
-            dinit[(hd * DK + ch) * DV + col0 + col] = Sh[ch][col];
+    for (int c = 0; c < nc; ++c) {
+        const SweepSet<DK> &P = L[c & 1];
+        const f32x4 vc = vn, tp = tpn;
+        load_slice(c + 1);
+        const int64_t slot = slot_of(cu, s, c);
+        float *ck = sck + (slot * H + h) * (int64_t)DK * DV + col0 + m;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ck[(16 * b + 4 * gq + j) * DV] = S[b][j];
+        f32x4 x = zero4();  // K+ S
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), S[b], x);
+        const f32x4 d = mma_f32_k16(tp, vc - x, zero4());  // Delta = T'(V - K+ S)
+        float *db = dbuf + (slot * H + h) * 16 * (int64_t)DV + col0 + m;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) db[(4 * gq + j) * DV] = d[j];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
+            S[b] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]), d, S[b] * gm);
         }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sfin[(hd * DK + 16 * b + 4 * gq + j) * DV + col0 + m] = S[b][j];
+}
+
+template <int DK, int DV, int NS, typename T>
+__global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ g, const T *__restrict__ beta,
+    const float *__restrict__ dO, const float *__restrict__ dfinal, const int32_t *__restrict__ cu, int32_t H,
+    const float *__restrict__ mats, float *__restrict__ hck, float *__restrict__ ebuf, float *__restrict__ dv,
+    float *__restrict__ dinit) {
+    constexpr int NB = DK / 16, NG = DV / 16 / NS, NP = SweepShape<NS>::NP;
+    const int chain = blockIdx.x / NG, sg = blockIdx.x % NG;
+    const int s = chain / H, h = chain % H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
+    __shared__ SweepSet<DK> L[2];
+    const int64_t hd = (int64_t)s * H + h;
+    const int64_t bos = cu[s], len = cu[s + 1] - bos;
+    const int nc = (int)((len + 15) / 16);
+
+    if (wave >= NS) {
+        // ---------------------------------------------------------------- producer
+        const int pw = wave - NS;
+        SweepPrep<DK, NP, true, T> pre;
+        auto load_raw = [&](int c) { pre.load(q, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane); };
+        load_raw(nc - 1);
+        pre.build(L[(nc - 1) & 1], pw, lane);
+        load_raw(nc - 2);
+        __syncthreads();
+        for (int c = nc - 1; c >= 0; --c) {
+            pre.build(L[(c - 1) & 1], pw, lane);
+            load_raw(c - 2);
+            __syncthreads();
+        }
+        return;
+    }
+    // -------------------------------------------------------------------- slice wave
+    const int col0 = (sg * NS + wave) * 16;
+    f32x4 Sh[NB];
+    {
+        const rsrc_t rf = make_rsrc(dfinal ? dfinal + hd * DK * DV : dfinal, dfinal ? DK * DV * 4u : 0u);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Sh[b] = load_col4<float>(rf, 4 * b + gq, 1, DV, col0 + m);
+        wait_vm0();
+    }
+    f32x4 on, bn, aqn, ttn;  // the next chunk's dO slice, beta, A_qk^T, T^T
+    auto load_slice = [&](int c) {
+        const int64_t t0 = bos + 16 * (int64_t)c;
+        const int n = chunk_len(len, c);
+        on = load_col4<float>(chunk_rsrc(dO, t0, n, H, h, DV), gq, H, DV, col0 + m);
+        bn = load_col4<T>(chunk_rsrc(beta, t0, n, H, h, 1), gq, H, 1, 0);
+        aqn = load_mat(mats, cu, s, c, nc, H, h, MAT_AQKT, lane);
+        ttn = load_mat(mats, cu, s, c, nc, H, h, MAT_TT, lane);
+    };
+    load_slice(nc - 1);
+    __syncthreads();
+    for (int c = nc - 1; c >= 0; --c) {
+        const SweepSet<DK> &P = L[c & 1];
+        const f32x4 ob = on, bt = bn, aq = aqn, tt = ttn;
+        load_slice(c - 1);
+        const int64_t slot = slot_of(cu, s, c);
+        const int64_t t0 = bos + 16 * (int64_t)c;
+        const int n = chunk_len(len, c);
+        float *hk = hck + (slot * H + h) * (int64_t)DK * DV + col0 + m;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hk[(16 * b + 4 * gq + j) * DV] = Sh[b][j];
+        f32x4 x = mma_f32_k16(aq, ob, zero4());  // A_qk^T dO + K~ S^
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), Sh[b], x);
+        const f32x4 e = mma_f32_k16(tt, x, zero4());  // E = T^T X
+        const f32x4 dvv = bt * e;
+        float *eb = ebuf + (slot * H + h) * 16 * (int64_t)DV + col0 + m;
+        const rsrc_t rdv = chunk_rsrc(dv, t0, n, H, h, DV);  // rows past n are dropped
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            eb[(4 * gq + j) * DV] = e[j];
+            buf_store_f32(dvv[j], rdv, ((uint32_t)(4 * gq + j) * (uint32_t)H * DV + col0 + m) * 4u);
+        }
+        const f32x4 nd = -dvv;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
+            f32x4 acc = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]), ob, Sh[b] * gm);
+            Sh[b] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trB[16 * b + m][4 * gq]), nd, acc);
+        }
+        __syncthreads();
+    }
+    if (dinit)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dinit[(hd * DK + 16 * b + 4 * gq + j) * DV + col0 + m] = Sh[b][j];
 }
 
 // ------------------------------------------------------------------ 3. per-chunk gradients
@@ -249,20 +530,14 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_grads_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g,
     const T *__restrict__ beta, const float *__restrict__ dO, const int32_t *__restrict__ cu, int32_t nseq,
     int32_t H, const float *__restrict__ sck, const float *__restrict__ hck, const float *__restrict__ dbuf,
-    const float *__restrict__ ebuf, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ incr,
+    const float *__restrict__ ebuf, const float *__restrict__ mats, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ incr,
     float *__restrict__ dbeta) {
     constexpr int NOUT = 16 * DK / BWD_THREADS > 0 ? 16 * DK / BWD_THREADS : 1;  // (r, ch) outputs per thread
     static_assert(16 * DK % BWD_THREADS == 0 || DK == 16, "outputs spread evenly");
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
     const int tid = threadIdx.x;
-    // the sequence owning this slot: the last s with cu[s]/16 + s <= slot
-    int s = 0, hi = nseq - 1;
-    while (s < hi) {
-        const int mid = (s + hi + 1) >> 1;
-        if (slot_of(cu, mid, 0) <= slot) s = mid;
-        else hi = mid - 1;
-    }
+    const int s = seq_of_slot(cu, nseq, slot);
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int c = (int)(slot - slot_of(cu, s, 0));
     if (16 * (int64_t)c >= len) return;  // a slot no chunk uses (the block is uniform)
@@ -275,6 +550,8 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_grads_kernel(
     __shared__ float M[4][16][16];
     __shared__ float dbp[16][16];
     chunk_prep<DK>(P, q, k, g, beta, t0, n, H, h);
+    P.Ap[tid / 16][tid % 16] = mats[((slot * H + h) * NMAT + MAT_AP) * 256 + tid];
+    __syncthreads();
 
     float QS[NOUT], DS[NOUT], ES[NOUT];
 #pragma unroll
@@ -399,6 +676,31 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_dg_scan_kernel(const int32_t 
 
 // ------------------------------------------------------------------ launch
 
+// Column slices per workgroup of the sweeps: as few as fill the chip (each slice gets a
+// SIMD to itself while there are fewer than about 256 workgroups), so the chunk's
+// operands are built by several waves only where the grid is large anyway.
+static int sweep_slices(int64_t chains, int nsl) {
+    int ns = 1;
+    while (ns < nsl && chains * (nsl / ns) > 256) ns *= 2;
+    return ns;
+}
+
+template <int DK, int DV, int NS, typename T>
+static hipError_t launch_sweeps(const BackwardArgs &a, const float *mats, float *sck, float *hck, float *dbuf,
+                                float *ebuf, float *sfin) {
+    const hipStream_t st = (hipStream_t)a.stream;
+    const unsigned grid = (unsigned)((int64_t)a.nseq * a.H * (DV / 16 / NS));
+    const dim3 block(SweepShape<NS>::THREADS);
+    hipLaunchKernelGGL((bwd_fwd_sweep_kernel<DK, DV, NS, T>), dim3(grid), block, 0, st, (const T *)a.k,
+                       (const T *)a.v, (const T *)a.g, a.init, a.cu, a.H, mats, sck, dbuf, sfin);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_adjoint_sweep_kernel<DK, DV, NS, T>), dim3(grid), block, 0, st, (const T *)a.q,
+                       (const T *)a.k, (const T *)a.g, (const T *)a.beta, a.dO, a.dfinal, a.cu, a.H, mats, hck, ebuf,
+                       a.dv, a.dinit);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, typename T>
 static hipError_t launch_bwd_t(const BackwardArgs &a) {
     const int64_t slots = chunk_slots(a.N, a.nseq);
@@ -406,24 +708,31 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     float *sck = a.ws, *hck = sck + blk;
     float *dbuf = hck + blk, *ebuf = dbuf + slots * a.H * 16 * (int64_t)DV;
     float *sfin = ebuf + slots * a.H * 16 * (int64_t)DV;
+    float *mats = sfin + (int64_t)a.nseq * a.H * DK * DV;
     const hipStream_t st = (hipStream_t)a.stream;
-    const unsigned chains = (unsigned)((int64_t)a.nseq * a.H * (DV / 16));
-    hipLaunchKernelGGL((bwd_fwd_ckpt_kernel<DK, DV, T>), dim3(chains), dim3(BWD_THREADS), 0, st,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta,
-                       a.init, a.cu, a.H, sck, dbuf, sfin);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_adjoint_kernel<DK, DV, T>), dim3(chains), dim3(BWD_THREADS), 0, st,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.g, (const T *)a.beta, a.dO, a.dfinal, a.cu,
-                       a.H, hck, ebuf, a.dv, a.dinit);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    const int64_t items = slots * a.H;
     if (a.N > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)(slots * a.H)), dim3(BWD_THREADS), 0, st,
-                           (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.dO,
-                           a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, a.dq, a.dk, a.dg, a.dbeta);
+        hipLaunchKernelGGL((bwd_mats_kernel<DK, T>), dim3((unsigned)((items + MATS_WAVES - 1) / MATS_WAVES)),
+                           dim3(64 * MATS_WAVES), 0, st, (const T *)a.q, (const T *)a.k, (const T *)a.g,
+                           (const T *)a.beta, a.cu, a.nseq, a.H, items, mats);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t items = (int64_t)a.nseq * a.H * DK;
-        hipLaunchKernelGGL((bwd_dg_scan_kernel<DV>), dim3((unsigned)((items + BWD_THREADS - 1) / BWD_THREADS)),
+    }
+    constexpr int NSL = DV / 16;
+    switch (sweep_slices((int64_t)a.nseq * a.H, NSL)) {
+    case 1: e = launch_sweeps<DK, DV, 1, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
+    case 2: if constexpr (NSL >= 2) e = launch_sweeps<DK, DV, 2, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
+    case 4: if constexpr (NSL >= 4) e = launch_sweeps<DK, DV, 4, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
+    default: if constexpr (NSL >= 8) e = launch_sweeps<DK, DV, 8, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
+    }
+    if (e != hipSuccess) return e;
+    if (a.N > 0) {
+        hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(BWD_THREADS), 0, st,
+                           (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.dO,
+                           a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, mats, a.dq, a.dk, a.dg, a.dbeta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t nitems = (int64_t)a.nseq * a.H * DK;
+        hipLaunchKernelGGL((bwd_dg_scan_kernel<DV>), dim3((unsigned)((nitems + BWD_THREADS - 1) / BWD_THREADS)),
                            dim3(BWD_THREADS), 0, st, a.cu, a.nseq, a.H, DK, a.dfinal, sfin, a.dg);
         e = hipGetLastError();
     }
@@ -447,7 +756,8 @@ hipError_t launch_backward(const BackwardArgs &a) {
 
 int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv) {
     const int64_t slots = chunk_slots(N, nseq);
-    return 2 * slots * H * (int64_t)dk * dv + 2 * slots * H * 16 * (int64_t)dv + (int64_t)nseq * H * dk * dv;
+    return 2 * slots * H * (int64_t)dk * dv + 2 * slots * H * 16 * (int64_t)dv + (int64_t)nseq * H * dk * dv +
+           slots * H * 4 * 256;  // S and S^ checkpoints, Delta and E, the final state, chunk matrices
 }
 
 }  // namespace kda
