@@ -32,53 +32,6 @@ namespace kda {
 
 constexpr int BWD_THREADS = 256;
 
-// The state-independent elementwise quantities of one chunk that the gradient kernel
-// reads (n <= 16 tokens; rows past n are zero with g = 0, an exact no-op), in fp32.
-// Rows are padded by one float, so reads of one channel across rows hit distinct banks.
-template <int DK>
-struct ChunkOps {
-    float Q[16][DK + 1], K[16][DK + 1];    // raw q, k
-    float G[16][DK + 1];                   // cumulative log-decay
-    float Kp[16][DK + 1], Km[16][DK + 1];  // K e^{G}, K e^{-G}
-    float Qp[16][DK + 1];                  // Q e^{G}
-    float gam[DK];                         // e^{G_n}
-    float Ap[16][16];                      // stril(K+ K-^T)
-    float beta[16];
-};
-
-template <int DK, typename T>
-__device__ void chunk_prep(ChunkOps<DK> &P, const T *q, const T *k, const T *g, const T *beta, int64_t t0,
-                           int n, int32_t H, int h) {
-    const int tid = threadIdx.x;
-    if (tid < 16) P.beta[tid] = tid < n ? load_in(beta + (t0 + tid) * H + h) : 0.f;
-    // One thread per key channel walks the chunk's rows: the cumulative log-decay in
-    // registers, one exp per element (e^{-G} from e^{G}).
-    for (int ch = tid; ch < DK; ch += BWD_THREADS) {
-        float G[16], qv[16], kv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t e = ((t0 + r) * H + h) * DK + ch;
-            const bool in = r < n;
-            G[r] = in ? load_in(g + e) : 0.f;
-            qv[r] = in ? load_in(q + e) : 0.f;
-            kv[r] = in ? load_in(k + e) : 0.f;
-        }
-#pragma unroll
-        for (int r = 1; r < 16; ++r) G[r] += G[r - 1];
-        P.gam[ch] = expf(G[15]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float ep = expf(G[r]), em = 1.f / ep;
-            P.Q[r][ch] = qv[r];
-            P.K[r][ch] = kv[r];
-            P.G[r][ch] = G[r];
-            P.Kp[r][ch] = kv[r] * ep;
-            P.Km[r][ch] = kv[r] * em;
-            P.Qp[r][ch] = qv[r] * ep;
-        }
-    }
-}
-
 // Chunk c of sequence s occupies slot cu[s]/16 + s + c (the prefill workspace's map).
 __device__ __forceinline__ int64_t slot_of(const int32_t *cu, int s, int c) {
     return (int64_t)cu[s] / 16 + s + c;
@@ -88,22 +41,25 @@ __device__ __forceinline__ int64_t slot_of(const int32_t *cu, int s, int c) {
 // Lane l = 16 g + m of a wave holds, of key-channel block b, token m and the four
 // channels 16b + 4g + j (j = 0..3): the A-operand layout of a product contracting
 // over the key channels (and, for the second factor of such a product, its B-operand
-// layout).  The cumulative log-decay of a channel over the chunk is then a prefix sum
-// across the 16 lanes of a DPP row, and its value at the last token sits in lane 15
-// of the row.
+// layout).  The cumulative decay e^{G} of a channel over the chunk is then a prefix
+// product across the 16 lanes of a DPP row, and its value at the last token sits in
+// lane 15 of the row.  (A running product of the per-token e^{g} keeps a few ulps of
+// relative error however far G falls; the exp of an fp32 cumulative sum would carry the
+// sum's absolute rounding, ~1e-5 at |G| = 80, into every factor.)
 
 template <int N>
-__device__ __forceinline__ float row_shr(float x) {  // lane m reads lane m - N of its row, 0 before it
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xF, 0xF, true));
+__device__ __forceinline__ float row_shr_or1(float x) {  // lane m reads lane m - N of its row, 1 before it
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), 0x110 | N, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ f32x4 row_prefix(f32x4 x) {
+__device__ __forceinline__ f32x4 row_prefix_prod(f32x4 x) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        x[j] += row_shr<1>(x[j]);
-        x[j] += row_shr<2>(x[j]);
-        x[j] += row_shr<4>(x[j]);
-        x[j] += row_shr<8>(x[j]);
+        x[j] *= row_shr_or1<1>(x[j]);
+        x[j] *= row_shr_or1<2>(x[j]);
+        x[j] *= row_shr_or1<4>(x[j]);
+        x[j] *= row_shr_or1<8>(x[j]);
     }
     return x;
 }
@@ -162,11 +118,14 @@ struct RowOps {
 };
 
 __device__ __forceinline__ RowOps row_ops(f32x4 g, f32x4 k, f32x4 q, int lane) {
-    const f32x4 G = row_prefix(g);
+    f32x4 a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = expf(g[j]);
+    const f32x4 P = row_prefix_prod(a);
     RowOps o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float ep = expf(G[j]), em = __builtin_amdgcn_rcpf(ep);
+        const float ep = P[j], em = __builtin_amdgcn_rcpf(ep);
         const float en = __shfl(ep, lane | 15);
         o.kp[j] = k[j] * ep;
         o.km[j] = k[j] * em;
@@ -405,19 +364,19 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
         const f32x4 vc = vn, tp = tpn;
         load_slice(c + 1);
         const int64_t slot = slot_of(cu, s, c);
-        float *ck = sck + (slot * H + h) * (int64_t)DK * DV + col0 + m;
+        float *ck = sck + (slot * H + h) * (int64_t)DK * DV + col0 * 16 + 4 * gq * 16 + m;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ck[(16 * b + 4 * gq + j) * DV] = S[b][j];
+            for (int j = 0; j < 4; ++j) ck[b * 16 * DV + j * 16] = S[b][j];
         f32x4 x = zero4();  // K+ S
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), S[b], x);
         const f32x4 d = mma_f32_k16(tp, vc - x, zero4());  // Delta = T'(V - K+ S)
-        float *db = dbuf + (slot * H + h) * 16 * (int64_t)DV + col0 + m;
+        float *db = dbuf + (slot * H + h) * 16 * (int64_t)DV + col0 * 16 + 4 * gq * 16 + m;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) db[(4 * gq + j) * DV] = d[j];
+        for (int j = 0; j < 4; ++j) db[j * 16] = d[j];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
@@ -490,22 +449,22 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
         const int64_t slot = slot_of(cu, s, c);
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(len, c);
-        float *hk = hck + (slot * H + h) * (int64_t)DK * DV + col0 + m;
+        float *hk = hck + (slot * H + h) * (int64_t)DK * DV + col0 * 16 + 4 * gq * 16 + m;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) hk[(16 * b + 4 * gq + j) * DV] = Sh[b][j];
+            for (int j = 0; j < 4; ++j) hk[b * 16 * DV + j * 16] = Sh[b][j];
         f32x4 x = mma_f32_k16(aq, ob, zero4());  // A_qk^T dO + K~ S^
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), Sh[b], x);
         const f32x4 e = mma_f32_k16(tt, x, zero4());  // E = T^T X
         const f32x4 dvv = bt * e;
-        float *eb = ebuf + (slot * H + h) * 16 * (int64_t)DV + col0 + m;
+        float *eb = ebuf + (slot * H + h) * 16 * (int64_t)DV + col0 * 16 + 4 * gq * 16 + m;
         const rsrc_t rdv = chunk_rsrc(dv, t0, n, H, h, DV);  // rows past n are dropped
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            eb[(4 * gq + j) * DV] = e[j];
+            eb[j * 16] = e[j];
             buf_store_f32(dvv[j], rdv, ((uint32_t)(4 * gq + j) * (uint32_t)H * DV + col0 + m) * 4u);
         }
         const f32x4 nd = -dvv;
@@ -525,115 +484,150 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
 }
 
 // ------------------------------------------------------------------ 3. per-chunk gradients
+// One wave per (chunk slot, head), on the fp32 matrix cores.  Contracting over the dv
+// columns in 16-column blocks cb, with the chunk's dO, Delta, E rows in the row layout
+// (lane (g, m): row m, columns 16cb + 4g + j) and the checkpoint tiles read the same way
+// (lane (g, n): state row 16b + n, the same columns), it forms
+//     dO S0^T, Delta S^^T, E S0^T   (16 x dk, tile b per key-channel block)
+//     M1 = Delta dO^T, M4 = dO Delta^T = M1^T, M3 = E Delta^T, M3^T
+// A 16x16 result held in the accumulator layout is the A operand of its transpose, which
+// is why both of each pair are formed.  Per channel block the triangular terms then come
+// from 16-long products with K-, Q+, K+ in the accumulator layout (lane (g, n): token
+// 4g + j, channel 16b + n), built in registers from q, k, g.  dbeta_r uses
+//     sum_col E (.) (K+ S0 + Ap Delta) = sum_ch K+ (.) (E S0^T) + sum_i Ap (.) M3   (row r),
+// so U itself is never formed.  The sweeps store the checkpoints as row-major 16x16 tiles
+// (tile (b, cb) of a dk x dv state, tile cb of a 16 x dv block), so each of these loads
+// is 1 KiB contiguous.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {  // lane m reads lane (m + N) mod 16 of its row
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 | N, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_sum(float x) {  // the sum over the 16 lanes of the row, in every lane
+    x += row_ror<1>(x);
+    x += row_ror<2>(x);
+    x += row_ror<4>(x);
+    x += row_ror<8>(x);
+    return x;
+}
+
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_grads_kernel(
+__global__ __launch_bounds__(64) void bwd_grads_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g,
     const T *__restrict__ beta, const float *__restrict__ dO, const int32_t *__restrict__ cu, int32_t nseq,
     int32_t H, const float *__restrict__ sck, const float *__restrict__ hck, const float *__restrict__ dbuf,
-    const float *__restrict__ ebuf, const float *__restrict__ mats, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ incr,
-    float *__restrict__ dbeta) {
-    constexpr int NOUT = 16 * DK / BWD_THREADS > 0 ? 16 * DK / BWD_THREADS : 1;  // (r, ch) outputs per thread
-    static_assert(16 * DK % BWD_THREADS == 0 || DK == 16, "outputs spread evenly");
-    const int64_t slot = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
-    const int tid = threadIdx.x;
+    const float *__restrict__ ebuf, const float *__restrict__ mats, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ incr, float *__restrict__ dbeta) {
+    constexpr int NB = DK / 16, NCB = DV / 16;
+    const int64_t item = blockIdx.x;
+    const int64_t slot = item / H;
+    const int h = (int)(item % H);
+    const int lane = threadIdx.x, gq = lane / 16, m = lane % 16;
     const int s = seq_of_slot(cu, nseq, slot);
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int c = (int)(slot - slot_of(cu, s, 0));
-    if (16 * (int64_t)c >= len) return;  // a slot no chunk uses (the block is uniform)
-    const int64_t t0 = bos + 16 * c;
-    const int n = (int)(len - 16 * c < 16 ? len - 16 * c : 16);
+    const int n = chunk_len(len, c);
+    if (n == 0) return;  // a slot no chunk uses
+    const int64_t t0 = bos + 16 * (int64_t)c;
+    const uint32_t ro = (uint32_t)(m * 16 + 4 * gq);  // this lane's place in a row-major tile
+    const float *S0 = sck + item * DK * DV + ro, *Sh = hck + item * DK * DV + ro;
+    const float *Dl = dbuf + item * 16 * DV + ro, *El = ebuf + item * 16 * DV + ro;
+    const rsrc_t rO = chunk_rsrc(dO, t0, n, H, h, DV), rV = chunk_rsrc(v, t0, n, H, h, DV);
 
-    __shared__ ChunkOps<DK> P;
-    __shared__ float S0[DK][17], Sh[DK][17];          // one 16-column slice of S0 and S^ (padded rows)
-    __shared__ float Ob[16][17], Dl[16][17], El[16][17], Vl[16][17];
-    __shared__ float M[4][16][16];
-    __shared__ float dbp[16][16];
-    chunk_prep<DK>(P, q, k, g, beta, t0, n, H, h);
-    P.Ap[tid / 16][tid % 16] = mats[((slot * H + h) * NMAT + MAT_AP) * 256 + tid];
-    __syncthreads();
+    f32x4 QS[NB], DS[NB], ES[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) QS[b] = DS[b] = ES[b] = zero4();
+    f32x4 m1 = zero4(), m4 = zero4(), m3 = zero4(), m3t = zero4();
+    float ev = 0.f;  // sum over this lane's columns of E (.) V, row m
+#pragma unroll 2
+    for (int cb = 0; cb < NCB; ++cb) {
+        const f32x4 o = load_row4<float>(rO, m, H, DV, 16 * cb + 4 * gq);
+        const f32x4 vv = load_row4<T>(rV, m, H, DV, 16 * cb + 4 * gq);
+        const f32x4 d = *reinterpret_cast<const f32x4 *>(Dl + cb * 256);
+        const f32x4 e = *reinterpret_cast<const f32x4 *>(El + cb * 256);
+        m1 = mma_f32_k16(d, o, m1);
+        m4 = mma_f32_k16(o, d, m4);
+        m3 = mma_f32_k16(e, d, m3);
+        m3t = mma_f32_k16(d, e, m3t);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ev += e[j] * vv[j];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(S0 + (b * NCB + cb) * 256);
+            const f32x4 sh = *reinterpret_cast<const f32x4 *>(Sh + (b * NCB + cb) * 256);
+            QS[b] = mma_f32_k16(o, s0, QS[b]);
+            ES[b] = mma_f32_k16(e, s0, ES[b]);
+            DS[b] = mma_f32_k16(d, sh, DS[b]);
+        }
+    }
 
-    float QS[NOUT], DS[NOUT], ES[NOUT];
+    // A operands of the masked 16x16 factors (lane (g, m), slot j: row m, column 4g + j).
+    const rsrc_t rb = chunk_rsrc(beta, t0, n, H, h, 1);
+    const f32x4 br = load_col4<T>(rb, gq, H, 1, 0);  // beta of tokens 4g + j
+    f32x4 aq, aa1, aa2, ab;
 #pragma unroll
-    for (int m = 0; m < NOUT; ++m) QS[m] = DS[m] = ES[m] = 0.f;
-    float M1 = 0.f, M2 = 0.f, M3 = 0.f, M4 = 0.f, dbacc = 0.f;
-    const int mr = tid / 16, mi = tid % 16;  // this thread's (r, i) entry of the 16x16 matrices
-    const float *S0g = sck + (slot * H + h) * (int64_t)DK * DV;
-    const float *Shg = hck + (slot * H + h) * (int64_t)DK * DV;
-    for (int col0 = 0; col0 < DV; col0 += 16) {
-        for (int idx = tid; idx < DK * 16; idx += BWD_THREADS) {
-            const int ch = idx / 16, col = idx % 16;
-            S0[ch][col] = S0g[ch * DV + col0 + col];
-            Sh[ch][col] = Shg[ch * DV + col0 + col];
-        }
-        {
-            const int r = tid / 16, col = tid % 16;
-            const bool in = r < n;
-            Ob[r][col] = in ? dO[((t0 + r) * H + h) * DV + col0 + col] : 0.f;
-            Dl[r][col] = dbuf[((slot * H + h) * 16 + r) * DV + col0 + col];
-            El[r][col] = ebuf[((slot * H + h) * 16 + r) * DV + col0 + col];
-            Vl[r][col] = in ? load_in(v + ((t0 + r) * H + h) * DV + col0 + col) : 0.f;
-        }
-        __syncthreads();
+    for (int j = 0; j < 4; ++j) {
+        const int col = 4 * gq + j;
+        aq[j] = col <= m ? m1[j] : 0.f;            // tril(M4)
+        aa1[j] = col >= m ? m4[j] : 0.f;           // triu(M1)
+        aa2[j] = col > m ? -br[j] * m3[j] : 0.f;   // -striu(M2), M2 = Delta dV^T = M3^T diag(beta)
+        ab[j] = col < m ? m3t[j] : 0.f;            // stril(M3)
+    }
+    const rsrc_t rq = chunk_rsrc(q, t0, n, H, h, DK), rk = chunk_rsrc(k, t0, n, H, h, DK);
+    const rsrc_t rg = chunk_rsrc(g, t0, n, H, h, DK);
+    const rsrc_t rdq = chunk_rsrc(dq, t0, n, H, h, DK), rdk = chunk_rsrc(dk, t0, n, H, h, DK);
+    const rsrc_t rin = chunk_rsrc(incr, t0, n, H, h, DK);
+    f32x4 kes = zero4();  // sum over channels of K+ (.) E S0^T, rows 4g + j
 #pragma unroll
-        for (int m = 0; m < NOUT; ++m) {
-            const int o = tid + BWD_THREADS * m;
-            const int r = o / DK, ch = o % DK;
-            if (r >= 16) continue;
-            float a = 0.f, b = 0.f, e = 0.f;
-            for (int j = 0; j < 16; ++j) {
-                a += Ob[r][j] * S0[ch][j];
-                b += Dl[r][j] * Sh[ch][j];
-                e += El[r][j] * S0[ch][j];
-            }
-            QS[m] += a;
-            DS[m] += b;
-            ES[m] += e;
-        }
-        for (int j = 0; j < 16; ++j) {
-            M1 += Dl[mr][j] * Ob[mi][j];
-            M2 += Dl[mr][j] * P.beta[mi] * El[mi][j];
-            M3 += El[mr][j] * Dl[mi][j];
-            M4 += Ob[mr][j] * Dl[mi][j];
-        }
-        {  // u_r at column col0 + mi, and its part of dbeta_r
-            float u = 0.f;
-            for (int ch = 0; ch < DK; ++ch) u += P.Kp[mr][ch] * S0[ch][mi];
-            for (int i = 0; i < 16; ++i) u += P.Ap[mr][i] * Dl[i][mi];
-            dbacc += El[mr][mi] * (Vl[mr][mi] - u);
-        }
-        __syncthreads();
-    }
-    M[0][mr][mi] = M1;
-    M[1][mr][mi] = M2;
-    M[2][mr][mi] = M3;
-    M[3][mr][mi] = M4;
-    dbp[mr][mi] = dbacc;
-    __syncthreads();
-    if (tid < 16 && tid < n) {
-        float x = 0.f;
-        for (int i = 0; i < 16; ++i) x += dbp[tid][i];
-        dbeta[(t0 + tid) * H + h] = x;
-    }
+    for (int b = 0; b < NB; ++b) {
+        const int ch = 16 * b + m;
+        const f32x4 qv = load_col4<T>(rq, gq, H, DK, ch), kv = load_col4<T>(rk, gq, H, DK, ch);
+        const f32x4 gv = load_col4<T>(rg, gq, H, DK, ch);
+        // e^{G} over the chunk's tokens: a running product within the lane, then across groups
+        f32x4 P;
 #pragma unroll
-    for (int m = 0; m < NOUT; ++m) {
-        const int o = tid + BWD_THREADS * m;
-        const int r = o / DK, ch = o % DK;
-        if (r >= n) continue;
-        float sq = QS[m], sa = 0.f, sb = ES[m];
-        for (int i = 0; i <= r; ++i) sq += M[3][r][i] * P.Km[i][ch];
-        for (int i = r; i < 16; ++i) sa += M[0][r][i] * P.Qp[i][ch];
-        for (int i = r + 1; i < 16; ++i) sa -= M[1][r][i] * P.Kp[i][ch];
-        for (int i = 0; i < r; ++i) sb += M[2][r][i] * P.Km[i][ch];
-        const float G = P.G[r][ch], ep = expf(G);
-        const float dqv = ep * sq;
-        const float av = expf(-G) * (sa + P.gam[ch] * DS[m]);
-        const float bv = P.beta[r] * ep * sb;
-        const int64_t e = ((t0 + r) * H + h) * DK + ch;
-        dq[e] = dqv;
-        dk[e] = av - bv;
-        incr[e] = P.Q[r][ch] * dqv - P.K[r][ch] * (av + bv);
+        for (int j = 0; j < 4; ++j) P[j] = expf(gv[j]);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) P[j] *= P[j - 1];
+        const float T0 = __shfl(P[3], m), T1 = __shfl(P[3], 16 + m), T2 = __shfl(P[3], 32 + m);
+        const float before = gq == 0 ? 1.f : (gq == 1 ? T0 : (gq == 2 ? T0 * T1 : (T0 * T1) * T2));
+        f32x4 ep, em, kp, km, qp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ep[j] = before * P[j];
+            em[j] = __builtin_amdgcn_rcpf(ep[j]);
+            kp[j] = kv[j] * ep[j];
+            km[j] = kv[j] * em[j];
+            qp[j] = qv[j] * ep[j];
+        }
+        const float egn = __shfl(ep[3], 48 + m);  // e^{G_n} of channel ch
+        const f32x4 tq = mma_f32_k16(aq, km, QS[b]);
+        const f32x4 ta = mma_f32_k16(aa2, kp, mma_f32_k16(aa1, qp, DS[b] * egn));
+        const f32x4 tb = mma_f32_k16(ab, km, ES[b]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float dqv = ep[j] * tq[j], av = em[j] * ta[j], bv = br[j] * ep[j] * tb[j];
+            const uint32_t off = ((uint32_t)(4 * gq + j) * (uint32_t)H * DK + (uint32_t)ch) * 4u;
+            buf_store_f32(dqv, rdq, off);
+            buf_store_f32(av - bv, rdk, off);
+            buf_store_f32(qv[j] * dqv - kv[j] * (av + bv), rin, off);
+            kes[j] += kp[j] * ES[b][j];
+        }
     }
+    // dbeta_r = sum_col E V - sum_ch K+ (.) E S0^T - sum_i Ap (.) M3
+    const float *ap = mats + (item * NMAT + MAT_AP) * 256;
+    f32x4 red;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[j] = row_sum(kes[j] + ap[(4 * gq + j) * 16 + m] * m3[j]);
+    ev += __shfl_xor(ev, 16);
+    ev += __shfl_xor(ev, 32);
+    // row m's reduced term sits in lane group m / 4, slot m % 4
+    const int src = 16 * (m / 4);
+    const float r0 = __shfl(red[0], src), r1 = __shfl(red[1], src), r2 = __shfl(red[2], src);
+    const float r3 = __shfl(red[3], src);
+    const int jm = m % 4;
+    const float rr = jm == 0 ? r0 : (jm == 1 ? r1 : (jm == 2 ? r2 : r3));
+    if (gq == 0) buf_store_f32(ev - rr, chunk_rsrc(dbeta, t0, n, H, h, 1), (uint32_t)m * (uint32_t)H * 4u);
 }
 
 // ------------------------------------------------------------------ 4. log-decay scan
@@ -727,7 +721,7 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     }
     if (e != hipSuccess) return e;
     if (a.N > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(BWD_THREADS), 0, st,
+        hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(64), 0, st,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.dO,
                            a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, mats, a.dq, a.dk, a.dg, a.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
