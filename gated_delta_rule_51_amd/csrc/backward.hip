@@ -25,6 +25,8 @@
 //   4. dg_scan   per (sequence, head, key channel): the reverse cumulative sum.
 // The column slices of 1 and 2 are independent (the state's columns evolve
 // separately), the chunks of 0 and 3 too, so only the recurrences in 1 and 2 are serial.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -95,14 +97,56 @@ __device__ __forceinline__ f32x4 load_row4(rsrc_t r, int m, int32_t H, int D, in
     return buf_in4<T>(r, ((uint32_t)m * (uint32_t)H * (uint32_t)D + (uint32_t)c0) * sizeof(T));
 }
 
-// Column col of the four tokens 4g + j (the accumulator layout), through chunk_rsrc.
+// Raw words of four consecutive input elements (row layout) and their widening.  The
+// sweeps carry raw words from one iteration to the next and widen them where they are
+// used: a conversion right after a load would make the compiler wait for it there.
 template <typename T>
-__device__ __forceinline__ f32x4 load_col4(rsrc_t r, int gq, int32_t H, int D, int col) {
+using Row4Raw = std::conditional_t<sizeof(T) == 4, u32x4, u32x2>;
+
+template <typename T>
+__device__ __forceinline__ Row4Raw<T> load_row4_raw(rsrc_t r, int m, int32_t H, int D, int c0) {
+    const uint32_t off = ((uint32_t)m * (uint32_t)H * (uint32_t)D + (uint32_t)c0) * sizeof(T);
+    if constexpr (sizeof(T) == 4) return buf_load_u32x4(r, off);
+    else return buf_load_u32x2(r, off);
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 widen_row4(Row4Raw<T> w) {
+    if constexpr (sizeof(T) == 4) return __builtin_bit_cast(f32x4, w);
+    else return unpack_bf16x4(w);
+}
+
+// Column col of the four tokens 4g + j (the accumulator layout), through chunk_rsrc, as
+// raw 32-bit words.  A bf16 element is read as the aligned word that holds it (its pair
+// partner lies in the same row, so the word never leaves the resource); widen_col4 takes
+// the right half.
+template <typename T>
+__device__ __forceinline__ uint32_t col_off(int gq, int j, int32_t H, int D, int col) {
+    return ((uint32_t)(4 * gq + j) * (uint32_t)H * (uint32_t)D + (uint32_t)col) * sizeof(T);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 load_col4_raw(rsrc_t r, int gq, int32_t H, int D, int col) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = buf_load_u32(r, col_off<T>(gq, j, H, D, col) & ~3u);
+    return w;
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 widen_col4(u32x4 w, int gq, int32_t H, int D, int col) {
     f32x4 x;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        x[j] = buf_in<T>(r, ((uint32_t)(4 * gq + j) * (uint32_t)H * (uint32_t)D + (uint32_t)col) * sizeof(T));
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 4) x[j] = __uint_as_float(w[j]);
+        else x[j] = (col_off<T>(gq, j, H, D, col) & 2u) ? hi_bf16(w[j]) : lo_bf16(w[j]);
+    }
     return x;
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 load_col4(rsrc_t r, int gq, int32_t H, int D, int col) {
+    return widen_col4<T>(load_col4_raw<T>(r, gq, H, D, col), gq, H, D, col);
 }
 
 // Tokens in chunk c of a sequence of len tokens (0 outside it), wave-uniform.
@@ -231,50 +275,55 @@ __global__ __launch_bounds__(64 * MATS_WAVES) void bwd_mats_kernel(
 
 
 // ------------------------------------------------------------------ 1/2. the two sweeps
-// A workgroup serves one (sequence, head) and NS 16-column slices of dv, one wave each;
-// the wave keeps its dk x 16 slice of the state (or of the adjoint) in registers as NB
-// accumulator tiles (tile b, lane (g, n): row 16b + 4g + j, column n of the slice).
-// Per chunk the waves first build the next chunk's decay operands together (channel
-// block b by wave b mod NS) into the other half of a double-buffered LDS set, then
-// advance their slice with fp32 MFMAs reading this chunk's set; one barrier per chunk.
-// Raw inputs are loaded two chunks ahead, per-slice inputs one chunk ahead.
-template <int DK>
+// A workgroup serves one (sequence, head) and NS 16-column slices of dv with two kinds
+// of waves:
+//   * NS slice waves keep their dk x 16 slice of the state (or of the adjoint) in
+//     registers as NB accumulator tiles (tile b, lane (g, n): row 16b + 4g + j, column n
+//     of the slice) and advance it with fp32 MFMAs;
+//   * NP producer waves build the decay operands of the next chunk (channel block b by
+//     producer b mod NP) into the other half of a double-buffered LDS set.
+// One barrier per chunk hands a set over.  Both roles hold their inputs for two chunks
+// in registers and load three chunks ahead (the loop is unrolled by two so that the
+// register sets are fixed); a look-ahead past either end of the sequence reads empty
+// resources, so the loop body has no branch.  The forward sweep walks the chunks in
+// order, the adjoint sweep in reverse; both count iterations i = 0, 1, ...
+template <int DK, bool ADJ>
 struct SweepSet {
-    float rows[16][DK + 4];  // forward: K+ rows;  adjoint: K~ rows
-    float trA[DK][20];       // forward: K~^T;     adjoint: Q+^T
-    float trB[DK][20];       // adjoint: K+^T
-    float gam[DK];           // e^{G_n}
+    float rows[16][DK + 4];       // forward: K+ rows;  adjoint: K~ rows
+    float trA[DK][20];            // forward: K~^T;     adjoint: Q+^T
+    float trB[ADJ ? DK : 1][20];  // adjoint: K+^T
+    float gam[DK];                // e^{G_n}
 };
 
-template <int DK, int NS, bool ADJ, typename T>
-struct SweepPrep {
-    // wave w builds channel blocks w, w + NS, ... (a block index past NB reads an empty
-    // resource and writes nothing); no branch around the loads, so the compiler waits
-    // for them only where build() uses them
-    static constexpr int NB = DK / 16, NBW = (NB + NS - 1) / NS;
-    f32x4 rg[NBW], rk[NBW], rq[NBW];
+template <int DK, int NP, bool ADJ, typename T>
+struct RawBlocks {
+    // producer w builds channel blocks w, w + NP, ... (a block index past NB reads an
+    // empty resource and writes nothing)
+    static constexpr int NB = DK / 16, NBW = (NB + NP - 1) / NP;
+    Row4Raw<T> rg[NBW], rk[NBW], rq[NBW];
 
     __device__ __forceinline__ void load(const T *q, const T *k, const T *g, int64_t t0, int n, int32_t H, int h,
                                          int wave, int lane) {
         const int m = lane % 16, gq = lane / 16;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
-            const int b = wave + NS * i;
+            const int b = wave + NP * i;
             const int nb = b < NB ? n : 0;
             const int c0 = (b < NB ? 16 * b : 0) + 4 * gq;
-            rg[i] = load_row4<T>(chunk_rsrc(g, t0, nb, H, h, DK), m, H, DK, c0);
-            rk[i] = load_row4<T>(chunk_rsrc(k, t0, nb, H, h, DK), m, H, DK, c0);
-            if (ADJ) rq[i] = load_row4<T>(chunk_rsrc(q, t0, nb, H, h, DK), m, H, DK, c0);
+            rg[i] = load_row4_raw<T>(chunk_rsrc(g, t0, nb, H, h, DK), m, H, DK, c0);
+            rk[i] = load_row4_raw<T>(chunk_rsrc(k, t0, nb, H, h, DK), m, H, DK, c0);
+            if (ADJ) rq[i] = load_row4_raw<T>(chunk_rsrc(q, t0, nb, H, h, DK), m, H, DK, c0);
         }
     }
 
-    __device__ __forceinline__ void build(SweepSet<DK> &P, int wave, int lane) const {
+    __device__ __forceinline__ void build(SweepSet<DK, ADJ> &P, int wave, int lane) const {
         const int m = lane % 16, gq = lane / 16;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
-            const int b = wave + NS * i;
-            const RowOps o = row_ops(rg[i], rk[i], ADJ ? rq[i] : rk[i], lane);
-            if (NB % NS != 0 && b >= NB) continue;
+            const int b = wave + NP * i;
+            const f32x4 kw = widen_row4<T>(rk[i]);
+            const RowOps o = row_ops(widen_row4<T>(rg[i]), kw, ADJ ? widen_row4<T>(rq[i]) : kw, lane);
+            if (NB % NP != 0 && b >= NB) continue;
             const int c0 = 16 * b + 4 * gq;
             *reinterpret_cast<f32x4 *>(&P.rows[m][c0]) = ADJ ? o.kt : o.kp;
 #pragma unroll
@@ -302,6 +351,28 @@ __device__ __forceinline__ f32x4 load_mat(const float *mats, const int32_t *cu, 
 // so the loop that follows carries no pending load into its first iteration.
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// A per-wave LDS stage turns a tile held in the accumulator layout (lane (g, n): rows
+// 4g + j, column n) into row-major order, which the wave then stores as one contiguous
+// 1 KiB piece (lane l: row l / 4, columns 4 (l % 4) .. +3) instead of four scattered
+// pieces per row group.  Row groups are 80 floats apart, so the four lane groups' writes
+// fall on distinct banks.  The wave's LDS operations run in order, so no barrier is needed
+// between its writes and its reads.
+constexpr int STAGE_TILE = 320;
+
+__device__ __forceinline__ void stage_put(float *st, f32x4 x, int gq, int m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[gq * 80 + j * 16 + m] = x[j];
+}
+
+__device__ __forceinline__ f32x4 stage_get(const float *st, int lane) {
+    const int r = lane / 4;
+    return *reinterpret_cast<const f32x4 *>(st + (r / 4) * 80 + (r % 4) * 16 + 4 * (lane % 4));
+}
+
+__device__ __forceinline__ void buf_store_f32x4(f32x4 x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+
 // Producer waves per workgroup of the sweeps: every SIMD gets work (a lone slice wave
 // has three helpers), at most one producer per SIMD.
 template <int NS>
@@ -310,41 +381,66 @@ struct SweepShape {
     static constexpr int THREADS = 64 * (NS + NP);
 };
 
+template <int P>
+using Par = std::integral_constant<int, P>;
+
+// Runs body(i, Par<i & 1>) for i = 0 .. nc - 1, two iterations per trip.
+template <typename F>
+__device__ __forceinline__ void unrolled_chunks(int nc, F &&body) {
+    int i = 0;
+    for (; i + 1 < nc; i += 2) {
+        body(i, Par<0>{});
+        body(i + 1, Par<1>{});
+    }
+    if (i < nc) body(i, Par<0>{});
+}
+
+template <int DK, int NP, bool ADJ, typename T>
+__device__ __forceinline__ void sweep_producer(SweepSet<DK, ADJ> (&L)[2], const T *q, const T *k, const T *g,
+                                               int64_t bos, int64_t len, int nc, int32_t H, int h, int pw,
+                                               int lane) {
+    RawBlocks<DK, NP, ADJ, T> raw[2];
+    auto chunk = [&](int i) { return ADJ ? nc - 1 - i : i; };
+    auto load = [&](RawBlocks<DK, NP, ADJ, T> &r, int i) {
+        const int c = chunk(i);
+        r.load(q, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane);
+    };
+    load(raw[0], 0);
+    load(raw[1], 1);
+    raw[0].build(L[0], pw, lane);
+    load(raw[0], 2);
+    __syncthreads();
+    unrolled_chunks(nc, [&](int i, auto par) {
+        constexpr int p = 1 - decltype(par)::value;  // the set of iteration i + 1
+        raw[p].build(L[p], pw, lane);
+        load(raw[p], i + 3);
+        __syncthreads();
+    });
+}
+
 template <int DK, int DV, int NS, typename T>
 __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g, const float *__restrict__ init,
     const int32_t *__restrict__ cu, int32_t H, const float *__restrict__ mats, float *__restrict__ sck,
     float *__restrict__ dbuf, float *__restrict__ sfin) {
-    constexpr int NB = DK / 16, NG = DV / 16 / NS, NP = SweepShape<NS>::NP;
+    constexpr int NB = DK / 16, NCB = DV / 16, NG = NCB / NS, NP = SweepShape<NS>::NP;
     const int chain = blockIdx.x / NG, sg = blockIdx.x % NG;
     const int s = chain / H, h = chain % H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
-    __shared__ SweepSet<DK> L[2];
+    __shared__ SweepSet<DK, false> L[2];
+    __shared__ __attribute__((aligned(16))) float stage_all[NS][NB][STAGE_TILE];
     const int64_t hd = (int64_t)s * H + h;
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int nc = (int)((len + 15) / 16);
 
     if (wave >= NS) {
-        // ---------------------------------------------------------------- producer
-        // Look-ahead past the last chunk reads empty resources and builds an unused set,
-        // so the loop body has no branch.
-        const int pw = wave - NS;
-        SweepPrep<DK, NP, false, T> pre;
-        auto load_raw = [&](int c) { pre.load(k, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane); };
-        load_raw(0);
-        pre.build(L[0], pw, lane);
-        load_raw(1);
-        __syncthreads();
-        for (int c = 0; c < nc; ++c) {
-            pre.build(L[(c + 1) & 1], pw, lane);
-            load_raw(c + 2);
-            __syncthreads();
-        }
+        sweep_producer<DK, NP, false, T>(L, k, k, g, bos, len, nc, H, h, wave - NS, lane);
         return;
     }
     // -------------------------------------------------------------------- slice wave
-    const int col0 = (sg * NS + wave) * 16;
+    const int cb = sg * NS + wave, col0 = 16 * cb;
+    float *stage = stage_all[wave][0];
     f32x4 S[NB];
     {  // (an empty resource without an initial state: its loads return 0)
         const rsrc_t ri = make_rsrc(init ? init + hd * DK * DV : init, init ? DK * DV * 4u : 0u);
@@ -352,38 +448,45 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
         for (int b = 0; b < NB; ++b) S[b] = load_col4<float>(ri, 4 * b + gq, 1, DV, col0 + m);
         wait_vm0();
     }
-    f32x4 vn, tpn;  // the next chunk's v slice and T'
-    auto load_slice = [&](int c) {
-        vn = load_col4<T>(chunk_rsrc(v, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, DV), gq, H, DV, col0 + m);
-        tpn = load_mat(mats, cu, s, c, nc, H, h, MAT_TP, lane);
+    u32x4 vn[2];  // v slice (raw words) and T' of the chunks two iterations ahead
+    f32x4 tpn[2];
+    auto load_slice = [&](int p, int c) {
+        vn[p] = load_col4_raw<T>(chunk_rsrc(v, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, DV), gq, H, DV,
+                                 col0 + m);
+        tpn[p] = load_mat(mats, cu, s, c, nc, H, h, MAT_TP, lane);
     };
-    load_slice(0);
+    load_slice(0, 0);
+    load_slice(1, 1);
     __syncthreads();
-    for (int c = 0; c < nc; ++c) {
-        const SweepSet<DK> &P = L[c & 1];
-        const f32x4 vc = vn, tp = tpn;
-        load_slice(c + 1);
-        const int64_t slot = slot_of(cu, s, c);
-        float *ck = sck + (slot * H + h) * (int64_t)DK * DV + col0 * 16 + 4 * gq * 16 + m;
+    unrolled_chunks(nc, [&](int c, auto par) {
+        constexpr int p = decltype(par)::value;
+        const SweepSet<DK, false> &P = L[p];
+        const u32x4 vraw = vn[p];
+        const f32x4 tp = tpn[p];
+        load_slice(p, c + 2);
+        const int64_t item = slot_of(cu, s, c) * H + h;
+        // the state at the chunk's start, staged to row-major tiles
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ck[b * 16 * DV + j * 16] = S[b][j];
+        for (int b = 0; b < NB; ++b) stage_put(stage + b * STAGE_TILE, S[b], gq, m);
         f32x4 x = zero4();  // K+ S
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), S[b], x);
-        const f32x4 d = mma_f32_k16(tp, vc - x, zero4());  // Delta = T'(V - K+ S)
-        float *db = dbuf + (slot * H + h) * 16 * (int64_t)DV + col0 * 16 + 4 * gq * 16 + m;
+        float *ck = sck + item * DK * DV + cb * 256 + 4 * lane;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) db[j * 16] = d[j];
+        for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<f32x4 *>(ck + b * NCB * 256) = stage_get(stage + b * STAGE_TILE, lane);
+        const f32x4 vc = widen_col4<T>(vraw, gq, H, DV, col0 + m);
+        const f32x4 d = mma_f32_k16(tp, vc - x, zero4());  // Delta = T'(V - K+ S)
+        stage_put(stage, d, gq, m);
+        *reinterpret_cast<f32x4 *>(dbuf + item * 16 * DV + cb * 256 + 4 * lane) = stage_get(stage, lane);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
             S[b] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]), d, S[b] * gm);
         }
         __syncthreads();
-    }
+    });
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -396,34 +499,24 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
     const float *__restrict__ dO, const float *__restrict__ dfinal, const int32_t *__restrict__ cu, int32_t H,
     const float *__restrict__ mats, float *__restrict__ hck, float *__restrict__ ebuf, float *__restrict__ dv,
     float *__restrict__ dinit) {
-    constexpr int NB = DK / 16, NG = DV / 16 / NS, NP = SweepShape<NS>::NP;
+    constexpr int NB = DK / 16, NCB = DV / 16, NG = NCB / NS, NP = SweepShape<NS>::NP;
     const int chain = blockIdx.x / NG, sg = blockIdx.x % NG;
     const int s = chain / H, h = chain % H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
-    __shared__ SweepSet<DK> L[2];
+    __shared__ SweepSet<DK, true> L[2];
+    __shared__ __attribute__((aligned(16))) float stage_all[NS][NB < 2 ? 2 : NB][STAGE_TILE];
     const int64_t hd = (int64_t)s * H + h;
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int nc = (int)((len + 15) / 16);
 
     if (wave >= NS) {
-        // ---------------------------------------------------------------- producer
-        const int pw = wave - NS;
-        SweepPrep<DK, NP, true, T> pre;
-        auto load_raw = [&](int c) { pre.load(q, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane); };
-        load_raw(nc - 1);
-        pre.build(L[(nc - 1) & 1], pw, lane);
-        load_raw(nc - 2);
-        __syncthreads();
-        for (int c = nc - 1; c >= 0; --c) {
-            pre.build(L[(c - 1) & 1], pw, lane);
-            load_raw(c - 2);
-            __syncthreads();
-        }
+        sweep_producer<DK, NP, true, T>(L, q, k, g, bos, len, nc, H, h, wave - NS, lane);
         return;
     }
     // -------------------------------------------------------------------- slice wave
-    const int col0 = (sg * NS + wave) * 16;
+    const int cb = sg * NS + wave, col0 = 16 * cb;
+    float *stage = stage_all[wave][0];
     f32x4 Sh[NB];
     {
         const rsrc_t rf = make_rsrc(dfinal ? dfinal + hd * DK * DV : dfinal, dfinal ? DK * DV * 4u : 0u);
@@ -431,42 +524,49 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
         for (int b = 0; b < NB; ++b) Sh[b] = load_col4<float>(rf, 4 * b + gq, 1, DV, col0 + m);
         wait_vm0();
     }
-    f32x4 on, bn, aqn, ttn;  // the next chunk's dO slice, beta, A_qk^T, T^T
-    auto load_slice = [&](int c) {
+    u32x4 on[2], bn[2];  // dO slice and beta (raw words), A_qk^T, T^T two iterations ahead
+    f32x4 aqn[2], ttn[2];
+    auto load_slice = [&](int p, int c) {
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(len, c);
-        on = load_col4<float>(chunk_rsrc(dO, t0, n, H, h, DV), gq, H, DV, col0 + m);
-        bn = load_col4<T>(chunk_rsrc(beta, t0, n, H, h, 1), gq, H, 1, 0);
-        aqn = load_mat(mats, cu, s, c, nc, H, h, MAT_AQKT, lane);
-        ttn = load_mat(mats, cu, s, c, nc, H, h, MAT_TT, lane);
+        on[p] = load_col4_raw<float>(chunk_rsrc(dO, t0, n, H, h, DV), gq, H, DV, col0 + m);
+        bn[p] = load_col4_raw<T>(chunk_rsrc(beta, t0, n, H, h, 1), gq, H, 1, 0);
+        aqn[p] = load_mat(mats, cu, s, c, nc, H, h, MAT_AQKT, lane);
+        ttn[p] = load_mat(mats, cu, s, c, nc, H, h, MAT_TT, lane);
     };
-    load_slice(nc - 1);
+    load_slice(0, nc - 1);
+    load_slice(1, nc - 2);
     __syncthreads();
-    for (int c = nc - 1; c >= 0; --c) {
-        const SweepSet<DK> &P = L[c & 1];
-        const f32x4 ob = on, bt = bn, aq = aqn, tt = ttn;
-        load_slice(c - 1);
-        const int64_t slot = slot_of(cu, s, c);
+    unrolled_chunks(nc, [&](int i, auto par) {
+        constexpr int p = decltype(par)::value;
+        const int c = nc - 1 - i;
+        const SweepSet<DK, true> &P = L[p];
+        const f32x4 ob = widen_col4<float>(on[p], gq, H, DV, col0 + m);
+        const f32x4 bt = widen_col4<T>(bn[p], gq, H, 1, 0);
+        const f32x4 aq = aqn[p], tt = ttn[p];
+        load_slice(p, c - 2);
+        const int64_t item = slot_of(cu, s, c) * H + h;
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(len, c);
-        float *hk = hck + (slot * H + h) * (int64_t)DK * DV + col0 * 16 + 4 * gq * 16 + m;
+        // the adjoint of the state after the chunk, staged to row-major tiles
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hk[b * 16 * DV + j * 16] = Sh[b][j];
+        for (int b = 0; b < NB; ++b) stage_put(stage + b * STAGE_TILE, Sh[b], gq, m);
         f32x4 x = mma_f32_k16(aq, ob, zero4());  // A_qk^T dO + K~ S^
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), Sh[b], x);
+        float *hk = hck + item * DK * DV + cb * 256 + 4 * lane;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<f32x4 *>(hk + b * NCB * 256) = stage_get(stage + b * STAGE_TILE, lane);
         const f32x4 e = mma_f32_k16(tt, x, zero4());  // E = T^T X
         const f32x4 dvv = bt * e;
-        float *eb = ebuf + (slot * H + h) * 16 * (int64_t)DV + col0 * 16 + 4 * gq * 16 + m;
-        const rsrc_t rdv = chunk_rsrc(dv, t0, n, H, h, DV);  // rows past n are dropped
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            eb[j * 16] = e[j];
-            buf_store_f32(dvv[j], rdv, ((uint32_t)(4 * gq + j) * (uint32_t)H * DV + col0 + m) * 4u);
-        }
+        stage_put(stage, e, gq, m);
+        stage_put(stage + STAGE_TILE, dvv, gq, m);
+        *reinterpret_cast<f32x4 *>(ebuf + item * 16 * DV + cb * 256 + 4 * lane) = stage_get(stage, lane);
+        // dV rows past n are dropped by the resource
+        buf_store_f32x4(stage_get(stage + STAGE_TILE, lane), chunk_rsrc(dv, t0, n, H, h, DV),
+                        ((uint32_t)(lane / 4) * (uint32_t)H * DV + col0 + 4 * (lane % 4)) * 4u);
         const f32x4 nd = -dvv;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -475,7 +575,7 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
             Sh[b] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trB[16 * b + m][4 * gq]), nd, acc);
         }
         __syncthreads();
-    }
+    });
     if (dinit)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -484,20 +584,25 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
 }
 
 // ------------------------------------------------------------------ 3. per-chunk gradients
-// One wave per (chunk slot, head), on the fp32 matrix cores.  Contracting over the dv
+// GW waves per (chunk slot, head), on the fp32 matrix cores.  Contracting over the dv
 // columns in 16-column blocks cb, with the chunk's dO, Delta, E rows in the row layout
 // (lane (g, m): row m, columns 16cb + 4g + j) and the checkpoint tiles read the same way
-// (lane (g, n): state row 16b + n, the same columns), it forms
-//     dO S0^T, Delta S^^T, E S0^T   (16 x dk, tile b per key-channel block)
-//     M1 = Delta dO^T, M4 = dO Delta^T = M1^T, M3 = E Delta^T, M3^T
-// A 16x16 result held in the accumulator layout is the A operand of its transpose, which
-// is why both of each pair are formed.  Per channel block the triangular terms then come
-// from 16-long products with K-, Q+, K+ in the accumulator layout (lane (g, n): token
-// 4g + j, channel 16b + n), built in registers from q, k, g.  dbeta_r uses
+// (lane (g, n): state row 16b + n, the same columns), wave w forms, for its channel
+// blocks b = w, w + GW, ...,
+//     dO S0^T, Delta S^^T, E S0^T   (16 x 16 tiles)
+// and its share of the four 16x16 Gram matrices
+//     M1 = Delta dO^T, M4 = dO Delta^T = M1^T, M3 = E Delta^T, M3^T,
+// which it passes to the others through LDS.  A 16x16 result held in the accumulator
+// layout is the A operand of its transpose, which is why both of each pair are formed.
+// Per channel block the triangular terms then come from 16-long products with K-, Q+, K+
+// in the accumulator layout (lane (g, n): token 4g + j, channel 16b + n), built in
+// registers from q, k, g.  dbeta_r uses
 //     sum_col E (.) (K+ S0 + Ap Delta) = sum_ch K+ (.) (E S0^T) + sum_i Ap (.) M3   (row r),
 // so U itself is never formed.  The sweeps store the checkpoints as row-major 16x16 tiles
 // (tile (b, cb) of a dk x dv state, tile cb of a 16 x dv block), so each of these loads
-// is 1 KiB contiguous.
+// is 1 KiB contiguous.  The log-decay increments leave as in-chunk reverse cumulative
+// sums, with the chunk's total per key channel in ctot (the carry from later chunks is
+// added by the two kernels after this one).
 template <int N>
 __device__ __forceinline__ float row_ror(float x) {  // lane m reads lane (m + N) mod 16 of its row
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 | N, 0xF, 0xF, false));
@@ -511,59 +616,126 @@ __device__ __forceinline__ float row_sum(float x) {  // the sum over the 16 lane
     return x;
 }
 
+template <int DK>
+struct GradShape {
+    static constexpr int NB = DK / 16;
+    static constexpr int GW = NB < 4 ? NB : 4;  // waves per (chunk, head)
+    static constexpr int NBW = NB / GW;         // channel blocks per wave
+};
+
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__(64) void bwd_grads_kernel(
+__global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g,
     const T *__restrict__ beta, const float *__restrict__ dO, const int32_t *__restrict__ cu, int32_t nseq,
     int32_t H, const float *__restrict__ sck, const float *__restrict__ hck, const float *__restrict__ dbuf,
     const float *__restrict__ ebuf, const float *__restrict__ mats, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ incr, float *__restrict__ dbeta) {
-    constexpr int NB = DK / 16, NCB = DV / 16;
+    float *__restrict__ dgs, float *__restrict__ dbeta, float *__restrict__ ctot) {
+    constexpr int NCB = DV / 16, GW = GradShape<DK>::GW, NBW = GradShape<DK>::NBW;
     const int64_t item = blockIdx.x;
     const int64_t slot = item / H;
     const int h = (int)(item % H);
-    const int lane = threadIdx.x, gq = lane / 16, m = lane % 16;
+    const int wave = GW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
+    __shared__ __attribute__((aligned(16))) float Ms[4][256];  // M1, M4, M3, M3^T (accumulator layout)
+    __shared__ float dbp[GW][16];
     const int s = seq_of_slot(cu, nseq, slot);
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int c = (int)(slot - slot_of(cu, s, 0));
     const int n = chunk_len(len, c);
-    if (n == 0) return;  // a slot no chunk uses
+    if (n == 0) return;  // a slot no chunk uses (uniform over the workgroup)
     const int64_t t0 = bos + 16 * (int64_t)c;
     const uint32_t ro = (uint32_t)(m * 16 + 4 * gq);  // this lane's place in a row-major tile
     const float *S0 = sck + item * DK * DV + ro, *Sh = hck + item * DK * DV + ro;
     const float *Dl = dbuf + item * 16 * DV + ro, *El = ebuf + item * 16 * DV + ro;
     const rsrc_t rO = chunk_rsrc(dO, t0, n, H, h, DV), rV = chunk_rsrc(v, t0, n, H, h, DV);
 
-    f32x4 QS[NB], DS[NB], ES[NB];
+    struct Ops {
+        f32x4 o, d, e, s0[NBW], sh[NBW];
+        Row4Raw<T> vv;
+    };
+    auto load_ops = [&](Ops &x, int cb) {
+        x.o = widen_row4<float>(load_row4_raw<float>(rO, m, H, DV, 16 * cb + 4 * gq));
+        x.vv = load_row4_raw<T>(rV, m, H, DV, 16 * cb + 4 * gq);
+        x.d = *reinterpret_cast<const f32x4 *>(Dl + cb * 256);
+        x.e = *reinterpret_cast<const f32x4 *>(El + cb * 256);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) QS[b] = DS[b] = ES[b] = zero4();
-    f32x4 m1 = zero4(), m4 = zero4(), m3 = zero4(), m3t = zero4();
-    float ev = 0.f;  // sum over this lane's columns of E (.) V, row m
-#pragma unroll 2
-    for (int cb = 0; cb < NCB; ++cb) {
-        const f32x4 o = load_row4<float>(rO, m, H, DV, 16 * cb + 4 * gq);
-        const f32x4 vv = load_row4<T>(rV, m, H, DV, 16 * cb + 4 * gq);
-        const f32x4 d = *reinterpret_cast<const f32x4 *>(Dl + cb * 256);
-        const f32x4 e = *reinterpret_cast<const f32x4 *>(El + cb * 256);
-        m1 = mma_f32_k16(d, o, m1);
-        m4 = mma_f32_k16(o, d, m4);
-        m3 = mma_f32_k16(e, d, m3);
-        m3t = mma_f32_k16(d, e, m3t);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ev += e[j] * vv[j];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(S0 + (b * NCB + cb) * 256);
-            const f32x4 sh = *reinterpret_cast<const f32x4 *>(Sh + (b * NCB + cb) * 256);
-            QS[b] = mma_f32_k16(o, s0, QS[b]);
-            ES[b] = mma_f32_k16(e, s0, ES[b]);
-            DS[b] = mma_f32_k16(d, sh, DS[b]);
+        for (int i = 0; i < NBW; ++i) {
+            const int b = wave + GW * i;
+            x.s0[i] = *reinterpret_cast<const f32x4 *>(S0 + (b * NCB + cb) * 256);
+            x.sh[i] = *reinterpret_cast<const f32x4 *>(Sh + (b * NCB + cb) * 256);
         }
+    };
+    // the epilogue's inputs, loaded now (raw words) so that their latency hides under the
+    // contraction
+    const rsrc_t rq = chunk_rsrc(q, t0, n, H, h, DK), rk = chunk_rsrc(k, t0, n, H, h, DK);
+    const rsrc_t rg = chunk_rsrc(g, t0, n, H, h, DK), rb = chunk_rsrc(beta, t0, n, H, h, 1);
+    u32x4 qraw[NBW], kraw[NBW], graw[NBW];
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        const int ch = 16 * (wave + GW * i) + m;
+        qraw[i] = load_col4_raw<T>(rq, gq, H, DK, ch);
+        kraw[i] = load_col4_raw<T>(rk, gq, H, DK, ch);
+        graw[i] = load_col4_raw<T>(rg, gq, H, DK, ch);
     }
+    const u32x4 braw = load_col4_raw<T>(rb, gq, H, 1, 0);
+    const float *ap = mats + (item * NMAT + MAT_AP) * 256;
+    f32x4 apv;  // stril(K+ K-^T) at rows 4g + j, column m
+#pragma unroll
+    for (int j = 0; j < 4; ++j) apv[j] = ap[(4 * gq + j) * 16 + m];
+
+    f32x4 QS[NBW], DS[NBW], ES[NBW];
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) QS[i] = DS[i] = ES[i] = zero4();
+    constexpr int NM = 4 / GW;  // Gram matrices per wave: wave w forms M_w, M_{w + GW}, ...
+    f32x4 mm[NM];
+#pragma unroll
+    for (int t = 0; t < NM; ++t) mm[t] = zero4();
+    float ev = 0.f;  // sum over this lane's columns of E (.) V, row m
+    auto step = [&](const Ops &x) {
+#pragma unroll
+        for (int t = 0; t < NM; ++t) {
+            // M_0 = Delta dO^T, M_1 = dO Delta^T, M_2 = E Delta^T, M_3 = Delta E^T, chosen by
+            // vector selects (with the wave index in a scalar register the compiler would
+            // branch, splitting the unrolled loop into small blocks)
+            const int id = (int)(threadIdx.x / 64) + GW * t;
+            f32x4 a, b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = id == 1 ? x.o[j] : (id == 2 ? x.e[j] : x.d[j]);
+                b[j] = id == 0 ? x.o[j] : (id == 3 ? x.e[j] : x.d[j]);
+            }
+            mm[t] = mma_f32_k16(a, b, mm[t]);
+        }
+        const f32x4 vv = widen_row4<T>(x.vv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ev += x.e[j] * vv[j];
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            QS[i] = mma_f32_k16(x.o, x.s0[i], QS[i]);
+            ES[i] = mma_f32_k16(x.e, x.s0[i], ES[i]);
+            DS[i] = mma_f32_k16(x.d, x.sh[i], DS[i]);
+        }
+    };
+    // the column blocks fully unrolled over a ring of three operand sets: the loads of
+    // block cb + 2 are in flight while block cb is used
+    Ops buf[3];
+    load_ops(buf[0], 0);
+    if (NCB > 1) load_ops(buf[1], 1);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        if (cb + 2 < NCB) load_ops(buf[(cb + 2) % 3], cb + 2);
+        step(buf[cb % 3]);
+    }
+#pragma unroll
+    for (int t = 0; t < NM; ++t) *reinterpret_cast<f32x4 *>(&Ms[wave + GW * t][4 * lane]) = mm[t];
+    __syncthreads();
+    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(&Ms[0][4 * lane]);
+    const f32x4 m4 = *reinterpret_cast<const f32x4 *>(&Ms[1][4 * lane]);
+    const f32x4 m3 = *reinterpret_cast<const f32x4 *>(&Ms[2][4 * lane]);
+    const f32x4 m3t = *reinterpret_cast<const f32x4 *>(&Ms[3][4 * lane]);
 
     // A operands of the masked 16x16 factors (lane (g, m), slot j: row m, column 4g + j).
-    const rsrc_t rb = chunk_rsrc(beta, t0, n, H, h, 1);
-    const f32x4 br = load_col4<T>(rb, gq, H, 1, 0);  // beta of tokens 4g + j
+    const f32x4 br = widen_col4<T>(braw, gq, H, 1, 0);  // beta of tokens 4g + j
     f32x4 aq, aa1, aa2, ab;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -573,16 +745,14 @@ __global__ __launch_bounds__(64) void bwd_grads_kernel(
         aa2[j] = col > m ? -br[j] * m3[j] : 0.f;   // -striu(M2), M2 = Delta dV^T = M3^T diag(beta)
         ab[j] = col < m ? m3t[j] : 0.f;            // stril(M3)
     }
-    const rsrc_t rq = chunk_rsrc(q, t0, n, H, h, DK), rk = chunk_rsrc(k, t0, n, H, h, DK);
-    const rsrc_t rg = chunk_rsrc(g, t0, n, H, h, DK);
     const rsrc_t rdq = chunk_rsrc(dq, t0, n, H, h, DK), rdk = chunk_rsrc(dk, t0, n, H, h, DK);
-    const rsrc_t rin = chunk_rsrc(incr, t0, n, H, h, DK);
+    const rsrc_t rin = chunk_rsrc(dgs, t0, n, H, h, DK);
     f32x4 kes = zero4();  // sum over channels of K+ (.) E S0^T, rows 4g + j
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int ch = 16 * b + m;
-        const f32x4 qv = load_col4<T>(rq, gq, H, DK, ch), kv = load_col4<T>(rk, gq, H, DK, ch);
-        const f32x4 gv = load_col4<T>(rg, gq, H, DK, ch);
+    for (int i = 0; i < NBW; ++i) {
+        const int ch = 16 * (wave + GW * i) + m;
+        const f32x4 qv = widen_col4<T>(qraw[i], gq, H, DK, ch), kv = widen_col4<T>(kraw[i], gq, H, DK, ch);
+        const f32x4 gv = widen_col4<T>(graw[i], gq, H, DK, ch);
         // e^{G} over the chunk's tokens: a running product within the lane, then across groups
         f32x4 P;
 #pragma unroll
@@ -601,70 +771,106 @@ __global__ __launch_bounds__(64) void bwd_grads_kernel(
             qp[j] = qv[j] * ep[j];
         }
         const float egn = __shfl(ep[3], 48 + m);  // e^{G_n} of channel ch
-        const f32x4 tq = mma_f32_k16(aq, km, QS[b]);
-        const f32x4 ta = mma_f32_k16(aa2, kp, mma_f32_k16(aa1, qp, DS[b] * egn));
-        const f32x4 tb = mma_f32_k16(ab, km, ES[b]);
+        const f32x4 tq = mma_f32_k16(aq, km, QS[i]);
+        const f32x4 ta = mma_f32_k16(aa2, kp, mma_f32_k16(aa1, qp, DS[i] * egn));
+        const f32x4 tb = mma_f32_k16(ab, km, ES[i]);
+        f32x4 inc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float dqv = ep[j] * tq[j], av = em[j] * ta[j], bv = br[j] * ep[j] * tb[j];
             const uint32_t off = ((uint32_t)(4 * gq + j) * (uint32_t)H * DK + (uint32_t)ch) * 4u;
             buf_store_f32(dqv, rdq, off);
             buf_store_f32(av - bv, rdk, off);
-            buf_store_f32(qv[j] * dqv - kv[j] * (av + bv), rin, off);
-            kes[j] += kp[j] * ES[b][j];
+            inc[j] = qv[j] * dqv - kv[j] * (av + bv);
+            kes[j] += kp[j] * ES[i][j];
         }
+        // reverse cumulative sum over the chunk's tokens: within the lane, then the later groups
+#pragma unroll
+        for (int j = 2; j >= 0; --j) inc[j] += inc[j + 1];
+        const float U1 = __shfl(inc[0], 16 + m), U2 = __shfl(inc[0], 32 + m), U3 = __shfl(inc[0], 48 + m);
+        const float after = gq == 3 ? 0.f : (gq == 2 ? U3 : (gq == 1 ? U3 + U2 : (U3 + U2) + U1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            buf_store_f32(inc[j] + after, rin, ((uint32_t)(4 * gq + j) * (uint32_t)H * DK + (uint32_t)ch) * 4u);
+        if (gq == 0) ctot[item * DK + ch] = inc[0] + after;
     }
     // dbeta_r = sum_col E V - sum_ch K+ (.) E S0^T - sum_i Ap (.) M3
-    const float *ap = mats + (item * NMAT + MAT_AP) * 256;
     f32x4 red;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[j] = row_sum(kes[j] + ap[(4 * gq + j) * 16 + m] * m3[j]);
-    ev += __shfl_xor(ev, 16);
-    ev += __shfl_xor(ev, 32);
+    for (int j = 0; j < 4; ++j) red[j] = row_sum(kes[j] + (wave == 0 ? apv[j] * m3[j] : 0.f));
     // row m's reduced term sits in lane group m / 4, slot m % 4
     const int src = 16 * (m / 4);
     const float r0 = __shfl(red[0], src), r1 = __shfl(red[1], src), r2 = __shfl(red[2], src);
     const float r3 = __shfl(red[3], src);
     const int jm = m % 4;
     const float rr = jm == 0 ? r0 : (jm == 1 ? r1 : (jm == 2 ? r2 : r3));
-    if (gq == 0) buf_store_f32(ev - rr, chunk_rsrc(dbeta, t0, n, H, h, 1), (uint32_t)m * (uint32_t)H * 4u);
+    ev += __shfl_xor(ev, 16);
+    ev += __shfl_xor(ev, 32);
+    if (gq == 0) dbp[wave][m] = (wave == 0 ? ev : 0.f) - rr;
+    __syncthreads();
+    if (wave == 0 && gq == 0) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < GW; ++w) x += dbp[w][m];
+        buf_store_f32(x, chunk_rsrc(dbeta, t0, n, H, h, 1), (uint32_t)m * (uint32_t)H * 4u);
+    }
 }
 
-// ------------------------------------------------------------------ 4. log-decay scan
+// ------------------------------------------------------------------ 4. log-decay carries
+// dlog_alpha_t = rowsum(dS_final (.) S_final) + sum_{s >= t} incr_s.  The gradient kernel
+// left the in-chunk part; per (sequence, head, key channel) dg_carry turns the chunk
+// totals into the sum over all later chunks plus the final-state term (in place), and
+// dg_apply adds that carry to the chunk's tokens.
 template <int DV>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_dg_scan_kernel(const int32_t *__restrict__ cu, int32_t nseq,
-                                                                   int32_t H, int32_t DK,
-                                                                   const float *__restrict__ dfinal,
-                                                                   const float *__restrict__ sfin,
-                                                                   float *__restrict__ dg) {
+__global__ __launch_bounds__(BWD_THREADS) void bwd_dg_carry_kernel(const int32_t *__restrict__ cu, int32_t nseq,
+                                                                    int32_t H, int32_t DK,
+                                                                    const float *__restrict__ dfinal,
+                                                                    const float *__restrict__ sfin,
+                                                                    float *__restrict__ ctot) {
     const int64_t i = (int64_t)blockIdx.x * BWD_THREADS + threadIdx.x;
     if (i >= (int64_t)nseq * H * DK) return;
-    const int64_t s = i / ((int64_t)H * DK);
-    const int64_t hc = i - s * H * DK;
-    const int h = (int)(hc / DK), ch = (int)(hc - (int64_t)h * DK);
+    const int s = (int)(i / ((int64_t)H * DK));
+    const int64_t hc = i - (int64_t)s * H * DK;  // h * DK + ch
     float run = 0.f;
     if (dfinal) {
         const float *a = dfinal + i * DV, *b = sfin + i * DV;
         for (int j = 0; j < DV; ++j) run += a[j] * b[j];
     }
-    // sixteen tokens per trip, their loads issued before the sums, so they overlap
-    const int64_t bos = cu[s];
-    int64_t t = cu[s + 1] - 1;
-    const int64_t step = (int64_t)H * DK;
-    for (; t - 15 >= bos; t -= 16) {
-        float x[16];
+    const int nc = (cu[s + 1] - cu[s] + 15) / 16;
+    const int64_t base = slot_of(cu, s, 0) * H * DK + hc, step = (int64_t)H * DK;
+    int c = nc - 1;
+    for (; c >= 7; c -= 8) {  // eight chunks per trip, their loads issued first
+        float x[8];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) x[m] = dg[((t - m) * H + h) * DK + ch];
+        for (int u = 0; u < 8; ++u) x[u] = ctot[base + (c - u) * step];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            run += x[m];
-            dg[((t - m) * H + h) * DK + ch] = run;
+        for (int u = 0; u < 8; ++u) {
+            ctot[base + (c - u) * step] = run;
+            run += x[u];
         }
     }
-    for (; t >= bos; --t) {
-        const int64_t e = t * step + (int64_t)h * DK + ch;
-        run += dg[e];
-        dg[e] = run;
+    for (; c >= 0; --c) {
+        const float x = ctot[base + c * step];
+        ctot[base + c * step] = run;
+        run += x;
+    }
+}
+
+template <int DK>
+__global__ __launch_bounds__(BWD_THREADS) void bwd_dg_apply_kernel(const int32_t *__restrict__ cu, int32_t nseq,
+                                                                    int32_t H, const float *__restrict__ ctot,
+                                                                    float *__restrict__ dg) {
+    const int64_t item = blockIdx.x;
+    const int64_t slot = item / H;
+    const int h = (int)(item % H);
+    const int s = seq_of_slot(cu, nseq, slot);
+    const int64_t bos = cu[s], len = cu[s + 1] - bos;
+    const int c = (int)(slot - slot_of(cu, s, 0));
+    const int n = chunk_len(len, c);
+    const int64_t t0 = bos + 16 * (int64_t)c;
+    for (int e = threadIdx.x; e < 16 * DK; e += BWD_THREADS) {
+        const int r = e / DK, ch = e % DK;
+        if (r < n) dg[((t0 + r) * H + h) * DK + ch] += ctot[item * DK + ch];
     }
 }
 
@@ -703,6 +909,7 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     float *dbuf = hck + blk, *ebuf = dbuf + slots * a.H * 16 * (int64_t)DV;
     float *sfin = ebuf + slots * a.H * 16 * (int64_t)DV;
     float *mats = sfin + (int64_t)a.nseq * a.H * DK * DV;
+    float *ctot = mats + slots * a.H * NMAT * 256;
     const hipStream_t st = (hipStream_t)a.stream;
     hipError_t e = hipSuccess;
     const int64_t items = slots * a.H;
@@ -721,13 +928,16 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     }
     if (e != hipSuccess) return e;
     if (a.N > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(64), 0, st,
+        hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(64 * GradShape<DK>::GW), 0, st,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.dO,
-                           a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, mats, a.dq, a.dk, a.dg, a.dbeta);
+                           a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, mats, a.dq, a.dk, a.dg, a.dbeta, ctot);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t nitems = (int64_t)a.nseq * a.H * DK;
-        hipLaunchKernelGGL((bwd_dg_scan_kernel<DV>), dim3((unsigned)((nitems + BWD_THREADS - 1) / BWD_THREADS)),
-                           dim3(BWD_THREADS), 0, st, a.cu, a.nseq, a.H, DK, a.dfinal, sfin, a.dg);
+        hipLaunchKernelGGL((bwd_dg_carry_kernel<DV>), dim3((unsigned)((nitems + BWD_THREADS - 1) / BWD_THREADS)),
+                           dim3(BWD_THREADS), 0, st, a.cu, a.nseq, a.H, DK, a.dfinal, sfin, ctot);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_dg_apply_kernel<DK>), dim3((unsigned)items), dim3(BWD_THREADS), 0, st, a.cu, a.nseq,
+                           a.H, ctot, a.dg);
         e = hipGetLastError();
     }
     return e;
@@ -750,8 +960,9 @@ hipError_t launch_backward(const BackwardArgs &a) {
 
 int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv) {
     const int64_t slots = chunk_slots(N, nseq);
+    // S and S^ checkpoints, Delta and E, the final state, chunk matrices, chunk log-decay totals
     return 2 * slots * H * (int64_t)dk * dv + 2 * slots * H * 16 * (int64_t)dv + (int64_t)nseq * H * dk * dv +
-           slots * H * 4 * 256;  // S and S^ checkpoints, Delta and E, the final state, chunk matrices
+           slots * H * 4 * 256 + slots * H * (int64_t)dk;
 }
 
 }  // namespace kda
