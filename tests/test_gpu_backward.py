@@ -60,6 +60,22 @@ def test_backward_matches_oracle(dev, dtype, dk, dv):
     _check(dev, x, d_o, S0, dF)
 
 
+# The sweeps put NS 16-column slices of dv in one workgroup, NS the smallest of 1, 2, 4, 8 for
+# which the (sequence, head, slice-group) grid stays within 256 workgroups, with 3, 2, 4, 4
+# producer waves; these shapes take each NS, and dk = 16 with two producers leaves one of
+# them without a channel block.
+@pytest.mark.parametrize("seqlens,H,dk,dv,dtype,ns", [
+    ([70, 23], 24, 128, 128, torch.bfloat16, 2),   # 2 x 24 x 8 = 384 slices
+    ([50], 96, 128, 128, torch.bfloat16, 4),       # 768 slices (the K3 layer's grouping)
+    ([37, 20], 96, 64, 128, torch.float32, 8),     # 1,536 slices
+    ([45], 64, 16, 128, torch.bfloat16, 2),        # dk = 16: one channel block, two producers
+])
+def test_backward_slice_groupings(dev, seqlens, H, dk, dv, dtype, ns):
+    x, d_o, S0, dF = _case(dev, seqlens, H, dk, dv, dtype, seed=H + dk)
+    say(f"  case: backward seqlens={seqlens} H={H} dk={dk} dv={dv} {dtype} (NS = {ns})")
+    _check(dev, x, d_o, S0, dF)
+
+
 def test_backward_without_initial_state_or_final_gradient(dev):
     x, d_o, _, _ = _case(dev, [33, 5], 3, 128, 64, torch.bfloat16, seed=3, init=False, dfinal=False)
     say("  case: backward without init / d_final")
