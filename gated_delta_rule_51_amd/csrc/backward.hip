@@ -465,13 +465,35 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
         const f32x4 tp = tpn[p];
         load_slice(p, c + 2);
         const int64_t item = slot_of(cu, s, c) * H + h;
+        // this chunk's operands; with one or two slice waves per workgroup all read from LDS
+        // before anything waits for one of them (the scheduling barrier keeps the compiler
+        // from moving the reads down next to their uses, where each would stall the product
+        // chain for a full LDS latency); with four or more, reading them at their uses
+        // measured faster (and with three waves per SIMD the early reads' registers spill)
+        f32x4 kr[NB], tr[NB], gm[NB];
+        constexpr bool EARLY = NS <= 2;
+        auto read_rows = [&](int b) { kr[b] = *reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]); };
+        auto read_upd = [&](int b) {
+            tr[b] = *reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]);
+            gm[b] = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
+        };
+        if constexpr (EARLY) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                read_rows(b);
+                read_upd(b);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // the state at the chunk's start, staged to row-major tiles
 #pragma unroll
         for (int b = 0; b < NB; ++b) stage_put(stage + b * STAGE_TILE, S[b], gq, m);
         f32x4 x = zero4();  // K+ S
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), S[b], x);
+        for (int b = 0; b < NB; ++b) {
+            if constexpr (!EARLY) read_rows(b);
+            x = mma_f32_k16(kr[b], S[b], x);
+        }
         float *ck = sck + item * DK * DV + cb * 256 + 4 * lane;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -482,8 +504,8 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
         *reinterpret_cast<f32x4 *>(dbuf + item * 16 * DV + cb * 256 + 4 * lane) = stage_get(stage, lane);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
-            S[b] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]), d, S[b] * gm);
+            if constexpr (!EARLY) read_upd(b);
+            S[b] = mma_f32_k16(tr[b], d, S[b] * gm[b]);
         }
         __syncthreads();
     });
@@ -548,13 +570,25 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
         const int64_t item = slot_of(cu, s, c) * H + h;
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(len, c);
+        // this chunk's operands read from LDS ahead of their uses: the K~ rows first, the rest
+        // while the first product runs
+        f32x4 kr[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) kr[b] = *reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]);
         // the adjoint of the state after the chunk, staged to row-major tiles
 #pragma unroll
         for (int b = 0; b < NB; ++b) stage_put(stage + b * STAGE_TILE, Sh[b], gq, m);
+        f32x4 qr[NB], pr[NB], gm[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            qr[b] = *reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]);
+            pr[b] = *reinterpret_cast<const f32x4 *>(&P.trB[16 * b + m][4 * gq]);
+            gm[b] = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
+        }
+        if constexpr (NS <= 4) __builtin_amdgcn_sched_barrier(0);  // (the reads stay ahead of the products)
         f32x4 x = mma_f32_k16(aq, ob, zero4());  // A_qk^T dO + K~ S^
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            x = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.rows[m][16 * b + 4 * gq]), Sh[b], x);
+        for (int b = 0; b < NB; ++b) x = mma_f32_k16(kr[b], Sh[b], x);
         float *hk = hck + item * DK * DV + cb * 256 + 4 * lane;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -569,11 +603,7 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
                         ((uint32_t)(lane / 4) * (uint32_t)H * DV + col0 + 4 * (lane % 4)) * 4u);
         const f32x4 nd = -dvv;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
-            f32x4 acc = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]), ob, Sh[b] * gm);
-            Sh[b] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(&P.trB[16 * b + m][4 * gq]), nd, acc);
-        }
+        for (int b = 0; b < NB; ++b) Sh[b] = mma_f32_k16(pr[b], nd, mma_f32_k16(qr[b], ob, Sh[b] * gm[b]));
         __syncthreads();
     });
     if (dinit)
