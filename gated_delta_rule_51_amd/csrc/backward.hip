@@ -15,14 +15,15 @@
 // (the last because raising g_t[c] only rescales row c of S_{t-1}).  T = (I + A_kk)^-1
 // itself is needed (E), not only T' = T diag(beta).
 //
-// Five kernels, all in fp32 (the products on the fp32 matrix cores where they are dense):
+// Six kernels, all in fp32 (the products on the fp32 matrix cores where they are dense):
 //   0. mats      per (chunk, head): T', T^T, A_qk^T and stril(K+ K-^T);
-//   1. fwd sweep per (sequence, head, slices of 16 dv columns): the forward chunk
+//   1. fwd sweep per (sequence, head, groups of 16-column dv slices): the forward chunk
 //      recurrence, writing S at every chunk start, every chunk's Delta, the final state;
 //   2. adjoint   the same grid, chunks in reverse: dV, S^ after every chunk, E, dinit;
-//   3. grads     per (chunk, head), all dv columns in 16-column slices: dq, dk, dbeta
-//      and the log-decay increments;
-//   4. dg_scan   per (sequence, head, key channel): the reverse cumulative sum.
+//   3. grads     per (chunk, head), all dv columns in 16-column blocks: dq, dk, dbeta
+//      and the log-decay terms as in-chunk reverse cumulative sums with chunk totals;
+//   4. dg_carry  per (sequence, head, key channel): the sum over later chunks;
+//   5. dg_apply  per (chunk, head): adds it to the chunk's tokens.
 // The column slices of 1 and 2 are independent (the state's columns evolve
 // separately), the chunks of 0 and 3 too, so only the recurrences in 1 and 2 are serial.
 #include <type_traits>
