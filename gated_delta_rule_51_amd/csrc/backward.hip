@@ -15,15 +15,13 @@
 // (the last because raising g_t[c] only rescales row c of S_{t-1}).  T = (I + A_kk)^-1
 // itself is needed (E), not only T' = T diag(beta).
 //
-// Six kernels, all in fp32 (the products on the fp32 matrix cores where they are dense):
+// Four kernels, all in fp32 (the products on the fp32 matrix cores where they are dense):
 //   0. mats      per (chunk, head): T', T^T, A_qk^T and stril(K+ K-^T);
 //   1. fwd sweep per (sequence, head, groups of 16-column dv slices): the forward chunk
-//      recurrence, writing S at every chunk start, every chunk's Delta, the final state;
+//      recurrence, writing S at every chunk start and every chunk's Delta;
 //   2. adjoint   the same grid, chunks in reverse: dV, S^ after every chunk, E, dinit;
-//   3. grads     per (chunk, head), all dv columns in 16-column blocks: dq, dk, dbeta
-//      and the log-decay terms as in-chunk reverse cumulative sums with chunk totals;
-//   4. dg_carry  per (sequence, head, key channel): the sum over later chunks;
-//   5. dg_apply  per (chunk, head): adds it to the chunk's tokens.
+//   3. grads     per (chunk, head), all dv columns in 16-column blocks: dq, dk, dbeta and
+//      dlog_alpha (its part from the later tokens read off the chunk's checkpoints).
 // The column slices of 1 and 2 are independent (the state's columns evolve
 // separately), the chunks of 0 and 3 too, so only the recurrences in 1 and 2 are serial.
 #include <type_traits>
@@ -32,8 +30,6 @@
 #include "kda_launch.hpp"
 
 namespace kda {
-
-constexpr int BWD_THREADS = 256;
 
 // Chunk c of sequence s occupies slot cu[s]/16 + s + c (the prefill workspace's map).
 __device__ __forceinline__ int64_t slot_of(const int32_t *cu, int s, int c) {
@@ -423,7 +419,7 @@ template <int DK, int DV, int NS, typename T>
 __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g, const float *__restrict__ init,
     const int32_t *__restrict__ cu, int32_t H, const float *__restrict__ mats, float *__restrict__ sck,
-    float *__restrict__ dbuf, float *__restrict__ sfin) {
+    float *__restrict__ dbuf) {
     constexpr int NB = DK / 16, NCB = DV / 16, NG = NCB / NS, NP = SweepShape<NS>::NP;
     const int chain = blockIdx.x / NG, sg = blockIdx.x % NG;
     const int s = chain / H, h = chain % H;
@@ -510,10 +506,6 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
         }
         __syncthreads();
     });
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sfin[(hd * DK + 16 * b + 4 * gq + j) * DV + col0 + m] = S[b][j];
 }
 
 template <int DK, int DV, int NS, typename T>
@@ -631,9 +623,16 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
 //     sum_col E (.) (K+ S0 + Ap Delta) = sum_ch K+ (.) (E S0^T) + sum_i Ap (.) M3   (row r),
 // so U itself is never formed.  The sweeps store the checkpoints as row-major 16x16 tiles
 // (tile (b, cb) of a dk x dv state, tile cb of a 16 x dv block), so each of these loads
-// is 1 KiB contiguous.  The log-decay increments leave as in-chunk reverse cumulative
-// sums, with the chunk's total per key channel in ctot (the carry from later chunks is
-// added by the two kernels after this one).
+// is 1 KiB contiguous.
+// The log-decay gradient is dg_t = rowsum(dS_T (.) S_T) + sum_{s >= t} incr_s with
+// incr_s = q_s (.) dq_s - k_s (.) (a_s + b_s).  Within the chunk this kernel sums the
+// increments itself; the rest, everything after the chunk's last token tau, is exactly
+// rowsum(S^ (.) S_tau): raising row c of S_tau by a factor is the same as raising the next
+// token's decay of channel c, and S^ (the adjoint of S_tau through the later tokens) is the
+// checkpoint this chunk reads.  With S_tau = Diag(e^{G_n}) S0 + K~^T Delta,
+//     rowsum(S^ (.) S_tau) = e^{G_n} (.) rowsum(S^ (.) S0) + sum_r K~_r (.) (Delta S^^T)_r,
+// both from quantities formed here anyway, so no sum runs over the whole sequence (whose
+// fp32 rounding would grow with its length).
 template <int N>
 __device__ __forceinline__ float row_ror(float x) {  // lane m reads lane (m + N) mod 16 of its row
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 | N, 0xF, 0xF, false));
@@ -655,12 +654,12 @@ struct GradShape {
 };
 
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
+__global__ __launch_bounds__(64 * GradShape<DK>::GW) __attribute__((amdgpu_waves_per_eu(2, 8))) void bwd_grads_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g,
     const T *__restrict__ beta, const float *__restrict__ dO, const int32_t *__restrict__ cu, int32_t nseq,
     int32_t H, const float *__restrict__ sck, const float *__restrict__ hck, const float *__restrict__ dbuf,
     const float *__restrict__ ebuf, const float *__restrict__ mats, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dgs, float *__restrict__ dbeta, float *__restrict__ ctot) {
+    float *__restrict__ dgs, float *__restrict__ dbeta) {
     constexpr int NCB = DV / 16, GW = GradShape<DK>::GW, NBW = GradShape<DK>::NBW;
     const int64_t item = blockIdx.x;
     const int64_t slot = item / H;
@@ -722,6 +721,9 @@ __global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
 #pragma unroll
     for (int t = 0; t < NM; ++t) mm[t] = zero4();
     float ev = 0.f;  // sum over this lane's columns of E (.) V, row m
+    f32x4 SH[NBW];   // S0 S^^T of each channel block (its diagonal is rowsum(S^ (.) S0))
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) SH[i] = zero4();
     auto step = [&](const Ops &x) {
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
@@ -745,17 +747,17 @@ __global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
             QS[i] = mma_f32_k16(x.o, x.s0[i], QS[i]);
             ES[i] = mma_f32_k16(x.e, x.s0[i], ES[i]);
             DS[i] = mma_f32_k16(x.d, x.sh[i], DS[i]);
+            SH[i] = mma_f32_k16(x.s0[i], x.sh[i], SH[i]);
         }
     };
-    // the column blocks fully unrolled over a ring of three operand sets: the loads of
-    // block cb + 2 are in flight while block cb is used
-    Ops buf[3];
+    // the column blocks fully unrolled over two operand sets: the loads of block cb + 1 are
+    // in flight while block cb is used
+    Ops buf[2];
     load_ops(buf[0], 0);
-    if (NCB > 1) load_ops(buf[1], 1);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        if (cb + 2 < NCB) load_ops(buf[(cb + 2) % 3], cb + 2);
-        step(buf[cb % 3]);
+        if (cb + 1 < NCB) load_ops(buf[(cb + 1) % 2], cb + 1);
+        step(buf[cb % 2]);
     }
 #pragma unroll
     for (int t = 0; t < NM; ++t) *reinterpret_cast<f32x4 *>(&Ms[wave + GW * t][4 * lane]) = mm[t];
@@ -806,6 +808,7 @@ __global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
         const f32x4 ta = mma_f32_k16(aa2, kp, mma_f32_k16(aa1, qp, DS[i] * egn));
         const f32x4 tb = mma_f32_k16(ab, km, ES[i]);
         f32x4 inc;
+        float kd = 0.f;  // sum over this lane's tokens of K~ (.) Delta S^^T, channel ch
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float dqv = ep[j] * tq[j], av = em[j] * ta[j], bv = br[j] * ep[j] * tb[j];
@@ -814,7 +817,17 @@ __global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
             buf_store_f32(av - bv, rdk, off);
             inc[j] = qv[j] * dqv - kv[j] * (av + bv);
             kes[j] += kp[j] * ES[i][j];
+            kd += kv[j] * (egn * em[j]) * DS[i][j];
         }
+        // everything after the chunk: e^{G_n} rowsum(S^ (.) S0) + sum_r K~ (.) Delta S^^T; the
+        // diagonal entry of channel m sits in lane group m / 4, slot m % 4
+        float dg0 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dg0 = 4 * gq + j == m ? SH[i][j] : dg0;
+        const float s0sh = __shfl(dg0, 16 * (m / 4) + m);
+        kd += __shfl_xor(kd, 16);
+        kd += __shfl_xor(kd, 32);
+        const float carry = egn * s0sh + kd;
         // reverse cumulative sum over the chunk's tokens: within the lane, then the later groups
 #pragma unroll
         for (int j = 2; j >= 0; --j) inc[j] += inc[j + 1];
@@ -822,8 +835,8 @@ __global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
         const float after = gq == 3 ? 0.f : (gq == 2 ? U3 : (gq == 1 ? U3 + U2 : (U3 + U2) + U1));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            buf_store_f32(inc[j] + after, rin, ((uint32_t)(4 * gq + j) * (uint32_t)H * DK + (uint32_t)ch) * 4u);
-        if (gq == 0) ctot[item * DK + ch] = inc[0] + after;
+            buf_store_f32((inc[j] + after) + carry, rin,
+                          ((uint32_t)(4 * gq + j) * (uint32_t)H * DK + (uint32_t)ch) * 4u);
     }
     // dbeta_r = sum_col E V - sum_ch K+ (.) E S0^T - sum_i Ap (.) M3
     f32x4 red;
@@ -847,64 +860,6 @@ __global__ __launch_bounds__(64 * GradShape<DK>::GW) void bwd_grads_kernel(
     }
 }
 
-// ------------------------------------------------------------------ 4. log-decay carries
-// dlog_alpha_t = rowsum(dS_final (.) S_final) + sum_{s >= t} incr_s.  The gradient kernel
-// left the in-chunk part; per (sequence, head, key channel) dg_carry turns the chunk
-// totals into the sum over all later chunks plus the final-state term (in place), and
-// dg_apply adds that carry to the chunk's tokens.
-template <int DV>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_dg_carry_kernel(const int32_t *__restrict__ cu, int32_t nseq,
-                                                                    int32_t H, int32_t DK,
-                                                                    const float *__restrict__ dfinal,
-                                                                    const float *__restrict__ sfin,
-                                                                    float *__restrict__ ctot) {
-    const int64_t i = (int64_t)blockIdx.x * BWD_THREADS + threadIdx.x;
-    if (i >= (int64_t)nseq * H * DK) return;
-    const int s = (int)(i / ((int64_t)H * DK));
-    const int64_t hc = i - (int64_t)s * H * DK;  // h * DK + ch
-    float run = 0.f;
-    if (dfinal) {
-        const float *a = dfinal + i * DV, *b = sfin + i * DV;
-        for (int j = 0; j < DV; ++j) run += a[j] * b[j];
-    }
-    const int nc = (cu[s + 1] - cu[s] + 15) / 16;
-    const int64_t base = slot_of(cu, s, 0) * H * DK + hc, step = (int64_t)H * DK;
-    int c = nc - 1;
-    for (; c >= 7; c -= 8) {  // eight chunks per trip, their loads issued first
-        float x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = ctot[base + (c - u) * step];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            ctot[base + (c - u) * step] = run;
-            run += x[u];
-        }
-    }
-    for (; c >= 0; --c) {
-        const float x = ctot[base + c * step];
-        ctot[base + c * step] = run;
-        run += x;
-    }
-}
-
-template <int DK>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_dg_apply_kernel(const int32_t *__restrict__ cu, int32_t nseq,
-                                                                    int32_t H, const float *__restrict__ ctot,
-                                                                    float *__restrict__ dg) {
-    const int64_t item = blockIdx.x;
-    const int64_t slot = item / H;
-    const int h = (int)(item % H);
-    const int s = seq_of_slot(cu, nseq, slot);
-    const int64_t bos = cu[s], len = cu[s + 1] - bos;
-    const int c = (int)(slot - slot_of(cu, s, 0));
-    const int n = chunk_len(len, c);
-    const int64_t t0 = bos + 16 * (int64_t)c;
-    for (int e = threadIdx.x; e < 16 * DK; e += BWD_THREADS) {
-        const int r = e / DK, ch = e % DK;
-        if (r < n) dg[((t0 + r) * H + h) * DK + ch] += ctot[item * DK + ch];
-    }
-}
-
 // ------------------------------------------------------------------ launch
 
 // Column slices per workgroup of the sweeps: as few as fill the chip (each slice gets a
@@ -918,12 +873,12 @@ static int sweep_slices(int64_t chains, int nsl) {
 
 template <int DK, int DV, int NS, typename T>
 static hipError_t launch_sweeps(const BackwardArgs &a, const float *mats, float *sck, float *hck, float *dbuf,
-                                float *ebuf, float *sfin) {
+                                float *ebuf) {
     const hipStream_t st = (hipStream_t)a.stream;
     const unsigned grid = (unsigned)((int64_t)a.nseq * a.H * (DV / 16 / NS));
     const dim3 block(SweepShape<NS>::THREADS);
     hipLaunchKernelGGL((bwd_fwd_sweep_kernel<DK, DV, NS, T>), dim3(grid), block, 0, st, (const T *)a.k,
-                       (const T *)a.v, (const T *)a.g, a.init, a.cu, a.H, mats, sck, dbuf, sfin);
+                       (const T *)a.v, (const T *)a.g, a.init, a.cu, a.H, mats, sck, dbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_adjoint_sweep_kernel<DK, DV, NS, T>), dim3(grid), block, 0, st, (const T *)a.q,
@@ -938,9 +893,7 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     const int64_t blk = slots * a.H * (int64_t)DK * DV;  // floats of one per-chunk state array
     float *sck = a.ws, *hck = sck + blk;
     float *dbuf = hck + blk, *ebuf = dbuf + slots * a.H * 16 * (int64_t)DV;
-    float *sfin = ebuf + slots * a.H * 16 * (int64_t)DV;
-    float *mats = sfin + (int64_t)a.nseq * a.H * DK * DV;
-    float *ctot = mats + slots * a.H * NMAT * 256;
+    float *mats = ebuf + slots * a.H * 16 * (int64_t)DV;
     const hipStream_t st = (hipStream_t)a.stream;
     hipError_t e = hipSuccess;
     const int64_t items = slots * a.H;
@@ -952,23 +905,16 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     }
     constexpr int NSL = DV / 16;
     switch (sweep_slices((int64_t)a.nseq * a.H, NSL)) {
-    case 1: e = launch_sweeps<DK, DV, 1, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
-    case 2: if constexpr (NSL >= 2) e = launch_sweeps<DK, DV, 2, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
-    case 4: if constexpr (NSL >= 4) e = launch_sweeps<DK, DV, 4, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
-    default: if constexpr (NSL >= 8) e = launch_sweeps<DK, DV, 8, T>(a, mats, sck, hck, dbuf, ebuf, sfin); break;
+    case 1: e = launch_sweeps<DK, DV, 1, T>(a, mats, sck, hck, dbuf, ebuf); break;
+    case 2: if constexpr (NSL >= 2) e = launch_sweeps<DK, DV, 2, T>(a, mats, sck, hck, dbuf, ebuf); break;
+    case 4: if constexpr (NSL >= 4) e = launch_sweeps<DK, DV, 4, T>(a, mats, sck, hck, dbuf, ebuf); break;
+    default: if constexpr (NSL >= 8) e = launch_sweeps<DK, DV, 8, T>(a, mats, sck, hck, dbuf, ebuf); break;
     }
     if (e != hipSuccess) return e;
     if (a.N > 0) {
         hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(64 * GradShape<DK>::GW), 0, st,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.dO,
-                           a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, mats, a.dq, a.dk, a.dg, a.dbeta, ctot);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t nitems = (int64_t)a.nseq * a.H * DK;
-        hipLaunchKernelGGL((bwd_dg_carry_kernel<DV>), dim3((unsigned)((nitems + BWD_THREADS - 1) / BWD_THREADS)),
-                           dim3(BWD_THREADS), 0, st, a.cu, a.nseq, a.H, DK, a.dfinal, sfin, ctot);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_dg_apply_kernel<DK>), dim3((unsigned)items), dim3(BWD_THREADS), 0, st, a.cu, a.nseq,
-                           a.H, ctot, a.dg);
+                           a.cu, a.nseq, a.H, sck, hck, dbuf, ebuf, mats, a.dq, a.dk, a.dg, a.dbeta);
         e = hipGetLastError();
     }
     return e;
@@ -991,9 +937,8 @@ hipError_t launch_backward(const BackwardArgs &a) {
 
 int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv) {
     const int64_t slots = chunk_slots(N, nseq);
-    // S and S^ checkpoints, Delta and E, the final state, chunk matrices, chunk log-decay totals
-    return 2 * slots * H * (int64_t)dk * dv + 2 * slots * H * 16 * (int64_t)dv + (int64_t)nseq * H * dk * dv +
-           slots * H * 4 * 256 + slots * H * (int64_t)dk;
+    // S and S^ checkpoints, Delta and E, chunk matrices
+    return 2 * slots * H * (int64_t)dk * dv + 2 * slots * H * 16 * (int64_t)dv + slots * H * 4 * 256;
 }
 
 }  // namespace kda

@@ -152,8 +152,7 @@ kda_status kda_inter_chunk(const void *q, const void *k, const void *v,
  *   d_beta: fp32 [N, H];  all written in full (d_init if not NULL).
  *   workspace: kda_prefill_backward_workspace_bytes(...) bytes, 16-byte aligned
  *   (per chunk slot and head: the state and its adjoint, dk x dv fp32 each,
- *   two 16 x dv blocks, four 16 x 16 chunk matrices and dk chunk totals; plus the
- *   final states). */
+ *   two 16 x dv blocks and four 16 x 16 chunk matrices). */
 size_t kda_prefill_backward_workspace_bytes(int64_t total_tokens, int32_t nseq,
                                             int32_t H, int32_t dk, int32_t dv,
                                             kda_dtype dt);

@@ -198,8 +198,7 @@ def test_layer_passes_reject_too_many_rows(lib):
 def test_backward_workspace_and_arguments(lib):
     nb = lib.kda_prefill_backward_workspace_bytes(64, 2, 3, 16, 32, 1)
     slots = 64 // 16 + 2
-    assert nb == 4 * (2 * slots * 3 * 16 * 32 + 2 * slots * 3 * 16 * 32 + 2 * 3 * 16 * 32 + slots * 3 * 4 * 256
-                      + slots * 3 * 16)
+    assert nb == 4 * (2 * slots * 3 * 16 * 32 + 2 * slots * 3 * 16 * 32 + slots * 3 * 4 * 256)
     assert lib.kda_prefill_backward_workspace_bytes(64, 0, 3, 16, 32, 1) == 0
     f = lib.kda_prefill_backward
     # q k v g b init cu nseq N H dk dv dt dO dF dq dk dv dg db dinit ws wsb stream

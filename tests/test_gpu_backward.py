@@ -12,10 +12,9 @@ from parity import assert_close, say
 pytestmark = pytest.mark.gpu
 
 # fp32 arithmetic throughout (inputs of either dtype are exact in it): the fp32 bar, except for
-# the log-decay gradient, a reverse cumulative sum over the sequence of per-token increments
-# larger than their sum (they partly cancel), whose fp32 error grows with the length (measured
-# up to 3.1e-5 RMS at 2048 tokens): 1e-4.
-TOLS = {"dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "dlog_alpha": 1e-4, "dbeta": 1e-5, "dinit": 1e-5}
+# the log-decay gradient, a sum of per-token increments larger than the result (they partly
+# cancel), so its error relative to its own RMS is the largest (measured up to 1.4e-5): 5e-5.
+TOLS = {"dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "dlog_alpha": 5e-5, "dbeta": 1e-5, "dinit": 1e-5}
 NAMES = tuple(TOLS)
 
 
@@ -37,7 +36,7 @@ def _case(dev, seqlens, H, dk, dv, dtype, seed, init=True, dfinal=True, gate="ne
     return x, d_o, S0, dF
 
 
-def _check(dev, x, d_o, S0, dF, heads=None):
+def _check(dev, x, d_o, S0, dF, heads=None, tols=TOLS):
     got = kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, x["cu_seqlens"], S0, dF)
     torch.cuda.synchronize()
     sel = (lambda t: t) if heads is None else (lambda t: t[:, heads])
@@ -46,7 +45,7 @@ def _check(dev, x, d_o, S0, dF, heads=None):
                           cu_seqlens=x["cu_seqlens"].cpu(), init_state=None if S0 is None else sel(S0).cpu(),
                           dfinal=None if dF is None else sel(dF).cpu())
     for n in NAMES:
-        assert_close(sel(got[n]), ref[n], TOLS[n], n)
+        assert_close(sel(got[n]), ref[n], tols[n], n)
     return got
 
 
@@ -112,3 +111,33 @@ def test_backward_batched_workload_sampled_heads(dev):
     dF = torch.randn((w.nseq, w.H, w.dk, w.dv), generator=gen, device=dev)
     say("  case: backward B=4 T=2048 H=8 d=128, heads [1, 6]")
     _check(dev, x, d_o, None, dF, heads=[1, 6])
+
+
+# A 65,536-token sequence runs the fp32 recurrences through 4,096 chunk steps each way, and
+# the largest deviation over 16.8 M values of a gradient grows past the short cases' 1e-5
+# (measured 1.3e-5 for dv, 1.4e-5 for dlog_alpha): 5e-5 for every gradient here, still far
+# below the 1e-2 bar stated for bf16 inputs.
+TOLS_LONG = {n: 5e-5 for n in NAMES}
+
+
+def test_backward_k3_layer_sampled_heads(dev):
+    """The K3 layer's shape (B=1, 65,536 tokens, H=96, d=128, bf16): the whole backward on the
+    GPU in the launch configuration the benchmark times (four slice waves per workgroup) and
+    with the log-decay carry over 4,096 chunks; the oracle on 2 sampled heads."""
+    w = workloads.workload(3)
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    d_o = torch.randn((w.total_tokens, w.H, w.dv), generator=gen, device=dev)
+    dF = torch.randn((w.nseq, w.H, w.dk, w.dv), generator=gen, device=dev)
+    say("  case: backward B=1 T=65536 H=96 d=128, heads [5, 77]")
+    _check(dev, x, d_o, None, dF, heads=[5, 77], tols=TOLS_LONG)
+
+
+def test_backward_is_deterministic(dev):
+    """No atomics anywhere: two calls on the same inputs agree bit for bit."""
+    x, d_o, S0, dF = _case(dev, [300, 45, 1], 24, 128, 128, torch.bfloat16, seed=21)
+    runs = [kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, x["cu_seqlens"], S0,
+                                     dF) for _ in range(2)]
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(runs[0][n], runs[1][n]), f"{n} differs between two identical calls"
