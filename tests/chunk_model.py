@@ -61,7 +61,7 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, init_state=None, chunk=C, keep=Fa
     return (o, fin, kept) if keep else (o, fin)
 
 
-def backward(q, k, v, g, beta, dO, cu_seqlens=None, init_state=None, dfinal=None, chunk=C):
+def backward(q, k, v, g, beta, dO, cu_seqlens=None, init_state=None, dfinal=None, chunk=C, dg_form="checkpoint"):
     """Gradients in chunk form (the algebra of the GPU backward), same outputs as the oracle's
     reverse mode.  Per chunk with incoming state S0, its Delta, and the adjoint S^ of the
     state after the chunk (dO of later chunks and dfinal included):
@@ -73,7 +73,13 @@ def backward(q, k, v, g, beta, dO, cu_seqlens=None, init_state=None, dfinal=None
         b  = diag(beta) e^{G} (.) (E S0^T + stril(E Delta^T) K-)
         dK = a - b,   U = K+ S0 + stril(K+ K-^T) Delta,   dbeta_r = eps_r . (v_r - u_r)
         dg_t = rowsum(dfinal (.) S_T) + sum_{s >= t} (q_s (.) dq_s - k_s (.) (a_s + b_s))
+
+    dg_form="scan" evaluates the last line as written (one reverse cumulative sum over the
+    sequence); "checkpoint" (the GPU kernel's form) sums only within the chunk and takes the
+    part from every later token as rowsum(S^ (.) S_tau), S_tau the state after the chunk:
+        rowsum(S^ (.) S_tau) = e^{G_n} (.) rowsum(S^ (.) S0) + sum_r K~_r (.) (Delta S^^T)_r.
     """
+    assert dg_form in ("checkpoint", "scan")
     q, k, v, g, beta, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta, dO))
     N, H, dk = q.shape
     dv = v.shape[2]
@@ -110,8 +116,13 @@ def backward(q, k, v, g, beta, dO, cu_seqlens=None, init_state=None, dfinal=None
                 out["dk"][c0:c1, h] = a - bb
                 out["dv"][c0:c1, h] = dV
                 out["dbeta"][c0:c1, h] = np.sum(E * (v[c0:c1, h] - U), axis=1)
-                incr[c0 - cu[s]:c1 - cu[s]] = q[c0:c1, h] * dQ - k[c0:c1, h] * (a + bb)
+                inc = q[c0:c1, h] * dQ - k[c0:c1, h] * (a + bb)
+                incr[c0 - cu[s]:c1 - cu[s]] = inc
+                if dg_form == "checkpoint":
+                    later = eGn * np.sum(Sh * S0, axis=1) + np.sum(loc["Kt"] * (D @ Sh.T), axis=0)
+                    out["dlog_alpha"][c0:c1, h] = np.cumsum(inc[::-1], axis=0)[::-1] + later[None, :]
                 Sh = eGn[:, None] * Sh + loc["Qp"].T @ Ob - loc["Kp"].T @ dV
             out["dinit"][s, h] = Sh
-            out["dlog_alpha"][cu[s]:cu[s + 1], h] = boundary[None, :] + np.cumsum(incr[::-1], axis=0)[::-1]
+            if dg_form == "scan":
+                out["dlog_alpha"][cu[s]:cu[s + 1], h] = boundary[None, :] + np.cumsum(incr[::-1], axis=0)[::-1]
     return out

@@ -79,9 +79,10 @@ def test_chunked_backward_matches_oracle_reverse_mode(seqlens, init, dfin):
     S0 = rng.standard_normal((len(seqlens), H, dk, dv)) if init else None
     dF = rng.standard_normal((len(seqlens), H, dk, dv)) if dfin else None
     ref = oracle.backward(q, k, v, g, b, dO, cu_seqlens=cu, init_state=S0, dfinal=dF)
-    got = chunk_model.backward(q, k, v, g, b, dO, cu_seqlens=cu, init_state=S0, dfinal=dF)
-    for name in ref:
-        r = ref[name]
-        scale = max(1e-300, float(np.sqrt(np.mean(r * r)))) if r.size else 1.0
-        err = float(np.max(np.abs(got[name] - r))) if r.size else 0.0
-        assert err <= 1e-9 * max(scale, 1.0), f"{name}: max|err| = {err:.3e} (rms {scale:.3e})"
+    for form in ("checkpoint", "scan"):
+        got = chunk_model.backward(q, k, v, g, b, dO, cu_seqlens=cu, init_state=S0, dfinal=dF, dg_form=form)
+        for name in ref:
+            r = ref[name]
+            scale = max(1e-300, float(np.sqrt(np.mean(r * r)))) if r.size else 1.0
+            err = float(np.max(np.abs(got[name] - r))) if r.size else 0.0
+            assert err <= 1e-9 * max(scale, 1.0), f"{form} {name}: max|err| = {err:.3e} (rms {scale:.3e})"
