@@ -143,10 +143,12 @@ kda_status kda_inter_chunk(const void *q, const void *k, const void *v,
  * forward call.  The recurrence (same page, update equation) is differentiated
  * in chunk form: a forward sweep recomputes the state at every chunk start, a
  * reverse sweep carries the state adjoint A (A <- Diag(e^{G_n}) A + Q+^T dO -
- * K+^T dV per chunk), and a parallel pass forms dq, dk, dbeta per chunk; the
- * log-decay gradient is the reverse cumulative sum over each sequence of
- * q (.) dq - k (.) (the two parts of dk's sum), started from
- * rowsum(d_final (.) final_state).  fp32 throughout.
+ * K+^T dV per chunk), and a parallel pass forms dq, dk, dbeta and the log-decay
+ * gradient per chunk.  The log-decay gradient is the reverse cumulative sum over
+ * each sequence of q (.) dq - k (.) (the two parts of dk's sum), started from
+ * rowsum(d_final (.) final_state); each chunk sums its own tokens and reads the
+ * part from all later tokens off its checkpoints, rowsum(A (.) S) with S the
+ * state after the chunk, so no sum runs over a whole sequence.  fp32 throughout.
  *   d_o: fp32 [N, H, dv];  d_final, d_init: fp32 [nseq, H, dk, dv] or NULL;
  *   d_q, d_k, d_log_alpha: fp32 [N, H, dk];  d_v: fp32 [N, H, dv];
  *   d_beta: fp32 [N, H];  all written in full (d_init if not NULL).
