@@ -15,10 +15,12 @@ The JSON line also carries, measured in the same run:
     output-gate epilogue) on the K3 layer shape, and the fused decode step against the
     same operations as separate launches,
   * "backward": the prefill backward on the batched workload and the K3 layer,
+  * "context_parallel": the prefill with every sequence split into R segments (intra-device
+    context parallelism) against the plain prefill,
   * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
 each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|layer|backward|varlen|none]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|layer|backward|cp|varlen|none]
 """
 from __future__ import annotations
 
@@ -520,13 +522,44 @@ def bench_backward(index, torch, kda, workloads, dev, reps: int):
     return res
 
 
+def bench_cp(index, torch, kda, workloads, dev, segments, reps: int):
+    """Intra-device context parallelism (kda_prefill_cp): every sequence in R segments run as
+    independent chains (three recurrence passes and a scan), against kda_prefill on the same
+    inputs."""
+    w = workloads.workload(index)
+    log(f"[bench] generating workload {w.name} for context parallelism")
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    N = w.total_tokens
+    lib = kda.load_library()
+    ws = kda.alloc_workspace(N, w.nseq, w.H, w.dk, w.dv, x["q"].dtype, dev)
+
+    def plain():
+        kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], workspace=ws)
+    res = {"workload": w.name, "ms_prefill": round(_event_ms(torch, plain, reps), 4)}
+    del ws
+    for R in segments:
+        nb = int(lib.kda_prefill_cp_workspace_bytes(N, w.nseq, w.H, w.dk, w.dv, 1, R))
+        wcp = torch.empty(nb // 4, dtype=torch.float32, device=dev)
+
+        def cp():
+            kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], segments=R,
+                               workspace=wcp)
+        ms = _event_ms(torch, cp, reps)
+        res[f"ms_cp_{R}"] = round(ms, 4)
+        res[f"cp_{R}_over_prefill"] = round(ms / res["ms_prefill"], 3)
+        del wcp
+    del x
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    choices=["all", "main", "k3", "decode", "layer", "backward", "varlen", "none"])
+                    choices=["all", "main", "k3", "decode", "layer", "backward", "cp", "varlen", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for scaling hardware byte counters)")
@@ -600,6 +633,10 @@ def main() -> int:
         log("[bench] prefill backward: batched workload and the K3 layer")
         out["backward"] = {"batched": bench_backward(2, torch, kda, workloads, dev, reps=5),
                            "k3_layer": bench_backward(3, torch, kda, workloads, dev, reps=2)}
+    if args.only in ("all", "cp"):
+        log("[bench] intra-device context parallelism: batched workload and the K3 layer")
+        out["context_parallel"] = {"batched": bench_cp(2, torch, kda, workloads, dev, (2, 4, 8), reps=10),
+                                   "k3_layer": bench_cp(3, torch, kda, workloads, dev, (2, 4), reps=2)}
     if args.only in ("all", "layer"):
         log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
         out["layer"] = bench_layer(torch, kda, workloads, dev)

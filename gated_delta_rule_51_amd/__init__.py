@@ -31,6 +31,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE"
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
+           "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
            "kda_gate", "kda_short_conv", "kda_out_norm_gate",
            "kda_status_string", "kda_last_hip_error")
 
@@ -83,6 +84,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill_backward.restype = ctypes.c_int
     lib.kda_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_prefill_cp_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_cp_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int, i32]
+    lib.kda_prefill_cp.restype = ctypes.c_int
+    lib.kda_prefill_cp.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int, i32,
+                                   vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_gate.restype = ctypes.c_int
     lib.kda_gate.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_short_conv.restype = ctypes.c_int
@@ -194,6 +200,35 @@ def kda_prefill(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
     _check(load_library().kda_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
         H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, final_state
+
+
+def kda_prefill_cp(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *, segments: int = 2,
+                   output_final_state: bool = True, o=None, final_state=None, workspace=None,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_prefill with every sequence split into ``segments`` chunk-aligned pieces run as
+    independent chains, their incoming states recovered by a scan (see include/kda.h).
+    Same arguments and results as kda_prefill."""
+    N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    cu = _cu(cu_seqlens, N, q.device)
+    nseq = cu.numel() - 1
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    if init_state is not None and (init_state.dtype != torch.float32 or tuple(init_state.shape) != (nseq, H, dk, dv)
+                                   or not init_state.is_contiguous()):
+        raise ValueError("init_state must be contiguous fp32 [nseq, H, dk, dv]")
+    lib = load_library()
+    if workspace is None:
+        nbytes = int(lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, _dtype_code(q.dtype), int(segments)))
+        if nbytes == 0:
+            raise KDAError(3, "kda_prefill_cp: unsupported shape or segment count")
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    _check(lib.kda_prefill_cp(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
+        H, dk, dv, _dtype_code(q.dtype), int(segments), _ptr(o), _ptr(final_state), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, final_state
 

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libkda_mi355x.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk_local.hip", "inter_chunk.hip", "inter_chunk_ws.hip", "layer.hip", "backward.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk_local.hip", "inter_chunk.hip", "inter_chunk_ws.hip", "layer.hip", "backward.hip",
+           "cp.hip"]
 ARCH = "gfx950"
 # Per-file additions.  chunk_local: matrix-core results in VGPRs (not AGPRs) --
 # every result there is read by the vector ALU next, and the accumulator-register

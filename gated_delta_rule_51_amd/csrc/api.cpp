@@ -31,6 +31,25 @@ kda_status check_common(int32_t nseq, int64_t total_tokens, int32_t H, int32_t d
     return KDA_OK;
 }
 
+// Workspace of kda_prefill_cp: the segments' chunk-local operands, the segment list, and
+// per segment and head S~, M and S_in, each region 256-byte aligned.  0 = invalid.
+constexpr int32_t CP_MAX_SEGMENTS = 64;
+struct CpLayout {
+    size_t cl, cu, st, m, sin, total;
+};
+CpLayout cp_layout(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R) {
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t segs = (size_t)nseq * (size_t)R;
+    CpLayout L;
+    L.cl = 0;
+    L.cu = L.cl + up((size_t)kda::chunk_slots(total_tokens, (int32_t)segs) * H * kda::WS_FLOATS_PER_CHUNK_HEAD * 4);
+    L.st = L.cu + up((segs + 1) * 4);
+    L.m = L.st + up(segs * H * (size_t)dk * dv * 4);
+    L.sin = L.m + up(segs * H * (size_t)dk * dk * 4);
+    L.total = L.sin + up(segs * H * (size_t)dk * dv * 4);
+    return L;
+}
+
 size_t workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H) {
     return static_cast<size_t>(kda::chunk_slots(total_tokens, nseq)) * static_cast<size_t>(H) *
            kda::WS_FLOATS_PER_CHUNK_HEAD * sizeof(float);
@@ -159,6 +178,64 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
     if (st != KDA_OK) return st;
     return kda_inter_chunk(q, k, v, log_alpha, init_state, cu_seqlens, nseq, total_tokens, H, dk,
                            dv, dt, workspace, ws_bytes, o, final_state, stream);
+}
+
+size_t kda_prefill_cp_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv,
+                                      kda_dtype dt, int32_t segments) {
+    if (segments < 1 || segments > CP_MAX_SEGMENTS) return 0;
+    if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    if (check_common((int32_t)((int64_t)nseq * segments), total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    return cp_layout(total_tokens, nseq, H, dk, dv, segments).total;
+}
+
+kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const void *log_alpha, const void *beta,
+                          const float *init_state, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                          int32_t H, int32_t dk, int32_t dv, kda_dtype dt, int32_t segments, float *o,
+                          float *final_state, void *workspace, size_t ws_bytes, void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    if (segments < 1 || segments > CP_MAX_SEGMENTS) return KDA_ERR_SHAPE;
+    const int64_t segs = (int64_t)nseq * segments;
+    if (segs >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    st = check_common((int32_t)segs, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
+    if (st != KDA_OK) return st;
+    if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    const CpLayout L = cp_layout(total_tokens, nseq, H, dk, dv, segments);
+    if (!workspace || ws_bytes < L.total) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    char *w = static_cast<char *>(workspace);
+    float *cl = reinterpret_cast<float *>(w + L.cl), *St = reinterpret_cast<float *>(w + L.st);
+    float *M = reinterpret_cast<float *>(w + L.m), *Sin = reinterpret_cast<float *>(w + L.sin);
+    int32_t *cu_seg = reinterpret_cast<int32_t *>(w + L.cu);
+    const bool bf16 = dt == KDA_BF16;
+    const int32_t ns = (int32_t)segs;
+    hipError_t e = kda::launch_cp_segments(cu_seqlens, nseq, segments, cu_seg, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (total_tokens > 0) {
+        kda::ChunkLocalArgs c{q, k, log_alpha, beta, cu_seg, ns, H, dk, total_tokens, bf16, cl, stream};
+        if ((e = kda::launch_chunk_local(c)) != hipSuccess) return hip_status(e);
+    }
+    // each segment from a zero state: S~ (outputs not written)
+    kda::InterChunkArgs a1{q, k, v, log_alpha, nullptr, cu_seg, ns, H, dk, dv, total_tokens, bf16, cl,
+                           nullptr, St, 0, stream};
+    if ((e = kda::launch_inter_chunk(a1)) != hipSuccess) return hip_status(e);
+    // each segment's transition M: v = 0 from the identity, in place
+    if ((e = kda::launch_cp_identity(M, segs * H, dk, stream)) != hipSuccess) return hip_status(e);
+    kda::InterChunkArgs a2{q, k, nullptr, log_alpha, M, cu_seg, ns, H, dk, dk, total_tokens, bf16, cl,
+                           nullptr, M, 0, stream};
+    if ((e = kda::launch_inter_chunk(a2)) != hipSuccess) return hip_status(e);
+    if ((e = kda::launch_cp_scan(init_state, M, St, Sin, nseq, H, dk, dv, segments, stream)) != hipSuccess)
+        return hip_status(e);
+    // the outputs from the exact incoming states; each segment's final state replaces its S_in
+    kda::InterChunkArgs a3{q, k, v, log_alpha, Sin, cu_seg, ns, H, dk, dv, total_tokens, bf16, cl,
+                           o, Sin, 0, stream};
+    if ((e = kda::launch_inter_chunk(a3)) != hipSuccess) return hip_status(e);
+    if (final_state) e = kda::launch_cp_final(Sin, final_state, nseq, H, dk, dv, segments, stream);
+    return hip_status(e);
 }
 
 kda_status kda_decode_step_fused(const void *q, const void *k, const void *v, const void *gate,

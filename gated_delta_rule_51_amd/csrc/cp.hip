@@ -1,0 +1,159 @@
+// Intra-device context parallelism for the KDA prefill (gfx950): one sequence split
+// into R chunk-aligned segments that run as independent chains, their exact incoming
+// states recovered by a scan.  The algebra is the one the Kimi K3 report digest gives
+// for splitting a sequence across devices ("KDA 컨텍스트 병렬화": each segment's state
+// map is affine, S_out = M S_in + S~, with M the product of the per-token transitions
+// (I - beta k k^T) Diag(alpha)), used here between the compute units of one device
+// ("KDA 알고리즘과 시스템의 공동 설계", intra-device CP).
+//
+// The passes (kda_prefill_cp in api.cpp) reuse the prefill kernels on the segmented
+// sequence list:
+//   1. cp_segments: segment r of sequence s covers its chunks [nc r / R, nc (r+1) / R);
+//   2. chunk_local over the segments (a chunk's T' and A_qk depend only on its tokens, so
+//      one pass serves all three recurrences below);
+//   3. inter_chunk from zero states: each segment's S~ (outputs not written);
+//   4. inter_chunk with v = 0 from the identity (a dk x dk "state"): each segment's M;
+//   5. cp_scan per (sequence, head): S_in,0 = the initial state, S_in,r+1 = M_r S_in,r + S~_r;
+//   6. inter_chunk from the exact S_in,r: the outputs, and each segment's final state in
+//      place of its S_in (the last one is the sequence's, copied out by cp_final).
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+constexpr int CP_THREADS = 256;
+
+__global__ __launch_bounds__(CP_THREADS) void cp_segments_kernel(const int32_t *__restrict__ cu, int32_t nseq,
+                                                                 int32_t R, int32_t *__restrict__ cu_seg) {
+    const int s = blockIdx.x * CP_THREADS + threadIdx.x;
+    if (s > nseq) return;
+    if (s == nseq) {
+        cu_seg[(int64_t)nseq * R] = cu[nseq];
+        return;
+    }
+    const int32_t bos = cu[s], eos = cu[s + 1];
+    const int64_t nc = (eos - bos + 15) / 16;
+    for (int r = 0; r < R; ++r) {
+        const int64_t c0 = nc * r / R;
+        const int64_t t = bos + 16 * c0;
+        cu_seg[(int64_t)s * R + r] = (int32_t)(t < eos ? t : eos);
+    }
+}
+
+__global__ __launch_bounds__(CP_THREADS) void cp_identity_kernel(float *__restrict__ M, int64_t total, int32_t dk) {
+    const int64_t i = (int64_t)blockIdx.x * CP_THREADS + threadIdx.x;
+    if (i >= total) return;
+    const int64_t e = i % ((int64_t)dk * dk);
+    M[i] = (e / dk == e % dk) ? 1.f : 0.f;
+}
+
+// One workgroup of 16 waves per (sequence, head); the waves share the 16x16 tiles of each
+// product M_r S_in,r on the fp32 matrix cores.  The current state stays in LDS (two
+// buffers, rows padded by 4 floats), so each step reads only M_r and S~_r from memory; every
+// S_in,r is also written out for the last recurrence pass.
+constexpr int SCAN_THREADS = 1024;
+
+template <int DK, int DV>
+__global__ __launch_bounds__(SCAN_THREADS) void cp_scan_kernel(const float *__restrict__ init,
+                                                               const float *__restrict__ M,
+                                                               const float *__restrict__ St, float *__restrict__ Sin,
+                                                               int32_t H, int32_t R) {
+    constexpr int LD = DV + 4;
+    __shared__ __attribute__((aligned(16))) float S[2][DK * LD];
+    const int s = blockIdx.x / H, h = blockIdx.x % H;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, gq = lane / 16, m = lane % 16;
+    auto seg = [&](int r) { return ((int64_t)s * R + r) * H + h; };
+    {
+        float *S0 = Sin + seg(0) * DK * DV;
+        const float *I0 = init ? init + ((int64_t)s * H + h) * DK * DV : nullptr;
+        for (int i = tid; i < DK * DV; i += SCAN_THREADS) {
+            const float x = I0 ? I0[i] : 0.f;
+            S0[i] = x;
+            S[0][(i / DV) * LD + i % DV] = x;
+        }
+    }
+    __syncthreads();
+    for (int r = 0; r + 1 < R; ++r) {
+        const float *Mr = M + seg(r) * DK * DK, *Tr = St + seg(r) * DK * DV;
+        const float *Sr = S[r & 1];
+        float *Sl = S[(r + 1) & 1];
+        float *Sn = Sin + seg(r + 1) * DK * DV;
+        for (int t = wave; t < (DK / 16) * (DV / 16); t += SCAN_THREADS / 64) {
+            const int I = t / (DV / 16), J = t % (DV / 16);
+            f32x4 c = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; ++kb) {
+                // A operand: rows 16I + m of M, columns 16kb + 4g ..; B operand: rows 16kb + 4g + j
+                // of S, column 16J + m
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(Mr + (16 * I + m) * DK + 16 * kb + 4 * gq);
+                f32x4 b;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = Sr[(16 * kb + 4 * gq + j) * LD + 16 * J + m];
+                c = mma_f32_k16(a, b, c);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * I + 4 * gq + j, col = 16 * J + m;
+                const float x = c[j] + Tr[row * DV + col];
+                Sn[row * DV + col] = x;
+                Sl[row * LD + col] = x;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(CP_THREADS) void cp_final_kernel(const float *__restrict__ Sin, float *__restrict__ fin,
+                                                              int32_t nseq, int32_t H, int32_t R, int64_t per_head) {
+    const int64_t i = (int64_t)blockIdx.x * CP_THREADS + threadIdx.x;
+    if (i >= (int64_t)nseq * H * per_head) return;
+    const int64_t sh = i / per_head, e = i - sh * per_head;
+    const int64_t s = sh / H, h = sh - s * H;
+    fin[i] = Sin[((s * R + R - 1) * H + h) * per_head + e];
+}
+
+static unsigned blocks_for(int64_t n) { return (unsigned)((n + CP_THREADS - 1) / CP_THREADS); }
+
+hipError_t launch_cp_segments(const int32_t *cu, int32_t nseq, int32_t R, int32_t *cu_seg, void *stream) {
+    hipLaunchKernelGGL(cp_segments_kernel, dim3(blocks_for((int64_t)nseq + 1)), dim3(CP_THREADS), 0,
+                       (hipStream_t)stream, cu, nseq, R, cu_seg);
+    return hipGetLastError();
+}
+
+hipError_t launch_cp_identity(float *M, int64_t n_mats, int32_t dk, void *stream) {
+    const int64_t total = n_mats * dk * dk;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(cp_identity_kernel, dim3(blocks_for(total)), dim3(CP_THREADS), 0, (hipStream_t)stream, M,
+                       total, dk);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_scan_t(const float *init, const float *M, const float *St, float *Sin, int32_t nseq,
+                                int32_t H, int32_t R, void *stream) {
+    hipLaunchKernelGGL((cp_scan_kernel<DK, DV>), dim3((unsigned)((int64_t)nseq * H)), dim3(SCAN_THREADS), 0,
+                       (hipStream_t)stream, init, M, St, Sin, H, R);
+    return hipGetLastError();
+}
+
+hipError_t launch_cp_scan(const float *init, const float *M, const float *St, float *Sin, int32_t nseq, int32_t H,
+                          int32_t dk, int32_t dv, int32_t R, void *stream) {
+#define KDA_CP_CASE(DKV, DVV) \
+    if (dk == DKV && dv == DVV) return launch_scan_t<DKV, DVV>(init, M, St, Sin, nseq, H, R, stream);
+#define KDA_CP_ROW(DKV) KDA_CP_CASE(DKV, 16) KDA_CP_CASE(DKV, 32) KDA_CP_CASE(DKV, 64) KDA_CP_CASE(DKV, 128)
+    KDA_CP_ROW(16) KDA_CP_ROW(32) KDA_CP_ROW(64) KDA_CP_ROW(128)
+#undef KDA_CP_ROW
+#undef KDA_CP_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cp_final(const float *Sin, float *fin, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R,
+                           void *stream) {
+    const int64_t per_head = (int64_t)dk * dv, total = (int64_t)nseq * H * per_head;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(cp_final_kernel, dim3(blocks_for(total)), dim3(CP_THREADS), 0, (hipStream_t)stream, Sin, fin,
+                       nseq, H, R, per_head);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -191,10 +191,13 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
     // Buffer resource of chunk c for this head: base = the head's slice of the
     // chunk's first token.  Rows at or past the chunk length are parked at an
     // out-of-bounds offset, so their loads return zeros and stores are dropped.
+    // (a NULL base -- v in a pass that only propagates the state's transition -- is an
+    // empty resource: its loads return zeros)
     auto rsrc_in = [&](const T *base, int c, int d) {
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(c);
-        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB);
+        return make_rsrc(base ? base + (t0 * H + h) * d : base,
+                         base ? (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB : 0u);
     };
     // Look-ahead loads past the last chunk re-read the last chunk (results unused).
     auto clampc = [&](int c) { return c < nc ? c : nc - 1; };
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
         }
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(c);
-        const rsrc_t ro = make_rsrc(o + (t0 * H + h) * DV, (uint32_t)n * rowO);
+        const rsrc_t ro = make_rsrc(o ? o + (t0 * H + h) * DV : o, o ? (uint32_t)n * rowO : 0u);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int t = 4 * g4 + jj;

@@ -120,14 +120,16 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
         return __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left < 16 ? left : 16));
     };
     // Buffer resource over chunk c of this head: base = the chunk's first token,
-    // length = its rows (an empty resource past the end).
+    // length = its rows (an empty resource past the end, and for a NULL v or o: v reads
+    // as zeros, o is not written).
     auto rsrc_in = [&](const __bf16 *base, int c, int d) {
         const int64_t t0 = bos + 16 * (int64_t)c;
-        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)chunk_len(c) * (uint32_t)H * d * EB);
+        return make_rsrc(base ? base + (t0 * H + h) * d : base,
+                         base ? (uint32_t)chunk_len(c) * (uint32_t)H * d * EB : 0u);
     };
     auto rsrc_out = [&](int c) {
         const int64_t t0 = bos + 16 * (int64_t)c;
-        return make_rsrc(o + (t0 * H + h) * DV, (uint32_t)chunk_len(c) * rowO);
+        return make_rsrc(o ? o + (t0 * H + h) * DV : o, o ? (uint32_t)chunk_len(c) * rowO : 0u);
     };
     auto rsrc_ws = [&](int c) {
         return make_rsrc(ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD,

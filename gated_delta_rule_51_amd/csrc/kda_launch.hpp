@@ -131,6 +131,14 @@ struct BackwardArgs {
 hipError_t launch_backward(const BackwardArgs &a);
 int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv);
 
+// Intra-device context parallelism (cp.hip): the small kernels around the prefill passes.
+hipError_t launch_cp_segments(const int32_t *cu, int32_t nseq, int32_t R, int32_t *cu_seg, void *stream);
+hipError_t launch_cp_identity(float *M, int64_t n_mats, int32_t dk, void *stream);
+hipError_t launch_cp_scan(const float *init, const float *M, const float *St, float *Sin, int32_t nseq, int32_t H,
+                          int32_t dk, int32_t dv, int32_t R, void *stream);
+hipError_t launch_cp_final(const float *Sin, float *fin, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R,
+                           void *stream);
+
 hipError_t launch_gate(const GateArgs &a);
 hipError_t launch_short_conv(const ShortConvArgs &a);
 hipError_t launch_out_norm_gate(const OutNormGateArgs &a);

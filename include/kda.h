@@ -137,6 +137,31 @@ kda_status kda_inter_chunk(const void *q, const void *k, const void *v,
                            size_t workspace_bytes, float *o,
                            float *final_state, void *stream);
 
+/* kda_prefill with intra-device context parallelism: every sequence is split into
+ * `segments` chunk-aligned pieces (segment r covers chunks [nc r / R, nc (r+1) / R)
+ * of a sequence of nc chunks) that run as independent chains, and the exact state
+ * entering each piece is recovered by a scan over the pieces' affine state maps
+ * S_out = M S_in + S~ (Kimi K3 report digest, context parallelism of KDA: the same
+ * algebra as across devices, here between the compute units of one GPU).  Three
+ * recurrence passes over the pieces (S~ from zero states; M from the identity with
+ * v = 0; the outputs from the exact states) and one chunk-local pass.  Same inputs,
+ * outputs and precision as kda_prefill; segments = 1 reduces to it (at three times the
+ * recurrence work).
+ *   segments: 1 .. 64.
+ *   workspace: kda_prefill_cp_workspace_bytes(...) bytes, 16-byte aligned (chunk-local
+ *   operands of the pieces; per piece and head S~, S_in (dk x dv) and M (dk x dk), fp32). */
+size_t kda_prefill_cp_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
+                                      int32_t dk, int32_t dv, kda_dtype dt,
+                                      int32_t segments);
+
+kda_status kda_prefill_cp(const void *q, const void *k, const void *v,
+                          const void *log_alpha, const void *beta,
+                          const float *init_state, const int32_t *cu_seqlens,
+                          int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk,
+                          int32_t dv, kda_dtype dt, int32_t segments, float *o,
+                          float *final_state, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 /* Backward pass of kda_prefill (for training): the gradients of a loss L with
  * dL/do = d_o and dL/d(final_state) = d_final (NULL = zero) with respect to q,
  * k, v, log_alpha, beta and the initial state, for the same inputs as the

@@ -217,3 +217,34 @@ def test_backward_workspace_and_arguments(lib):
     assert call(a22=16) == 5            # workspace too small
     assert call(a10=24) == 4            # dk
     assert call(a7=0) == 3              # nseq
+
+
+def test_prefill_cp_workspace_and_arguments(lib):
+    # per segment and head: S~ and S_in (dk x dv) and M (dk x dk); the chunk-local operands of
+    # the segments; the segment list; each region 256-byte aligned
+    N, nseq, H, dk, dv, R = 64, 2, 3, 16, 32, 4
+    up = lambda x: (x + 255) // 256 * 256
+    segs = nseq * R
+    cl = (N // 16 + segs) * H * 512 * 4
+    want = up(cl) + up((segs + 1) * 4) + 2 * up(segs * H * dk * dv * 4) + up(segs * H * dk * dk * 4)
+    assert lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, 1, R) == want
+    assert lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, 1, 0) == 0    # segments < 1
+    assert lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, 1, 65) == 0   # segments > 64
+    f = lib.kda_prefill_cp
+    # q k v g b init cu nseq N H dk dv dt R o fin ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 64, 1, 16, 16, 1, 2, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a13=0) == 3             # no segments
+    assert call(a13=65) == 3            # too many segments
+    assert call(a14=None) == 1          # o missing
+    assert call(a4=None) == 1           # beta missing
+    assert call(a16=None) == 5          # no workspace
+    assert call(a17=16) == 5            # workspace too small
+    assert call(a10=24) == 4            # dk
+    assert call(a12=7) == 4             # dtype
+    assert call(a15=FAKE + 4) == 2      # final_state misaligned

@@ -1,0 +1,73 @@
+"""GPU parity of the context-parallel prefill (kda_prefill_cp, through the C ABI): every
+sequence split into R chunk-aligned segments run as independent chains, the incoming states
+recovered by a scan over the segments' affine maps.  Against the fp64 oracle at the prefill's
+bar (1e-2 RMS for bf16 inputs, 1e-5 for fp32), and against kda_prefill on the same inputs."""
+import pytest
+import torch
+
+import gated_delta_rule_51_amd as kda
+import workloads
+from parity import TOL, assert_close, oracle_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    kda.load_library()
+    return torch.device("cuda:0")
+
+
+def _cp_case(dev, seqlens, H, dk, dv, dtype, R, seed=0, init=True, heads=None):
+    w = workloads.custom(seqlens, H, dk, dv, dtype, "neg_softplus")
+    x = workloads.prefill_inputs(w, device=dev, seed=seed)
+    S0 = workloads.random_state(len(seqlens), H, dk, dv, device=dev, seed=seed) if init else None
+    say(f"  case: cp R={R} seqlens={list(seqlens)[:6]} H={H} dk={dk} dv={dv} {dtype} init={init}")
+    o, fin = kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], S0, segments=R)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x, S0, heads=heads)
+    if heads is not None:
+        o, fin = o[:, heads], fin[:, heads]
+    assert_close(o, o_ref, TOL[dtype], "o")
+    assert_close(fin, f_ref, TOL[dtype], "final_state")
+    return x, S0, o, fin
+
+
+# Segments shorter than a chunk, sequences shorter than R chunks (empty segments), an empty
+# sequence, ragged tails; R = 1 (the plain recurrence run three times) up to 7.
+@pytest.mark.parametrize("dtype,dk,dv,R", [(torch.float32, 16, 16, 3), (torch.float32, 32, 64, 1),
+                                           (torch.float32, 64, 16, 7), (torch.bfloat16, 128, 128, 4),
+                                           (torch.bfloat16, 32, 128, 2), (torch.bfloat16, 128, 64, 5)])
+def test_cp_matches_oracle(dev, dtype, dk, dv, R):
+    _cp_case(dev, [200, 17, 0, 33, 1, 96], 2, dk, dv, dtype, R, seed=dk + dv + R)
+
+
+def test_cp_without_initial_state(dev):
+    _cp_case(dev, [129, 64], 3, 128, 128, torch.bfloat16, 4, seed=9, init=False)
+
+
+def test_cp_agrees_with_prefill(dev):
+    """The same inputs through kda_prefill and kda_prefill_cp (R = 4): the two differ only by
+    the order of fp32 rounding in the state, far inside the bf16 bar."""
+    w = workloads.custom([500, 260, 31], 4, 128, 128, torch.bfloat16, "neg_softplus")
+    x = workloads.prefill_inputs(w, device=dev, seed=5)
+    S0 = workloads.random_state(3, 4, 128, 128, device=dev, seed=5)
+    o1, f1 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], S0)
+    o2, f2 = kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], S0, segments=4)
+    torch.cuda.synchronize()
+    assert_close(o2, o1.double().cpu().numpy(), 1e-3, "o (cp vs prefill)")
+    assert_close(f2, f1.double().cpu().numpy(), 1e-3, "final_state (cp vs prefill)")
+
+
+def test_cp_batched_workload_sampled_heads(dev):
+    """The batched workload's shape (B=4 x 2048 tokens, H=8, d=128, bf16) with R = 4 segments
+    per sequence (128 chains instead of 32), the oracle on 2 sampled heads."""
+    w = workloads.workload(2)
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    say("  case: cp R=4, B=4 T=2048 H=8 d=128, heads [2, 5]")
+    o, fin = kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], segments=4)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x, None, heads=[2, 5])
+    assert_close(o[:, [2, 5]], o_ref, TOL[torch.bfloat16], "o")
+    assert_close(fin[:, [2, 5]], f_ref, TOL[torch.bfloat16], "final_state")
