@@ -191,13 +191,16 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
     // Buffer resource of chunk c for this head: base = the head's slice of the
     // chunk's first token.  Rows at or past the chunk length are parked at an
     // out-of-bounds offset, so their loads return zeros and stores are dropped.
-    // (a NULL base -- v in a pass that only propagates the state's transition -- is an
-    // empty resource: its loads return zeros)
-    auto rsrc_in = [&](const T *base, int c, int d) {
+    // A NULL v (a pass that only propagates the state's transition) reads as zeros and a
+    // NULL o is not written: their resources get length 0 (on q as a stand-in base),
+    // decided once here rather than by a null test at each resource.
+    const uint32_t v_on = v ? 1u : 0u, o_on = o ? 1u : 0u;
+    const T *vb = v ? v : q;
+    float *obase = o ? o : reinterpret_cast<float *>(const_cast<T *>(q));
+    auto rsrc_in = [&](const T *base, int c, int d, uint32_t on) {
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(c);
-        return make_rsrc(base ? base + (t0 * H + h) * d : base,
-                         base ? (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB : 0u);
+        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)(n > 0 ? n : 0) * (uint32_t)H * d * EB * on);
     };
     // Look-ahead loads past the last chunk re-read the last chunk (results unused).
     auto clampc = [&](int c) { return c < nc ? c : nc - 1; };
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
     };
     auto load_units = [&](Units &U, int c) {
         const int n = chunk_len(c);
-        const rsrc_t rq = rsrc_in(q, c, DK), rk = rsrc_in(k, c, DK), rg = rsrc_in(g, c, DK);
+        const rsrc_t rq = rsrc_in(q, c, DK, 1u), rk = rsrc_in(k, c, DK, 1u), rg = rsrc_in(g, c, DK, 1u);
 #pragma unroll
         for (int ui = 0; ui < UPT; ++ui) {
             const int u = tid + ui * NT;
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
             }
         }
         {
-            const rsrc_t rv = rsrc_in(v, c, DV);
+            const rsrc_t rv = rsrc_in(vb, c, DV, v_on);
             const int t = tid / (VW / 4), a = tid % (VW / 4);
             const uint32_t off = t < n ? t * rowV + (split * VW + 4 * a) * EB : OOB;
             if constexpr (F32) U.v = buf_load_u32x4(rv, off);
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
         }
         const int64_t t0 = bos + 16 * (int64_t)c;
         const int n = chunk_len(c);
-        const rsrc_t ro = make_rsrc(o ? o + (t0 * H + h) * DV : o, o ? (uint32_t)n * rowO : 0u);
+        const rsrc_t ro = make_rsrc(obase + (t0 * H + h) * DV, (uint32_t)n * rowO * o_on);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int t = 4 * g4 + jj;

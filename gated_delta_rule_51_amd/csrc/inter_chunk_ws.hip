@@ -120,16 +120,20 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
         return __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left < 16 ? left : 16));
     };
     // Buffer resource over chunk c of this head: base = the chunk's first token,
-    // length = its rows (an empty resource past the end, and for a NULL v or o: v reads
-    // as zeros, o is not written).
-    auto rsrc_in = [&](const __bf16 *base, int c, int d) {
+    // length = its rows (an empty resource past the end).  A NULL v reads as zeros and a
+    // NULL o is not written: their resources get length 0 (on q as a stand-in base),
+    // decided once here -- a null test at each resource would compile to branches that
+    // split the chunk loop.
+    const uint32_t v_on = v ? 1u : 0u, o_on = o ? 1u : 0u;
+    const __bf16 *vb = v ? v : q;
+    float *ob = o ? o : reinterpret_cast<float *>(const_cast<__bf16 *>(q));
+    auto rsrc_in = [&](const __bf16 *base, int c, int d, uint32_t on) {
         const int64_t t0 = bos + 16 * (int64_t)c;
-        return make_rsrc(base ? base + (t0 * H + h) * d : base,
-                         base ? (uint32_t)chunk_len(c) * (uint32_t)H * d * EB : 0u);
+        return make_rsrc(base + (t0 * H + h) * d, (uint32_t)chunk_len(c) * (uint32_t)H * d * EB * on);
     };
     auto rsrc_out = [&](int c) {
         const int64_t t0 = bos + 16 * (int64_t)c;
-        return make_rsrc(o ? o + (t0 * H + h) * DV : o, o ? (uint32_t)chunk_len(c) * rowO : 0u);
+        return make_rsrc(ob + (t0 * H + h) * DV, (uint32_t)chunk_len(c) * rowO * o_on);
     };
     auto rsrc_ws = [&](int c) {
         return make_rsrc(ws + ((slot0 + c) * H + h) * (int64_t)WS_FLOATS_PER_CHUNK_HEAD,
@@ -172,7 +176,7 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                 const rsrc_t rw = rsrc_ws(c);
                 X.tp = buf_load_u32x4(rw, lane * 16u);
                 X.aq = buf_load_u32x4(rw, (64 + lane) * 16u);
-                const rsrc_t rv = rsrc_in(v, c, DV);
+                const rsrc_t rv = rsrc_in(vb, c, DV, v_on);
                 X.v = buf_load_u32x2(rv, l16 * rowV + (col0 + 4 * g4) * EB);
             };
             auto advance = [&](int ob, const CIn &X, int c) {
@@ -316,7 +320,7 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
             u32x4 d[3][NPW];  // q, k, g
         };
         auto pload = [&](PIn &R, int c) {
-            const rsrc_t rq = rsrc_in(q, c, DK), rk = rsrc_in(k, c, DK), rg = rsrc_in(g, c, DK);
+            const rsrc_t rq = rsrc_in(q, c, DK, 1u), rk = rsrc_in(k, c, DK, 1u), rg = rsrc_in(g, c, DK, 1u);
 #pragma unroll
             for (int pp = 0; pp < NPW; ++pp) {
                 const uint32_t off = (lane >> 2) * rowK + 64u * (pair0 + pp) + 16u * (lane & 3);
