@@ -71,3 +71,17 @@ def test_cp_batched_workload_sampled_heads(dev):
     o_ref, f_ref = oracle_prefill(x, None, heads=[2, 5])
     assert_close(o[:, [2, 5]], o_ref, TOL[torch.bfloat16], "o")
     assert_close(fin[:, [2, 5]], f_ref, TOL[torch.bfloat16], "final_state")
+
+
+def test_cp_no_tokens(dev):
+    """N = 0: every segment is empty, so the final states are the initial ones exactly."""
+    H, dk, dv = 2, 32, 64
+    e = torch.empty((0, H, dk), dtype=torch.bfloat16, device=dev)
+    ev = torch.empty((0, H, dv), dtype=torch.bfloat16, device=dev)
+    eb = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(4, dtype=torch.int32, device=dev)
+    S0 = torch.randn((3, H, dk, dv), device=dev)
+    o, fin = kda.kda_prefill_cp(e, e, ev, e, eb, cu, S0, segments=3)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, dv)
+    assert torch.equal(fin, S0)
