@@ -284,23 +284,33 @@ __global__ __launch_bounds__(64 * MATS_WAVES) void bwd_mats_kernel(
 // register sets are fixed); a look-ahead past either end of the sequence reads empty
 // resources, so the loop body has no branch.  The forward sweep walks the chunks in
 // order, the adjoint sweep in reverse; both count iterations i = 0, 1, ...
-template <int DK, bool ADJ>
+template <int DK, bool ADJ, bool TRA = true>
 struct SweepSet {
     float rows[16][DK + 4];       // forward: K+ rows;  adjoint: K~ rows
-    float trA[DK][20];            // forward: K~^T;     adjoint: Q+^T
+    float trA[TRA ? DK : 1][20];  // forward: K~^T;     adjoint: Q+^T (when the slice waves form Q+^T dO)
     float trB[ADJ ? DK : 1][20];  // adjoint: K+^T
     float gam[DK];                // e^{G_n}
 };
 
-template <int DK, int NP, bool ADJ, typename T>
+// Adjoint sweep with NQ <= 2 slice waves: the producers also form Q+^T dO for every slice
+// (it does not depend on the adjoint, so it is off the slice waves' chain) and hand it over
+// as accumulator-layout tiles: t[slice][block][lane].
+template <int DK, int NQ>
+struct QoSet {
+    f32x4 t[NQ][DK / 16][64];
+};
+
+template <int DK, int NP, bool ADJ, typename T, int NQ = 0>
 struct RawBlocks {
     // producer w builds channel blocks w, w + NP, ... (a block index past NB reads an
-    // empty resource and writes nothing)
+    // empty resource and writes nothing); with NQ > 0 it also forms Q+^T dO of its blocks
+    // for the NQ slices of the workgroup (dO slices loaded with the rest)
     static constexpr int NB = DK / 16, NBW = (NB + NP - 1) / NP;
     Row4Raw<T> rg[NBW], rk[NBW], rq[NBW];
+    u32x4 ro[NQ > 0 ? NQ : 1];
 
     __device__ __forceinline__ void load(const T *q, const T *k, const T *g, int64_t t0, int n, int32_t H, int h,
-                                         int wave, int lane) {
+                                         int wave, int lane, const float *dO = nullptr, int DV = 0, int col0 = 0) {
         const int m = lane % 16, gq = lane / 16;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
@@ -311,9 +321,17 @@ struct RawBlocks {
             rk[i] = load_row4_raw<T>(chunk_rsrc(k, t0, nb, H, h, DK), m, H, DK, c0);
             if (ADJ) rq[i] = load_row4_raw<T>(chunk_rsrc(q, t0, nb, H, h, DK), m, H, DK, c0);
         }
+        if constexpr (NQ > 0) {
+            const rsrc_t rO = chunk_rsrc(dO, t0, n, H, h, DV);
+#pragma unroll
+            for (int sl = 0; sl < NQ; ++sl) ro[sl] = load_col4_raw<float>(rO, gq, H, DV, col0 + 16 * sl + m);
+        }
     }
 
-    __device__ __forceinline__ void build(SweepSet<DK, ADJ> &P, int wave, int lane) const {
+    // tsc: this producer's 16 x 20 LDS scratch (NQ > 0: the transpose of its Q+ block)
+    template <bool TRA>
+    __device__ __forceinline__ void build(SweepSet<DK, ADJ, TRA> &P, int wave, int lane, QoSet<DK, (NQ > 0 ? NQ : 1)> *Qo,
+                                          float (*tsc)[20], int32_t H, int DV, int col0) const {
         const int m = lane % 16, gq = lane / 16;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
@@ -325,10 +343,22 @@ struct RawBlocks {
             *reinterpret_cast<f32x4 *>(&P.rows[m][c0]) = ADJ ? o.kt : o.kp;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                P.trA[c0 + j][m] = ADJ ? o.qp[j] : o.kt[j];
+                if constexpr (TRA) P.trA[c0 + j][m] = ADJ ? o.qp[j] : o.kt[j];
                 if (ADJ) P.trB[c0 + j][m] = o.kp[j];
             }
             if (m == 15) *reinterpret_cast<f32x4 *>(&P.gam[c0]) = o.egn;
+            if constexpr (NQ > 0) {
+                // Q+ of this block transposed through the scratch (this wave's own writes and
+                // reads, which the LDS performs in order), then one 16-long product per slice:
+                // (Q+^T dO)[16b + r][col] = sum_t Q+[t][16b + r] dO[t][col]
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tsc[4 * gq + j][m] = o.qp[j];
+                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&tsc[m][4 * gq]);
+#pragma unroll
+                for (int sl = 0; sl < NQ; ++sl)
+                    Qo->t[sl][b][lane] = mma_f32_k16(qa, widen_col4<float>(ro[sl], gq, H, DV, col0 + 16 * sl + m),
+                                                     zero4());
+            }
         }
     }
 };
@@ -392,24 +422,26 @@ __device__ __forceinline__ void unrolled_chunks(int nc, F &&body) {
     if (i < nc) body(i, Par<0>{});
 }
 
-template <int DK, int NP, bool ADJ, typename T>
-__device__ __forceinline__ void sweep_producer(SweepSet<DK, ADJ> (&L)[2], const T *q, const T *k, const T *g,
+template <int DK, int NP, bool ADJ, typename T, int NQ = 0, bool TRA = true>
+__device__ __forceinline__ void sweep_producer(SweepSet<DK, ADJ, TRA> (&L)[2], const T *q, const T *k, const T *g,
                                                int64_t bos, int64_t len, int nc, int32_t H, int h, int pw,
-                                               int lane) {
-    RawBlocks<DK, NP, ADJ, T> raw[2];
+                                               int lane, QoSet<DK, (NQ > 0 ? NQ : 1)> *Qo = nullptr,
+                                               float (*tsc)[20] = nullptr, const float *dO = nullptr, int DV = 0,
+                                               int col0 = 0) {
+    RawBlocks<DK, NP, ADJ, T, NQ> raw[2];
     auto chunk = [&](int i) { return ADJ ? nc - 1 - i : i; };
-    auto load = [&](RawBlocks<DK, NP, ADJ, T> &r, int i) {
+    auto load = [&](RawBlocks<DK, NP, ADJ, T, NQ> &r, int i) {
         const int c = chunk(i);
-        r.load(q, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane);
+        r.load(q, k, g, bos + 16 * (int64_t)c, chunk_len(len, c), H, h, pw, lane, dO, DV, col0);
     };
     load(raw[0], 0);
     load(raw[1], 1);
-    raw[0].build(L[0], pw, lane);
+    raw[0].build(L[0], pw, lane, Qo, tsc, H, DV, col0);
     load(raw[0], 2);
     __syncthreads();
     unrolled_chunks(nc, [&](int i, auto par) {
         constexpr int p = 1 - decltype(par)::value;  // the set of iteration i + 1
-        raw[p].build(L[p], pw, lane);
+        raw[p].build(L[p], pw, lane, Qo ? Qo + p : Qo, tsc, H, DV, col0);
         load(raw[p], i + 3);
         __syncthreads();
     });
@@ -519,14 +551,26 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
     const int s = chain / H, h = chain % H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64, gq = lane / 16, m = lane % 16;
-    __shared__ SweepSet<DK, true> L[2];
+    // with one or two slice waves the producers (then on SIMDs of their own) form Q+^T dO
+    // (QO); with four, a producer shares each slice wave's SIMD and matrix core, and moving
+    // the products there measured slower (K3 layer 12.6 -> 13.5 ms); with eight the LDS
+    // would not hold the tiles
+    constexpr bool QO = NS <= 2;
+    constexpr int NQ = QO ? NS : 1;
+    __shared__ SweepSet<DK, true, !QO> L[2];
+    __shared__ QoSet<DK, NQ> Qo[QO ? 2 : 1];
+    __shared__ float tsc_all[QO ? NP : 1][16][20];
     __shared__ __attribute__((aligned(16))) float stage_all[NS][NB < 2 ? 2 : NB][STAGE_TILE];
     const int64_t hd = (int64_t)s * H + h;
     const int64_t bos = cu[s], len = cu[s + 1] - bos;
     const int nc = (int)((len + 15) / 16);
 
     if (wave >= NS) {
-        sweep_producer<DK, NP, true, T>(L, q, k, g, bos, len, nc, H, h, wave - NS, lane);
+        if constexpr (QO)
+            sweep_producer<DK, NP, true, T, NS, false>(L, q, k, g, bos, len, nc, H, h, wave - NS, lane, Qo,
+                                                       tsc_all[wave - NS], dO, DV, sg * NS * 16);
+        else
+            sweep_producer<DK, NP, true, T, 0, true>(L, q, k, g, bos, len, nc, H, h, wave - NS, lane);
         return;
     }
     // -------------------------------------------------------------------- slice wave
@@ -555,7 +599,7 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
     unrolled_chunks(nc, [&](int i, auto par) {
         constexpr int p = decltype(par)::value;
         const int c = nc - 1 - i;
-        const SweepSet<DK, true> &P = L[p];
+        const SweepSet<DK, true, !QO> &P = L[p];
         const f32x4 ob = widen_col4<float>(on[p], gq, H, DV, col0 + m);
         const f32x4 bt = widen_col4<T>(bn[p], gq, H, 1, 0);
         const f32x4 aq = aqn[p], tt = ttn[p];
@@ -571,10 +615,11 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
         // the adjoint of the state after the chunk, staged to row-major tiles
 #pragma unroll
         for (int b = 0; b < NB; ++b) stage_put(stage + b * STAGE_TILE, Sh[b], gq, m);
-        f32x4 qr[NB], pr[NB], gm[NB];
+        f32x4 qr[NB], pr[NB], gm[NB];  // qr: Q+^T rows, or with QO the producers' Q+^T dO tile
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            qr[b] = *reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]);
+            if constexpr (QO) qr[b] = Qo[p].t[wave][b][lane];
+            else qr[b] = *reinterpret_cast<const f32x4 *>(&P.trA[16 * b + m][4 * gq]);
             pr[b] = *reinterpret_cast<const f32x4 *>(&P.trB[16 * b + m][4 * gq]);
             gm[b] = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * gq]);
         }
@@ -596,7 +641,10 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_adjoint_sweep_ker
                         ((uint32_t)(lane / 4) * (uint32_t)H * DV + col0 + 4 * (lane % 4)) * 4u);
         const f32x4 nd = -dvv;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) Sh[b] = mma_f32_k16(pr[b], nd, mma_f32_k16(qr[b], ob, Sh[b] * gm[b]));
+        for (int b = 0; b < NB; ++b) {
+            if constexpr (QO) Sh[b] = mma_f32_k16(pr[b], nd, Sh[b] * gm[b] + qr[b]);
+            else Sh[b] = mma_f32_k16(pr[b], nd, mma_f32_k16(qr[b], ob, Sh[b] * gm[b]));
+        }
         __syncthreads();
     });
     if (dinit)
