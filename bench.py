@@ -16,7 +16,9 @@ The JSON line also carries, measured in the same run:
     same operations as separate launches,
   * "backward": the prefill backward on the batched workload and the K3 layer,
   * "context_parallel": the prefill with every sequence split into R segments (intra-device
-    context parallelism) against the plain prefill,
+    context parallelism) against the plain prefill, on the batched workload, the K3 layer and
+    the K3 layer's 65,536-token sequence with 12 heads (its share of one device when the 96
+    heads are split eight ways),
   * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
 each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
 
@@ -522,11 +524,11 @@ def bench_backward(index, torch, kda, workloads, dev, reps: int):
     return res
 
 
-def bench_cp(index, torch, kda, workloads, dev, segments, reps: int):
+def bench_cp(wl, torch, kda, workloads, dev, segments, reps: int):
     """Intra-device context parallelism (kda_prefill_cp): every sequence in R segments run as
     independent chains (three recurrence passes and a scan), against kda_prefill on the same
-    inputs."""
-    w = workloads.workload(index)
+    inputs.  wl is a workload index or a Workload."""
+    w = workloads.workload(wl) if isinstance(wl, int) else wl
     log(f"[bench] generating workload {w.name} for context parallelism")
     x = workloads.prefill_inputs(w, device=dev, seed=0)
     N = w.total_tokens
@@ -636,7 +638,10 @@ def main() -> int:
     if args.only in ("all", "cp"):
         log("[bench] intra-device context parallelism: batched workload and the K3 layer")
         out["context_parallel"] = {"batched": bench_cp(2, torch, kda, workloads, dev, (2, 4, 8), reps=10),
-                                   "k3_layer": bench_cp(3, torch, kda, workloads, dev, (2, 4), reps=2)}
+                                   "k3_layer": bench_cp(3, torch, kda, workloads, dev, (2, 4), reps=2),
+                                   "k3_sequence_12_heads": bench_cp(
+                                       workloads.custom([65536], 12, 128, 128, name="k3_sequence_12_heads"),
+                                       torch, kda, workloads, dev, (4, 8, 10, 16), reps=3)}
     if args.only in ("all", "layer"):
         log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
         out["layer"] = bench_layer(torch, kda, workloads, dev)

@@ -47,58 +47,74 @@ __global__ __launch_bounds__(CP_THREADS) void cp_identity_kernel(float *__restri
     M[i] = (e / dk == e % dk) ? 1.f : 0.f;
 }
 
-// One workgroup of 16 waves per (sequence, head); the waves share the 16x16 tiles of each
-// product M_r S_in,r on the fp32 matrix cores.  The current state stays in LDS (two
-// buffers, rows padded by 4 floats), so each step reads only M_r and S~_r from memory; every
-// S_in,r is also written out for the last recurrence pass.
-constexpr int SCAN_THREADS = 1024;
-
+// The columns of the state evolve independently under S_in,r+1 = M_r S_in,r + S~_r (M_r acts
+// from the left), so one workgroup serves one (sequence, head, 16-column slice): DK/16 waves,
+// wave I owning the 16x16 tile of rows 16I.. of the slice, on the fp32 matrix cores.  The
+// slice of the current state stays in LDS (two buffers, one barrier per segment); each wave
+// holds its row block of M_r and its tile of S~_r in registers and loads those of the next
+// segment before the product, so a step waits on memory only when the product is shorter
+// than a load.  Every S_in,r is also written out for the last recurrence pass.
 template <int DK, int DV>
-__global__ __launch_bounds__(SCAN_THREADS) void cp_scan_kernel(const float *__restrict__ init,
-                                                               const float *__restrict__ M,
-                                                               const float *__restrict__ St, float *__restrict__ Sin,
-                                                               int32_t H, int32_t R) {
-    constexpr int LD = DV + 4;
+__global__ __launch_bounds__(64 * (DK / 16)) void cp_scan_kernel(const float *__restrict__ init,
+                                                                const float *__restrict__ M,
+                                                                const float *__restrict__ St,
+                                                                float *__restrict__ Sin, int32_t H, int32_t R) {
+    constexpr int NKB = DK / 16, NJ = DV / 16, LD = 20;
     __shared__ __attribute__((aligned(16))) float S[2][DK * LD];
-    const int s = blockIdx.x / H, h = blockIdx.x % H;
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, gq = lane / 16, m = lane % 16;
+    const int J = blockIdx.x % NJ, sh = blockIdx.x / NJ;
+    const int s = sh / H, h = sh % H;
+    const int lane = threadIdx.x % 64, I = threadIdx.x / 64, gq = lane / 16, m = lane % 16;
+    const int col = 16 * J + m;
     auto seg = [&](int r) { return ((int64_t)s * R + r) * H + h; };
+    // this lane's operands of segment r: A = rows 16I + m of M_r, columns 16kb + 4gq ..;
+    // the S~_r values at rows 16I + 4gq + j, column col
+    auto load_ops = [&](int r, f32x4 (&a)[NKB], f32x4 &t) {
+        const float *Mr = M + seg(r) * DK * DK + (16 * I + m) * DK + 4 * gq;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) a[kb] = *reinterpret_cast<const f32x4 *>(Mr + 16 * kb);
+        const float *Tr = St + seg(r) * DK * DV + (16 * I + 4 * gq) * DV + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = Tr[j * DV];
+    };
     {
-        float *S0 = Sin + seg(0) * DK * DV;
         const float *I0 = init ? init + ((int64_t)s * H + h) * DK * DV : nullptr;
-        for (int i = tid; i < DK * DV; i += SCAN_THREADS) {
-            const float x = I0 ? I0[i] : 0.f;
-            S0[i] = x;
-            S[0][(i / DV) * LD + i % DV] = x;
+        float *S0 = Sin + seg(0) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * I + 4 * gq + j;
+            const float x = I0 ? I0[row * DV + col] : 0.f;
+            S0[row * DV + col] = x;
+            S[0][row * LD + m] = x;
         }
     }
+    f32x4 a[NKB], t;
+    if (R > 1) load_ops(0, a, t);
     __syncthreads();
     for (int r = 0; r + 1 < R; ++r) {
-        const float *Mr = M + seg(r) * DK * DK, *Tr = St + seg(r) * DK * DV;
+        // segment r + 1 <= R - 1 exists (M and S~ are kept for every segment)
+        f32x4 an[NKB], tn;
+        load_ops(r + 1, an, tn);
         const float *Sr = S[r & 1];
         float *Sl = S[(r + 1) & 1];
-        float *Sn = Sin + seg(r + 1) * DK * DV;
-        for (int t = wave; t < (DK / 16) * (DV / 16); t += SCAN_THREADS / 64) {
-            const int I = t / (DV / 16), J = t % (DV / 16);
-            f32x4 c = zero4();
+        f32x4 c = zero4();
 #pragma unroll
-            for (int kb = 0; kb < DK / 16; ++kb) {
-                // A operand: rows 16I + m of M, columns 16kb + 4g ..; B operand: rows 16kb + 4g + j
-                // of S, column 16J + m
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(Mr + (16 * I + m) * DK + 16 * kb + 4 * gq);
-                f32x4 b;
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x4 b;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = Sr[(16 * kb + 4 * gq + j) * LD + 16 * J + m];
-                c = mma_f32_k16(a, b, c);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * I + 4 * gq + j, col = 16 * J + m;
-                const float x = c[j] + Tr[row * DV + col];
-                Sn[row * DV + col] = x;
-                Sl[row * LD + col] = x;
-            }
+            for (int j = 0; j < 4; ++j) b[j] = Sr[(16 * kb + 4 * gq + j) * LD + m];
+            c = mma_f32_k16(a[kb], b, c);
         }
+        float *Sn = Sin + seg(r + 1) * DK * DV;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * I + 4 * gq + j;
+            const float x = c[j] + t[j];
+            Sn[row * DV + col] = x;
+            Sl[row * LD + m] = x;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) a[kb] = an[kb];
+        t = tn;
         __syncthreads();
     }
 }
@@ -131,7 +147,9 @@ hipError_t launch_cp_identity(float *M, int64_t n_mats, int32_t dk, void *stream
 template <int DK, int DV>
 static hipError_t launch_scan_t(const float *init, const float *M, const float *St, float *Sin, int32_t nseq,
                                 int32_t H, int32_t R, void *stream) {
-    hipLaunchKernelGGL((cp_scan_kernel<DK, DV>), dim3((unsigned)((int64_t)nseq * H)), dim3(SCAN_THREADS), 0,
+    const int64_t grid = (int64_t)nseq * H * (DV / 16);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((cp_scan_kernel<DK, DV>), dim3((unsigned)grid), dim3(64 * (DK / 16)), 0,
                        (hipStream_t)stream, init, M, St, Sin, H, R);
     return hipGetLastError();
 }

@@ -73,6 +73,29 @@ def test_cp_batched_workload_sampled_heads(dev):
     assert_close(fin[:, [2, 5]], f_ref, TOL[torch.bfloat16], "final_state")
 
 
+
+def test_cp_few_heads_long_sequence(dev):
+    """Where context parallelism pays: one 65,536-token sequence with 12 heads (the K3 layer's
+    share of one device when its 96 heads are split eight ways), R = 10 segments as timed by
+    the benchmark.  The oracle on 2 sampled heads, and every head against kda_prefill.
+    With the workload's decay and erase rates a 6,554-token segment forgets its incoming
+    state entirely (its map M is about 1e-10 in norm), so here the log-decay is scaled by 1e-4
+    and beta by 1e-2: each segment's map then keeps about half of the incoming state (norm
+    ratio 0.46 in a CPU estimate) and the scan's products count."""
+    w = workloads.custom([65536], 12, 128, 128, torch.bfloat16, "neg_softplus")
+    x = workloads.prefill_inputs(w, device=dev, seed=3)
+    x["log_alpha"] = (x["log_alpha"].float() * 1e-4).to(torch.bfloat16)
+    x["beta"] = (x["beta"].float() * 1e-2).to(torch.bfloat16)
+    say("  case: cp R=10, T=65536 H=12 d=128, log-decay x 1e-4, beta x 1e-2, heads [3, 10] + all vs kda_prefill")
+    o, fin = kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], segments=10)
+    o1, f1 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert_close(o, o1.double().cpu().numpy(), 1e-3, "o (cp vs prefill)")
+    assert_close(fin, f1.double().cpu().numpy(), 1e-3, "final_state (cp vs prefill)")
+    o_ref, f_ref = oracle_prefill(x, None, heads=[3, 10], nthreads=2)
+    assert_close(o[:, [3, 10]], o_ref, TOL[torch.bfloat16], "o")
+    assert_close(fin[:, [3, 10]], f_ref, TOL[torch.bfloat16], "final_state")
+
 def test_cp_no_tokens(dev):
     """N = 0: every segment is empty, so the final states are the initial ones exactly."""
     H, dk, dv = 2, 32, 64
