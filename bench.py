@@ -4,7 +4,9 @@ One step = one pass of the whole hot path over one batch: the chunk-local kernel
 inter-chunk kernel (prefill of the batch) and one decode step per sequence continuing
 from the prefill's final states.  The headline batch is B=4, H=8, T=2048, dk=dv=128,
 bf16 inputs, fp32 state.  Three input sets are rotated so the ~105 MB working set
-cannot stay resident in the 256 MB Infinity Cache.
+cannot stay resident in the 256 MB Infinity Cache.  --graph also times the step replayed
+from HIP graphs (its three launches captured once per input set), reported beside the
+eager time.
 
 The JSON line also carries, measured in the same run:
   * "k3_layer": prefill of B=1, H=96, T=65,536 (the K3 layer shape),
@@ -215,6 +217,25 @@ def bench_main(args, torch, kda, workloads, dev):
         step(i, False)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    graph_ms = None
+    if args.graph:
+        # the same steps replayed from HIP graphs (one per input set: the three launches of a
+        # step captured once); on this stack a replay costs more than the launch gaps it removes
+        graphs = []
+        for i in range(3):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i, False)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % 3].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % 3].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graphs
     # per-kernel durations: the same K steps again with HIP events around each launch
     for i in range(args.steps):
         step(i, True)
@@ -224,7 +245,7 @@ def bench_main(args, torch, kda, workloads, dev):
     th = N * H
     flops = th * prefill_flops_per_token_head(dk, dv)
     return {
-        "w": w, "wall_ms": wall_ms, "tokens": tokens, "ms_chunk_local": ms_cl, "ms_inter_chunk": ms_ic,
+        "w": w, "wall_ms": wall_ms, "graph_ms": graph_ms, "tokens": tokens, "ms_chunk_local": ms_cl, "ms_inter_chunk": ms_ic,
         "ms_decode": ms_dec, "prefill_tflops": flops / ((ms_cl + ms_ic) * 1e-3) / 1e12,
         "ic_bytes": th * inter_chunk_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4,
         "cl_bytes": th * (2 * (2 * dk + dk + 1)) + (N // 16 + nseq) * H * 2048,
@@ -563,6 +584,8 @@ def main() -> int:
     ap.add_argument("--only", default="all",
                     choices=["all", "main", "k3", "decode", "layer", "backward", "cp", "varlen", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the headline step as HIP graph replays (reported beside the eager time)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -595,6 +618,8 @@ def main() -> int:
         w = m["w"]
         out["value"] = m["tokens"] / (m["wall_ms"] * 1e-3)
         out["ms_per_step"] = round(m["wall_ms"], 5)
+        if m["graph_ms"] is not None:
+            out["ms_per_step_graph_replay"] = round(m["graph_ms"], 5)
         out["config"] = {"workload": "batched_prefill_then_decode", "batch": w.nseq, "heads": w.H,
                          "seq_len": w.seqlens[0], "dk": w.dk, "dv": w.dv, "chunk": CHUNK,
                          "inputs": "bf16", "state": "fp32", "output": "fp32",
