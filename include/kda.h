@@ -45,6 +45,8 @@
  * library never allocates, frees or synchronises.  Pointers are device
  * pointers unless stated otherwise.  Work is enqueued on `stream` (a
  * hipStream_t; NULL = the default stream) and the call returns at once.
+ * A call enqueues kernel launches only (no memset, copy or event), so it can
+ * be recorded into a HIP graph by stream capture and replayed.
  * Inputs are read-only; o / final_state must not alias the inputs (except the
  * final_state == init_state case above).  Alignment: fp32 buffers (state,
  * o, init/final state, workspace) 16 bytes; q, k, v, log_alpha four elements
