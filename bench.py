@@ -1,14 +1,23 @@
 """Benchmark of the MI355X KDA library (one GPU).
 
-One step = one pass of the whole hot path over one batch: the chunk-local kernel, the
-inter-chunk kernel (prefill of the batch) and one decode step per sequence continuing
-from the prefill's final states.  The headline batch is B=4, H=8, T=2048, dk=dv=128,
-bf16 inputs, fp32 state.  Three input sets are rotated so the ~105 MB working set
-cannot stay resident in the 256 MB Infinity Cache.  --graph also times the step replayed
-from HIP graphs (its three launches captured once per input set), reported beside the
-eager time.
+One step = one pass of the whole hot path over one batch: the prefill of the 1,048,576-token
+varlen workload (27 packed sequences of log-uniform length in [512, 262,144], H=96, dk=dv=128,
+bf16 inputs, fp32 state and output) and one decode step per sequence continuing from the
+prefill's final states.  The inputs (155 GB) are resident in HBM before timing starts and far
+exceed the 256 MB Infinity Cache.  The headline line carries:
+  * value / ms_per_step: tokens (prefill tokens + one decode token per sequence) per second over
+    K steps bracketed by device synchronisation, plus median and minimum step times from HIP
+    events;
+  * roofline: the dominant kernel's algorithmic bytes (q, k, v, log_alpha, beta read once, o
+    written once, final states written) over its average launch time from HIP events on the
+    stream it runs on, against 8 TB/s, with HBM traffic from committed rocprofv3 counters;
+  * parity: the outputs of the last timed step (o, the decode output and the state after the
+    decode step) against the fp64 oracle on 8 heads (one per residue mod 8) of every sequence;
+  * cpu_baseline: the oracle's time on those 8 heads, extrapolated to all 96, with the CPU model,
+    the threads it used and a single-thread rate.
 
-The JSON line also carries, measured in the same run:
+Sub-objects of the same line, each measured in the same run:
+  * "batched": prefill of B=4, H=8, T=2048 + one decode token (three input sets rotated),
   * "k3_layer": prefill of B=1, H=96, T=65,536 (the K3 layer shape),
   * "decode":   128 recurrent steps over B=256 x H=96 heads (1.6 GB of fp32 state),
   * "decode_window_4" / "_8": the same 128 steps as windows of 4 or 8 draft tokens
@@ -18,13 +27,10 @@ The JSON line also carries, measured in the same run:
     same operations as separate launches,
   * "backward": the prefill backward on the batched workload and the K3 layer,
   * "context_parallel": the prefill with every sequence split into R segments (intra-device
-    context parallelism) against the plain prefill, on the batched workload, the K3 layer and
-    the K3 layer's 65,536-token sequence with 12 heads (its share of one device when the 96
-    heads are split eight ways),
-  * "varlen_1m": prefill of 1,048,576 packed tokens in log-uniform sequences,
-each with tokens/s (or GB/s), TFLOP/s and the fraction of the roofline that bounds it.
+    context parallelism) against the plain prefill.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|k3|decode|layer|backward|cp|varlen|none]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only main|batched|k3|decode|layer|backward|cp|none]
 """
 from __future__ import annotations
 
@@ -55,12 +61,6 @@ def prefill_bytes_per_token_head(dk: int, dv: int, in_bytes: int = 2) -> float:
     return in_bytes * (3 * dk + dv + 1) + 4 * dv
 
 
-def inter_chunk_bytes_per_token_head(dk: int, dv: int, in_bytes: int = 2) -> float:
-    """The inter-chunk kernel's own algorithmic traffic: q, k, log_alpha, v read, o written, and the
-    chunk-local matrices T' and A_qk (2 x 16 x 16 fp32 per 16 tokens) read."""
-    return in_bytes * (3 * dk + dv) + 4 * dv + 2 * 16 * 16 * 4 / CHUNK
-
-
 def decode_bytes_per_head(dk: int, dv: int, in_bytes: int = 2) -> float:
     """Decode step: fp32 state read + written, q, k, log_alpha, v, beta read, o written."""
     return 2 * dk * dv * 4 + in_bytes * (3 * dk + dv + 1) + 4 * dv
@@ -76,9 +76,28 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/inter_chunk.hip", "gated_delta_rule_51_amd/csrc/inter_chunk_ws.hip",
-                  "gated_delta_rule_51_amd/csrc/kda_device.hpp", "gated_delta_rule_51_amd/csrc/kda_launch.hpp")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "inter_chunk_batched_prefill_traffic.txt")
+def host_info() -> dict:
+    """CPU model and the logical cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"cpu_model": model, "cores_available": cores}
+
+
+KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/chunk_local.hip", "gated_delta_rule_51_amd/csrc/inter_chunk.hip",
+                  "gated_delta_rule_51_amd/csrc/inter_chunk_ws.hip", "gated_delta_rule_51_amd/csrc/kda_device.hpp",
+                  "gated_delta_rule_51_amd/csrc/kda_launch.hpp")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_1m_traffic.txt")
 
 
 def kernel_source_hash() -> str:
@@ -86,18 +105,20 @@ def kernel_source_hash() -> str:
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        path = os.path.join(ROOT, rel)
+        if os.path.exists(path):
+            with open(path, "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """(HBM bytes per inter-chunk launch, HIP kernel name) from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or (None, None) when it is missing or was taken on
-    different kernel sources."""
+def measured_traffic(path: str = TRAFFIC_SUMMARY):
+    """(HBM bytes per launch, HIP kernel name) from a committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or (None, None) when it is missing or was taken on different kernel
+    sources."""
     try:
         fields = {}
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     key, val = line.split(":", 1)
@@ -143,43 +164,178 @@ class Timer:
         return sum(s.elapsed_time(e) for s, e in zip(self.start[:self.i], self.end[:self.i])) / max(self.i, 1)
 
 
-def cpu_baseline(workload, seed: int = 0) -> dict:
-    """The fp64 oracle (as it stands) on the host cores: the whole headline batch
-    (prefill of every sequence and head, then one decode token per sequence)."""
+# heads the oracle recomputes on the headline workload: one per residue mod 8 (the XCD a
+# (sequence, head) chain runs on is its index mod 8, and with 96 heads that is the head mod 8)
+PARITY_HEADS = (0, 13, 26, 39, 52, 65, 78, 91)
+
+
+def oracle_check(x, o, od, state, d, heads, tol: float, group: int = 4) -> dict:
+    """Run the fp64 oracle on ``heads`` of every sequence of the prefill inputs ``x`` (device
+    tensors), then one decode step with the decode inputs ``d``; compare with the GPU's prefill
+    output ``o``, decode output ``od`` and state after the decode step ``state``.  Heads go
+    through the oracle ``group`` at a time (host memory: ~5.4 GB of fp64 per head at 1M tokens).
+    Returns the errors (max|err| / RMS(ref), pooled over the heads) and the oracle's wall time."""
     import numpy as np
-    import torch
 
     import oracle
-    import workloads
 
-    x = workloads.prefill_inputs(workload, device="cpu", seed=seed)
-    d = workloads.decode_step_inputs(workloads.custom([1] * workload.nseq, workload.H, workload.dk, workload.dv),
-                                     0, device="cpu", seed=seed)
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
+    info = host_info()
+    threads = info["cores_available"]
     names = ("q", "k", "v", "log_alpha", "beta")
-    args = [x[n].double().numpy() for n in names]
-    dargs = [d[n].double().numpy() for n in names]
-    threads = min(cores, workload.nseq * workload.H)  # the oracle runs one thread per (sequence, head) at most
-    # the whole batch, repeated until about 10 s of host time have been measured
-    reps, dt = 0, 0.0
-    while dt < 10.0 or reps < 1:
+    cu = x["cu_seqlens"].cpu().numpy()
+    err = {"o": [0.0, 0.0], "decode_o": [0.0, 0.0], "state": [0.0, 0.0]}  # [sum sq ref, max abs err]
+    seconds = 0.0
+    for g0 in range(0, len(heads), group):
+        hs = list(heads[g0:g0 + group])
+        cpu = {n: x[n][:, hs].contiguous().cpu() for n in names}
         t0 = time.perf_counter()
-        _, fin = oracle.prefill(*args, cu_seqlens=x["cu_seqlens"].numpy(), nthreads=threads)
-        oracle.decode(*dargs, fin, nthreads=threads)
-        dt += time.perf_counter() - t0
-        reps += 1
-    tokens = (workload.total_tokens + workload.nseq) * reps
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": dt, "repetitions": reps,
-            "sample": f"whole batch, {reps} times: prefill of {workload.nseq}x{workload.seqlens[0]} tokens x "
-                      f"{workload.H} heads (dk=dv={workload.dk}) + 1 decode token per sequence, fp64, "
-                      f"{threads} threads"}
+        o_ref, f_ref = oracle.prefill(*(cpu[n] for n in names), cu_seqlens=cu, nthreads=threads)
+        seconds += time.perf_counter() - t0
+        del cpu
+        od_ref, s_ref = oracle.decode(*(d[n][:, hs].contiguous().cpu() for n in names), f_ref, nthreads=threads)
+        for key, got, ref in (("o", o[:, hs], o_ref), ("decode_o", od[:, hs], od_ref), ("state", state[:, hs], s_ref)):
+            g = got.contiguous().cpu().double().numpy()
+            if not np.all(np.isfinite(g)):
+                err[key][1] = float("inf")
+            err[key][0] += float(np.sum(ref * ref))
+            err[key][1] = max(err[key][1], float(np.max(np.abs(g - ref))) if ref.size else 0.0)
+        del o_ref, f_ref, od_ref, s_ref
+    counts = {"o": o[:, list(heads)].numel(), "decode_o": od[:, list(heads)].numel(),
+              "state": state[:, list(heads)].numel()}
+    out = {"heads": list(heads), "tol_max_err_over_rms": tol}
+    for key, (ss, mx) in err.items():
+        rms = (ss / max(counts[key], 1)) ** 0.5
+        out[f"{key}_max_err_over_rms"] = mx / rms if rms > 0 else mx
+    out["pass"] = all(out[f"{k}_max_err_over_rms"] <= tol for k in err)
+    return {"parity": out, "oracle_seconds": seconds, "threads": threads, "cpu_model": info["cpu_model"]}
 
 
-def bench_main(args, torch, kda, workloads, dev):
+def oracle_single_thread_rate(x, seqlen: int = 8192) -> float:
+    """Token-heads per second of the oracle on one thread: the first ``seqlen`` tokens of the
+    longest sequence, head 0."""
+    import numpy as np
+
+    import oracle
+
+    cu = x["cu_seqlens"].cpu().numpy()
+    lens = np.diff(cu)
+    s = int(np.argmax(lens))
+    n = int(min(seqlen, lens[s]))
+    a, b = int(cu[s]), int(cu[s]) + n
+    cpu = [x[nm][a:b, :1].contiguous().cpu() for nm in ("q", "k", "v", "log_alpha", "beta")]
+    t0 = time.perf_counter()
+    oracle.prefill(*cpu, nthreads=1)
+    return n / (time.perf_counter() - t0)
+
+
+def bench_headline(args, torch, kda, workloads, dev, cpu_baseline: bool = True) -> dict:
+    """The headline step on the varlen 1M workload: kda_prefill over 1,048,576 packed tokens
+    (27 sequences, H=96, dk=dv=128, bf16), then kda_decode_step of one more token per sequence
+    from the final states.  Returns the fields of the JSON line."""
+    import statistics
+
+    w = workloads.workload(5)
+    N, H, dk, dv, nseq = w.total_tokens, w.H, w.dk, w.dv, w.nseq
+    log(f"[bench] generating workload {w.name}: {w.notes}")
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    dw = workloads.custom([1] * nseq, H, dk, dv)
+    dsets = [workloads.decode_step_inputs(dw, 0, device=dev, seed=s) for s in range(3)]
+    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
+    o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+    od = torch.empty((nseq, H, dv), dtype=torch.float32, device=dev)
+    args_x = (x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+
+    def step(i):
+        d = dsets[i % 3]
+        kda.kda_prefill(*args_x, o=o, final_state=fin, workspace=ws)
+        kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
+
+    log(f"[bench] headline: {args.warmup} warm-up + {args.steps} timed steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    last = (args.steps - 1) % 3  # decode inputs of the last timed step
+
+    # parity of the last timed step's outputs, and the oracle's time on the same heads
+    check = None
+    if cpu_baseline:
+        log(f"[bench] oracle on heads {PARITY_HEADS} of every sequence (parity of the timed outputs)")
+        check = oracle_check(x, o, od, fin, dsets[last], PARITY_HEADS, tol=1e-2)
+        log(f"[bench] parity: {check['parity']}")
+
+    # per-kernel durations: the prefill's two kernels and the decode step, HIP events on the
+    # stream every call is enqueued on (torch's current stream)
+    reps = max(3, min(args.steps, 10))
+    t_cl, t_ic, t_dec = Timer(torch, reps), Timer(torch, reps), Timer(torch, reps)
+    for i in range(reps):
+        d = dsets[i % 3]
+        with t_cl:
+            kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+        with t_ic:
+            kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
+                                o=o, final_state=fin)
+        with t_dec:
+            kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
+    torch.cuda.synchronize()
+    kernels = {"chunk_local": t_cl.mean_ms(), "inter_chunk": t_ic.mean_ms(), "decode": t_dec.mean_ms()}
+    kernel_names = {"chunk_local": "chunk_local_bf16_kernel<128>", "inter_chunk": "inter_chunk_ws_kernel<128,128,4,4>",
+                    "decode": "decode_kernel"}
+    th = N * H
+    prefill_ms = kernels["chunk_local"] + kernels["inter_chunk"]
+    flops = th * prefill_flops_per_token_head(dk, dv)
+    alg_bytes = th * prefill_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4
+    dom = max(("chunk_local", "inter_chunk"), key=lambda k: kernels[k])
+    ach = alg_bytes / (kernels[dom] * 1e-3) / 1e9
+    traffic, hip_kernel = measured_traffic()
+    res = {
+        "value": (N + nseq) / (wall_ms * 1e-3), "ms_per_step": round(wall_ms, 4),
+        "ms_per_step_median": round(statistics.median(step_ms), 4), "ms_per_step_min": round(min(step_ms), 4),
+        "config": {"workload": w.name, "tokens": N, "sequences": nseq, "seqlens": list(w.seqlens), "heads": H,
+                   "dk": dk, "dv": dv, "chunk": CHUNK, "inputs": "bf16", "state": "fp32", "output": "fp32",
+                   "step": "kda_prefill over the packed batch, then kda_decode_step (1 token per sequence) "
+                           "from the final states"},
+        "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
+        "prefill": {"ms": round(prefill_ms, 4), "tokens_per_s": N / (prefill_ms * 1e-3),
+                    "tflops": flops / (prefill_ms * 1e-3) / 1e12,
+                    "mfma_peak_frac": flops / (prefill_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "hbm_gbs_algorithmic": alg_bytes / (prefill_ms * 1e-3) / 1e9,
+                    "hbm_roofline_frac": alg_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "t_hbm_ms": alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3},
+        "roofline": {"kernel": dom, "hip_kernel": hip_kernel or kernel_names[dom], "bound": "hbm", "achieved": ach,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "bytes_formula": "N*H*(2*(3*dk+dv+1) + 4*dv) + nseq*H*dk*dv*4"},
+    }
+    if check is not None:
+        res["parity"] = check["parity"]
+        frac = len(PARITY_HEADS) / H
+        t_full = check["oracle_seconds"] / frac
+        st_rate = oracle_single_thread_rate(x)
+        res["cpu_baseline"] = {
+            "value": (N + nseq) / t_full, "unit": "tokens/s", "cores": check["threads"], "kind": "oracle",
+            "cpu_model": check["cpu_model"], "seconds_measured": round(check["oracle_seconds"], 3),
+            "extrapolated": True,
+            "sample": f"fp64 oracle prefill of all {nseq} sequences on heads {list(PARITY_HEADS)} "
+                      f"({len(PARITY_HEADS)} of {H}), {check['threads']} threads; time scaled by {H}/"
+                      f"{len(PARITY_HEADS)} to the whole workload (the decode token is not timed)",
+            "single_thread_token_heads_per_s": st_rate,
+            "single_thread_tokens_per_s": st_rate / H}
+    del x, ws, o, fin, od, dsets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_batched(args, torch, kda, workloads, dev):
     w = workloads.workload(2)
     N, H, dk, dv, nseq = w.total_tokens, w.H, w.dk, w.dv, w.nseq
     sets = [workloads.prefill_inputs(w, device=dev, seed=s) for s in range(3)]
@@ -247,8 +403,6 @@ def bench_main(args, torch, kda, workloads, dev):
     return {
         "w": w, "wall_ms": wall_ms, "graph_ms": graph_ms, "tokens": tokens, "ms_chunk_local": ms_cl, "ms_inter_chunk": ms_ic,
         "ms_decode": ms_dec, "prefill_tflops": flops / ((ms_cl + ms_ic) * 1e-3) / 1e12,
-        "ic_bytes": th * inter_chunk_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4,
-        "cl_bytes": th * (2 * (2 * dk + dk + 1)) + (N // 16 + nseq) * H * 2048,
     }
 
 
@@ -579,13 +733,13 @@ def bench_cp(wl, torch, kda, workloads, dev, segments, reps: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    choices=["all", "main", "k3", "decode", "layer", "backward", "cp", "varlen", "none"])
+                    choices=["all", "main", "batched", "k3", "decode", "layer", "backward", "cp", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
-                    help="also time the headline step as HIP graph replays (reported beside the eager time)")
+                    help="also time the batched step as HIP graph replays (reported beside the eager time)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -613,36 +767,23 @@ def main() -> int:
            "dtype": "bf16", "data": "synthetic"}
 
     if args.only in ("all", "main"):
-        log("[bench] headline step: batched prefill B=4 H=8 T=2048 + 1 decode token per sequence")
-        m = bench_main(args, torch, kda, workloads, dev)
+        log("[bench] headline step: varlen 1M prefill (27 sequences, H=96) + 1 decode token per sequence")
+        out.update(bench_headline(args, torch, kda, workloads, dev, cpu_baseline=not args.no_cpu_baseline))
+    if args.only in ("all", "batched"):
+        log("[bench] batched prefill B=4 H=8 T=2048 + 1 decode token per sequence")
+        m = bench_batched(args, torch, kda, workloads, dev)
         w = m["w"]
-        out["value"] = m["tokens"] / (m["wall_ms"] * 1e-3)
-        out["ms_per_step"] = round(m["wall_ms"], 5)
+        kernels = {"chunk_local": m["ms_chunk_local"], "inter_chunk": m["ms_inter_chunk"], "decode": m["ms_decode"]}
+        th = w.total_tokens * w.H
+        alg = th * prefill_bytes_per_token_head(w.dk, w.dv) + w.nseq * w.H * w.dk * w.dv * 4
+        out["batched"] = {
+            "workload": w.name, "batch": w.nseq, "heads": w.H, "seq_len": w.seqlens[0], "input_sets_rotated": 3,
+            "ms_per_step": round(m["wall_ms"], 5), "tokens_per_s": m["tokens"] / (m["wall_ms"] * 1e-3),
+            "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
+            "prefill_tflops": m["prefill_tflops"],
+            "inter_chunk_hbm_frac": alg / (m["ms_inter_chunk"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if m["graph_ms"] is not None:
-            out["ms_per_step_graph_replay"] = round(m["graph_ms"], 5)
-        out["config"] = {"workload": "batched_prefill_then_decode", "batch": w.nseq, "heads": w.H,
-                         "seq_len": w.seqlens[0], "dk": w.dk, "dv": w.dv, "chunk": CHUNK,
-                         "inputs": "bf16", "state": "fp32", "output": "fp32",
-                         "step": "kda_chunk_local + kda_inter_chunk over the batch, then kda_decode_step "
-                                 "(1 token per sequence) from the final states",
-                         "input_sets_rotated": 3}
-        kernels = {"chunk_local": m["ms_chunk_local"], "inter_chunk": m["ms_inter_chunk"],
-                   "decode": m["ms_decode"]}
-        out["kernel_ms"] = {k: round(v, 5) for k, v in kernels.items()}
-        out["prefill_tflops"] = m["prefill_tflops"]
-        out["prefill_mfma_peak_frac"] = m["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS
-        dom = max(("chunk_local", "inter_chunk"), key=lambda k: kernels[k])
-        b = m["ic_bytes"] if dom == "inter_chunk" else m["cl_bytes"]
-        ach = b / (kernels[dom] * 1e-3) / 1e9
-        traffic, hip_kernel = measured_traffic() if dom == "inter_chunk" else (None, None)
-        out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                           "algorithmic_bytes_per_launch": b}
-        if hip_kernel:
-            out["roofline"]["hip_kernel"] = hip_kernel
-        if not args.no_cpu_baseline:
-            log("[bench] cpu baseline: fp64 oracle on the same batch")
-            out["cpu_baseline"] = cpu_baseline(w)
+            out["batched"]["ms_per_step_graph_replay"] = round(m["graph_ms"], 5)
     if args.only in ("all", "k3"):
         log("[bench] K3 layer prefill B=1 H=96 T=65536")
         out["k3_layer"] = bench_prefill_workload(3, torch, kda, workloads, dev, reps=5)
@@ -670,9 +811,6 @@ def main() -> int:
     if args.only in ("all", "layer"):
         log("[bench] layer passes (gate, ShortConv, epilogue) and the fused decode step")
         out["layer"] = bench_layer(torch, kda, workloads, dev)
-    if args.only in ("all", "varlen"):
-        log("[bench] varlen 1M-token prefill")
-        out["varlen_1m"] = bench_prefill_workload(5, torch, kda, workloads, dev, reps=3)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -158,6 +158,52 @@ def _check_inputs(q, k, v, log_alpha, beta):
     return N, H, dk, dv
 
 
+def _check_dev(name, t, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device}); the KDA library has no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_gpu(name, t):
+    """t is a contiguous tensor on a GPU (the first operand, whose device the others must share)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); the KDA library has no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, device, nbytes: int):
+    """A caller-supplied workspace: a contiguous tensor on the inputs' device of at least nbytes."""
+    _check_dev("workspace", ws, device)
+    have = ws.numel() * ws.element_size()
+    if have < nbytes:
+        raise ValueError(f"workspace holds {have} bytes, {nbytes} needed")
+
+
+def _prefill_outputs(N, H, dk, dv, nseq, device, o, final_state, init_state, output_final_state):
+    """Allocate or check kda_prefill's outputs (o fp32 [N, H, dv], final_state fp32 [nseq, H, dk, dv])
+    and check init_state, so no wrong-sized or host buffer reaches a kernel."""
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=device)
+    _check_dev("o", o, device, torch.float32, (N, H, dv))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=device)
+    if final_state is not None:
+        _check_dev("final_state", final_state, device, torch.float32, (nseq, H, dk, dv))
+    if init_state is not None:
+        _check_dev("init_state", init_state, device, torch.float32, (nseq, H, dk, dv))
+    return o, final_state
+
+
 def kda_prefill_workspace_bytes(total_tokens: int, nseq: int, H: int, dk: int, dv: int,
                                 dtype: torch.dtype = torch.bfloat16) -> int:
     return int(load_library().kda_prefill_workspace_bytes(total_tokens, nseq, H, dk, dv, _dtype_code(dtype)))
@@ -188,15 +234,12 @@ def kda_prefill(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
     N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
     cu = _cu(cu_seqlens, N, q.device)
     nseq = cu.numel() - 1
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
-    if init_state is not None and (init_state.dtype != torch.float32 or tuple(init_state.shape) != (nseq, H, dk, dv)
-                                   or not init_state.is_contiguous()):
-        raise ValueError("init_state must be contiguous fp32 [nseq, H, dk, dv]")
+    o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
+                                      output_final_state)
+    nbytes = kda_prefill_workspace_bytes(N, nseq, H, dk, dv, q.dtype)
     if workspace is None:
         workspace = alloc_workspace(N, nseq, H, dk, dv, q.dtype, q.device)
+    _check_workspace(workspace, q.device, nbytes)
     _check(load_library().kda_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
         H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _ptr(workspace),
@@ -213,19 +256,15 @@ def kda_prefill_cp(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *
     N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
     cu = _cu(cu_seqlens, N, q.device)
     nseq = cu.numel() - 1
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
-    if init_state is not None and (init_state.dtype != torch.float32 or tuple(init_state.shape) != (nseq, H, dk, dv)
-                                   or not init_state.is_contiguous()):
-        raise ValueError("init_state must be contiguous fp32 [nseq, H, dk, dv]")
+    o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
+                                      output_final_state)
     lib = load_library()
+    nbytes = int(lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, _dtype_code(q.dtype), int(segments)))
+    if nbytes == 0:
+        raise KDAError(3, "kda_prefill_cp: unsupported shape or segment count")
     if workspace is None:
-        nbytes = int(lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, _dtype_code(q.dtype), int(segments)))
-        if nbytes == 0:
-            raise KDAError(3, "kda_prefill_cp: unsupported shape or segment count")
         workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    _check_workspace(workspace, q.device, nbytes)
     _check(lib.kda_prefill_cp(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
         H, dk, dv, _dtype_code(q.dtype), int(segments), _ptr(o), _ptr(final_state), _ptr(workspace),
@@ -235,8 +274,15 @@ def kda_prefill_cp(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *
 
 def kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, workspace, *, stream=None) -> torch.Tensor:
     """Chunk-local phase only; writes T' and A_qk per (chunk slot, head) into ``workspace``."""
+    _check_gpu("q", q)
+    for name, t in (("k", k), ("log_alpha", log_alpha), ("beta", beta)):
+        _check_dev(name, t, q.device, q.dtype)
     N, H, dk = q.shape
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(beta.shape) != (N, H):
+        raise ValueError("expected q, k, log_alpha [N, H, dk], beta [N, H]")
+    _check_dev("cu_seqlens", cu_seqlens, q.device, torch.int32)
     nseq = cu_seqlens.numel() - 1
+    _check_workspace(workspace, q.device, kda_prefill_workspace_bytes(N, nseq, H, dk, 16, q.dtype))
     _check(load_library().kda_chunk_local(
         _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), nseq, N, H, dk,
         _dtype_code(q.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -246,13 +292,18 @@ def kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, workspace, *, stream=None
 def kda_inter_chunk(q, k, v, log_alpha, cu_seqlens, workspace, init_state=None, *, o=None,
                     final_state=None, output_final_state: bool = True, stream=None):
     """Inter-chunk phase only; reads the workspace written by kda_chunk_local."""
+    _check_gpu("q", q)
+    for name, t in (("k", k), ("v", v), ("log_alpha", log_alpha)):
+        _check_dev(name, t, q.device, q.dtype)
     N, H, dk = q.shape
     dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(v.shape) != (N, H, dv):
+        raise ValueError("expected q, k, log_alpha [N, H, dk], v [N, H, dv]")
+    _check_dev("cu_seqlens", cu_seqlens, q.device, torch.int32)
     nseq = cu_seqlens.numel() - 1
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
+                                      output_final_state)
+    _check_workspace(workspace, q.device, kda_prefill_workspace_bytes(N, nseq, H, dk, dv, q.dtype))
     _check(load_library().kda_inter_chunk(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(init_state), _ptr(cu_seqlens), nseq, N, H,
         dk, dv, _dtype_code(q.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -271,6 +322,7 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None, stream=None) -> 
         raise ValueError("state must be contiguous fp32 [B, H, dk, dv] on the inputs' device")
     if o is None:
         o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    _check_dev("o", o, q.device, torch.float32, (B, H, dv))
     _check(load_library().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o), B, H, dk, dv,
         _dtype_code(q.dtype), _stream(stream)))
@@ -302,23 +354,12 @@ def kda_decode_window(q, k, v, log_alpha, beta, state, accept=None, *, o=None, o
         raise ValueError("accept must be a contiguous int32 [B] tensor on the inputs' device")
     if output_o and o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if output_o:
+        _check_dev("o", o, q.device, torch.float32, (B, T, H, dv))
     _check(load_library().kda_decode_window(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o if output_o else None),
         _ptr(accept), B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
     return o if output_o else None
-
-
-def _check_dev(name, t, device, dtype=None, shape=None):
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device != device:
-        raise ValueError(f"{name} must be on {device} (got {t.device}); the KDA library has no CPU path")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def kda_gate(z, A_log, *, out=None, stream=None) -> torch.Tensor:
@@ -415,6 +456,8 @@ def kda_decode_step_fused(q, k, v, gate, beta, state, *, gate_A_log=None, out_ga
         raise ValueError("output_o=False needs out_gate (nothing would be written)")
     if output_o and o is None:
         o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    if output_o:
+        _check_dev("o", o, q.device, torch.float32, (B, H, dv))
     _check(load_library().kda_decode_step_fused(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_A_log), _ptr(beta), _ptr(state),
         _ptr(o if output_o else None), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y), B, H, dk, dv,
@@ -444,6 +487,8 @@ def kda_decode_window_fused(q, k, v, gate, beta, state, accept=None, *, gate_A_l
     # the window's epilogue runs over o, so o is materialised whenever out_gate is given
     if (output_o or out_gate is not None) and o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if o is not None:
+        _check_dev("o", o, q.device, torch.float32, (B, T, H, dv))
     _check(load_library().kda_decode_window_fused(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_A_log), _ptr(beta), _ptr(state),
         _ptr(o), _ptr(accept), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
@@ -476,6 +521,8 @@ def kda_decode_layer_step(qkv, conv_w, conv_cache, gate, beta, state, *, dk: int
         raise ValueError("output_o=False needs out_gate (nothing would be written)")
     if output_o and o is None:
         o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    if output_o:
+        _check_dev("o", o, dev, torch.float32, (B, H, dv))
     _check(load_library().kda_decode_layer_step(
         _ptr(qkv), _ptr(conv_w), _ptr(conv_cache), float(l2_eps), _ptr(gate), _ptr(gate_A_log), _ptr(beta),
         _ptr(state), _ptr(o if output_o else None), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
@@ -498,9 +545,10 @@ def kda_prefill_backward(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, init_st
     if init_state is not None:
         _check_dev("init_state", init_state, dev, torch.float32, (nseq, H, dk, dv))
     lib = load_library()
+    nbytes = int(lib.kda_prefill_backward_workspace_bytes(N, nseq, H, dk, dv, _dtype_code(q.dtype)))
     if workspace is None:
-        nbytes = int(lib.kda_prefill_backward_workspace_bytes(N, nseq, H, dk, dv, _dtype_code(q.dtype)))
         workspace = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=dev)
+    _check_workspace(workspace, dev, nbytes)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dq": torch.empty((N, H, dk), **f32), "dk": torch.empty((N, H, dk), **f32),
            "dv": torch.empty((N, H, dv), **f32), "dlog_alpha": torch.empty((N, H, dk), **f32),

@@ -19,15 +19,28 @@ kda_status hip_status(hipError_t e) {
     return KDA_ERR_HIP;
 }
 
+// Launch limits.  A dispatch holds at most 2^32 - 1 work-items per grid dimension, and
+// the kernels keep per-chunk buffer extents and row strides in 32 bits.  The bounds
+// below follow each prefill-family launch's real work-item count, so a shape that
+// passes validation also launches:
+//   * recurrence kernels (inter-chunk, backward sweeps, context-parallel scan): at most
+//     4096 work-items per (sequence, head) chain -> chains < 2^20;
+//   * per-(chunk slot, head) kernels (backward matrices and gradients: 256 work-items,
+//     fp32 chunk-local: 64 per slot in x) -> slots * H < 2^24, fp32 slots < 2^26;
+//   * 16-token row extents 16 * H * d * 4 bytes in 32 bits -> H * d < 2^24.
+constexpr int64_t MAX_CHAINS = int64_t(1) << 20;
+constexpr int64_t MAX_SLOT_HEADS = int64_t(1) << 24;
+
 kda_status check_common(int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
                         kda_dtype dt) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
     if (nseq < 1 || H < 1 || total_tokens < 0 || total_tokens >= (int64_t(1) << 31))
         return KDA_ERR_SHAPE;
-    // grid limits: chunk slots and (sequence, head) chains must fit a 32-bit grid
-    if (kda::chunk_slots(total_tokens, nseq) >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
-    if ((int64_t)nseq * H >= (int64_t(1) << 28)) return KDA_ERR_SHAPE;
+    if ((int64_t)nseq * H >= MAX_CHAINS) return KDA_ERR_SHAPE;
+    if ((int64_t)H * (dk > dv ? dk : dv) >= (int64_t(1) << 24)) return KDA_ERR_SHAPE;
+    const int64_t slots = kda::chunk_slots(total_tokens, nseq);
+    if (dt == KDA_F32 && slots >= (int64_t(1) << 26)) return KDA_ERR_SHAPE;
     return KDA_OK;
 }
 
@@ -113,6 +126,15 @@ kda_status check_fusion(const float *A_log, const void *u, const float *w, float
     return KDA_OK;
 }
 
+// The backward's per-(chunk slot, head) kernels: up to 256 work-items each.
+kda_status check_backward_shape(int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                                kda_dtype dt) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    if (kda::chunk_slots(total_tokens, nseq) * H >= MAX_SLOT_HEADS) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,7 +206,9 @@ size_t kda_prefill_cp_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_
                                       kda_dtype dt, int32_t segments) {
     if (segments < 1 || segments > CP_MAX_SEGMENTS) return 0;
     if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
-    if (check_common((int32_t)((int64_t)nseq * segments), total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    const int64_t segs = (int64_t)nseq * segments;
+    if (check_common((int32_t)segs, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    if (segs * H * dk * (dk > dv ? dk : dv) >= (int64_t(1) << 31)) return 0;
     return cp_layout(total_tokens, nseq, H, dk, dv, segments).total;
 }
 
@@ -199,6 +223,9 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const voi
     if (segs >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     st = check_common((int32_t)segs, total_tokens, H, dk, dv, dt);
     if (st != KDA_OK) return st;
+    // the identity and final-copy kernels run one work-item per element of the pieces'
+    // dk x dk (or dk x dv) matrices in a 1-D grid
+    if (segs * H * dk * (dk > dv ? dk : dv) >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, total_tokens > 0);
     if (st != KDA_OK) return st;
     st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
@@ -321,9 +348,10 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v, const 
                                    nullptr, B, T, H, dk, dv, dt, stream);
 }
 
+
 size_t kda_prefill_backward_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
                                             int32_t dv, kda_dtype dt) {
-    if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    if (check_backward_shape(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
     return static_cast<size_t>(kda::backward_workspace_floats(total_tokens, nseq, H, dk, dv)) * sizeof(float);
 }
 
@@ -333,7 +361,7 @@ kda_status kda_prefill_backward(const void *q, const void *k, const void *v, con
                                 const float *d_o, const float *d_final, float *d_q, float *d_k, float *d_v,
                                 float *d_log_alpha, float *d_beta, float *d_init, void *workspace, size_t ws_bytes,
                                 void *stream) {
-    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    kda_status st = check_backward_shape(nseq, total_tokens, H, dk, dv, dt);
     if (st != KDA_OK) return st;
     const bool any = total_tokens > 0;
     st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, any);

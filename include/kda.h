@@ -40,6 +40,13 @@
  *
  * Supported shapes: dk, dv in {16, 32, 64, 128} (any combination); H >= 1;
  * nseq >= 1; total_tokens >= 0 (< 2^31).  Chunk length is fixed at 16 tokens.
+ * Launch limits of the prefill-family calls (a dispatch holds fewer than 2^32
+ * work-items, and 16-token row extents are kept in 32 bits): nseq * H < 2^20
+ * (sequence-head chains), H * max(dk, dv) < 2^24, and for KDA_F32 inputs
+ * floor(N/16) + nseq < 2^26 chunk slots; the backward also needs
+ * (floor(N/16) + nseq) * H < 2^24 and the context-parallel call
+ * nseq * segments * H * dk * max(dk, dv) < 2^31.  Larger shapes return
+ * KDA_ERR_SHAPE before any launch.
  *
  * Ownership and synchronisation: every buffer is allocated by the caller; the
  * library never allocates, frees or synchronises.  Pointers are device
@@ -76,7 +83,7 @@ typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,         /* a required pointer is NULL */
     KDA_ERR_ALIGN = 2,        /* a pointer violates the alignment rules above */
-    KDA_ERR_SHAPE = 3,        /* nseq < 1, H < 1, B < 1, or total_tokens out of range */
+    KDA_ERR_SHAPE = 3,        /* nseq < 1, H < 1, B < 1, total_tokens out of range, or a launch limit exceeded */
     KDA_ERR_UNSUPPORTED = 4,  /* dk / dv not in {16,32,64,128}, or unknown dtype */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kda_prefill_workspace_bytes */
     KDA_ERR_HIP = 6           /* a kernel launch failed; see kda_last_hip_error() */

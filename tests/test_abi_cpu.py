@@ -248,3 +248,26 @@ def test_prefill_cp_workspace_and_arguments(lib):
     assert call(a10=24) == 4            # dk
     assert call(a12=7) == 4             # dtype
     assert call(a15=FAKE + 4) == 2      # final_state misaligned
+
+
+def test_launch_limits_are_checked_before_any_launch(lib):
+    """Shapes whose launches would exceed 2^32 work-items in a grid dimension (or 32-bit row
+    extents) are rejected on the host with KDA_ERR_SHAPE, at each bound."""
+    # (sequence, head) chains: nseq * H < 2^20
+    assert lib.kda_prefill_workspace_bytes(0, (1 << 20) // 96 + 1, 96, 128, 128, 1) == 0
+    assert lib.kda_prefill_workspace_bytes(0, (1 << 20) // 96, 96, 128, 128, 1) > 0
+    assert _prefill(lib, nseq=1 << 14, H=64, wsb=1 << 40) == 3
+    assert _prefill(lib, nseq=(1 << 14) - 1, H=64, wsb=16) == 5           # in range: fails later, on the workspace
+    # 16-token row extents: H * max(dk, dv) < 2^24
+    assert _prefill(lib, H=1 << 17, dk=128, dv=16, wsb=1 << 40) == 3
+    assert _prefill(lib, H=(1 << 17) - 1, dk=128, dv=16, wsb=16) == 5
+    # fp32 chunk-local grid: floor(N/16) + nseq < 2^26 slots
+    assert _prefill(lib, N=1 << 30, dt=kda.KDA_F32, wsb=1 << 40) == 3
+    assert _prefill(lib, N=1 << 30, dt=kda.KDA_BF16, wsb=16) == 5         # bf16 launches in batches
+    # backward per-(slot, head) kernels: slots * H < 2^24
+    assert lib.kda_prefill_backward_workspace_bytes(1 << 24, 1, 16, 16, 16, 1) == 0
+    assert lib.kda_prefill_backward_workspace_bytes(1 << 24, 1, 15, 16, 16, 1) > 0
+    # context-parallel identity / final-copy grids: segs * H * dk * max(dk, dv) < 2^31
+    assert lib.kda_prefill_cp_workspace_bytes(64, 64, 64, 128, 128, 1, 32) == 0    # exactly 2^31
+    assert lib.kda_prefill_cp_workspace_bytes(64, 64, 64, 128, 128, 1, 16) > 0
+

@@ -34,7 +34,11 @@ def _prefill_case(dev, seqlens, H, dk, dv, dtype, seed=0, gate="neg_softplus", i
     init_state = workloads.random_state(len(seqlens), H, dk, dv, device=dev, seed=seed) if init else None
     say(f"  case: seqlens={list(seqlens)[:8]}{'...' if len(seqlens) > 8 else ''} N={w.total_tokens} "
         f"H={H} dk={dk} dv={dv} {dtype} init={init}")
-    o, fin = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], init_state)
+    # outputs start as NaN, so a row or state the kernels never write cannot pass
+    o = torch.full((w.total_tokens, H, dv), float("nan"), dtype=torch.float32, device=dev)
+    fin = torch.full((len(seqlens), H, dk, dv), float("nan"), dtype=torch.float32, device=dev)
+    kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], init_state,
+                    o=o, final_state=fin)
     torch.cuda.synchronize()
     o_ref, f_ref = oracle_prefill(x, init_state, heads=heads)
     if heads is not None:
