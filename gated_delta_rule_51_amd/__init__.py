@@ -8,7 +8,7 @@ there is no CPU or PyTorch fallback.  If the library has not been built the
 first call raises.
 
 Names mirror the C entry points:
-    kda_prefill, kda_chunk_local, kda_inter_chunk, kda_decode_step,
+    kda_prefill, kda_prefill_noalloc, kda_chunk_local, kda_inter_chunk, kda_decode_step,
     kda_decode_window, kda_prefill_workspace_bytes, kda_status_string,
     kda_gate, kda_short_conv, kda_out_norm_gate (the layer's passes around the recurrence).
 """
@@ -27,8 +27,8 @@ GATE_LOWER_BOUND = -5.0
 
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE",
-          4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP"}
-EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_chunk_local", "kda_inter_chunk",
+          4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_TOO_LARGE"}
+EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
@@ -59,6 +59,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                 vp, vp, vp, sz, vp]
+    lib.kda_prefill_noalloc.restype = ctypes.c_int
+    lib.kda_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                        vp, vp, vp]
     lib.kda_chunk_local.restype = ctypes.c_int
     lib.kda_chunk_local.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int, vp, sz, vp]
     lib.kda_inter_chunk.restype = ctypes.c_int
@@ -244,6 +247,24 @@ def kda_prefill(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
         H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, final_state
+
+
+def kda_prefill_noalloc(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
+                        output_final_state: bool = True, o=None, final_state=None,
+                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_prefill with the workspace in the library's static device scratch (no device
+    allocation by the library; pass ``o`` and ``final_state`` to allocate nothing here either).
+    Problems above the scratch size raise KDAError (KDA_ERR_TOO_LARGE); calls that overlap on one
+    GPU race on the shared scratch."""
+    N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    cu = _cu(cu_seqlens, N, q.device)
+    nseq = cu.numel() - 1
+    o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
+                                      output_final_state)
+    _check(load_library().kda_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
+        H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _stream(stream)))
     return o, final_state
 
 

@@ -137,6 +137,10 @@ kda_status check_backward_shape(int32_t nseq, int64_t total_tokens, int32_t H, i
 
 }  // namespace
 
+namespace kda {
+kda_status record_hip_error(hipError_t e) { return hip_status(e); }
+}  // namespace kda
+
 extern "C" {
 
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
@@ -445,6 +449,8 @@ const char *kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk/dv not in {16,32,64,128} or unknown dtype";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed (see kda_last_hip_error)";
+        case KDA_ERR_TOO_LARGE: return "KDA_ERR_TOO_LARGE: the problem's workspace exceeds the static scratch of "
+                                       "kda_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES)";
         default: return "KDA: unknown status";
     }
 }

@@ -6,7 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/kda.h"
+
 namespace kda {
+
+// KDA_OK for hipSuccess; otherwise keeps e for kda_last_hip_error() (per thread) and
+// returns KDA_ERR_HIP.  Defined in api.cpp.
+kda_status record_hip_error(hipError_t e);
 
 // Workspace per (chunk slot, head): T' = (I + A_kk)^-1 diag(beta), then A_qk,
 // each stored as the A-operand fragment of a 16x16 MFMA (64 lanes x 16 bytes:

@@ -86,7 +86,8 @@ typedef enum kda_status {
     KDA_ERR_SHAPE = 3,        /* nseq < 1, H < 1, B < 1, total_tokens out of range, or a launch limit exceeded */
     KDA_ERR_UNSUPPORTED = 4,  /* dk / dv not in {16,32,64,128}, or unknown dtype */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kda_prefill_workspace_bytes */
-    KDA_ERR_HIP = 6           /* a kernel launch failed; see kda_last_hip_error() */
+    KDA_ERR_HIP = 6,          /* a kernel launch failed; see kda_last_hip_error() */
+    KDA_ERR_TOO_LARGE = 7     /* kda_prefill_noalloc: workspace above KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -346,6 +347,26 @@ kda_status kda_short_conv(const void *x, const float *w, const float *cache_in,
 kda_status kda_out_norm_gate(const float *o, const void *u, const float *w,
                              float eps, int64_t N, int32_t H, int32_t dv,
                              kda_dtype dt, void *y, void *stream);
+
+/* kda_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as kda_prefill, without the workspace: the
+ * library keeps it in a static device array of KDA_NOALLOC_SCRATCH_BYTES bytes
+ * (128 MiB), one per GPU the library runs on, held until the process ends.
+ * Problems whose kda_prefill_workspace_bytes exceed it return
+ * KDA_ERR_TOO_LARGE before any launch (2 KiB per chunk slot and head:
+ * (floor(N/16) + nseq) * H <= 65,536).  The call allocates nothing; on its
+ * first call on a device it looks up the array's device address (a failure
+ * there returns KDA_ERR_HIP).  Every call on one GPU shares that GPU's array
+ * and the array keeps the last call's contents: calls that overlap on one GPU
+ * (different streams or threads without ordering) race, so serialise them. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
+                               const void *log_alpha, const void *beta,
+                               const float *init_state, const int32_t *cu_seqlens,
+                               int32_t nseq, int64_t total_tokens, int32_t H,
+                               int32_t dk, int32_t dv, kda_dtype dt,
+                               float *o, float *final_state, void *stream);
 
 /* Static string naming a status code. */
 const char *kda_status_string(kda_status s);

@@ -271,3 +271,9 @@ def test_launch_limits_are_checked_before_any_launch(lib):
     assert lib.kda_prefill_cp_workspace_bytes(64, 64, 64, 128, 128, 1, 32) == 0    # exactly 2^31
     assert lib.kda_prefill_cp_workspace_bytes(64, 64, 64, 128, 128, 1, 16) > 0
 
+
+def test_noalloc_rejects_problems_above_the_scratch_on_the_host(lib):
+    # (floor(N/16) + nseq) * H * 2 KiB > 128 MiB: rejected before the scratch is looked up
+    f = lib.kda_prefill_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1 << 20, 96, 128, 128, 1, FAKE, None, None) == 7
+    assert kda.kda_status_string(7).startswith("KDA_ERR_TOO_LARGE")
