@@ -94,9 +94,7 @@ def host_info() -> dict:
     return {"cpu_model": model, "cores_available": cores}
 
 
-KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/chunk_local.hip", "gated_delta_rule_51_amd/csrc/inter_chunk.hip",
-                  "gated_delta_rule_51_amd/csrc/inter_chunk_ws.hip", "gated_delta_rule_51_amd/csrc/kda_device.hpp",
-                  "gated_delta_rule_51_amd/csrc/kda_launch.hpp")
+KERNEL_SOURCES = ("gated_delta_rule_51_amd/csrc/prefill_fused.hip", "gated_delta_rule_51_amd/csrc/kda_device.hpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_1m_traffic.txt")
 
 
@@ -240,15 +238,20 @@ def bench_headline(args, torch, kda, workloads, dev, cpu_baseline: bool = True) 
     x = workloads.prefill_inputs(w, device=dev, seed=0)
     dw = workloads.custom([1] * nseq, H, dk, dv)
     dsets = [workloads.decode_step_inputs(dw, 0, device=dev, seed=s) for s in range(3)]
-    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
+    ws_bytes = kda.kda_prefill_workspace_bytes(N, nseq, H, dk, dv, torch.bfloat16)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev) if ws_bytes else None
+    single_pass = ws_bytes == 0
     o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     fin = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
     od = torch.empty((nseq, H, dv), dtype=torch.float32, device=dev)
     args_x = (x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
 
+    def prefill():
+        kda.kda_prefill(*args_x, o=o, final_state=fin, workspace=ws)
+
     def step(i):
         d = dsets[i % 3]
-        kda.kda_prefill(*args_x, o=o, final_state=fin, workspace=ws)
+        prefill()
         kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
 
     log(f"[bench] headline: {args.warmup} warm-up + {args.steps} timed steps")
@@ -273,29 +276,38 @@ def bench_headline(args, torch, kda, workloads, dev, cpu_baseline: bool = True) 
         check = oracle_check(x, o, od, fin, dsets[last], PARITY_HEADS, tol=1e-2)
         log(f"[bench] parity: {check['parity']}")
 
-    # per-kernel durations: the prefill's two kernels and the decode step, HIP events on the
-    # stream every call is enqueued on (torch's current stream)
+    # per-kernel durations: HIP events on the stream every call is enqueued on (torch's
+    # current stream) around the prefill (one kernel on this shape) and the decode step
     reps = max(3, min(args.steps, 10))
-    t_cl, t_ic, t_dec = Timer(torch, reps), Timer(torch, reps), Timer(torch, reps)
+    t_pf, t_dec = Timer(torch, reps), Timer(torch, reps)
     for i in range(reps):
         d = dsets[i % 3]
-        with t_cl:
-            kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
-        with t_ic:
-            kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
-                                o=o, final_state=fin)
+        with t_pf:
+            prefill()
         with t_dec:
             kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
     torch.cuda.synchronize()
-    kernels = {"chunk_local": t_cl.mean_ms(), "inter_chunk": t_ic.mean_ms(), "decode": t_dec.mean_ms()}
-    kernel_names = {"chunk_local": "chunk_local_bf16_kernel<128>", "inter_chunk": "inter_chunk_ws_kernel<128,128,4,4>",
-                    "decode": "decode_kernel"}
+    kernels = {"prefill": t_pf.mean_ms(), "decode": t_dec.mean_ms()}
+    # the two-kernel path (chunk-local pass, then the recurrence) on the same inputs, for reference
+    two = None
+    if single_pass and not args.no_two_kernel:
+        wsp = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
+        t_cl, t_ic = Timer(torch, 3), Timer(torch, 3)
+        for _ in range(3):
+            with t_cl:
+                kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], wsp)
+            with t_ic:
+                kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], wsp, None,
+                                    o=o, final_state=fin)
+        torch.cuda.synchronize()
+        two = {"chunk_local_ms": round(t_cl.mean_ms(), 4), "inter_chunk_ms": round(t_ic.mean_ms(), 4),
+               "total_ms": round(t_cl.mean_ms() + t_ic.mean_ms(), 4)}
+        del wsp
     th = N * H
-    prefill_ms = kernels["chunk_local"] + kernels["inter_chunk"]
+    prefill_ms = kernels["prefill"]
     flops = th * prefill_flops_per_token_head(dk, dv)
     alg_bytes = th * prefill_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4
-    dom = max(("chunk_local", "inter_chunk"), key=lambda k: kernels[k])
-    ach = alg_bytes / (kernels[dom] * 1e-3) / 1e9
+    ach = alg_bytes / (prefill_ms * 1e-3) / 1e9
     traffic, hip_kernel = measured_traffic()
     res = {
         "value": (N + nseq) / (wall_ms * 1e-3), "ms_per_step": round(wall_ms, 4),
@@ -305,17 +317,19 @@ def bench_headline(args, torch, kda, workloads, dev, cpu_baseline: bool = True) 
                    "step": "kda_prefill over the packed batch, then kda_decode_step (1 token per sequence) "
                            "from the final states"},
         "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
-        "prefill": {"ms": round(prefill_ms, 4), "tokens_per_s": N / (prefill_ms * 1e-3),
+        "prefill": {"ms": round(prefill_ms, 4), "single_pass": single_pass, "tokens_per_s": N / (prefill_ms * 1e-3),
                     "tflops": flops / (prefill_ms * 1e-3) / 1e12,
                     "mfma_peak_frac": flops / (prefill_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                    "hbm_gbs_algorithmic": alg_bytes / (prefill_ms * 1e-3) / 1e9,
-                    "hbm_roofline_frac": alg_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "hbm_gbs_algorithmic": ach, "hbm_roofline_frac": ach / HBM_PEAK_GBS,
                     "t_hbm_ms": alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3},
-        "roofline": {"kernel": dom, "hip_kernel": hip_kernel or kernel_names[dom], "bound": "hbm", "achieved": ach,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": alg_bytes,
+        "roofline": {"kernel": "prefill" if single_pass else "prefill (chunk_local + inter_chunk)",
+                     "hip_kernel": hip_kernel or ("prefill_fused_kernel<128,128,4,2>" if single_pass else None),
+                     "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
                      "bytes_formula": "N*H*(2*(3*dk+dv+1) + 4*dv) + nseq*H*dk*dv*4"},
     }
+    if two is not None:
+        res["prefill"]["two_kernel_path"] = two
     if check is not None:
         res["parity"] = check["parity"]
         frac = len(PARITY_HEADS) / H
@@ -336,32 +350,30 @@ def bench_headline(args, torch, kda, workloads, dev, cpu_baseline: bool = True) 
 
 
 def bench_batched(args, torch, kda, workloads, dev):
+    """B=4, H=8, T=2048 (three input sets rotated, ~105 MB each, so no set stays in the 256 MB
+    Infinity Cache): kda_prefill then one decode token per sequence from the final states."""
     w = workloads.workload(2)
     N, H, dk, dv, nseq = w.total_tokens, w.H, w.dk, w.dv, w.nseq
     sets = [workloads.prefill_inputs(w, device=dev, seed=s) for s in range(3)]
     dw = workloads.custom([1] * nseq, H, dk, dv)
     dsets = [workloads.decode_step_inputs(dw, 0, device=dev, seed=s) for s in range(3)]
-    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
     o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     fin = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
     od = torch.empty((nseq, H, dv), dtype=torch.float32, device=dev)
-    n_ev = args.warmup + args.steps
-    t_cl, t_ic, t_dec = Timer(torch, n_ev), Timer(torch, n_ev), Timer(torch, n_ev)
+    n_ev = args.steps
+    t_pf, t_dec = Timer(torch, n_ev), Timer(torch, n_ev)
 
     def step(i, timed):
         x, d = sets[i % 3], dsets[i % 3]
         if timed:
-            with t_cl:
-                kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
-            with t_ic:
-                kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
-                                    o=o, final_state=fin)
+            with t_pf:
+                kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], o=o,
+                                final_state=fin)
             with t_dec:
                 kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
         else:
-            kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
-            kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, None,
-                                o=o, final_state=fin)
+            kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], o=o,
+                            final_state=fin)
             kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], fin, o=od)
 
     for i in range(args.warmup):
@@ -375,8 +387,8 @@ def bench_batched(args, torch, kda, workloads, dev):
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     graph_ms = None
     if args.graph:
-        # the same steps replayed from HIP graphs (one per input set: the three launches of a
-        # step captured once); on this stack a replay costs more than the launch gaps it removes
+        # the same steps replayed from HIP graphs (one per input set: the launches of a step
+        # captured once)
         graphs = []
         for i in range(3):
             g = torch.cuda.CUDAGraph()
@@ -396,24 +408,26 @@ def bench_batched(args, torch, kda, workloads, dev):
     for i in range(args.steps):
         step(i, True)
     torch.cuda.synchronize()
-    ms_cl, ms_ic, ms_dec = t_cl.mean_ms(), t_ic.mean_ms(), t_dec.mean_ms()
+    ms_pf, ms_dec = t_pf.mean_ms(), t_dec.mean_ms()
     tokens = N + nseq
     th = N * H
     flops = th * prefill_flops_per_token_head(dk, dv)
-    return {
-        "w": w, "wall_ms": wall_ms, "graph_ms": graph_ms, "tokens": tokens, "ms_chunk_local": ms_cl, "ms_inter_chunk": ms_ic,
-        "ms_decode": ms_dec, "prefill_tflops": flops / ((ms_cl + ms_ic) * 1e-3) / 1e12,
-    }
+    return {"w": w, "wall_ms": wall_ms, "graph_ms": graph_ms, "tokens": tokens, "ms_prefill": ms_pf,
+            "ms_decode": ms_dec, "prefill_tflops": flops / (ms_pf * 1e-3) / 1e12}
 
 
 def bench_prefill_workload(index, torch, kda, workloads, dev, reps: int):
+    """kda_prefill on a prefill workload (one kernel for bf16 with dk = dv = 128), and the two-kernel
+    path (kda_chunk_local + kda_inter_chunk) on the same inputs for reference."""
     w = workloads.workload(index)
     N, H, dk, dv, nseq = w.total_tokens, w.H, w.dk, w.dv, w.nseq
     log(f"[bench] generating workload {w.name}: {w.notes}")
     x = workloads.prefill_inputs(w, device=dev, seed=0)
-    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
     o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     fin = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+    args_x = (x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    ms = _event_ms(torch, lambda: kda.kda_prefill(*args_x, o=o, final_state=fin), reps)
+    ws = kda.alloc_workspace(N, nseq, H, dk, dv, torch.bfloat16, dev)
     t_cl, t_ic = Timer(torch, reps + 1), Timer(torch, reps + 1)
 
     def run():
@@ -430,13 +444,13 @@ def bench_prefill_workload(index, torch, kda, workloads, dev, reps: int):
         run()
     torch.cuda.synchronize()
     ms_cl, ms_ic = t_cl.mean_ms(), t_ic.mean_ms()
-    ms = ms_cl + ms_ic
     th = N * H
     flops = th * prefill_flops_per_token_head(dk, dv)
     alg_bytes = th * prefill_bytes_per_token_head(dk, dv) + nseq * H * dk * dv * 4
     res = {
         "workload": w.name, "tokens": N, "heads": H, "sequences": nseq, "ms": round(ms, 4),
-        "ms_chunk_local": round(ms_cl, 4), "ms_inter_chunk": round(ms_ic, 4),
+        "two_kernel_path": {"ms_chunk_local": round(ms_cl, 4), "ms_inter_chunk": round(ms_ic, 4),
+                            "ms": round(ms_cl + ms_ic, 4)},
         "tokens_per_s": N / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
         "mfma_peak_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "hbm_gbs_algorithmic": alg_bytes / (ms * 1e-3) / 1e9,
@@ -738,6 +752,8 @@ def main() -> int:
     ap.add_argument("--only", default="all",
                     choices=["all", "main", "batched", "k3", "decode", "layer", "backward", "cp", "none"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-two-kernel", action="store_true",
+                    help="skip timing the two-kernel prefill path beside the single-pass kernel")
     ap.add_argument("--graph", action="store_true",
                     help="also time the batched step as HIP graph replays (reported beside the eager time)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -773,7 +789,7 @@ def main() -> int:
         log("[bench] batched prefill B=4 H=8 T=2048 + 1 decode token per sequence")
         m = bench_batched(args, torch, kda, workloads, dev)
         w = m["w"]
-        kernels = {"chunk_local": m["ms_chunk_local"], "inter_chunk": m["ms_inter_chunk"], "decode": m["ms_decode"]}
+        kernels = {"prefill": m["ms_prefill"], "decode": m["ms_decode"]}
         th = w.total_tokens * w.H
         alg = th * prefill_bytes_per_token_head(w.dk, w.dv) + w.nseq * w.H * w.dk * w.dv * 4
         out["batched"] = {
@@ -781,7 +797,7 @@ def main() -> int:
             "ms_per_step": round(m["wall_ms"], 5), "tokens_per_s": m["tokens"] / (m["wall_ms"] * 1e-3),
             "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
             "prefill_tflops": m["prefill_tflops"],
-            "inter_chunk_hbm_frac": alg / (m["ms_inter_chunk"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "prefill_hbm_frac": alg / (m["ms_prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if m["graph_ms"] is not None:
             out["batched"]["ms_per_step_graph_replay"] = round(m["graph_ms"], 5)
     if args.only in ("all", "k3"):

@@ -28,7 +28,8 @@ GATE_LOWER_BOUND = -5.0
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE",
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_TOO_LARGE"}
-EXPORTS = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
+EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_prefill", "kda_prefill_single_pass",
+           "kda_inter_chunk_shaped", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
@@ -56,12 +57,20 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.kda_prefill_workspace_bytes.restype = sz
     lib.kda_prefill_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_chunk_workspace_bytes.restype = sz
+    lib.kda_chunk_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                 vp, vp, vp, sz, vp]
     lib.kda_prefill_noalloc.restype = ctypes.c_int
     lib.kda_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                         vp, vp, vp]
+    lib.kda_prefill_single_pass.restype = ctypes.c_int
+    lib.kda_prefill_single_pass.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                            i32, i32, vp, vp, vp]
+    lib.kda_inter_chunk_shaped.restype = ctypes.c_int
+    lib.kda_inter_chunk_shaped.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
+                                           vp, sz, i32, i32, vp, vp, vp]
     lib.kda_chunk_local.restype = ctypes.c_int
     lib.kda_chunk_local.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int, vp, sz, vp]
     lib.kda_inter_chunk.restype = ctypes.c_int
@@ -209,7 +218,15 @@ def _prefill_outputs(N, H, dk, dv, nseq, device, o, final_state, init_state, out
 
 def kda_prefill_workspace_bytes(total_tokens: int, nseq: int, H: int, dk: int, dv: int,
                                 dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes kda_prefill needs (0: none -- bf16 with dk = dv = 128 and at least 256
+    (sequence, head) chains runs in one kernel)."""
     return int(load_library().kda_prefill_workspace_bytes(total_tokens, nseq, H, dk, dv, _dtype_code(dtype)))
+
+
+def kda_chunk_workspace_bytes(total_tokens: int, nseq: int, H: int, dk: int, dv: int,
+                              dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of the two phases (kda_chunk_local, kda_inter_chunk)."""
+    return int(load_library().kda_chunk_workspace_bytes(total_tokens, nseq, H, dk, dv, _dtype_code(dtype)))
 
 
 def _cu(cu_seqlens, N, device):
@@ -221,7 +238,8 @@ def _cu(cu_seqlens, N, device):
 
 
 def alloc_workspace(total_tokens: int, nseq: int, H: int, dk: int, dv: int, dtype, device) -> torch.Tensor:
-    nbytes = kda_prefill_workspace_bytes(total_tokens, nseq, H, dk, dv, dtype)
+    """A workspace for the two phases (kda_chunk_local, kda_inter_chunk)."""
+    nbytes = kda_chunk_workspace_bytes(total_tokens, nseq, H, dk, dv, dtype)
     return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=device)
 
 
@@ -240,13 +258,31 @@ def kda_prefill(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
     o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
                                       output_final_state)
     nbytes = kda_prefill_workspace_bytes(N, nseq, H, dk, dv, q.dtype)
-    if workspace is None:
-        workspace = alloc_workspace(N, nseq, H, dk, dv, q.dtype, q.device)
-    _check_workspace(workspace, q.device, nbytes)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    if workspace is not None:
+        _check_workspace(workspace, q.device, nbytes)
     _check(load_library().kda_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
         H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, final_state
+
+
+def kda_prefill_single_pass(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *, consumers: int = 0,
+                            slices: int = 0, output_final_state: bool = True, o=None, final_state=None,
+                            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The single-pass prefill kernel (bf16, dk = dv = 128) with an explicit workgroup shape
+    (consumers, slices) in {(2, 1), (4, 1), (4, 2)}; (0, 0) chooses.  For tuning and tests."""
+    N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    cu = _cu(cu_seqlens, N, q.device)
+    nseq = cu.numel() - 1
+    o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
+                                      output_final_state)
+    _check(load_library().kda_prefill_single_pass(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N,
+        H, dk, dv, _dtype_code(q.dtype), int(consumers), int(slices), _ptr(o), _ptr(final_state),
+        _stream(stream)))
     return o, final_state
 
 
@@ -303,7 +339,7 @@ def kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, workspace, *, stream=None
         raise ValueError("expected q, k, log_alpha [N, H, dk], beta [N, H]")
     _check_dev("cu_seqlens", cu_seqlens, q.device, torch.int32)
     nseq = cu_seqlens.numel() - 1
-    _check_workspace(workspace, q.device, kda_prefill_workspace_bytes(N, nseq, H, dk, 16, q.dtype))
+    _check_workspace(workspace, q.device, kda_chunk_workspace_bytes(N, nseq, H, dk, 16, q.dtype))
     _check(load_library().kda_chunk_local(
         _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), nseq, N, H, dk,
         _dtype_code(q.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -311,8 +347,10 @@ def kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, workspace, *, stream=None
 
 
 def kda_inter_chunk(q, k, v, log_alpha, cu_seqlens, workspace, init_state=None, *, o=None,
-                    final_state=None, output_final_state: bool = True, stream=None):
-    """Inter-chunk phase only; reads the workspace written by kda_chunk_local."""
+                    final_state=None, output_final_state: bool = True, consumers: int = 0, producers: int = 0,
+                    stream=None):
+    """Inter-chunk phase only; reads the workspace written by kda_chunk_local.  ``consumers`` and
+    ``producers`` pick the warp-specialised kernel's workgroup shape (0, 0 = choose)."""
     _check_gpu("q", q)
     for name, t in (("k", k), ("v", v), ("log_alpha", log_alpha)):
         _check_dev(name, t, q.device, q.dtype)
@@ -324,11 +362,11 @@ def kda_inter_chunk(q, k, v, log_alpha, cu_seqlens, workspace, init_state=None, 
     nseq = cu_seqlens.numel() - 1
     o, final_state = _prefill_outputs(N, H, dk, dv, nseq, q.device, o, final_state, init_state,
                                       output_final_state)
-    _check_workspace(workspace, q.device, kda_prefill_workspace_bytes(N, nseq, H, dk, dv, q.dtype))
-    _check(load_library().kda_inter_chunk(
+    _check_workspace(workspace, q.device, kda_chunk_workspace_bytes(N, nseq, H, dk, dv, q.dtype))
+    _check(load_library().kda_inter_chunk_shaped(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(init_state), _ptr(cu_seqlens), nseq, N, H,
         dk, dv, _dtype_code(q.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _ptr(o), _ptr(final_state), _stream(stream)))
+        int(consumers), int(producers), _ptr(o), _ptr(final_state), _stream(stream)))
     return o, final_state
 
 

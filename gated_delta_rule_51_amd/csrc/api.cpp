@@ -143,9 +143,16 @@ kda_status record_hip_error(hipError_t e) { return hip_status(e); }
 
 extern "C" {
 
+size_t kda_chunk_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
+                                 int32_t dv, kda_dtype dt) {
+    if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    return workspace_bytes(total_tokens, nseq, H);
+}
+
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
                                    int32_t dv, kda_dtype dt) {
     if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    if (kda::prefill_fused_supported(dk, dv, dt == KDA_BF16, (int64_t)nseq * H)) return 0;  // single pass
     return workspace_bytes(total_tokens, nseq, H);
 }
 
@@ -181,7 +188,32 @@ kda_status kda_inter_chunk(const void *q, const void *k, const void *v, const vo
     if (!aligned16(workspace)) return KDA_ERR_ALIGN;
     kda::InterChunkArgs a{q, k, v, log_alpha, init_state, cu_seqlens, nseq, H, dk, dv,
                           total_tokens, dt == KDA_BF16, static_cast<const float *>(workspace), o,
-                          final_state, 0, stream};
+                          final_state, 0, 0, stream};
+    return hip_status(kda::launch_inter_chunk(a));
+}
+
+kda_status kda_inter_chunk_shaped(const void *q, const void *k, const void *v, const void *log_alpha,
+                                  const float *init_state, const int32_t *cu_seqlens, int32_t nseq,
+                                  int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                  const void *workspace, size_t ws_bytes, int32_t consumers, int32_t producers,
+                                  float *o, float *final_state, void *stream) {
+    if (consumers == 0 && producers == 0)
+        return kda_inter_chunk(q, k, v, log_alpha, init_state, cu_seqlens, nseq, total_tokens, H, dk, dv, dt,
+                               workspace, ws_bytes, o, final_state, stream);
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    if (dt != KDA_BF16 || dk < 32 || !kda::inter_chunk_ws_shape_built(dk, dv, consumers, producers))
+        return KDA_ERR_UNSUPPORTED;
+    st = check_inputs({q, k, v, log_alpha}, false, nullptr, true, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
+    if (st != KDA_OK) return st;
+    if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    if (!workspace || ws_bytes < workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    kda::InterChunkArgs a{q, k, v, log_alpha, init_state, cu_seqlens, nseq, H, dk, dv,
+                          total_tokens, true, static_cast<const float *>(workspace), o,
+                          final_state, consumers, producers, stream};
     return hip_status(kda::launch_inter_chunk(a));
 }
 
@@ -197,6 +229,12 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
     st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
     if (st != KDA_OK) return st;
     if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    if (kda::prefill_fused_supported(dk, dv, dt == KDA_BF16, (int64_t)nseq * H)) {
+        // one kernel: the chunk-local operands stay on chip, the workspace is not used
+        kda::PrefillFusedArgs a{q, k, v, log_alpha, beta, init_state, cu_seqlens, nseq, H, dk, dv,
+                                true, o, final_state, stream};
+        return hip_status(kda::launch_prefill_fused(a, 0, 0));
+    }
     if (!workspace || ws_bytes < workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KDA_ERR_ALIGN;
     st = kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, nseq, total_tokens, H, dk, dt,
@@ -204,6 +242,25 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
     if (st != KDA_OK) return st;
     return kda_inter_chunk(q, k, v, log_alpha, init_state, cu_seqlens, nseq, total_tokens, H, dk,
                            dv, dt, workspace, ws_bytes, o, final_state, stream);
+}
+
+kda_status kda_prefill_single_pass(const void *q, const void *k, const void *v, const void *log_alpha,
+                                   const void *beta, const float *init_state, const int32_t *cu_seqlens,
+                                   int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                                   kda_dtype dt, int32_t consumers, int32_t slices, float *o, float *final_state,
+                                   void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    if (dt != KDA_BF16 || dk != 128 || dv != 128 || !kda::prefill_fused_shape_built(consumers, slices))
+        return KDA_ERR_UNSUPPORTED;
+    st = check_inputs({q, k, v, log_alpha}, true, beta, true, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens}, {init_state, final_state, o});
+    if (st != KDA_OK) return st;
+    if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    kda::PrefillFusedArgs a{q, k, v, log_alpha, beta, init_state, cu_seqlens, nseq, H, dk, dv,
+                            true, o, final_state, stream};
+    return hip_status(kda::launch_prefill_fused(a, consumers, slices));
 }
 
 size_t kda_prefill_cp_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv,
@@ -252,18 +309,18 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const voi
     }
     // each segment from a zero state: S~ (outputs not written)
     kda::InterChunkArgs a1{q, k, v, log_alpha, nullptr, cu_seg, ns, H, dk, dv, total_tokens, bf16, cl,
-                           nullptr, St, 0, stream};
+                           nullptr, St, 0, 0, stream};
     if ((e = kda::launch_inter_chunk(a1)) != hipSuccess) return hip_status(e);
     // each segment's transition M: v = 0 from the identity, in place
     if ((e = kda::launch_cp_identity(M, segs * H, dk, stream)) != hipSuccess) return hip_status(e);
     kda::InterChunkArgs a2{q, k, nullptr, log_alpha, M, cu_seg, ns, H, dk, dk, total_tokens, bf16, cl,
-                           nullptr, M, 0, stream};
+                           nullptr, M, 0, 0, stream};
     if ((e = kda::launch_inter_chunk(a2)) != hipSuccess) return hip_status(e);
     if ((e = kda::launch_cp_scan(init_state, M, St, Sin, nseq, H, dk, dv, segments, stream)) != hipSuccess)
         return hip_status(e);
     // the outputs from the exact incoming states; each segment's final state replaces its S_in
     kda::InterChunkArgs a3{q, k, v, log_alpha, Sin, cu_seg, ns, H, dk, dv, total_tokens, bf16, cl,
-                           o, Sin, 0, stream};
+                           o, Sin, 0, 0, stream};
     if ((e = kda::launch_inter_chunk(a3)) != hipSuccess) return hip_status(e);
     if (final_state) e = kda::launch_cp_final(Sin, final_state, nseq, H, dk, dv, segments, stream);
     return hip_status(e);

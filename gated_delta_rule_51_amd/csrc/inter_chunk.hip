@@ -33,7 +33,6 @@
 // K~^T Delta use split-bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation;
 // the state stays fp32.  fp32 inputs use fp32 MFMAs throughout.
 #include <stdio.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -537,38 +536,21 @@ hipError_t launch_inter_chunk(const InterChunkArgs &a) {
     // serial recurrence is latency-bound (few (sequence, head) chains) and when
     // thousands of chains make the work throughput-bound.  This file's kernel
     // serves fp32 inputs and dk = 16.
-    // Tuning knobs: KDA_WS = "<consumers>x<producers>" forces the warp-
-    // specialised kernel with that shape; KDA_WAVES in {2, 4, 8} forces this
-    // file's kernel with that many waves (dk = dv = 128).
     const int64_t nchains = (int64_t)a.nseq * a.H;
-    const char *classic = getenv("KDA_WAVES");
-    const char *ws_shape = getenv("KDA_WS");
-    const bool big = a.dk == 128 && a.dv == 128 && nchains >= 256;
-    if (a.bf16 && a.dk >= 32 && a.waves_per_group == 0 && !classic) {
-        int ncw = nchains < 64 ? 2 : 4;
-        if (ncw > a.dv / 16) ncw = a.dv / 16;
-        int npw = a.dk / 16 < 4 ? a.dk / 16 : 4;
-        if (ws_shape) {
-            int c = 0, p = 0;
-            if (sscanf(ws_shape, "%dx%d", &c, &p) == 2) {
-                ncw = c;
-                npw = p;
-            }
+    if (a.bf16 && a.dk >= 32) {
+        int ncw = a.ws_consumers, npw = a.ws_producers;
+        if (ncw == 0 && npw == 0) {
+            ncw = nchains < 64 ? 2 : 4;
+            if (ncw > a.dv / 16) ncw = a.dv / 16;
+            npw = a.dk / 16 < 4 ? a.dk / 16 : 4;
         }
         return launch_inter_chunk_ws(a, ncw, npw);
     }
-    int nw = a.waves_per_group;
-    if (nw <= 0) {
-        nw = default_waves(a.dk, a.dv);
-        // dk = dv = 128: one 8-wave workgroup per (sequence, head) when there are
-        // enough chains to give every CU one; otherwise two 4-wave workgroups per
-        // chain so that twice as many CUs work on the serial recurrence.
-        if (a.dk == 128 && a.dv == 128) nw = big ? 8 : 4;
-        if (a.dk == 128 && a.dv == 128 && classic) {
-            const int w = atoi(classic);
-            if (w == 2 || w == 4 || w == 8) nw = w;
-        }
-    }
+    int nw = default_waves(a.dk, a.dv);
+    // dk = dv = 128: one 8-wave workgroup per (sequence, head) when there are enough
+    // chains to give every CU one; otherwise two 4-wave workgroups per chain so that
+    // twice as many CUs work on the serial recurrence.
+    if (a.dk == 128 && a.dv == 128) nw = nchains >= 256 ? 8 : 4;
     return a.bf16 ? launch_ic_dt<__bf16>(a, nw) : launch_ic_dt<float>(a, nw);
 }
 

@@ -38,7 +38,6 @@
 // residuals lo = x - hi of those splits are formed on the matrix cores (an
 // exact product with -I), which keeps the vector ALUs -- the busiest unit
 // here -- for the rest.
-#include <stdlib.h>
 
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
@@ -261,6 +260,11 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
             cload(X1, 1);
             cload(X2, 2);
             __syncthreads();  // operand set 0 ready
+            // Everything loaded so far (state, first inputs) has arrived before the loop: the
+            // wait-count pass otherwise merges these loads, issued with few others after them,
+            // into the loop header and makes the first chunks of every unrolled trip wait for
+            // the loads and stores of the chunk just before.
+            __builtin_amdgcn_s_waitcnt(0);
             auto citer = [&](int c, CIn &X) {
                 advance(c & 1, X, c);
                 cload(X, c + 3);
@@ -456,24 +460,33 @@ static hipError_t launch_ws_t(const InterChunkArgs &a) {
 
 // Shapes: consumers NC (16 columns each), producers NP.  Returns
 // hipErrorInvalidValue for a shape that is not instantiated.
+// Shapes built: for dk = dv = 128 four or two consumers with four producers; for the other
+// head sizes min(dv/16, 4) or min(dv/16, 2) consumers with min(dk/16, 4) producers.
+#define KDA_WS_SHAPES(CASE) \
+    CASE(128, 128, 4, 4) CASE(128, 128, 2, 4) \
+    KDA_WS_ROW(CASE, 32) KDA_WS_ROW(CASE, 64) KDA_WS_ROW(CASE, 128)
+#define KDA_WS_DEF(CASE, DKV, DVV) CASE(DKV, DVV, ((DVV / 16) < 4 ? (DVV / 16) : 4), ((DKV / 16) < 4 ? (DKV / 16) : 4))
+#define KDA_WS_DEF2(CASE, DKV, DVV) CASE(DKV, DVV, ((DVV / 16) < 2 ? (DVV / 16) : 2), ((DKV / 16) < 4 ? (DKV / 16) : 4))
+#define KDA_WS_ROW(CASE, DKV) KDA_WS_DEF(CASE, DKV, 16) KDA_WS_DEF(CASE, DKV, 32) KDA_WS_DEF(CASE, DKV, 64) \
+    KDA_WS_DEF(CASE, DKV, 128) KDA_WS_DEF2(CASE, DKV, 64) KDA_WS_DEF2(CASE, DKV, 128)
+
+bool inter_chunk_ws_shape_built(int dk, int dv, int ncw, int npw) {
+#define KDA_WS_HAS(DKV, DVV, NCV, NPV) if (dk == DKV && dv == DVV && ncw == NCV && npw == NPV) return true;
+    KDA_WS_SHAPES(KDA_WS_HAS)
+#undef KDA_WS_HAS
+    return false;
+}
+
 hipError_t launch_inter_chunk_ws(const InterChunkArgs &a, int ncw, int npw) {
 #define KDA_WS_CASE(DKV, DVV, NCV, NPV) \
     if (a.dk == DKV && a.dv == DVV && ncw == NCV && npw == NPV) return launch_ws_t<DKV, DVV, NCV, NPV>(a);
-    // dk = dv = 128: the default shapes (4 or 2 consumers, 4 producers) and
-    // the others a tuning sweep may pick
-    KDA_WS_CASE(128, 128, 4, 4) KDA_WS_CASE(128, 128, 2, 4) KDA_WS_CASE(128, 128, 4, 2)
-    KDA_WS_CASE(128, 128, 1, 4) KDA_WS_CASE(128, 128, 2, 2) KDA_WS_CASE(128, 128, 1, 2)
-    // the other head sizes: min(dv/16, 4) or min(dv/16, 2) consumers, min(dk/16, 4) producers
-#define KDA_WS_DEF(DKV, DVV) KDA_WS_CASE(DKV, DVV, ((DVV / 16) < 4 ? (DVV / 16) : 4), ((DKV / 16) < 4 ? (DKV / 16) : 4))
-#define KDA_WS_DEF2(DKV, DVV) KDA_WS_CASE(DKV, DVV, ((DVV / 16) < 2 ? (DVV / 16) : 2), ((DKV / 16) < 4 ? (DKV / 16) : 4))
-#define KDA_WS_ROW(DKV) KDA_WS_DEF(DKV, 16) KDA_WS_DEF(DKV, 32) KDA_WS_DEF(DKV, 64) KDA_WS_DEF(DKV, 128) \
-    KDA_WS_DEF2(DKV, 64) KDA_WS_DEF2(DKV, 128)
-    KDA_WS_ROW(32) KDA_WS_ROW(64) KDA_WS_ROW(128)
-#undef KDA_WS_ROW
-#undef KDA_WS_DEF2
-#undef KDA_WS_DEF
+    KDA_WS_SHAPES(KDA_WS_CASE)
 #undef KDA_WS_CASE
     return hipErrorInvalidValue;
 }
+#undef KDA_WS_ROW
+#undef KDA_WS_DEF2
+#undef KDA_WS_DEF
+#undef KDA_WS_SHAPES
 
 }  // namespace kda

@@ -76,7 +76,18 @@ struct InterChunkArgs {
     bool bf16;
     const float *ws;
     float *o, *fin;
-    int32_t waves_per_group;  // 0 = choose automatically
+    int32_t ws_consumers, ws_producers;  // warp-specialised kernel shape; 0, 0 = choose automatically
+    void *stream;
+};
+
+// Single-pass prefill (prefill_fused.hip): bf16 inputs, dk = dv = 128, many chains; no workspace.
+struct PrefillFusedArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float *init;
+    const int32_t *cu;
+    int32_t nseq, H, dk, dv;
+    bool bf16;
+    float *o, *fin;
     void *stream;
 };
 
@@ -144,6 +155,13 @@ hipError_t launch_cp_scan(const float *init, const float *M, const float *St, fl
                           int32_t dk, int32_t dv, int32_t R, void *stream);
 hipError_t launch_cp_final(const float *Sin, float *fin, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R,
                            void *stream);
+
+bool prefill_fused_supported(int dk, int dv, bool bf16, int64_t chains);
+// consumers nc with sl 16-column slices each; (0, 0) = choose from the number of chains;
+// hipErrorInvalidValue for a shape that is not built
+hipError_t launch_prefill_fused(const PrefillFusedArgs &a, int nc, int sl);
+bool prefill_fused_shape_built(int nc, int sl);
+bool inter_chunk_ws_shape_built(int dk, int dv, int ncw, int npw);
 
 hipError_t launch_gate(const GateArgs &a);
 hipError_t launch_short_conv(const ShortConvArgs &a);

@@ -85,7 +85,7 @@ typedef enum kda_status {
     KDA_ERR_ALIGN = 2,        /* a pointer violates the alignment rules above */
     KDA_ERR_SHAPE = 3,        /* nseq < 1, H < 1, B < 1, total_tokens out of range, or a launch limit exceeded */
     KDA_ERR_UNSUPPORTED = 4,  /* dk / dv not in {16,32,64,128}, or unknown dtype */
-    KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kda_prefill_workspace_bytes */
+    KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the call needs */
     KDA_ERR_HIP = 6,          /* a kernel launch failed; see kda_last_hip_error() */
     KDA_ERR_TOO_LARGE = 7     /* kda_prefill_noalloc: workspace above KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
@@ -98,21 +98,36 @@ typedef enum kda_dtype {
 #define KDA_CHUNK 16
 #define KDA_GATE_LOWER_BOUND (-5.0f)
 
-/* Bytes of device workspace kda_prefill / kda_chunk_local / kda_inter_chunk
- * need: per chunk slot and head, the 16x16 matrices T' = (I + A_kk)^-1
- * diag(beta) and A_qk, each as a 1 KiB matrix-core operand fragment (a
- * hi/lo bfloat16 pair per element for KDA_BF16, fp32 for KDA_F32), for
- * floor(N/16) + nseq chunk slots.  The layout is private to the library.
- * Returns 0 for invalid arguments. */
+/* Bytes of device workspace kda_chunk_local / kda_inter_chunk need (and
+ * kda_prefill, where it runs those two phases): per chunk slot and head, the
+ * 16x16 matrices T' = (I + A_kk)^-1 diag(beta) and A_qk, each as a 1 KiB
+ * matrix-core operand fragment (a hi/lo bfloat16 pair per element for
+ * KDA_BF16, fp32 for KDA_F32), for floor(N/16) + nseq chunk slots.  The
+ * layout is private to the library.  Returns 0 for invalid arguments. */
+size_t kda_chunk_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
+                                 int32_t dk, int32_t dv, kda_dtype dt);
+
+/* Bytes of device workspace kda_prefill needs for these arguments.  KDA_BF16
+ * inputs with dk = dv = 128 (the K3 layer's heads) and at least 256
+ * (sequence, head) chains run a single-pass kernel that keeps the chunk-local
+ * operands on chip: 0 bytes, and the workspace may be NULL.  Every other shape
+ * runs the two phases and needs kda_chunk_workspace_bytes(...).  0 is also
+ * returned for invalid arguments; kda_prefill then reports which argument is
+ * wrong. */
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype dt);
 
-/* Chunkwise prefill over packed variable-length sequences: the chunk-local
- * phase (kda_chunk_local) followed by the inter-chunk phase
- * (kda_inter_chunk) on `stream`.  Computes o for every token and, if
- * final_state != NULL, the state after each sequence's last token.
- * (Chunked form: same page, "chunk-parallel form" paragraph and equation
- * O_[t] = (Gamma (.) Q_[t]) S_[t] + A_[t] V~_[t].) */
+/* Chunkwise prefill over packed variable-length sequences.  Computes o for
+ * every token and, if final_state != NULL, the state after each sequence's
+ * last token.  (Chunked form: same page, "chunk-parallel form" paragraph and
+ * equation O_[t] = (Gamma (.) Q_[t]) S_[t] + A_[t] V~_[t].)
+ * KDA_BF16 with dk = dv = 128 and nseq * H >= 256: one kernel per call, in which producer waves
+ * form the chunk-local operands (cumulative decay, the inverse of I + A_kk,
+ * A_qk) two chunks ahead of the waves that carry the state, so the inputs are
+ * read from HBM once and nothing goes through a workspace (the overlap of the
+ * token-parallel and the serial phases that the page's systems section
+ * describes).  Other shapes: the chunk-local phase (kda_chunk_local) then the
+ * inter-chunk phase (kda_inter_chunk), with the workspace between them. */
 kda_status kda_prefill(const void *q, const void *k, const void *v,
                        const void *log_alpha, const void *beta,
                        const float *init_state, const int32_t *cu_seqlens,
@@ -146,6 +161,35 @@ kda_status kda_inter_chunk(const void *q, const void *k, const void *v,
                            int32_t dv, kda_dtype dt, const void *workspace,
                            size_t workspace_bytes, float *o,
                            float *final_state, void *stream);
+
+/* The two prefill kernels with an explicit workgroup shape, for tuning and for
+ * tests that must reach every shape (kda_prefill and kda_inter_chunk choose
+ * the shape from the number of (sequence, head) chains).  Same arguments,
+ * results and errors as kda_prefill / kda_inter_chunk.
+ *   kda_prefill_single_pass: the single-pass kernel (KDA_BF16, dk = dv = 128
+ *     only) with `consumers` state waves per workgroup, each holding `slices`
+ *     16-column slices of dv: (2, 1), (4, 1) or (4, 2); (0, 0) chooses.
+ *   kda_inter_chunk_shaped: the warp-specialised inter-chunk kernel (KDA_BF16,
+ *     dk >= 32) with `consumers` 16-column state waves and `producers` operand
+ *     waves per workgroup: (2, 4) or (4, 4) for dk = dv = 128, (min(dv/16, 4) or
+ *     min(dv/16, 2), min(dk/16, 4)) otherwise; (0, 0) chooses.
+ * A shape that is not built returns KDA_ERR_UNSUPPORTED before any launch. */
+kda_status kda_prefill_single_pass(const void *q, const void *k, const void *v,
+                                   const void *log_alpha, const void *beta,
+                                   const float *init_state, const int32_t *cu_seqlens,
+                                   int32_t nseq, int64_t total_tokens, int32_t H,
+                                   int32_t dk, int32_t dv, kda_dtype dt,
+                                   int32_t consumers, int32_t slices,
+                                   float *o, float *final_state, void *stream);
+
+kda_status kda_inter_chunk_shaped(const void *q, const void *k, const void *v,
+                                  const void *log_alpha, const float *init_state,
+                                  const int32_t *cu_seqlens, int32_t nseq,
+                                  int64_t total_tokens, int32_t H, int32_t dk,
+                                  int32_t dv, kda_dtype dt, const void *workspace,
+                                  size_t workspace_bytes, int32_t consumers,
+                                  int32_t producers, float *o, float *final_state,
+                                  void *stream);
 
 /* kda_prefill with intra-device context parallelism: every sequence is split into
  * `segments` chunk-aligned pieces (segment r covers chunks [nc r / R, nc (r+1) / R)

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import gated_delta_rule_51_amd as kda
 
@@ -52,7 +53,13 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     # floor(N/16) + nseq chunk slots, 2 KiB per slot and head
+    assert kda.kda_chunk_workspace_bytes(65536, 1, 96, 128, 128) == (4096 + 1) * 96 * 2048
+    assert kda.kda_chunk_workspace_bytes(0, 3, 2, 16, 16) == 3 * 2 * 2048
+    # kda_prefill: bf16 with dk = dv = 128 and >= 256 chains runs in one kernel without a workspace
+    assert kda.kda_prefill_workspace_bytes(65536, 3, 96, 128, 128) == 0
     assert kda.kda_prefill_workspace_bytes(65536, 1, 96, 128, 128) == (4096 + 1) * 96 * 2048
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 96, 128, 128, torch.float32) == (4096 + 1) * 96 * 2048
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 96, 64, 128) == (4096 + 1) * 96 * 2048
     assert kda.kda_prefill_workspace_bytes(0, 3, 2, 16, 16) == 3 * 2 * 2048
     assert kda.kda_prefill_workspace_bytes(64, 1, 1, 24, 16) == 0   # unsupported dk
     assert kda.kda_prefill_workspace_bytes(64, 0, 1, 16, 16) == 0   # nseq < 1
@@ -254,8 +261,8 @@ def test_launch_limits_are_checked_before_any_launch(lib):
     """Shapes whose launches would exceed 2^32 work-items in a grid dimension (or 32-bit row
     extents) are rejected on the host with KDA_ERR_SHAPE, at each bound."""
     # (sequence, head) chains: nseq * H < 2^20
-    assert lib.kda_prefill_workspace_bytes(0, (1 << 20) // 96 + 1, 96, 128, 128, 1) == 0
-    assert lib.kda_prefill_workspace_bytes(0, (1 << 20) // 96, 96, 128, 128, 1) > 0
+    assert lib.kda_chunk_workspace_bytes(0, (1 << 20) // 96 + 1, 96, 128, 128, 1) == 0
+    assert lib.kda_chunk_workspace_bytes(0, (1 << 20) // 96, 96, 128, 128, 1) > 0
     assert _prefill(lib, nseq=1 << 14, H=64, wsb=1 << 40) == 3
     assert _prefill(lib, nseq=(1 << 14) - 1, H=64, wsb=16) == 5           # in range: fails later, on the workspace
     # 16-token row extents: H * max(dk, dv) < 2^24
@@ -275,5 +282,7 @@ def test_launch_limits_are_checked_before_any_launch(lib):
 def test_noalloc_rejects_problems_above_the_scratch_on_the_host(lib):
     # (floor(N/16) + nseq) * H * 2 KiB > 128 MiB: rejected before the scratch is looked up
     f = lib.kda_prefill_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1 << 20, 96, 64, 128, 1, FAKE, None, None) == 7
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1 << 20, 96, 128, 128, 0, FAKE, None, None) == 7
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1 << 20, 96, 128, 128, 1, FAKE, None, None) == 7
     assert kda.kda_status_string(7).startswith("KDA_ERR_TOO_LARGE")

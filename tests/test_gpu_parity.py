@@ -296,14 +296,26 @@ def test_ragged_lengths_and_shapes(dev, dk, dv, dtype):
     _prefill_case(dev, [17, 0, 1, 33, 100, 16, 15], 3, dk, dv, dtype, seed=dk + dv, init=True)
 
 
-@pytest.mark.parametrize("shape", ["2x4", "4x4", "1x4"])
-def test_ragged_lengths_warp_specialised_shapes(dev, monkeypatch, shape):
+@pytest.mark.parametrize("shape", [(2, 4), (4, 4)])
+def test_ragged_lengths_warp_specialised_shapes(dev, shape):
     """The warp-specialised inter-chunk shapes on empty, single-chunk, two-chunk and
     ragged sequences with an initial state (every remainder of the three-chunk unrolled
     loop)."""
-    monkeypatch.setenv("KDA_WS", shape)
-    _prefill_case(dev, [17, 0, 1, 33, 100, 16, 15, 48, 49], 2, 128, 128, torch.bfloat16, seed=21,
-                  init=True)
+    seqlens, H = [17, 0, 1, 33, 100, 16, 15, 48, 49], 2
+    w = workloads.custom(seqlens, H, 128, 128, torch.bfloat16)
+    x = workloads.prefill_inputs(w, device=dev, seed=21)
+    init = workloads.random_state(len(seqlens), H, 128, 128, device=dev, seed=21)
+    ws = kda.alloc_workspace(w.total_tokens, len(seqlens), H, 128, 128, torch.bfloat16, dev)
+    kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+    o = torch.full((w.total_tokens, H, 128), float("nan"), dtype=torch.float32, device=dev)
+    fin = torch.full((len(seqlens), H, 128, 128), float("nan"), dtype=torch.float32, device=dev)
+    say(f"  case: warp-specialised shape {shape}")
+    kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws, init, o=o, final_state=fin,
+                        consumers=shape[0], producers=shape[1])
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x, init)
+    assert_close(o, o_ref, TOL[torch.bfloat16], "o")
+    assert_close(fin, f_ref, TOL[torch.bfloat16], "final_state")
 
 
 def test_zero_tokens(dev):
@@ -445,27 +457,36 @@ def test_graph_replays_match_eager(dev):
         assert torch.equal(o, ref[0]) and torch.equal(od, ref[2])
 
 
-@pytest.mark.parametrize("knob,values", [
-    ("KDA_WAVES", ("2", "4", "8")),                          # one-role kernel
-    ("KDA_WS", ("4x4", "2x4", "4x2", "1x4", "2x2", "1x2")),  # consumer x producer waves
-])
-def test_workgroup_shape_variants_agree(dev, monkeypatch, knob, values):
-    """Every workgroup shape of both inter-chunk kernels meets the bar, is bitwise
-    reproducible on its own, and agrees with the other shapes (the per-channel decay sums
-    are grouped differently per shape, so shapes agree to the tolerance, not bitwise)."""
+def test_workgroup_shape_variants_agree(dev):
+    """Every workgroup shape of the warp-specialised inter-chunk kernel and of the single-pass
+    prefill meets the bar, is bitwise reproducible on its own, and agrees with the other shapes
+    (the per-channel decay sums and the inverse are grouped differently per kernel, so shapes
+    agree to the tolerance, not bitwise)."""
     w = workloads.custom([130, 64], 3, 128, 128, torch.bfloat16)
     x = workloads.prefill_inputs(w, device=dev, seed=10)
     o_ref, f_ref = oracle_prefill(x)
+    ws = kda.alloc_workspace(w.total_tokens, 2, 3, 128, 128, torch.bfloat16, dev)
+    args = (x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+
+    def two_kernel(shape):
+        kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+        return kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws,
+                                   consumers=shape[0], producers=shape[1])
+
+    def single_pass(shape):
+        return kda.kda_prefill_single_pass(*args, consumers=shape[0], slices=shape[1])
+
+    runs = [(f"inter-chunk {s}", two_kernel, s) for s in ((4, 4), (2, 4))]
+    runs += [(f"single pass {s}", single_pass, s) for s in ((2, 1), (4, 1), (4, 2))]
     outs = []
-    for val in values:
-        monkeypatch.setenv(knob, val)
-        say(f"{knob}={val}")
-        outs.append(kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"]))
-        again = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    for name, fn, shape in runs:
+        say(name)
+        outs.append(fn(shape))
+        again = fn(shape)
         torch.cuda.synchronize()
         assert torch.equal(outs[-1][0], again[0]) and torch.equal(outs[-1][1], again[1])
-        assert_close(outs[-1][0], o_ref, TOL[torch.bfloat16], f"o ({knob}={val})")
-        assert_close(outs[-1][1], f_ref, TOL[torch.bfloat16], f"final_state ({knob}={val})")
+        assert_close(outs[-1][0], o_ref, TOL[torch.bfloat16], f"o ({name})")
+        assert_close(outs[-1][1], f_ref, TOL[torch.bfloat16], f"final_state ({name})")
     for o, f in outs[1:]:
         assert rel_err(o, outs[0][0].double().cpu().numpy()) <= TOL[torch.bfloat16]
         assert rel_err(f, outs[0][1].double().cpu().numpy()) <= TOL[torch.bfloat16]
