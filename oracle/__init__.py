@@ -121,15 +121,19 @@ class Oracle:
             raise RuntimeError(f"kda_oracle_prefill_f64 failed with code {rc}")
         return o, fin
 
-    def decode(self, q, k, v, log_alpha, beta, state, nthreads: int = 0):
+    def decode(self, q, k, v, log_alpha, beta, state, nthreads: int = 0, inplace: bool = False):
         """One token for each of B x H heads.
 
         q, k, log_alpha: [B, H, dk]; v: [B, H, dv]; beta: [B, H];
         state: [B, H, dk, dv].  Returns (o [B, H, dv], new_state) in float64;
-        the input array is not modified.
+        the input array is not modified, unless inplace=True and it is a C-contiguous
+        float64 numpy array (then it is advanced in place and returned).
         """
         q, k, v, g, b = (_as_f64(t) for t in (q, k, v, log_alpha, beta))
-        st = _as_f64(state).copy()
+        if inplace and isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous:
+            st = state
+        else:
+            st = _as_f64(state).copy()
         B, H, dk = q.shape
         dv = v.shape[2]
         if st.shape != (B, H, dk, dv) or b.shape != (B, H):

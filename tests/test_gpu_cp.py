@@ -24,7 +24,11 @@ def _cp_case(dev, seqlens, H, dk, dv, dtype, R, seed=0, init=True, heads=None):
     x = workloads.prefill_inputs(w, device=dev, seed=seed)
     S0 = workloads.random_state(len(seqlens), H, dk, dv, device=dev, seed=seed) if init else None
     say(f"  case: cp R={R} seqlens={list(seqlens)[:6]} H={H} dk={dk} dv={dv} {dtype} init={init}")
-    o, fin = kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], S0, segments=R)
+    # outputs start as NaN, so a row or state the kernels never write cannot pass
+    o = torch.full((w.total_tokens, H, dv), float("nan"), dtype=torch.float32, device=dev)
+    fin = torch.full((len(seqlens), H, dk, dv), float("nan"), dtype=torch.float32, device=dev)
+    kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], S0, segments=R,
+                       o=o, final_state=fin)
     torch.cuda.synchronize()
     o_ref, f_ref = oracle_prefill(x, S0, heads=heads)
     if heads is not None:
@@ -95,6 +99,28 @@ def test_cp_few_heads_long_sequence(dev):
     o_ref, f_ref = oracle_prefill(x, None, heads=[3, 10], nthreads=2)
     assert_close(o[:, [3, 10]], o_ref, TOL[torch.bfloat16], "o")
     assert_close(fin[:, [3, 10]], f_ref, TOL[torch.bfloat16], "final_state")
+
+def test_cp_long_sequence_workload_rates(dev):
+    """One 65,536-token sequence with 12 heads at R = 10 with the workload's own decay and write
+    rates (where a segment's map is far below fp32 resolution, so the scan must not disturb the
+    exact states): outputs start as NaN, every head against kda_prefill, the oracle on heads 0-7
+    (one per residue mod 8)."""
+    w = workloads.custom([65536], 12, 128, 128, torch.bfloat16, "neg_softplus")
+    x = workloads.prefill_inputs(w, device=dev, seed=4)
+    o = torch.full((65536, 12, 128), float("nan"), dtype=torch.float32, device=dev)
+    fin = torch.full((1, 12, 128, 128), float("nan"), dtype=torch.float32, device=dev)
+    say("  case: cp R=10, T=65536 H=12 d=128, workload rates")
+    kda.kda_prefill_cp(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], segments=10, o=o,
+                       final_state=fin)
+    o1, f1 = kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert_close(o, o1.double().cpu().numpy(), 1e-3, "o (cp vs prefill)")
+    assert_close(fin, f1.double().cpu().numpy(), 1e-3, "final_state (cp vs prefill)")
+    hs = list(range(8))
+    o_ref, f_ref = oracle_prefill(x, None, heads=hs)
+    assert_close(o[:, hs], o_ref, TOL[torch.bfloat16], "o")
+    assert_close(fin[:, hs], f_ref, TOL[torch.bfloat16], "final_state")
+
 
 def test_cp_no_tokens(dev):
     """N = 0: every segment is empty, so the final states are the initial ones exactly."""
