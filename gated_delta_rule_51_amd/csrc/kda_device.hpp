@@ -107,9 +107,11 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // A single 16-long contraction runs on the 32-long instruction with the upper
-// half zero.  The 16x16x16 bf16 MFMA is deliberately not used: chained with the
-// 16x16x32 form in these kernels it produced wrong, schedule-dependent results
-// on gfx950, while the 16x16x32-only code is exact in the same tests.
+// half zero, so every bf16 product in the library uses one instruction form and
+// one operand layout.  (An earlier version that mixed in the 16x16x16 form gave
+// wrong results for some workgroup shapes; the cause was not established -- an
+// operand-layout assumption or a missing wait in that code are as likely as the
+// instruction itself -- and the single-form code passes every test.)
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     const bf16x4 z = {};
     return mma32(cat(a, z), cat(b, z), c);

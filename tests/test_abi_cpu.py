@@ -16,6 +16,11 @@ HEADER = os.path.join(ROOT, "include", "kda.h")
 
 @pytest.fixture(scope="module")
 def lib():
+    # KDA_ABI_TEST_LIBRARY: the validation layer built on the CPU with sanitizers
+    # (test_sanitizers_cpu.py) instead of the product library
+    alt = os.environ.get("KDA_ABI_TEST_LIBRARY")
+    if alt:
+        return kda.load_library(alt)
     if not os.path.exists(kda.LIBRARY):
         import __graft_entry__
 
