@@ -61,6 +61,43 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, init_state=None, chunk=C, keep=Fa
     return (o, fin, kept) if keep else (o, fin)
 
 
+def prefill_lookahead(q, k, v, g, beta, cu_seqlens=None, init_state=None, chunk=C):
+    """The chunk recurrence with one chunk of lookahead (a way to take the state update off the
+    serial chain between two chunks; a single-pass kernel built on it was slower than the plain
+    form on gfx950, because forming C moves work onto the producer waves).  With S_c the state entering chunk c, Gamma_c = e^{G_n} of chunk c and
+    K~_c = K-_c (.) Gamma_c, the next chunk's K+ S is split into a part known from the state
+    entering the current chunk and a 16 x 16 product with the current Delta:
+        K+_{c+1} S_{c+1} = (K+_{c+1} Diag(Gamma_c)) S_c + (K+_{c+1} K~_c^T) Delta_c
+                         = W'_{c+1} S_c + C_{c+1} Delta_c,     C_{c+1} = W'_{c+1} K-_c^T
+    so only C Delta lies on the serial chain between two chunks' Delta."""
+    q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.array([0, N]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    nseq = len(cu) - 1
+    o = np.zeros((N, H, dv))
+    fin = np.zeros((nseq, H, dk, dv))
+    for s in range(nseq):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if init_state is None else np.array(init_state[s, h], dtype=np.float64)
+            gam_prev = np.ones(dk)                 # no chunk before the first
+            km_prev, d_prev = np.zeros((chunk, dk)), np.zeros((chunk, dv))
+            S_prev = S                             # state entering the (virtual) previous chunk
+            for c0 in range(cu[s], cu[s + 1], chunk):
+                c1 = min(cu[s + 1], c0 + chunk)
+                loc = chunk_local(q[c0:c1, h], k[c0:c1, h], g[c0:c1, h], beta[c0:c1, h])
+                Wp = loc["Kp"] * gam_prev[None, :]
+                Cm = Wp @ km_prev[:d_prev.shape[0]].T
+                X = Wp @ S_prev + Cm @ d_prev       # = K+ S
+                D = loc["Tp"] @ (v[c0:c1, h] - X)
+                o[c0:c1, h] = loc["Qp"] @ S + loc["Aqk"] @ D
+                gam = np.exp(loc["G"][-1])
+                S_prev, S = S, gam[:, None] * S + loc["Kt"].T @ D
+                gam_prev, km_prev, d_prev = gam, loc["Km"], D
+            fin[s, h] = S
+    return o, fin
+
+
 def backward(q, k, v, g, beta, dO, cu_seqlens=None, init_state=None, dfinal=None, chunk=C, dg_form="checkpoint"):
     """Gradients in chunk form (the algebra of the GPU backward), same outputs as the oracle's
     reverse mode.  Per chunk with incoming state S0, its Delta, and the adjoint S^ of the

@@ -40,6 +40,19 @@ def test_chunked_form_varlen_and_gate_floor():
     assert _rel(o, o_ref) < 1e-11 and _rel(f, f_ref) < 1e-11
 
 
+@pytest.mark.parametrize("lens,init", [([64], True), ([50, 0, 17, 33, 1, 16], True), ([37, 80], False)])
+def test_lookahead_form_matches_oracle(lens, init):
+    """Lookahead form: the next chunk's K+ S from the state entering the current chunk plus one
+    16 x 16 product with the current Delta (gate floor included)."""
+    q, k, v, g, b = _inputs(sum(lens), 2, 32, 24, seed=len(lens) + 7)
+    g[::5] = -5.0
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S0 = np.random.default_rng(2).standard_normal((len(lens), 2, 32, 24)) * 0.1 if init else None
+    o_ref, f_ref = oracle.prefill(q, k, v, g, b, cu_seqlens=cu, init_state=S0)
+    o, f = chunk_model.prefill_lookahead(q, k, v, g, b, cu_seqlens=cu, init_state=S0)
+    assert _rel(o, o_ref) < 1e-11 and _rel(f, f_ref) < 1e-11
+
+
 def test_unit_lower_inverse_is_nilpotent_product():
     """A_kk is strictly lower triangular (A^16 = 0), so (I + A)^{-1} equals
     (I - A)(I + A^2)(I + A^4)(I + A^8)."""
