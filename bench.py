@@ -592,7 +592,26 @@ def bench_layer(torch, kda, workloads, dev):
     ms = _event_ms(torch, layer_prefill, 5)
     res["prefill_layer_k3"] = {"tokens": N, "heads": H, "ms": round(ms, 5), "tokens_per_s": N / (ms * 1e-3),
                                "launches": 8}
-    del x3, lq, ws, bufs, o3, fin3, y3, cache3
+    del bufs, ws
+    torch.cuda.empty_cache()
+
+    # the same layer core with the prologue fused into the recurrence's loads: ShortConv + Swish
+    # (+ L2) of the raw q, k, v and the gate inside chunk-local and inter-chunk, then the cache
+    # copy and the epilogue (four launches)
+    wsl = torch.empty(kda.kda_prefill_layer_workspace_bytes(N, 1, H) // 4 + 4, dtype=torch.float32, device=dev)
+    conv_w3 = torch.cat([lq["conv_w"]] * 3, dim=1).contiguous()
+    cache3c = torch.zeros((1, H, 3 * d, 3), dtype=torch.float32, device=dev)
+
+    def layer_prefill_fused():
+        kda.kda_prefill_layer(x3["q"], x3["k"], x3["v"], conv_w3, lq["z"], lq["A_log"], x3["beta"], cu,
+                              conv_cache_out=cache3c, out_gate=lq["u"], norm_w=lq["norm_w"], o=o3,
+                              final_state=fin3, y=y3, workspace=wsl)
+
+    ms_f = _event_ms(torch, layer_prefill_fused, 5)
+    res["prefill_layer_k3_fused"] = {"tokens": N, "heads": H, "ms": round(ms_f, 5),
+                                     "tokens_per_s": N / (ms_f * 1e-3), "launches": 4,
+                                     "speedup_vs_separate": ms / ms_f}
+    del x3, lq, o3, fin3, y3, cache3, wsl, conv_w3, cache3c
     torch.cuda.empty_cache()
 
     w4 = workloads.workload(4)

@@ -33,8 +33,8 @@ EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_pref
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
-           "kda_gate", "kda_short_conv", "kda_out_norm_gate",
-           "kda_status_string", "kda_last_hip_error")
+           "kda_gate", "kda_short_conv", "kda_out_norm_gate", "kda_prefill_layer_workspace_bytes",
+           "kda_prefill_layer", "kda_status_string", "kda_last_hip_error")
 
 _lib = None
 
@@ -107,6 +107,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_short_conv.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, ctypes.c_int, vp, vp]
     lib.kda_out_norm_gate.restype = ctypes.c_int
     lib.kda_out_norm_gate.argtypes = [vp, vp, vp, f32, i64, i32, i32, ctypes.c_int, vp, vp]
+    lib.kda_prefill_layer_workspace_bytes.restype = sz
+    lib.kda_prefill_layer_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_prefill_layer.restype = ctypes.c_int
+    lib.kda_prefill_layer.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                      ctypes.c_int, vp, sz, vp, vp, vp, vp, f32, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_hip_error.restype = i32
@@ -267,6 +272,53 @@ def kda_prefill(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *,
         H, dk, dv, _dtype_code(q.dtype), _ptr(o), _ptr(final_state), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, final_state
+
+
+def kda_prefill_layer_workspace_bytes(total_tokens: int, nseq: int, H: int, dk: int = 128, dv: int = 128,
+                                      dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of kda_prefill_layer (0: shape not supported)."""
+    return int(load_library().kda_prefill_layer_workspace_bytes(total_tokens, nseq, H, dk, dv, _dtype_code(dtype)))
+
+
+def kda_prefill_layer(q, k, v, conv_w, z, A_log, beta, cu_seqlens=None, init_state=None, *, conv_cache=None,
+                      conv_cache_out=None, l2_eps: float = 1e-6, out_gate=None, norm_w=None, norm_eps: float = 1e-6,
+                      output_final_state: bool = True, o=None, final_state=None, y=None, workspace=None,
+                      stream=None):
+    """The layer core of a prefill with the prologue fused into the recurrence's loads (see
+    include/kda.h): q, k, v raw projections [N, H, 128] (bf16), conv_w fp32 [H, 384, 4] (q | k | v
+    channels), z decay logits [N, H, 128], A_log fp32 [H], beta [N, H]; conv_cache / conv_cache_out
+    fp32 [nseq, H, 384, 3] (or None); out_gate [N, H, 128] with norm_w fp32 [128] adds the epilogue.
+    Returns (o fp32 [N, H, 128], final_state or None, y or None)."""
+    N, H, dk, dv = _check_inputs(q, k, v, z, beta)
+    dev = q.device
+    C = 2 * dk + dv
+    cu = _cu(cu_seqlens, N, dev)
+    nseq = cu.numel() - 1
+    _check_dev("conv_w", conv_w, dev, torch.float32, (H, C, 4))
+    _check_dev("A_log", A_log, dev, torch.float32, (H,))
+    for name, c in (("conv_cache", conv_cache), ("conv_cache_out", conv_cache_out)):
+        if c is not None:
+            _check_dev(name, c, dev, torch.float32, (nseq, H, C, 3))
+    o, final_state = _prefill_outputs(N, H, dk, dv, nseq, dev, o, final_state, init_state, output_final_state)
+    if out_gate is not None:
+        _check_dev("out_gate", out_gate, dev, q.dtype, (N, H, dv))
+        _check_dev("norm_w", norm_w, dev, torch.float32, (dv,))
+        if y is None:
+            y = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+        _check_dev("y", y, dev, q.dtype, (N, H, dv))
+    nbytes = kda_prefill_layer_workspace_bytes(N, nseq, H, dk, dv, q.dtype)
+    if nbytes == 0:
+        raise KDAError(4, "kda_prefill_layer: bf16 with dk = dv = 128 only")
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=dev)
+    _check_workspace(workspace, dev, nbytes)
+    _check(load_library().kda_prefill_layer(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w), _ptr(conv_cache), _ptr(conv_cache_out), float(l2_eps), _ptr(z),
+        _ptr(A_log), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N, H, dk, dv, _dtype_code(q.dtype),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(o), _ptr(final_state),
+        _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y if out_gate is not None else None),
+        _stream(stream)))
+    return o, final_state, (y if out_gate is not None else None)
 
 
 def kda_prefill_single_pass(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, *, consumers: int = 0,

@@ -68,6 +68,15 @@ size_t workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H) {
            kda::WS_FLOATS_PER_CHUNK_HEAD * sizeof(float);
 }
 
+// Fused layer prefill: the chunk workspace, then the prologue's q, k and log-decay
+// (bf16 [3, N, H, 128]).
+size_t layer_qkg_offset(int64_t total_tokens, int32_t nseq, int32_t H) {
+    return (workspace_bytes(total_tokens, nseq, H) + 255) / 256 * 256;
+}
+size_t layer_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H) {
+    return layer_qkg_offset(total_tokens, nseq, H) + (size_t)total_tokens * H * 3 * 128 * 2;
+}
+
 kda_status check_ptrs(std::initializer_list<const void *> required,
                       std::initializer_list<const void *> optional) {
     for (const void *p : required)
@@ -242,6 +251,69 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
     if (st != KDA_OK) return st;
     return kda_inter_chunk(q, k, v, log_alpha, init_state, cu_seqlens, nseq, total_tokens, H, dk,
                            dv, dt, workspace, ws_bytes, o, final_state, stream);
+}
+
+size_t kda_prefill_layer_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv,
+                                         kda_dtype dt) {
+    if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
+    if (dt != KDA_BF16 || dk != 128 || dv != 128) return 0;
+    return layer_workspace_bytes(total_tokens, nseq, H);
+}
+
+kda_status kda_prefill_layer(const void *q, const void *k, const void *v, const float *conv_w,
+                             const float *conv_cache_in, float *conv_cache_out, float l2_eps, const void *z,
+                             const float *A_log, const void *beta, const float *init_state,
+                             const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk,
+                             int32_t dv, kda_dtype dt, void *workspace, size_t ws_bytes, float *o,
+                             float *final_state, const void *out_gate, const float *norm_w, float norm_eps,
+                             void *y, void *stream) {
+    kda_status st = check_common(nseq, total_tokens, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    if (dt != KDA_BF16 || dk != 128 || dv != 128) return KDA_ERR_UNSUPPORTED;
+    if (!(l2_eps >= 0.f && l2_eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    st = check_inputs({q, k, v, z}, true, beta, true, total_tokens > 0);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({cu_seqlens, conv_w}, {init_state, final_state, o});
+    if (st != KDA_OK) return st;
+    if (!A_log) return KDA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(A_log) & 3u) || (conv_cache_in && (reinterpret_cast<uintptr_t>(conv_cache_in) & 3u)) ||
+        (conv_cache_out && (reinterpret_cast<uintptr_t>(conv_cache_out) & 3u)))
+        return KDA_ERR_ALIGN;
+    if (!o && total_tokens > 0) return KDA_ERR_NULL;
+    if (out_gate) {
+        st = check_rows16({out_gate, y}, total_tokens > 0);
+        if (st != KDA_OK) return st;
+        st = check_ptrs({norm_w}, {});
+        if (st != KDA_OK) return st;
+        if (!(norm_eps >= 0.f && norm_eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    }
+    if (!workspace || ws_bytes < layer_workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    float *ws = static_cast<float *>(workspace);
+    uint16_t *qkg = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
+                                                 layer_qkg_offset(total_tokens, nseq, H));
+    const size_t plane = (size_t)total_tokens * H * dk;
+    const kda::LayerPrologue lp{conv_w, conv_cache_in, A_log, qkg, l2_eps, 2 * dk + dv, total_tokens};
+    if (total_tokens > 0) {
+        kda::ChunkLocalArgs cl{q, k, z, beta, cu_seqlens, nseq, H, dk, total_tokens, true, ws, stream, &lp};
+        st = hip_status(kda::launch_chunk_local(cl));
+        if (st != KDA_OK) return st;
+    }
+    // the recurrence on the prologue's q, k, log-decay; v raw (its prologue is applied on load)
+    kda::InterChunkArgs ic{qkg, qkg + plane, v, qkg + 2 * plane, init_state, cu_seqlens, nseq, H, dk, dv,
+                           total_tokens, true, ws, o, final_state, 0, 0, stream, &lp};
+    st = hip_status(kda::launch_inter_chunk(ic));
+    if (st != KDA_OK) return st;
+    if (conv_cache_out) {
+        st = hip_status(kda::launch_layer_conv_cache(q, k, v, conv_cache_in, conv_cache_out, cu_seqlens, nseq, H,
+                                                     dk, dv, stream));
+        if (st != KDA_OK) return st;
+    }
+    if (out_gate && total_tokens > 0) {
+        kda::OutNormGateArgs a{o, out_gate, norm_w, norm_eps, total_tokens, H, dv, true, y, stream};
+        st = hip_status(kda::launch_out_norm_gate(a));
+    }
+    return st;
 }
 
 kda_status kda_prefill_single_pass(const void *q, const void *k, const void *v, const void *log_alpha,

@@ -21,12 +21,16 @@
 // 16x16xdk matrix products on the matrix cores; e^{+-G} are formed as running
 // products of e^{+-g} (no exp of a large argument).
 //
-// Precision: A_kk uses single-bf16 operands (its rounding error is damped by
-// the triangular solve); A_qk uses split-bf16 operands (hi*hi + lo*hi + hi*lo,
-// ~16-bit mantissas) because it feeds the output directly.  fp32 inputs use
-// fp32 MFMAs throughout.
+// Precision: A_kk and A_qk use split-bf16 operands (hi*hi + lo*hi + hi*lo,
+// ~16-bit mantissas).  A single-bf16 A_kk is enough for mild decay, but with
+// strong decay and heavy-tailed values (the layer's ShortConv outputs under a
+// gate near its -5 floor) its rounding became the largest error term of the
+// output in an fp64 emulation (5e-3 of RMS on one 8192-token head, growing with
+// the number of samples), and this kernel has matrix-core time to spare.  fp32
+// inputs use fp32 MFMAs throughout.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "layer_prologue.hpp"
 
 namespace kda {
 
@@ -194,11 +198,20 @@ __global__ __launch_bounds__(64) void chunk_local_f32_kernel(
 //   * the hi/lo splits of Q+ and K- take their residuals from the matrix core
 //     (an exact product with -I) instead of vector-ALU unpacking;
 //   * the triangular solve reads the rows of A_kk as 16-byte vectors.
-template <int DK>
+//
+// With LAYER the kernel is the first pass of the fused layer prefill: q, k and g
+// are the raw q and k projections and the decay logits z, and the layer
+// prologue (layer_prologue.hpp) turns them into the normalised q, k and the
+// log-decay in registers, which the kernel also writes (bf16, lp.qkg) for the
+// inter-chunk pass: computing the prologue once and storing its results costs
+// less than recomputing it in both passes (it is a vector-ALU load comparable
+// to the chunk-local work itself).
+template <int DK, bool LAYER>
 __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ g,
     const __bf16 *__restrict__ beta, const int32_t *__restrict__ cu, int32_t nseq, int32_t H,
-    float *__restrict__ ws, int64_t base) {
+    float *__restrict__ ws, int64_t base, LayerPrologue lp) {
+    static_assert(!LAYER || DK == 128, "the fused layer prologue is built for dk = 128");
     constexpr int NB = DK / 16;
     constexpr uint32_t EB = 2;
     // Item id = slot * H + head: the heads of one chunk are neighbours, so the
@@ -243,16 +256,94 @@ __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
     const uint32_t row = l16 < n ? l16 * rowK : OOB;
     u32x2 gr[NB], kr[NB], qr[NB];
     if constexpr (NB % 2 == 0) {
+        uint32_t gx[NB / 2][4], kx[NB / 2][4], qx[NB / 2][4];
 #pragma unroll
         for (int p = 0; p < NB / 2; ++p) {
             const uint32_t o = row == OOB ? OOB : row + (32 * p + 8 * g4) * EB;
-            const u32x4 gx = buf_load_u32x4(rg, o), kx = buf_load_u32x4(rk, o), qx = buf_load_u32x4(rq, o);
-            gr[2 * p] = u32x2{gx[0], gx[1]};
-            gr[2 * p + 1] = u32x2{gx[2], gx[3]};
-            kr[2 * p] = u32x2{kx[0], kx[1]};
-            kr[2 * p + 1] = u32x2{kx[2], kx[3]};
-            qr[2 * p] = u32x2{qx[0], qx[1]};
-            qr[2 * p + 1] = u32x2{qx[2], qx[3]};
+            const u32x4 gv = buf_load_u32x4(rg, o), kv = buf_load_u32x4(rk, o), qv = buf_load_u32x4(rq, o);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gx[p][i] = gv[i];
+                kx[p][i] = kv[i];
+                qx[p][i] = qv[i];
+            }
+        }
+        if constexpr (LAYER) {
+            // The three tokens before the chunk (lanes l16 = 13..15): packed rows of the same
+            // sequence, or its cache before the first chunk.
+            uint32_t hq[NB / 2][4], hk[NB / 2][4];
+            if (j > 0) {
+                const rsrc_t hq_r = make_rsrc(q + ((t0 - 3) * H + h) * DK, 3u * rowK);
+                const rsrc_t hk_r = make_rsrc(k + ((t0 - 3) * H + h) * DK, 3u * rowK);
+#pragma unroll
+                for (int p = 0; p < NB / 2; ++p) {
+                    const uint32_t o = l16 >= 13 ? (l16 - 13) * rowK + (32 * p + 8 * g4) * EB : OOB;
+                    const u32x4 a = buf_load_u32x4(hq_r, o), b = buf_load_u32x4(hk_r, o);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        hq[p][i] = a[i];
+                        hk[p][i] = b[i];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < NB / 2; ++p) {
+                    cache_halo<4>(lp.cache, (int64_t)s * H + h, lp.cw, 32 * p + 8 * g4, l16, hq[p]);
+                    cache_halo<4>(lp.cache, (int64_t)s * H + h, lp.cw, DK + 32 * p + 8 * g4, l16, hk[p]);
+                }
+            }
+            // ShortConv + Swish of q and k, then the L2 norms of the rows.  The 128 channels
+            // of token l16 sit in lanes l16 + 16 g4, octet 4 p + g4 in pair p; the octets are
+            // added in the order of the stand-alone pass's butterfly over the octet index
+            // (bits 0, 1 of it are g4: across lanes; bits 2, 3 are p: in the lane).
+            float yq[NB / 2][8], yk[NB / 2][8];
+            float oq[NB / 2], ok[NB / 2];
+#pragma unroll
+            for (int p = 0; p < NB / 2; ++p) {
+                f32x4 w[8];
+                conv_weights<4>(lp.conv_w, h, lp.cw, 32 * p + 8 * g4, w);
+                conv_swish<4>(qx[p], hq[p], w, l16, yq[p]);
+                conv_weights<4>(lp.conv_w, h, lp.cw, DK + 32 * p + 8 * g4, w);
+                conv_swish<4>(kx[p], hk[p], w, l16, yk[p]);
+                oq[p] = octet_sumsq(yq[p]);
+                ok[p] = octet_sumsq(yk[p]);
+                oq[p] += __shfl_xor(oq[p], 16);
+                ok[p] += __shfl_xor(ok[p], 16);
+                oq[p] += __shfl_xor(oq[p], 32);
+                ok[p] += __shfl_xor(ok[p], 32);
+            }
+            const float sq = (oq[0] + oq[1]) + (oq[2] + oq[3]), sk = (ok[0] + ok[1]) + (ok[2] + ok[3]);
+            const float iq = __builtin_amdgcn_rsqf(sq + lp.l2_eps), ik = __builtin_amdgcn_rsqf(sk + lp.l2_eps);
+            const bool valid = l16 < n;
+            const float eA = __expf(lp.A_log[h]);
+#pragma unroll
+            for (int p = 0; p < NB / 2; ++p) {
+                pack_scaled<4>(yq[p], iq, valid, qx[p]);
+                pack_scaled<4>(yk[p], ik, valid, kx[p]);
+                gate_words<4>(gx[p], eA, valid, gx[p]);
+            }
+            // the prologue's outputs for the inter-chunk pass (token rows of this chunk only)
+            if (valid) {
+                __bf16 *qo = static_cast<__bf16 *>(lp.qkg);
+                const int64_t plane = (int64_t)lp.n_tokens * H * DK;
+                const int64_t rowo = ((t0 + l16) * H + h) * DK;
+#pragma unroll
+                for (int p = 0; p < NB / 2; ++p) {
+                    const int64_t e = rowo + 32 * p + 8 * g4;
+                    *reinterpret_cast<u32x4 *>(qo + e) = u32x4{qx[p][0], qx[p][1], qx[p][2], qx[p][3]};
+                    *reinterpret_cast<u32x4 *>(qo + plane + e) = u32x4{kx[p][0], kx[p][1], kx[p][2], kx[p][3]};
+                    *reinterpret_cast<u32x4 *>(qo + 2 * plane + e) = u32x4{gx[p][0], gx[p][1], gx[p][2], gx[p][3]};
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NB / 2; ++p) {
+            gr[2 * p] = u32x2{gx[p][0], gx[p][1]};
+            gr[2 * p + 1] = u32x2{gx[p][2], gx[p][3]};
+            kr[2 * p] = u32x2{kx[p][0], kx[p][1]};
+            kr[2 * p + 1] = u32x2{kx[p][2], kx[p][3]};
+            qr[2 * p] = u32x2{qx[p][0], qx[p][1]};
+            qr[2 * p + 1] = u32x2{qx[p][2], qx[p][3]};
         }
     } else {
 #pragma unroll
@@ -324,8 +415,11 @@ __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
         }
         const SplitPair qs = split_pair(r.qp[0], r.qp[1]);
         const SplitPair ms = split_pair(r.km[0], r.km[1]);
-        // A_kk: single bf16;  A_qk: hi*hi + lo*hi + hi*lo
-        akk = mma32(cat(to_bf16x4(r.kp[0]), to_bf16x4(r.kp[1])), ms.hi, akk);
+        const SplitPair ps = split_pair(r.kp[0], r.kp[1]);
+        // A_kk and A_qk: hi*hi + lo*hi + hi*lo
+        akk = mma32(ps.hi, ms.hi, akk);
+        akk = mma32(ps.lo, ms.hi, akk);
+        akk = mma32(ps.hi, ms.lo, akk);
         aqk = mma32(qs.hi, ms.hi, aqk);
         aqk = mma32(qs.lo, ms.hi, aqk);
         aqk = mma32(qs.hi, ms.lo, aqk);
@@ -388,16 +482,31 @@ static hipError_t launch_cl_t(const ChunkLocalArgs &a) {
         const int64_t items = slots * a.H, per_launch = int64_t(1) << 25;
         for (int64_t base = 0; base < items; base += per_launch) {
             const int64_t n = items - base < per_launch ? items - base : per_launch;
-            hipLaunchKernelGGL((chunk_local_bf16_kernel<DK>), dim3((unsigned)n), dim3(64), 0, (hipStream_t)a.stream,
-                               (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.g,
-                               (const __bf16 *)a.beta, a.cu, a.nseq, a.H, a.ws, base);
+            if constexpr (DK == 128) {
+                if (a.layer) {
+                    hipLaunchKernelGGL((chunk_local_bf16_kernel<DK, true>), dim3((unsigned)n), dim3(64), 0,
+                                       (hipStream_t)a.stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
+                                       (const __bf16 *)a.g, (const __bf16 *)a.beta, a.cu, a.nseq, a.H, a.ws, base,
+                                       *a.layer);
+                    const hipError_t e = hipGetLastError();
+                    if (e != hipSuccess) return e;
+                    continue;
+                }
+            }
+            if (a.layer) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((chunk_local_bf16_kernel<DK, false>), dim3((unsigned)n), dim3(64), 0,
+                               (hipStream_t)a.stream, (const __bf16 *)a.q, (const __bf16 *)a.k,
+                               (const __bf16 *)a.g, (const __bf16 *)a.beta, a.cu, a.nseq, a.H, a.ws, base,
+                               LayerPrologue{});
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-    } else
+    } else {
+        if (a.layer) return hipErrorInvalidValue;
         hipLaunchKernelGGL((chunk_local_f32_kernel<DK, T>), grid, dim3(64), 0, (hipStream_t)a.stream,
                            (const T *)a.q, (const T *)a.k, (const T *)a.g, (const T *)a.beta, a.cu,
                            a.nseq, a.H, a.ws);
+    }
     return hipGetLastError();
 }
 

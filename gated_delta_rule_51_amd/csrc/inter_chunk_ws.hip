@@ -33,14 +33,20 @@
 // last chunk load as zeros (g = 0 keeps the decay unchanged, k = 0 removes
 // them from every product).
 //
-// Precision as in inter_chunk.hip: K+ S single bf16, everything else split
-// bf16 (hi*hi + lo*hi + hi*lo) with fp32 accumulation, fp32 state.  The
+// Precision: every product split bf16 (hi*hi + lo*hi + hi*lo) with fp32
+// accumulation, fp32 state.  (K+ S in single bf16, enough for mild decay,
+// became the largest output error with strong decay -- a gate at its -5 floor
+// on every channel and heavy-tailed values, as the layer's ShortConv produces
+// -- where the emulated error of a 65,536-token head dropped from 3e-3 to
+// 4e-4 of RMS with the split; the classic kernel in inter_chunk.hip keeps the
+// single form.)  The
 // residuals lo = x - hi of those splits are formed on the matrix cores (an
 // exact product with -I), which keeps the vector ALUs -- the busiest unit
 // here -- for the rest.
 
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "layer_prologue.hpp"
 
 namespace kda {
 
@@ -68,17 +74,27 @@ struct WsOps {
     static constexpr int NB = DK / 16, NPAIR = NB / 2;
     bf16x8 qp_hi[NPAIR][64];  // Q+ A-fragments, block pairs packed (one K=32 MFMA operand)
     bf16x8 qp_lo[NPAIR][64];
-    bf16x8 kp[NPAIR][64];     // K+ (single bf16), same packing
+    bf16x8 kp[NPAIR][64];     // K+ as hi + lo, same packing
+    bf16x8 kp_lo[NPAIR][64];
     Split4 kt[NB][64];        // K~^T A-fragments (channel rows, 4 tokens per lane), {hi, lo}
     float gam[DK];            // e^{G_n} per channel
 };
 
-template <int DK, int DV, int NC, int NP>
+// With LAYER the kernel is the second pass of the fused layer prefill: q, k and g
+// are the normalised q, k and the log-decay the chunk-local pass computed, and v
+// is the raw projection, to which the consumers apply the layer prologue
+// (layer_prologue.hpp: ShortConv + Swish) as they load it.  The convolution's
+// three earlier tokens are the previous chunk's raw rows, or the sequence's cache
+// before its first chunk.  (Recomputing the q and k prologue here as well, from
+// row norms the first pass stored, doubled this kernel's time: the producer waves
+// have no vector-ALU time to spare for it.)
+template <int DK, int DV, int NC, int NP, bool LAYER>
 __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_waves_per_eu(2, 2))) void inter_chunk_ws_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
     int32_t H, const float *__restrict__ ws, float *__restrict__ o, float *__restrict__ fin,
-    int32_t nsplit, int32_t nchains) {
+    int32_t nsplit, int32_t nchains, LayerPrologue lp) {
+    static_assert(!LAYER || (DK == 128 && DV == 128), "the fused layer prologue is built for dk = dv = 128");
     constexpr int NB = DK / 16, NPAIR = NB / 2, BPW = NB / NP;
     constexpr uint32_t EB = 2;
     static_assert(NB % 2 == 0 && NB % NP == 0, "channel blocks split evenly over producers");
@@ -171,6 +187,21 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
             };
             const bf16x4 ID = identity_operand(g4, l16);
             const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
+            // layer prologue of v: the 4 taps of this lane's columns and the raw v of the
+            // chunk before (lanes l16 = 13..15 hold its last rows; first the sequence's
+            // cache).  Both live in LDS, where each lane reads back what it wrote itself:
+            // registers are short here.
+            __shared__ f32x4 wv_lds[LAYER ? NC : 1][4][4];
+            __shared__ u32x2 vprev_lds[LAYER ? NC : 1][64];
+            if constexpr (LAYER) {
+                f32x4 w[4];
+                conv_weights<2>(lp.conv_w, h, lp.cw, 2 * DK + col0 + 4 * g4, w);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) wv_lds[wave][g4][m] = w[m];
+                uint32_t hv[2];
+                cache_halo<2>(lp.cache, hd, lp.cw, 2 * DK + col0 + 4 * g4, l16, hv);
+                vprev_lds[wave][lane] = u32x2{hv[0], hv[1]};
+            }
             auto cload = [&](CIn &X, int c) {
                 const rsrc_t rw = rsrc_ws(c);
                 X.tp = buf_load_u32x4(rw, lane * 16u);
@@ -180,20 +211,35 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
             };
             auto advance = [&](int ob, const CIn &X, int c) {
                 const WsOps<DK> &P = ops[ob];
-                // Operand reads go out first, in two batches, so their LDS latency
-                // overlaps the state split and the K+ S products instead of
-                // stalling each matrix-core instruction that consumes them.
-                bf16x8 kpr[NPAIR], qhr[NPAIR], qlr[NPAIR];
+                // (layer: ShortConv + Swish of v first, while few registers are live)
+                u32x2 vin = X.v;
+                if constexpr (LAYER) {
+                    const uint32_t cur[2] = {X.v[0], X.v[1]};
+                    const u32x2 pv = vprev_lds[wave][lane];
+                    const uint32_t prev[2] = {pv[0], pv[1]};
+                    const f32x4 wv[4] = {wv_lds[wave][g4][0], wv_lds[wave][g4][1], wv_lds[wave][g4][2],
+                                         wv_lds[wave][g4][3]};
+                    float y[4];
+                    uint32_t vh[2];
+                    conv_swish<2>(cur, prev, wv, l16, y);
+                    pack_scaled<2>(y, 1.f, true, vh);
+                    vprev_lds[wave][lane] = X.v;
+                    vin = u32x2{vh[0], vh[1]};
+                }
+                // Operand reads go out first, in two batches (K+ for X; then Q+, K~ and
+                // Gamma), so their LDS latency overlaps the state split and the K+ S
+                // products instead of stalling each matrix-core instruction that
+                // consumes them.
+                bf16x8 kpr[NPAIR], kplr[NPAIR];
 #pragma unroll
                 for (int p = 0; p < NPAIR; ++p) {
                     kpr[p] = P.kp[p][lane];
-                    qhr[p] = P.qp_hi[p][lane];
-                    qlr[p] = P.qp_lo[p][lane];
+                    kplr[p] = P.kp_lo[p][lane];
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const Split4 Tp = __builtin_bit_cast(Split4, X.tp);
                 const Split4 Aq = __builtin_bit_cast(Split4, X.aq);
-                const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, X.v), ID, zero4());
+                const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, vin), ID, zero4());
                 // S = Shi + Slo (bf16), residuals on the matrix cores
                 bf16x8 Shi[NPAIR], Slo[NPAIR];
 #pragma unroll
@@ -202,12 +248,19 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                     Slo[p] = cat(to_bf16x4(mma32(NIL, Shi[p], S[2 * p])),
                                  to_bf16x4(mma32(NIH, Shi[p], S[2 * p + 1])));
                 }
-                // X = K+ S (single bf16), two independent partial sums
-                f32x4 Xa = zero4(), Xb = zero4();
+                // X = K+ S (hi*hi + lo*hi + hi*lo, in three independent sums)
+                f32x4 Xa = zero4(), Xb = zero4(), Xc = zero4();
 #pragma unroll
                 for (int p = 0; p < NPAIR; ++p) {
-                    if (p & 1) Xb = mma32(kpr[p], Shi[p], Xb);
-                    else Xa = mma32(kpr[p], Shi[p], Xa);
+                    Xa = mma32(kpr[p], Shi[p], Xa);
+                    Xb = mma32(kplr[p], Shi[p], Xb);
+                    Xc = mma32(kpr[p], Slo[p], Xc);
+                }
+                bf16x8 qhr[NPAIR], qlr[NPAIR];
+#pragma unroll
+                for (int p = 0; p < NPAIR; ++p) {
+                    qhr[p] = P.qp_hi[p][lane];
+                    qlr[p] = P.qp_lo[p][lane];
                 }
                 Split4 ktr[NB];
                 f32x4 gmr[NB];
@@ -229,7 +282,7 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                 }
                 // Delta = T' (V - X)
                 bf16x8 yhh, dhh;
-                const bf16x4 ylo = split_lo(vc - (Xa + Xb), NIL, yhh);
+                const bf16x4 ylo = split_lo(vc - (Xa + (Xb + Xc)), NIL, yhh);
                 const bf16x8 tpp = cat(Tp.hi, Tp.lo);
                 f32x4 D = mma32(tpp, yhh, zero4());
                 D = mma32(tpp, cat(ylo, ylo), D);
@@ -376,7 +429,7 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                 // G at token l16, channels 16 b + 4 g4 + jj; Gs at tokens 4 g4 + jj, channel 16 b + l16
                 const f32x4 GT[2] = {mma32(gf, LTL, zero4()), mma32(gf, LTH, zero4())};
                 const f32x4 GS[2] = {mma32(UTL, gf, zero4()), mma32(UTH, gf, zero4())};
-                f32x4 Pp[2], qv[2], ktv[2];
+                f32x4 Pp[2], qv[2], ktv[2], kpv[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     f32x4 F;
@@ -386,13 +439,16 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                         F[j] = decay_exp_fast(GS[u][j]);       // e^{G_n - G_r}
                     }
                     qv[u] = unpack_bf16x4(Rq[u]) * Pp[u];
+                    kpv[u] = unpack_bf16x4(Rk[u]) * Pp[u];
                     ktv[u] = kc[u] * F;
                 }
-                // Q+ and K~ as hi + lo (both held in the accumulator layout of a tile:
-                // Q+^T and K~), residuals from the matrix core
+                // Q+, K+ and K~ as hi + lo (all held in the accumulator layout of a tile:
+                // Q+^T, K+^T and K~), residuals from the matrix core
                 const bf16x8 qh = cat(to_bf16x4(qv[0]), to_bf16x4(qv[1]));
+                const bf16x8 kph = cat(to_bf16x4(kpv[0]), to_bf16x4(kpv[1]));
                 const bf16x8 kth = cat(to_bf16x4(ktv[0]), to_bf16x4(ktv[1]));
                 const bf16x4 ql[2] = {to_bf16x4(mma32(NIL, qh, qv[0])), to_bf16x4(mma32(NIH, qh, qv[1]))};
+                const bf16x4 kpl[2] = {to_bf16x4(mma32(NIL, kph, kpv[0])), to_bf16x4(mma32(NIH, kph, kpv[1]))};
                 const bf16x4 ktl[2] = {to_bf16x4(mma32(NIL, kth, ktv[0])), to_bf16x4(mma32(NIH, kth, ktv[1]))};
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
@@ -401,9 +457,11 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                     bf16x4 *qhp = reinterpret_cast<bf16x4 *>(&P.qp_hi[b >> 1][lane]) + (b & 1);
                     bf16x4 *qlp = reinterpret_cast<bf16x4 *>(&P.qp_lo[b >> 1][lane]) + (b & 1);
                     bf16x4 *kpp = reinterpret_cast<bf16x4 *>(&P.kp[b >> 1][lane]) + (b & 1);
+                    bf16x4 *kplp = reinterpret_cast<bf16x4 *>(&P.kp_lo[b >> 1][lane]) + (b & 1);
                     *qhp = u ? __builtin_shufflevector(qh, qh, 4, 5, 6, 7) : __builtin_shufflevector(qh, qh, 0, 1, 2, 3);
                     *qlp = ql[u];
-                    *kpp = to_bf16x4(unpack_bf16x4(Rk[u]) * Pp[u]);
+                    *kpp = u ? __builtin_shufflevector(kph, kph, 4, 5, 6, 7) : __builtin_shufflevector(kph, kph, 0, 1, 2, 3);
+                    *kplp = kpl[u];
                     P.kt[b][lane] = Split4{u ? __builtin_shufflevector(kth, kth, 4, 5, 6, 7)
                                              : __builtin_shufflevector(kth, kth, 0, 1, 2, 3),
                                            ktl[u]};
@@ -451,10 +509,20 @@ static hipError_t launch_ws_t(const InterChunkArgs &a) {
     const int nchains = a.nseq * a.H;
     const int nsplit = DV / (16 * NC);
     const int64_t grid = ((int64_t)nchains + 7) / 8 * 8 * nsplit;
-    hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP>), dim3((unsigned)grid),
+    if (a.layer) {
+        if constexpr (DK == 128 && DV == 128) {
+            hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP, true>), dim3((unsigned)grid),
+                               dim3(64 * WsLayout<NC, NP>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
+                               (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
+                               a.H, a.ws, a.o, a.fin, nsplit, nchains, *a.layer);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP, false>), dim3((unsigned)grid),
                        dim3(64 * WsLayout<NC, NP>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
                        (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
-                       a.H, a.ws, a.o, a.fin, nsplit, nchains);
+                       a.H, a.ws, a.o, a.fin, nsplit, nchains, LayerPrologue{});
     return hipGetLastError();
 }
 

@@ -57,6 +57,19 @@ struct DecodeWindowArgs {
     DecodeFusion fx;
 };
 
+// The fused layer prefill's prologue on load (layer_prologue.hpp): what the two
+// prefill kernels need besides their usual inputs.
+struct LayerPrologue {
+    const float *conv_w;  // fp32 [H, 2 dk + dv, 4], tap j multiplies x_{t-j}; channels q, k, v
+    const float *cache;   // fp32 [nseq, H, 2 dk + dv, 3]: the 3 inputs before each sequence, oldest first; NULL = 0
+    const float *A_log;   // fp32 [H]
+    void *qkg;            // bf16 [3, N, H, dk]: the prologue's q, k and log-decay, written by the
+                          // chunk-local pass for the inter-chunk pass
+    float l2_eps;
+    int32_t cw;           // 2 dk + dv: channels per head of conv_w and cache
+    int64_t n_tokens;     // N (the planes of qkg)
+};
+
 struct ChunkLocalArgs {
     const void *q, *k, *g, *beta;
     const int32_t *cu;
@@ -65,6 +78,7 @@ struct ChunkLocalArgs {
     bool bf16;
     float *ws;
     void *stream;
+    const LayerPrologue *layer = nullptr;  // fused layer prologue on load (bf16, dk = 128), or none
 };
 
 struct InterChunkArgs {
@@ -78,6 +92,7 @@ struct InterChunkArgs {
     float *o, *fin;
     int32_t ws_consumers, ws_producers;  // warp-specialised kernel shape; 0, 0 = choose automatically
     void *stream;
+    const LayerPrologue *layer = nullptr;  // fused layer prologue on load (bf16, dk = dv = 128), or none
 };
 
 // Single-pass prefill (prefill_fused.hip): bf16 inputs, dk = dv = 128, many chains; no workspace.
@@ -164,6 +179,10 @@ bool prefill_fused_shape_built(int nc, int sl);
 bool inter_chunk_ws_shape_built(int dk, int dv, int ncw, int npw);
 
 hipError_t launch_gate(const GateArgs &a);
+// The combined q | k | v convolution cache after a fused layer prefill (bf16 inputs).
+hipError_t launch_layer_conv_cache(const void *q, const void *k, const void *v, const float *cache_in,
+                                   float *cache_out, const int32_t *cu, int32_t nseq, int32_t H, int32_t dk,
+                                   int32_t dv, void *stream);
 hipError_t launch_short_conv(const ShortConvArgs &a);
 hipError_t launch_out_norm_gate(const OutNormGateArgs &a);
 hipError_t launch_decode(const DecodeArgs &a);

@@ -11,15 +11,13 @@
 // a row sum (L2 or RMS norm) is a few cross-lane adds.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "layer_prologue.hpp"  // the elementwise arithmetic shared with the fused layer prefill
 
 namespace kda {
 
 constexpr int LAYER_THREADS = 256;
-constexpr float GATE_MIN = -5.0f;  // g_min of the bounded gate
 
-// Sigmoid on the hardware exp and reciprocal (about 1e-6 relative; every use
-// here is rounded to the input dtype or compared at the fp32 bar).
-__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf(float x) { return layer_sigmoid(x); }
 
 // Eight consecutive elements of one row: one 16-byte access for bf16, two for fp32.
 struct V8 {
@@ -63,8 +61,8 @@ __device__ __forceinline__ void store8(T *p, const V8 &x) {
 }
 
 __device__ __forceinline__ float sumsq(const V8 &x) {
-    const f32x4 s = x.a * x.a + x.b * x.b;
-    return (s[0] + s[1]) + (s[2] + s[3]);
+    const float c[8] = {x.a[0], x.a[1], x.a[2], x.a[3], x.b[0], x.b[1], x.b[2], x.b[3]};
+    return octet_sumsq(c);
 }
 
 // Sum over the R lanes of a row (R a power of two, rows aligned to R lanes).
@@ -101,8 +99,8 @@ __global__ __launch_bounds__(LAYER_THREADS) void gate_kernel(const T *__restrict
             const float s = __expf(A_log[row % (uint32_t)H]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                x[u].a[j] = GATE_MIN * sigmoidf(s * x[u].a[j]);
-                x[u].b[j] = GATE_MIN * sigmoidf(s * x[u].b[j]);
+                x[u].a[j] = gate_of(s, x[u].a[j]);
+                x[u].b[j] = gate_of(s, x[u].b[j]);
             }
             store8(g + 8 * i, x[u]);
         }
@@ -200,12 +198,10 @@ __global__ __launch_bounds__(LAYER_THREADS) void short_conv_kernel(
             V8 r;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const float aa = wv[0][m] * xt.a[m] + wv[1][m] * win[0].a[m] + wv[2][m] * win[1].a[m] +
-                                 wv[3][m] * win[2].a[m];
-                const float ab = wv[0][m + 4] * xt.b[m] + wv[1][m + 4] * win[0].b[m] +
-                                 wv[2][m + 4] * win[1].b[m] + wv[3][m + 4] * win[2].b[m];
-                r.a[m] = aa * sigmoidf(aa);  // Swish
-                r.b[m] = ab * sigmoidf(ab);
+                r.a[m] = conv4_swish(f32x4{wv[0][m], wv[1][m], wv[2][m], wv[3][m]}, xt.a[m], win[0].a[m],
+                                     win[1].a[m], win[2].a[m]);
+                r.b[m] = conv4_swish(f32x4{wv[0][m + 4], wv[1][m + 4], wv[2][m + 4], wv[3][m + 4]}, xt.b[m],
+                                     win[0].b[m], win[1].b[m], win[2].b[m]);
             }
             if (l2norm) {
                 const float inv = __builtin_amdgcn_rsqf(row_sum<R>(sumsq(r)) + eps);
@@ -247,6 +243,48 @@ __global__ __launch_bounds__(LAYER_THREADS) void conv_cache_kernel(const T *__re
     }
 #pragma unroll
     for (int m = 0; m < 3; ++m) cache_out[i * 3 + m] = v[m];
+}
+
+// The cache after a fused layer prefill (q, k and v read raw by the prefill
+// kernels): per (sequence, head), for each channel of the combined q | k | v axis
+// (2 dk + dv channels, the layout of the decode layer step's cache), the last 3
+// inputs, oldest first, reaching into the incoming cache for short sequences.
+// As above, each thread reads its sources before writing, so the caches may alias.
+__global__ __launch_bounds__(LAYER_THREADS) void layer_conv_cache_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *cache_in, const int32_t *__restrict__ cu, int64_t items, int32_t H, int32_t dk, int32_t dv,
+    float *cache_out) {
+    const int64_t i = (int64_t)blockIdx.x * LAYER_THREADS + threadIdx.x;
+    if (i >= items) return;
+    const int cw = 2 * dk + dv;
+    const int64_t s = i / ((int64_t)H * cw);
+    const int64_t hc = i - s * H * cw;
+    const int h = (int)(hc / cw), c = (int)(hc - (int64_t)h * cw);
+    const __bf16 *x = c < dk ? q : (c < 2 * dk ? k : v);
+    const int d = c < 2 * dk ? dk : dv;
+    const int cc = c < dk ? c : (c < 2 * dk ? c - dk : c - 2 * dk);
+    const int64_t bos = cu[s], eos = cu[s + 1], len = eos - bos;
+    float r[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        const int64_t src = eos - 3 + m;
+        if (src >= bos)
+            r[m] = load_in(x + (src * H + h) * d + cc);
+        else
+            r[m] = cache_in ? cache_in[i * 3 + m + len] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) cache_out[i * 3 + m] = r[m];
+}
+
+hipError_t launch_layer_conv_cache(const void *q, const void *k, const void *v, const float *cache_in,
+                                   float *cache_out, const int32_t *cu, int32_t nseq, int32_t H, int32_t dk,
+                                   int32_t dv, void *stream) {
+    const int64_t items = (int64_t)nseq * H * (2 * dk + dv);
+    hipLaunchKernelGGL(layer_conv_cache_kernel, dim3((unsigned)((items + LAYER_THREADS - 1) / LAYER_THREADS)),
+                       dim3(LAYER_THREADS), 0, (hipStream_t)stream, (const __bf16 *)q, (const __bf16 *)k,
+                       (const __bf16 *)v, cache_in, cu, items, H, dk, dv, cache_out);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ epilogue

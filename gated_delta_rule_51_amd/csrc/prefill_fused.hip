@@ -27,9 +27,10 @@
 // the solver completes chunk c + 1 (T' and Aqk into set (c + 1) % 3) and the producers
 // build chunk c + 2 (set (c + 2) % 3, partials into buffer (c + 2) % 2).
 //
-// Precision (as in the two-kernel path): K+ S and A single bf16, everything else split
-// bf16 (hi*hi + lo*hi + hi*lo, and lo*lo where it is free) with fp32 accumulation; the
-// products of the inverse use both halves of both factors.  State and output fp32.
+// Precision (as in the two-kernel path): every product split bf16 (hi*hi + lo*hi + hi*lo,
+// and lo*lo where it is free) with fp32 accumulation; the products of the inverse use both
+// halves of both factors.  State and output fp32.  (K+ S and A in single bf16 were enough
+// for mild decay, not for a gate at its -5 floor with heavy-tailed values.)
 //
 // Layout conventions and the key-channel relabelling inside block pairs are those of the
 // warp-specialised inter-chunk kernel: internal channel 16 (2P + h) + 4 g4 + j is memory
@@ -61,7 +62,8 @@ struct FusedOps {
     static constexpr int NB = DK / 16, NPAIR = NB / 2;
     bf16x8 qp_hi[NPAIR][64];  // Q+ A-operand fragments, block pairs packed
     bf16x8 qp_lo[NPAIR][64];
-    bf16x8 kp[NPAIR][64];     // K+ (single bf16)
+    bf16x8 kp[NPAIR][64];     // K+ as hi + lo
+    bf16x8 kp_lo[NPAIR][64];
     Split4 kt[NB][64];        // K~^T (channel rows, 4 tokens per lane), {hi, lo}
     Split4 tp[64];            // T' as the A operand of Delta = T' Y: lane (g4, m) holds T'[m][4 g4 + j]
     Split4 aq[64];            // Aqk as the A operand of Aqk Delta
@@ -174,35 +176,38 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                     X.v[sl] = buf_load_u32x2(rv, l16 * rowV + (col0[sl] + 4 * g4) * EB);
             };
             auto advance = [&](const FusedOps<DK> &P, const CIn &X, int c) {
-                bf16x8 kpr[NPAIR], qhr[NPAIR], qlr[NPAIR];
+                // K+ (hi, lo) read first, so its LDS latency overlaps the state split
+                bf16x8 kpa[NPAIR], kla[NPAIR];
 #pragma unroll
                 for (int p = 0; p < NPAIR; ++p) {
-                    kpr[p] = P.kp[p][lane];
-                    qhr[p] = P.qp_hi[p][lane];
-                    qlr[p] = P.qp_lo[p][lane];
+                    kpa[p] = P.kp[p][lane];
+                    kla[p] = P.kp_lo[p][lane];
                 }
                 const Split4 Tp = P.tp[lane];
                 const Split4 Aq = P.aq[lane];
                 __builtin_amdgcn_sched_barrier(0);
                 const bf16x8 tpp = cat(Tp.hi, Tp.lo);
                 // Per block pair and slice: the state's bf16 split, then every product that
-                // reads it (X = K+ S single bf16; Q+ S as hi*hi, lo*hi, hi*lo), so a split lives
+                // reads it (X = K+ S and Q+ S, each as hi*hi, lo*hi, hi*lo), so a split lives
                 // only briefly and the slices' independent chains interleave.
                 f32x4 Xa[SL], Xb[SL], Oa[SL], Ob[SL], Oc[SL];
 #pragma unroll
                 for (int sl = 0; sl < SL; ++sl) Xa[sl] = Xb[sl] = Oa[sl] = Ob[sl] = Oc[sl] = zero4();
 #pragma unroll
                 for (int p = 0; p < NPAIR; ++p) {
+                    const bf16x8 kpr = kpa[p], kplr = kla[p];
+                    const bf16x8 qhr = P.qp_hi[p][lane], qlr = P.qp_lo[p][lane];
 #pragma unroll
                     for (int sl = 0; sl < SL; ++sl) {
                         const bf16x8 Shi = cat(to_bf16x4(S[sl][2 * p]), to_bf16x4(S[sl][2 * p + 1]));
                         const bf16x8 Slo = cat(to_bf16x4(mma32(NIL, Shi, S[sl][2 * p])),
                                                to_bf16x4(mma32(NIH, Shi, S[sl][2 * p + 1])));
-                        if (p & 1) Xb[sl] = mma32(kpr[p], Shi, Xb[sl]);
-                        else Xa[sl] = mma32(kpr[p], Shi, Xa[sl]);
-                        Oa[sl] = mma32(qhr[p], Shi, Oa[sl]);
-                        Ob[sl] = mma32(qlr[p], Shi, Ob[sl]);
-                        Oc[sl] = mma32(qhr[p], Slo, Oc[sl]);
+                        Xa[sl] = mma32(kpr, Shi, Xa[sl]);
+                        Xb[sl] = mma32(kplr, Shi, Xb[sl]);
+                        Xb[sl] = mma32(kpr, Slo, Xb[sl]);
+                        Oa[sl] = mma32(qhr, Shi, Oa[sl]);
+                        Ob[sl] = mma32(qlr, Shi, Ob[sl]);
+                        Oc[sl] = mma32(qhr, Slo, Oc[sl]);
                     }
                 }
                 // Delta = T' (V - X), per slice
@@ -361,7 +366,7 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                 kmv[u] = kk * Pm[u];
                 ktv[u] = kc[u] * F;
             }
-            // Q+, K~ and K- as hi + lo (residuals from the matrix core); K+ single
+            // Q+, K+, K~ and K- as hi + lo (residuals from the matrix core)
             const bf16x8 qh = cat(to_bf16x4(qv[0]), to_bf16x4(qv[1]));
             const bf16x8 kth = cat(to_bf16x4(ktv[0]), to_bf16x4(ktv[1]));
             const bf16x8 kmh = cat(to_bf16x4(kmv[0]), to_bf16x4(kmv[1]));
@@ -369,9 +374,11 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
             const bf16x8 ql = cat(to_bf16x4(mma32(NIL, qh, qv[0])), to_bf16x4(mma32(NIH, qh, qv[1])));
             const bf16x4 ktl[2] = {to_bf16x4(mma32(NIL, kth, ktv[0])), to_bf16x4(mma32(NIH, kth, ktv[1]))};
             const bf16x8 kml = cat(to_bf16x4(mma32(NIL, kmh, kmv[0])), to_bf16x4(mma32(NIH, kmh, kmv[1])));
+            const bf16x8 kpl = cat(to_bf16x4(mma32(NIL, kpp, kpv[0])), to_bf16x4(mma32(NIH, kpp, kpv[1])));
             P.qp_hi[pw][lane] = qh;
             P.qp_lo[pw][lane] = ql;
             P.kp[pw][lane] = kpp;
+            P.kp_lo[pw][lane] = kpl;
             P.kt[b0][lane] = Split4{__builtin_shufflevector(kth, kth, 0, 1, 2, 3), ktl[0]};
             P.kt[b1][lane] = Split4{__builtin_shufflevector(kth, kth, 4, 5, 6, 7), ktl[1]};
             if (l16 == 15) {
@@ -379,10 +386,14 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                 *reinterpret_cast<f32x4 *>(&P.gam[16 * b1 + 4 * g4]) = Pp[1];
             }
             if (pw == 0 && lane < 16) P.beta[lane] = A.b;
-            // partial sums over this wave's 32 key channels (single bf16 for A, split for Aqk):
+            // partial sums over this wave's 32 key channels (split bf16, hi*hi + lo*hi + hi*lo):
             // A = K+ K-^T, A^T = K- K+^T, Aqk^T = K- Q+^T, all in the accumulator layout
-            pp[0][lane] = mma32(kpp, kmh, zero4());
-            pp[1][lane] = mma32(kmh, kpp, zero4());
+            f32x4 at = mma32(kpp, kmh, zero4());
+            at = mma32(kpl, kmh, at);
+            pp[0][lane] = mma32(kpp, kml, at);
+            f32x4 bt = mma32(kmh, kpp, zero4());
+            bt = mma32(kml, kpp, bt);
+            pp[1][lane] = mma32(kmh, kpl, bt);
             f32x4 aqt = mma32(kmh, qh, zero4());
             aqt = mma32(kml, qh, aqt);
             pp[2][lane] = mma32(kmh, ql, aqt);

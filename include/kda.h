@@ -392,6 +392,54 @@ kda_status kda_out_norm_gate(const float *o, const void *u, const float *w,
                              float eps, int64_t N, int32_t H, int32_t dv,
                              kda_dtype dt, void *y, void *stream);
 
+/* The layer core of a prefill in one call, with the prologue applied where the
+ * recurrence's kernels load their inputs (same page: the paragraph after the
+ * update equation and the bounded-decay section) instead of as separate passes
+ * (bit for bit the results of kda_short_conv, kda_gate, kda_prefill's two-kernel
+ * path and kda_out_norm_gate run in sequence on bf16-valued caches):
+ * q, k and v are the raw (pre-convolution) projections; each goes through the
+ * 4-tap causal ShortConv and Swish, q and k are L2-normalised (l2_eps), and the
+ * log-decay is g = -5 Sigmoid(exp(A_log[h]) z) from the decay logits z.  These
+ * are rounded to bf16 -- the values kda_short_conv and kda_gate would have
+ * written -- and then run through the recurrence as in kda_prefill; with
+ * out_gate != NULL the epilogue of kda_out_norm_gate follows (a separate pass
+ * over o: the row norm spans the whole of dv, which the recurrence's
+ * workgroups split).  bf16 with dk = dv = 128 only (else KDA_ERR_UNSUPPORTED).
+ *   q, k, z       : [N, H, 128] raw projections and decay logits (bf16);
+ *   v             : [N, H, 128] raw projection;  beta : [N, H];
+ *   conv_w        : fp32 [H, 2 dk + dv, 4] (q, k, v channels per head, as in
+ *                   kda_decode_layer_step; tap j multiplies x_{t-j}), 16-byte
+ *                   aligned;
+ *   conv_cache_in : fp32 [nseq, H, 2 dk + dv, 3], the 3 inputs before each
+ *                   sequence (oldest first), or NULL (zeros).  The prefill
+ *                   reads them rounded to bf16 (the inputs they hold are in
+ *                   the input dtype; caches written by these calls are exact);
+ *   conv_cache_out: same shape or NULL: each sequence's last 3 raw inputs,
+ *                   reaching into conv_cache_in for sequences shorter than 3
+ *                   tokens (may equal conv_cache_in; written after everything
+ *                   else has read it), ready for kda_decode_layer_step;
+ *   A_log         : fp32 [H];
+ *   init_state, cu_seqlens, nseq, total_tokens, H, final_state: as kda_prefill;
+ *   o             : fp32 [N, H, dv], required;
+ *   out_gate, y   : [N, H, dv] bf16, 16-byte aligned, with norm_w fp32 [dv]
+ *                   (16-byte aligned) and norm_eps >= 0; out_gate NULL = no
+ *                   epilogue (y, norm_w unused);
+ *   workspace     : kda_prefill_layer_workspace_bytes(...) bytes, 16-byte
+ *                   aligned (the chunk-local operands, then the prologue's q,
+ *                   k and log-decay in bf16, which the first of the two
+ *                   recurrence kernels computes and the second reads; v's
+ *                   prologue is applied where the second kernel loads v).
+ * Errors as for kda_prefill; l2_eps and norm_eps must be finite and >= 0. */
+size_t kda_prefill_layer_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv,
+                                         kda_dtype dt);
+kda_status kda_prefill_layer(const void *q, const void *k, const void *v, const float *conv_w,
+                             const float *conv_cache_in, float *conv_cache_out, float l2_eps, const void *z,
+                             const float *A_log, const void *beta, const float *init_state,
+                             const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, int32_t H, int32_t dk,
+                             int32_t dv, kda_dtype dt, void *workspace, size_t ws_bytes, float *o,
+                             float *final_state, const void *out_gate, const float *norm_w, float norm_eps,
+                             void *y, void *stream);
+
 /* kda_prefill for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
  * arguments, results and errors as kda_prefill, without the workspace: the

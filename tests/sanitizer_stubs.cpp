@@ -18,6 +18,10 @@ hipError_t launch_decode(const DecodeArgs &) { return hipSuccess; }
 hipError_t launch_decode_window(const DecodeWindowArgs &) { return hipSuccess; }
 hipError_t launch_backward(const BackwardArgs &) { return hipSuccess; }
 hipError_t launch_gate(const GateArgs &) { return hipSuccess; }
+hipError_t launch_layer_conv_cache(const void *, const void *, const void *, const float *, float *, const int32_t *,
+                                   int32_t, int32_t, int32_t, int32_t, void *) {
+    return hipSuccess;
+}
 hipError_t launch_short_conv(const ShortConvArgs &) { return hipSuccess; }
 hipError_t launch_out_norm_gate(const OutNormGateArgs &) { return hipSuccess; }
 hipError_t launch_prefill_fused(const PrefillFusedArgs &, int, int) { return hipSuccess; }

@@ -200,6 +200,42 @@ def test_decode_layer_step_rejects_bad_arguments(lib):
              None) == 4
 
 
+def _prefill_layer(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, cin=None, cout=None, l2=1e-6, z=FAKE, A=FAKE, b=FAKE, init=None,
+             cu=FAKE, nseq=1, N=64, H=1, dk=128, dv=128, dt=kda.KDA_BF16, ws=FAKE, wsb=1 << 30, o=FAKE, fin=None,
+             u=None, nw=None, neps=1e-6, y=None, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_layer(a["q"], a["k"], a["v"], a["w"], a["cin"], a["cout"], a["l2"], a["z"], a["A"],
+                                 a["b"], a["init"], a["cu"], a["nseq"], a["N"], a["H"], a["dk"], a["dv"], a["dt"],
+                                 a["ws"], a["wsb"], a["o"], a["fin"], a["u"], a["nw"], a["neps"], a["y"],
+                                 a["stream"])
+
+
+def test_prefill_layer_workspace_and_arguments(lib):
+    # the chunk workspace (256-byte aligned end) plus bf16 q, k, log-decay (768 bytes per (token, head))
+    ws = (4096 + 1) * 96 * 2048
+    assert kda.kda_prefill_layer_workspace_bytes(65536, 1, 96) == ws + 65536 * 96 * 768
+    assert kda.kda_prefill_layer_workspace_bytes(17, 2, 3) == 256 * ((1 + 2) * 3 * 2048 // 256) + 17 * 3 * 768
+    assert kda.kda_prefill_layer_workspace_bytes(64, 1, 1, 64, 128) == 0              # dk = dv = 128 only
+    assert kda.kda_prefill_layer_workspace_bytes(64, 1, 1, 128, 128, torch.float32) == 0
+    assert _prefill_layer(lib, q=None) == 1                                            # KDA_ERR_NULL
+    assert _prefill_layer(lib, w=None) == 1
+    assert _prefill_layer(lib, A=None) == 1
+    assert _prefill_layer(lib, o=None) == 1
+    assert _prefill_layer(lib, u=FAKE, y=FAKE, nw=None) == 1                           # epilogue without norm_w
+    assert _prefill_layer(lib, w=FAKE + 4) == 2                                        # KDA_ERR_ALIGN
+    assert _prefill_layer(lib, cin=FAKE + 2) == 2
+    assert _prefill_layer(lib, u=FAKE + 8, y=FAKE, nw=FAKE) == 2
+    assert _prefill_layer(lib, l2=-1.0) == 3                                           # KDA_ERR_SHAPE
+    assert _prefill_layer(lib, u=FAKE, y=FAKE, nw=FAKE, neps=float("inf")) == 3
+    assert _prefill_layer(lib, nseq=0) == 3
+    assert _prefill_layer(lib, dk=64) == 4                                             # KDA_ERR_UNSUPPORTED
+    assert _prefill_layer(lib, dt=kda.KDA_F32) == 4
+    assert _prefill_layer(lib, wsb=1000) == 5                                          # KDA_ERR_WORKSPACE
+    assert _prefill_layer(lib, ws=None) == 5
+    assert _prefill_layer(lib, ws=FAKE + 8) == 2
+
+
 def test_layer_passes_reject_too_many_rows(lib):
     N, H = 1 << 26, 64  # N * H = 2^32 (token, head) rows
     assert lib.kda_gate(FAKE, FAKE, N, H, 16, 1, FAKE, None) == 3
