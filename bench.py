@@ -734,8 +734,9 @@ def bench_backward(index, torch, kda, workloads, dev, reps: int):
 
 def bench_cp(wl, torch, kda, workloads, dev, segments, reps: int):
     """Intra-device context parallelism (kda_prefill_cp): every sequence in R segments run as
-    independent chains (three recurrence passes and a scan), against kda_prefill on the same
-    inputs.  wl is a workload index or a Workload."""
+    independent chains (up to three recurrence passes and a scan), against the plain two-kernel
+    prefill on the same inputs, and kda_prefill with its own choice between them.  wl is a
+    workload index or a Workload."""
     w = workloads.workload(wl) if isinstance(wl, int) else wl
     log(f"[bench] generating workload {w.name} for context parallelism")
     x = workloads.prefill_inputs(w, device=dev, seed=0)
@@ -744,9 +745,19 @@ def bench_cp(wl, torch, kda, workloads, dev, segments, reps: int):
     ws = kda.alloc_workspace(N, w.nseq, w.H, w.dk, w.dv, x["q"].dtype, dev)
 
     def plain():
-        kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], workspace=ws)
+        kda.kda_chunk_local(x["q"], x["k"], x["log_alpha"], x["beta"], x["cu_seqlens"], ws)
+        kda.kda_inter_chunk(x["q"], x["k"], x["v"], x["log_alpha"], x["cu_seqlens"], ws)
     res = {"workload": w.name, "ms_prefill": round(_event_ms(torch, plain, reps), 4)}
     del ws
+    nb = kda.kda_prefill_workspace_bytes(N, w.nseq, w.H, w.dk, w.dv, x["q"].dtype)
+    wp = torch.empty(max(nb, 16) // 4, dtype=torch.float32, device=dev)
+
+    def auto():
+        kda.kda_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"], workspace=wp)
+    res["ms_kda_prefill"] = round(_event_ms(torch, auto, reps), 4)
+    res["kda_prefill_uses_cp"] = nb != kda.kda_chunk_workspace_bytes(N, w.nseq, w.H, w.dk, w.dv, x["q"].dtype) \
+        and nb > 0
+    del wp
     for R in segments:
         nb = int(lib.kda_prefill_cp_workspace_bytes(N, w.nseq, w.H, w.dk, w.dv, 1, R))
         wcp = torch.empty(nb // 4, dtype=torch.float32, device=dev)

@@ -48,7 +48,7 @@ kda_status check_common(int32_t nseq, int64_t total_tokens, int32_t H, int32_t d
 // per segment and head S~, M and S_in, each region 256-byte aligned.  0 = invalid.
 constexpr int32_t CP_MAX_SEGMENTS = 64;
 struct CpLayout {
-    size_t cl, cu, st, m, sin, total;
+    size_t cl, cu, st, m, sin, flags, total;
 };
 CpLayout cp_layout(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -59,8 +59,30 @@ CpLayout cp_layout(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, in
     L.st = L.cu + up((segs + 1) * 4);
     L.m = L.st + up(segs * H * (size_t)dk * dv * 4);
     L.sin = L.m + up(segs * H * (size_t)dk * dk * 4);
-    L.total = L.sin + up(segs * H * (size_t)dk * dv * 4);
+    L.flags = L.sin + up(segs * H * (size_t)dk * dv * 4);
+    L.total = L.flags + up(segs * H * 4);
     return L;
+}
+
+// kda_prefill's choice of intra-device context parallelism: bf16 with dk >= 32 (the
+// warp-specialised kernels), at most 64 (sequence, head) chains -- so the plain pass holds at
+// most a quarter of the chip's workgroup slots -- and sequences of 16,384 tokens or more on
+// average (the host does not read cu_seqlens), so each of CP's passes is long against its
+// fixed cost.  R = 128 / chains segments (2..16): about 240 workgroups in all.  0 = no CP.
+bool cp_lengths_ok(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R) {
+    if (R < 1 || R > CP_MAX_SEGMENTS) return false;
+    const int64_t segs = (int64_t)nseq * R;
+    if (segs >= (int64_t(1) << 31)) return false;
+    if (check_common((int32_t)segs, total_tokens, H, dk, dv, KDA_BF16) != KDA_OK) return false;
+    return segs * H * dk * (dk > dv ? dk : dv) < (int64_t(1) << 31);
+}
+int32_t auto_cp_segments(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk, int32_t dv, kda_dtype dt) {
+    if (dt != KDA_BF16 || dk < 32 || nseq < 1 || H < 1) return 0;
+    const int64_t chains = (int64_t)nseq * H;
+    if (chains > 64 || total_tokens / nseq < 16384) return 0;
+    int64_t R = 128 / chains;
+    R = R < 2 ? 2 : (R > 16 ? 16 : R);
+    return cp_lengths_ok(total_tokens, nseq, H, dk, dv, (int32_t)R) ? (int32_t)R : 0;
 }
 
 size_t workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H) {
@@ -162,6 +184,8 @@ size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H
                                    int32_t dv, kda_dtype dt) {
     if (check_common(nseq, total_tokens, H, dk, dv, dt) != KDA_OK) return 0;
     if (kda::prefill_fused_supported(dk, dv, dt == KDA_BF16, (int64_t)nseq * H)) return 0;  // single pass
+    const int32_t R = auto_cp_segments(total_tokens, nseq, H, dk, dv, dt);
+    if (R > 0) return cp_layout(total_tokens, nseq, H, dk, dv, R).total;  // context parallelism
     return workspace_bytes(total_tokens, nseq, H);
 }
 
@@ -244,6 +268,11 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
                                 true, o, final_state, stream};
         return hip_status(kda::launch_prefill_fused(a, 0, 0));
     }
+    // few long chains: intra-device context parallelism
+    const int32_t R = auto_cp_segments(total_tokens, nseq, H, dk, dv, dt);
+    if (R > 0)
+        return kda_prefill_cp(q, k, v, log_alpha, beta, init_state, cu_seqlens, nseq, total_tokens, H, dk, dv, dt, R,
+                              o, final_state, workspace, ws_bytes, stream);
     if (!workspace || ws_bytes < workspace_bytes(total_tokens, nseq, H)) return KDA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KDA_ERR_ALIGN;
     st = kda_chunk_local(q, k, log_alpha, beta, cu_seqlens, nseq, total_tokens, H, dk, dt,
@@ -371,9 +400,13 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const voi
     float *cl = reinterpret_cast<float *>(w + L.cl), *St = reinterpret_cast<float *>(w + L.st);
     float *M = reinterpret_cast<float *>(w + L.m), *Sin = reinterpret_cast<float *>(w + L.sin);
     int32_t *cu_seg = reinterpret_cast<int32_t *>(w + L.cu);
+    int32_t *negligible = reinterpret_cast<int32_t *>(w + L.flags);
     const bool bf16 = dt == KDA_BF16;
     const int32_t ns = (int32_t)segs;
     hipError_t e = kda::launch_cp_segments(cu_seqlens, nseq, segments, cu_seg, stream);
+    if (e != hipSuccess) return hip_status(e);
+    // segments whose transition is provably below fp32 resolution skip the M pass
+    e = kda::launch_cp_bound(k, log_alpha, beta, cu_seg, ns, H, dk, bf16, negligible, stream);
     if (e != hipSuccess) return hip_status(e);
     if (total_tokens > 0) {
         kda::ChunkLocalArgs c{q, k, log_alpha, beta, cu_seg, ns, H, dk, total_tokens, bf16, cl, stream};
@@ -387,8 +420,10 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const voi
     if ((e = kda::launch_cp_identity(M, segs * H, dk, stream)) != hipSuccess) return hip_status(e);
     kda::InterChunkArgs a2{q, k, nullptr, log_alpha, M, cu_seg, ns, H, dk, dk, total_tokens, bf16, cl,
                            nullptr, M, 0, 0, stream};
+    a2.skip = negligible;
     if ((e = kda::launch_inter_chunk(a2)) != hipSuccess) return hip_status(e);
-    if ((e = kda::launch_cp_scan(init_state, M, St, Sin, nseq, H, dk, dv, segments, stream)) != hipSuccess)
+    if ((e = kda::launch_cp_scan(init_state, M, St, negligible, Sin, nseq, H, dk, dv, segments, stream)) !=
+        hipSuccess)
         return hip_status(e);
     // the outputs from the exact incoming states; each segment's final state replaces its S_in
     kda::InterChunkArgs a3{q, k, v, log_alpha, Sin, cu_seg, ns, H, dk, dv, total_tokens, bf16, cl,

@@ -12,8 +12,10 @@
 //   2. chunk_local over the segments (a chunk's T' and A_qk depend only on its tokens, so
 //      one pass serves all three recurrences below);
 //   3. inter_chunk from zero states: each segment's S~ (outputs not written);
-//   4. inter_chunk with v = 0 from the identity (a dk x dk "state"): each segment's M;
-//   5. cp_scan per (sequence, head): S_in,0 = the initial state, S_in,r+1 = M_r S_in,r + S~_r;
+//   4. inter_chunk with v = 0 from the identity (a dk x dk "state"): each segment's M,
+//      except for segments whose transition is provably negligible (cp_bound below);
+//   5. cp_scan per (sequence, head): S_in,0 = the initial state, S_in,r+1 = M_r S_in,r + S~_r
+//      (S~_r alone where M_r was skipped);
 //   6. inter_chunk from the exact S_in,r: the outputs, and each segment's final state in
 //      place of its S_in (the last one is the sequence's, copied out by cp_final).
 #include "kda_device.hpp"
@@ -40,6 +42,51 @@ __global__ __launch_bounds__(CP_THREADS) void cp_segments_kernel(const int32_t *
     }
 }
 
+// A bound on each segment's transition M = prod_t (I - beta_t k_t k_t^T) Diag(alpha_t):
+// ||Diag(alpha)||_2 = max_i alpha_i and ||I - beta k k^T||_2 = max(1, |1 - beta ||k||^2|), so
+//     log ||M||_2 <= sum_t ( max_i g_t,i + log max(1, |1 - beta_t ||k_t||^2|) )
+// (g = log alpha <= 0).  Where it is below log 2^-30 the term M_r S_in,r changes S_in,r+1 by
+// less than 2^-30 of S_in,r -- far below fp32 resolution of the state -- so the segment's M
+// is not computed and the scan takes S_in,r+1 = S~_r.  At the rates of the pages' workloads
+// (channels' largest log-decay around -0.07 per token) this holds for every segment longer
+// than a few hundred tokens.  One workgroup per (segment, head), one token row per thread.
+constexpr float CP_LOG_NEGLIGIBLE = -20.794415f;  // log 2^-30
+
+template <typename T, int DK>
+__global__ __launch_bounds__(CP_THREADS) void cp_bound_kernel(const T *__restrict__ k, const T *__restrict__ g,
+                                                              const T *__restrict__ beta,
+                                                              const int32_t *__restrict__ cu_seg, int32_t H,
+                                                              int32_t *__restrict__ flags) {
+    const int64_t sh = blockIdx.x;
+    const int64_t seg = sh / H;
+    const int h = (int)(sh - seg * H);
+    const int64_t t0 = cu_seg[seg], t1 = cu_seg[seg + 1];
+    float lsum = 0.f;
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += CP_THREADS) {
+        const T *gr = g + (t * H + h) * DK, *kr = k + (t * H + h) * DK;
+        float gm = -3.4e38f, kk = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < DK; c += 4) {
+            const f32x4 gv = load_in4(gr + c), kv = load_in4(kr + c);
+            gm = fmaxf(gm, fmaxf(fmaxf(gv[0], gv[1]), fmaxf(gv[2], gv[3])));
+            kk += (kv[0] * kv[0] + kv[1] * kv[1]) + (kv[2] * kv[2] + kv[3] * kv[3]);
+        }
+        const float e = fabsf(1.f - load_in(beta + t * H + h) * kk);
+        lsum += gm + (e > 1.f ? logf(e) : 0.f);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) lsum += __shfl_xor(lsum, m);
+    __shared__ float part[CP_THREADS / 64];
+    if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = lsum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < CP_THREADS / 64; ++w) tot += part[w];
+        flags[sh] = (tot < CP_LOG_NEGLIGIBLE) ? 1 : 0;  // (false for NaN input)
+    }
+}
+
 __global__ __launch_bounds__(CP_THREADS) void cp_identity_kernel(float *__restrict__ M, int64_t total, int32_t dk) {
     const int64_t i = (int64_t)blockIdx.x * CP_THREADS + threadIdx.x;
     if (i >= total) return;
@@ -58,6 +105,7 @@ template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 16)) void cp_scan_kernel(const float *__restrict__ init,
                                                                 const float *__restrict__ M,
                                                                 const float *__restrict__ St,
+                                                                const int32_t *__restrict__ skip,
                                                                 float *__restrict__ Sin, int32_t H, int32_t R) {
     constexpr int NKB = DK / 16, NJ = DV / 16, LD = 20;
     __shared__ __attribute__((aligned(16))) float S[2][DK * LD];
@@ -105,10 +153,11 @@ __global__ __launch_bounds__(64 * (DK / 16)) void cp_scan_kernel(const float *__
             c = mma_f32_k16(a[kb], b, c);
         }
         float *Sn = Sin + seg(r + 1) * DK * DV;
+        const bool negligible = skip && skip[seg(r)];  // M_r not computed (it holds the identity)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * I + 4 * gq + j;
-            const float x = c[j] + t[j];
+            const float x = negligible ? t[j] : c[j] + t[j];
             Sn[row * DV + col] = x;
             Sl[row * LD + m] = x;
         }
@@ -145,19 +194,42 @@ hipError_t launch_cp_identity(float *M, int64_t n_mats, int32_t dk, void *stream
 }
 
 template <int DK, int DV>
-static hipError_t launch_scan_t(const float *init, const float *M, const float *St, float *Sin, int32_t nseq,
-                                int32_t H, int32_t R, void *stream) {
+static hipError_t launch_scan_t(const float *init, const float *M, const float *St, const int32_t *skip, float *Sin,
+                                int32_t nseq, int32_t H, int32_t R, void *stream) {
     const int64_t grid = (int64_t)nseq * H * (DV / 16);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((cp_scan_kernel<DK, DV>), dim3((unsigned)grid), dim3(64 * (DK / 16)), 0,
-                       (hipStream_t)stream, init, M, St, Sin, H, R);
+                       (hipStream_t)stream, init, M, St, skip, Sin, H, R);
     return hipGetLastError();
 }
 
-hipError_t launch_cp_scan(const float *init, const float *M, const float *St, float *Sin, int32_t nseq, int32_t H,
-                          int32_t dk, int32_t dv, int32_t R, void *stream) {
+template <typename T>
+static hipError_t launch_bound_t(const void *k, const void *g, const void *beta, const int32_t *cu_seg, int32_t nseg,
+                                 int32_t H, int32_t dk, int32_t *flags, void *stream) {
+    const unsigned grid = (unsigned)((int64_t)nseg * H);
+    if (grid == 0) return hipSuccess;
+    const hipStream_t st = (hipStream_t)stream;
+    const T *kk = (const T *)k, *gg = (const T *)g, *bb = (const T *)beta;
+    switch (dk) {
+        case 16: hipLaunchKernelGGL((cp_bound_kernel<T, 16>), dim3(grid), dim3(CP_THREADS), 0, st, kk, gg, bb, cu_seg, H, flags); break;
+        case 32: hipLaunchKernelGGL((cp_bound_kernel<T, 32>), dim3(grid), dim3(CP_THREADS), 0, st, kk, gg, bb, cu_seg, H, flags); break;
+        case 64: hipLaunchKernelGGL((cp_bound_kernel<T, 64>), dim3(grid), dim3(CP_THREADS), 0, st, kk, gg, bb, cu_seg, H, flags); break;
+        case 128: hipLaunchKernelGGL((cp_bound_kernel<T, 128>), dim3(grid), dim3(CP_THREADS), 0, st, kk, gg, bb, cu_seg, H, flags); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_cp_bound(const void *k, const void *g, const void *beta, const int32_t *cu_seg, int32_t nseg,
+                           int32_t H, int32_t dk, bool bf16, int32_t *flags, void *stream) {
+    return bf16 ? launch_bound_t<__bf16>(k, g, beta, cu_seg, nseg, H, dk, flags, stream)
+                : launch_bound_t<float>(k, g, beta, cu_seg, nseg, H, dk, flags, stream);
+}
+
+hipError_t launch_cp_scan(const float *init, const float *M, const float *St, const int32_t *skip, float *Sin,
+                          int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R, void *stream) {
 #define KDA_CP_CASE(DKV, DVV) \
-    if (dk == DKV && dv == DVV) return launch_scan_t<DKV, DVV>(init, M, St, Sin, nseq, H, R, stream);
+    if (dk == DKV && dv == DVV) return launch_scan_t<DKV, DVV>(init, M, St, skip, Sin, nseq, H, R, stream);
 #define KDA_CP_ROW(DKV) KDA_CP_CASE(DKV, 16) KDA_CP_CASE(DKV, 32) KDA_CP_CASE(DKV, 64) KDA_CP_CASE(DKV, 128)
     KDA_CP_ROW(16) KDA_CP_ROW(32) KDA_CP_ROW(64) KDA_CP_ROW(128)
 #undef KDA_CP_ROW

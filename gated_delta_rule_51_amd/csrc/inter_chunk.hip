@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
     int32_t nseq, int32_t H, const float *__restrict__ ws, float *__restrict__ o,
-    float *__restrict__ fin, int32_t nsplit, int32_t nchains) {
+    float *__restrict__ fin, int32_t nsplit, int32_t nchains, const int32_t *__restrict__ skip) {
     using C = IC<DK, DV, T, NW>;
     using OpT = typename C::OpT;
     using Raw4 = typename C::Raw4;
@@ -150,6 +150,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 4 ? 2 : 1)) void inter_chunk_kernel
     const int split = sx % nsplit;
     const int chain = (sx / nsplit) * 8 + xcd;
     if (chain >= nchains) return;
+    if (skip && skip[chain]) return;  // (context parallelism: a transition known to be negligible)
     const int s = chain / H, h = chain % H;
 
     const int tid = threadIdx.x;
@@ -504,7 +505,7 @@ static hipError_t launch_ic_t(const InterChunkArgs &a) {
     const int64_t grid = groups * 8 * nsplit;
     hipLaunchKernelGGL((inter_chunk_kernel<DK, DV, T, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                        (hipStream_t)a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.v,
-                       (const T *)a.g, a.init, a.cu, a.nseq, a.H, a.ws, a.o, a.fin, nsplit, nchains);
+                       (const T *)a.g, a.init, a.cu, a.nseq, a.H, a.ws, a.o, a.fin, nsplit, nchains, a.skip);
     return hipGetLastError();
 }
 

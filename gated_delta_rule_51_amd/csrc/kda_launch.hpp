@@ -93,6 +93,7 @@ struct InterChunkArgs {
     int32_t ws_consumers, ws_producers;  // warp-specialised kernel shape; 0, 0 = choose automatically
     void *stream;
     const LayerPrologue *layer = nullptr;  // fused layer prologue on load (bf16, dk = dv = 128), or none
+    const int32_t *skip = nullptr;         // per chain (s * H + h): nonzero = leave that chain untouched
 };
 
 // Single-pass prefill (prefill_fused.hip): bf16 inputs, dk = dv = 128, many chains; no workspace.
@@ -166,8 +167,12 @@ int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk
 // Intra-device context parallelism (cp.hip): the small kernels around the prefill passes.
 hipError_t launch_cp_segments(const int32_t *cu, int32_t nseq, int32_t R, int32_t *cu_seg, void *stream);
 hipError_t launch_cp_identity(float *M, int64_t n_mats, int32_t dk, void *stream);
-hipError_t launch_cp_scan(const float *init, const float *M, const float *St, float *Sin, int32_t nseq, int32_t H,
-                          int32_t dk, int32_t dv, int32_t R, void *stream);
+// Per (segment, head): nonzero when the bound on the segment's transition, ||M||_2 <=
+// prod_t max_i alpha_t,i max(1, |1 - beta_t ||k_t||^2|), is below 2^-30.
+hipError_t launch_cp_bound(const void *k, const void *g, const void *beta, const int32_t *cu_seg, int32_t nseg,
+                           int32_t H, int32_t dk, bool bf16, int32_t *flags, void *stream);
+hipError_t launch_cp_scan(const float *init, const float *M, const float *St, const int32_t *skip, float *Sin,
+                          int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R, void *stream);
 hipError_t launch_cp_final(const float *Sin, float *fin, int32_t nseq, int32_t H, int32_t dk, int32_t dv, int32_t R,
                            void *stream);
 

@@ -110,10 +110,13 @@ size_t kda_chunk_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
 /* Bytes of device workspace kda_prefill needs for these arguments.  KDA_BF16
  * inputs with dk = dv = 128 (the K3 layer's heads) and at least 256
  * (sequence, head) chains run a single-pass kernel that keeps the chunk-local
- * operands on chip: 0 bytes, and the workspace may be NULL.  Every other shape
- * runs the two phases and needs kda_chunk_workspace_bytes(...).  0 is also
- * returned for invalid arguments; kda_prefill then reports which argument is
- * wrong. */
+ * operands on chip: 0 bytes, and the workspace may be NULL.  KDA_BF16 inputs
+ * with dk >= 32, at most 64 chains and at least 16,384 tokens per sequence on
+ * average run with intra-device context parallelism in R = clamp(128 / chains,
+ * 2, 16) segments (kda_prefill_cp): kda_prefill_cp_workspace_bytes(..., R).
+ * Every other shape runs the two phases and needs kda_chunk_workspace_bytes(...).
+ * 0 is also returned for invalid arguments; kda_prefill then reports which
+ * argument is wrong. */
 size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype dt);
 
@@ -126,8 +129,10 @@ size_t kda_prefill_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H
  * A_qk) two chunks ahead of the waves that carry the state, so the inputs are
  * read from HBM once and nothing goes through a workspace (the overlap of the
  * token-parallel and the serial phases that the page's systems section
- * describes).  Other shapes: the chunk-local phase (kda_chunk_local) then the
- * inter-chunk phase (kda_inter_chunk), with the workspace between them. */
+ * describes).  Few long chains (see kda_prefill_workspace_bytes): kda_prefill_cp,
+ * which spreads each sequence over more compute units (same page, intra-device
+ * context parallelism).  Other shapes: the chunk-local phase (kda_chunk_local)
+ * then the inter-chunk phase (kda_inter_chunk), with the workspace between them. */
 kda_status kda_prefill(const void *q, const void *k, const void *v,
                        const void *log_alpha, const void *beta,
                        const float *init_state, const int32_t *cu_seqlens,
@@ -198,12 +203,15 @@ kda_status kda_inter_chunk_shaped(const void *q, const void *k, const void *v,
  * S_out = M S_in + S~ (Kimi K3 report digest, context parallelism of KDA: the same
  * algebra as across devices, here between the compute units of one GPU).  Three
  * recurrence passes over the pieces (S~ from zero states; M from the identity with
- * v = 0; the outputs from the exact states) and one chunk-local pass.  Same inputs,
- * outputs and precision as kda_prefill; segments = 1 reduces to it (at three times the
- * recurrence work).
+ * v = 0; the outputs from the exact states) and one chunk-local pass.  A piece whose
+ * transition is provably negligible -- the bound ||M||_2 <= prod_t max_i alpha_t,i
+ * max(1, |1 - beta_t ||k_t||^2|), evaluated on the device from its inputs, below 2^-30 --
+ * skips the M pass and enters the scan with M = 0.  Same inputs, outputs and precision
+ * as kda_prefill; segments = 1 reduces to it (at up to three times the recurrence work).
  *   segments: 1 .. 64.
  *   workspace: kda_prefill_cp_workspace_bytes(...) bytes, 16-byte aligned (chunk-local
- *   operands of the pieces; per piece and head S~, S_in (dk x dv) and M (dk x dk), fp32). */
+ *   operands of the pieces; per piece and head S~, S_in (dk x dv) and M (dk x dk), fp32,
+ *   and a flag). */
 size_t kda_prefill_cp_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H,
                                       int32_t dk, int32_t dv, kda_dtype dt,
                                       int32_t segments);

@@ -27,8 +27,12 @@ hipError_t launch_out_norm_gate(const OutNormGateArgs &) { return hipSuccess; }
 hipError_t launch_prefill_fused(const PrefillFusedArgs &, int, int) { return hipSuccess; }
 hipError_t launch_cp_segments(const int32_t *, int32_t, int32_t, int32_t *, void *) { return hipSuccess; }
 hipError_t launch_cp_identity(float *, int64_t, int32_t, void *) { return hipSuccess; }
-hipError_t launch_cp_scan(const float *, const float *, const float *, float *, int32_t, int32_t, int32_t, int32_t,
-                          int32_t, void *) {
+hipError_t launch_cp_scan(const float *, const float *, const float *, const int32_t *, float *, int32_t, int32_t,
+                          int32_t, int32_t, int32_t, void *) {
+    return hipSuccess;
+}
+hipError_t launch_cp_bound(const void *, const void *, const void *, const int32_t *, int32_t, int32_t, int32_t, bool,
+                           int32_t *, void *) {
     return hipSuccess;
 }
 hipError_t launch_cp_final(const float *, float *, int32_t, int32_t, int32_t, int32_t, int32_t, void *) {

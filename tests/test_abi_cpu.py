@@ -268,14 +268,25 @@ def test_backward_workspace_and_arguments(lib):
 
 
 def test_prefill_cp_workspace_and_arguments(lib):
-    # per segment and head: S~ and S_in (dk x dv) and M (dk x dk); the chunk-local operands of
-    # the segments; the segment list; each region 256-byte aligned
+    # per segment and head: S~ and S_in (dk x dv), M (dk x dk) and a flag; the chunk-local
+    # operands of the segments; the segment list; each region 256-byte aligned
     N, nseq, H, dk, dv, R = 64, 2, 3, 16, 32, 4
     up = lambda x: (x + 255) // 256 * 256
     segs = nseq * R
     cl = (N // 16 + segs) * H * 512 * 4
-    want = up(cl) + up((segs + 1) * 4) + 2 * up(segs * H * dk * dv * 4) + up(segs * H * dk * dk * 4)
+    want = up(cl) + up((segs + 1) * 4) + 2 * up(segs * H * dk * dv * 4) + up(segs * H * dk * dk * 4) + \
+        up(segs * H * 4)
     assert lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, 1, R) == want
+    # kda_prefill takes context parallelism for <= 64 chains of >= 16,384 tokens on average (bf16,
+    # dk >= 32), with R = clamp(128 / chains, 2, 16): its workspace is then kda_prefill_cp's
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 12, 128, 128) == \
+        lib.kda_prefill_cp_workspace_bytes(65536, 1, 12, 128, 128, 1, 10)
+    assert kda.kda_prefill_workspace_bytes(65536, 2, 32, 128, 128) == \
+        lib.kda_prefill_cp_workspace_bytes(65536, 2, 32, 128, 128, 1, 2)
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 65, 128, 128) == (4096 + 1) * 65 * 2048   # 65 chains
+    assert kda.kda_prefill_workspace_bytes(16383, 1, 12, 128, 128) == (1023 + 1) * 12 * 2048   # short
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 12, 16, 128) == (4096 + 1) * 12 * 2048    # dk = 16
+    assert kda.kda_prefill_workspace_bytes(65536, 1, 12, 128, 128, torch.float32) == (4096 + 1) * 12 * 2048
     assert lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, 1, 0) == 0    # segments < 1
     assert lib.kda_prefill_cp_workspace_bytes(N, nseq, H, dk, dv, 1, 65) == 0   # segments > 64
     f = lib.kda_prefill_cp
