@@ -525,6 +525,47 @@ def bench_decode_window(torch, kda, workloads, dev, steps, T: int):
     return res
 
 
+def bench_decode_window_replay(torch, kda, workloads, dev, steps, T: int):
+    """The same windows as a serving loop runs them: each kda_decode_window_replay call replays
+    the previous window's accepted prefix (counts drawn uniform on [1, T], known only after that
+    window ran), commits the state after it, and runs the new window without committing it."""
+    w = workloads.workload(4)
+    B, H, dk, dv = w.nseq, w.H, w.dk, w.dv
+    state = workloads.decode_initial_state(B, H, dk, dv, device=dev)
+    names = ("q", "k", "v", "log_alpha", "beta")
+    nwin = len(steps) // T
+    wins = [{n: torch.stack([steps[i * T + t][n] for t in range(T)], dim=1).contiguous() for n in names}
+            for i in range(nwin)]
+    accs = [workloads.window_accept(B, T, device=dev, seed=i, lo=1) for i in range(nwin)]
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+
+    def prev_of(i):
+        x = wins[i - 1]
+        return {"q": x["q"], "k": x["k"], "v": x["v"], "gate": x["log_alpha"], "beta": x["beta"]}
+    scratch = state.clone()
+    kda.kda_decode_window_replay(prev_of(1), accs[0], *(wins[1][n] for n in names), scratch, o=o)
+    del scratch
+    torch.cuda.synchronize()
+    t = Timer(torch, nwin - 1)
+    for i in range(1, nwin):  # window 0 only supplies the first replay
+        x = wins[i]
+        with t:
+            kda.kda_decode_window_replay(prev_of(i), accs[i - 1], *(x[n] for n in names), state, o=o)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    replayed = float(torch.stack(accs[:-1]).double().mean())
+    # state read + written once, T new and (on average) `replayed` replayed tokens of inputs, T outputs
+    per_call = B * H * (window_bytes_per_head(dk, dv, T) + replayed * (2 * (3 * dk + dv + 1)))
+    gbs = per_call / (ms * 1e-3) / 1e9
+    res = {"workload": f"{w.name}_window_replay", "T": T, "heads": B * H, "calls": nwin - 1,
+           "ms_per_call": round(ms, 5), "replayed_tokens_mean": replayed, "gbs": gbs,
+           "hbm_peak_frac": gbs / HBM_PEAK_GBS, "accepted_tokens_per_s": replayed * B / (ms * 1e-3),
+           "draft_tokens_per_s": B * T / (ms * 1e-3)}
+    del state, wins, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def _event_ms(torch, fn, reps: int) -> float:
     """Mean milliseconds per call of fn() over reps back-to-back calls on torch's current stream
     (every library call is enqueued there), after one untimed call."""
@@ -841,6 +882,7 @@ def main() -> int:
         for T in (4, 8):
             log(f"[bench] decode windows of {T} drafts (speculative verification), B=256 H=96")
             out[f"decode_window_{T}"] = bench_decode_window(torch, kda, workloads, dev, steps, T)
+            out[f"decode_window_replay_{T}"] = bench_decode_window_replay(torch, kda, workloads, dev, steps, T)
         del steps
         torch.cuda.empty_cache()
     if args.only in ("all", "backward"):

@@ -31,6 +31,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE"
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_prefill", "kda_prefill_single_pass",
            "kda_inter_chunk_shaped", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
+           "kda_decode_window_replay",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
            "kda_gate", "kda_short_conv", "kda_out_norm_gate", "kda_prefill_layer_workspace_bytes",
@@ -88,6 +89,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_window_fused.restype = ctypes.c_int
     lib.kda_decode_window_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
                                             i32, i32, ctypes.c_int, vp]
+    lib.kda_decode_window_replay.restype = ctypes.c_int
+    lib.kda_decode_window_replay.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             f32, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.kda_decode_layer_step.restype = ctypes.c_int
     lib.kda_decode_layer_step.argtypes = [vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
                                           i32, ctypes.c_int, vp]
@@ -605,6 +609,42 @@ def kda_decode_window_fused(q, k, v, gate, beta, state, accept=None, *, gate_A_l
         _ptr(o), _ptr(accept), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
         B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
     return (o if output_o else None), y
+
+
+def kda_decode_window_replay(prev, replay, q, k, v, gate, beta, state, *, gate_A_log=None, out_gate=None,
+                             norm_w=None, norm_eps: float = 1e-6, o=None, y=None, stream=None):
+    """One speculative-decoding call as a serving loop makes it: replay the accepted prefix of
+    the previous window (``prev`` = dict or tuple of its q, k, v, gate, beta [B, Tp, H, .] or
+    None; ``replay`` int32 [B] accepted counts, known only now), commit the state after it, then
+    run this window's T tokens (q, k, v, gate [B, T, H, .], beta [B, T, H]) without committing
+    them.  Returns (o [B, T, H, dv], y or None)."""
+    _check_tensors(q, k, v, gate, beta)
+    if q.dim() != 4:
+        raise ValueError("expected q, k, gate [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, T, H, dk) or gate.shape != (B, T, H, dk) or v.shape != (B, T, H, dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("expected q, k, gate [B, T, H, dk], v [B, T, H, dv], beta [B, T, H]")
+    _check_dev("state", state, q.device, torch.float32, (B, H, dk, dv))
+    Tp = 0
+    p = (None,) * 5
+    if prev is not None:
+        p = tuple(prev[n] for n in ("q", "k", "v", "gate", "beta")) if isinstance(prev, dict) else tuple(prev)
+        Tp = p[0].shape[1]
+        for name, t, shp in zip(("q", "k", "v", "gate", "beta"), p,
+                                ((B, Tp, H, dk), (B, Tp, H, dk), (B, Tp, H, dv), (B, Tp, H, dk), (B, Tp, H))):
+            _check_dev("prev " + name, t, q.device, q.dtype, shp)
+        _check_dev("replay", replay, q.device, torch.int32, (B,))
+    y = _fusion_args((B, T, H, dv), q.dtype, q.device, H, dv, gate_A_log, out_gate, norm_w, y, True)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    _check_dev("o", o, q.device, torch.float32, (B, T, H, dv))
+    _check(load_library().kda_decode_window_replay(
+        *(_ptr(t) for t in p), _ptr(replay if Tp > 0 else None), Tp, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+        _ptr(gate_A_log), _ptr(beta), _ptr(state), _ptr(o), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
+        B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
+    return o, y
 
 
 def kda_decode_layer_step(qkv, conv_w, conv_cache, gate, beta, state, *, dk: int, l2_eps: float = 1e-6,

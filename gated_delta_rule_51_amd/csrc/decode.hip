@@ -293,17 +293,27 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 // are half as large (two per compute unit, at most 128 registers per lane) so
 // that one's barrier waits are filled by the other's arithmetic.  Inputs are
 // [B, Tw, H, ...] (token-major within a sequence).
+//
+// With a replay (the serving form of the same page's scheme: the verifier's
+// accepted count for a window is known only after the window ran), the tokens
+// of a (sequence, head) are first rp = replay[b] tokens of the previous window
+// (inputs [B, Tp, H, ...], no outputs), then the Tw tokens of this window; the
+// state is written back after token rp + acc, acc = accept[b] (or acc_default),
+// so with no accept the committed state is the one after the accepted prefix
+// of the previous window and this window's drafts stay uncommitted.
 // Threads per window workgroup, at most.
 constexpr int WINDOW_THREADS = 512;
 
-template <int DK, int DV, typename T, bool FX>
+template <int DK, int DV, typename T, bool FX, bool REPLAY>
 __global__ __launch_bounds__((DecodeShape<DK, DV, WINDOW_THREADS>::NT))
 __attribute__((amdgpu_waves_per_eu((2 * DecodeShape<DK, DV, WINDOW_THREADS>::NT + 255) / 256, 8)))
 void decode_window_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
     float *__restrict__ o, const int32_t *__restrict__ accept, int64_t heads, int32_t H, int32_t Tw,
-    DecodeFusion fx) {
+    DecodeFusion fx, const T *__restrict__ pq, const T *__restrict__ pk, const T *__restrict__ pv,
+    const T *__restrict__ pg, const T *__restrict__ pb, const int32_t *__restrict__ replay, int32_t Tp,
+    int32_t acc_default) {
     using Sh = DecodeShape<DK, DV, WINDOW_THREADS>;
     constexpr int NC4 = Sh::NC4, RP = Sh::RP, NR = Sh::NR, P = Sh::P, NKW = Sh::NKW;
     const int tid = threadIdx.x;
@@ -320,17 +330,28 @@ void decode_window_kernel(
         float k, q, g, b;  // k, q, g of key channel tid (tid < DK)
         f32x4 v;           // v of columns 4 c4 .. +3
     };
+    // Replayed tokens of a head's sequence (0 without a replay), uniform per head.
+    auto replay_of = [&](int64_t hd) -> int {
+        if constexpr (!REPLAY) return 0;
+        const int r = replay[hd / H];
+        return r < 0 ? 0 : (r > Tp ? Tp : r);
+    };
     // Token inputs through buffer resources based at the token's row (uniform),
     // so every lane offset is a loop-invariant 32-bit register.  Head indices
-    // stay below 2^31 (B * T * H < 2^31 is checked on the host).
+    // stay below 2^31 (B * T * H < 2^31 is checked on the host).  Token t of a
+    // head is replayed token t (t < rp) or window token t - rp.
     auto load_tok = [&](Tok &x, uint32_t hd, int t) {
         const uint32_t bq = hd / (uint32_t)H;
-        const int64_t row = ((int64_t)bq * Tw + t) * H + (hd - bq * (uint32_t)H);
+        const int rp = replay_of(hd);
+        const bool rep = REPLAY && t < rp;
+        const int64_t row = rep ? ((int64_t)bq * Tp + t) * H + (hd - bq * (uint32_t)H)
+                                : ((int64_t)bq * Tw + (t - rp)) * H + (hd - bq * (uint32_t)H);
+        const T *kb = rep ? pk : k, *qb = rep ? pq : q, *gb = rep ? pg : g, *vb = rep ? pv : v, *bb = rep ? pb : beta;
         if (tid < DK) {
             const uint32_t off = tid * (uint32_t)sizeof(T);
-            const rsrc_t rk = make_rsrc(k + row * DK, DK * sizeof(T));
-            const rsrc_t rq = make_rsrc(q + row * DK, DK * sizeof(T));
-            const rsrc_t rgt = make_rsrc(g + row * DK, DK * sizeof(T));
+            const rsrc_t rk = make_rsrc(kb + row * DK, DK * sizeof(T));
+            const rsrc_t rq = make_rsrc(qb + row * DK, DK * sizeof(T));
+            const rsrc_t rgt = make_rsrc(gb + row * DK, DK * sizeof(T));
             if constexpr (sizeof(T) == 4) {
                 x.k = __uint_as_float(buf_load_u32(rk, off));
                 x.q = __uint_as_float(buf_load_u32(rq, off));
@@ -343,12 +364,12 @@ void decode_window_kernel(
         } else {
             x.k = x.q = x.g = 0.f;
         }
-        const rsrc_t rv = make_rsrc(v + row * DV, DV * sizeof(T));
+        const rsrc_t rv = make_rsrc(vb + row * DV, DV * sizeof(T));
         if constexpr (sizeof(T) == 4)
             x.v = __builtin_bit_cast(f32x4, buf_load_u32x4(rv, 16u * c4));
         else
             x.v = unpack_bf16x4(buf_load_u32x2(rv, 8u * c4));
-        x.b = load_in(beta + row);
+        x.b = load_in(bb + row);
     };
     // State rows go through a buffer resource per head: one 32-bit lane offset
     // (row rg, quad c4) serves all NR rows, the row step is the uniform offset.
@@ -372,15 +393,17 @@ void decode_window_kernel(
     // loaded during the first token, its first token during the last.
     auto window = [&](f32x4 (&rows)[NR], f32x4 (&nrows)[NR], int64_t head) {
         const int64_t bq = head / H;
-        int acc = Tw;
+        int acc = acc_default;
         if (accept) {
             acc = accept[bq];
             acc = acc < 0 ? 0 : (acc > Tw ? Tw : acc);
         }
+        const int rp = replay_of(head), n = rp + Tw;
+        acc += rp;  // the state is written back after token acc (not at all when 0)
         const bool more = head + stride < heads;
         const rsrc_t rs = state_rsrc(head);
         const float gscale = FX && fx.A_log ? __expf(fx.A_log[head - bq * H]) : 0.f;
-        for (int t = 0; t < Tw; ++t) {
+        for (int t = 0; t < n; ++t) {
             // LDS reuse across tokens as across heads in the single-token kernel
             if (tid < DK) {
                 s_k[tid] = cur.k;
@@ -396,7 +419,7 @@ void decode_window_kernel(
             const f32x4 vv = cur.v;
             const float bb = cur.b;
             if (t == 0 && more) load_rows(nrows, head + stride);
-            if (t + 1 < Tw) {
+            if (t + 1 < n) {
                 load_tok(nxt, head, t + 1);
             } else if (more) {
                 load_tok(nxt, head + stride, 0);
@@ -434,8 +457,8 @@ void decode_window_kernel(
 #pragma unroll
             for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
             const f32x4 delta = bb * (vv - vhat);
-            const int64_t orow = (bq * Tw + t) * H + (head - bq * H);
-            if (o && rg == 0) reinterpret_cast<f32x4 *>(o + orow * DV)[c4] = rq + kq * delta;
+            const int64_t orow = (bq * Tw + (t - rp)) * H + (head - bq * H);
+            if (o && rg == 0 && t >= rp) reinterpret_cast<f32x4 *>(o + orow * DV)[c4] = rq + kq * delta;
 #pragma unroll
             for (int r = 0; r < NR; ++r) rows[r] += kr[r] * delta;  // erase + write
             if (t + 1 == acc) {
@@ -504,10 +527,13 @@ static hipError_t launch_window_t(const DecodeWindowArgs &a) {
     const int64_t cap = GRID_THREADS / Sh::NT;
     const int64_t grid = heads < cap ? heads : cap;
     const bool fused = a.fx.A_log != nullptr;
-    hipLaunchKernelGGL((fused ? decode_window_kernel<DK, DV, T, true> : decode_window_kernel<DK, DV, T, false>),
+    auto kern = a.replay ? (fused ? decode_window_kernel<DK, DV, T, true, true> : decode_window_kernel<DK, DV, T, false, true>)
+                         : (fused ? decode_window_kernel<DK, DV, T, true, false> : decode_window_kernel<DK, DV, T, false, false>);
+    hipLaunchKernelGGL(kern,
                        dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.state, a.o,
-                       a.accept, heads, a.H, a.T, a.fx);
+                       a.accept, heads, a.H, a.T, a.fx, (const T *)a.pq, (const T *)a.pk, (const T *)a.pv,
+                       (const T *)a.pg, (const T *)a.pbeta, a.replay, a.Tp, a.acc_default < 0 ? a.T : a.acc_default);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.fx.u) return e;
     // The epilogue as a second pass over the window's outputs: inside the window

@@ -50,11 +50,17 @@ struct DecodeArgs {
 struct DecodeWindowArgs {
     const void *q, *k, *v, *g, *beta;
     float *state, *o;          // o may be NULL (no outputs)
-    const int32_t *accept;     // device [B] or NULL (all T tokens accepted)
+    const int32_t *accept;     // device [B] or NULL (all T tokens accepted; none with a replay)
     int32_t B, T, H, dk, dv;
     bool bf16;
     void *stream;
     DecodeFusion fx;
+    // Replay before the window: the previous window's inputs ([B, Tp, H, .]) and, per
+    // sequence, how many of its tokens were accepted (replayed and committed first).
+    const void *pq = nullptr, *pk = nullptr, *pv = nullptr, *pg = nullptr, *pbeta = nullptr;
+    const int32_t *replay = nullptr;
+    int32_t Tp = 0;
+    int32_t acc_default = -1;  // tokens of this window committed without accept (-1: all T)
 };
 
 // The fused layer prefill's prologue on load (layer_prologue.hpp): what the two

@@ -299,6 +299,28 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v,
                              int32_t B, int32_t T, int32_t H, int32_t dk,
                              int32_t dv, kda_dtype dt, void *stream);
 
+/* Speculative decoding as a serving loop runs it (Kimi K3 report digest,
+ * serving section: the state cannot be rolled back, so the accepted drafts are
+ * replayed from their cached projected inputs and only verified states are
+ * written back).  The verifier's accepted count for a window is known only after
+ * the window ran, so each call first replays, per sequence, the first
+ * clamp(replay[b], 0, Tp) tokens of the PREVIOUS window (inputs pq, pk, pv,
+ * pgate, pbeta: [B, Tp, H, .] as in kda_decode_window; no outputs), writes the
+ * state back once after them (no write when that count is 0), and then runs the
+ * T tokens of this window (the bonus token and the new drafts) from that state,
+ * writing o [B, T, H, dv] for all of them and committing none.  One state read
+ * and at most one write per call.  Tp = 0: nothing to replay (the p* pointers and
+ * replay may be NULL).  gate_A_log, out_gate, norm_w, norm_eps, y as in
+ * kda_decode_window_fused (the gate applies to replayed and new tokens, the
+ * epilogue to the new tokens' outputs).  replay: device int32 [B], 4-byte
+ * aligned.  B * T * H and B * Tp * H < 2^31.  Errors as for kda_decode_window. */
+kda_status kda_decode_window_replay(const void *pq, const void *pk, const void *pv, const void *pgate,
+                                    const void *pbeta, const int32_t *replay, int32_t Tp, const void *q,
+                                    const void *k, const void *v, const void *gate, const float *gate_A_log,
+                                    const void *beta, float *state, float *o, const void *out_gate,
+                                    const float *norm_w, float norm_eps, void *y, int32_t B, int32_t T, int32_t H,
+                                    int32_t dk, int32_t dv, kda_dtype dt, void *stream);
+
 /* kda_decode_step and kda_decode_window with the layer's gate and epilogue
  * fused in (the passes below, evaluated where the decode kernels already hold
  * the operands, so a decode step of the layer is one launch):

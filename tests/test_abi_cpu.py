@@ -186,6 +186,28 @@ def test_fused_decode_rejects_bad_arguments(lib):
              None) == 3
 
 
+def test_decode_window_replay_rejects_bad_arguments(lib):
+    f = lib.kda_decode_window_replay
+    # pq pk pv pg pb replay Tp | q k v g A b state o u nw neps y B T H dk dv dt stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0,
+            None, 2, 3, 1, 16, 16, kda.KDA_BF16, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a5=None) == 1            # replay counts missing with Tp > 0
+    assert call(a0=None) == 1            # previous window's q missing
+    assert call(a5=FAKE + 2) == 2        # replay misaligned
+    assert call(a1=FAKE + 2) == 2        # previous window's k misaligned
+    assert call(a6=-1) == 3              # Tp < 0
+    assert call(a20=0) == 3              # T < 1
+    assert call(a23=48) == 4             # dv
+    assert call(a12=None) == 1           # state missing
+    assert call(a14=FAKE, a15=FAKE, a18=FAKE, a13=None) == 1   # epilogue without o
+
+
 def test_decode_layer_step_rejects_bad_arguments(lib):
     f = lib.kda_decode_layer_step  # qkv w cache eps gate A beta state o u nw neps y B H dk dv dt stream
     assert f(FAKE, None, FAKE, 1e-6, FAKE, None, FAKE, FAKE, FAKE, None, None, 0.0, None, 1, 1, 16, 16, 1,
