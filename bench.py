@@ -768,7 +768,22 @@ def bench_backward(index, torch, kda, workloads, dev, reps: int):
            "backward_over_forward": ms_b / ms_f, "tokens_per_s": N / (ms_b * 1e-3),
            "algorithmic_bytes": N * H * per_th, "gbs": gbs, "hbm_peak_frac": gbs / HBM_PEAK_GBS,
            "workspace_bytes": nbytes}
-    del x, d_o, d_f, ws
+    del ws
+    torch.cuda.empty_cache()
+    if w.nseq == 1 and N > 16384:
+        # one long sequence: the slabbed backward, one slab's workspace at a time
+        slab = 16384
+        nb2 = kda.kda_prefill_backward_slabbed_workspace_bytes(N, H, dk, dv, slab, x["q"].dtype)
+        ws2 = torch.empty(nb2 // 4 + 4, dtype=torch.float32, device=dev)
+
+        def bwd_slabbed():
+            kda.kda_prefill_backward_slabbed(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, None, d_f,
+                                             slab_tokens=slab, workspace=ws2)
+        ms_s = _event_ms(torch, bwd_slabbed, reps)
+        res["slabbed"] = {"slab_tokens": slab, "ms_backward": round(ms_s, 4), "over_unsliced": ms_s / ms_b,
+                          "workspace_bytes": nb2}
+        del ws2
+    del x, d_o, d_f
     torch.cuda.empty_cache()
     return res
 

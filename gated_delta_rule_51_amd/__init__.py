@@ -33,6 +33,7 @@ EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_pref
            "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
            "kda_decode_window_replay",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
+           "kda_prefill_backward_slabbed_workspace_bytes", "kda_prefill_backward_slabbed",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
            "kda_gate", "kda_short_conv", "kda_out_norm_gate", "kda_prefill_layer_workspace_bytes",
            "kda_prefill_layer", "kda_status_string", "kda_last_hip_error")
@@ -100,6 +101,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill_backward.restype = ctypes.c_int
     lib.kda_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, ctypes.c_int,
                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_prefill_backward_slabbed_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_backward_slabbed_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.c_int, i64]
+    lib.kda_prefill_backward_slabbed.restype = ctypes.c_int
+    lib.kda_prefill_backward_slabbed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_int, vp, vp,
+                                                 vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
     lib.kda_prefill_cp_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_prefill_cp_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.kda_prefill_cp.restype = ctypes.c_int
@@ -709,5 +715,43 @@ def kda_prefill_backward(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, init_st
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu), nseq, N, H, dk, dv,
         _dtype_code(q.dtype), _ptr(d_o), _ptr(d_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
         _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dinit"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kda_prefill_backward_slabbed_workspace_bytes(total_tokens: int, H: int, dk: int, dv: int, slab_tokens: int,
+                                                 dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of kda_prefill_backward_slabbed (0: invalid arguments)."""
+    return int(load_library().kda_prefill_backward_slabbed_workspace_bytes(total_tokens, H, dk, dv,
+                                                                          _dtype_code(dtype), slab_tokens))
+
+
+def kda_prefill_backward_slabbed(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, *,
+                                 slab_tokens: int = 16384, need_d_init: bool = True, workspace=None, stream=None):
+    """kda_prefill_backward for one long sequence (q ... [N, H, .]) with the memory of one slab of
+    ``slab_tokens`` tokens (a multiple of 16).  Returns the same dict as kda_prefill_backward."""
+    N, H, dk, dv = _check_inputs(q, k, v, log_alpha, beta)
+    dev = q.device
+    _check_dev("d_o", d_o, dev, torch.float32, (N, H, dv))
+    if d_final is not None:
+        _check_dev("d_final", d_final, dev, torch.float32, (1, H, dk, dv))
+    if init_state is not None:
+        _check_dev("init_state", init_state, dev, torch.float32, (1, H, dk, dv))
+    lib = load_library()
+    nbytes = kda_prefill_backward_slabbed_workspace_bytes(N, H, dk, dv, slab_tokens, q.dtype)
+    if nbytes == 0:
+        raise KDAError(3, "kda_prefill_backward_slabbed: invalid shape or slab_tokens")
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=dev)
+    _check_workspace(workspace, dev, nbytes)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((N, H, dk), **f32), "dk": torch.empty((N, H, dk), **f32),
+           "dv": torch.empty((N, H, dv), **f32), "dlog_alpha": torch.empty((N, H, dk), **f32),
+           "dbeta": torch.empty((N, H), **f32),
+           "dinit": torch.empty((1, H, dk, dv), **f32) if need_d_init else None}
+    _check(lib.kda_prefill_backward_slabbed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), N, H, dk, dv,
+        _dtype_code(q.dtype), _ptr(d_o), _ptr(d_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dinit"]), int(slab_tokens), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

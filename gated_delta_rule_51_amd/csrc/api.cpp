@@ -594,6 +594,109 @@ kda_status kda_prefill_backward(const void *q, const void *k, const void *v, con
     return hip_status(kda::launch_backward(a));
 }
 
+// Slabbed backward of one sequence (see kda.h): the slabs' {0, length} lists, the state at
+// every slab boundary, two adjoint buffers, then one slab's backward workspace.
+struct SlabLayout {
+    size_t cu, bnd, adj, ws, total;
+    int32_t nslab;
+};
+SlabLayout slab_layout(int64_t N, int32_t H, int32_t dk, int32_t dv, int64_t L) {
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    SlabLayout S{};
+    S.nslab = N > L ? (int32_t)((N + L - 1) / L) : 1;
+    const size_t state = (size_t)H * dk * dv * 4;
+    S.cu = 0;
+    S.bnd = up((size_t)S.nslab * 8);
+    S.adj = S.bnd + up((size_t)(S.nslab > 1 ? S.nslab - 1 : 0) * state);
+    S.ws = S.adj + up(2 * state);
+    S.total = S.ws + up((size_t)kda::backward_workspace_floats(L < N ? L : N, 1, H, dk, dv) * 4);
+    return S;
+}
+kda_status check_slab(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt, int64_t L) {
+    kda_status st = check_backward_shape(1, N, H, dk, dv, dt);
+    if (st != KDA_OK) return st;
+    if (L < 16 || L % 16 != 0 || L >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    if ((N + L - 1) / L >= (int64_t(1) << 24)) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+size_t kda_prefill_backward_slabbed_workspace_bytes(int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                                                    kda_dtype dt, int64_t slab_tokens) {
+    if (check_slab(total_tokens, H, dk, dv, dt, slab_tokens) != KDA_OK) return 0;
+    return slab_layout(total_tokens, H, dk, dv, slab_tokens).total;
+}
+
+kda_status kda_prefill_backward_slabbed(const void *q, const void *k, const void *v, const void *log_alpha,
+                                        const void *beta, const float *init_state, int64_t total_tokens, int32_t H,
+                                        int32_t dk, int32_t dv, kda_dtype dt, const float *d_o, const float *d_final,
+                                        float *d_q, float *d_k, float *d_v, float *d_log_alpha, float *d_beta,
+                                        float *d_init, int64_t slab_tokens, void *workspace, size_t ws_bytes,
+                                        void *stream) {
+    kda_status st = check_slab(total_tokens, H, dk, dv, dt, slab_tokens);
+    if (st != KDA_OK) return st;
+    const bool any = total_tokens > 0;
+    st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, any);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({}, {init_state, d_final, d_init});
+    if (st != KDA_OK) return st;
+    for (const void *p : {static_cast<const void *>(d_o), static_cast<const void *>(d_q),
+                          static_cast<const void *>(d_k), static_cast<const void *>(d_v),
+                          static_cast<const void *>(d_log_alpha), static_cast<const void *>(d_beta)}) {
+        if (!p && any) return KDA_ERR_NULL;
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return KDA_ERR_ALIGN;
+    }
+    const SlabLayout S = slab_layout(total_tokens, H, dk, dv, slab_tokens);
+    if (!workspace || ws_bytes < S.total) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_ALIGN;
+    char *w = static_cast<char *>(workspace);
+    int32_t *cu = reinterpret_cast<int32_t *>(w + S.cu);
+    float *bnd = reinterpret_cast<float *>(w + S.bnd), *adj = reinterpret_cast<float *>(w + S.adj);
+    float *ws = reinterpret_cast<float *>(w + S.ws);
+    const int64_t state = (int64_t)H * dk * dv;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const bool bf16 = dt == KDA_BF16;
+    if (S.nslab <= 1) {  // one slab: the plain backward (also for N = 0, with a one-element list)
+        if ((st = hip_status(kda::launch_backward_slab_cu(cu, total_tokens, slab_tokens, 1, stream))) != KDA_OK)
+            return st;
+        kda::BackwardArgs a{q, k, v, log_alpha, beta, init_state, cu, 1, total_tokens, H, dk, dv, bf16, d_o,
+                            d_final, d_q, d_k, d_v, d_log_alpha, d_beta, d_init, ws, stream};
+        return hip_status(kda::launch_backward(a));
+    }
+    if ((st = hip_status(kda::launch_backward_slab_cu(cu, total_tokens, slab_tokens, S.nslab, stream))) != KDA_OK)
+        return st;
+    // token views and boundary states of slab s (boundary s = the state entering slab s + 1)
+    auto in = [&](const void *p, int s, int64_t d) {
+        return p ? static_cast<const void *>(static_cast<const char *>(p) + (size_t)s * slab_tokens * H * d * esz)
+                 : nullptr;
+    };
+    auto f32 = [&](const float *p, int s, int64_t d) { return p ? p + (size_t)s * slab_tokens * H * d : nullptr; };
+    auto f32w = [&](float *p, int s, int64_t d) { return p ? p + (size_t)s * slab_tokens * H * d : nullptr; };
+    auto len_of = [&](int s) {
+        const int64_t a = (int64_t)s * slab_tokens;
+        return (total_tokens - a < slab_tokens ? total_tokens - a : slab_tokens);
+    };
+    auto init_of = [&](int s) { return s == 0 ? init_state : bnd + (size_t)(s - 1) * state; };
+    // 1. boundary states, slab by slab, by the backward's own fp32 forward sweep
+    for (int s = 0; s + 1 < S.nslab; ++s) {
+        kda::BackwardArgs a{in(q, s, dk), in(k, s, dk), in(v, s, dv), in(log_alpha, s, dk), in(beta, s, 1),
+                            init_of(s), cu + 2 * s, 1, len_of(s), H, dk, dv, bf16, nullptr, nullptr, nullptr,
+                            nullptr, nullptr, nullptr, nullptr, nullptr, ws, stream};
+        if ((st = hip_status(kda::launch_backward_states(a, bnd + (size_t)s * state))) != KDA_OK) return st;
+    }
+    // 2. the slabs' gradients in reverse; the adjoint of a slab's initial state is the next
+    //    (earlier) slab's final-state adjoint
+    for (int s = S.nslab - 1; s >= 0; --s) {
+        const float *dfin = s == S.nslab - 1 ? d_final : adj + (size_t)((s + 1) & 1) * state;
+        float *dini = s == 0 ? d_init : adj + (size_t)(s & 1) * state;
+        kda::BackwardArgs a{in(q, s, dk), in(k, s, dk), in(v, s, dv), in(log_alpha, s, dk), in(beta, s, 1),
+                            init_of(s), cu + 2 * s, 1, len_of(s), H, dk, dv, bf16, f32(d_o, s, dv), dfin,
+                            f32w(d_q, s, dk), f32w(d_k, s, dk), f32w(d_v, s, dv), f32w(d_log_alpha, s, dk),
+                            f32w(d_beta, s, 1), dini, ws, stream};
+        if ((st = hip_status(kda::launch_backward(a))) != KDA_OK) return st;
+    }
+    return KDA_OK;
+}
+
 kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int32_t dk, kda_dtype dt,
                     void *log_alpha, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;

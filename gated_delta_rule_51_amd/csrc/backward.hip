@@ -447,11 +447,13 @@ __device__ __forceinline__ void sweep_producer(SweepSet<DK, ADJ, TRA> (&L)[2], c
     });
 }
 
+// fin != NULL: the state after each sequence's last chunk is also written there ([nseq, H,
+// dk, dv]; the boundary pass of a slabbed backward).
 template <int DK, int DV, int NS, typename T>
 __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ g, const float *__restrict__ init,
     const int32_t *__restrict__ cu, int32_t H, const float *__restrict__ mats, float *__restrict__ sck,
-    float *__restrict__ dbuf) {
+    float *__restrict__ dbuf, float *__restrict__ fin) {
     constexpr int NB = DK / 16, NCB = DV / 16, NG = NCB / NS, NP = SweepShape<NS>::NP;
     const int chain = blockIdx.x / NG, sg = blockIdx.x % NG;
     const int s = chain / H, h = chain % H;
@@ -538,6 +540,12 @@ __global__ __launch_bounds__(SweepShape<NS>::THREADS) void bwd_fwd_sweep_kernel(
         }
         __syncthreads();
     });
+    if (fin) {  // accumulator layout: rows 16 b + 4 gq + j, column col0 + m
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fin[(hd * DK + 16 * b + 4 * gq + j) * DV + col0 + m] = S[b][j];
+    }
 }
 
 template <int DK, int DV, int NS, typename T>
@@ -921,22 +929,24 @@ static int sweep_slices(int64_t chains, int nsl) {
 
 template <int DK, int DV, int NS, typename T>
 static hipError_t launch_sweeps(const BackwardArgs &a, const float *mats, float *sck, float *hck, float *dbuf,
-                                float *ebuf) {
+                                float *ebuf, float *fin_only) {
     const hipStream_t st = (hipStream_t)a.stream;
     const unsigned grid = (unsigned)((int64_t)a.nseq * a.H * (DV / 16 / NS));
     const dim3 block(SweepShape<NS>::THREADS);
     hipLaunchKernelGGL((bwd_fwd_sweep_kernel<DK, DV, NS, T>), dim3(grid), block, 0, st, (const T *)a.k,
-                       (const T *)a.v, (const T *)a.g, a.init, a.cu, a.H, mats, sck, dbuf);
+                       (const T *)a.v, (const T *)a.g, a.init, a.cu, a.H, mats, sck, dbuf, fin_only);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || fin_only) return e;
     hipLaunchKernelGGL((bwd_adjoint_sweep_kernel<DK, DV, NS, T>), dim3(grid), block, 0, st, (const T *)a.q,
                        (const T *)a.k, (const T *)a.g, (const T *)a.beta, a.dO, a.dfinal, a.cu, a.H, mats, hck, ebuf,
                        a.dv, a.dinit);
     return hipGetLastError();
 }
 
+// fin_only != NULL: only the chunk matrices and the forward sweep, which also writes the
+// final states there (the boundary pass of a slabbed backward).
 template <int DK, int DV, typename T>
-static hipError_t launch_bwd_t(const BackwardArgs &a) {
+static hipError_t launch_bwd_t(const BackwardArgs &a, float *fin_only = nullptr) {
     const int64_t slots = chunk_slots(a.N, a.nseq);
     const int64_t blk = slots * a.H * (int64_t)DK * DV;  // floats of one per-chunk state array
     float *sck = a.ws, *hck = sck + blk;
@@ -953,12 +963,12 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
     }
     constexpr int NSL = DV / 16;
     switch (sweep_slices((int64_t)a.nseq * a.H, NSL)) {
-    case 1: e = launch_sweeps<DK, DV, 1, T>(a, mats, sck, hck, dbuf, ebuf); break;
-    case 2: if constexpr (NSL >= 2) e = launch_sweeps<DK, DV, 2, T>(a, mats, sck, hck, dbuf, ebuf); break;
-    case 4: if constexpr (NSL >= 4) e = launch_sweeps<DK, DV, 4, T>(a, mats, sck, hck, dbuf, ebuf); break;
-    default: if constexpr (NSL >= 8) e = launch_sweeps<DK, DV, 8, T>(a, mats, sck, hck, dbuf, ebuf); break;
+    case 1: e = launch_sweeps<DK, DV, 1, T>(a, mats, sck, hck, dbuf, ebuf, fin_only); break;
+    case 2: if constexpr (NSL >= 2) e = launch_sweeps<DK, DV, 2, T>(a, mats, sck, hck, dbuf, ebuf, fin_only); break;
+    case 4: if constexpr (NSL >= 4) e = launch_sweeps<DK, DV, 4, T>(a, mats, sck, hck, dbuf, ebuf, fin_only); break;
+    default: if constexpr (NSL >= 8) e = launch_sweeps<DK, DV, 8, T>(a, mats, sck, hck, dbuf, ebuf, fin_only); break;
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || fin_only) return e;
     if (a.N > 0) {
         hipLaunchKernelGGL((bwd_grads_kernel<DK, DV, T>), dim3((unsigned)items), dim3(64 * GradShape<DK>::GW), 0, st,
                            (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.dO,
@@ -969,9 +979,9 @@ static hipError_t launch_bwd_t(const BackwardArgs &a) {
 }
 
 template <typename T>
-static hipError_t launch_bwd_dt(const BackwardArgs &a) {
+static hipError_t launch_bwd_dt(const BackwardArgs &a, float *fin_only) {
 #define KDA_BWD_CASE(DKV, DVV) \
-    if (a.dk_ == DKV && a.dv_ == DVV) return launch_bwd_t<DKV, DVV, T>(a);
+    if (a.dk_ == DKV && a.dv_ == DVV) return launch_bwd_t<DKV, DVV, T>(a, fin_only);
 #define KDA_BWD_ROW(DKV) KDA_BWD_CASE(DKV, 16) KDA_BWD_CASE(DKV, 32) KDA_BWD_CASE(DKV, 64) KDA_BWD_CASE(DKV, 128)
     KDA_BWD_ROW(16) KDA_BWD_ROW(32) KDA_BWD_ROW(64) KDA_BWD_ROW(128)
 #undef KDA_BWD_ROW
@@ -980,7 +990,27 @@ static hipError_t launch_bwd_dt(const BackwardArgs &a) {
 }
 
 hipError_t launch_backward(const BackwardArgs &a) {
-    return a.bf16 ? launch_bwd_dt<__bf16>(a) : launch_bwd_dt<float>(a);
+    return a.bf16 ? launch_bwd_dt<__bf16>(a, nullptr) : launch_bwd_dt<float>(a, nullptr);
+}
+
+hipError_t launch_backward_states(const BackwardArgs &a, float *fin) {
+    return a.bf16 ? launch_bwd_dt<__bf16>(a, fin) : launch_bwd_dt<float>(a, fin);
+}
+
+// Per-slab sequence lists of a slabbed backward over one sequence of N tokens: slab s covers
+// tokens [s L, min(N, (s+1) L)), and its list is {0, its length}.
+__global__ void bwd_slab_cu_kernel(int32_t *cu, int64_t N, int64_t L, int32_t nslab) {
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nslab) return;
+    const int64_t a = (int64_t)s * L, b = a + L < N ? a + L : N;
+    cu[2 * s] = 0;
+    cu[2 * s + 1] = (int32_t)(b - a);
+}
+
+hipError_t launch_backward_slab_cu(int32_t *cu, int64_t N, int64_t L, int32_t nslab, void *stream) {
+    hipLaunchKernelGGL(bwd_slab_cu_kernel, dim3((unsigned)((nslab + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, cu, N, L, nslab);
+    return hipGetLastError();
 }
 
 int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv) {

@@ -339,10 +339,10 @@ void decode_window_kernel(
     // Token inputs through buffer resources based at the token's row (uniform),
     // so every lane offset is a loop-invariant 32-bit register.  Head indices
     // stay below 2^31 (B * T * H < 2^31 is checked on the host).  Token t of a
-    // head is replayed token t (t < rp) or window token t - rp.
-    auto load_tok = [&](Tok &x, uint32_t hd, int t) {
+    // head is replayed token t (t < rp, the head's replay count) or window token
+    // t - rp.
+    auto load_tok = [&](Tok &x, uint32_t hd, int t, int rp) {
         const uint32_t bq = hd / (uint32_t)H;
-        const int rp = replay_of(hd);
         const bool rep = REPLAY && t < rp;
         const int64_t row = rep ? ((int64_t)bq * Tp + t) * H + (hd - bq * (uint32_t)H)
                                 : ((int64_t)bq * Tw + (t - rp)) * H + (hd - bq * (uint32_t)H);
@@ -401,6 +401,7 @@ void decode_window_kernel(
         const int rp = replay_of(head), n = rp + Tw;
         acc += rp;  // the state is written back after token acc (not at all when 0)
         const bool more = head + stride < heads;
+        const int rp_next = more ? replay_of(head + stride) : 0;
         const rsrc_t rs = state_rsrc(head);
         const float gscale = FX && fx.A_log ? __expf(fx.A_log[head - bq * H]) : 0.f;
         for (int t = 0; t < n; ++t) {
@@ -420,9 +421,9 @@ void decode_window_kernel(
             const float bb = cur.b;
             if (t == 0 && more) load_rows(nrows, head + stride);
             if (t + 1 < n) {
-                load_tok(nxt, head, t + 1);
+                load_tok(nxt, head, t + 1, rp);
             } else if (more) {
-                load_tok(nxt, head + stride, 0);
+                load_tok(nxt, head + stride, 0, rp_next);
             }
             __syncthreads();
 
@@ -477,7 +478,7 @@ void decode_window_kernel(
     if (head >= heads) return;
     f32x4 ra[NR], rb[NR];
     load_rows(ra, head);
-    load_tok(cur, head, 0);
+    load_tok(cur, head, 0, replay_of(head));
     nxt = cur;
     for (;;) {  // two heads per trip so the register sets swap roles without copies
         window(ra, rb, head);

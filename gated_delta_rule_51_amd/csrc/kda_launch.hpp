@@ -168,6 +168,11 @@ struct BackwardArgs {
 };
 
 hipError_t launch_backward(const BackwardArgs &a);
+// Only the chunk matrices and the forward sweep of the backward (fp32), which also writes the
+// state after each sequence to fin; the workspace is that of launch_backward.
+hipError_t launch_backward_states(const BackwardArgs &a, float *fin);
+// Per-slab {0, length} sequence lists (2 int32 per slab) of a slabbed backward.
+hipError_t launch_backward_slab_cu(int32_t *cu, int64_t N, int64_t L, int32_t nslab, void *stream);
 int64_t backward_workspace_floats(int64_t N, int32_t nseq, int32_t H, int32_t dk, int32_t dv);
 
 // Intra-device context parallelism (cp.hip): the small kernels around the prefill passes.

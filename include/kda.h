@@ -257,6 +257,30 @@ kda_status kda_prefill_backward(const void *q, const void *k, const void *v,
                                 float *d_init, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* kda_prefill_backward for one long sequence with bounded memory: the sequence
+ * is cut into slabs of slab_tokens tokens (a multiple of 16) and only one slab's
+ * workspace is held at a time.  A first pass carries the fp32 state through the
+ * slabs with the backward's own forward sweep and keeps the state at each slab
+ * boundary; the slabs are then differentiated in reverse, each from its boundary
+ * state, with the adjoint of the state it hands on -- the adjoint of the next
+ * slab's initial state -- as its d_final (the chain rule across the cut is exact,
+ * so the result is the unsliced backward's up to fp32 rounding).  The extra cost
+ * is one forward sweep over the sequence.  (FlashKDA serves training; the K3
+ * report digest's chunkwise-kernel paragraph.)
+ *   Arguments as kda_prefill_backward with nseq = 1 and no cu_seqlens;
+ *   slab_tokens >= 16, a multiple of 16;
+ *   workspace: kda_prefill_backward_slabbed_workspace_bytes(...) bytes, 16-byte
+ *   aligned: one slab's backward workspace plus one state per slab boundary
+ *   and two (dk x dv fp32 per head each). */
+size_t kda_prefill_backward_slabbed_workspace_bytes(int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                                                    kda_dtype dt, int64_t slab_tokens);
+kda_status kda_prefill_backward_slabbed(const void *q, const void *k, const void *v, const void *log_alpha,
+                                        const void *beta, const float *init_state, int64_t total_tokens, int32_t H,
+                                        int32_t dk, int32_t dv, kda_dtype dt, const float *d_o, const float *d_final,
+                                        float *d_q, float *d_k, float *d_v, float *d_log_alpha, float *d_beta,
+                                        float *d_init, int64_t slab_tokens, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
 /* One recurrent decode step for B x H heads: the state is read once and
  * written once, in place.  (Per-token update equation; serving section:
  * decode is bound by the in-place state update.) */

@@ -289,6 +289,37 @@ def test_backward_workspace_and_arguments(lib):
     assert call(a7=0) == 3              # nseq
 
 
+def test_backward_slabbed_workspace_and_arguments(lib):
+    # one slab's backward workspace, the slab lists, one state per inner boundary, two adjoints
+    up = lambda x: (x + 255) // 256 * 256
+    N, H, dk, dv, L = 1000, 3, 32, 64, 256
+    nslab = 4
+    state = H * dk * dv * 4
+    slab_ws = int(lib.kda_prefill_backward_workspace_bytes(L, 1, H, dk, dv, 1))
+    want = up(nslab * 8) + up((nslab - 1) * state) + up(2 * state) + up(slab_ws)
+    assert kda.kda_prefill_backward_slabbed_workspace_bytes(N, H, dk, dv, L) == want
+    assert kda.kda_prefill_backward_slabbed_workspace_bytes(N, H, dk, dv, 100) == 0   # not a multiple of 16
+    assert kda.kda_prefill_backward_slabbed_workspace_bytes(N, H, dk, dv, 0) == 0
+    # 262,144 tokens x 96 heads in slabs of 16,384: about 15 GB (the unsliced backward: 238 GB)
+    assert kda.kda_prefill_backward_slabbed_workspace_bytes(262144, 96, 128, 128, 16384) < 16 * 2**30
+    f = lib.kda_prefill_backward_slabbed
+    # q k v g b init N H dk dv dt dO dF dq dk dv dg db dinit L ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 1, 16, 16, kda.KDA_BF16, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+            None, 32, FAKE, 1 << 30, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a19=40) == 3          # slab not a multiple of 16
+    assert call(a11=None) == 1        # d_o missing
+    assert call(a13=FAKE + 2) == 2    # d_q misaligned
+    assert call(a21=16) == 5          # workspace too small
+    assert call(a20=None) == 5        # no workspace
+    assert call(a8=48) == 4           # dk
+
+
 def test_prefill_cp_workspace_and_arguments(lib):
     # per segment and head: S~ and S_in (dk x dv), M (dk x dk) and a flag; the chunk-local
     # operands of the segments; the segment list; each region 256-byte aligned

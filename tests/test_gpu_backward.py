@@ -141,3 +141,74 @@ def test_backward_is_deterministic(dev):
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(runs[0][n], runs[1][n]), f"{n} differs between two identical calls"
+
+
+def _slabbed(x, d_o, S0, dF, slab):
+    return kda.kda_prefill_backward_slabbed(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, S0, dF,
+                                           slab_tokens=slab)
+
+
+@pytest.mark.parametrize("T,slab,dtype,dk,dv", [(1000, 256, torch.bfloat16, 128, 128), (700, 96, torch.float32, 32, 64),
+                                                (50, 64, torch.bfloat16, 64, 32), (512, 256, torch.bfloat16, 128, 64)])
+def test_backward_slabbed_matches_oracle(dev, T, slab, dtype, dk, dv):
+    """One sequence cut into slabs (a ragged last slab, a single slab, slabs ending exactly at
+    the sequence's end), with an initial state and a final-state gradient: every gradient
+    against the oracle's reverse mode, and against the unsliced backward."""
+    x, d_o, S0, dF = _case(dev, [T], 3, dk, dv, dtype, seed=T + slab)
+    say(f"  case: slabbed backward T={T} slab={slab} H=3 dk={dk} dv={dv} {dtype}")
+    got = _slabbed(x, d_o, S0, dF, slab)
+    whole = kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, x["cu_seqlens"], S0, dF)
+    torch.cuda.synchronize()
+    cpu = {n: x[n].cpu() for n in ("q", "k", "v", "log_alpha", "beta")}
+    ref = oracle.backward(cpu["q"], cpu["k"], cpu["v"], cpu["log_alpha"], cpu["beta"], d_o.cpu(),
+                          cu_seqlens=x["cu_seqlens"].cpu(), init_state=S0.cpu(), dfinal=dF.cpu())
+    for n in NAMES:
+        assert_close(got[n], ref[n], TOLS[n], n)
+        assert_close(got[n], whole[n].double().cpu().numpy(), 2e-6, n + " (slabbed vs whole)")
+
+
+def test_backward_slabbed_k3_layer_against_whole(dev):
+    """The K3 layer's shape (65,536 tokens, 96 heads) in slabs of 16,384 tokens: a quarter of
+    the unsliced backward's workspace (15 GB instead of 60 GB); every gradient of every head
+    against the unsliced backward (the same fp32 arithmetic, cut at the slab boundaries)."""
+    w = workloads.workload(3)
+    x = workloads.prefill_inputs(w, device=dev, seed=0)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    d_o = torch.randn((w.total_tokens, w.H, w.dv), generator=gen, device=dev)
+    dF = torch.randn((1, w.H, w.dk, w.dv), generator=gen, device=dev)
+    nb_slab = kda.kda_prefill_backward_slabbed_workspace_bytes(w.total_tokens, w.H, 128, 128, 16384)
+    nb_whole = int(kda.load_library().kda_prefill_backward_workspace_bytes(w.total_tokens, 1, w.H, 128, 128, 1))
+    say(f"  case: slabbed backward K3 layer, workspace {nb_slab / 2**30:.1f} GiB vs {nb_whole / 2**30:.1f} GiB")
+    assert nb_slab < nb_whole / 3.5
+    got = _slabbed(x, d_o, None, dF, 16384)
+    torch.cuda.synchronize()
+    whole = kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], d_o, x["cu_seqlens"], None,
+                                     dF)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert_close(got[n], whole[n].double().cpu().numpy(), 5e-6, n + " (slabbed vs whole)")
+    del x, d_o, dF, got, whole
+    torch.cuda.empty_cache()
+
+
+def test_backward_slabbed_262k_tokens(dev):
+    """262,144 tokens x 96 heads (four times the K3 layer; the unsliced backward would need
+    238 GB of workspace): slabs of 16,384 tokens, the oracle's reverse mode on one head (fp32
+    chains of 16,384 chunk steps each way: the long-sequence bar)."""
+    N, H = 262144, 96
+    w = workloads.custom([N], H, 128, 128, torch.bfloat16, "neg_softplus")
+    x = workloads.prefill_inputs(w, device=dev, seed=2)
+    gen = torch.Generator(device=dev).manual_seed(13)
+    d_o = torch.randn((N, H, 128), generator=gen, device=dev)
+    say(f"  case: slabbed backward T={N} H={H}, workspace "
+        f"{kda.kda_prefill_backward_slabbed_workspace_bytes(N, H, 128, 128, 16384) / 2**30:.1f} GiB, oracle on head 40")
+    got = _slabbed(x, d_o, None, None, 16384)
+    torch.cuda.synchronize()
+    hs = [40]
+    cpu = {n: x[n][:, hs].cpu() for n in ("q", "k", "v", "log_alpha", "beta")}
+    ref = oracle.backward(cpu["q"], cpu["k"], cpu["v"], cpu["log_alpha"], cpu["beta"], d_o[:, hs].cpu(),
+                          cu_seqlens=x["cu_seqlens"].cpu())
+    for n in NAMES:
+        assert_close(got[n][:, hs], ref[n], TOLS_LONG[n], n)
+    del x, d_o, got
+    torch.cuda.empty_cache()
