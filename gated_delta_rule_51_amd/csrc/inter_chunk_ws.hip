@@ -93,7 +93,7 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ g, const float *__restrict__ init, const int32_t *__restrict__ cu,
     int32_t H, const float *__restrict__ ws, float *__restrict__ o, float *__restrict__ fin,
-    int32_t nsplit, int32_t nchains, LayerPrologue lp, const int32_t *__restrict__ skip) {
+    int32_t nsplit, int32_t nchains, LayerPrologue lp, const int32_t *__restrict__ skip, int32_t nsort) {
     static_assert(!LAYER || (DK == 128 && DV == 128), "the fused layer prologue is built for dk = dv = 128");
     constexpr int NB = DK / 16, NPAIR = NB / 2, BPW = NB / NP;
     constexpr uint32_t EB = 2;
@@ -105,8 +105,9 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
     const int xcd = L & 7;
     const int sx = L >> 3;
     const int split = sx % nsplit;
-    const int chain = (sx / nsplit) * 8 + xcd;
-    if (chain >= nchains) return;
+    const int slot = (sx / nsplit) * 8 + xcd;
+    if (slot >= nchains) return;
+    const int chain = lpt_chain(cu, nsort, H, slot);
     if (skip && skip[chain]) return;  // (context parallelism: a transition known to be negligible)
     const int s = chain / H, h = chain % H;
 
@@ -510,12 +511,13 @@ static hipError_t launch_ws_t(const InterChunkArgs &a) {
     const int nchains = a.nseq * a.H;
     const int nsplit = DV / (16 * NC);
     const int64_t grid = ((int64_t)nchains + 7) / 8 * 8 * nsplit;
+    const int nsort = a.nseq <= LPT_MAX_SEQS ? a.nseq : 0;
     if (a.layer) {
         if constexpr (DK == 128 && DV == 128) {
             hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP, true>), dim3((unsigned)grid),
                                dim3(64 * WsLayout<NC, NP>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
                                (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
-                               a.H, a.ws, a.o, a.fin, nsplit, nchains, *a.layer, a.skip);
+                               a.H, a.ws, a.o, a.fin, nsplit, nchains, *a.layer, a.skip, nsort);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
@@ -523,7 +525,7 @@ static hipError_t launch_ws_t(const InterChunkArgs &a) {
     hipLaunchKernelGGL((inter_chunk_ws_kernel<DK, DV, NC, NP, false>), dim3((unsigned)grid),
                        dim3(64 * WsLayout<NC, NP>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
                        (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, a.init, a.cu,
-                       a.H, a.ws, a.o, a.fin, nsplit, nchains, LayerPrologue{}, a.skip);
+                       a.H, a.ws, a.o, a.fin, nsplit, nchains, LayerPrologue{}, a.skip, nsort);
     return hipGetLastError();
 }
 

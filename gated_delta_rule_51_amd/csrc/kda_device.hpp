@@ -244,4 +244,35 @@ __device__ __forceinline__ bf16x4 split_lo(f32x4 x, const bf16x8 &nil, bf16x8 &h
     return to_bf16x4(mma32(nil, hh, x));
 }
 
+// Longest chains first.  A chain is one (sequence, head) recurrence, and its cost
+// grows with its sequence's length; workgroups go to compute units in blockIdx
+// order as units free up, so in index order a long sequence that comes late ends
+// the launch well after the average.  With the sequences ranked by length,
+// longest first (ties in index order), dispatch slot p runs head p % H of the
+// sequence of rank p / H: greedy list scheduling with the longest jobs first,
+// which ends within about one short chain of the average.  Every thread of the
+// workgroup calls it (two barriers); nsort is the number of sequences when it is
+// in [2, LPT_MAX_SEQS], else 0 and the slot is the chain.
+constexpr int LPT_MAX_SEQS = 128;
+__device__ __forceinline__ int lpt_chain(const int32_t *__restrict__ cu, int nsort, int H, int slot) {
+    if (nsort < 2 || nsort > LPT_MAX_SEQS) return slot;
+    __shared__ int32_t s_len[LPT_MAX_SEQS];
+    __shared__ int32_t s_pick;
+    const int nt = (int)blockDim.x;
+    for (int t = (int)threadIdx.x; t < nsort; t += nt) s_len[t] = cu[t + 1] - cu[t];
+    __syncthreads();
+    const int r = slot / H;
+    for (int t = (int)threadIdx.x; t < nsort; t += nt) {
+        const int lt = s_len[t];
+        int rank = 0;
+        for (int u = 0; u < nsort; ++u) {
+            const int lu = s_len[u];
+            rank += (lu > lt) | ((lu == lt) & (u < t));
+        }
+        if (rank == r) s_pick = t;
+    }
+    __syncthreads();
+    return s_pick * H + slot % H;
+}
+
 }  // namespace kda

@@ -84,7 +84,7 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                           const __bf16 *__restrict__ v, const __bf16 *__restrict__ g,
                           const __bf16 *__restrict__ beta, const float *__restrict__ init,
                           const int32_t *__restrict__ cu, int32_t H, float *__restrict__ o,
-                          float *__restrict__ fin, int32_t nsplit, int32_t nchains) {
+                          float *__restrict__ fin, int32_t nsplit, int32_t nchains, int32_t nsort) {
     constexpr int NP = 4;
     constexpr int NB = DK / 16, NPAIR = NB / 2, BPW = NB / NP;
     constexpr uint32_t EB = 2;
@@ -93,13 +93,15 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
     static_assert(DV % (16 * NC * SL) == 0, "column slices");
     using Layout = FusedLayout<NC, NP>;
 
-    // XCD-aware order: all column groups of one chain share an XCD (blockIdx mod 8).
+    // XCD-aware order: all column groups of one chain share an XCD (blockIdx mod 8);
+    // the chains in dispatch order go longest first.
     const int L = blockIdx.x;
     const int xcd = L & 7;
     const int sx = L >> 3;
     const int split = sx % nsplit;
-    const int chain = (sx / nsplit) * 8 + xcd;
-    if (chain >= nchains) return;
+    const int slot = (sx / nsplit) * 8 + xcd;
+    if (slot >= nchains) return;
+    const int chain = lpt_chain(cu, nsort, H, slot);
     const int s = chain / H, h = chain % H;
 
     const int tid = threadIdx.x;
@@ -503,7 +505,7 @@ static hipError_t launch_fused_t(const PrefillFusedArgs &a) {
     hipLaunchKernelGGL((prefill_fused_kernel<DK, DV, NC, SL>), dim3((unsigned)grid),
                        dim3(64 * FusedLayout<NC, 4>::NW), 0, (hipStream_t)a.stream, (const __bf16 *)a.q,
                        (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g, (const __bf16 *)a.beta,
-                       a.init, a.cu, a.H, a.o, a.fin, nsplit, nchains);
+                       a.init, a.cu, a.H, a.o, a.fin, nsplit, nchains, a.nseq <= LPT_MAX_SEQS ? a.nseq : 0);
     return hipGetLastError();
 }
 
