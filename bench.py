@@ -517,9 +517,19 @@ def bench_decode_window(torch, kda, workloads, dev, steps, T: int):
     gbs = per_win / (ms * 1e-3) / 1e9
     accepted = float(torch.stack(accs).double().mean()) * B
     res = {"workload": f"{w.name}_window", "T": T, "heads": B * H, "windows": nwin,
+           "form": "one chunk (matrix cores)" if T >= 6 else "token by token",
            "ms_per_window": round(ms, 5), "bytes_per_window": per_win, "gbs": gbs,
            "hbm_peak_frac": gbs / HBM_PEAK_GBS, "draft_tokens_per_s": B * T / (ms * 1e-3),
            "accepted_tokens_per_s": accepted / (ms * 1e-3)}
+    if T >= 6:  # the token-by-token form on the same windows, for comparison
+        state2 = workloads.decode_initial_state(B, H, dk, dv, device=dev)
+        t1 = Timer(torch, nwin)
+        for x, a in zip(wins, accs):
+            with t1:
+                kda.kda_decode_window(*(x[n] for n in names), state2, a, o=o, form=1)
+        torch.cuda.synchronize()
+        res["ms_per_window_token_form"] = round(t1.mean_ms(), 5)
+        del state2
     del state, wins, o
     torch.cuda.empty_cache()
     return res

@@ -30,7 +30,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_ALIGN", 3: "KDA_ERR_SHAPE"
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_TOO_LARGE"}
 EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_prefill", "kda_prefill_single_pass",
            "kda_inter_chunk_shaped", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
-           "kda_decode_step", "kda_decode_window", "kda_decode_step_fused", "kda_decode_window_fused",
+           "kda_decode_step", "kda_decode_window", "kda_decode_window_form", "kda_decode_step_fused",
+           "kda_decode_window_fused",
            "kda_decode_window_replay",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_backward_slabbed_workspace_bytes", "kda_prefill_backward_slabbed",
@@ -83,6 +84,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_window.restype = ctypes.c_int
     lib.kda_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                       vp]
+    lib.kda_decode_window_form.restype = ctypes.c_int
+    lib.kda_decode_window_form.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                           i32, vp]
     i64, f32 = ctypes.c_int64, ctypes.c_float
     lib.kda_decode_step_fused.restype = ctypes.c_int
     lib.kda_decode_step_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32,
@@ -451,13 +455,14 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None, stream=None) -> 
 
 
 def kda_decode_window(q, k, v, log_alpha, beta, state, accept=None, *, o=None, output_o: bool = True,
-                      stream=None) -> Optional[torch.Tensor]:
+                      form=None, stream=None) -> Optional[torch.Tensor]:
     """A window of T tokens per sequence (speculative verification); ``state`` is updated in place.
 
     q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H].  ``accept``: int32 [B] on
     the device (None = all T accepted); the state ends after the first clamp(accept[b], 0, T)
     tokens of sequence b.  Returns o fp32 [B, T, H, dv] (the output of every token of the
-    window), or None with ``output_o=False``.
+    window), or None with ``output_o=False``.  ``form`` (kda_decode_window_form): None or 0 =
+    automatic, 1 = token by token, 2 = one chunk on the matrix cores.
     """
     _check_tensors(q, k, v, log_alpha, beta)
     if q.dim() != 4:
@@ -477,9 +482,12 @@ def kda_decode_window(q, k, v, log_alpha, beta, state, accept=None, *, o=None, o
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     if output_o:
         _check_dev("o", o, q.device, torch.float32, (B, T, H, dv))
-    _check(load_library().kda_decode_window(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o if output_o else None),
-        _ptr(accept), B, T, H, dk, dv, _dtype_code(q.dtype), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o if output_o else None),
+            _ptr(accept), B, T, H, dk, dv, _dtype_code(q.dtype))
+    if form is None:
+        _check(load_library().kda_decode_window(*args, _stream(stream)))
+    else:
+        _check(load_library().kda_decode_window_form(*args, int(form), _stream(stream)))
     return o if output_o else None
 
 

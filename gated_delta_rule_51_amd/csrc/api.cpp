@@ -559,6 +559,25 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v, const 
                                    nullptr, B, T, H, dk, dv, dt, stream);
 }
 
+kda_status kda_decode_window_form(const void *q, const void *k, const void *v, const void *log_alpha,
+                                  const void *beta, float *state, float *o, const int32_t *accept,
+                                  int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                  int32_t form, void *stream) {
+    if (form < 0 || form > 2) return KDA_ERR_SHAPE;
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || (int64_t)B * T * H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({q, k, v, log_alpha}, true, beta, dt == KDA_BF16, true);
+    if (st != KDA_OK) return st;
+    st = check_ptrs({state}, {o});
+    if (st != KDA_OK) return st;
+    if (accept && (reinterpret_cast<uintptr_t>(accept) & 3u)) return KDA_ERR_ALIGN;
+    kda::DecodeWindowArgs a{q, k, v, log_alpha, beta, state, o, accept, B, T, H, dk, dv, dt == KDA_BF16, stream, {}};
+    a.form = form;
+    if (form == 2 && !kda::window_chunk_supported(a)) return KDA_ERR_UNSUPPORTED;
+    return hip_status(kda::launch_decode_window(a));
+}
+
 
 size_t kda_prefill_backward_workspace_bytes(int64_t total_tokens, int32_t nseq, int32_t H, int32_t dk,
                                             int32_t dv, kda_dtype dt) {

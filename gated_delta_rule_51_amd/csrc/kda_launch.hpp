@@ -61,7 +61,17 @@ struct DecodeWindowArgs {
     const int32_t *replay = nullptr;
     int32_t Tp = 0;
     int32_t acc_default = -1;  // tokens of this window committed without accept (-1: all T)
+    // Evaluation form: 0 automatic, 1 token by token (vector ALUs), 2 the window as one
+    // chunk on the matrix cores (decode_chunk.hip).
+    int32_t form = 0;
 };
+
+// Shapes the one-chunk window form serves: bf16, dk = dv = 128, no fused gate, and the
+// window's tokens (with a replay in front) within one 16-token chunk.
+inline bool window_chunk_supported(const DecodeWindowArgs &a) {
+    const int64_t tokens = (int64_t)a.T + (a.replay ? a.Tp : 0);
+    return a.bf16 && a.dk == 128 && a.dv == 128 && !a.fx.A_log && a.T >= 1 && tokens <= 16;
+}
 
 // The fused layer prefill's prologue on load (layer_prologue.hpp): what the two
 // prefill kernels need besides their usual inputs.
@@ -203,6 +213,7 @@ hipError_t launch_short_conv(const ShortConvArgs &a);
 hipError_t launch_out_norm_gate(const OutNormGateArgs &a);
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_decode_window(const DecodeWindowArgs &a);
+hipError_t launch_window_chunk(const DecodeWindowArgs &a);
 hipError_t launch_chunk_local(const ChunkLocalArgs &a);
 hipError_t launch_inter_chunk(const InterChunkArgs &a);
 // Warp-specialised inter-chunk kernel (bf16, dk >= 32): ncw consumer and npw

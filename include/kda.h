@@ -315,13 +315,32 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  *
  * State traffic is that of one decode step per window, so a T-token window
  * costs far less than T single steps while T stays small; long windows
- * (hundreds of tokens) belong to kda_prefill instead.  Errors as for
+ * (hundreds of tokens) belong to kda_prefill instead.
+ *
+ * Evaluation: token by token on the vector ALUs (the arithmetic of
+ * kda_decode_step), except for bf16 inputs with dk = dv = 128 and 6 <= T <= 16,
+ * where the window is one 16-token chunk of the prefill's chunked form on the
+ * matrix cores (same report section as kda_prefill; split-bf16 products, fp32
+ * accumulation), whose arithmetic per state element does not grow with T.  The
+ * two forms agree to the prefill's precision, not bit for bit; in either form
+ * the committed state depends only on the accepted prefix.  Errors as for
  * kda_decode_step. */
 kda_status kda_decode_window(const void *q, const void *k, const void *v,
                              const void *log_alpha, const void *beta,
                              float *state, float *o, const int32_t *accept,
                              int32_t B, int32_t T, int32_t H, int32_t dk,
                              int32_t dv, kda_dtype dt, void *stream);
+
+/* kda_decode_window with the evaluation form named by the caller (for tests
+ * and tuning): form 0 = the automatic choice above, 1 = token by token (every
+ * shape), 2 = one chunk on the matrix cores (KDA_BF16, dk = dv = 128,
+ * T <= 16; KDA_ERR_UNSUPPORTED otherwise).  Other values: KDA_ERR_SHAPE.
+ * Arguments and errors otherwise as for kda_decode_window. */
+kda_status kda_decode_window_form(const void *q, const void *k, const void *v,
+                                  const void *log_alpha, const void *beta,
+                                  float *state, float *o, const int32_t *accept,
+                                  int32_t B, int32_t T, int32_t H, int32_t dk,
+                                  int32_t dv, kda_dtype dt, int32_t form, void *stream);
 
 /* Speculative decoding as a serving loop runs it (Kimi K3 report digest,
  * serving section: the state cannot be rolled back, so the accepted drafts are
@@ -337,7 +356,9 @@ kda_status kda_decode_window(const void *q, const void *k, const void *v,
  * replay may be NULL).  gate_A_log, out_gate, norm_w, norm_eps, y as in
  * kda_decode_window_fused (the gate applies to replayed and new tokens, the
  * epilogue to the new tokens' outputs).  replay: device int32 [B], 4-byte
- * aligned.  B * T * H and B * Tp * H < 2^31.  Errors as for kda_decode_window. */
+ * aligned.  B * T * H and B * Tp * H < 2^31.  The form is chosen as for
+ * kda_decode_window, on T + Tp tokens (one chunk holds the replay and the
+ * window when T + Tp <= 16).  Errors as for kda_decode_window. */
 kda_status kda_decode_window_replay(const void *pq, const void *pk, const void *pv, const void *pgate,
                                     const void *pbeta, const int32_t *replay, int32_t Tp, const void *q,
                                     const void *k, const void *v, const void *gate, const float *gate_A_log,

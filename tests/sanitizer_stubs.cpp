@@ -16,6 +16,7 @@ hipError_t launch_inter_chunk(const InterChunkArgs &) { return hipSuccess; }
 hipError_t launch_inter_chunk_ws(const InterChunkArgs &, int, int) { return hipSuccess; }
 hipError_t launch_decode(const DecodeArgs &) { return hipSuccess; }
 hipError_t launch_decode_window(const DecodeWindowArgs &) { return hipSuccess; }
+hipError_t launch_window_chunk(const DecodeWindowArgs &) { return hipSuccess; }
 hipError_t launch_backward(const BackwardArgs &) { return hipSuccess; }
 hipError_t launch_backward_states(const BackwardArgs &, float *) { return hipSuccess; }
 hipError_t launch_backward_slab_cu(int32_t *, int64_t, int64_t, int32_t, void *) { return hipSuccess; }

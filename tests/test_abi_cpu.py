@@ -134,6 +134,19 @@ def test_decode_window_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 16, 16, 3, None) == 4
 
 
+def test_decode_window_form_rejects_bad_arguments(lib):
+    f = lib.kda_decode_window_form
+    # q k v g beta state o accept B T H dk dv dt form stream
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 128, 128, 1, 3, None) == 3   # no such form
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 128, 128, 1, -1, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 128, 128, 0, 2, None) == 4   # chunk: bf16 only
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 64, 128, 1, 2, None) == 4    # dk = dv = 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 17, 1, 128, 128, 1, 2, None) == 4  # one chunk
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 1, 8, 1, 128, 128, 1, 2, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 1, 128, 128, 1, 2, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 0, 1, 128, 128, 1, 1, None) == 3
+
+
 def test_python_binding_refuses_cpu_tensors(lib):
     import torch
 

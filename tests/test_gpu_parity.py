@@ -230,13 +230,13 @@ def test_decode_window_long_strong_decay(dev, dtype):
 
 
 def test_decode_window_equals_decode_steps(dev):
-    """A fully accepted window and the same tokens through kda_decode_step one by one; a
-    window of one token and a single step."""
+    """A fully accepted window in the token-by-token form and the same tokens through
+    kda_decode_step one by one; a window of one token and a single step."""
     w = workloads.custom([1] * 4, 3, 128, 128, torch.bfloat16)
     x = workloads.decode_window_inputs(w, 6, 0, device=dev, seed=11)
     init = workloads.random_state(4, 3, 128, 128, device=dev, seed=11)
     sw, ss = init.clone(), init.clone()
-    ow = kda.kda_decode_window(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], sw)
+    ow = kda.kda_decode_window(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], sw, form=1)
     os_ = torch.stack([kda.kda_decode_step(*(x[n][:, t].contiguous()
                                              for n in ("q", "k", "v", "log_alpha", "beta")), ss)
                        for t in range(6)], dim=1)

@@ -1,8 +1,9 @@
 """GPU parity of speculative decoding as a serving loop runs it (kda_decode_window_replay): each
 call replays the previous window's accepted prefix (counts known only after that window ran),
 commits the state after it, and runs the new window without committing it.  Against the fp64
-oracle's decode steps window by window, and bit for bit against the same schedule through
-kda_decode_window with the accepted counts given at launch.  Outputs start as NaN."""
+oracle's decode steps window by window, and against the same schedule through kda_decode_window
+with the accepted counts given at launch (the committed states bit for bit).  Outputs start as
+NaN.  From 6 tokens per call (T + Tp) the replay runs as one chunk on the matrix cores."""
 import numpy as np
 import pytest
 import torch
@@ -96,19 +97,26 @@ def test_replay_serving_loop_matches_oracle(dev, dtype, dk, dv):
     assert torch.equal(state[5], init[5]), "a sequence that accepted nothing changed its state"
 
 
-def test_replay_equals_windows_with_known_acceptance(dev):
+@pytest.mark.parametrize("T,form", [(2, 1), (5, 2)])
+def test_replay_equals_windows_with_known_acceptance(dev, T, form):
     """The same schedule through kda_decode_window, which needs the accepted counts at launch:
-    window i with accept = acc_i commits what the replay call of window i + 1 commits, and
-    window i + 1 from that state (accept = 0) gives the replay call's outputs, bit for bit."""
-    B, T, H, W = 8, 5, 4, 4
+    window i with accept = acc_i commits what the replay call of window i + 1 commits, bit for
+    bit, and window i + 1 from that state (accept = 0) gives the replay call's outputs.  With
+    T + Tp = 4 tokens per call both run token by token and the outputs agree bit for bit; with
+    10 the replay runs as one chunk (the window through form 2 as well), whose outputs come
+    from a chunk that starts before the replayed tokens, so they agree to the bar."""
+    B, H, W = 8, 4, 4
     xs, accepts, init, outs, state = _serving_loop(dev, B, T, H, 128, 128, torch.bfloat16, W, seed=7)
     ref = init.clone()
     zero = torch.zeros(B, dtype=torch.int32, device=dev)
     for i, x in enumerate(xs):
-        o_ref = kda.kda_decode_window(*(x[n] for n in NAMES), ref.clone(), zero)
+        o_ref = kda.kda_decode_window(*(x[n] for n in NAMES), ref.clone(), zero, form=form)
         torch.cuda.synchronize()
-        assert torch.equal(outs[i], o_ref), f"window {i}: outputs differ from kda_decode_window"
-        kda.kda_decode_window(*(x[n] for n in NAMES), ref, accepts[i], output_o=False)
+        if form == 1:
+            assert torch.equal(outs[i], o_ref), f"window {i}: outputs differ from kda_decode_window"
+        else:
+            assert_close(outs[i], _np(o_ref), TOL[torch.bfloat16], f"window {i} o against the window form")
+        kda.kda_decode_window(*(x[n] for n in NAMES), ref, accepts[i], output_o=False, form=form)
     torch.cuda.synchronize()
     assert torch.equal(state, ref), "committed state differs from kda_decode_window with known counts"
 
