@@ -26,14 +26,15 @@
 // exact zeros: the committed state is the same, bit for bit, as this kernel gives
 // for the accepted prefix alone, whatever drafts follow it.
 //
-// A workgroup of four waves serves one (sequence, head) at a time and loops over
-// heads (a persistent grid of two workgroups per compute unit, so that one
-// workgroup's loads overlap the others' arithmetic).  Wave w builds the operands
-// of key-channel block pair w, as the single-pass prefill's producers do; wave 0
-// then inverts I + A while every wave forms K+ S and Q+ S for its 32 state columns
-// (two 16-column slices), and after a barrier every wave finishes Delta, O and the
-// committed state of its columns.  The next head's inputs are loaded during the
-// current head's build, its state after the current state is written.
+// A workgroup of eight waves serves one (sequence, head) at a time and loops over
+// heads (a persistent grid, one workgroup per compute unit).  Waves 0..3 build the
+// operands of key-channel block pairs 0..3, as the single-pass prefill's producers
+// do; wave 4 then inverts I + A while every wave forms K+ S and Q+ S for its 16
+// state columns, and after a barrier every wave finishes Delta, O and the committed
+// state of its columns.  The head's state is the bound: its rows are loaded one head
+// ahead (a state load is in flight through the whole of the previous head, 64 KB
+// per compute unit at all times) and pass through an LDS copy in both directions
+// (below); the next head's inputs are loaded during the current head's build.
 //
 // Layout conventions and the key-channel relabelling inside block pairs are those
 // of the prefill kernels: internal channel 16 (2P + h) + 4 g4 + j is memory channel
@@ -48,11 +49,13 @@ namespace {
 constexpr int WC_D = 128;               // dk = dv
 constexpr int WC_NB = WC_D / 16;        // 16-channel blocks
 constexpr int WC_NPAIR = WC_NB / 2;     // block pairs = waves
-constexpr int WC_SL = 2;                // 16-column state slices per wave
-constexpr int WC_WAVES = 4;
-constexpr int WC_BLOCKS_PER_CU = 2;
+constexpr int WC_SL = 1;                // 16-column state slices per wave
+constexpr int WC_WAVES = 8;
+constexpr int WC_BUILDERS = 4;          // waves that build the operands, one block pair each
+constexpr int WC_SOLVER = 4;            // the wave that inverts I + A (shares a SIMD with builder 0)
+constexpr int WC_LP = WC_D + 4;         // padded row of the state's LDS copy (16-byte aligned rows)
 
-static_assert(WC_NPAIR == WC_WAVES && WC_WAVES * WC_SL * 16 == WC_D, "one block pair and 32 columns per wave");
+static_assert(WC_NPAIR == WC_BUILDERS && WC_WAVES * WC_SL * 16 == WC_D, "one block pair per builder, 16 columns per wave");
 
 // The state-independent operands of a head's chunk (A-operand fragments; block
 // pairs packed as in the prefill kernels).
@@ -86,12 +89,13 @@ struct WcHead {
     int rp;   // replayed tokens in front of the window's (rows 0 .. rp - 1)
     int n;    // tokens of the chunk: rp + Tw
     int acc;  // tokens whose state is committed (0: none)
+    uint32_t on;  // 1; 0 makes every load of the head read zeros without touching memory
 };
 
 }  // namespace
 
 template <bool REPLAY>
-__global__ __launch_bounds__(64 * WC_WAVES) __attribute__((amdgpu_waves_per_eu(WC_BLOCKS_PER_CU, WC_BLOCKS_PER_CU)))
+__global__ __launch_bounds__(64 * WC_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
                          const __bf16 *__restrict__ g, const __bf16 *__restrict__ beta, float *__restrict__ state,
                          float *__restrict__ o, const int32_t *__restrict__ accept, uint32_t heads, uint32_t H,
@@ -108,7 +112,8 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
     const uint32_t rowB = H * EB;         // ... in beta
 
     __shared__ __attribute__((aligned(16))) WcOps ops;
-    __shared__ __attribute__((aligned(16))) WcStage stage[WC_WAVES];
+    __shared__ __attribute__((aligned(16))) WcStage stage[WC_BUILDERS];
+    __shared__ __attribute__((aligned(16))) float lst[WC_D * WC_LP];  // the head's state
 
     auto head_of = [&](uint32_t hd) {
         WcHead x;
@@ -127,15 +132,16 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
         x.rp = __builtin_amdgcn_readfirstlane(rp);
         x.n = x.rp + Tw;
         x.acc = __builtin_amdgcn_readfirstlane(a) + x.rp;
+        x.on = 1;
         return x;
     };
     // Token rows of the chunk: row r < rp is token r of the previous window, row r >= rp
     // token r - rp of this one; rows past n and every unused source read as zeros.
-    auto cur_rsrc = [&](const __bf16 *base, const WcHead &x, uint32_t row, uint32_t d) {
-        return make_rsrc(base + ((int64_t)x.b * Tw * H + x.h) * d, (uint32_t)Tw * row);
+    auto cur_rsrc = [&](const __bf16 *base, const WcHead &x, uint32_t row, uint32_t d, uint32_t on = 1) {
+        return make_rsrc(base + ((int64_t)x.b * Tw * H + x.h) * d, (uint32_t)Tw * row * (x.on & on));
     };
-    auto prev_rsrc = [&](const __bf16 *base, const WcHead &x, uint32_t row, uint32_t d) {
-        return make_rsrc(base + ((int64_t)x.b * Tp * H + x.h) * d, (uint32_t)x.rp * row);
+    auto prev_rsrc = [&](const __bf16 *base, const WcHead &x, uint32_t row, uint32_t d, uint32_t on = 1) {
+        return make_rsrc(base + ((int64_t)x.b * Tp * H + x.h) * d, (uint32_t)x.rp * row * (x.on & on));
     };
     auto cur_off = [&](const WcHead &x, int r, uint32_t row, uint32_t inrow) {
         return r >= x.rp ? (uint32_t)(r - x.rp) * row + inrow : OOB;
@@ -151,26 +157,32 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
     const bf16x8 IDL = cat(ID, z4), IDH = cat(z4, ID), LTL = cat(LT, z4), LTH = cat(z4, LT);
     const bf16x8 NIL = neg_identity_operand<0>(g4, l16), NIH = neg_identity_operand<1>(g4, l16);
 
+    // (with a replay the rows of both windows load into registers of their own and are
+    // combined where they are used: a combination right after the loads would make the
+    // compiler wait there for every load in flight)
     struct PIn {
-        u32x4 d[3];
-        uint32_t b;
+        u32x4 d[3], pd[3];
+        uint32_t b, pb;
     };
     // q, k, g rows of block pair w (four consecutive lanes per token row) and beta of token l16
+    // (every wave issues these loads, so the wait counts are the same on every path; only
+    // the builders' read memory)
+    const uint32_t builder = w < WC_BUILDERS ? 1u : 0u;
     auto pload = [&](PIn &R, const WcHead &x) {
         const int r = lane >> 2;
-        const uint32_t inrow = 64u * w + 16u * (lane & 3);
+        const uint32_t inrow = 64u * (w & 3) + 16u * (lane & 3);
         const uint32_t oc = cur_off(x, r, rowK, inrow);
         const uint32_t ob = cur_off(x, l16, rowB, 0);
-        R.d[0] = buf_load_u32x4(cur_rsrc(q, x, rowK, WC_D), oc);
-        R.d[1] = buf_load_u32x4(cur_rsrc(k, x, rowK, WC_D), oc);
-        R.d[2] = buf_load_u32x4(cur_rsrc(g, x, rowK, WC_D), oc);
-        R.b = buf_load_u16(cur_rsrc(beta, x, rowB, 1), ob);
+        R.d[0] = buf_load_u32x4(cur_rsrc(q, x, rowK, WC_D, builder), oc);
+        R.d[1] = buf_load_u32x4(cur_rsrc(k, x, rowK, WC_D, builder), oc);
+        R.d[2] = buf_load_u32x4(cur_rsrc(g, x, rowK, WC_D, builder), oc);
+        R.b = buf_load_u16(cur_rsrc(beta, x, rowB, 1, builder), ob);
         if constexpr (REPLAY) {
             const uint32_t op = (uint32_t)r * rowK + inrow;
-            R.d[0] |= buf_load_u32x4(prev_rsrc(pq, x, rowK, WC_D), op);
-            R.d[1] |= buf_load_u32x4(prev_rsrc(pk, x, rowK, WC_D), op);
-            R.d[2] |= buf_load_u32x4(prev_rsrc(pg, x, rowK, WC_D), op);
-            R.b |= buf_load_u16(prev_rsrc(pb, x, rowB, 1), (uint32_t)l16 * rowB);
+            R.pd[0] = buf_load_u32x4(prev_rsrc(pq, x, rowK, WC_D, builder), op);
+            R.pd[1] = buf_load_u32x4(prev_rsrc(pk, x, rowK, WC_D, builder), op);
+            R.pd[2] = buf_load_u32x4(prev_rsrc(pg, x, rowK, WC_D, builder), op);
+            R.pb = buf_load_u16(prev_rsrc(pb, x, rowB, 1, builder), (uint32_t)l16 * rowB);
         }
     };
     struct AIn {
@@ -179,12 +191,12 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
     };
     auto stage_put = [&](const PIn &R) {
 #pragma unroll
-        for (int t = 0; t < 3; ++t) stage[w].rows[t][lane >> 2][lane & 3] = R.d[t];
+        for (int t = 0; t < 3; ++t) stage[w].rows[t][lane >> 2][lane & 3] = REPLAY ? (R.d[t] | R.pd[t]) : R.d[t];
     };
     auto stage_get = [&](AIn &A, const PIn &R) {
 #pragma unroll
         for (int t = 0; t < 3; ++t) A.d[t] = stage[w].rows[t][l16][g4];
-        A.b = bf16_bits_to_f32((uint16_t)R.b);
+        A.b = bf16_bits_to_f32((uint16_t)(REPLAY ? (R.b | R.pb) : R.b));
     };
     auto half = [](const u32x4 &x, int hh) { return hh ? u32x2{x[2], x[3]} : u32x2{x[0], x[1]}; };
 
@@ -281,7 +293,7 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
     auto solve = [&]() {
         f32x4 Am = stage[0].part[0][lane], Bm = stage[0].part[1][lane], Qm = stage[0].part[2][lane];
 #pragma unroll
-        for (int u = 1; u < WC_WAVES; ++u) {
+        for (int u = 1; u < WC_BUILDERS; ++u) {
             Am += stage[u].part[0][lane];
             Bm += stage[u].part[1][lane];
             Qm += stage[u].part[2][lane];
@@ -314,140 +326,153 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
     };
 
     // ---------------------------------------------------------------- state columns (every wave)
-    // State slices: internal rows 16 b + 4 g4 + jj, column col0 + l16; internal row
+    // The state moves between HBM and the waves through an LDS copy of the head's 128 x 128
+    // matrix (rows padded to WC_LP floats): HBM sees whole 512-byte rows in 16-byte pieces
+    // (wave w, lane l: rows 16 w + 2 i + l / 32, columns 4 (l % 32) .. +3, i = 0..7), eight
+    // loads and eight stores per wave and head -- few enough that the compiler's wait
+    // counters track the next head's loads across the current head instead of draining
+    // them -- and each wave reads its 16 columns in the accumulator layout from LDS.
+    // Wave w's slice: internal rows 16 b + 4 g4 + jj, column 16 w + l16; internal row
     // 16 b + 4 g4 + jj is memory key channel mrow(b, jj).
-    int col0[WC_SL];
-#pragma unroll
-    for (int sl = 0; sl < WC_SL; ++sl) col0[sl] = (w * WC_SL + sl) * 16;
+    const int col0 = 16 * w;
+    auto mrow = [&](int b, int jj) { return 32 * (b >> 1) + 8 * g4 + 4 * (b & 1) + jj; };
     auto state_rsrc = [&](const WcHead &x) {
-        return make_rsrc(state + ((int64_t)x.b * H + x.h) * (WC_D * WC_D), WC_D * WC_D * 4u);
+        return make_rsrc(state + ((int64_t)x.b * H + x.h) * (WC_D * WC_D), WC_D * WC_D * 4u * x.on);
     };
-    // Byte offset of state element (mrow(b, jj), col0[sl] + l16): a per-lane part (one
-    // register for all 64 elements) plus a constant that goes into the scalar offset.
-    const uint32_t s_voff = ((8 * g4) * WC_D + col0[0] + l16) * 4u;
-    auto s_soff = [](int sl, int b, int jj) {
-        return (uint32_t)(((32 * (b >> 1) + 4 * (b & 1) + jj) * WC_D + 16 * sl) * 4);
-    };
-    auto load_state = [&](f32x4 (&S)[WC_SL][WC_NB], const WcHead &x) {
+    const int row0 = 16 * w + (lane >> 5), c4 = 4 * (lane & 31);
+    const uint32_t row_voff = (uint32_t)(row0 * WC_D + c4) * 4u;
+    typedef u32x4 Rows[8];
+    auto load_rows = [&](Rows &P, const WcHead &x) {
         const rsrc_t rs = state_rsrc(x);
 #pragma unroll
-        for (int sl = 0; sl < WC_SL; ++sl)
-#pragma unroll
-            for (int b = 0; b < WC_NB; ++b)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    S[sl][b][jj] = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, s_soff(sl, b, jj), 0));
+        for (int i = 0; i < 8; ++i) P[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, row_voff, i * 2u * WC_D * 4u, 0);
     };
-    // v of token l16, columns col0 + 4 g4 .. +3 of each slice
-    struct CIn {
-        u32x2 v[WC_SL];
-    };
-    auto cload = [&](CIn &X, const WcHead &x) {
-        const rsrc_t rv = cur_rsrc(v, x, rowK, WC_D);
+    auto rows_to_lds = [&](const Rows &P) {
 #pragma unroll
-        for (int sl = 0; sl < WC_SL; ++sl) {
-            const uint32_t in = (col0[sl] + 4 * g4) * EB;
-            X.v[sl] = buf_load_u32x2(rv, cur_off(x, l16, rowK, in));
-            if constexpr (REPLAY) X.v[sl] |= buf_load_u32x2(prev_rsrc(pv, x, rowK, WC_D), (uint32_t)l16 * rowK + in);
-        }
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(&lst[(row0 + 2 * i) * WC_LP + c4]) = P[i];
+    };
+    // v of token l16, columns col0 + 4 g4 .. +3
+    struct VIn {
+        u32x2 c, p;  // this window's and (with a replay) the previous window's rows
+    };
+    auto cload = [&](VIn &X, const WcHead &x) {
+        const uint32_t in = (col0 + 4 * g4) * EB;
+        X.c = buf_load_u32x2(cur_rsrc(v, x, rowK, WC_D), cur_off(x, l16, rowK, in));
+        if constexpr (REPLAY) X.p = buf_load_u32x2(prev_rsrc(pv, x, rowK, WC_D), (uint32_t)l16 * rowK + in);
     };
 
-    uint32_t hd = blockIdx.x;
-    if (hd >= heads) return;
-    WcHead cur = head_of(hd);
+    // One head: its state rows in P (loaded one head earlier) and its v in X; the next
+    // head's rows go into P once these are in LDS, its v into Xn, its q/k/g into R.
     PIn R;
-    CIn X;
-    f32x4 S[WC_SL][WC_NB];
-    pload(R, cur);
-    cload(X, cur);
-    load_state(S, cur);
-    for (;;) {
+    Rows P;
+    // (The next head's loads are issued in the order q/k/g, state rows, v, each into the
+    // registers its own data came in, so no load result is copied and the waits for one
+    // never include the ones issued after it.)
+    auto process = [&](const VIn &X, VIn &Xn, const WcHead &cur, bool more, const WcHead &nxt) {
+        rows_to_lds(P);
         AIn A;
-        stage_put(R);
-        stage_get(A, R);  // (the wave's own LDS accesses stay in order)
-        const uint32_t nh = hd + gridDim.x;
-        const bool more = nh < heads;
-        WcHead nxt = cur;
-        if (more) {
-            nxt = head_of(nh);
-            pload(R, nxt);
+        if (w < WC_BUILDERS) {
+            stage_put(R);
+            stage_get(A, R);  // (the wave's own LDS accesses stay in order)
         }
-        build(A, cur);
-        __syncthreads();  // operands and partials of this head
-        if (w == 0) solve();
-        // X = K+ S and Q+ S per slice, each as hi*hi, lo*hi, hi*lo
-        f32x4 Xa[WC_SL], Xb[WC_SL], Oa[WC_SL], Ob[WC_SL], Oc[WC_SL];
+        __builtin_amdgcn_sched_barrier(0);  // R read before it is reloaded
+        WcHead ld = nxt;  // past the last head: loads that read zeros
+        ld.on = more ? 1u : 0u;
+        pload(R, ld);
+        load_rows(P, ld);
+        cload(Xn, ld);
+        if (w < WC_BUILDERS) build(A, cur);
+        __syncthreads();  // operands, partials and the state copy of this head
+        if (w == WC_SOLVER) solve();
+        f32x4 S[WC_NB];
 #pragma unroll
-        for (int sl = 0; sl < WC_SL; ++sl) Xa[sl] = Xb[sl] = Oa[sl] = Ob[sl] = Oc[sl] = zero4();
+        for (int b = 0; b < WC_NB; ++b)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) S[b][jj] = lst[mrow(b, jj) * WC_LP + col0 + l16];
+        // X = K+ S and Q+ S, each as hi*hi, lo*hi, hi*lo
+        f32x4 Xa = zero4(), Xb = zero4(), Oa = zero4(), Ob = zero4(), Oc = zero4();
 #pragma unroll
         for (int p = 0; p < WC_NPAIR; ++p) {
             const bf16x8 kpr = ops.kp[p][lane], kplr = ops.kp_lo[p][lane];
             const bf16x8 qhr = ops.qp_hi[p][lane], qlr = ops.qp_lo[p][lane];
-#pragma unroll
-            for (int sl = 0; sl < WC_SL; ++sl) {
-                const bf16x8 Shi = cat(to_bf16x4(S[sl][2 * p]), to_bf16x4(S[sl][2 * p + 1]));
-                const bf16x8 Slo = cat(to_bf16x4(mma32(NIL, Shi, S[sl][2 * p])),
-                                       to_bf16x4(mma32(NIH, Shi, S[sl][2 * p + 1])));
-                Xa[sl] = mma32(kpr, Shi, Xa[sl]);
-                Xb[sl] = mma32(kplr, Shi, Xb[sl]);
-                Xb[sl] = mma32(kpr, Slo, Xb[sl]);
-                Oa[sl] = mma32(qhr, Shi, Oa[sl]);
-                Ob[sl] = mma32(qlr, Shi, Ob[sl]);
-                Oc[sl] = mma32(qhr, Slo, Oc[sl]);
-            }
+            const bf16x8 Shi = cat(to_bf16x4(S[2 * p]), to_bf16x4(S[2 * p + 1]));
+            const bf16x8 Slo = cat(to_bf16x4(mma32(NIL, Shi, S[2 * p])), to_bf16x4(mma32(NIH, Shi, S[2 * p + 1])));
+            Xa = mma32(kpr, Shi, Xa);
+            Xb = mma32(kplr, Shi, Xb);
+            Xb = mma32(kpr, Slo, Xb);
+            Oa = mma32(qhr, Shi, Oa);
+            Ob = mma32(qlr, Shi, Ob);
+            Oc = mma32(qhr, Slo, Oc);
         }
-        __syncthreads();  // T' and Aqk of this head
+        __syncthreads();  // T' and Aqk of this head; every wave's state copy read
         const Split4 Tp4 = ops.tp[lane], Aq = ops.aq[lane];
         const bf16x8 tpp = cat(Tp4.hi, Tp4.lo), aqq = cat(Aq.hi, Aq.lo);
         const rsrc_t ro = make_rsrc(o ? o + ((int64_t)cur.b * Tw * H + cur.h) * WC_D : o, o ? (uint32_t)Tw * rowO : 0u);
-        // output rows 4 g4 + jj of this window (rows of the replay and past the window dropped)
-        uint32_t o_voff[4];
+        // Delta = T' (V - X); O = Q+ S + Aqk Delta for the rows of this window (rows of the
+        // replay and past the window dropped)
+        const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, REPLAY ? (X.c | X.p) : X.c), ID, zero4());
+        bf16x8 yhh, dhh;
+        const bf16x4 ylo = split_lo(vc - (Xa + Xb), NIL, yhh);
+        f32x4 D = mma32(tpp, yhh, zero4());
+        D = mma32(tpp, cat(ylo, ylo), D);
+        const bf16x4 dlo = split_lo(D, NIL, dhh);
+        const bf16x8 dll = cat(dlo, dlo);
+        f32x4 O = mma32(aqq, dhh, Oa + (Ob + Oc));
+        O = mma32(aqq, dll, O);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) o_voff[jj] = cur_off(cur, 4 * g4 + jj, rowO, (col0[0] + l16) * 4u);
-        bf16x8 dhh[WC_SL], dll[WC_SL];
-#pragma unroll
-        for (int sl = 0; sl < WC_SL; ++sl) {
-            // Delta = T' (V - X); O = Q+ S + Aqk Delta for the rows of this window
-            const f32x4 vc = mma16(__builtin_bit_cast(bf16x4, X.v[sl]), ID, zero4());
-            bf16x8 yhh;
-            const bf16x4 ylo = split_lo(vc - (Xa[sl] + Xb[sl]), NIL, yhh);
-            f32x4 D = mma32(tpp, yhh, zero4());
-            D = mma32(tpp, cat(ylo, ylo), D);
-            const bf16x4 dlo = split_lo(D, NIL, dhh[sl]);
-            dll[sl] = cat(dlo, dlo);
-            f32x4 O = mma32(aqq, dhh[sl], Oa[sl] + (Ob[sl] + Oc[sl]));
-            O = mma32(aqq, dll[sl], O);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[jj]), ro, o_voff[jj], 64u * sl, 0);
-        }
-        if (cur.acc > 0) {
-            // S_a = Diag(e^{G_{a-1}}) S + K~_a^T Delta, written back
-            const rsrc_t rs = state_rsrc(cur);
+        for (int jj = 0; jj < 4; ++jj)
+            buf_store_f32(O[jj], ro, cur_off(cur, 4 * g4 + jj, rowO, (col0 + l16) * 4u));
+        {
+            // S_a = Diag(e^{G_{a-1}}) S + K~_a^T Delta, through the LDS copy back to HBM; with
+            // a = 0 the stores go to an empty buffer (dropped) rather than behind a branch, so
+            // the wait counts of the next head's loads are the same on every path
 #pragma unroll
             for (int b = 0; b < WC_NB; ++b) {
                 const Split4 kt = ops.kt[b][lane];
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(&ops.gam[16 * b + 4 * g4]);
                 const bf16x8 ktt = cat(kt.hi, kt.lo);
+                const f32x4 Sn = mma32(ktt, dll, mma32(ktt, dhh, S[b] * gm));
 #pragma unroll
-                for (int sl = 0; sl < WC_SL; ++sl) {
-                    const f32x4 acc = mma32(ktt, dhh[sl], S[sl][b] * gm);
-                    const f32x4 Sn = mma32(ktt, dll[sl], acc);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Sn[jj]), rs, s_voff, s_soff(sl, b, jj), 0);
-                }
+                for (int jj = 0; jj < 4; ++jj) lst[mrow(b, jj) * WC_LP + col0 + l16] = Sn[jj];
             }
+            __syncthreads();  // the committed state in LDS
+            WcHead st = cur;
+            st.on = cur.acc > 0 ? 1u : 0u;
+            const rsrc_t rs = state_rsrc(st);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(&lst[(row0 + 2 * i) * WC_LP + c4]),
+                                                       rs, row_voff, i * 2u * WC_D * 4u, 0);
         }
-        if (more) {
-            cload(X, nxt);
-            load_state(S, nxt);
-        }
-        __syncthreads();  // operands of this head read by every wave
-        if (!more) break;
-        hd = nh;
+        __syncthreads();  // operands and the state copy of this head no longer read
+    };
+
+    const uint32_t G = gridDim.x;
+    uint32_t hd = blockIdx.x;
+    if (hd >= heads) return;
+    VIn XA, XB;
+    WcHead cur = head_of(hd);
+    pload(R, cur);
+    load_rows(P, cur);
+    cload(XA, cur);
+    // Two heads per trip, so the two v registers swap roles without a copy; the first head
+    // is peeled off, so the loop is entered where it loops back (same loads in flight on
+    // both edges, and the wait counts at its head stay exact).
+    bool more = hd + G < heads;
+    WcHead nxt = more ? head_of(hd + G) : cur;
+    process(XA, XB, cur, more, nxt);
+    while (more) {
+        hd += G;
         cur = nxt;
+        more = hd + G < heads;
+        nxt = more ? head_of(hd + G) : cur;
+        process(XB, XA, cur, more, nxt);
+        if (!more) break;
+        hd += G;
+        cur = nxt;
+        more = hd + G < heads;
+        nxt = more ? head_of(hd + G) : cur;
+        process(XA, XB, cur, more, nxt);
     }
 }
 
@@ -458,7 +483,7 @@ hipError_t launch_window_chunk(const DecodeWindowArgs &a) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const int64_t cap = (int64_t)cus * WC_BLOCKS_PER_CU;
+    const int64_t cap = cus;  // one workgroup per compute unit
     const int64_t grid = heads < cap ? heads : cap;
     const int acc_default = a.acc_default < 0 ? a.T : a.acc_default;
     auto kern = a.replay ? window_chunk_kernel<true> : window_chunk_kernel<false>;
