@@ -292,6 +292,14 @@ __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
                     cache_halo<4>(lp.cache, (int64_t)s * H + h, lp.cw, DK + 32 * p + 8 * g4, l16, hk[p]);
                 }
             }
+            // The head's q and k taps (2 x 128 channels x 4, contiguous in conv_w) pass through
+            // LDS: four coalesced 16-byte loads per lane instead of 64 row-broadcast ones.
+            __shared__ __attribute__((aligned(16))) f32x4 sW[2 * DK];
+            {
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(lp.conv_w + (int64_t)h * lp.cw * 4);
+#pragma unroll
+                for (int i = 0; i < 2 * DK / 64; ++i) sW[64 * i + lane] = src[64 * i + lane];
+            }
             // ShortConv + Swish of q and k, then the L2 norms of the rows.  The 128 channels
             // of token l16 sit in lanes l16 + 16 g4, octet 4 p + g4 in pair p; the octets are
             // added in the order of the stand-alone pass's butterfly over the octet index
@@ -301,9 +309,11 @@ __global__ __launch_bounds__(64) void chunk_local_bf16_kernel(
 #pragma unroll
             for (int p = 0; p < NB / 2; ++p) {
                 f32x4 w[8];
-                conv_weights<4>(lp.conv_w, h, lp.cw, 32 * p + 8 * g4, w);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) w[m] = sW[32 * p + 8 * g4 + m];
                 conv_swish<4>(qx[p], hq[p], w, l16, yq[p]);
-                conv_weights<4>(lp.conv_w, h, lp.cw, DK + 32 * p + 8 * g4, w);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) w[m] = sW[DK + 32 * p + 8 * g4 + m];
                 conv_swish<4>(kx[p], hk[p], w, l16, yk[p]);
                 oq[p] = octet_sumsq(yq[p]);
                 ok[p] = octet_sumsq(yk[p]);
