@@ -32,7 +32,7 @@ EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_pref
            "kda_inter_chunk_shaped", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_window_form", "kda_decode_step_fused",
            "kda_decode_window_fused",
-           "kda_decode_window_replay",
+           "kda_decode_window_replay", "kda_decode_layer_window_replay",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_backward_slabbed_workspace_bytes", "kda_prefill_backward_slabbed",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
@@ -97,6 +97,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_window_replay.restype = ctypes.c_int
     lib.kda_decode_window_replay.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              f32, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.kda_decode_layer_window_replay.restype = ctypes.c_int
+    lib.kda_decode_layer_window_replay.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                                   f32, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.kda_decode_layer_step.restype = ctypes.c_int
     lib.kda_decode_layer_step.argtypes = [vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
                                           i32, ctypes.c_int, vp]
@@ -693,6 +696,46 @@ def kda_decode_layer_step(qkv, conv_w, conv_cache, gate, beta, state, *, dk: int
         _ptr(state), _ptr(o if output_o else None), _ptr(out_gate), _ptr(norm_w), float(norm_eps), _ptr(y),
         B, H, dk, dv, _dtype_code(qkv.dtype), _stream(stream)))
     return (o if output_o else None), y
+
+
+def kda_decode_layer_window_replay(prev, replay, qkv, gate, beta, conv_w, conv_cache, state, *, dk: int,
+                                   l2_eps: float = 1e-6, gate_A_log=None, out_gate=None, norm_w=None,
+                                   norm_eps: float = 1e-6, o=None, y=None, stream=None):
+    """The layer core's speculative-decoding call: replay the previous window's accepted prefix
+    (``prev`` = dict or tuple of its qkv, gate, beta [B, Tp, H, .] or None; ``replay`` int32 [B])
+    through ShortConv (+ L2 for q, k), the gate and the recurrence, commit state and
+    ``conv_cache`` after it, then run this window's T tokens (qkv [B, T, H, 2 dk + dv], gate
+    [B, T, H, dk], beta [B, T, H]) without committing them.  Returns (o [B, T, H, dv], y or None)."""
+    if not isinstance(qkv, torch.Tensor) or qkv.device.type != "cuda":
+        raise ValueError("qkv must be a tensor on a GPU; the KDA library has no CPU path")
+    if qkv.dim() != 4:
+        raise ValueError("expected qkv [B, T, H, 2 dk + dv]")
+    B, T, H, C = qkv.shape
+    dv = C - 2 * dk
+    dev = qkv.device
+    _check_dev("qkv", qkv, dev)
+    _check_dev("gate", gate, dev, qkv.dtype, (B, T, H, dk))
+    _check_dev("beta", beta, dev, qkv.dtype, (B, T, H))
+    _check_dev("conv_w", conv_w, dev, torch.float32, (H, C, 4))
+    _check_dev("conv_cache", conv_cache, dev, torch.float32, (B, H, C, 3))
+    _check_dev("state", state, dev, torch.float32, (B, H, dk, dv))
+    Tp = 0
+    p = (None,) * 3
+    if prev is not None:
+        p = tuple(prev[n] for n in ("qkv", "gate", "beta")) if isinstance(prev, dict) else tuple(prev)
+        Tp = p[0].shape[1]
+        for name, t, shp in zip(("qkv", "gate", "beta"), p, ((B, Tp, H, C), (B, Tp, H, dk), (B, Tp, H))):
+            _check_dev("prev " + name, t, dev, qkv.dtype, shp)
+        _check_dev("replay", replay, dev, torch.int32, (B,))
+    y = _fusion_args((B, T, H, dv), qkv.dtype, dev, H, dv, gate_A_log, out_gate, norm_w, y, True)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _check_dev("o", o, dev, torch.float32, (B, T, H, dv))
+    _check(load_library().kda_decode_layer_window_replay(
+        *(_ptr(t) for t in p), _ptr(replay if Tp > 0 else None), Tp, _ptr(qkv), _ptr(gate), _ptr(beta),
+        _ptr(conv_w), _ptr(conv_cache), float(l2_eps), _ptr(gate_A_log), _ptr(state), _ptr(o), _ptr(out_gate),
+        _ptr(norm_w), float(norm_eps), _ptr(y), B, T, H, dk, dv, _dtype_code(qkv.dtype), _stream(stream)))
+    return o, y
 
 
 def kda_prefill_backward(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, init_state=None, d_final=None, *,

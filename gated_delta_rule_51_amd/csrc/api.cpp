@@ -551,6 +551,49 @@ kda_status kda_decode_window_replay(const void *pq, const void *pk, const void *
     return hip_status(kda::launch_decode_window(a));
 }
 
+kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, const void *pbeta,
+                                          const int32_t *replay, int32_t Tp, const void *qkv, const void *gate,
+                                          const void *beta, const float *conv_w, float *conv_cache, float l2_eps,
+                                          const float *gate_A_log, float *state, float *o, const void *out_gate,
+                                          const float *norm_w, float norm_eps, void *y, int32_t B, int32_t T,
+                                          int32_t H, int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || T < 1 || H < 1 || Tp < 0 || (int64_t)B * T * H >= (int64_t(1) << 31) ||
+        (int64_t)B * Tp * H >= (int64_t(1) << 31))
+        return KDA_ERR_SHAPE;
+    if (!(l2_eps >= 0.f && l2_eps <= 3.4e38f)) return KDA_ERR_SHAPE;
+    kda_status st = check_inputs({qkv, gate}, true, beta, dt == KDA_BF16, true);
+    if (st != KDA_OK) return st;
+    if (Tp > 0) {
+        if (!replay) return KDA_ERR_NULL;
+        if (reinterpret_cast<uintptr_t>(replay) & 3u) return KDA_ERR_ALIGN;
+        st = check_inputs({pqkv, pgate}, true, pbeta, dt == KDA_BF16, true);
+        if (st != KDA_OK) return st;
+    }
+    st = check_ptrs({state, conv_w, o}, {});
+    if (st != KDA_OK) return st;
+    if (!conv_cache) return KDA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(conv_cache) & 3u) return KDA_ERR_ALIGN;
+    st = check_fusion(gate_A_log, out_gate, norm_w, norm_eps, y, dt == KDA_BF16);
+    if (st != KDA_OK) return st;
+    if (out_gate) {  // the epilogue runs over o: rows 16-byte aligned
+        st = check_rows16({out_gate, y}, true);
+        if (st != KDA_OK) return st;
+    }
+    kda::DecodeWindowArgs a{qkv, nullptr, nullptr, gate, beta, state, o, nullptr, B, T, H, dk, dv, dt == KDA_BF16,
+                            stream, {gate_A_log, out_gate, norm_w, norm_eps, y, conv_w, conv_cache, l2_eps}};
+    a.acc_default = 0;  // this window's drafts are not committed
+    if (Tp > 0) {
+        a.pq = pqkv;
+        a.pg = pgate;
+        a.pbeta = pbeta;
+        a.replay = replay;
+        a.Tp = Tp;
+    }
+    return hip_status(kda::launch_decode_window(a));
+}
+
 kda_status kda_decode_window(const void *q, const void *k, const void *v, const void *log_alpha,
                              const void *beta, float *state, float *o, const int32_t *accept,
                              int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,

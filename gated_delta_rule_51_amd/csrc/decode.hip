@@ -301,12 +301,23 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 // state is written back after token rp + acc, acc = accept[b] (or acc_default),
 // so with no accept the committed state is the one after the accepted prefix
 // of the previous window and this window's drafts stay uncommitted.
+//
+// With CONV (the layer's decode window, same page's layer paragraph: ShortConv of
+// size 4 + Swish on q, k, v, L2 norms of q and k) q points at pre-convolution rows
+// q | k | v of 2 dk + dv channels ([B, Tw, H, .], the replay's at pq): each token
+// is convolved in order from a three-input window per channel that starts as the
+// sequence's cache (fx.conv_cache) and slides through the replayed and the new
+// tokens; at the commit point the cache receives the window as it stands, so
+// cache and state are committed together.  q and k channel c sit with thread
+// c < dk, v column 4 c4 + rg with row group rg < 4 (shared through LDS); the norms
+// of q and k join the k.q sums and are applied where q and k are read, as in the
+// single-token kernel.
 // Threads per window workgroup, at most.
 constexpr int WINDOW_THREADS = 512;
 
-template <int DK, int DV, typename T, bool FX, bool REPLAY>
+template <int DK, int DV, typename T, bool FX, bool REPLAY, bool CONV = false>
 __global__ __launch_bounds__((DecodeShape<DK, DV, WINDOW_THREADS>::NT))
-__attribute__((amdgpu_waves_per_eu((2 * DecodeShape<DK, DV, WINDOW_THREADS>::NT + 255) / 256, 8)))
+__attribute__((amdgpu_waves_per_eu(CONV ? (DecodeShape<DK, DV, WINDOW_THREADS>::NT + 255) / 256 : (2 * DecodeShape<DK, DV, WINDOW_THREADS>::NT + 255) / 256, 8)))
 void decode_window_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, float *__restrict__ state,
@@ -325,6 +336,9 @@ void decode_window_kernel(
     __shared__ __attribute__((aligned(16))) float s_red[2][RP][Sh::STRIDE];
     __shared__ __attribute__((aligned(16))) float s_fin[2][DV];
     __shared__ float s_kq[2][NKW];
+    __shared__ float s_nq[CONV ? NKW : 1], s_nk[CONV ? NKW : 1];
+    __shared__ __attribute__((aligned(16))) float s_vv[CONV ? 2 : 1][CONV ? DV : 4];
+    constexpr int RS = 2 * DK + DV;  // pre-convolution row (q | k | v channels)
 
     struct Tok {
         float k, q, g, b;  // k, q, g of key channel tid (tid < DK)
@@ -347,6 +361,28 @@ void decode_window_kernel(
         const int64_t row = rep ? ((int64_t)bq * Tp + t) * H + (hd - bq * (uint32_t)H)
                                 : ((int64_t)bq * Tw + (t - rp)) * H + (hd - bq * (uint32_t)H);
         const T *kb = rep ? pk : k, *qb = rep ? pq : q, *gb = rep ? pg : g, *vb = rep ? pv : v, *bb = rep ? pb : beta;
+        if constexpr (CONV) {
+            // q and k channel tid, v column 4 c4 + rg (rg < 4) of the pre-convolution row
+            const rsrc_t rx = make_rsrc(qb + row * RS, RS * sizeof(T));
+            const rsrc_t rgt = make_rsrc(gb + row * DK, DK * sizeof(T));
+            auto elem = [&](const rsrc_t &r, int i) {
+                if constexpr (sizeof(T) == 4)
+                    return __uint_as_float(buf_load_u32(r, (uint32_t)i * 4u));
+                else
+                    return bf16_bits_to_f32(buf_load_u16(r, (uint32_t)i * 2u));
+            };
+            if (tid < DK) {
+                x.q = elem(rx, tid);
+                x.k = elem(rx, DK + tid);
+                x.g = elem(rgt, tid);
+            } else {
+                x.k = x.q = x.g = 0.f;
+            }
+            x.v = zero4();
+            if (rg < 4) x.v[0] = elem(rx, 2 * DK + 4 * c4 + rg);
+            x.b = load_in(bb + row);
+            return;
+        }
         if (tid < DK) {
             const uint32_t off = tid * (uint32_t)sizeof(T);
             const rsrc_t rk = make_rsrc(kb + row * DK, DK * sizeof(T));
@@ -404,20 +440,71 @@ void decode_window_kernel(
         const int rp_next = more ? replay_of(head + stride) : 0;
         const rsrc_t rs = state_rsrc(head);
         const float gscale = FX && fx.A_log ? __expf(fx.A_log[head - bq * H]) : 0.f;
+        // (layer) the convolution windows (oldest first) and taps of this thread's channels
+        float cwq[3] = {0.f, 0.f, 0.f}, cwk[3] = {0.f, 0.f, 0.f}, cwv[3] = {0.f, 0.f, 0.f};
+        f32x4 wq4 = zero4(), wk4 = zero4(), wv4 = zero4();
+        float *ccache = nullptr;
+        const int vcol = 2 * DK + 4 * c4 + rg;  // (rg < 4)
+        if constexpr (CONV) {
+            ccache = fx.conv_cache + head * (int64_t)(RS * 3);
+            const float *wr = fx.conv_w + (head - bq * H) * (int64_t)(RS * 4);
+            if (tid < DK) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    cwq[j] = ccache[tid * 3 + j];
+                    cwk[j] = ccache[(DK + tid) * 3 + j];
+                }
+                wq4 = *reinterpret_cast<const f32x4 *>(wr + tid * 4);
+                wk4 = *reinterpret_cast<const f32x4 *>(wr + (DK + tid) * 4);
+            }
+            if (rg < 4) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) cwv[j] = ccache[vcol * 3 + j];
+                wv4 = *reinterpret_cast<const f32x4 *>(wr + vcol * 4);
+            }
+        }
+        // Swish of the 4-tap convolution (w[j] on x_{t-j}), then the window slides
+        auto conv_step = [](const f32x4 &w4, float x, float (&c)[3]) {
+            const float a = w4[0] * x + w4[1] * c[2] + w4[2] * c[1] + w4[3] * c[0];
+            c[0] = c[1];
+            c[1] = c[2];
+            c[2] = x;
+            return a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+        };
         for (int t = 0; t < n; ++t) {
             // LDS reuse across tokens as across heads in the single-token kernel
+            float kk = cur.k, qq = cur.q;
+            if constexpr (CONV) {
+                if (tid < DK) {
+                    qq = conv_step(wq4, cur.q, cwq);
+                    kk = conv_step(wk4, cur.k, cwk);
+                }
+                if (rg < 4) s_vv[par][vcol - 2 * DK] = conv_step(wv4, cur.v[0], cwv);
+            }
             if (tid < DK) {
-                s_k[tid] = cur.k;
-                s_q[tid] = cur.q;
+                s_k[tid] = kk;
+                s_q[tid] = qq;
                 s_a[tid] = decay_exp(FX && fx.A_log ? gate_from_logit(cur.g, gscale) : cur.g);
             }
             if (tid < 64 * NKW) {
-                float kq = cur.k * cur.q;
+                float kq = kk * qq, nq = qq * qq, nk = kk * kk;
 #pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
-                if ((tid & 63) == 0) s_kq[par][tid >> 6] = kq;
+                for (int m = 32; m >= 1; m >>= 1) {
+                    kq += __shfl_xor(kq, m);
+                    if (CONV) {
+                        nq += __shfl_xor(nq, m);
+                        nk += __shfl_xor(nk, m);
+                    }
+                }
+                if ((tid & 63) == 0) {
+                    s_kq[par][tid >> 6] = kq;
+                    if (CONV) {
+                        s_nq[tid >> 6] = nq;
+                        s_nk[tid >> 6] = nk;
+                    }
+                }
             }
-            const f32x4 vv = cur.v;
+            f32x4 vv = cur.v;
             const float bb = cur.b;
             if (t == 0 && more) load_rows(nrows, head + stride);
             if (t + 1 < n) {
@@ -427,15 +514,27 @@ void decode_window_kernel(
             }
             __syncthreads();
 
+            // (layer) L2 normalisation of q and k, applied where they are read
+            float inv_q = 1.f, inv_k = 1.f;
+            if constexpr (CONV) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int w = 0; w < NKW; ++w) {
+                    sq += s_nq[w];
+                    sk += s_nk[w];
+                }
+                inv_q = __builtin_amdgcn_rsqf(sq + fx.l2eps);
+                inv_k = __builtin_amdgcn_rsqf(sk + fx.l2eps);
+            }
             f32x4 pv = zero4(), pq = zero4();
             float kr[NR];
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const int row = rg + r * RP;
-                kr[r] = s_k[row];
+                kr[r] = CONV ? s_k[row] * inv_k : s_k[row];
                 rows[r] = rows[r] * s_a[row];  // forget
                 pv += kr[r] * rows[r];
-                pq += s_q[row] * rows[r];
+                pq += (CONV ? s_q[row] * inv_q : s_q[row]) * rows[r];
             }
             *reinterpret_cast<f32x4 *>(&s_red[0][rg][4 * c4]) = pv;
             *reinterpret_cast<f32x4 *>(&s_red[1][rg][4 * c4]) = pq;
@@ -457,6 +556,10 @@ void decode_window_kernel(
             float kq = 0.f;
 #pragma unroll
             for (int w = 0; w < NKW; ++w) kq += s_kq[par][w];
+            if constexpr (CONV) {
+                kq *= inv_k * inv_q;
+                vv = *reinterpret_cast<const f32x4 *>(&s_vv[par][4 * c4]);
+            }
             const f32x4 delta = bb * (vv - vhat);
             const int64_t orow = (bq * Tw + (t - rp)) * H + (head - bq * H);
             if (o && rg == 0 && t >= rp) reinterpret_cast<f32x4 *>(o + orow * DV)[c4] = rq + kq * delta;
@@ -467,6 +570,19 @@ void decode_window_kernel(
                 for (int r = 0; r < NR; ++r)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, rows[r]), rs, soff,
                                                            r * ROW_STEP, NT_POLICY);
+                if constexpr (CONV) {  // the convolution cache, committed with the state
+                    if (tid < DK) {
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) {
+                            ccache[tid * 3 + j] = cwq[j];
+                            ccache[(DK + tid) * 3 + j] = cwk[j];
+                        }
+                    }
+                    if (rg < 4) {
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) ccache[vcol * 3 + j] = cwv[j];
+                    }
+                }
             }
 
             cur = nxt;
@@ -528,8 +644,11 @@ static hipError_t launch_window_t(const DecodeWindowArgs &a) {
     const int64_t cap = GRID_THREADS / Sh::NT;
     const int64_t grid = heads < cap ? heads : cap;
     const bool fused = a.fx.A_log != nullptr;
-    auto kern = a.replay ? (fused ? decode_window_kernel<DK, DV, T, true, true> : decode_window_kernel<DK, DV, T, false, true>)
-                         : (fused ? decode_window_kernel<DK, DV, T, true, false> : decode_window_kernel<DK, DV, T, false, false>);
+    auto kern = a.fx.conv_w
+                    ? (a.replay ? decode_window_kernel<DK, DV, T, true, true, true>
+                                : decode_window_kernel<DK, DV, T, true, false, true>)
+                    : a.replay ? (fused ? decode_window_kernel<DK, DV, T, true, true> : decode_window_kernel<DK, DV, T, false, true>)
+                               : (fused ? decode_window_kernel<DK, DV, T, true, false> : decode_window_kernel<DK, DV, T, false, false>);
     hipLaunchKernelGGL(kern,
                        dim3((unsigned)grid), dim3(Sh::NT), 0, (hipStream_t)a.stream, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, a.state, a.o,

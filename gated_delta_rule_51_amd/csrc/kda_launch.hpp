@@ -31,8 +31,9 @@ struct DecodeFusion {
     const float *w;            // [dv] RMSNorm weight
     float eps;
     void *y;                   // shaped like o, input dtype
-    // ShortConv prologue (single-step kernel only): q points at the pre-convolution
-    // rows [B, H, 2 dk + dv] (q | k | v channels), k and v are unused
+    // ShortConv prologue (single-token and token-by-token window kernels): q points at
+    // the pre-convolution rows [B, (T,) H, 2 dk + dv] (q | k | v channels), k and v are
+    // unused
     const float *conv_w;       // [H, 2 dk + dv, 4], tap j on x_{t-j}
     float *conv_cache;         // [B, H, 2 dk + dv, 3], oldest first, updated in place
     float l2eps;               // L2 normalisation of q and k
@@ -66,11 +67,12 @@ struct DecodeWindowArgs {
     int32_t form = 0;
 };
 
-// Shapes the one-chunk window form serves: bf16, dk = dv = 128, no fused gate, and the
-// window's tokens (with a replay in front) within one 16-token chunk.
+// Shapes the one-chunk window form serves: bf16, dk = dv = 128, no fused gate or
+// ShortConv prologue, and the window's tokens (with a replay in front) within one
+// 16-token chunk.
 inline bool window_chunk_supported(const DecodeWindowArgs &a) {
     const int64_t tokens = (int64_t)a.T + (a.replay ? a.Tp : 0);
-    return a.bf16 && a.dk == 128 && a.dv == 128 && !a.fx.A_log && a.T >= 1 && tokens <= 16;
+    return a.bf16 && a.dk == 128 && a.dv == 128 && !a.fx.A_log && !a.fx.conv_w && a.T >= 1 && tokens <= 16;
 }
 
 // The fused layer prefill's prologue on load (layer_prologue.hpp): what the two

@@ -459,6 +459,39 @@ kda_status kda_short_conv(const void *x, const float *w, const float *cache_in,
                           int32_t l2norm, float eps, kda_dtype dt, void *y,
                           void *stream);
 
+/* Speculative decoding of the whole layer core as a serving loop runs it (the
+ * replay scheme of kda_decode_window_replay with the prologue of
+ * kda_decode_layer_step; Kimi K3 report digest, serving section: the accepted
+ * drafts are replayed from their cached projected inputs through the short
+ * convolution, the norms, the gate and the recurrence, and only verified state is
+ * written back).  Per sequence b the call first replays the first
+ * clamp(replay[b], 0, Tp) tokens of the previous window -- pqkv, pgate, pbeta
+ * [B, Tp, H, .] as qkv, gate, beta below -- and commits both the recurrent state
+ * and the convolution cache after them (neither is written when that count is
+ * 0); then it runs the T tokens of this window from there, writing o (and y) for
+ * all of them and committing neither.  Each token is convolved in order from the
+ * committed cache through the replayed and the new tokens, so the outputs are
+ * those of T more kda_decode_layer_step calls after the replayed ones.
+ *   qkv   : [B, T, H, 2 dk + dv] pre-convolution activations (as in
+ *           kda_decode_layer_step, with the window axis after B);
+ *   gate  : [B, T, H, dk] decay logits with gate_A_log (or log-decay with
+ *           gate_A_log == NULL); beta [B, T, H];
+ *   conv_w, conv_cache (fp32 [B, H, 2 dk + dv, 3], committed in place), l2_eps
+ *           as in kda_decode_layer_step;
+ *   state, o [B, T, H, dv] (required), out_gate, norm_w, norm_eps, y as in
+ *           kda_decode_window_replay.
+ * Tp = 0: nothing to replay (the p* pointers and replay may be NULL).  The window
+ * runs token by token.  B * T * H and B * Tp * H < 2^31.  Errors as for
+ * kda_decode_layer_step. */
+kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, const void *pbeta,
+                                          const int32_t *replay, int32_t Tp, const void *qkv,
+                                          const void *gate, const void *beta, const float *conv_w,
+                                          float *conv_cache, float l2_eps, const float *gate_A_log,
+                                          float *state, float *o, const void *out_gate,
+                                          const float *norm_w, float norm_eps, void *y, int32_t B,
+                                          int32_t T, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                          void *stream);
+
 /* Output epilogue: y = Sigmoid(u) * o / sqrt(mean_c(o_c^2) + eps) * w over
  * the dv channels of each (token, head).  o: fp32 [N, H, dv] (the recurrence's
  * output); u: gate logits [N, H, dv] (input dtype); w: fp32 [dv]; y: [N, H, dv]

@@ -134,6 +134,30 @@ def test_decode_window_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 16, 16, 3, None) == 4
 
 
+def test_decode_layer_window_replay_rejects_bad_arguments(lib):
+    f = lib.kda_decode_layer_window_replay
+    # pqkv pg pb replay Tp | qkv g b conv_w cache l2eps A state o u nw neps y B T H dk dv dt stream
+    base = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, None, FAKE, FAKE, None, None, 0.0,
+            None, 2, 3, 1, 16, 16, kda.KDA_BF16, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a3=None) == 1            # replay counts missing with Tp > 0
+    assert call(a9=None) == 1            # no convolution cache
+    assert call(a8=None) == 1            # no taps
+    assert call(a13=None) == 1           # o is required
+    assert call(a9=FAKE + 2) == 2        # cache 4-byte aligned
+    assert call(a8=FAKE + 4) == 2        # taps 16-byte aligned
+    assert call(a10=-1.0) == 3           # l2_eps
+    assert call(a4=-1) == 3
+    assert call(a19=0) == 3
+    assert call(a21=24) == 4
+    assert call(a3=None, a4=0, a0=None, a1=None, a2=None, a19=0) == 3  # Tp = 0 allows NULL p*, T still checked
+
+
 def test_decode_window_form_rejects_bad_arguments(lib):
     f = lib.kda_decode_window_form
     # q k v g beta state o accept B T H dk dv dt form stream
