@@ -743,7 +743,32 @@ def bench_layer(torch, kda, workloads, dev):
     ms_f, ms_s = _event_ms(torch, wfused, 20), _event_ms(torch, wseparate, 20)
     res["decode_window4_b256"] = {"batch": B, "T": T, "heads": Hd, "ms_fused": round(ms_f, 5),
                                   "ms_separate": round(ms_s, 5), "speedup": ms_s / ms_f}
-    del xw, lk, lv, state, o, yv, gz
+
+    # the layer core's speculative-decoding call at B=256, T=4: the previous window's accepted
+    # prefix replayed and the new window run through ShortConv (+ L2), gate and recurrence in one
+    # launch, the state and convolution cache committed after the prefix, then the epilogue pass
+    C = 2 * dk + dv
+    lwins = []
+    for i in range(3):
+        lx = workloads.layer_inputs(B * T, Hd, C, torch.bfloat16, nseq=B, device=dev, seed=20 + i)
+        lz = workloads.layer_inputs(B * T, Hd, dk, torch.bfloat16, device=dev, seed=30 + i)
+        lwins.append({"qkv": lx["x"].view(B, T, Hd, C), "gate": lz["z"].view(B, T, Hd, dk), "beta": xw["beta"]})
+    conv_w = lx["conv_w"]
+    cache = workloads.layer_inputs(B, Hd, C, torch.bfloat16, nseq=B, device=dev, seed=40)["conv_cache"]
+    calls = [0]
+
+    def lwin():
+        i = calls[0] = calls[0] + 1
+        kda.kda_decode_layer_window_replay(lwins[(i - 1) % 3], acc, lwins[i % 3]["qkv"], lwins[i % 3]["gate"],
+                                           lwins[i % 3]["beta"], conv_w, cache, state, dk=dk,
+                                           gate_A_log=lk["A_log"], out_gate=u, norm_w=lv["norm_w"], o=o, y=yv)
+
+    ms_l = _event_ms(torch, lwin, 20)
+    replayed = float(acc.double().mean())
+    res["decode_layer_window_replay4_b256"] = {"batch": B, "T": T, "heads": Hd, "ms_per_call": round(ms_l, 5),
+                                               "replayed_tokens_mean": replayed,
+                                               "token_steps_per_s": B * (T + replayed) / (ms_l * 1e-3)}
+    del xw, lk, lv, state, o, yv, gz, lwins, cache
     torch.cuda.empty_cache()
     return res
 
