@@ -17,15 +17,18 @@
 // digest's "chunkwise kernel" paragraph describes, laid out for 64-lane wavefronts):
 //   * NC consumer waves keep SL fp32 state slices (128 x 16 each) in registers and
 //     advance them chunk by chunk on the matrix cores (the serial part);
-//   * NP = 4 producer waves build everything that does not depend on the state, two
+//   * NP = 4 producer waves build everything that does not depend on the state, three
 //     chunks ahead: per chunk they stage q, k, g through LDS, form G (0/1-triangle
 //     products on the matrix cores), e^{+-G}, Q+, K+, K~, Gamma and, over their own key
 //     channels, partial sums of A, A^T and Aqk^T; one producer per chunk (in turn) then
 //     adds the partials and inverts I + A as the product (I - B)(I + B^2)(I + B^4)(I + B^8)
-//     (B = A^T is strictly upper triangular, so B^16 = 0) on the matrix cores.
-// One barrier per chunk.  In interval c the consumers advance chunk c (operand set c % 3),
-// the solver completes chunk c + 1 (T' and Aqk into set (c + 1) % 3) and the producers
-// build chunk c + 2 (set (c + 2) % 3, partials into buffer (c + 2) % 2).
+//     (B = A^T is strictly upper triangular, so B^16 = 0) on the matrix cores, in two
+//     halves over two intervals (the solve is a chain of dependent products; done whole
+//     beside a build it made that wave the last at every barrier).
+// One barrier per chunk.  In interval c the consumers advance chunk c (operand set c % 4),
+// producer (c + 1) % 4 finishes the solve of chunk c + 1 (T' and Aqk into set (c + 1) % 4),
+// producer (c + 2) % 4 begins that of chunk c + 2 (partials from buffer c % 2) and the
+// producers build chunk c + 3 (set (c + 3) % 4, partials into buffer (c + 1) % 2).
 //
 // Precision (as in the two-kernel path): every product split bf16 (hi*hi + lo*hi + hi*lo,
 // and lo*lo where it is free) with fp32 accumulation; the products of the inverse use both
@@ -86,6 +89,7 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                           const int32_t *__restrict__ cu, int32_t H, float *__restrict__ o,
                           float *__restrict__ fin, int32_t nsplit, int32_t nchains, int32_t nsort) {
     constexpr int NP = 4;
+    constexpr int NSETS = 4;  // operand sets: chunks c .. c + 3 are in flight in interval c
     constexpr int NB = DK / 16, NPAIR = NB / 2, BPW = NB / NP;
     constexpr uint32_t EB = 2;
     static_assert(DK == 128, "the fused kernel is built for 128 key channels (one block pair per producer)");
@@ -109,7 +113,7 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
     const int role = Layout::role(tid >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
 
-    __shared__ __attribute__((aligned(16))) FusedOps<DK> ops[3];
+    __shared__ __attribute__((aligned(16))) FusedOps<DK> ops[NSETS];
     // partial sums per producer: A, A^T, Aqk^T in the accumulator layout
     __shared__ __attribute__((aligned(16))) f32x4 part[2][NP][3][64];
 
@@ -142,7 +146,7 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
     if (role == -NP - 1) {
         // idle wave: the same barriers as the others (two before the chunk loop)
         if (nc > 0)
-            for (int c = 0; c < nc + 2; ++c) __syncthreads();
+            for (int c = 0; c < nc + 3; ++c) __syncthreads();
     } else if (role >= 0) {
         // ============================================================ consumer
         const int wave = role;
@@ -257,13 +261,14 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
             cload(X2, 2);
             __syncthreads();  // chunk 0 built (partials)
             __syncthreads();  // chunk 0 complete (T', Aqk); chunk 1 built
+            __syncthreads();  // chunk 1 half solved; chunk 2 built
             // Everything loaded so far (state, first inputs) has arrived before the loop: the
             // wait-count pass otherwise merges these loads, issued with few others after them,
             // into the loop header and makes the first chunks of every unrolled trip wait for
             // the loads and stores of the chunk just before.
             __builtin_amdgcn_s_waitcnt(0);
-            auto citer = [&](int c, CIn &X, int set) {
-                advance(ops[set], X, c);
+            auto citer = [&](int c, CIn &X) {
+                advance(ops[c & (NSETS - 1)], X, c);
                 cload(X, c + 3);
                 __syncthreads();
             };
@@ -271,12 +276,12 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
             // body made the compiler wait for every load in flight at the loop head)
             int c = 0;
             for (; c + 3 <= nc; c += 3) {
-                citer(c, X0, 0);
-                citer(c + 1, X1, 1);
-                citer(c + 2, X2, 2);
+                citer(c, X0);
+                citer(c + 1, X1);
+                citer(c + 2, X2);
             }
-            if (c < nc) citer(c, X0, 0);
-            if (c + 1 < nc) citer(c + 1, X1, 1);
+            if (c < nc) citer(c, X0);
+            if (c + 1 < nc) citer(c + 1, X1);
         }
         if (fin) {
 #pragma unroll
@@ -415,7 +420,13 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
             c = mma32(a, cat(y.hi, y.hi), c);
             return mma32(a, cat(y.lo, y.lo), c);
         };
-        auto solve = [&](FusedOps<DK> &P, const f32x4 (&pp)[NP][3][64]) {
+        // The solve in two halves, run in consecutive intervals by the same wave: the first
+        // adds the partials and forms B^2, B^4 and (I - B)(I + B^2); the second finishes the
+        // product and writes T' and Aqk.
+        struct SolveMid {
+            f32x4 A4, B4, R1, Qm, brow;
+        };
+        auto solve1 = [&](const FusedOps<DK> &P, const f32x4 (&pp)[NP][3][64]) {
             f32x4 Am = pp[0][0][lane], Bm = pp[0][1][lane], Qm = pp[0][2][lane];
 #pragma unroll
             for (int w = 1; w < NP; ++w) {
@@ -438,27 +449,37 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
             // powers: A^2 = A A (left A: accumulator layout of A^T = B), B^2 = B B, ...
             const f32x4 A2 = prod(sB, sA, zero4()), B2 = prod(sA, sB, zero4());
             const SplitT sA2 = splitT(A2), sB2 = splitT(B2), sR0 = splitT(R0);
-            const f32x4 A4 = prod(sB2, sA2, zero4()), B4 = prod(sA2, sB2, zero4());
+            SolveMid m;
+            m.A4 = prod(sB2, sA2, zero4());
+            m.B4 = prod(sA2, sB2, zero4());
             // T^T = (I + B)^-1 = (I - B)(I + B^2)(I + B^4)(I + B^8): R <- R + B^(2^k) R, the left
             // factor B^(2^k) given by the accumulator layout of its transpose A^(2^k)
-            const f32x4 R1 = prod(sA2, sR0, R0);
-            const SplitT sA4 = splitT(A4), sB4 = splitT(B4), sR1 = splitT(R1);
+            m.R1 = prod(sA2, sR0, R0);
+            m.Qm = Qm;
+            m.brow = brow;
+            return m;
+        };
+        auto solve2 = [&](FusedOps<DK> &P, const SolveMid &m) {
+            const SplitT sA4 = splitT(m.A4), sB4 = splitT(m.B4), sR1 = splitT(m.R1);
             const f32x4 A8 = prod(sB4, sA4, zero4());
-            const f32x4 R2 = prod(sA4, sR1, R1);
+            const f32x4 R2 = prod(sA4, sR1, m.R1);
             const SplitT sA8 = splitT(A8), sR2 = splitT(R2);
             f32x4 Tt = prod(sA8, sR2, R2);
             // T'^T = diag(beta) T^T: the accumulator layout of T'^T is the A operand of T'
-            Tt *= brow;
-            const SplitT st = splitT(Tt), sq = splitT(Qm);
+            Tt *= m.brow;
+            const SplitT st = splitT(Tt), sq = splitT(m.Qm);
             P.tp[lane] = Split4{st.hi, st.lo};
             P.aq[lane] = Split4{sq.hi, sq.lo};
         };
 
-        // Iteration c completes chunk c + 1 (solver pw == (c + 1) % NP), builds chunk c + 2
-        // (staged in A), stages chunk c + 3 (loaded three iterations earlier) and loads
-        // chunk c + 6; register sets rotate R0 -> R1 -> R2.
+        // Interval c: the wave pw == (c + 1) % NP finishes the solve of chunk c + 1 (begun in
+        // interval c - 1), the wave pw == (c + 2) % NP begins that of chunk c + 2, and every
+        // producer builds its part of chunk c + 3 (staged in the interval before), stages
+        // chunk c + 4 and loads chunk c + 7; register sets rotate R1 -> R2 -> R0.  Priority
+        // goes to the solve, whose chain the consumers wait for at the next barrier.
         PIn R0, R1, R2;
         AIn A;
+        SolveMid mid;
         pload(R0, 0);
         pload(R1, 1);
         pload(R2, 2);
@@ -470,29 +491,44 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
         stage_get(A, R1);
         pload(R1, 4);
         __syncthreads();  // partials of chunk 0 complete
-        if (pw == 0) solve(ops[0], part[0]);
+        if (pw == 0) solve2(ops[0], solve1(ops[0], part[0]));
         build(A, ops[1], part[1][pw]);
         stage_put(R2);
         stage_get(A, R2);
         pload(R2, 5);
-        __syncthreads();  // chunk 0 complete
+        __syncthreads();  // chunk 0 complete; partials of chunk 1 complete
+        if (pw == 1) mid = solve1(ops[1], part[1]);
+        build(A, ops[2], part[0][pw]);
+        stage_put(R0);
+        stage_get(A, R0);
+        pload(R0, 6);
+        __syncthreads();  // chunk 1 half solved, chunk 2 built
         __builtin_amdgcn_s_waitcnt(0);  // (as for the consumers: no merged waits in the loop)
-        auto piter = [&](int c, PIn &R, int s1, int s2) {
-            if (pw == (c + 1) % NP) solve(ops[s1], part[(c + 1) & 1]);
-            build(A, ops[s2], part[c & 1][pw]);
+        auto piter = [&](int c, PIn &R) {
+            if (pw == (c + 1) % NP) {
+                __builtin_amdgcn_s_setprio(3);
+                solve2(ops[(c + 1) & (NSETS - 1)], mid);
+                __builtin_amdgcn_s_setprio(0);
+            }
+            if (pw == (c + 2) % NP) {
+                __builtin_amdgcn_s_setprio(3);
+                mid = solve1(ops[(c + 2) & (NSETS - 1)], part[c & 1]);
+                __builtin_amdgcn_s_setprio(0);
+            }
+            build(A, ops[(c + 3) & (NSETS - 1)], part[(c + 1) & 1][pw]);
             stage_put(R);
             stage_get(A, R);
-            pload(R, c + 6);
+            pload(R, c + 7);
             __syncthreads();
         };
         int c = 0;
         for (; c + 3 <= nc; c += 3) {
-            piter(c, R0, 1, 2);
-            piter(c + 1, R1, 2, 0);
-            piter(c + 2, R2, 0, 1);
+            piter(c, R1);
+            piter(c + 1, R2);
+            piter(c + 2, R0);
         }
-        if (c < nc) piter(c, R0, 1, 2);
-        if (c + 1 < nc) piter(c + 1, R1, 2, 0);
+        if (c < nc) piter(c, R1);
+        if (c + 1 < nc) piter(c + 1, R2);
     }
 }
 
