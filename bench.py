@@ -745,8 +745,9 @@ def bench_layer(torch, kda, workloads, dev):
                                   "ms_separate": round(ms_s, 5), "speedup": ms_s / ms_f}
 
     # the layer core's speculative-decoding call at B=256, T=4: the previous window's accepted
-    # prefix replayed and the new window run through ShortConv (+ L2), gate and recurrence in one
-    # launch, the state and convolution cache committed after the prefix, then the epilogue pass
+    # prefix replayed and the new window run through ShortConv (+ L2), gate and recurrence, the
+    # state and convolution cache committed after the prefix, then the epilogue pass; the one-chunk
+    # form (prologue pass + chunk kernel, chosen for T + Tp = 8) and the token-by-token kernel
     C = 2 * dk + dv
     lwins = []
     for i in range(3):
@@ -757,18 +758,32 @@ def bench_layer(torch, kda, workloads, dev):
     cache = workloads.layer_inputs(B, Hd, C, torch.bfloat16, nseq=B, device=dev, seed=40)["conv_cache"]
     calls = [0]
 
-    def lwin():
+    need = kda.kda_decode_layer_window_workspace_bytes(B, T, T, Hd, dk, dv, torch.bfloat16)
+    lws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def lwin(form):
         i = calls[0] = calls[0] + 1
         kda.kda_decode_layer_window_replay(lwins[(i - 1) % 3], acc, lwins[i % 3]["qkv"], lwins[i % 3]["gate"],
                                            lwins[i % 3]["beta"], conv_w, cache, state, dk=dk,
-                                           gate_A_log=lk["A_log"], out_gate=u, norm_w=lv["norm_w"], o=o, y=yv)
+                                           gate_A_log=lk["A_log"], out_gate=u, norm_w=lv["norm_w"], o=o, y=yv,
+                                           form=form, workspace=lws if form != 1 else None)
 
-    ms_l = _event_ms(torch, lwin, 20)
+    ms_l = _event_ms(torch, lambda: lwin(None), 20)
+    ms_t = _event_ms(torch, lambda: lwin(1), 20)
     replayed = float(acc.double().mean())
-    res["decode_layer_window_replay4_b256"] = {"batch": B, "T": T, "heads": Hd, "ms_per_call": round(ms_l, 5),
+    # algorithmic HBM bytes: the state read and written once per head; per replayed token its raw
+    # q | k | v row, gate logits and beta; per window token those, o (fp32), u and y
+    bpt_r = 2 * (C + dk + 1)
+    bpt_w = bpt_r + 4 * dv + 2 * dv + 2 * dv
+    nbytes = B * Hd * (2 * dk * dv * 4 + replayed * bpt_r + T * bpt_w)
+    res["decode_layer_window_replay4_b256"] = {"batch": B, "T": T, "heads": Hd, "form": "one chunk" if need else
+                                               "token by token", "ms_per_call": round(ms_l, 5),
+                                               "ms_token_by_token": round(ms_t, 5),
                                                "replayed_tokens_mean": replayed,
-                                               "token_steps_per_s": B * (T + replayed) / (ms_l * 1e-3)}
-    del xw, lk, lv, state, o, yv, gz, lwins, cache
+                                               "token_steps_per_s": B * (T + replayed) / (ms_l * 1e-3),
+                                               "hbm_gbs_algorithmic": nbytes / (ms_l * 1e-3) / 1e9,
+                                               "hbm_roofline_frac": nbytes / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del xw, lk, lv, state, o, yv, gz, lwins, cache, lws
     torch.cuda.empty_cache()
     return res
 

@@ -32,7 +32,7 @@ EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_pref
            "kda_inter_chunk_shaped", "kda_prefill_noalloc", "kda_chunk_local", "kda_inter_chunk",
            "kda_decode_step", "kda_decode_window", "kda_decode_window_form", "kda_decode_step_fused",
            "kda_decode_window_fused",
-           "kda_decode_window_replay", "kda_decode_layer_window_replay",
+           "kda_decode_window_replay", "kda_decode_layer_window_replay", "kda_decode_layer_window_workspace_bytes",
            "kda_decode_layer_step", "kda_prefill_backward_workspace_bytes", "kda_prefill_backward",
            "kda_prefill_backward_slabbed_workspace_bytes", "kda_prefill_backward_slabbed",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
@@ -99,7 +99,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                              f32, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.kda_decode_layer_window_replay.restype = ctypes.c_int
     lib.kda_decode_layer_window_replay.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
-                                                   f32, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+                                                   f32, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp,
+                                                   ctypes.c_size_t, vp]
+    lib.kda_decode_layer_window_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_decode_layer_window_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
     lib.kda_decode_layer_step.restype = ctypes.c_int
     lib.kda_decode_layer_step.argtypes = [vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32,
                                           i32, ctypes.c_int, vp]
@@ -698,14 +701,22 @@ def kda_decode_layer_step(qkv, conv_w, conv_cache, gate, beta, state, *, dk: int
     return (o if output_o else None), y
 
 
+def kda_decode_layer_window_workspace_bytes(B: int, T: int, Tp: int, H: int, dk: int, dv: int, dtype) -> int:
+    """Workspace bytes of kda_decode_layer_window_replay's one-chunk form (0: the shape runs token by token)."""
+    return int(load_library().kda_decode_layer_window_workspace_bytes(B, T, Tp, H, dk, dv, _dtype_code(dtype)))
+
+
 def kda_decode_layer_window_replay(prev, replay, qkv, gate, beta, conv_w, conv_cache, state, *, dk: int,
                                    l2_eps: float = 1e-6, gate_A_log=None, out_gate=None, norm_w=None,
-                                   norm_eps: float = 1e-6, o=None, y=None, stream=None):
+                                   norm_eps: float = 1e-6, o=None, y=None, form=None, workspace=None, stream=None):
     """The layer core's speculative-decoding call: replay the previous window's accepted prefix
     (``prev`` = dict or tuple of its qkv, gate, beta [B, Tp, H, .] or None; ``replay`` int32 [B])
     through ShortConv (+ L2 for q, k), the gate and the recurrence, commit state and
     ``conv_cache`` after it, then run this window's T tokens (qkv [B, T, H, 2 dk + dv], gate
-    [B, T, H, dk], beta [B, T, H]) without committing them.  Returns (o [B, T, H, dv], y or None)."""
+    [B, T, H, dk], beta [B, T, H]) without committing them.  Returns (o [B, T, H, dv], y or None).
+    ``form``: None chooses (the one-chunk form where the library serves the shape, with a
+    workspace allocated here unless ``workspace`` is given), 1 token by token, 2 the one-chunk
+    form (ValueError where the shape has none)."""
     if not isinstance(qkv, torch.Tensor) or qkv.device.type != "cuda":
         raise ValueError("qkv must be a tensor on a GPU; the KDA library has no CPU path")
     if qkv.dim() != 4:
@@ -731,10 +742,22 @@ def kda_decode_layer_window_replay(prev, replay, qkv, gate, beta, conv_w, conv_c
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     _check_dev("o", o, dev, torch.float32, (B, T, H, dv))
+    if form not in (None, 1, 2):
+        raise ValueError("form must be None, 1 (token by token) or 2 (one chunk)")
+    need = kda_decode_layer_window_workspace_bytes(B, T, Tp, H, dk, dv, qkv.dtype)
+    if form == 2 and need == 0:
+        raise ValueError("the one-chunk form serves bf16 with dk = dv = 128 and 6 <= T + Tp <= 16")
+    ws, ws_bytes = None, 0
+    if form != 1 and need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check_dev("workspace", workspace, dev)
+        ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     _check(load_library().kda_decode_layer_window_replay(
         *(_ptr(t) for t in p), _ptr(replay if Tp > 0 else None), Tp, _ptr(qkv), _ptr(gate), _ptr(beta),
         _ptr(conv_w), _ptr(conv_cache), float(l2_eps), _ptr(gate_A_log), _ptr(state), _ptr(o), _ptr(out_gate),
-        _ptr(norm_w), float(norm_eps), _ptr(y), B, T, H, dk, dv, _dtype_code(qkv.dtype), _stream(stream)))
+        _ptr(norm_w), float(norm_eps), _ptr(y), B, T, H, dk, dv, _dtype_code(qkv.dtype), _ptr(ws), ws_bytes,
+        _stream(stream)))
     return o, y
 
 

@@ -556,7 +556,8 @@ kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, c
                                           const void *beta, const float *conv_w, float *conv_cache, float l2_eps,
                                           const float *gate_A_log, float *state, float *o, const void *out_gate,
                                           const float *norm_w, float norm_eps, void *y, int32_t B, int32_t T,
-                                          int32_t H, int32_t dk, int32_t dv, kda_dtype dt, void *stream) {
+                                          int32_t H, int32_t dk, int32_t dv, kda_dtype dt, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
     if (B < 1 || T < 1 || H < 1 || Tp < 0 || (int64_t)B * T * H >= (int64_t(1) << 31) ||
@@ -591,7 +592,22 @@ kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, c
         a.replay = replay;
         a.Tp = Tp;
     }
+    if (workspace && kda::layer_window_chunk_supported(a) && T + Tp >= kda::WINDOW_CHUNK_MIN_TOKENS) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 15u) return KDA_ERR_ALIGN;
+        if (workspace_bytes < kda::layer_window_chunk_bytes(B, T, Tp, H)) return KDA_ERR_SHAPE;
+        return hip_status(kda::launch_layer_window_chunk(a, workspace));
+    }
     return hip_status(kda::launch_decode_window(a));
+}
+
+size_t kda_decode_layer_window_workspace_bytes(int32_t B, int32_t T, int32_t Tp, int32_t H, int32_t dk,
+                                               int32_t dv, kda_dtype dt) {
+    if (B < 1 || T < 1 || H < 1 || Tp < 0 || (int64_t)B * T * H >= (int64_t(1) << 31) ||
+        (int64_t)B * Tp * H >= (int64_t(1) << 31))
+        return 0;
+    if (!(dt == KDA_BF16 && dk == 128 && dv == 128 && T + Tp >= kda::WINDOW_CHUNK_MIN_TOKENS && T + Tp <= 16))
+        return 0;
+    return kda::layer_window_chunk_bytes(B, T, Tp, H);
 }
 
 kda_status kda_decode_window(const void *q, const void *k, const void *v, const void *log_alpha,

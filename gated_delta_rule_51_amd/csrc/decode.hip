@@ -674,12 +674,6 @@ static hipError_t launch_window_dt(const DecodeWindowArgs &a) {
     return hipErrorInvalidValue;
 }
 
-// Calls of this many tokens per (sequence, head) on (the window's, plus the replay's at
-// most) go through the one-chunk form where it serves the shape: below it the
-// token-by-token kernel's arithmetic hides behind its state traffic (B=256 x H=96:
-// 0.58 against 0.63 ms at 4 tokens, 0.74 against 0.68 at 6, 0.99 against 0.68 at 8).
-constexpr int WINDOW_CHUNK_MIN_TOKENS = 6;
-
 hipError_t launch_decode_window(const DecodeWindowArgs &a) {
     const int64_t tokens = (int64_t)a.T + (a.replay ? a.Tp : 0);
     if (a.form == 2 || (a.form == 0 && tokens >= WINDOW_CHUNK_MIN_TOKENS && window_chunk_supported(a)))

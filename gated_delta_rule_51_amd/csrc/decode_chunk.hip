@@ -41,6 +41,7 @@
 // 32 P + 8 g4 + 4 h + j, so one lane's part of a block pair is one 16-byte piece.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "layer_prologue.hpp"
 
 namespace kda {
 
@@ -496,6 +497,148 @@ hipError_t launch_window_chunk(const DecodeWindowArgs &a) {
     if (e != hipSuccess || !a.fx.u) return e;
     const OutNormGateArgs ep{a.o, a.fx.u, a.fx.w, a.fx.eps, (int64_t)a.B * a.T, a.H, a.dv, a.bf16, a.fx.y, a.stream};
     return launch_out_norm_gate(ep);
+}
+
+// ------------------------------------------------------------------ the layer's window
+// The layer's decode window (ShortConv + Swish on q, k, v, L2 norms of q and k, the gate
+// from logits; Kimi K3 report digest, "Kimi Delta Attention", the paragraph after the
+// update equation, and the bounded-decay section) in the one-chunk form: a prologue pass
+// runs each (sequence, head) through its replayed prefix and the window's tokens in order,
+// from the sequence's convolution cache, and writes the chunk kernel's bf16 inputs -- the
+// normalised q and k, Swish(conv(v)) and the log-decay -- to a workspace; it commits the
+// cache after the prefix (where the chunk kernel commits the state).  The chunk kernel then
+// runs on those rows, and the output epilogue on o.
+//
+// One wave per (sequence, head); lane l holds channels 2 l and 2 l + 1 of q, k, v and the
+// gate, carries the convolution's three earlier inputs of each in registers, and the row
+// norms are butterfly sums over the wave.
+constexpr int WP_WAVES = 4;
+
+__global__ __launch_bounds__(64 * WP_WAVES) void window_prologue_kernel(
+    const __bf16 *__restrict__ qkv, const __bf16 *__restrict__ gate, const __bf16 *__restrict__ pqkv,
+    const __bf16 *__restrict__ pgate, const int32_t *__restrict__ replay, int32_t Tp, int32_t Tw, int32_t H,
+    int64_t heads, const float *__restrict__ conv_w, float *__restrict__ conv_cache, float l2eps,
+    const float *__restrict__ A_log, __bf16 *__restrict__ ws) {
+    constexpr int D = WC_D, C = 3 * WC_D;
+    const int lane = threadIdx.x & 63;
+    const int64_t head = (int64_t)blockIdx.x * WP_WAVES + (threadIdx.x >> 6);
+    if (head >= heads) return;  // (whole waves)
+    const int64_t b = head / H;
+    const int h = (int)(head - b * H);
+    int rp = 0;
+    if (Tp > 0) {
+        rp = replay[b];
+        rp = rp < 0 ? 0 : (rp > Tp ? Tp : rp);
+    }
+    const int n = rp + Tw;
+    // workspace: q, k, v, g rows of the window ([B, Tw, H, D] each), then of the prefix
+    // ([B, Tp, H, D] each)
+    const int64_t cur_sz = heads * Tw * D, pre_sz = heads * Tp * D;
+    float x1[3][2], x2[3][2], x3[3][2];  // inputs t - 1, t - 2, t - 3 of q, k, v
+    f32x4 w[3][2];
+    float *cc = conv_cache + head * (int64_t)C * 3;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int ch = t * D + 2 * lane + m;
+            x3[t][m] = cc[ch * 3 + 0];
+            x2[t][m] = cc[ch * 3 + 1];
+            x1[t][m] = cc[ch * 3 + 2];
+            w[t][m] = *reinterpret_cast<const f32x4 *>(conv_w + ((int64_t)h * C + ch) * 4);
+        }
+    const float eA = A_log ? __expf(A_log[h]) : 0.f;
+    for (int j = 0; j < n; ++j) {
+        const bool pre = j < rp;
+        const int64_t row = pre ? ((b * Tp + j) * H + h) : ((b * Tw + (j - rp)) * H + h);
+        const __bf16 *src = (pre ? pqkv : qkv) + row * C;
+        const uint32_t gw = *reinterpret_cast<const uint32_t *>((pre ? pgate : gate) + row * D + 2 * lane);
+        float x0[3][2], y[3][2];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const uint32_t xw = *reinterpret_cast<const uint32_t *>(src + t * D + 2 * lane);
+            x0[t][0] = lo_bf16(xw);
+            x0[t][1] = hi_bf16(xw);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) y[t][m] = conv4_swish(w[t][m], x0[t][m], x1[t][m], x2[t][m], x3[t][m]);
+        }
+        float sq = __builtin_fmaf(y[0][0], y[0][0], y[0][1] * y[0][1]);
+        float sk = __builtin_fmaf(y[1][0], y[1][0], y[1][1] * y[1][1]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            sq += __shfl_xor(sq, m);
+            sk += __shfl_xor(sk, m);
+        }
+        const float iq = __builtin_amdgcn_rsqf(sq + l2eps), ik = __builtin_amdgcn_rsqf(sk + l2eps);
+        float g0 = lo_bf16(gw), g1 = hi_bf16(gw);
+        if (A_log) {
+            g0 = gate_of(eA, g0);
+            g1 = gate_of(eA, g1);
+        }
+        const bf16x4 qk = to_bf16x4(f32x4{y[0][0] * iq, y[0][1] * iq, y[1][0] * ik, y[1][1] * ik});
+        const bf16x4 vg = to_bf16x4(f32x4{y[2][0], y[2][1], g0, g1});
+        const u32x2 qkw = __builtin_bit_cast(u32x2, qk), vgw = __builtin_bit_cast(u32x2, vg);
+        __bf16 *dst = ws + (pre ? 4 * cur_sz : 0) + row * D + 2 * lane;
+        const int64_t step = pre ? pre_sz : cur_sz;
+        *reinterpret_cast<uint32_t *>(dst) = qkw[0];
+        *reinterpret_cast<uint32_t *>(dst + step) = qkw[1];
+        *reinterpret_cast<uint32_t *>(dst + 2 * step) = vgw[0];
+        *reinterpret_cast<uint32_t *>(dst + 3 * step) = vgw[1];
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                x3[t][m] = x2[t][m];
+                x2[t][m] = x1[t][m];
+                x1[t][m] = x0[t][m];
+            }
+        if (j + 1 == rp) {  // the commit point: the cache holds the three inputs before it
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int ch = t * D + 2 * lane + m;
+                    cc[ch * 3 + 0] = x3[t][m];
+                    cc[ch * 3 + 1] = x2[t][m];
+                    cc[ch * 3 + 2] = x1[t][m];
+                }
+        }
+    }
+}
+
+size_t layer_window_chunk_bytes(int64_t B, int64_t T, int64_t Tp, int64_t H) {
+    return (size_t)(4 * WC_D * 2) * (size_t)(B * H * (T + Tp));
+}
+
+hipError_t launch_layer_window_chunk(const DecodeWindowArgs &a, void *ws) {
+    if (!layer_window_chunk_supported(a) || !ws) return hipErrorInvalidValue;
+    const int64_t heads = (int64_t)a.B * a.H;
+    const int64_t blocks = (heads + WP_WAVES - 1) / WP_WAVES;
+    const int32_t Tp = a.replay ? a.Tp : 0;
+    __bf16 *w = static_cast<__bf16 *>(ws);
+    hipLaunchKernelGGL(window_prologue_kernel, dim3((unsigned)blocks), dim3(64 * WP_WAVES), 0, (hipStream_t)a.stream,
+                       (const __bf16 *)a.q, (const __bf16 *)a.g, (const __bf16 *)a.pq, (const __bf16 *)a.pg,
+                       a.replay, Tp, a.T, a.H, heads, a.fx.conv_w, a.fx.conv_cache, a.fx.l2eps, a.fx.A_log, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t cur_sz = heads * a.T * WC_D, pre_sz = heads * Tp * WC_D;
+    DecodeWindowArgs c = a;
+    c.q = w;
+    c.k = w + cur_sz;
+    c.v = w + 2 * cur_sz;
+    c.g = w + 3 * cur_sz;
+    if (Tp > 0) {
+        __bf16 *p = w + 4 * cur_sz;
+        c.pq = p;
+        c.pk = p + pre_sz;
+        c.pv = p + 2 * pre_sz;
+        c.pg = p + 3 * pre_sz;
+    }
+    c.fx.A_log = nullptr;
+    c.fx.conv_w = nullptr;
+    c.fx.conv_cache = nullptr;
+    c.form = 2;
+    return launch_window_chunk(c);
 }
 
 }  // namespace kda

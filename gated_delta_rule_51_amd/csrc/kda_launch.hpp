@@ -75,6 +75,22 @@ inline bool window_chunk_supported(const DecodeWindowArgs &a) {
     return a.bf16 && a.dk == 128 && a.dv == 128 && !a.fx.A_log && !a.fx.conv_w && a.T >= 1 && tokens <= 16;
 }
 
+// Calls of this many tokens per (sequence, head) on (the window's, plus the replay's at
+// most) go through the one-chunk form where it serves the shape: below it the
+// token-by-token kernel's arithmetic hides behind its state traffic (B=256 x H=96:
+// 0.58 against 0.63 ms at 4 tokens, 0.74 against 0.68 at 6, 0.99 against 0.68 at 8).
+constexpr int WINDOW_CHUNK_MIN_TOKENS = 6;
+
+// The layer's window (fx.conv_w set: pre-convolution q | k | v rows) in the one-chunk form:
+// a prologue pass writes the chunk kernel's inputs to a workspace of
+// layer_window_chunk_bytes(B, T, Tp, H) bytes (decode_chunk.hip).
+inline bool layer_window_chunk_supported(const DecodeWindowArgs &a) {
+    const int64_t tokens = (int64_t)a.T + (a.replay ? a.Tp : 0);
+    return a.bf16 && a.dk == 128 && a.dv == 128 && a.fx.conv_w && a.fx.conv_cache && a.T >= 1 && tokens <= 16;
+}
+size_t layer_window_chunk_bytes(int64_t B, int64_t T, int64_t Tp, int64_t H);
+hipError_t launch_layer_window_chunk(const DecodeWindowArgs &a, void *ws);
+
 // The fused layer prefill's prologue on load (layer_prologue.hpp): what the two
 // prefill kernels need besides their usual inputs.
 struct LayerPrologue {

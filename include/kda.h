@@ -480,9 +480,18 @@ kda_status kda_short_conv(const void *x, const float *w, const float *cache_in,
  *           as in kda_decode_layer_step;
  *   state, o [B, T, H, dv] (required), out_gate, norm_w, norm_eps, y as in
  *           kda_decode_window_replay.
- * Tp = 0: nothing to replay (the p* pointers and replay may be NULL).  The window
- * runs token by token.  B * T * H and B * Tp * H < 2^31.  Errors as for
- * kda_decode_layer_step. */
+ * Tp = 0: nothing to replay (the p* pointers and replay may be NULL).
+ * Evaluation: with a workspace (device, 16-byte aligned, workspace_bytes at
+ * least kda_decode_layer_window_workspace_bytes(B, T, Tp, H, dk, dv, dt)) and
+ * bf16 inputs with dk = dv = 128 and 6 <= T + Tp <= 16, a prologue pass writes
+ * the convolved, normalised q, k, v and the log-decay rows, rounded to bf16, to
+ * the workspace (committing the cache after the prefix), and the window runs as
+ * one chunk on the matrix cores (the form of kda_decode_window); otherwise, and
+ * with workspace == NULL, it runs token by token in one kernel, q, k, v and the
+ * decay staying fp32.  The committed cache is the same in both (it holds raw
+ * inputs).  B * T * H and B * Tp * H < 2^31.  Errors as for
+ * kda_decode_layer_step; a workspace that is misaligned gives KDA_ERR_ALIGN, one
+ * smaller than required KDA_ERR_SHAPE. */
 kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, const void *pbeta,
                                           const int32_t *replay, int32_t Tp, const void *qkv,
                                           const void *gate, const void *beta, const float *conv_w,
@@ -490,7 +499,14 @@ kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, c
                                           float *state, float *o, const void *out_gate,
                                           const float *norm_w, float norm_eps, void *y, int32_t B,
                                           int32_t T, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
-                                          void *stream);
+                                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace kda_decode_layer_window_replay needs for its one-chunk form
+ * (1,024 B per (sequence, head, token) of T + Tp: bf16 q, k, v and log-decay of
+ * 128 channels); 0 when that form does not apply to the shape (then the call
+ * runs token by token and needs none) or the shape is invalid. */
+size_t kda_decode_layer_window_workspace_bytes(int32_t B, int32_t T, int32_t Tp, int32_t H, int32_t dk,
+                                               int32_t dv, kda_dtype dt);
 
 /* Output epilogue: y = Sigmoid(u) * o / sqrt(mean_c(o_c^2) + eps) * w over
  * the dv channels of each (token, head).  o: fp32 [N, H, dv] (the recurrence's

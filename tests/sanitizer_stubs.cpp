@@ -17,6 +17,10 @@ hipError_t launch_inter_chunk_ws(const InterChunkArgs &, int, int) { return hipS
 hipError_t launch_decode(const DecodeArgs &) { return hipSuccess; }
 hipError_t launch_decode_window(const DecodeWindowArgs &) { return hipSuccess; }
 hipError_t launch_window_chunk(const DecodeWindowArgs &) { return hipSuccess; }
+hipError_t launch_layer_window_chunk(const DecodeWindowArgs &, void *) { return hipSuccess; }
+size_t layer_window_chunk_bytes(int64_t B, int64_t T, int64_t Tp, int64_t H) {
+    return (size_t)1024 * (size_t)(B * H * (T + Tp));  // bf16 q, k, v, log-decay of 128 channels
+}
 hipError_t launch_backward(const BackwardArgs &) { return hipSuccess; }
 hipError_t launch_backward_states(const BackwardArgs &, float *) { return hipSuccess; }
 hipError_t launch_backward_slab_cu(int32_t *, int64_t, int64_t, int32_t, void *) { return hipSuccess; }

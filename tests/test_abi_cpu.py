@@ -136,9 +136,9 @@ def test_decode_window_rejects_bad_arguments(lib):
 
 def test_decode_layer_window_replay_rejects_bad_arguments(lib):
     f = lib.kda_decode_layer_window_replay
-    # pqkv pg pb replay Tp | qkv g b conv_w cache l2eps A state o u nw neps y B T H dk dv dt stream
+    # pqkv pg pb replay Tp | qkv g b conv_w cache l2eps A state o u nw neps y B T H dk dv dt ws ws_bytes stream
     base = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, None, FAKE, FAKE, None, None, 0.0,
-            None, 2, 3, 1, 16, 16, kda.KDA_BF16, None]
+            None, 2, 3, 1, 16, 16, kda.KDA_BF16, None, 0, None]
 
     def call(**kw):
         a = list(base)
@@ -156,6 +156,25 @@ def test_decode_layer_window_replay_rejects_bad_arguments(lib):
     assert call(a19=0) == 3
     assert call(a21=24) == 4
     assert call(a3=None, a4=0, a0=None, a1=None, a2=None, a19=0) == 3  # Tp = 0 allows NULL p*, T still checked
+    # the one-chunk form's workspace (bf16, dk = dv = 128, T + Tp = 7): 16-byte aligned, large enough
+    need = lib.kda_decode_layer_window_workspace_bytes(2, 3, 4, 1, 128, 128, kda.KDA_BF16)
+    assert need == 1024 * 2 * 1 * 7
+    assert call(a4=4, a21=128, a22=128, a24=FAKE + 8, a25=need) == 2
+    assert call(a4=4, a21=128, a22=128, a24=FAKE, a25=need - 1) == 3
+
+
+def test_layer_window_workspace_bytes(lib):
+    f = lib.kda_decode_layer_window_workspace_bytes
+    # B T Tp H dk dv dt: 1,024 bytes per (sequence, head, token) where the one-chunk form serves the shape
+    assert f(256, 4, 4, 96, 128, 128, kda.KDA_BF16) == 1024 * 256 * 96 * 8
+    assert f(3, 6, 0, 2, 128, 128, kda.KDA_BF16) == 1024 * 3 * 2 * 6
+    assert f(3, 16, 0, 2, 128, 128, kda.KDA_BF16) == 1024 * 3 * 2 * 16
+    assert f(3, 5, 0, 2, 128, 128, kda.KDA_BF16) == 0     # below 6 tokens: token by token
+    assert f(3, 12, 5, 2, 128, 128, kda.KDA_BF16) == 0    # more than one chunk
+    assert f(3, 8, 0, 2, 128, 128, kda.KDA_F32) == 0      # bf16 only
+    assert f(3, 8, 0, 2, 64, 128, kda.KDA_BF16) == 0      # dk = dv = 128 only
+    assert f(0, 8, 0, 2, 128, 128, kda.KDA_BF16) == 0     # invalid shape
+    assert f(3, 8, -1, 2, 128, 128, kda.KDA_BF16) == 0
 
 
 def test_decode_window_form_rejects_bad_arguments(lib):
