@@ -486,7 +486,12 @@ def bench_decode(torch, kda, workloads, dev, steps):
     res = {"workload": w.name, "heads": B * H, "steps": w.decode_steps, "ms_per_step": round(ms, 5),
            "bytes_per_step": per_step, "gbs": gbs, "hbm_peak_frac": gbs / HBM_PEAK_GBS,
            "tokens_per_s": B / (ms * 1e-3)}
-    del state, o
+    # context beside the published peak: torch's device-to-device copy of the state (the same
+    # bytes read and written once)
+    dst = torch.empty_like(state)
+    ms_copy = _event_ms(torch, lambda: dst.copy_(state), 10)
+    res["torch_copy_gbs"] = 2 * state.numel() * 4 / (ms_copy * 1e-3) / 1e9
+    del state, o, dst
     torch.cuda.empty_cache()
     return res
 
@@ -743,6 +748,33 @@ def bench_layer(torch, kda, workloads, dev):
     ms_f, ms_s = _event_ms(torch, wfused, 20), _event_ms(torch, wseparate, 20)
     res["decode_window4_b256"] = {"batch": B, "T": T, "heads": Hd, "ms_fused": round(ms_f, 5),
                                   "ms_separate": round(ms_s, 5), "speedup": ms_s / ms_f}
+
+    # windows of 8 with the gate from logits and the epilogue: one chunk on the matrix cores (the
+    # gate in fp32 inside the chunk kernel), against the gate pass + the window + the epilogue pass
+    T8 = 8
+    w8 = workloads.workload(4)
+    x8 = workloads.decode_window_inputs(w8, T8, 0, device=dev)
+    k8 = workloads.layer_inputs(B * T8, Hd, dk, torch.bfloat16, device=dev, seed=5)
+    v8 = workloads.layer_inputs(B * T8, Hd, dv, torch.bfloat16, device=dev, seed=6)
+    z8, u8 = k8["z"].view(B, T8, Hd, dk), v8["u"].view(B, T8, Hd, dv)
+    acc8 = workloads.window_accept(B, T8, device=dev, seed=0, lo=1)
+    o8 = torch.empty((B, T8, Hd, dv), dtype=torch.float32, device=dev)
+    y8 = torch.empty((B, T8, Hd, dv), dtype=torch.bfloat16, device=dev)
+    g8 = torch.empty_like(z8)
+
+    def w8fused():
+        kda.kda_decode_window_fused(x8["q"], x8["k"], x8["v"], z8, x8["beta"], state, acc8, gate_A_log=k8["A_log"],
+                                    out_gate=u8, norm_w=v8["norm_w"], o=o8, output_o=False, y=y8)
+
+    def w8separate():
+        kda.kda_gate(k8["z"], k8["A_log"], out=g8.view(B * T8, Hd, dk))
+        kda.kda_decode_window(x8["q"], x8["k"], x8["v"], g8, x8["beta"], state, acc8, o=o8)
+        kda.kda_out_norm_gate(o8.view(B * T8, Hd, dv), v8["u"], v8["norm_w"], 1e-6, y=y8.view(B * T8, Hd, dv))
+
+    ms_f8, ms_s8 = _event_ms(torch, w8fused, 20), _event_ms(torch, w8separate, 20)
+    res["decode_window8_b256"] = {"batch": B, "T": T8, "heads": Hd, "ms_fused": round(ms_f8, 5),
+                                  "ms_separate": round(ms_s8, 5), "speedup": ms_s8 / ms_f8}
+    del x8, k8, v8, z8, u8, acc8, o8, y8, g8
 
     # the layer core's speculative-decoding call at B=256, T=4: the previous window's accepted
     # prefix replayed and the new window run through ShortConv (+ L2), gate and recurrence, the

@@ -91,6 +91,7 @@ struct WcHead {
     int n;    // tokens of the chunk: rp + Tw
     int acc;  // tokens whose state is committed (0: none)
     uint32_t on;  // 1; 0 makes every load of the head read zeros without touching memory
+    float eA;     // e^{A_h} of the gate from logits (0 without)
 };
 
 }  // namespace
@@ -103,7 +104,7 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
                          int32_t Tw, const __bf16 *__restrict__ pq, const __bf16 *__restrict__ pk,
                          const __bf16 *__restrict__ pv, const __bf16 *__restrict__ pg,
                          const __bf16 *__restrict__ pb, const int32_t *__restrict__ replay, int32_t Tp,
-                         int32_t acc_default) {
+                         int32_t acc_default, const float *__restrict__ A_log) {
     constexpr uint32_t EB = 2;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,6 +135,7 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
         x.n = x.rp + Tw;
         x.acc = __builtin_amdgcn_readfirstlane(a) + x.rp;
         x.on = 1;
+        x.eA = A_log ? __expf(A_log[x.h]) : 0.f;
         return x;
     };
     // Token rows of the chunk: row r < rp is token r of the previous window, row r >= rp
@@ -214,14 +216,38 @@ void window_chunk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict_
         const bf16x8 UTL = cat(UT, z4), UTH = cat(z4, UT);
         const u32x2 Rq[2] = {half(A.d[0], 0), half(A.d[0], 1)};
         const u32x2 Rk[2] = {half(A.d[1], 0), half(A.d[1], 1)};
-        const bf16x8 ga = __builtin_bit_cast(bf16x8, A.d[2]);
         const bf16x8 ka = __builtin_bit_cast(bf16x8, A.d[1]);
-        // g and k as tokens 4 g4 + jj of channel 16 b + l16 (exact: bf16 values)
-        const bf16x8 gf = cat(to_bf16x4(mma32(ga, IDL, zero4())), to_bf16x4(mma32(ga, IDH, zero4())));
         const f32x4 kc[2] = {mma32(ka, IDL, zero4()), mma32(ka, IDH, zero4())};
-        // G at token l16, channels 16 b + 4 g4 + jj; Gs at tokens 4 g4 + jj, channel 16 b + l16
-        const f32x4 GT[2] = {mma32(gf, LTL, zero4()), mma32(gf, LTH, zero4())};
-        const f32x4 GS[2] = {mma32(UTL, gf, zero4()), mma32(UTH, gf, zero4())};
+        // g and k as tokens 4 g4 + jj of channel 16 b + l16 (exact for bf16 values); G at token
+        // l16, channels 16 b + 4 g4 + jj; Gs at tokens 4 g4 + jj, channel 16 b + l16
+        f32x4 GT[2], GS[2];
+        if (A_log) {
+            // the gate from logits, -5 Sigmoid(e^{A_h} z), in fp32 and split hi + lo for the
+            // transposes and the triangle sums (rows past the head's tokens: g = 0)
+            const bf16x8 za = __builtin_bit_cast(bf16x8, A.d[2]);
+            const bool row = l16 < x.n;
+            f32x4 gv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gv[u][j] = row ? gate_of(x.eA, (float)za[4 * u + j]) : 0.f;
+            const bf16x4 gh0 = to_bf16x4(gv[0]), gh1 = to_bf16x4(gv[1]);
+            const bf16x8 gah = cat(gh0, gh1);
+            const bf16x8 gal = cat(to_bf16x4(gv[0] - from_bf16x4(gh0)), to_bf16x4(gv[1] - from_bf16x4(gh1)));
+            const bf16x8 gfh = cat(to_bf16x4(mma32(gah, IDL, zero4())), to_bf16x4(mma32(gah, IDH, zero4())));
+            const bf16x8 gfl = cat(to_bf16x4(mma32(gal, IDL, zero4())), to_bf16x4(mma32(gal, IDH, zero4())));
+            GT[0] = mma32(gfl, LTL, mma32(gfh, LTL, zero4()));
+            GT[1] = mma32(gfl, LTH, mma32(gfh, LTH, zero4()));
+            GS[0] = mma32(UTL, gfl, mma32(UTL, gfh, zero4()));
+            GS[1] = mma32(UTH, gfl, mma32(UTH, gfh, zero4()));
+        } else {
+            const bf16x8 ga = __builtin_bit_cast(bf16x8, A.d[2]);
+            const bf16x8 gf = cat(to_bf16x4(mma32(ga, IDL, zero4())), to_bf16x4(mma32(ga, IDH, zero4())));
+            GT[0] = mma32(gf, LTL, zero4());
+            GT[1] = mma32(gf, LTH, zero4());
+            GS[0] = mma32(UTL, gf, zero4());
+            GS[1] = mma32(UTH, gf, zero4());
+        }
         f32x4 Pp[2], qv[2], ktv[2], kmv[2], kpv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -492,7 +518,7 @@ hipError_t launch_window_chunk(const DecodeWindowArgs &a) {
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (const __bf16 *)a.g,
                        (const __bf16 *)a.beta, a.state, a.o, a.accept, (uint32_t)heads, (uint32_t)a.H, a.T,
                        (const __bf16 *)a.pq, (const __bf16 *)a.pk, (const __bf16 *)a.pv, (const __bf16 *)a.pg,
-                       (const __bf16 *)a.pbeta, a.replay, a.Tp, acc_default);
+                       (const __bf16 *)a.pbeta, a.replay, a.Tp, acc_default, a.fx.A_log);
     e = hipGetLastError();
     if (e != hipSuccess || !a.fx.u) return e;
     const OutNormGateArgs ep{a.o, a.fx.u, a.fx.w, a.fx.eps, (int64_t)a.B * a.T, a.H, a.dv, a.bf16, a.fx.y, a.stream};

@@ -67,12 +67,12 @@ struct DecodeWindowArgs {
     int32_t form = 0;
 };
 
-// Shapes the one-chunk window form serves: bf16, dk = dv = 128, no fused gate or
-// ShortConv prologue, and the window's tokens (with a replay in front) within one
-// 16-token chunk.
+// Shapes the one-chunk window form serves: bf16, dk = dv = 128 (with or without the gate
+// from logits), no ShortConv prologue, and the window's tokens (with a replay in front)
+// within one 16-token chunk.
 inline bool window_chunk_supported(const DecodeWindowArgs &a) {
     const int64_t tokens = (int64_t)a.T + (a.replay ? a.Tp : 0);
-    return a.bf16 && a.dk == 128 && a.dv == 128 && !a.fx.A_log && !a.fx.conv_w && a.T >= 1 && tokens <= 16;
+    return a.bf16 && a.dk == 128 && a.dv == 128 && !a.fx.conv_w && a.T >= 1 && tokens <= 16;
 }
 
 // Calls of this many tokens per (sequence, head) on (the window's, plus the replay's at

@@ -213,3 +213,38 @@ def test_chunk_window_workload_shape(dev):
         assert_close(state[bi, hi], ref_state, TOL[BF], f"window {win} state")
     del state
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [6, 8, 16])
+def test_chunk_window_gate_from_logits(dev, T):
+    """kda_decode_window_fused with decay logits and the per-head gate from 6 tokens on runs as
+    one chunk (the gate in fp32, split hi + lo for the chunk's decay sums), with the epilogue:
+    outputs, y and the state after each accepted count against the oracles (gate, decode steps,
+    epilogue)."""
+    from oracle import layer
+    B, H = 5, 3
+    w = workloads.custom([1] * B, H, 128, 128, BF)
+    x = workloads.decode_window_inputs(w, T, 0, device=dev, seed=70 + T)
+    lk = workloads.layer_inputs(B * T, H, 128, BF, device=dev, seed=71 + T)
+    lv = workloads.layer_inputs(B * T, H, 128, BF, device=dev, seed=72 + T)
+    z = lk["z"].view(B, T, H, 128).contiguous()
+    u = lv["u"].view(B, T, H, 128).contiguous()
+    init = workloads.random_state(B, H, 128, 128, device=dev, seed=T)
+    state = init.clone()
+    accepts = [0, 1, T // 2, T - 1, T]
+    acc = torch.tensor(accepts, dtype=torch.int32, device=dev)
+    say(f"  case: chunk-form window with the gate from logits B={B} T={T} H={H}")
+    o = torch.full((B, T, H, 128), float("nan"), dtype=torch.float32, device=dev)
+    o, y = kda.kda_decode_window_fused(x["q"], x["k"], x["v"], z, x["beta"], state, acc, gate_A_log=lk["A_log"],
+                                       out_gate=u, norm_w=lv["norm_w"], o=o)
+    torch.cuda.synchronize()
+    g = layer.gate(_np(lk["z"]), _np(lk["A_log"])).reshape(B, T, H, 128)
+    y_dict = dict(x)
+    y_dict["log_alpha"] = torch.from_numpy(g)
+    o_ref, st_ref = _oracle_window(y_dict, init, accepts)
+    assert_close(o, o_ref, TOL[BF], "o")
+    assert_close(state, st_ref, TOL[BF], "state")
+    assert torch.equal(state[0], init[0]), "sequence 0 accepted nothing but its state changed"
+    y_ref = layer.out_norm_gate(o_ref, _np(u), _np(lv["norm_w"]), 1e-6)
+    rms = float(np.sqrt(np.mean(y_ref * y_ref)))
+    assert np.all(np.abs(_np(y) - y_ref) <= TOL[BF] * rms + 2.0 ** -8 * np.abs(y_ref)), "y"
