@@ -371,7 +371,9 @@ kda_status kda_decode_window_replay(const void *pq, const void *pk, const void *
  * the operands, so a decode step of the layer is one launch):
  *   * gate_A_log != NULL: `gate` holds the decay logits z (same layout as
  *     log_alpha) and the kernel takes log-decay g = -5 Sigmoid(exp(A_log[h]) z)
- *     in fp32 (not rounded to the input dtype); gate_A_log is fp32 [H].
+ *     in fp32 (not rounded to the input dtype; a window evaluated as one chunk
+ *     enters it into its decay sums as a hi + lo pair of bf16, 16 significant
+ *     bits); gate_A_log is fp32 [H].
  *     NULL: `gate` is log_alpha as in kda_decode_step.
  *   * out_gate != NULL: y = Sigmoid(out_gate) * o / sqrt(mean(o^2) + norm_eps)
  *     * norm_w over the dv channels of each output row, written in the input
