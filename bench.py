@@ -803,11 +803,12 @@ def bench_layer(torch, kda, workloads, dev):
     ms_l = _event_ms(torch, lambda: lwin(None), 20)
     ms_t = _event_ms(torch, lambda: lwin(1), 20)
     replayed = float(acc.double().mean())
-    # algorithmic HBM bytes: the state read and written once per head; per replayed token its raw
-    # q | k | v row, gate logits and beta; per window token those, o (fp32), u and y
+    # algorithmic HBM bytes: the state and the convolution cache (fp32, 3 inputs per channel) read
+    # and written once per head; per replayed token its raw q | k | v row, gate logits and beta;
+    # per window token those, o (fp32), u and y
     bpt_r = 2 * (C + dk + 1)
     bpt_w = bpt_r + 4 * dv + 2 * dv + 2 * dv
-    nbytes = B * Hd * (2 * dk * dv * 4 + replayed * bpt_r + T * bpt_w)
+    nbytes = B * Hd * (2 * dk * dv * 4 + 2 * C * 3 * 4 + replayed * bpt_r + T * bpt_w)
     res["decode_layer_window_replay4_b256"] = {"batch": B, "T": T, "heads": Hd, "form": "one chunk" if need else
                                                "token by token", "ms_per_call": round(ms_l, 5),
                                                "ms_token_by_token": round(ms_t, 5),
