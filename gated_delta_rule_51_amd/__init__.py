@@ -37,7 +37,7 @@ EXPORTS = ("kda_prefill_workspace_bytes", "kda_chunk_workspace_bytes", "kda_pref
            "kda_prefill_backward_slabbed_workspace_bytes", "kda_prefill_backward_slabbed",
            "kda_prefill_cp_workspace_bytes", "kda_prefill_cp",
            "kda_gate", "kda_short_conv", "kda_out_norm_gate", "kda_prefill_layer_workspace_bytes",
-           "kda_prefill_layer", "kda_status_string", "kda_last_hip_error")
+           "kda_prefill_layer", "kda_check_cu_seqlens", "kda_status_string", "kda_last_hip_error")
 
 _lib = None
 
@@ -132,6 +132,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill_layer.restype = ctypes.c_int
     lib.kda_prefill_layer.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                       ctypes.c_int, vp, sz, vp, vp, vp, vp, f32, vp, vp]
+    lib.kda_check_cu_seqlens.restype = ctypes.c_int
+    lib.kda_check_cu_seqlens.argtypes = [vp, i32, i64, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_hip_error.restype = i32
@@ -759,6 +761,23 @@ def kda_decode_layer_window_replay(prev, replay, qkv, gate, beta, conv_w, conv_c
         _ptr(norm_w), float(norm_eps), _ptr(y), B, T, H, dk, dv, _dtype_code(qkv.dtype), _ptr(ws), ws_bytes,
         _stream(stream)))
     return o, y
+
+
+def kda_check_cu_seqlens(cu_seqlens, total_tokens: int, *, result=None, stream=None) -> torch.Tensor:
+    """Check a device cu_seqlens (int32 [nseq + 1]) against the layout contract on the GPU.
+    Returns the int32 device tensor [1] the kernel writes: -1 when valid, else the first index
+    that breaks it (read it with .item(), which synchronises)."""
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.device.type != "cuda":
+        raise ValueError("cu_seqlens must be a tensor on a GPU; the KDA library has no CPU path")
+    _check_dev("cu_seqlens", cu_seqlens, cu_seqlens.device, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [nseq + 1] with nseq >= 1")
+    if result is None:
+        result = torch.empty(1, dtype=torch.int32, device=cu_seqlens.device)
+    _check_dev("result", result, cu_seqlens.device, torch.int32, (1,))
+    _check(load_library().kda_check_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.numel() - 1, int(total_tokens),
+                                               _ptr(result), _stream(stream)))
+    return result
 
 
 def kda_prefill_backward(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, init_state=None, d_final=None, *,

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libkda_mi355x.so")
 SOURCES = ["api.cpp", "decode.hip", "decode_chunk.hip", "chunk_local.hip", "inter_chunk.hip", "inter_chunk_ws.hip", "layer.hip", "backward.hip",
-           "cp.hip", "noalloc.hip",
+           "cp.hip", "noalloc.hip", "checks.hip",
            "prefill_fused.hip"]
 ARCH = "gfx950"
 # Per-file additions.  chunk_local: matrix-core results in VGPRs (not AGPRs) --

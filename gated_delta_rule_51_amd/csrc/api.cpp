@@ -788,6 +788,16 @@ kda_status kda_gate(const void *z, const float *A_log, int64_t N, int32_t H, int
     return hip_status(kda::launch_gate(a));
 }
 
+kda_status kda_check_cu_seqlens(const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, int32_t *result,
+                                void *stream) {
+    if (!cu_seqlens || !result) return KDA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) || (reinterpret_cast<uintptr_t>(result) & 3u))
+        return KDA_ERR_ALIGN;
+    if (nseq < 1 || nseq >= (int32_t(1) << 30) || total_tokens < 0 || total_tokens >= (int64_t(1) << 31))
+        return KDA_ERR_SHAPE;
+    return hip_status(kda::launch_check_cu_seqlens(cu_seqlens, nseq, total_tokens, result, stream));
+}
+
 kda_status kda_short_conv(const void *x, const float *w, const float *cache_in, float *cache_out,
                           const int32_t *cu_seqlens, int32_t nseq, int64_t N, int32_t H, int32_t d,
                           int32_t l2norm, float eps, kda_dtype dt, void *y, void *stream) {

@@ -232,6 +232,7 @@ hipError_t launch_out_norm_gate(const OutNormGateArgs &a);
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_decode_window(const DecodeWindowArgs &a);
 hipError_t launch_window_chunk(const DecodeWindowArgs &a);
+hipError_t launch_check_cu_seqlens(const int32_t *cu, int32_t nseq, int64_t N, int32_t *result, void *stream);
 hipError_t launch_chunk_local(const ChunkLocalArgs &a);
 hipError_t launch_inter_chunk(const InterChunkArgs &a);
 // Warp-specialised inter-chunk kernel (bf16, dk >= 32): ncw consumer and npw

@@ -586,6 +586,20 @@ kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
                                int32_t dk, int32_t dv, kda_dtype dt,
                                float *o, float *final_state, void *stream);
 
+/* Opt-in check of a device-resident cu_seqlens against the layout contract above
+ * (cu[0] = 0, non-decreasing, every entry in [0, total_tokens], cu[nseq] =
+ * total_tokens), which the prefill-family calls assume without reading it on the
+ * host.  One small kernel on `stream` writes to *result (device int32, 4-byte
+ * aligned): -1 when the contract holds, else the smallest index i whose entry
+ * breaks it (0: cu[0] != 0; i: cu[i] < cu[i-1] or out of range; nseq: the last
+ * entry is not total_tokens).  For callers that build the offsets on the device
+ * (a malformed one makes the kernels read and write outside the caller's
+ * buffers).  Kernel launch only, like every call.  Errors: NULL pointers
+ * KDA_ERR_NULL, misalignment KDA_ERR_ALIGN, nseq < 1 or total_tokens out of
+ * range KDA_ERR_SHAPE. */
+kda_status kda_check_cu_seqlens(const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, int32_t *result,
+                                void *stream);
+
 /* Static string naming a status code. */
 const char *kda_status_string(kda_status s);
 

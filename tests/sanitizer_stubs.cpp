@@ -18,6 +18,7 @@ hipError_t launch_decode(const DecodeArgs &) { return hipSuccess; }
 hipError_t launch_decode_window(const DecodeWindowArgs &) { return hipSuccess; }
 hipError_t launch_window_chunk(const DecodeWindowArgs &) { return hipSuccess; }
 hipError_t launch_layer_window_chunk(const DecodeWindowArgs &, void *) { return hipSuccess; }
+hipError_t launch_check_cu_seqlens(const int32_t *, int32_t, int64_t, int32_t *, void *) { return hipSuccess; }
 size_t layer_window_chunk_bytes(int64_t B, int64_t T, int64_t Tp, int64_t H) {
     return (size_t)1024 * (size_t)(B * H * (T + Tp));  // bf16 q, k, v, log-decay of 128 channels
 }

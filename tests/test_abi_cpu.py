@@ -447,3 +447,14 @@ def test_noalloc_rejects_problems_above_the_scratch_on_the_host(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1 << 20, 96, 128, 128, 0, FAKE, None, None) == 7
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1 << 20, 96, 128, 128, 1, FAKE, None, None) == 7
     assert kda.kda_status_string(7).startswith("KDA_ERR_TOO_LARGE")
+
+
+def test_check_cu_seqlens_rejects_bad_arguments(lib):
+    f = lib.kda_check_cu_seqlens  # cu nseq N result stream
+    assert f(None, 2, 10, FAKE, None) == 1
+    assert f(FAKE, 2, 10, None, None) == 1
+    assert f(FAKE + 2, 2, 10, FAKE, None) == 2
+    assert f(FAKE, 2, 10, FAKE + 1, None) == 2
+    assert f(FAKE, 0, 10, FAKE, None) == 3
+    assert f(FAKE, 2, -1, FAKE, None) == 3
+    assert f(FAKE, 2, 1 << 31, FAKE, None) == 3

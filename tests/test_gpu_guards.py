@@ -225,3 +225,21 @@ def test_decode_window_is_independent_of_batch_order(dev):
                                acc[perm].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(o1[perm], o2) and torch.equal(s1[perm], s2)
+
+
+def test_check_cu_seqlens(dev):
+    """The opt-in device check of cu_seqlens: -1 for valid offsets (empty sequences included),
+    else the first index that breaks the contract."""
+    def check(cu, N):
+        return int(kda.kda_check_cu_seqlens(torch.tensor(cu, dtype=torch.int32, device=dev), N).item())
+    assert check([0, 5, 5, 12], 12) == -1
+    assert check([0, 0], 0) == -1
+    assert check([1, 5, 12], 12) == 0          # does not start at 0
+    assert check([0, 7, 5, 12], 12) == 2       # decreasing
+    assert check([0, 5, 11], 12) == 2          # does not end at N
+    assert check([0, 5, 13, 12], 12) == 2      # beyond N
+    assert check([0, -1, 3], 3) == 1           # negative
+    big = list(range(0, 3 * 5000 + 1, 3))      # 5,000 sequences: several strides of the workgroup
+    assert check(big, 15000) == -1
+    big[4321] = big[4320] - 1
+    assert check(big, 15000) == 4321
