@@ -592,7 +592,7 @@ kda_status kda_decode_layer_window_replay(const void *pqkv, const void *pgate, c
         a.replay = replay;
         a.Tp = Tp;
     }
-    if (workspace && kda::layer_window_chunk_supported(a) && T + Tp >= kda::WINDOW_CHUNK_MIN_TOKENS) {
+    if (workspace && kda::layer_window_chunk_supported(a) && (int64_t)T + Tp >= kda::WINDOW_CHUNK_MIN_TOKENS) {
         if (reinterpret_cast<uintptr_t>(workspace) & 15u) return KDA_ERR_ALIGN;
         if (workspace_bytes < kda::layer_window_chunk_bytes(B, T, Tp, H)) return KDA_ERR_SHAPE;
         return hip_status(kda::launch_layer_window_chunk(a, workspace));
@@ -605,7 +605,8 @@ size_t kda_decode_layer_window_workspace_bytes(int32_t B, int32_t T, int32_t Tp,
     if (B < 1 || T < 1 || H < 1 || Tp < 0 || (int64_t)B * T * H >= (int64_t(1) << 31) ||
         (int64_t)B * Tp * H >= (int64_t(1) << 31))
         return 0;
-    if (!(dt == KDA_BF16 && dk == 128 && dv == 128 && T + Tp >= kda::WINDOW_CHUNK_MIN_TOKENS && T + Tp <= 16))
+    const int64_t tokens = (int64_t)T + Tp;
+    if (!(dt == KDA_BF16 && dk == 128 && dv == 128 && tokens >= kda::WINDOW_CHUNK_MIN_TOKENS && tokens <= 16))
         return 0;
     return kda::layer_window_chunk_bytes(B, T, Tp, H);
 }

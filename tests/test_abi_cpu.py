@@ -175,6 +175,7 @@ def test_layer_window_workspace_bytes(lib):
     assert f(3, 8, 0, 2, 64, 128, kda.KDA_BF16) == 0      # dk = dv = 128 only
     assert f(0, 8, 0, 2, 128, 128, kda.KDA_BF16) == 0     # invalid shape
     assert f(3, 8, -1, 2, 128, 128, kda.KDA_BF16) == 0
+    assert f(1, (1 << 31) - 1, (1 << 31) - 1, 1, 128, 128, kda.KDA_BF16) == 0  # no int overflow in T + Tp
 
 
 def test_decode_window_form_rejects_bad_arguments(lib):
