@@ -222,3 +222,84 @@ def test_layer_window_chunk_form_is_the_automatic_choice(dev):
     with pytest.raises(ValueError):
         kda.kda_decode_layer_window_replay(None, None, wins[1]["qkv"], wins[1]["gate"], wins[1]["beta"], ex["conv_w"],
                                            ex["cache"].clone(), state0.clone(), dk=dk, form=2)  # 4 tokens: no chunk form
+
+
+def test_layer_window_workload_shape_sampled_heads(dev):
+    """The decode workload's shape (B=256 x H=96) in the launch configuration the benchmark times:
+    windows of 4 with the previous window's accepted prefix replayed (T + Tp = 8: one chunk, the
+    prologue pass over 24,576 heads), gate from logits; two calls.  On 48 sampled (sequence,
+    head) pairs: the prologue's bf16 rows in the workspace within one bf16 rounding of the fp64
+    stage oracles; the recurrence oracle fed those rows (the recurrence's own inputs -- an
+    oracle that rounds by itself lands a few heavy-tailed values on the other side of a bf16
+    boundary) against o and the committed state; the committed cache exactly."""
+    w = workloads.workload(4)
+    B, H, T, dk, dv = w.nseq, w.H, 4, 128, 128
+    C = 2 * dk + dv
+    wins = []
+    for i in range(3):
+        lx = workloads.layer_inputs(B * T, H, C, torch.bfloat16, nseq=B, device=dev, seed=60 + i)
+        lz = workloads.layer_inputs(B * T, H, dk, torch.bfloat16, device=dev, seed=70 + i)
+        xw = workloads.decode_window_inputs(w, T, i, device=dev)
+        wins.append({"qkv": lx["x"].view(B, T, H, C), "gate": lz["z"].view(B, T, H, dk), "beta": xw["beta"]})
+    conv_w, A_log = lx["conv_w"], lz["A_log"]
+    cache = workloads.layer_inputs(B, H, C, torch.bfloat16, nseq=B, device=dev, seed=80)["conv_cache"]
+    state = workloads.decode_initial_state(B, H, dk, dv, device=dev)
+    accs = [workloads.window_accept(B, T, device=dev, seed=s, lo=0) for s in (1, 2)]
+    rng = np.random.default_rng(11)
+    bi, hi = rng.integers(0, B, 48), rng.integers(0, H, 48)
+    bt, ht = torch.tensor(bi, device=dev), torch.tensor(hi, device=dev)
+    ref_state = state[bt, ht].double().cpu().numpy()
+    ref_cache = cache[bt, ht].double().cpu().numpy()
+    need = kda.kda_decode_layer_window_workspace_bytes(B, T, T, H, dk, dv, torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    cw, A = _np(conv_w), _np(A_log)
+    say(f"  case: layer window B={B} H={H} T={T} with replay, 48 sampled heads")
+    for i in (1, 2):
+        o = torch.full((B, T, H, dv), float("nan"), dtype=torch.float32, device=dev)
+        o, _ = kda.kda_decode_layer_window_replay(wins[i - 1], accs[i - 1], wins[i]["qkv"], wins[i]["gate"],
+                                                  wins[i]["beta"], conv_w, cache, state, dk=dk, gate_A_log=A_log,
+                                                  o=o, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all(), "an output row was not written"
+        wb = ws.view(torch.bfloat16)
+        cur = wb[:4 * B * T * H * 128].view(4, B, T, H, 128)[:, bt, :, ht].double().cpu().numpy()  # [48, 4, T, 128]
+        pre = wb[4 * B * T * H * 128:].view(4, B, T, H, 128)[:, bt, :, ht].double().cpu().numpy()
+        o_got = o[bt, :, ht].double().cpu().numpy()
+        acc = accs[i - 1].cpu().numpy()
+        o_ref = np.zeros_like(o_got)
+        worst = 0.0
+        for n in range(48):
+            b, h = int(bi[n]), int(hi[n])
+            rp = int(acc[b])
+            rows = np.concatenate([_np(wins[i - 1]["qkv"][b, :rp, h]), _np(wins[i]["qkv"][b, :, h])])  # [rp + T, C]
+            z = np.concatenate([_np(wins[i - 1]["gate"][b, :rp, h]), _np(wins[i]["gate"][b, :, h])])
+            beta = np.concatenate([_np(wins[i - 1]["beta"][b, :rp, h]), _np(wins[i]["beta"][b, :, h])])
+            # the prologue's rows against the stage oracles, within one bf16 rounding
+            got = np.concatenate([pre[n][:, :rp], cur[n]], axis=1)  # [4 (q, k, v, g), rp + T, 128]
+            stage = []
+            for lo, l2 in ((0, True), (dk, True), (2 * dk, False)):
+                stage.append(layer.short_conv(rows[:, None, lo:lo + 128], cw[h:h + 1, lo:lo + 128], None,
+                                              ref_cache[n][None, None, lo:lo + 128], l2norm=l2, eps=1e-6)[0][:, 0])
+            stage.append(layer.gate(z[:, None], A[h:h + 1])[:, 0])
+            for j in range(4):
+                ref = stage[j]
+                tol = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.sqrt(np.mean(ref * ref))
+                assert np.all(np.abs(got[j] - ref) <= tol), f"call {i}, pair {n}: prologue output {'qkvg'[j]}"
+            # the recurrence on those rows; the state commits after the prefix
+            st = ref_state[n][None, None]
+            committed = st
+            for t in range(rp + T):
+                ot, st = oracle.decode(got[0, t][None, None], got[1, t][None, None], got[2, t][None, None],
+                                       got[3, t][None, None], beta[t][None, None], st)
+                if t + 1 == rp:
+                    committed = st
+                if t >= rp:
+                    o_ref[n, t - rp] = ot[0, 0]
+            ref_state[n] = committed[0, 0]
+            ref_cache[n] = layer.short_conv(rows[:rp, None], cw[h:h + 1], None, ref_cache[n][None, None])[1][0, 0] \
+                if rp > 0 else ref_cache[n]
+        assert_close(o_got, o_ref, TOL[torch.bfloat16], f"call {i} o (sampled heads)")
+    assert_close(state[bt, ht], ref_state, TOL[torch.bfloat16], "committed state (sampled heads)")
+    assert np.array_equal(cache[bt, ht].double().cpu().numpy(), ref_cache), "committed convolution cache"
+    del state, cache, ws
+    torch.cuda.empty_cache()
