@@ -282,6 +282,9 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                     Ob = mma32(qlr[p], Shi[p], Ob);
                     Oc = mma32(qhr[p], Slo[p], Oc);
                 }
+                // Diag(Gamma) S now: it does not depend on Delta and fills the Delta chain's gaps
+#pragma unroll
+                for (int b = 0; b < NB; ++b) S[b] *= gmr[b];
                 // Delta = T' (V - X)
                 bf16x8 yhh, dhh;
                 const bf16x4 ylo = split_lo(vc - (Xa + (Xb + Xc)), NIL, yhh);
@@ -290,11 +293,11 @@ __global__ __launch_bounds__((64 * WsLayout<NC, NP>::NW)) __attribute__((amdgpu_
                 D = mma32(tpp, cat(ylo, ylo), D);
                 const bf16x4 dlo = split_lo(D, NIL, dhh);
                 const bf16x8 dll = cat(dlo, dlo);
-                // S <- Diag(Gamma) S + K~^T Delta
+                // S <- (Diag(Gamma) S, formed above) + K~^T Delta
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const bf16x8 ktt = cat(ktr[b].hi, ktr[b].lo);
-                    const f32x4 acc = mma32(ktt, dhh, S[b] * gmr[b]);
+                    const f32x4 acc = mma32(ktt, dhh, S[b]);
                     S[b] = mma32(ktt, dll, acc);
                 }
                 // O = Q+ S + A_qk Delta

@@ -216,6 +216,13 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                         Oc[sl] = mma32(qhr, Slo, Oc[sl]);
                     }
                 }
+                // Diag(Gamma) S now: it does not depend on Delta and fills the Delta chain's gaps
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * g4]);
+#pragma unroll
+                    for (int sl = 0; sl < SL; ++sl) S[sl][b] *= gm;
+                }
                 // Delta = T' (V - X), per slice
                 f32x4 Op[SL];
                 bf16x8 dhh[SL], dll[SL];
@@ -230,15 +237,14 @@ void prefill_fused_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict
                     dll[sl] = cat(dlo, dlo);
                     Op[sl] = Oa[sl] + (Ob[sl] + Oc[sl]);
                 }
-                // S <- Diag(Gamma) S + K~^T Delta, one key block at a time for every slice
+                // S <- (Diag(Gamma) S, formed above) + K~^T Delta, one key block at a time for every slice
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const Split4 kt = P.kt[b][lane];
-                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(&P.gam[16 * b + 4 * g4]);
                     const bf16x8 ktt = cat(kt.hi, kt.lo);
 #pragma unroll
                     for (int sl = 0; sl < SL; ++sl) {
-                        const f32x4 acc = mma32(ktt, dhh[sl], S[sl][b] * gm);
+                        const f32x4 acc = mma32(ktt, dhh[sl], S[sl][b]);
                         S[sl][b] = mma32(ktt, dll[sl], acc);
                     }
                 }
