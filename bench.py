@@ -72,6 +72,27 @@ def window_bytes_per_head(dk: int, dv: int, T: int, in_bytes: int = 2) -> float:
     return 2 * dk * dv * 4 + T * (in_bytes * (3 * dk + dv + 1) + 4 * dv)
 
 
+N_CU = 256  # MI355X compute units
+
+
+def bound_fields(flops: float, alg_bytes: float, ms: float, seqlens, H: int) -> dict:
+    """The prefill's ceilings beside its time: HBM time and matrix-core time of the algorithmic
+    bytes and flops (the active bound is the larger), the attainable rate min(MFMA peak,
+    arithmetic intensity x HBM peak) and the fraction of it reached, and the serial-chain view:
+    chunk steps of the longest (sequence, head) chain and of an even share of all chains per
+    compute unit, with the time per step of each."""
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    att = min(MFMA_BF16_PEAK_TFLOPS, flops / alg_bytes * HBM_PEAK_GBS / 1e3)
+    longest = -(-max(seqlens) // CHUNK)
+    per_cu = sum(-(-n // CHUNK) for n in seqlens) * H / N_CU
+    return {"t_hbm_ms": t_hbm, "t_mfma_ms": t_mfma, "active_bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "time_over_bound": ms / max(t_hbm, t_mfma), "attainable_tflops": att,
+            "attainable_frac": flops / (ms * 1e-3) / 1e12 / att,
+            "longest_chain_steps": longest, "ns_per_longest_chain_step": ms * 1e6 / longest,
+            "chain_steps_per_cu": per_cu, "ns_per_chain_step_per_cu": ms * 1e6 / max(per_cu, 1e-9)}
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -321,7 +342,7 @@ def bench_headline(args, torch, kda, workloads, dev, cpu_baseline: bool = True) 
                     "tflops": flops / (prefill_ms * 1e-3) / 1e12,
                     "mfma_peak_frac": flops / (prefill_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                     "hbm_gbs_algorithmic": ach, "hbm_roofline_frac": ach / HBM_PEAK_GBS,
-                    "t_hbm_ms": alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3},
+                    **bound_fields(flops, alg_bytes, prefill_ms, w.seqlens, H)},
         "roofline": {"kernel": "prefill" if single_pass else "prefill (chunk_local + inter_chunk)",
                      "hip_kernel": hip_kernel or ("prefill_fused_kernel<128,128,4,2>" if single_pass else None),
                      "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -455,7 +476,7 @@ def bench_prefill_workload(index, torch, kda, workloads, dev, reps: int):
         "mfma_peak_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "hbm_gbs_algorithmic": alg_bytes / (ms * 1e-3) / 1e9,
         "hbm_roofline_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "t_hbm_ms": alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+        **bound_fields(flops, alg_bytes, ms, w.seqlens, H),
     }
     if index == 5:
         res["seqlens"] = list(w.seqlens)
@@ -966,7 +987,9 @@ def main() -> int:
             "ms_per_step": round(m["wall_ms"], 5), "tokens_per_s": m["tokens"] / (m["wall_ms"] * 1e-3),
             "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
             "prefill_tflops": m["prefill_tflops"],
-            "prefill_hbm_frac": alg / (m["ms_prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "prefill_hbm_frac": alg / (m["ms_prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "prefill_bounds": bound_fields(th * prefill_flops_per_token_head(w.dk, w.dv), alg, m["ms_prefill"],
+                                           w.seqlens, w.H)}
         if m["graph_ms"] is not None:
             out["batched"]["ms_per_step_graph_replay"] = round(m["graph_ms"], 5)
     if args.only in ("all", "k3"):
