@@ -84,13 +84,13 @@ def bound_fields(flops: float, alg_bytes: float, ms: float, seqlens, H: int) -> 
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
     t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
     att = min(MFMA_BF16_PEAK_TFLOPS, flops / alg_bytes * HBM_PEAK_GBS / 1e3)
-    longest = -(-max(seqlens) // CHUNK)
-    per_cu = sum(-(-n // CHUNK) for n in seqlens) * H / N_CU
+    longest = max(1, -(-max(seqlens) // CHUNK))
+    per_cu = max(1.0, sum(-(-n // CHUNK) for n in seqlens) * H / N_CU)
     return {"t_hbm_ms": t_hbm, "t_mfma_ms": t_mfma, "active_bound": "hbm" if t_hbm >= t_mfma else "mfma",
             "time_over_bound": ms / max(t_hbm, t_mfma), "attainable_tflops": att,
             "attainable_frac": flops / (ms * 1e-3) / 1e12 / att,
             "longest_chain_steps": longest, "ns_per_longest_chain_step": ms * 1e6 / longest,
-            "chain_steps_per_cu": per_cu, "ns_per_chain_step_per_cu": ms * 1e6 / max(per_cu, 1e-9)}
+            "chain_steps_per_cu": per_cu, "ns_per_chain_step_per_cu": ms * 1e6 / per_cu}
 
 
 def log(msg: str) -> None:
